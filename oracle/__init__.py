@@ -1,0 +1,351 @@
+"""CPU oracle for the N:M structured-sparse linear layer Y = S(X) . W^T.
+
+TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package.  The library's GPU path never calls it, and
+it shares no code, table or helper with the GPU path: it is written from the papers'
+descriptions, plain and unblocked, so that a reader can check each step by eye.
+
+Conventions
+-----------
+* bf16 tensors are numpy ``uint16`` arrays of bit patterns, row-major, K fastest.
+* Floating-point results are computed in fp64 (every bf16 x bf16 product is exact in
+  fp64; the only rounding is the fp64 summation, far below the GPU's fp32 rounding).
+* "Group" = m contiguous elements along K; group g of a row covers k in [g*m, g*m+m).
+
+Sources (cited by page title and section)
+-----------------------------------------
+[FLEX]  "Motivating Next-Gen Accelerators with Flexible (N:M) Activation Sparsity via
+        Benchmarking Lightweight Post-Training Sparsification Approaches"
+        - technical summary section 1 (configuration counts 6 and 12,870; metadata cost),
+          section 2.A (ACT score = activation magnitude), section 2.C (patterns 2:4, 4:8,
+          8:16, 16:32 along the reduction dimension).
+[SLIDE] "SlideSparse: Fast and Flexible (2N-2):2N Structured Sparsity"
+        - technical summary section 2.A (N-1 overlapping windows of width 4, stride 2,
+          at most 2 non-zeros each, overflow carried to the next window; gamma=(2N-2)/N),
+          section 2.B (activation lifting), section 2.C (offline packer), section 4
+          (theoretical speedup N/(N-1)).
+[SPENSE] "SpenseGPT: Practical One-shot Pruning Enabling Sparse and Dense GEMMs for LLM
+        Inference" - technical summary section 2.A (dense region + 2:4 region, input
+        split with accumulation), section 2.B (dense indices permuted into a contiguous
+        block).
+
+Readings where the pages are silent (each is listed in the design notes):
+* Ties in the magnitude order go to the lower in-group index.
+* Magnitude order = order of the 15 low bits of the bf16 pattern (sign dropped).  This
+  equals the |x| order for every finite or infinite value; +0 and -0 tie; a NaN ranks
+  above infinity.
+* Pruned entries of S(X) are +0.0 (bits 0x0000); kept entries are copied bit for bit.
+* Index metadata: one byte per kept value holding its in-group position (0..m-1), kept
+  values stored in ascending position; for 2:4 the same positions can be packed two bits
+  each (byte j//4, bits 2*(j%4)) where j is the kept-value slot.
+* Sliding windows: kept positions are visited in ascending order and each goes to the
+  lowest-numbered window that covers it and still holds fewer than two ("overflow moves
+  to the next window").  Window w of group g occupies lowered positions
+  g*4(N-1) + 4w + s holding original position g*2N + 2w + s.
+* Hybrid split: dense columns = the K_d columns with the largest L2 norm over the output
+  dimension (sum of squares in fp64, o ascending; ties to the lower column); sparse
+  region first, then dense region, each in ascending original column order; the sparse
+  region is pruned 2:4 by magnitude over consecutive permuted columns.
+* fp8 weights: OCP E4M3FN codes with one fp32 scale per output row, applied after the
+  K reduction.
+"""
+from __future__ import annotations
+
+
+import numpy as np
+
+__all__ = [
+    "magnitude_key", "bf16_to_f64", "select_keep", "sparsify", "pack_mask", "compress",
+    "pack_meta_2bit", "unpack_meta_2bit", "decompress", "slide_windows",
+    "slide_lower", "slide_scatter_back", "lift", "column_sq_norms", "hybrid_columns",
+    "hybrid_pack", "gemm", "spmm_act", "spmm_slide", "hybrid_gemm", "fp8_e4m3_to_f64",
+    "spmm_act_fp8", "lowered_k",
+]
+
+
+# ----------------------------------------------------------------------------- bf16 ---
+
+def magnitude_key(bits: np.ndarray) -> np.ndarray:
+    """Magnitude order key of a bf16 bit pattern: the 15 bits below the sign.
+    [FLEX] 2.A: the ACT score is the absolute value of the activation."""
+    return (np.asarray(bits, dtype=np.uint16) & np.uint16(0x7FFF)).astype(np.int32)
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> fp64 values (exact)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------- select ---
+
+def _groups(bits: np.ndarray, m: int) -> np.ndarray:
+    r, k = bits.shape
+    if k % m:
+        raise ValueError("K must be a multiple of m")
+    return bits.reshape(r, k // m, m)
+
+
+def select_keep(bits: np.ndarray, n: int, m: int, row_chunk: int = 256) -> np.ndarray:
+    """Boolean keep mask of the per-group magnitude top-n.  [FLEX] 2.A, 2.C.
+
+    In every group of m contiguous values along K, position i has
+        rank_i = #{j : key_j > key_i} + #{j < i : key_j == key_i}
+    and is kept iff rank_i < n (largest magnitudes first, ties to the lower index).
+    """
+    bits = np.asarray(bits, dtype=np.uint16)
+    if not (1 <= n <= m):
+        raise ValueError("need 1 <= n <= m")
+    r, k = bits.shape
+    keep = np.empty((r, k), dtype=bool)
+    lower = np.tril(np.ones((m, m), dtype=bool), k=-1)   # lower[i, j] = (j < i)
+    for r0 in range(0, r, row_chunk):
+        key = magnitude_key(_groups(bits[r0:r0 + row_chunk], m))   # [R, G, m]
+        ki = key[..., :, None]                                     # key_i
+        kj = key[..., None, :]                                     # key_j
+        rank = (kj > ki).sum(-1) + ((kj == ki) & lower).sum(-1)
+        keep[r0:r0 + row_chunk] = (rank < n).reshape(-1, k)
+    return keep
+
+
+def sparsify(bits: np.ndarray, n: int, m: int):
+    """S(X): kept values copied bit for bit, pruned values +0.0.  Returns (S bits, keep)."""
+    keep = select_keep(bits, n, m)
+    return np.where(keep, bits, np.uint16(0)).astype(np.uint16), keep
+
+
+def pack_mask(keep: np.ndarray) -> np.ndarray:
+    """Bitmask words: word [r][k // 32], bit (k % 32) set iff position k is kept."""
+    r, k = keep.shape
+    words = (k + 31) // 32
+    out = np.zeros((r, words), dtype=np.uint32)
+    for kk in range(k):
+        out[:, kk // 32] |= keep[:, kk].astype(np.uint32) << np.uint32(kk % 32)
+    return out
+
+
+def compress(bits: np.ndarray, n: int, m: int):
+    """Compressed form: values [R][K*n/m] (kept values of each group in ascending
+    position) and idx [R][K*n/m] uint8 (their in-group positions).  [FLEX] section 1
+    (values plus index metadata)."""
+    keep = select_keep(bits, n, m)
+    r, k = bits.shape
+    g = k // m
+    pos = np.broadcast_to(np.arange(m), (r, g, m))
+    kg = keep.reshape(r, g, m)
+    # each group holds exactly n kept positions; boolean indexing keeps ascending order
+    idx = pos[kg].reshape(r, g * n).astype(np.uint8)
+    vals = bits.reshape(r, g, m)[kg].reshape(r, g * n).astype(np.uint16)
+    return vals, idx
+
+
+def pack_meta_2bit(idx: np.ndarray) -> np.ndarray:
+    """2:4 metadata, two bits per kept value: slot j -> byte j // 4, bits 2*(j % 4)."""
+    r, s = idx.shape
+    out = np.zeros((r, (s + 3) // 4), dtype=np.uint8)
+    for j in range(s):
+        if np.any(idx[:, j] > 3):
+            raise ValueError("2-bit metadata needs positions < 4")
+        out[:, j // 4] |= (idx[:, j].astype(np.uint8) << np.uint8(2 * (j % 4)))
+    return out
+
+
+def unpack_meta_2bit(meta: np.ndarray, slots: int) -> np.ndarray:
+    r = meta.shape[0]
+    out = np.zeros((r, slots), dtype=np.uint8)
+    for j in range(slots):
+        out[:, j] = (meta[:, j // 4] >> np.uint8(2 * (j % 4))) & np.uint8(3)
+    return out
+
+
+def decompress(vals: np.ndarray, idx: np.ndarray, n: int, m: int, k: int) -> np.ndarray:
+    """Inverse of compress: scatter value slot (g, i) to position g*m + idx, +0.0 elsewhere."""
+    r = vals.shape[0]
+    g = k // m
+    out = np.zeros((r, k), dtype=np.uint16)
+    v = vals.reshape(r, g, n)
+    ix = idx.reshape(r, g, n).astype(np.int64)
+    base = (np.arange(g) * m)[None, :, None]
+    rows = np.arange(r)[:, None, None]
+    out[np.broadcast_to(rows, ix.shape), base + ix] = v
+    return out
+
+
+# ---------------------------------------------------------------------- slide (6:8) ---
+
+def lowered_k(k: int, ns: int) -> int:
+    """K' = K * (2N-2)/N: each group of 2N positions becomes N-1 windows of 4.
+    [SLIDE] 2.A (expansion factor gamma)."""
+    if k % (2 * ns):
+        raise ValueError("K must be a multiple of 2N")
+    return (k // (2 * ns)) * 4 * (ns - 1)
+
+
+def slide_windows(kept_positions, ns: int):
+    """Assign the kept positions of one group of 2N to the N-1 windows
+    (window w covers positions 2w .. 2w+3).  Returns a list of per-window position lists.
+    [SLIDE] 2.A: visit kept positions in ascending order, each to the lowest covering
+    window still holding fewer than two; overflow moves to the next window."""
+    windows = [[] for _ in range(ns - 1)]
+    for p in sorted(kept_positions):
+        placed = False
+        for w in range(ns - 1):
+            if 2 * w <= p <= 2 * w + 3 and len(windows[w]) < 2:
+                windows[w].append(p)
+                placed = True
+                break
+        if not placed:
+            raise ValueError(f"position {p} cannot be placed: not a (2N-2):2N group")
+    return windows
+
+
+def slide_lower(vals: np.ndarray, idx: np.ndarray, k: int, ns: int):
+    """Offline packer: a (2N-2):2N matrix given as (values, u8 idx) -> the lowered 2:4
+    matrix over K' (values [R][K'/2], idx [R][K'/2] with in-window slots 0..3).
+    [SLIDE] 2.A, 2.C.  Window w of group g holds lowered positions g*4(N-1)+4w+s."""
+    n = 2 * ns - 2
+    m = 2 * ns
+    r = vals.shape[0]
+    g_count = k // m
+    kp = lowered_k(k, ns)
+    out_v = np.zeros((r, kp // 2), dtype=np.uint16)
+    out_i = np.zeros((r, kp // 2), dtype=np.uint8)
+    for row in range(r):
+        for g in range(g_count):
+            pos = [int(p) for p in idx[row, g * n:(g + 1) * n]]
+            val = [vals[row, g * n + j] for j in range(n)]
+            byp = dict(zip(pos, val))
+            wins = slide_windows(pos, ns)
+            for w, plist in enumerate(wins):
+                if len(plist) != 2:
+                    raise ValueError("window not filled with exactly two")
+                for j, p in enumerate(plist):      # ascending in-window slot order
+                    slot = (g * (ns - 1) + w) * 2 + j
+                    out_v[row, slot] = byp[p]
+                    out_i[row, slot] = p - 2 * w
+    return out_v, out_i
+
+
+def slide_scatter_back(vals_p: np.ndarray, idx_p: np.ndarray, k: int, ns: int) -> np.ndarray:
+    """Sum the windows back onto the original 2N positions (dense bf16 bits [R][K]).
+    Each original position receives at most one window entry."""
+    r = vals_p.shape[0]
+    out = np.zeros((r, k), dtype=np.uint16)
+    filled = np.zeros((r, k), dtype=bool)
+    wcount = (k // (2 * ns)) * (ns - 1)
+    for row in range(r):
+        for wi in range(wcount):
+            g, w = divmod(wi, ns - 1)
+            for j in range(2):
+                slot = wi * 2 + j
+                p = g * 2 * ns + 2 * w + int(idx_p[row, slot])
+                if filled[row, p]:
+                    raise ValueError("two windows claim one position")
+                filled[row, p] = True
+                out[row, p] = vals_p[row, slot]
+    return out
+
+
+def lift(x_bits: np.ndarray, ns: int) -> np.ndarray:
+    """Activation lifting: X'[t][g*4(N-1) + 4w + s] = X[t][g*2N + 2w + s].  [SLIDE] 2.B."""
+    t, k = x_bits.shape
+    kp = lowered_k(k, ns)
+    out = np.empty((t, kp), dtype=np.uint16)
+    for kk in range(kp):
+        g, rem = divmod(kk, 4 * (ns - 1))
+        w, s = divmod(rem, 4)
+        out[:, kk] = x_bits[:, g * 2 * ns + 2 * w + s]
+    return out
+
+
+# -------------------------------------------------------------------------- hybrid ---
+
+def column_sq_norms(w_bits: np.ndarray) -> np.ndarray:
+    """c_k = sum over o (ascending) of W[o][k]^2 in fp64 (squares of bf16 are exact)."""
+    w = bf16_to_f64(w_bits)
+    c = np.zeros(w.shape[1], dtype=np.float64)
+    for o in range(w.shape[0]):
+        c = c + w[o] * w[o]
+    return c
+
+
+def hybrid_columns(w_bits: np.ndarray, k_dense: int):
+    """[SPENSE] 2.A/2.B: choose the dense columns (largest L2 norm, ties to the lower
+    column) and order the sparse region first, dense region second, each ascending."""
+    c = column_sq_norms(w_bits)
+    k = c.shape[0]
+    order = sorted(range(k), key=lambda j: (-c[j], j))
+    dense = np.array(sorted(order[:k_dense]), dtype=np.int32)
+    is_dense = np.zeros(k, dtype=bool)
+    is_dense[dense] = True
+    sparse = np.array([j for j in range(k) if not is_dense[j]], dtype=np.int32)
+    return sparse, dense
+
+
+def hybrid_pack(w_bits: np.ndarray, k_dense: int):
+    """Offline hybrid packing: (sparse_cols, dense_cols, W_s values, W_s idx, W_d)."""
+    sparse, dense = hybrid_columns(w_bits, k_dense)
+    ws = np.ascontiguousarray(w_bits[:, sparse])
+    wd = np.ascontiguousarray(w_bits[:, dense])
+    if ws.shape[1]:
+        v, i = compress(ws, 2, 4)
+    else:
+        v = np.zeros((w_bits.shape[0], 0), np.uint16)
+        i = np.zeros((w_bits.shape[0], 0), np.uint8)
+    return sparse, dense, v, i, wd
+
+
+# ---------------------------------------------------------------------------- GEMM ---
+
+def gemm(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    """Y[t][o] = sum_k a[t][k] * b[o][k] in fp64 (library matrix product)."""
+    return bf16_to_f64(a_bits) @ bf16_to_f64(b_bits).T
+
+
+def spmm_act(x_bits: np.ndarray, w_bits: np.ndarray, n: int, m: int) -> np.ndarray:
+    """Activation-sparse layer Y = S(X) . W^T.  [FLEX] 2.A, 2.C."""
+    s, _ = sparsify(x_bits, n, m)
+    return gemm(s, w_bits)
+
+
+def spmm_slide(x_bits: np.ndarray, vals_p: np.ndarray, idx_p: np.ndarray, ns: int) -> np.ndarray:
+    """Lowered weight-sparse layer Y = lift(X) . W'^T.  [SLIDE] 2.A-2.C."""
+    k = x_bits.shape[1]
+    kp = lowered_k(k, ns)
+    wp = decompress(vals_p, idx_p, 2, 4, kp)
+    return gemm(lift(x_bits, ns), wp)
+
+
+def hybrid_gemm(x_bits, sparse_cols, dense_cols, ws_vals, ws_idx, wd_bits) -> np.ndarray:
+    """[SPENSE] 2.A input split: Y = X_s . W_s^T + X_d . W_d^T, where X_s / X_d are the
+    columns of X in the sparse / dense region order and W_s is 2:4 compressed."""
+    ks = len(sparse_cols)
+    y = np.zeros((x_bits.shape[0], wd_bits.shape[0] if wd_bits.size else ws_vals.shape[0]))
+    if ks:
+        ws = decompress(ws_vals, ws_idx, 2, 4, ks)
+        y = y + gemm(np.ascontiguousarray(x_bits[:, sparse_cols]), ws)
+    if len(dense_cols):
+        y = y + gemm(np.ascontiguousarray(x_bits[:, dense_cols]), wd_bits)
+    return y
+
+
+# ----------------------------------------------------------------------------- fp8 ---
+
+def fp8_e4m3_to_f64(q: np.ndarray) -> np.ndarray:
+    """OCP E4M3FN decode: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent 0 is
+    subnormal (m * 2^-9); S.1111.111 is NaN; there is no infinity."""
+    q = np.asarray(q, dtype=np.uint8).astype(np.int64)
+    s = np.where(q >> 7, -1.0, 1.0)
+    e = (q >> 3) & 15
+    mant = q & 7
+    normal = s * np.ldexp(1.0 + mant / 8.0, e - 7)
+    sub = s * mant * 2.0 ** -9
+    out = np.where(e == 0, sub, normal)
+    return np.where((e == 15) & (mant == 7), np.nan, out)
+
+
+def spmm_act_fp8(x_bits: np.ndarray, w8: np.ndarray, scale: np.ndarray, n: int, m: int) -> np.ndarray:
+    """Y[t][o] = scale[o] * sum_k S(X)[t][k] * dec(W8[o][k]); scale applied after the sum."""
+    s, _ = sparsify(x_bits, n, m)
+    acc = bf16_to_f64(s) @ fp8_e4m3_to_f64(w8).T
+    return acc * np.asarray(scale, dtype=np.float64)[None, :]

@@ -1,0 +1,389 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+the pages' printed figures, hand-worked examples, brute force over tiny inputs,
+exact rational arithmetic, closed forms and an independent library (torch's fp8)."""
+import json
+import math
+import os
+import struct
+from fractions import Fraction
+from itertools import combinations, product
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def bits_of(v):
+    """Python float / "-0" -> bf16 bits (values in the fixtures are exact in bf16)."""
+    if v == "-0":
+        return 0x8000
+    return struct.unpack("<I", struct.pack("<f", float(v)))[0] >> 16
+
+
+def value_of(b):
+    return struct.unpack("<f", struct.pack("<I", int(b) << 16))[0]
+
+
+def arr(rows):
+    return np.array([[bits_of(v) for v in r] for r in rows], dtype=np.uint16)
+
+
+# ------------------------------------------------------------------ brute force ---
+
+def brute_keep(group_vals, n):
+    """Independent definition: among all n-subsets (lexicographic order) take the first
+    one with the largest sum of |x|.  Equals top-n by magnitude with ties to the lower
+    index (the lexicographically smallest tuple takes the lowest-index ties)."""
+    best, best_sum = None, None
+    for comb in combinations(range(len(group_vals)), n):
+        s = sum(abs(Fraction(group_vals[i])) for i in comb)
+        if best_sum is None or s > best_sum:
+            best, best_sum = comb, s
+    keep = [False] * len(group_vals)
+    for i in best:
+        keep[i] = True
+    return keep
+
+
+ALPHABET = [0x0000, 0x8000, 0x3F00, 0xBF00, 0x3F80, 0xBF80, 0x4000, 0xC000]  # 0,-0,.5,-.5,1,-1,2,-2
+
+
+def test_select_bruteforce_all_2of4_alphabet_groups():
+    groups = np.array(list(product(ALPHABET, repeat=4)), dtype=np.uint16)   # 4096 groups
+    vals = [[value_of(b) for b in g] for g in groups]
+    for n in range(1, 5):
+        keep = O.select_keep(groups, n, 4)
+        for gi in range(len(groups)):
+            assert list(keep[gi]) == brute_keep(vals[gi], n), (n, groups[gi])
+
+
+def test_select_bruteforce_m8_three_magnitudes():
+    mags = [0x0000, 0x3F80, 0x4000]      # 0, 1, 2 -> many ties
+    rng = np.random.default_rng(11)
+    groups = np.array(list(product(mags, repeat=8)), dtype=np.uint16)        # 6561 groups
+    signs = rng.integers(0, 2, size=groups.shape).astype(np.uint16) << np.uint16(15)
+    groups = groups | signs
+    vals = [[value_of(b) for b in g] for g in groups]
+    for n in (1, 3, 4, 6, 7):
+        keep = O.select_keep(groups, n, 8)
+        for gi in range(0, len(groups), 3):
+            assert list(keep[gi]) == brute_keep(vals[gi], n)
+
+
+def test_select_bruteforce_m16_random_ties():
+    rng = np.random.default_rng(12)
+    g = rng.choice(np.array(ALPHABET, dtype=np.uint16), size=(12, 16))
+    vals = [[value_of(b) for b in row] for row in g]
+    for n in (4, 8, 12):
+        keep = O.select_keep(g, n, 16)
+        for gi in range(len(g)):
+            assert list(keep[gi]) == brute_keep(vals[gi], n)
+
+
+def _certificate(vals_bits, keep_row, n):
+    """Exchange certificate: exactly n kept and every kept i precedes every pruned j in
+    the order (|x| descending, index ascending)."""
+    mags = [abs(value_of(b)) if not math.isnan(value_of(b)) else math.inf for b in vals_bits]
+    kept = [i for i, k in enumerate(keep_row) if k]
+    pruned = [j for j, k in enumerate(keep_row) if not k]
+    assert len(kept) == n
+    for i in kept:
+        for j in pruned:
+            assert mags[i] > mags[j] or (mags[i] == mags[j] and i < j)
+
+
+def test_select_certificate_m32_and_all_n():
+    rng = np.random.default_rng(13)
+    x = synth.student_t_bf16(rng, (6, 32 * 8), 4.0, 0.5)
+    x[0, :32] = 0x3F80                   # a fully tied group
+    x[1, 32:64] = rng.choice(np.array(ALPHABET, np.uint16), size=32)
+    for m in (4, 8, 16, 32):
+        for n in sorted({1, m // 4 or 1, m // 2, m - 1, m}):
+            keep = O.select_keep(x, n, m)
+            for r in range(x.shape[0]):
+                for g in range(x.shape[1] // m):
+                    _certificate(x[r, g * m:(g + 1) * m], keep[r, g * m:(g + 1) * m], n)
+
+
+def test_select_special_values():
+    # subnormal < smallest normal; inf beats finite; NaN ranks above inf (policy); +0 == -0
+    sub, norm, inf, nan = 0x0001, 0x0080, 0x7F80, 0x7FC0
+    g = np.array([[sub, norm, 0x8000, 0x0000],
+                  [0x4000, inf | 0x8000, 0x3F80, 0x0000],
+                  [inf, 0x3F80, nan, 0x4000],
+                  [0x8000, 0x0000, 0x8000, 0x0000]], dtype=np.uint16)
+    keep = O.select_keep(g, 2, 4)
+    assert keep.tolist() == [[True, True, False, False],
+                             [True, True, False, False],
+                             [True, False, True, False],
+                             [True, True, False, False]]
+
+
+# ------------------------------------------------------------- page figures ---
+
+def test_page_configuration_counts(golden_dir):
+    fig = json.load(open(os.path.join(golden_dir, "page_figures.json")))
+    for (n, m), key in [((2, 4), "configs_2of4"), ((8, 16), "configs_8of16")]:
+        subsets = list(combinations(range(m), n))
+        x = np.full((len(subsets), m), 0x3F80, dtype=np.uint16)        # magnitude 1
+        for r, s in enumerate(subsets):
+            x[r, list(s)] = 0x4000                                       # magnitude 2
+        keep = O.select_keep(x, n, m)
+        masks = {tuple(np.flatnonzero(row)) for row in keep}
+        assert masks == set(subsets)                                      # every mask reachable
+        assert len(masks) == fig[key]["value"] == math.comb(m, n)
+
+
+def test_page_slide_figures(golden_dir):
+    fig = json.load(open(os.path.join(golden_dir, "page_figures.json")))
+    ns = 4
+    assert ns - 1 == fig["slide_6of8_windows"]["value"]
+    assert O.lowered_k(8, ns) / 8 == fig["slide_6of8_gamma"]["value"]
+    k = 4096
+    executed = O.lowered_k(k, ns) // 2          # 2:4 hardware executes half of K'
+    assert k / executed == pytest.approx(fig["slide_6of8_speedup"]["value"], rel=1e-15)
+    assert 1 - 6 / 8 == fig["prune_frac_6of8"]["value"]
+    assert 1 - 4 / 6 == pytest.approx(fig["prune_frac_4of6"]["value"])
+
+
+# --------------------------------------------------------- hand-worked fixtures ---
+
+def test_select_handworked(golden_dir):
+    cases = json.load(open(os.path.join(golden_dir, "select_handworked.json")))["cases"]
+    for c in cases:
+        n, m = c["n"], c["m"]
+        x = arr(c["x"])
+        s, keep = O.sparsify(x, n, m)
+        assert s.tolist() == arr(c["s"]).tolist()
+        v, i = O.compress(x, n, m)
+        assert v.tolist() == arr(c["values"]).tolist()
+        assert i.tolist() == c["idx"]
+        assert O.pack_mask(keep).tolist() == c["mask"]
+        if "meta2bit" in c:
+            assert O.pack_meta_2bit(i).tolist() == c["meta2bit"]
+
+
+def test_slide_handworked(golden_dir):
+    fx = json.load(open(os.path.join(golden_dir, "slide_handworked.json")))
+    ns = fx["ns"]
+    for c in fx["cases"]:
+        wins = O.slide_windows(c["kept"], ns)
+        assert wins == c["windows"]
+        slots = [[p - 2 * w for p in pl] for w, pl in enumerate(wins)]
+        assert slots == c["slots"]
+        # through slide_lower on a one-group row with distinct values
+        vals = np.array([[0x3F80 + 0x80 * j for j in range(6)]], dtype=np.uint16)
+        idx = np.array([c["kept"]], dtype=np.uint8)
+        vp, ip = O.slide_lower(vals, idx, 8, ns)
+        assert ip.reshape(-1).tolist() == [s for sl in c["slots"] for s in sl]
+        order = {p: j for j, p in enumerate(c["kept"])}
+        assert vp.reshape(-1).tolist() == [int(vals[0, order[p]]) for pl in c["windows"] for p in pl]
+
+
+# ------------------------------------------------------------------ invariants ---
+
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8), (8, 16), (16, 32), (1, 4), (3, 8), (5, 16), (31, 32)])
+def test_invariants(n, m):
+    rng = np.random.default_rng(n * 100 + m)
+    x = synth.student_t_bf16(rng, (7, m * 6), 4.0, 1.0)
+    x[0, :m] = 0x8000                                  # -0 group
+    x[1, :m] = 0x3F80                                  # all ties
+    s, keep = O.sparsify(x, n, m)
+    assert (keep.reshape(7, -1, m).sum(-1) == n).all()          # exactly n per group
+    v, i = O.compress(x, n, m)
+    assert (np.diff(i.reshape(7, -1, n).astype(int), axis=-1) > 0).all()   # ascending
+    assert (i < m).all()
+    assert (O.decompress(v, i, n, m, x.shape[1]) == s).all()     # round trip = S(X)
+    # mask <-> idx bijection
+    g = np.arange(x.shape[1] // m)
+    pos = (g[None, :, None] * m + i.reshape(7, -1, n).astype(int)).reshape(7, -1)
+    rebuilt = np.zeros_like(keep)
+    np.put_along_axis(rebuilt, pos, True, axis=1)
+    assert (rebuilt == keep).all()
+    words = O.pack_mask(keep)
+    pop = sum(bin(int(w)).count("1") for w in words.reshape(-1))
+    assert pop == keep.sum()
+    # values are x at idx
+    assert (np.take_along_axis(x, pos, 1) == v).all()
+    # compress(decompress(v, i)) == (v, i) when no kept value is +-0
+    nz = (v & 0x7FFF) != 0
+    rows = np.flatnonzero(nz.all(1))
+    if len(rows):
+        v2, i2 = O.compress(O.decompress(v[rows], i[rows], n, m, x.shape[1]), n, m)
+        assert (v2 == v[rows]).all() and (i2 == i[rows]).all()
+
+
+def test_n_equals_m_is_identity_and_dense_gemm():
+    rng = np.random.default_rng(3)
+    x = synth.normal_bf16(rng, (5, 64))
+    w = synth.normal_bf16(rng, (9, 64), 0.02)
+    for m in (4, 8, 16, 32):
+        s, keep = O.sparsify(x, m, m)
+        assert keep.all() and (s == x).all()
+        assert (O.spmm_act(x, w, m, m) == O.gemm(x, w)).all()
+
+
+def test_meta_2bit_roundtrip():
+    rng = np.random.default_rng(4)
+    x = synth.normal_bf16(rng, (6, 4 * 9))
+    v, i = O.compress(x, 2, 4)
+    meta = O.pack_meta_2bit(i)
+    assert meta.shape == (6, (i.shape[1] + 3) // 4)
+    assert (O.unpack_meta_2bit(meta, i.shape[1]) == i).all()
+
+
+# ------------------------------------------------------------------ GEMM exactness ---
+
+def test_gemm_against_exact_rationals():
+    rng = np.random.default_rng(5)
+    a = synth.student_t_bf16(rng, (3, 48), 4.0, 1.0)
+    b = synth.normal_bf16(rng, (4, 48), 0.02)
+    y = O.gemm(a, b)
+    for t in range(3):
+        for o in range(4):
+            exact = sum(Fraction(value_of(a[t, k])) * Fraction(value_of(b[o, k])) for k in range(48))
+            absum = sum(abs(value_of(a[t, k]) * value_of(b[o, k])) for k in range(48))
+            assert abs(Fraction(y[t, o]) - exact) <= Fraction(48 * 2.0 ** -53 * absum * 1.01)
+
+
+def test_spmm_act_matches_masked_rational_product():
+    rng = np.random.default_rng(6)
+    x = synth.student_t_bf16(rng, (2, 32), 4.0, 0.5)
+    w = synth.normal_bf16(rng, (3, 32), 0.02)
+    y = O.spmm_act(x, w, 8, 16)
+    for t in range(2):
+        xv = [value_of(b) for b in x[t]]
+        keep = brute_keep(xv[:16], 8) + brute_keep(xv[16:], 8)
+        for o in range(3):
+            exact = sum(Fraction(xv[k]) * Fraction(value_of(w[o, k])) for k in range(32) if keep[k])
+            assert abs(Fraction(y[t, o]) - exact) <= Fraction(1e-15)
+
+
+# ------------------------------------------------------------------------- slide ---
+
+@pytest.mark.parametrize("ns", [2, 3, 4, 5, 6])
+def test_slide_exhaustive_masks(ns):
+    m = 2 * ns
+    n = 2 * ns - 2
+    count = 0
+    for kept in combinations(range(m), n):
+        wins = O.slide_windows(list(kept), ns)
+        assert all(len(w) == 2 for w in wins)
+        for w, pl in enumerate(wins):
+            assert all(2 * w <= p <= 2 * w + 3 for p in pl)
+        assert sorted(p for pl in wins for p in pl) == list(kept)
+        count += 1
+    assert count == math.comb(m, n)
+    # N-2 windows hold at most 2N-4 < 2N-2 values: never enough
+    assert 2 * (ns - 2) < n
+    assert O.lowered_k(m, ns) == 4 * (ns - 1)
+
+
+def test_slide_pipeline_reconstructs_and_multiplies():
+    rng = np.random.default_rng(7)
+    ns = 4
+    w = synth.normal_bf16(rng, (6, 64), 0.02)
+    w[0, :8] = 0x3F80                                  # fully tied group
+    x = synth.normal_bf16(rng, (5, 64))
+    v, i = O.compress(w, 6, 8)
+    vp, ip = O.slide_lower(v, i, 64, ns)
+    assert vp.shape == (6, O.lowered_k(64, ns) // 2)
+    pruned, _ = O.sparsify(w, 6, 8)
+    assert (O.slide_scatter_back(vp, ip, 64, ns) == pruned).all()
+    y_slide = O.spmm_slide(x, vp, ip, ns)
+    xl = O.lift(x, ns)
+    for t in range(5):
+        for o in range(6):
+            wd = O.decompress(vp[o:o + 1], ip[o:o + 1], 2, 4, O.lowered_k(64, ns))[0]
+            exact_lifted = sum(Fraction(value_of(xl[t, k])) * Fraction(value_of(wd[k])) for k in range(len(wd)))
+            exact_dense = sum(Fraction(value_of(x[t, k])) * Fraction(value_of(pruned[o, k])) for k in range(64))
+            assert exact_lifted == exact_dense
+            assert abs(Fraction(y_slide[t, o]) - exact_dense) <= Fraction(1e-15)
+
+
+def test_lift_positions():
+    x = np.arange(16, dtype=np.uint16)[None, :]
+    xl = O.lift(x, 4)
+    assert xl[0].tolist() == [0, 1, 2, 3, 2, 3, 4, 5, 4, 5, 6, 7, 8, 9, 10, 11, 10, 11, 12, 13, 12, 13, 14, 15]
+
+
+# ------------------------------------------------------------------------ hybrid ---
+
+def test_hybrid_column_choice_constructed():
+    rng = np.random.default_rng(8)
+    o, k, kd = 16, 32, 8
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    big = [3, 5, 17, 18, 20, 26, 30, 31]
+    for c in big:
+        w[:, c] = synth.bf16_bits_from_f32(synth.f32_from_bf16_bits(w[:, c]) * np.float32(64.0))
+    sp, de = O.hybrid_columns(w, kd)
+    assert de.tolist() == big
+    assert sp.tolist() == [c for c in range(k) if c not in big]
+    # norm ties resolve to the lower column
+    w2 = np.full((4, 8), 0x3F80, dtype=np.uint16)
+    sp2, de2 = O.hybrid_columns(w2, 3)
+    assert de2.tolist() == [0, 1, 2]
+
+
+def test_hybrid_norms_exact():
+    rng = np.random.default_rng(9)
+    w = synth.normal_bf16(rng, (40, 6), 0.02)
+    c = O.column_sq_norms(w)
+    for j in range(6):
+        exact = sum(Fraction(value_of(w[o, j])) ** 2 for o in range(40))
+        assert abs(Fraction(c[j]) - exact) <= exact * Fraction(2.0 ** -50)
+
+
+@pytest.mark.parametrize("kd", [0, 8, 32])
+def test_hybrid_split_sum(kd):
+    rng = np.random.default_rng(10 + kd)
+    o, k = 12, 32
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    x = synth.normal_bf16(rng, (5, k))
+    sp, de, v, i, wd = O.hybrid_pack(w, kd)
+    assert len(sp) + len(de) == k and len(de) == kd
+    y = O.hybrid_gemm(x, sp, de, v, i, wd)
+    # W_h: sparse columns replaced by their 2:4 pruned values scattered back
+    wh = w.copy()
+    if len(sp):
+        ws_pruned = O.decompress(v, i, 2, 4, len(sp))
+        wh[:, sp] = ws_pruned
+        # the sparse region is exactly the 2:4 magnitude pruning of the permuted columns
+        assert (ws_pruned == O.sparsify(np.ascontiguousarray(w[:, sp]), 2, 4)[0]).all()
+    assert np.allclose(y, O.gemm(x, wh), rtol=1e-12, atol=1e-15)
+    if kd == k:
+        assert np.allclose(y, O.gemm(x, w), rtol=1e-12, atol=1e-15)
+    if kd == 0:
+        assert (sp == np.arange(k)).all()
+        assert np.allclose(y, O.spmm_act(w, x, 2, 4).T, rtol=1e-12, atol=1e-15)
+
+
+# --------------------------------------------------------------------------- fp8 ---
+
+def test_fp8_decode_all_codes_vs_torch():
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ours = O.fp8_e4m3_to_f64(codes)
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float32).numpy().astype(np.float64)
+    nan = np.isnan(ref)
+    assert (np.isnan(ours) == nan).all() and nan.sum() == 2
+    assert (ours[~nan] == ref[~nan]).all()
+    assert np.nanmax(ours) == 448.0
+    # every finite code is exactly representable in bf16
+    b = synth.bf16_bits_from_f32(ours[~nan].astype(np.float32))
+    assert (synth.f32_from_bf16_bits(b).astype(np.float64) == ours[~nan]).all()
+
+
+def test_fp8_layer_equals_scaled_bf16_layer():
+    rng = np.random.default_rng(14)
+    w = synth.normal_bf16(rng, (6, 64), 0.02)
+    x = synth.student_t_bf16(rng, (4, 64), 4.0, 1.0)
+    q, s = synth.fp8_e4m3_quantize_rows(w)
+    y8 = O.spmm_act_fp8(x, q, s, 8, 16)
+    wdeq = O.fp8_e4m3_to_f64(q) * s[:, None].astype(np.float64)
+    sx, _ = O.sparsify(x, 8, 16)
+    assert np.allclose(y8, O.bf16_to_f64(sx) @ wdeq.T, rtol=1e-12, atol=1e-14)
