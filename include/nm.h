@@ -1,0 +1,232 @@
+/*
+ * nm.h -- C ABI of libnmsparse: N:M structured-sparse linear layers on AMD MI355X (gfx950).
+ *
+ * The library computes Y = S(X) . W^T where S keeps, in every group of m contiguous
+ * values along the reduction dimension K, the n values of largest magnitude (ties to
+ * the lower index), and the sparse operand is contracted in compressed form (values
+ * plus index metadata).  Sources, by page title and section:
+ *   [FLEX]   "Motivating Next-Gen Accelerators with Flexible (N:M) Activation Sparsity
+ *            via Benchmarking Lightweight Post-Training Sparsification Approaches",
+ *            technical summary sections 1, 2.A (ACT: activation magnitude), 2.C (patterns).
+ *   [SLIDE]  "SlideSparse: Fast and Flexible (2N-2):2N Structured Sparsity",
+ *            technical summary sections 2.A (sliding windows), 2.B (activation lifting),
+ *            2.C (packer, load-time compression, online kernel).
+ *   [SPENSE] "SpenseGPT: Practical One-shot Pruning Enabling Sparse and Dense GEMMs for
+ *            LLM Inference", technical summary sections 2.A (dense + 2:4 regions,
+ *            input split with accumulation) and 2.B (dense indices permuted contiguous).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensor pointers are DEVICE pointers owned by the caller.  The library never
+ *    allocates, frees or keeps a pointer past the call.
+ *  - bf16 tensors are 16-bit bf16 bit patterns; row-major with an explicit leading
+ *    dimension in ELEMENTS (ld >= K).  Compressed arrays are dense row-major with no
+ *    padding: values [rows][K*n/m] (bf16), U8 metadata [rows][K*n/m] (one byte per kept
+ *    value = its in-group position 0..m-1, kept values in ascending position), 2-bit
+ *    metadata [rows][ceil(K/8)] bytes (2:4 only; kept slot j of a row -> byte j/4,
+ *    bits 2*(j%4)..2*(j%4)+1).  Bitmasks are uint32 words [rows][ceil(K/32)], bit k%32 of
+ *    word k/32 set iff position k is kept.
+ *  - Magnitude order is the order of the low 15 bits of the bf16 pattern: |x| order for
+ *    every finite and infinite value, +0 ties -0, NaN ranks above infinity.  Pruned
+ *    outputs are +0.0; kept values are copied bit for bit.
+ *  - Every call validates its arguments on the host first and returns an nm_status.  On
+ *    NM_OK the work has been ENQUEUED on `stream` (a hipStream_t passed as void*, NULL =
+ *    the default stream); nothing is synchronised.  A device-side fault surfaces at the
+ *    caller's next synchronisation.  No call throws; all are thread-safe and stateless.
+ *  - Alignment: every device pointer must be 16-byte aligned and every bf16 leading
+ *    dimension a multiple of 8 elements (nm_sparsify / nm_compress / nm_decompress with
+ *    m = 4 accept a multiple of 4, nm_slide_lift any); fp8 weights need a leading
+ *    dimension that is a multiple of 16 bytes (NM_EALIGN otherwise).  fp32 outputs take
+ *    any leading dimension >= O.
+ *  - Supported patterns: m in {4, 8, 16, 32}, 1 <= n <= m, K % m == 0.
+ *  - Sizes are int64_t; rows, K, T, O >= 0 (zero-size calls return NM_OK and launch
+ *    nothing, except that nm_spmm / nm_hybrid_gemm with K == 0 still write Y = 0 (or
+ *    leave it unchanged when accumulating)).
+ */
+#ifndef NM_SPARSE_H
+#define NM_SPARSE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NM_OK = 0,
+  NM_EINVAL = 1,        /* null required pointer, bad enum value, n or m out of range  */
+  NM_ESHAPE = 2,        /* inconsistent sizes: K % m, ld < K, negative or overflowing  */
+  NM_EALIGN = 3,        /* pointer not 16-byte aligned or leading dimension % 8 != 0    */
+  NM_EUNSUPPORTED = 4,  /* well-formed request outside what the kernels implement       */
+  NM_EHIP = 5           /* the HIP runtime reported an error when launching            */
+} nm_status;
+
+typedef enum { NM_META_U8 = 0, NM_META_2BIT = 1 } nm_meta;
+typedef enum { NM_W_BF16 = 0, NM_W_FP8E4M3 = 1 } nm_wdtype;
+
+/* Human-readable name of a status code (static storage). */
+const char* nm_status_str(nm_status s);
+/* Library version: major*10000 + minor*100 + patch. */
+int nm_version(void);
+
+/*
+ * nm_sparsify -- S(X): per-group magnitude top-n along K.  [FLEX] 2.A (ACT score) and
+ * 2.C (N:M patterns along the reduction dimension).
+ *   x     bf16 [rows][ldx]                      input
+ *   y     bf16 [rows][ldy] or NULL              S(X): kept values copied, pruned = +0.0
+ *   mask  uint32 [rows][ceil(k/32)] or NULL     keep bitmask
+ * At least one of y, mask must be non-NULL (NM_EINVAL).  y may alias x when ldy == ldx.
+ */
+nm_status nm_sparsify(const void* x, int64_t rows, int64_t k, int64_t ldx, int n, int m,
+                      void* y, int64_t ldy, uint32_t* mask, void* stream);
+
+/*
+ * nm_compress -- select and compact in one pass, straight from the dense input.
+ * [FLEX] 1 (values plus index metadata), [SLIDE] 2.C (load-time compression).
+ *   x       bf16 [rows][ldx]
+ *   values  bf16 [rows][k*n/m]                    kept values, ascending position
+ *   meta    U8: uint8 [rows][k*n/m]; 2BIT: uint8 [rows][ceil(k/8)] (needs n == 2, m == 4)
+ *   mask    uint32 [rows][ceil(k/32)] or NULL     optional keep bitmask
+ */
+nm_status nm_compress(const void* x, int64_t rows, int64_t k, int64_t ldx, int n, int m,
+                      void* values, void* meta, nm_meta fmt, uint32_t* mask, void* stream);
+
+/*
+ * nm_decompress -- inverse of nm_compress: scatter values to their positions, +0.0
+ * elsewhere.  y bf16 [rows][ldy].  Metadata entries must be valid positions (< m,
+ * strictly ascending within a group); other metadata is a caller error with an
+ * unspecified (but in-bounds) result.
+ */
+nm_status nm_decompress(const void* values, const void* meta, nm_meta fmt, int64_t rows,
+                        int64_t k, int n, int m, void* y, int64_t ldy, void* stream);
+
+/*
+ * nm_lower_slide -- offline packer for (2N-2):2N weights.  [SLIDE] 2.A and 2.C.
+ * Input: the compressed form (values bf16 [rows][k*(2N-2)/(2N)], idx uint8 same shape,
+ * in-group positions 0..2N-1 ascending) of a matrix with exactly 2N-2 kept per group of
+ * 2N.  Output: the equivalent 2:4 matrix over K' = k*(N-1)/N*2 = k*(2N-2)/N: each group
+ * becomes N-1 overlapping windows of width 4 and stride 2 (window w covers positions
+ * 2w..2w+3); kept positions are placed in ascending order, each in the lowest covering
+ * window that holds fewer than two.  Window w of group g occupies lowered positions
+ * g*4(N-1) + 4w + s.  values_out bf16 [rows][K'/2]; meta_out U8 [rows][K'/2] (in-window
+ * slot 0..3) or 2BIT [rows][ceil(K'/8)].  Requires k % (2N) == 0 and 2 <= N <= 8.
+ * Input that is not (2N-2):2N (a window overflow) is a caller error: the affected
+ * group's output is unspecified but every access stays in bounds.
+ */
+nm_status nm_lower_slide(const void* values, const uint8_t* idx, int64_t rows, int64_t k,
+                         int ns, void* values_out, void* meta_out, nm_meta fmt, void* stream);
+
+/*
+ * nm_slide_lift -- explicit activation lifting, X' [t][ldo] over K' = k*(2N-2)/N:
+ * X'[t][g*4(N-1) + 4w + s] = X[t][g*2N + 2w + s].  [SLIDE] 2.B.  nm_spmm performs the
+ * same lifting inside its operand loader; this call exists for inspection and tests.
+ */
+nm_status nm_slide_lift(const void* x, int64_t t, int64_t k, int64_t ldx, int ns,
+                        void* x_out, int64_t ldo, void* stream);
+
+/* Operating modes of nm_spmm. */
+typedef enum {
+  NM_ACT_DYNAMIC = 0,    /* X dense; select n:m of X inside the call, then contract     */
+  NM_ACT_COMPRESSED = 1, /* X given compressed (values + meta from nm_compress)          */
+  NM_W_COMPRESSED = 2,   /* W given as 2:4 compressed (values + meta); X dense           */
+  NM_W_SLIDE = 3         /* W given lowered by nm_lower_slide (2:4 over K'); X lifted on
+                            the fly inside the operand loader                            */
+} nm_spmm_mode;
+
+/*
+ * Arguments of nm_spmm.  Y[t][o] (fp32, row stride ldy) = sum_k A[t][k] * B[o][k] with
+ *   ACT_DYNAMIC:    A = S_{n:m}(x),         B = w (bf16 [o][ldw] or fp8 [o][ldw] bytes)
+ *   ACT_COMPRESSED: A = decompress(x, x_meta) (x = values [t][k*n/m]), B = w as above
+ *   W_COMPRESSED:   A = x (bf16 [t][ldx]),  B = decompress(w, w_meta), 2:4 over k
+ *   W_SLIDE:        A = lift_ns(x),          B = decompress(w, w_meta), 2:4 over
+ *                   K' = k*(2ns-2)/ns  (equals x . Wpruned^T)
+ * then, when w_scale != NULL (fp8 weights), Y[t][o] *= w_scale[o]; finally Y = result
+ * (accumulate == 0) or Y += result (accumulate == 1).
+ * Optional fields (may be NULL / 0):
+ *   x_mask_out  ACT_DYNAMIC only: receives the selection bitmask of x [t][ceil(k/32)]
+ *   w_kmajor    ACT_DYNAMIC, bf16 W only: the same weights stored K-major [k][o]
+ *               (row stride o); used for single-token calls, which then read only the
+ *               selected K-rows of W.
+ *   workspace   device scratch; with workspace_bytes >= nm_spmm_workspace_size(args)
+ *               ACT_DYNAMIC may run select and product as two passes.  Calls sharing a
+ *               workspace must be ordered (same stream).
+ */
+typedef struct {
+  int mode;               /* nm_spmm_mode                                          */
+  int n, m;               /* activation pattern (ACT_*); ignored for W_* modes     */
+  int ns;                 /* N of the (2N-2):2N family (W_SLIDE only)              */
+  int64_t t, o, k;        /* tokens, output features, ORIGINAL reduction length    */
+  const void* x;          /* see mode                                              */
+  int64_t ldx;            /* elements; ignored for ACT_COMPRESSED                  */
+  const void* x_meta;     /* ACT_COMPRESSED metadata                               */
+  int x_meta_fmt;         /* nm_meta                                               */
+  const void* w;          /* see mode                                              */
+  int64_t ldw;            /* elements (bf16) or bytes (fp8); ignored for W_* modes */
+  int w_dtype;            /* nm_wdtype (ACT_* modes)                               */
+  const void* w_meta;     /* W_* metadata                                          */
+  int w_meta_fmt;         /* nm_meta                                               */
+  const float* w_scale;   /* fp32 [o] per-row scale (required for fp8, else NULL)  */
+  const void* w_kmajor;   /* optional, see above                                   */
+  float* y;               /* fp32 [t][ldy]                                         */
+  int64_t ldy;
+  int accumulate;         /* 0: Y = result, 1: Y += result                         */
+  uint32_t* x_mask_out;   /* optional                                              */
+  void* workspace;        /* optional                                              */
+  int64_t workspace_bytes;
+} nm_spmm_args;
+
+/*
+ * nm_spmm -- the structured-sparse linear layer.  [FLEX] 2.A/2.C (activation N:M),
+ * [SLIDE] 2.A-2.C (lowered (2N-2):2N weights with lifted activations), 2:4 weights as
+ * the special case N = 2.  W_COMPRESSED and W_SLIDE run on the gfx950 sparse matrix
+ * instructions (2:4 along K); activation patterns other than 2:4 run on dense matrix
+ * instructions over the selected (zero-filled) operand.
+ */
+nm_status nm_spmm(const nm_spmm_args* args, void* stream);
+
+/* Bytes of workspace that let nm_spmm take its two-pass route (0 if none is used). */
+int64_t nm_spmm_workspace_size(const nm_spmm_args* args);
+
+/*
+ * nm_hybrid_pack -- offline packing of the hybrid dense + 2:4 format.  [SPENSE] 2.A
+ * (a dense region and a 2:4 region) and 2.B (chosen dense indices permuted into one
+ * contiguous block).  Dense columns = the k_dense columns of W with the largest L2 norm
+ * over the output dimension (sum of squares in fp64, accumulated in ascending o; ties to
+ * the lower column).  Outputs:
+ *   sparse_cols int32 [k - k_dense] ascending; dense_cols int32 [k_dense] ascending
+ *   ws_values bf16 [o][(k-k_dense)/2], ws_meta (U8 [o][(k-k_dense)/2] or 2BIT
+ *   [o][ceil((k-k_dense)/8)]): W restricted to sparse_cols, pruned 2:4 by magnitude
+ *   wd bf16 [o][ldwd]: W restricted to dense_cols
+ *   workspace: device scratch of at least nm_hybrid_pack_workspace_size(k) bytes
+ *   (column norms and flags; its contents after the call are unspecified).
+ * Requires (k - k_dense) % 4 == 0, 0 <= k_dense <= k, k <= 65536.
+ */
+nm_status nm_hybrid_pack(const void* w, int64_t o, int64_t k, int64_t ldw, int64_t k_dense,
+                         int32_t* sparse_cols, int32_t* dense_cols, void* ws_values,
+                         void* ws_meta, nm_meta fmt, void* wd, int64_t ldwd, void* workspace,
+                         int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes nm_hybrid_pack needs for a reduction length k. */
+int64_t nm_hybrid_pack_workspace_size(int64_t k);
+
+/*
+ * nm_hybrid_gemm -- input-split product of the hybrid format, one accumulator:
+ *   Y[t][o] (=|+=) sum_{j<K_s} x[t][sparse_cols[j]] * Ws[o][j]
+ *                + sum_{j<K_d} x[t][dense_cols[j]]  * Wd[o][j]
+ * with Ws the 2:4 compressed sparse region (sparse matrix instructions) and Wd the dense
+ * region (dense matrix instructions).  [SPENSE] 2.A (input split with accumulation).
+ * sparse_cols / dense_cols may both be NULL, in which case x is taken as already
+ * permuted: columns [0, K_s) are the sparse region and [K_s, K_s+K_d) the dense one.
+ * Requires K_s % 4 == 0.
+ */
+nm_status nm_hybrid_gemm(const void* x, int64_t t, int64_t ldx, const int32_t* sparse_cols,
+                         int64_t k_s, const int32_t* dense_cols, int64_t k_d,
+                         const void* ws_values, const void* ws_meta, nm_meta fmt,
+                         const void* wd, int64_t ldwd, int64_t o, float* y, int64_t ldy,
+                         int accumulate, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NM_SPARSE_H */

@@ -1,0 +1,250 @@
+"""Python binding of libnmsparse (N:M structured-sparse linear layers on MI355X / gfx950).
+
+Thin ctypes layer: every function has the name of the C entry point it calls and only
+marshals arguments (device pointers, sizes, leading dimensions, the current HIP stream).
+All arithmetic runs in the library's HIP kernels.  torch tensors serve as device memory:
+bf16 data may be any 2-byte dtype (torch.bfloat16, int16, uint16 holding bf16 bits).
+
+The library must have been built (``semi_structured_sparse_amd.build.build()``); there is
+no fallback: importing the binding without the shared library raises ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "NMError", "lib", "NM_OK", "NM_EINVAL", "NM_ESHAPE", "NM_EALIGN", "NM_EUNSUPPORTED", "NM_EHIP",
+    "NM_META_U8", "NM_META_2BIT", "NM_W_BF16", "NM_W_FP8E4M3", "NM_ACT_DYNAMIC", "NM_ACT_COMPRESSED",
+    "NM_W_COMPRESSED", "NM_W_SLIDE", "nm_spmm_args", "nm_status_str", "nm_version", "nm_sparsify",
+    "nm_compress", "nm_decompress", "nm_lower_slide", "nm_slide_lift", "nm_spmm",
+    "nm_spmm_workspace_size", "nm_hybrid_pack", "nm_hybrid_pack_workspace_size", "nm_hybrid_gemm",
+    "lowered_k",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnmsparse.so")
+
+NM_OK, NM_EINVAL, NM_ESHAPE, NM_EALIGN, NM_EUNSUPPORTED, NM_EHIP = range(6)
+NM_META_U8, NM_META_2BIT = 0, 1
+NM_W_BF16, NM_W_FP8E4M3 = 0, 1
+NM_ACT_DYNAMIC, NM_ACT_COMPRESSED, NM_W_COMPRESSED, NM_W_SLIDE = range(4)
+
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_vp = ctypes.c_void_p
+
+
+class nm_spmm_args(ctypes.Structure):
+    _fields_ = [
+        ("mode", _int), ("n", _int), ("m", _int), ("ns", _int),
+        ("t", _i64), ("o", _i64), ("k", _i64),
+        ("x", _vp), ("ldx", _i64), ("x_meta", _vp), ("x_meta_fmt", _int),
+        ("w", _vp), ("ldw", _i64), ("w_dtype", _int), ("w_meta", _vp), ("w_meta_fmt", _int),
+        ("w_scale", _vp), ("w_kmajor", _vp),
+        ("y", _vp), ("ldy", _i64), ("accumulate", _int),
+        ("x_mask_out", _vp), ("workspace", _vp), ("workspace_bytes", _i64),
+    ]
+
+
+class NMError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {nm_status_str(status)}")
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libnmsparse.so once; raise ImportError if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with semi_structured_sparse_amd.build.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    L.nm_status_str.restype = ctypes.c_char_p
+    L.nm_status_str.argtypes = [_int]
+    L.nm_version.restype = _int
+    L.nm_version.argtypes = []
+    L.nm_sparsify.restype = _int
+    L.nm_sparsify.argtypes = [_vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _vp]
+    L.nm_compress.restype = _int
+    L.nm_compress.argtypes = [_vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _int, _vp, _vp]
+    L.nm_decompress.restype = _int
+    L.nm_decompress.argtypes = [_vp, _vp, _int, _i64, _i64, _int, _int, _vp, _i64, _vp]
+    L.nm_lower_slide.restype = _int
+    L.nm_lower_slide.argtypes = [_vp, _vp, _i64, _i64, _int, _vp, _vp, _int, _vp]
+    L.nm_slide_lift.restype = _int
+    L.nm_slide_lift.argtypes = [_vp, _i64, _i64, _i64, _int, _vp, _i64, _vp]
+    L.nm_spmm.restype = _int
+    L.nm_spmm.argtypes = [ctypes.POINTER(nm_spmm_args), _vp]
+    L.nm_spmm_workspace_size.restype = _i64
+    L.nm_spmm_workspace_size.argtypes = [ctypes.POINTER(nm_spmm_args)]
+    L.nm_hybrid_pack.restype = _int
+    L.nm_hybrid_pack.argtypes = [_vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _int, _vp, _i64, _vp, _i64, _vp]
+    L.nm_hybrid_pack_workspace_size.restype = _i64
+    L.nm_hybrid_pack_workspace_size.argtypes = [_i64]
+    L.nm_hybrid_gemm.restype = _int
+    L.nm_hybrid_gemm.argtypes = [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _int, _vp, _i64, _i64, _vp,
+                                 _i64, _int, _vp]
+    _LIB = L
+    return L
+
+
+# ------------------------------------------------------------------- marshalling ---
+
+def _ptr(t):
+    """Device pointer of a tensor (None -> NULL).  Integers pass through as raw pointers."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _ld(t, default=0):
+    if t is None:
+        return default
+    if t.dim() == 2:
+        if t.stride(1) != 1:
+            raise ValueError("innermost dimension must be contiguous")
+        return t.stride(0)
+    return default
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != NM_OK:
+        raise NMError(status, where)
+
+
+def nm_status_str(status: int) -> str:
+    return lib().nm_status_str(int(status)).decode()
+
+
+def nm_version() -> int:
+    return int(lib().nm_version())
+
+
+def lowered_k(k: int, ns: int) -> int:
+    """Reduction length after (2N-2):2N -> 2:4 lowering: k * (2N-2) / N."""
+    return (k // (2 * ns)) * 4 * (ns - 1)
+
+
+# ------------------------------------------------------------------- entry points ---
+
+def nm_sparsify(x, n, m, y=None, mask=None, stream=None, *, rows=None, k=None, ldx=None, ldy=None, check=True):
+    rows = x.shape[0] if rows is None else rows
+    k = x.shape[1] if k is None else k
+    st = lib().nm_sparsify(_ptr(x), rows, k, _ld(x) if ldx is None else ldx, n, m, _ptr(y),
+                           _ld(y) if ldy is None else ldy, _ptr(mask), _stream(stream))
+    if check:
+        _check(st, "nm_sparsify")
+    return st
+
+
+def nm_compress(x, n, m, values, meta, fmt=NM_META_U8, mask=None, stream=None, *, rows=None, k=None, ldx=None,
+                check=True):
+    rows = x.shape[0] if rows is None else rows
+    k = x.shape[1] if k is None else k
+    st = lib().nm_compress(_ptr(x), rows, k, _ld(x) if ldx is None else ldx, n, m, _ptr(values), _ptr(meta), fmt,
+                           _ptr(mask), _stream(stream))
+    if check:
+        _check(st, "nm_compress")
+    return st
+
+
+def nm_decompress(values, meta, fmt, rows, k, n, m, y, stream=None, *, ldy=None, check=True):
+    st = lib().nm_decompress(_ptr(values), _ptr(meta), fmt, rows, k, n, m, _ptr(y), _ld(y) if ldy is None else ldy,
+                             _stream(stream))
+    if check:
+        _check(st, "nm_decompress")
+    return st
+
+
+def nm_lower_slide(values, idx, rows, k, ns, values_out, meta_out, fmt=NM_META_2BIT, stream=None, *, check=True):
+    st = lib().nm_lower_slide(_ptr(values), _ptr(idx), rows, k, ns, _ptr(values_out), _ptr(meta_out), fmt,
+                              _stream(stream))
+    if check:
+        _check(st, "nm_lower_slide")
+    return st
+
+
+def nm_slide_lift(x, ns, x_out, stream=None, *, t=None, k=None, ldx=None, ldo=None, check=True):
+    t = x.shape[0] if t is None else t
+    k = x.shape[1] if k is None else k
+    st = lib().nm_slide_lift(_ptr(x), t, k, _ld(x) if ldx is None else ldx, ns, _ptr(x_out),
+                             _ld(x_out) if ldo is None else ldo, _stream(stream))
+    if check:
+        _check(st, "nm_slide_lift")
+    return st
+
+
+def nm_spmm(args: nm_spmm_args, stream=None, *, check=True):
+    st = lib().nm_spmm(ctypes.byref(args), _stream(stream))
+    if check:
+        _check(st, "nm_spmm")
+    return st
+
+
+def nm_spmm_workspace_size(args: nm_spmm_args) -> int:
+    return int(lib().nm_spmm_workspace_size(ctypes.byref(args)))
+
+
+def make_spmm_args(mode, t, o, k, x, w, y, *, n=2, m=4, ns=2, ldx=None, x_meta=None, x_meta_fmt=NM_META_U8,
+                   ldw=None, w_dtype=NM_W_BF16, w_meta=None, w_meta_fmt=NM_META_2BIT, w_scale=None,
+                   w_kmajor=None, ldy=None, accumulate=0, x_mask_out=None, workspace=None, workspace_bytes=0):
+    """Fill an nm_spmm_args from tensors (pointers and leading dimensions only).  The
+    returned struct keeps references to the tensors so that their memory stays allocated
+    while the struct is alive (it holds raw device pointers)."""
+    a = nm_spmm_args()
+    a._tensors = [v for v in (x, w, y, x_meta, w_meta, w_scale, w_kmajor, x_mask_out, workspace)
+                  if v is not None and not isinstance(v, int)]
+    a.mode, a.n, a.m, a.ns = mode, n, m, ns
+    a.t, a.o, a.k = t, o, k
+    a.x, a.ldx = _ptr(x), (_ld(x) if ldx is None else ldx)
+    a.x_meta, a.x_meta_fmt = _ptr(x_meta), x_meta_fmt
+    a.w, a.ldw, a.w_dtype = _ptr(w), (_ld(w) if ldw is None else ldw), w_dtype
+    a.w_meta, a.w_meta_fmt = _ptr(w_meta), w_meta_fmt
+    a.w_scale, a.w_kmajor = _ptr(w_scale), _ptr(w_kmajor)
+    a.y, a.ldy, a.accumulate = _ptr(y), (_ld(y) if ldy is None else ldy), accumulate
+    a.x_mask_out = _ptr(x_mask_out)
+    a.workspace, a.workspace_bytes = _ptr(workspace), workspace_bytes
+    return a
+
+
+def nm_hybrid_pack(w, k_dense, sparse_cols, dense_cols, ws_values, ws_meta, fmt, wd, workspace, stream=None, *,
+                   o=None, k=None, ldw=None, ldwd=None, workspace_bytes=None, check=True):
+    o = w.shape[0] if o is None else o
+    k = w.shape[1] if k is None else k
+    wsb = (workspace.numel() * workspace.element_size()) if workspace_bytes is None else workspace_bytes
+    st = lib().nm_hybrid_pack(_ptr(w), o, k, _ld(w) if ldw is None else ldw, k_dense, _ptr(sparse_cols),
+                              _ptr(dense_cols), _ptr(ws_values), _ptr(ws_meta), fmt, _ptr(wd),
+                              _ld(wd) if ldwd is None else ldwd, _ptr(workspace), wsb, _stream(stream))
+    if check:
+        _check(st, "nm_hybrid_pack")
+    return st
+
+
+def nm_hybrid_pack_workspace_size(k: int) -> int:
+    return int(lib().nm_hybrid_pack_workspace_size(k))
+
+
+def nm_hybrid_gemm(x, sparse_cols, k_s, dense_cols, k_d, ws_values, ws_meta, fmt, wd, o, y, accumulate=0,
+                   stream=None, *, t=None, ldx=None, ldwd=None, ldy=None, check=True):
+    t = x.shape[0] if t is None else t
+    st = lib().nm_hybrid_gemm(_ptr(x), t, _ld(x) if ldx is None else ldx, _ptr(sparse_cols), k_s,
+                              _ptr(dense_cols), k_d, _ptr(ws_values), _ptr(ws_meta), fmt, _ptr(wd),
+                              _ld(wd) if ldwd is None else ldwd, o, _ptr(y), _ld(y) if ldy is None else ldy,
+                              accumulate, _stream(stream))
+    if check:
+        _check(st, "nm_hybrid_gemm")
+    return st
+

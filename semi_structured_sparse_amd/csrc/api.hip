@@ -1,0 +1,377 @@
+// C ABI of libnmsparse: host-side validation and dispatch.  Every entry point checks
+// its arguments completely before the first HIP call and then enqueues kernels on the
+// caller's stream.  See include/nm.h for the contract of each call.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+
+#include "nm.h"
+#include "nm_launch.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool supported_m(int m) { return m == 4 || m == 8 || m == 16 || m == 32; }
+
+inline bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  return !__builtin_mul_overflow(a, b, out);
+}
+
+// rows x ld matrix addressable (and no int64 overflow when scaled by 8 bytes)
+inline bool span_ok(int64_t rows, int64_t ld) {
+  int64_t e, b;
+  return mul_ok(rows, ld, &e) && mul_ok(e, 8, &b);
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline nm_status hip_status(hipError_t e) { return e == hipSuccess ? NM_OK : NM_EHIP; }
+
+__global__ void k_fill_zero_f32(float* y, int64_t rows, int64_t cols, int64_t ldy) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * cols) return;
+  const int64_t r = i / cols, c = i - r * cols;
+  y[r * ldy + c] = 0.f;
+}
+
+nm_status zero_output(float* y, int64_t rows, int64_t cols, int64_t ldy, hipStream_t s) {
+  const int64_t n = rows * cols;
+  if (n == 0) return NM_OK;
+  k_fill_zero_f32<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(y, rows, cols, ldy);
+  return hip_status(hipGetLastError());
+}
+
+// Common checks of a dense bf16 operand [rows][ld] covering k columns.  ld_mult: the
+// leading dimension must be a multiple of this many elements (8 = 16-byte rows).
+nm_status check_bf16(const void* p, int64_t rows, int64_t k, int64_t ld, bool required, int ld_mult = 8) {
+  if (p == nullptr) return (required && rows > 0 && k > 0) ? NM_EINVAL : NM_OK;
+  if (ld < k) return NM_ESHAPE;
+  if (!span_ok(rows, ld)) return NM_ESHAPE;
+  if (!aligned16(p) || (ld % ld_mult) != 0) return NM_EALIGN;
+  return NM_OK;
+}
+
+// Row alignment the group kernels need: one group of m bf16 per lane, loaded in one
+// piece of min(16, 2m) bytes.
+inline int group_ld_mult(int m) { return m < 8 ? m : 8; }
+
+nm_status check_pattern(int64_t k, int n, int m) {
+  if (!supported_m(m)) return (m >= 1 && n >= 1 && n <= m) ? NM_EUNSUPPORTED : NM_EINVAL;
+  if (n < 1 || n > m) return NM_EINVAL;
+  if (k < 0 || (k % m) != 0) return NM_ESHAPE;
+  return NM_OK;
+}
+
+// Which activation route nm_spmm takes (overridable for A/B measurement).
+enum ActRoute { ROUTE_FUSED = 0, ROUTE_MASK = 1 };
+
+ActRoute act_route(int64_t t) {
+  const char* e = std::getenv("NM_ACT_ROUTE");
+  if (e != nullptr) {
+    if (std::strcmp(e, "fused") == 0) return ROUTE_FUSED;
+    if (std::strcmp(e, "mask") == 0) return ROUTE_MASK;
+  }
+  return t >= 512 ? ROUTE_MASK : ROUTE_FUSED;
+}
+
+int64_t mask_words(int64_t t, int64_t k) { return t * ((k + 31) / 32); }
+
+}  // namespace
+
+extern "C" {
+
+const char* nm_status_str(nm_status s) {
+  switch (s) {
+    case NM_OK: return "NM_OK";
+    case NM_EINVAL: return "NM_EINVAL: invalid argument";
+    case NM_ESHAPE: return "NM_ESHAPE: inconsistent sizes";
+    case NM_EALIGN: return "NM_EALIGN: misaligned pointer or leading dimension";
+    case NM_EUNSUPPORTED: return "NM_EUNSUPPORTED: valid but not implemented";
+    case NM_EHIP: return "NM_EHIP: HIP runtime error";
+  }
+  return "NM_?: unknown status";
+}
+
+int nm_version(void) { return kVersion; }
+
+nm_status nm_sparsify(const void* x, int64_t rows, int64_t k, int64_t ldx, int n, int m, void* y,
+                      int64_t ldy, uint32_t* mask, void* stream) {
+  nm_status st = check_pattern(k, n, m);
+  if (st) return st;
+  if (rows < 0) return NM_ESHAPE;
+  if (y == nullptr && mask == nullptr) return NM_EINVAL;
+  if ((st = check_bf16(x, rows, k, ldx, true, group_ld_mult(m)))) return st;
+  if ((st = check_bf16(y, rows, k, ldy, false, group_ld_mult(m)))) return st;
+  if (mask != nullptr && !aligned16(mask)) return NM_EALIGN;
+  if (rows == 0 || k == 0) return NM_OK;
+  return hip_status(nml::launch_select(m, (const uint16_t*)x, rows, k, ldx, n, (uint16_t*)y, ldy, mask,
+                                       nullptr, nullptr, 0, as_stream(stream)));
+}
+
+nm_status nm_compress(const void* x, int64_t rows, int64_t k, int64_t ldx, int n, int m, void* values,
+                      void* meta, nm_meta fmt, uint32_t* mask, void* stream) {
+  nm_status st = check_pattern(k, n, m);
+  if (st) return st;
+  if (rows < 0) return NM_ESHAPE;
+  if (fmt != NM_META_U8 && fmt != NM_META_2BIT) return NM_EINVAL;
+  if (fmt == NM_META_2BIT && !(n == 2 && m == 4)) return NM_EINVAL;
+  if ((st = check_bf16(x, rows, k, ldx, true, group_ld_mult(m)))) return st;
+  if (rows > 0 && k > 0 && (values == nullptr || meta == nullptr)) return NM_EINVAL;
+  if (!span_ok(rows, k)) return NM_ESHAPE;
+  if ((values && !aligned16(values)) || (meta && !aligned16(meta)) || (mask && !aligned16(mask)))
+    return NM_EALIGN;
+  if (rows == 0 || k == 0) return NM_OK;
+  return hip_status(nml::launch_select(m, (const uint16_t*)x, rows, k, ldx, n, nullptr, 0, mask,
+                                       (uint16_t*)values, (uint8_t*)meta, fmt == NM_META_2BIT ? 1 : 0,
+                                       as_stream(stream)));
+}
+
+nm_status nm_decompress(const void* values, const void* meta, nm_meta fmt, int64_t rows, int64_t k, int n,
+                        int m, void* y, int64_t ldy, void* stream) {
+  nm_status st = check_pattern(k, n, m);
+  if (st) return st;
+  if (rows < 0) return NM_ESHAPE;
+  if (fmt != NM_META_U8 && fmt != NM_META_2BIT) return NM_EINVAL;
+  if (fmt == NM_META_2BIT && !(n == 2 && m == 4)) return NM_EINVAL;
+  if (rows > 0 && k > 0 && (values == nullptr || meta == nullptr)) return NM_EINVAL;
+  if ((st = check_bf16(y, rows, k, ldy, true, group_ld_mult(m)))) return st;
+  if (!span_ok(rows, k)) return NM_ESHAPE;
+  if ((values && !aligned16(values)) || (meta && !aligned16(meta))) return NM_EALIGN;
+  if (rows == 0 || k == 0) return NM_OK;
+  return hip_status(nml::launch_decompress(m, (const uint16_t*)values, (const uint8_t*)meta,
+                                           fmt == NM_META_2BIT ? 1 : 0, rows, k, n, (uint16_t*)y, ldy,
+                                           as_stream(stream)));
+}
+
+nm_status nm_lower_slide(const void* values, const uint8_t* idx, int64_t rows, int64_t k, int ns,
+                         void* values_out, void* meta_out, nm_meta fmt, void* stream) {
+  if (ns < 2 || ns > 8) return (ns > 8) ? NM_EUNSUPPORTED : NM_EINVAL;
+  if (fmt != NM_META_U8 && fmt != NM_META_2BIT) return NM_EINVAL;
+  if (rows < 0 || k < 0 || (k % (2 * ns)) != 0) return NM_ESHAPE;
+  if (!span_ok(rows, 2 * k)) return NM_ESHAPE;
+  if (rows > 0 && k > 0 && (!values || !idx || !values_out || !meta_out)) return NM_EINVAL;
+  if ((values && !aligned16(values)) || (idx && !aligned16(idx)) || (values_out && !aligned16(values_out)) ||
+      (meta_out && !aligned16(meta_out)))
+    return NM_EALIGN;
+  if (rows == 0 || k == 0) return NM_OK;
+  return hip_status(nml::launch_lower_slide(ns, (const uint16_t*)values, idx, rows, k, (uint16_t*)values_out,
+                                            (uint8_t*)meta_out, fmt == NM_META_2BIT ? 1 : 0,
+                                            as_stream(stream)));
+}
+
+nm_status nm_slide_lift(const void* x, int64_t t, int64_t k, int64_t ldx, int ns, void* x_out, int64_t ldo,
+                        void* stream) {
+  if (ns < 2 || ns > 8) return (ns > 8) ? NM_EUNSUPPORTED : NM_EINVAL;
+  if (t < 0 || k < 0 || (k % (2 * ns)) != 0) return NM_ESHAPE;
+  const int64_t kp = (k / (2 * ns)) * 4 * (ns - 1);
+  nm_status st;   // element-wise kernel: any leading dimension
+  if ((st = check_bf16(x, t, k, ldx, true, 1))) return st;
+  if ((st = check_bf16(x_out, t, kp, ldo, true, 1))) return st;
+  if (t == 0 || k == 0) return NM_OK;
+  return hip_status(nml::launch_lift(ns, (const uint16_t*)x, t, k, ldx, (uint16_t*)x_out, ldo, as_stream(stream)));
+}
+
+int64_t nm_spmm_workspace_size(const nm_spmm_args* a) {
+  if (a == nullptr || a->t < 0 || a->k < 0) return 0;
+  if (a->mode == NM_ACT_DYNAMIC) {
+    if (a->n == 2 && a->m == 4) return a->t * (a->k / 2) * 2 + a->t * ((a->k + 7) / 8) + 64;
+    return mask_words(a->t, a->k) * 4;
+  }
+  if (a->mode == NM_ACT_COMPRESSED) return a->t * a->k * 2;
+  return 0;
+}
+
+nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
+  if (a == nullptr) return NM_EINVAL;
+  const hipStream_t s = as_stream(stream);
+  const int64_t T = a->t, O = a->o, K = a->k;
+  if (T < 0 || O < 0 || K < 0) return NM_ESHAPE;
+  if (a->accumulate != 0 && a->accumulate != 1) return NM_EINVAL;
+  if (T > 0 && O > 0 && a->y == nullptr) return NM_EINVAL;
+  if (a->y != nullptr) {
+    if (a->ldy < O || !span_ok(T, a->ldy)) return NM_ESHAPE;
+    if (!aligned16(a->y)) return NM_EALIGN;
+  }
+  nm_status st;
+  switch (a->mode) {
+    case NM_ACT_DYNAMIC:
+    case NM_ACT_COMPRESSED: {
+      if ((st = check_pattern(K, a->n, a->m))) return st;
+      if (a->w_dtype != NM_W_BF16 && a->w_dtype != NM_W_FP8E4M3) return NM_EINVAL;
+      const bool fp8 = a->w_dtype == NM_W_FP8E4M3;
+      if (fp8) {
+        if (a->w == nullptr && O > 0 && K > 0) return NM_EINVAL;
+        if (a->ldw < K || !span_ok(O, a->ldw)) return NM_ESHAPE;
+        if ((a->w && !aligned16(a->w)) || (a->ldw % 16) != 0) return NM_EALIGN;
+        if (a->w_scale == nullptr && O > 0) return NM_EINVAL;
+      } else {
+        if ((st = check_bf16(a->w, O, K, a->ldw, true))) return st;
+      }
+      if (a->w_scale != nullptr && !aligned16(a->w_scale)) return NM_EALIGN;
+      if (a->mode == NM_ACT_DYNAMIC) {
+        if ((st = check_bf16(a->x, T, K, a->ldx, true))) return st;
+      } else {
+        if (a->x_meta_fmt != NM_META_U8 && a->x_meta_fmt != NM_META_2BIT) return NM_EINVAL;
+        if (a->x_meta_fmt == NM_META_2BIT && !(a->n == 2 && a->m == 4)) return NM_EINVAL;
+        if (T > 0 && K > 0 && (a->x == nullptr || a->x_meta == nullptr)) return NM_EINVAL;
+        if ((a->x && !aligned16(a->x)) || (a->x_meta && !aligned16(a->x_meta))) return NM_EALIGN;
+      }
+      if (a->x_mask_out != nullptr && !aligned16(a->x_mask_out)) return NM_EALIGN;
+      if (a->workspace != nullptr && !aligned16(a->workspace)) return NM_EALIGN;
+      if (T == 0 || O == 0) return NM_OK;
+      if (K == 0) return a->accumulate ? NM_OK : zero_output(a->y, T, O, a->ldy, s);
+
+      nml::GemmArgs g{};
+      g.w = a->w; g.ldw = a->ldw; g.w_fp8 = fp8 ? 1 : 0; g.w_scale = a->w_scale;
+      g.n = a->n; g.m = a->m; g.t = T; g.o = O; g.k = K;
+      g.y = a->y; g.ldy = a->ldy; g.accumulate = a->accumulate;
+      const int64_t ws_need = nm_spmm_workspace_size(a);
+      const bool have_ws = a->workspace != nullptr && a->workspace_bytes >= ws_need;
+
+      if (a->mode == NM_ACT_COMPRESSED) {
+        if (a->n == 2 && a->m == 4 && a->x_meta_fmt == NM_META_2BIT && !fp8 && a->w_scale == nullptr) {
+          // 2:4 activations: X is the sparse operand of the sparse matrix instruction
+          nml::SparseArgs sa{};
+          sa.w_vals = (const uint16_t*)a->x; sa.w_meta = (const uint8_t*)a->x_meta; sa.kc = K;
+          sa.x = (const uint16_t*)a->w; sa.ldx = a->ldw; sa.loader = nml::XL_PLAIN;
+          sa.t = O; sa.o = T; sa.y = a->y; sa.ldy = a->ldy; sa.accumulate = a->accumulate; sa.trans_out = 1;
+          return hip_status(nml::launch_gemm_sparse(sa, s));
+        }
+        if (!have_ws) return NM_EINVAL;   // decompressed X needs the workspace
+        uint16_t* xd = (uint16_t*)a->workspace;
+        hipError_t e = nml::launch_decompress(a->m, (const uint16_t*)a->x, (const uint8_t*)a->x_meta,
+                                              a->x_meta_fmt == NM_META_2BIT, T, K, a->n, xd, K, s);
+        if (e != hipSuccess) return NM_EHIP;
+        g.x = xd; g.ldx = K; g.prologue = nml::PRO_NONE;
+        return hip_status(nml::launch_gemm_dense(g, s));
+      }
+
+      // ACT_DYNAMIC
+      g.x = (const uint16_t*)a->x; g.ldx = a->ldx;
+      if (a->n == 2 && a->m == 4 && !fp8 && a->w_scale == nullptr && have_ws) {
+        // 2:4: compress X once, then the sparse matrix instruction with X as sparse operand
+        uint16_t* xv = (uint16_t*)a->workspace;
+        uint8_t* xm = (uint8_t*)a->workspace + ((T * (K / 2) * 2 + 15) / 16) * 16;
+        hipError_t e = nml::launch_select(4, (const uint16_t*)a->x, T, K, a->ldx, 2, nullptr, 0, a->x_mask_out,
+                                          xv, xm, 1, s);
+        if (e != hipSuccess) return NM_EHIP;
+        nml::SparseArgs sa{};
+        sa.w_vals = xv; sa.w_meta = xm; sa.kc = K;
+        sa.x = (const uint16_t*)a->w; sa.ldx = a->ldw; sa.loader = nml::XL_PLAIN;
+        sa.t = O; sa.o = T; sa.y = a->y; sa.ldy = a->ldy; sa.accumulate = a->accumulate; sa.trans_out = 1;
+        return hip_status(nml::launch_gemm_sparse(sa, s));
+      }
+      const ActRoute route = act_route(T);
+      uint32_t* mask = a->x_mask_out;
+      if (route == ROUTE_MASK && (mask != nullptr || have_ws)) {
+        if (mask == nullptr) mask = (uint32_t*)a->workspace;
+        hipError_t e = nml::launch_select(a->m, (const uint16_t*)a->x, T, K, a->ldx, a->n, nullptr, 0, mask,
+                                          nullptr, nullptr, 0, s);
+        if (e != hipSuccess) return NM_EHIP;
+        g.prologue = nml::PRO_MASK; g.x_mask = mask;
+        return hip_status(nml::launch_gemm_dense(g, s));
+      }
+      g.prologue = nml::PRO_SELECT; g.mask_out = a->x_mask_out;
+      return hip_status(nml::launch_gemm_dense(g, s));
+    }
+    case NM_W_COMPRESSED:
+    case NM_W_SLIDE: {
+      int64_t kc = K;
+      int ns = 2;
+      if (a->mode == NM_W_SLIDE) {
+        ns = a->ns;
+        if (ns < 2 || ns > 8) return ns > 8 ? NM_EUNSUPPORTED : NM_EINVAL;
+        if (K % (2 * ns)) return NM_ESHAPE;
+        kc = (K / (2 * ns)) * 4 * (ns - 1);
+      } else if (K % 4) {
+        return NM_ESHAPE;
+      }
+      if (a->w_meta_fmt != NM_META_2BIT) return NM_EUNSUPPORTED;
+      if ((st = check_bf16(a->x, T, K, a->ldx, true))) return st;
+      if (O > 0 && kc > 0 && (a->w == nullptr || a->w_meta == nullptr)) return NM_EINVAL;
+      if ((a->w && !aligned16(a->w)) || (a->w_meta && !aligned16(a->w_meta))) return NM_EALIGN;
+      if (!span_ok(O, kc)) return NM_ESHAPE;
+      if (T == 0 || O == 0) return NM_OK;
+      if (K == 0) return a->accumulate ? NM_OK : zero_output(a->y, T, O, a->ldy, s);
+      nml::SparseArgs sa{};
+      sa.w_vals = (const uint16_t*)a->w; sa.w_meta = (const uint8_t*)a->w_meta; sa.kc = kc;
+      sa.x = (const uint16_t*)a->x; sa.ldx = a->ldx; sa.ns = ns;
+      sa.loader = a->mode == NM_W_SLIDE ? nml::XL_LIFT : nml::XL_PLAIN;
+      sa.t = T; sa.o = O; sa.y = a->y; sa.ldy = a->ldy; sa.accumulate = a->accumulate; sa.trans_out = 0;
+      return hip_status(nml::launch_gemm_sparse(sa, s));
+    }
+    default:
+      return NM_EINVAL;
+  }
+}
+
+int64_t nm_hybrid_pack_workspace_size(int64_t k) { return k <= 0 ? 0 : k * 12 + 64; }
+
+nm_status nm_hybrid_pack(const void* w, int64_t o, int64_t k, int64_t ldw, int64_t k_dense, int32_t* sparse_cols,
+                         int32_t* dense_cols, void* ws_values, void* ws_meta, nm_meta fmt, void* wd, int64_t ldwd,
+                         void* workspace, int64_t workspace_bytes, void* stream) {
+  if (o < 0 || k < 0 || k_dense < 0 || k_dense > k || k > 65536) return NM_ESHAPE;
+  if (((k - k_dense) % 4) != 0) return NM_ESHAPE;
+  if (fmt != NM_META_U8 && fmt != NM_META_2BIT) return NM_EINVAL;
+  nm_status st;
+  if ((st = check_bf16(w, o, k, ldw, true))) return st;
+  const int64_t ks = k - k_dense;
+  if (k > 0 && workspace_bytes < nm_hybrid_pack_workspace_size(k)) return NM_EINVAL;
+  if (k > 0 && workspace == nullptr) return NM_EINVAL;
+  if (ks > 0 && (sparse_cols == nullptr || (o > 0 && (ws_values == nullptr || ws_meta == nullptr)))) return NM_EINVAL;
+  if (k_dense > 0 && dense_cols == nullptr) return NM_EINVAL;
+  if (k_dense > 0 && (st = check_bf16(wd, o, k_dense, ldwd, true))) return st;
+  if ((sparse_cols && !aligned16(sparse_cols)) || (dense_cols && !aligned16(dense_cols)) ||
+      (ws_values && !aligned16(ws_values)) || (ws_meta && !aligned16(ws_meta)) ||
+      (workspace && !aligned16(workspace)))
+    return NM_EALIGN;
+  if (k == 0) return NM_OK;
+  return hip_status(nml::launch_hybrid_pack((const uint16_t*)w, o, k, ldw, k_dense, sparse_cols, dense_cols,
+                                            (uint16_t*)ws_values, (uint8_t*)ws_meta, fmt == NM_META_2BIT ? 1 : 0,
+                                            (uint16_t*)wd, ldwd, workspace, as_stream(stream)));
+}
+
+nm_status nm_hybrid_gemm(const void* x, int64_t t, int64_t ldx, const int32_t* sparse_cols, int64_t k_s,
+                         const int32_t* dense_cols, int64_t k_d, const void* ws_values, const void* ws_meta,
+                         nm_meta fmt, const void* wd, int64_t ldwd, int64_t o, float* y, int64_t ldy,
+                         int accumulate, void* stream) {
+  if (t < 0 || o < 0 || k_s < 0 || k_d < 0) return NM_ESHAPE;
+  if ((k_s % 4) != 0) return NM_ESHAPE;
+  if (accumulate != 0 && accumulate != 1) return NM_EINVAL;
+  if (fmt != NM_META_2BIT) return (fmt == NM_META_U8) ? NM_EUNSUPPORTED : NM_EINVAL;
+  const bool gathered = sparse_cols != nullptr || dense_cols != nullptr;
+  if (gathered && ((k_s > 0 && sparse_cols == nullptr) || (k_d > 0 && dense_cols == nullptr))) return NM_EINVAL;
+  const int64_t kx = gathered ? 1 : k_s + k_d;      // columns of x that must exist (gathered: unknown)
+  nm_status st;
+  if (x == nullptr && t > 0) return NM_EINVAL;
+  if (x != nullptr) {
+    if (ldx < kx || !span_ok(t, ldx)) return NM_ESHAPE;
+    if (!aligned16(x) || (ldx % 8) != 0) return NM_EALIGN;
+  }
+  if (!gathered && (k_s % 8) != 0 && k_d > 0) return NM_EALIGN;
+  if (o > 0 && k_s > 0 && (ws_values == nullptr || ws_meta == nullptr)) return NM_EINVAL;
+  if ((ws_values && !aligned16(ws_values)) || (ws_meta && !aligned16(ws_meta))) return NM_EALIGN;
+  if (k_d > 0 && (st = check_bf16(wd, o, k_d, ldwd, true))) return st;
+  if (t > 0 && o > 0 && y == nullptr) return NM_EINVAL;
+  if (y != nullptr) {
+    if (ldy < o || !span_ok(t, ldy)) return NM_ESHAPE;
+    if (!aligned16(y)) return NM_EALIGN;
+  }
+  if ((sparse_cols && !aligned16(sparse_cols)) || (dense_cols && !aligned16(dense_cols))) return NM_EALIGN;
+  if (t == 0 || o == 0) return NM_OK;
+  const hipStream_t s = as_stream(stream);
+  if (k_s == 0 && k_d == 0) return accumulate ? NM_OK : zero_output(y, t, o, ldy, s);
+  nml::SparseArgs sa{};
+  sa.w_vals = (const uint16_t*)ws_values; sa.w_meta = (const uint8_t*)ws_meta; sa.kc = k_s;
+  sa.x = (const uint16_t*)x; sa.ldx = ldx; sa.loader = gathered ? nml::XL_GATHER : nml::XL_PLAIN;
+  sa.cols = sparse_cols; sa.t = t; sa.o = o;
+  sa.wd = (const uint16_t*)wd; sa.ldwd = ldwd; sa.kd = k_d; sa.dcols = dense_cols;
+  sa.y = y; sa.ldy = ldy; sa.accumulate = accumulate; sa.trans_out = 0;
+  return hip_status(nml::launch_gemm_sparse(sa, s));
+}
+
+}  // extern "C"

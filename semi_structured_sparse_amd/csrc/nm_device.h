@@ -1,0 +1,74 @@
+// Device-side helpers shared by the libnmsparse kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nmk {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------------------------
+// Magnitude top-n of one group of M bf16 values.
+//
+// Order: larger magnitude first (the 15 bits below the sign), ties to the lower index.
+// Each element gets a unique 32-bit composite key  (magnitude << 16) | (0xFFFF - i),
+// so "rank < n" becomes "key >= the n-th largest key".  The n-th largest key comes
+// from a bitonic sorting network on the composites (branch-free, register resident).
+// ---------------------------------------------------------------------------------
+
+template <int M>
+__device__ __forceinline__ void sort_desc(uint32_t (&c)[M]) {
+#pragma unroll
+  for (int size = 2; size <= M; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+#pragma unroll
+      for (int i = 0; i < M; ++i) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const uint32_t a = c[i], b = c[j];
+          const uint32_t hi = a > b ? a : b, lo = a > b ? b : a;
+          if ((i & size) == 0) { c[i] = hi; c[j] = lo; } else { c[i] = lo; c[j] = hi; }
+        }
+      }
+    }
+  }
+}
+
+// d: the group as packed dwords (element 2q in the low half of d[q]).  Returns the keep
+// bits (bit i set iff element i is kept), exactly n bits set for 1 <= n <= M.
+template <int M>
+__device__ __forceinline__ uint32_t topn_bits(const uint32_t (&d)[M / 2], int n) {
+  uint32_t c[M], s[M];
+#pragma unroll
+  for (int q = 0; q < M / 2; ++q) {
+    c[2 * q] = ((d[q] << 16) & 0x7FFF0000u) | (0xFFFFu - 2 * q);
+    c[2 * q + 1] = (d[q] & 0x7FFF0000u) | (0xFFFFu - 2 * q - 1);
+  }
+#pragma unroll
+  for (int i = 0; i < M; ++i) s[i] = c[i];
+  sort_desc<M>(s);
+  uint32_t tau = s[0];
+#pragma unroll
+  for (int j = 1; j < M; ++j) tau = (j == n - 1) ? s[j] : tau;
+  uint32_t bits = 0;
+#pragma unroll
+  for (int i = 0; i < M; ++i) bits |= (c[i] >= tau ? 1u : 0u) << i;
+  return bits;
+}
+
+// Zero the pruned halves of a packed dword pair-of-bf16 given 2 keep bits.
+__device__ __forceinline__ uint32_t mask_pair(uint32_t d, uint32_t two_bits) {
+  const uint32_t lo = (two_bits & 1u) ? 0x0000FFFFu : 0u;
+  const uint32_t hi = (two_bits & 2u) ? 0xFFFF0000u : 0u;
+  return d & (lo | hi);
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+}  // namespace nmk

@@ -1,0 +1,146 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function nm.h
+declares, and rejects every malformed call with the documented status before any HIP
+call is made.  Pointers here are fake, aligned or misaligned addresses that are never
+dereferenced (validation fails first, or the call is a documented no-op)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import semi_structured_sparse_amd as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+P = 4096          # a fake, 16-byte aligned device address
+Q = 8192
+MIS = 4098        # misaligned
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "nm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nm_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"nm_sparsify", "nm_compress", "nm_lower_slide", "nm_spmm", "nm_hybrid_gemm"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (nm_[a-z0-9_]+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    L = S.lib()
+    for n in names:
+        assert hasattr(L, n)
+
+
+def test_status_strings_and_version():
+    for code in range(6):
+        assert S.nm_status_str(code).startswith("NM_")
+    assert S.nm_version() >= 100
+
+
+def st(fn, *a, **kw):
+    return fn(*a, check=False, stream=0, **kw)
+
+
+def test_sparsify_validation():
+    f = S.nm_sparsify
+    assert st(f, P, 2, 4, y=None, mask=None, rows=4, k=8, ldx=8, ldy=8) == S.NM_EINVAL       # no output
+    assert st(f, None, 2, 4, y=Q, rows=4, k=8, ldx=8, ldy=8) == S.NM_EINVAL                   # null x
+    assert st(f, P, 0, 4, y=Q, rows=4, k=8, ldx=8, ldy=8) == S.NM_EINVAL                      # n < 1
+    assert st(f, P, 5, 4, y=Q, rows=4, k=8, ldx=8, ldy=8) == S.NM_EINVAL                      # n > m
+    assert st(f, P, 2, 6, y=Q, rows=4, k=12, ldx=16, ldy=16) == S.NM_EUNSUPPORTED             # m = 6
+    assert st(f, P, 2, 4, y=Q, rows=4, k=10, ldx=16, ldy=16) == S.NM_ESHAPE                   # k % m
+    assert st(f, P, 2, 4, y=Q, rows=4, k=16, ldx=8, ldy=16) == S.NM_ESHAPE                    # ldx < k
+    assert st(f, P, 2, 4, y=Q, rows=-1, k=16, ldx=16, ldy=16) == S.NM_ESHAPE                  # rows < 0
+    assert st(f, MIS, 2, 4, y=Q, rows=4, k=16, ldx=16, ldy=16) == S.NM_EALIGN                 # pointer
+    assert st(f, P, 4, 8, y=Q, rows=4, k=16, ldx=20, ldy=16) == S.NM_EALIGN                   # ld % 8
+    assert st(f, P, 2, 4, y=Q, rows=4, k=16, ldx=18, ldy=16) == S.NM_EALIGN                   # ld % 4 (m=4)
+    assert st(f, P, 2, 4, y=None, mask=MIS, rows=4, k=16, ldx=16, ldy=0) == S.NM_EALIGN
+    assert st(f, P, 2, 4, y=Q, rows=1 << 62, k=16, ldx=16, ldy=16) == S.NM_ESHAPE             # overflow
+    assert st(f, P, 2, 4, y=Q, rows=0, k=16, ldx=16, ldy=16) == S.NM_OK                       # empty: no-op
+    assert st(f, P, 2, 4, y=Q, rows=3, k=0, ldx=0, ldy=0) == S.NM_OK
+
+
+def test_compress_decompress_validation():
+    c = S.nm_compress
+    assert st(c, P, 4, 8, Q, Q, S.NM_META_2BIT, rows=2, k=16, ldx=16) == S.NM_EINVAL          # 2bit needs 2:4
+    assert st(c, P, 2, 4, None, Q, S.NM_META_U8, rows=2, k=16, ldx=16) == S.NM_EINVAL         # null values
+    assert st(c, P, 2, 4, Q, Q, 7, rows=2, k=16, ldx=16) == S.NM_EINVAL                       # bad fmt
+    assert st(c, P, 2, 4, Q + 2, Q, S.NM_META_U8, rows=2, k=16, ldx=16) == S.NM_EALIGN
+    d = S.nm_decompress
+    assert st(d, P, Q, S.NM_META_2BIT, 2, 16, 4, 8, Q, ldy=16) == S.NM_EINVAL
+    assert st(d, P, Q, S.NM_META_U8, 2, 16, 2, 4, None, ldy=16) == S.NM_EINVAL
+    assert st(d, P, Q, S.NM_META_U8, 2, 18, 2, 4, Q, ldy=24) == S.NM_ESHAPE
+
+
+def test_slide_validation():
+    f = S.nm_lower_slide
+    assert st(f, P, P, 4, 16, 1, Q, Q, S.NM_META_2BIT) == S.NM_EINVAL                         # N < 2
+    assert st(f, P, P, 4, 18 * 2, 9, Q, Q, S.NM_META_2BIT) == S.NM_EUNSUPPORTED               # N > 8
+    assert st(f, P, P, 4, 12, 4, Q, Q, S.NM_META_2BIT) == S.NM_ESHAPE                         # k % 2N
+    assert st(f, None, P, 4, 16, 4, Q, Q, S.NM_META_2BIT) == S.NM_EINVAL
+    assert st(f, P, P, 4, 16, 4, Q, Q, 3) == S.NM_EINVAL
+    g = S.nm_slide_lift
+    assert st(g, P, 4, Q, t=2, k=16, ldx=16, ldo=8) == S.NM_ESHAPE                           # ldo < K'
+    assert st(g, P + 8, 4, Q, t=2, k=16, ldx=16, ldo=24) == S.NM_EALIGN
+    assert st(g, P, 4, None, t=2, k=16, ldx=16, ldo=24) == S.NM_EINVAL
+
+
+def spmm_args(**kw):
+    base = dict(mode=S.NM_ACT_DYNAMIC, t=4, o=8, k=16, x=P, w=Q, y=P + 1024, n=2, m=4, ldx=16, ldw=16, ldy=8)
+    base.update(kw)
+    mode, t, o, k, x, w, y = (base.pop(key) for key in ("mode", "t", "o", "k", "x", "w", "y"))
+    return S.make_spmm_args(mode, t, o, k, x, w, y, **base)
+
+
+def test_spmm_validation():
+    f = lambda a: S.nm_spmm(a, check=False, stream=0)  # noqa: E731
+    assert S.lib().nm_spmm(None, None) == S.NM_EINVAL
+    assert f(spmm_args(mode=9)) == S.NM_EINVAL
+    assert f(spmm_args(y=None)) == S.NM_EINVAL
+    assert f(spmm_args(ldy=4)) == S.NM_ESHAPE                         # ldy < o
+    assert f(spmm_args(y=P + 1028)) == S.NM_EALIGN                    # y not 16-byte aligned
+    assert f(spmm_args(accumulate=2)) == S.NM_EINVAL
+    assert f(spmm_args(k=18)) == S.NM_ESHAPE                          # k % m
+    assert f(spmm_args(n=9, m=8)) == S.NM_EINVAL
+    assert f(spmm_args(w_dtype=S.NM_W_FP8E4M3, w_scale=None)) == S.NM_EINVAL   # fp8 needs scales
+    assert f(spmm_args(w_dtype=S.NM_W_FP8E4M3, w_scale=P, ldw=24)) == S.NM_EALIGN
+    assert f(spmm_args(x=MIS)) == S.NM_EALIGN
+    assert f(spmm_args(mode=S.NM_W_COMPRESSED, w_meta=P, w_meta_fmt=S.NM_META_U8)) == S.NM_EUNSUPPORTED
+    assert f(spmm_args(mode=S.NM_W_COMPRESSED, w_meta=None, w_meta_fmt=S.NM_META_2BIT)) == S.NM_EINVAL
+    assert f(spmm_args(mode=S.NM_W_SLIDE, ns=4, k=12, w_meta=P)) == S.NM_ESHAPE
+    assert f(spmm_args(mode=S.NM_W_SLIDE, ns=1, w_meta=P)) == S.NM_EINVAL
+    assert f(spmm_args(mode=S.NM_ACT_COMPRESSED, x_meta=None)) == S.NM_EINVAL
+    assert f(spmm_args(mode=S.NM_ACT_COMPRESSED, x_meta=P, x_meta_fmt=S.NM_META_2BIT, n=4, m=8)) == S.NM_EINVAL
+    assert f(spmm_args(t=0)) == S.NM_OK                                # empty: no-op
+    a = spmm_args(t=64, k=4096)
+    assert S.nm_spmm_workspace_size(a) == 64 * 2048 * 2 + 64 * 512 + 64
+    a = spmm_args(t=64, k=4096, n=8, m=16)
+    assert S.nm_spmm_workspace_size(a) == 64 * 128 * 4
+
+
+def test_hybrid_validation():
+    g = lambda *a, **kw: S.nm_hybrid_gemm(*a, check=False, stream=0, **kw)  # noqa: E731
+    assert g(P, P, 6, P, 2, Q, Q, S.NM_META_2BIT, Q, 8, P, t=4, ldx=16, ldwd=8, ldy=8) == S.NM_ESHAPE  # k_s % 4
+    assert g(P, P, 8, P, 8, Q, Q, S.NM_META_U8, Q, 8, P, t=4, ldx=16, ldwd=8, ldy=8) == S.NM_EUNSUPPORTED
+    assert g(P, None, 8, P, 8, Q, Q, S.NM_META_2BIT, Q, 8, P, t=4, ldx=16, ldwd=8, ldy=8) == S.NM_EINVAL
+    assert g(P, None, 12, None, 4, Q, Q, S.NM_META_2BIT, Q, 8, P, t=4, ldx=16, ldwd=8, ldy=8) == S.NM_EALIGN
+    assert g(P, P, 8, P, 8, None, Q, S.NM_META_2BIT, Q, 8, P, t=4, ldx=16, ldwd=8, ldy=8) == S.NM_EINVAL
+    assert g(P, P, 8, P, 8, Q, Q, S.NM_META_2BIT, Q, 8, None, t=4, ldx=16, ldwd=8, ldy=8) == S.NM_EINVAL
+    p = lambda *a, **kw: S.nm_hybrid_pack(*a, check=False, stream=0, **kw)  # noqa: E731
+    assert S.nm_hybrid_pack_workspace_size(4096) >= 4096 * 12
+    assert p(P, 20, P, P, Q, Q, S.NM_META_2BIT, Q, P, o=8, k=16, ldw=16, ldwd=16, workspace_bytes=1 << 20) == S.NM_ESHAPE
+    assert p(P, 6, P, P, Q, Q, S.NM_META_2BIT, Q, P, o=8, k=16, ldw=16, ldwd=8, workspace_bytes=1 << 20) == S.NM_ESHAPE
+    assert p(P, 4, P, P, Q, Q, S.NM_META_2BIT, Q, P, o=8, k=16, ldw=16, ldwd=8, workspace_bytes=16) == S.NM_EINVAL
+    assert p(P, 4, P, P, Q, Q, S.NM_META_2BIT, Q, None, o=8, k=16, ldw=16, ldwd=8, workspace_bytes=1 << 20) == S.NM_EINVAL
+    assert p(P, 4, P, P, Q, Q, 5, Q, P, o=8, k=16, ldw=16, ldwd=8, workspace_bytes=1 << 20) == S.NM_EINVAL
+
+
+def test_binding_lowered_k_matches_oracle():
+    import oracle as O
+    for ns in range(2, 9):
+        for k in (2 * ns, 2 * ns * 7, 4096 - 4096 % (2 * ns)):
+            assert S.lowered_k(k, ns) == O.lowered_k(k, ns)
+

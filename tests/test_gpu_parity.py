@@ -1,0 +1,510 @@
+"""GPU <-> oracle parity through the C ABI (needs an MI355X and the built library).
+
+Integer / byte work (masks, S(X), compressed values, index bytes, 2-bit metadata,
+lowered windows, hybrid column lists and packed weights) must match the oracle bit for
+bit.  Products must meet: relative Frobenius error <= 1e-3 and per element
+|err| <= 1e-2 * (|A|.|B|) + 1e-4 against the oracle's fp64 result on the same bf16 inputs.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+from nm_testutil import check_gemm, dev, empty, host, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import semi_structured_sparse_amd as S  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    S.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+def special_rows(k, rng):
+    """Rows full of ties, signed zeros, subnormals, infinities and NaN."""
+    rows = [np.full(k, 0x3F80, np.uint16),                       # all equal
+            np.where(rng.random(k) < 0.5, 0x8000, 0x0000).astype(np.uint16),
+            rng.choice(np.array([0x0001, 0x0002, 0x8001, 0x0080, 0x7F80, 0xFF80, 0x7FC0, 0x3F80, 0xBF80, 0],
+                                np.uint16), size=k),
+            rng.choice(np.array([0x3F00, 0xBF00, 0x3F80, 0xBF80, 0x4000], np.uint16), size=k)]
+    return np.stack(rows)
+
+
+# --------------------------------------------------------------------- select ---
+
+SELECT_CASES = [(2, 4), (1, 4), (3, 4), (4, 8), (6, 8), (1, 8), (8, 16), (5, 16), (16, 32), (1, 32), (31, 32),
+                (4, 4), (32, 32)]
+
+
+@pytest.mark.parametrize("n,m", SELECT_CASES)
+@pytest.mark.parametrize("rows,groups,pad", [(37, 131, 0), (5, 3, 8), (1, 64, 16), (70, 64, 0)])
+def test_select_bitexact(n, m, rows, groups, pad):
+    print(f"select n={n} m={m} rows={rows} groups={groups} pad={pad}", flush=True)
+    rng = np.random.default_rng(1000 * m + n + rows)
+    k = groups * m
+    x = synth.student_t_bf16(rng, (rows, k), 4.0, 0.5)
+    x[: min(4, rows)] = special_rows(k, rng)[: min(4, rows)]
+    ld = k + pad
+    xd = dev(x, ld)
+    y = empty((rows, ld), np.uint16, fill=-1)
+    words = (k + 31) // 32
+    mask = empty((rows, words), np.uint32, fill=-1)
+    S.nm_sparsify(xd, n, m, y, mask, k=k)
+    kc = k * n // m
+    vals = empty((rows, kc), np.uint16, fill=-1)
+    idx = empty((rows, kc), np.uint8, fill=255)
+    mask2 = empty((rows, words), np.uint32, fill=-1)
+    S.nm_compress(xd, n, m, vals, idx, S.NM_META_U8, mask2, k=k)
+    sync()
+    s_ref, keep = O.sparsify(x, n, m)
+    v_ref, i_ref = O.compress(x, n, m)
+    m_ref = O.pack_mask(keep)
+    assert (host(y, np.uint16)[:, :k] == s_ref).all()
+    assert (host(y, np.uint16)[:, k:] == 0xFFFF).all()          # padding untouched
+    assert (host(mask, np.uint32) == m_ref).all()
+    assert (host(mask2, np.uint32) == m_ref).all()
+    assert (host(vals, np.uint16) == v_ref).all()
+    assert (host(idx, np.uint8) == i_ref).all()
+    if (n, m) == (2, 4):
+        meta = empty((rows, (k + 7) // 8), np.uint8, fill=255)
+        vals2 = empty((rows, kc), np.uint16, fill=-1)
+        S.nm_compress(xd, 2, 4, vals2, meta, S.NM_META_2BIT, None, k=k)
+        sync()
+        assert (host(meta, np.uint8) == O.pack_meta_2bit(i_ref)).all()
+        assert (host(vals2, np.uint16) == v_ref).all()
+
+
+@pytest.mark.parametrize("n,m", [(8, 16), (16, 32), (2, 4)])
+def test_select_full_size_sampled(n, m):
+    """Down-projection activations at full size (8192 x 14336); oracle on sampled rows."""
+    print(f"select full n={n} m={m}", flush=True)
+    d = synth.mlp_down_8of16(t_max=8192)
+    x = d["x"]
+    t, k = x.shape
+    xd = dev(x)
+    kc = k * n // m
+    vals = empty((t, kc), np.uint16)
+    idx = empty((t, kc), np.uint8)
+    mask = empty((t, (k + 31) // 32), np.uint32)
+    S.nm_compress(xd, n, m, vals, idx, S.NM_META_U8, mask)
+    sync()
+    rows = sample_rows(t, 40)
+    v_ref, i_ref = O.compress(x[rows], n, m)
+    keep = O.select_keep(x[rows], n, m)
+    assert (host(vals, np.uint16)[rows] == v_ref).all()
+    assert (host(idx, np.uint8)[rows] == i_ref).all()
+    assert (host(mask, np.uint32)[rows] == O.pack_mask(keep)).all()
+    # invariant on every row: exactly n kept per group
+    pop = np.unpackbits(host(mask, np.uint32).view(np.uint8), axis=1, bitorder="little")
+    assert (pop.reshape(t, -1, m).sum(-1) == n).all()
+
+
+def test_select_deterministic():
+    rng = np.random.default_rng(5)
+    x = synth.student_t_bf16(rng, (256, 4096), 4.0, 1.0)
+    xd = dev(x)
+    outs = []
+    for _ in range(10):
+        v = empty((256, 2048), np.uint16)
+        i = empty((256, 2048), np.uint8)
+        S.nm_compress(xd, 8, 16, v, i, S.NM_META_U8)
+        sync()
+        outs.append((host(v, np.uint16).copy(), host(i, np.uint8).copy()))
+    for v, i in outs[1:]:
+        assert (v == outs[0][0]).all() and (i == outs[0][1]).all()
+
+
+@pytest.mark.parametrize("n,m,fmt", [(2, 4, 1), (2, 4, 0), (8, 16, 0), (16, 32, 0), (6, 8, 0), (3, 8, 0)])
+def test_decompress_roundtrip(n, m, fmt):
+    rng = np.random.default_rng(77 + m)
+    rows, k = 29, m * 45
+    x = synth.normal_bf16(rng, (rows, k))
+    v_ref, i_ref = O.compress(x, n, m)
+    meta = O.pack_meta_2bit(i_ref) if fmt == 1 else i_ref
+    y = empty((rows, k), np.uint16, fill=-1)
+    S.nm_decompress(dev(v_ref), dev(meta), fmt, rows, k, n, m, y)
+    sync()
+    assert (host(y, np.uint16) == O.decompress(v_ref, i_ref, n, m, k)).all()
+
+
+# ---------------------------------------------------------------------- slide ---
+
+@pytest.mark.parametrize("ns", [2, 3, 4, 5, 8])
+@pytest.mark.parametrize("fmt", [0, 1])
+def test_lower_slide_bitexact(ns, fmt):
+    rng = np.random.default_rng(ns * 10 + fmt)
+    m, n = 2 * ns, 2 * ns - 2
+    rows, k = 23, 2 * ns * 37
+    w = synth.normal_bf16(rng, (rows, k), 0.02)
+    w[0, :m] = 0x3F80                                 # a fully tied group
+    v, i = O.compress(w, n, m)
+    vp_ref, ip_ref = O.slide_lower(v, i, k, ns)
+    kp = O.lowered_k(k, ns)
+    vo = empty((rows, kp // 2), np.uint16, fill=-1)
+    mo = empty((rows, kp // 2 if fmt == 0 else (kp + 7) // 8), np.uint8, fill=255)
+    S.nm_lower_slide(dev(v), dev(i), rows, k, ns, vo, mo, fmt)
+    sync()
+    assert (host(vo, np.uint16) == vp_ref).all()
+    want = ip_ref if fmt == 0 else O.pack_meta_2bit(ip_ref)
+    assert (host(mo, np.uint8) == want).all()
+
+
+@pytest.mark.parametrize("ns", [2, 4, 6])
+def test_lift_bitexact(ns):
+    rng = np.random.default_rng(ns)
+    t, k = 19, 2 * ns * 21
+    x = synth.normal_bf16(rng, (t, k))
+    kp = O.lowered_k(k, ns)
+    xo = empty((t, kp + 8), np.uint16, fill=-1)
+    S.nm_slide_lift(dev(x), ns, xo, k=k, ldo=kp + 8)
+    sync()
+    assert (host(xo, np.uint16)[:, :kp] == O.lift(x, ns)).all()
+
+
+# -------------------------------------------------------------- activation spmm ---
+
+def run_act(x, w, n, m, route=None, w8=None, s8=None, workspace=True, accumulate=0, y0=None):
+    t, k = x.shape
+    o = w.shape[0] if w is not None else w8.shape[0]
+    xd = dev(x)
+    if w8 is not None:
+        wd_, dtype, sd = dev(w8), S.NM_W_FP8E4M3, dev(s8)
+    else:
+        wd_, dtype, sd = dev(w), S.NM_W_BF16, None
+    y = dev(y0.astype(np.float32)) if y0 is not None else empty((t, o), np.float32, fill=float("nan"))
+    mask = empty((t, (k + 31) // 32), np.uint32, fill=-1)
+    a = S.make_spmm_args(S.NM_ACT_DYNAMIC, t, o, k, xd, wd_, y, n=n, m=m, w_dtype=dtype, w_scale=sd,
+                         x_mask_out=mask, accumulate=accumulate)
+    ws = None
+    if workspace:
+        nb = S.nm_spmm_workspace_size(a)
+        ws = empty((max(nb, 16),), np.uint8)
+        a.workspace, a.workspace_bytes = ws.data_ptr(), nb
+    old = os.environ.get("NM_ACT_ROUTE")
+    try:
+        if route is not None:
+            os.environ["NM_ACT_ROUTE"] = route
+        S.nm_spmm(a)
+        sync()
+    finally:
+        if old is None:
+            os.environ.pop("NM_ACT_ROUTE", None)
+        else:
+            os.environ["NM_ACT_ROUTE"] = old
+    return host(y, np.float32), host(mask, np.uint32)
+
+
+@pytest.mark.parametrize("n,m", [(8, 16), (16, 32), (4, 8), (2, 4), (1, 4), (6, 8)])
+@pytest.mark.parametrize("route", ["fused", "mask"])
+@pytest.mark.parametrize("t,o,k", [(300, 200, 1024), (17, 520, 1056), (513, 264, 2048)])
+def test_spmm_act_dynamic(n, m, route, t, o, k):
+    print(f"spmm act n={n} m={m} route={route} t={t} o={o} k={k}", flush=True)
+    if k % m:
+        pytest.skip("k not a multiple of m")
+    rng = np.random.default_rng(t + o + k + m)
+    x = synth.student_t_bf16(rng, (t, k), 4.0, 0.5)
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    y, mask = run_act(x, w, n, m, route=route)
+    sx, keep = O.sparsify(x, n, m)
+    assert (mask == O.pack_mask(keep)).all()
+    check_gemm(y, O.gemm(sx, w), sx, w, label=f"act {n}:{m} {route}")
+
+
+def test_spmm_act_2of4_layer():
+    """Single 2:4 activation-sparse layer (X 64x512, W 512x512): sparse matrix path
+    (compress + SMFMAC with X as the sparse operand) and the fused dense path."""
+    d = synth.layer_2of4_small()
+    x, w = d["x"], d["w"]
+    sx, keep = O.sparsify(x, 2, 4)
+    ref = O.gemm(sx, w)
+    for ws in (True, False):
+        y, mask = run_act(x, w, 2, 4, workspace=ws)
+        assert (mask == O.pack_mask(keep)).all()
+        check_gemm(y, ref, sx, w, label=f"2:4 layer ws={ws}")
+
+
+def test_spmm_act_compressed_2of4_and_8of16():
+    rng = np.random.default_rng(9)
+    for n, m, fmt in [(2, 4, 1), (8, 16, 0), (2, 4, 0)]:
+        t, o, k = 150, 272, 512
+        x = synth.normal_bf16(rng, (t, k))
+        w = synth.normal_bf16(rng, (o, k), 0.02)
+        v, i = O.compress(x, n, m)
+        meta = O.pack_meta_2bit(i) if fmt == 1 else i
+        y = empty((t, o), np.float32, fill=float("nan"))
+        a = S.make_spmm_args(S.NM_ACT_COMPRESSED, t, o, k, dev(v), dev(w), y, n=n, m=m, x_meta=dev(meta),
+                             x_meta_fmt=fmt, ldx=0)
+        nb = S.nm_spmm_workspace_size(a)
+        ws = empty((nb,), np.uint8)
+        a.workspace, a.workspace_bytes = ws.data_ptr(), nb
+        S.nm_spmm(a)
+        sync()
+        sx, _ = O.sparsify(x, n, m)
+        check_gemm(host(y, np.float32), O.gemm(sx, w), sx, w, label=f"compressed {n}:{m} fmt={fmt}")
+
+
+def test_spmm_act_accumulate_and_fp8():
+    rng = np.random.default_rng(11)
+    t, o, k = 96, 384, 2048
+    x = synth.student_t_bf16(rng, (t, k), 4.0, 1.0)
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    q, s = synth.fp8_e4m3_quantize_rows(w)
+    y0 = rng.standard_normal((t, o)).astype(np.float32)
+    for route in ("fused", "mask"):
+        y, _ = run_act(x, None, 16, 32, route=route, w8=q, s8=s)
+        sx, _ = O.sparsify(x, 16, 32)
+        wdeq = O.fp8_e4m3_to_f64(q) * s[:, None].astype(np.float64)
+        check_gemm(y, O.spmm_act_fp8(x, q, s, 16, 32), sx, wdeq, label=f"fp8 {route}")
+        y2, _ = run_act(x, w, 8, 16, route=route, accumulate=1, y0=y0)
+        sx, _ = O.sparsify(x, 8, 16)
+        check_gemm(y2 - y0, O.gemm(sx, w), sx, w, label=f"accumulate {route}")
+
+
+def test_fp8_decode_all_codes():
+    """Every finite e4m3 code through the fp8 weight loader equals the oracle's decode."""
+    codes = np.arange(256, dtype=np.uint8)
+    codes[np.isnan(O.fp8_e4m3_to_f64(codes))] = 0                 # the two NaN codes -> +0
+    k = 256
+    w8 = np.zeros((len(codes), k), np.uint8)
+    w8[:, 5] = codes                                               # one code per row, column 5
+    x = np.zeros((1, k), np.uint16)
+    x[0, :] = 0x3F80                                               # all ones: 8:16 keeps the first 8
+    y, _ = run_act(x, None, 8, 16, route="fused", w8=w8, s8=np.ones(len(codes), np.float32))
+    assert (y[0].astype(np.float64) == O.fp8_e4m3_to_f64(codes)).all()
+
+
+@pytest.mark.parametrize("route", ["fused", "mask"])
+def test_spmm_act_full_size_sampled(route):
+    """8:16 down-projection at 2048 and 8192 tokens; oracle on sampled output rows."""
+    print(f"act full route={route}", flush=True)
+    d = synth.mlp_down_8of16(t_max=8192)
+    x_all, w = d["x"], d["w"]
+    for t in (2048, 8192):
+        x = x_all[:t]
+        y, mask = run_act(x, w, 8, 16, route=route)
+        rows = sample_rows(t, 24, seed=t)
+        sx, keep = O.sparsify(x[rows], 8, 16)
+        assert (mask[rows] == O.pack_mask(keep)).all()
+        check_gemm(y[rows], O.gemm(sx, w), sx, w, label=f"full t={t}")
+
+
+# ------------------------------------------------------------------- weight 2:4 ---
+
+def gpu_compress_2of4(w):
+    o, k = w.shape
+    v = empty((o, k // 2), np.uint16)
+    mt = empty((o, (k + 7) // 8), np.uint8)
+    S.nm_compress(dev(w), 2, 4, v, mt, S.NM_META_2BIT)
+    return v, mt
+
+
+@pytest.mark.parametrize("t,o,k", [(77, 300, 512), (256, 256, 1024), (5, 33, 96)])
+def test_spmm_w_compressed(t, o, k):
+    rng = np.random.default_rng(t * o)
+    x = synth.normal_bf16(rng, (t, k))
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    v, mt = gpu_compress_2of4(w)
+    y = empty((t, o), np.float32, fill=float("nan"))
+    a = S.make_spmm_args(S.NM_W_COMPRESSED, t, o, k, dev(x), v, y, w_meta=mt, w_meta_fmt=S.NM_META_2BIT)
+    S.nm_spmm(a)
+    sync()
+    ws, _ = O.sparsify(w, 2, 4)
+    check_gemm(host(y, np.float32), O.gemm(x, ws), x, ws, label="w 2:4")
+
+
+def slide_pack_gpu(w, ns):
+    o, k = w.shape
+    n, m = 2 * ns - 2, 2 * ns
+    v = empty((o, k * n // m), np.uint16)
+    i = empty((o, k * n // m), np.uint8)
+    S.nm_compress(dev(w), n, m, v, i, S.NM_META_U8)
+    kp = O.lowered_k(k, ns)
+    vp = empty((o, kp // 2), np.uint16)
+    mp = empty((o, (kp + 7) // 8), np.uint8)
+    S.nm_lower_slide(v, i, o, k, ns, vp, mp, S.NM_META_2BIT)
+    return vp, mp
+
+
+@pytest.mark.parametrize("ns", [4, 2, 8])
+@pytest.mark.parametrize("t", [1, 16, 130, 300])
+def test_spmm_w_slide(ns, t):
+    print(f"slide ns={ns} t={t}", flush=True)
+    rng = np.random.default_rng(ns * 1000 + t)
+    o, k = 264, 2 * ns * 40
+    x = synth.normal_bf16(rng, (t, k))
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    vp, mp = slide_pack_gpu(w, ns)
+    sync()
+    pruned, _ = O.sparsify(w, 2 * ns - 2, 2 * ns)
+    v, i = O.compress(w, 2 * ns - 2, 2 * ns)
+    vp_ref, ip_ref = O.slide_lower(v, i, k, ns)
+    assert (host(vp, np.uint16) == vp_ref).all()
+    assert (host(mp, np.uint8) == O.pack_meta_2bit(ip_ref)).all()
+    y = empty((t, o), np.float32, fill=float("nan"))
+    a = S.make_spmm_args(S.NM_W_SLIDE, t, o, k, dev(x), vp, y, ns=ns, w_meta=mp, w_meta_fmt=S.NM_META_2BIT)
+    S.nm_spmm(a)
+    sync()
+    # the lowered product must equal the dense product on the same pruned W
+    check_gemm(host(y, np.float32), O.gemm(x, pruned), x, pruned, label=f"slide ns={ns}")
+
+
+@pytest.mark.parametrize("ns", [3, 5])
+def test_spmm_w_slide_odd_family(ns):
+    """4:6 and 8:10 weights: compressed on the host (the GPU select covers m in
+    {4, 8, 16, 32}), lowered and multiplied on the GPU."""
+    rng = np.random.default_rng(ns)
+    t, o, k = 70, 136, 2 * ns * 24
+    x = synth.normal_bf16(rng, (t, k))
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    v, i = O.compress(w, 2 * ns - 2, 2 * ns)
+    kp = O.lowered_k(k, ns)
+    vp = empty((o, kp // 2), np.uint16)
+    mp = empty((o, (kp + 7) // 8), np.uint8)
+    S.nm_lower_slide(dev(v), dev(i), o, k, ns, vp, mp, S.NM_META_2BIT)
+    y = empty((t, o), np.float32, fill=float("nan"))
+    a = S.make_spmm_args(S.NM_W_SLIDE, t, o, k, dev(x), vp, y, ns=ns, w_meta=mp, w_meta_fmt=S.NM_META_2BIT)
+    S.nm_spmm(a)
+    sync()
+    pruned, _ = O.sparsify(w, 2 * ns - 2, 2 * ns)
+    check_gemm(host(y, np.float32), O.gemm(x, pruned), x, pruned, label=f"slide ns={ns}")
+
+
+def test_spmm_w_slide_full_size_sampled():
+    """6:8 weights 4096x4096 lowered to 2:4 over K'=6144, T in {1,16,128,4096}."""
+    d = synth.slide_6of8_layer(t_max=4096)
+    x_all, w = d["x"], d["w"]
+    o, k = w.shape
+    vp, mp = slide_pack_gpu(w, 4)
+    sync()
+    pruned, _ = O.sparsify(w, 6, 8)
+    rows_w = sample_rows(o, 32, seed=3)
+    v, i = O.compress(w[rows_w], 6, 8)
+    vp_ref, ip_ref = O.slide_lower(v, i, k, 4)
+    assert (host(vp, np.uint16)[rows_w] == vp_ref).all()
+    assert (host(mp, np.uint8)[rows_w] == O.pack_meta_2bit(ip_ref)).all()
+    for t in (1, 16, 128, 4096):
+        x = x_all[:t]
+        y = empty((t, o), np.float32, fill=float("nan"))
+        a = S.make_spmm_args(S.NM_W_SLIDE, t, o, k, dev(x), vp, y, ns=4, w_meta=mp, w_meta_fmt=S.NM_META_2BIT)
+        S.nm_spmm(a)
+        sync()
+        rows = sample_rows(t, 16, seed=t)
+        check_gemm(host(y, np.float32)[rows], O.gemm(x[rows], pruned), x[rows], pruned, label=f"slide full t={t}")
+
+
+# ----------------------------------------------------------------------- hybrid ---
+
+def hybrid_pack_gpu(w, kd, fmt=S.NM_META_2BIT):
+    o, k = w.shape
+    ks = k - kd
+    sc = empty((max(ks, 1),), np.int32, fill=-1)
+    dc = empty((max(kd, 1),), np.int32, fill=-1)
+    wv = empty((o, max(ks // 2, 1)), np.uint16, fill=-1)
+    wm = empty((o, max((ks + 7) // 8 if fmt else ks // 2, 1)), np.uint8, fill=255)
+    wdd = empty((o, max(kd, 8)), np.uint16, fill=-1)
+    ws = empty((S.nm_hybrid_pack_workspace_size(k),), np.uint8)
+    S.nm_hybrid_pack(dev(w), kd, sc, dc, wv, wm, fmt, wdd, ws, ldwd=max(kd, 8))
+    return sc, dc, wv, wm, wdd
+
+
+@pytest.mark.parametrize("o,k,kd", [(100, 256, 64), (64, 128, 0), (48, 96, 96), (300, 512, 128)])
+def test_hybrid_pack_and_gemm(o, k, kd):
+    rng = np.random.default_rng(o + k + kd)
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    x = synth.normal_bf16(rng, (130, k))
+    sc, dc, wv, wm, wdd = hybrid_pack_gpu(w, kd)
+    sync()
+    sp, de, v, i, wd = O.hybrid_pack(w, kd)
+    ks = k - kd
+    if ks:
+        assert (host(sc, np.int32)[:ks] == sp).all()
+        assert (host(wv, np.uint16)[:, :ks // 2] == v).all()
+        assert (host(wm, np.uint8)[:, :(ks + 7) // 8] == O.pack_meta_2bit(i)).all()
+    if kd:
+        assert (host(dc, np.int32)[:kd] == de).all()
+        assert (host(wdd, np.uint16)[:, :kd] == wd).all()
+    y = empty((130, o), np.float32, fill=float("nan"))
+    S.nm_hybrid_gemm(dev(x), sc if ks else None, ks, dc if kd else None, kd, wv, wm, S.NM_META_2BIT,
+                     wdd if kd else None, o, y, ldwd=max(kd, 8))
+    sync()
+    ref = O.hybrid_gemm(x, sp, de, v, i, wd)
+    wh = w.copy()
+    if ks:
+        wh[:, sp] = O.decompress(v, i, 2, 4, ks)
+    check_gemm(host(y, np.float32), ref, x, wh, label="hybrid")
+
+
+def test_hybrid_prepermuted_input():
+    """Column lists NULL: x already holds the sparse region then the dense region."""
+    rng = np.random.default_rng(21)
+    o, k, kd = 136, 512, 128
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    x = synth.normal_bf16(rng, (70, k))
+    sc, dc, wv, wm, wdd = hybrid_pack_gpu(w, kd)
+    sync()
+    sp, de, v, i, wd = O.hybrid_pack(w, kd)
+    xp = np.ascontiguousarray(np.concatenate([x[:, sp], x[:, de]], axis=1))
+    y = empty((70, o), np.float32, fill=float("nan"))
+    S.nm_hybrid_gemm(dev(xp), None, k - kd, None, kd, wv, wm, S.NM_META_2BIT, wdd, o, y, ldwd=max(kd, 8))
+    sync()
+    wh = w.copy()
+    wh[:, sp] = O.decompress(v, i, 2, 4, k - kd)
+    check_gemm(host(y, np.float32), O.hybrid_gemm(x, sp, de, v, i, wd), x, wh, label="hybrid prepermuted")
+
+
+def test_hybrid_full_size_sampled():
+    """W 14336x4096, 25% dense columns; T in {1, 8, 32, 64, 2048}."""
+    d = synth.hybrid_up_layer(t_max=2048)
+    x_all, w, kd = d["x"], d["w"], d["k_dense"]
+    o, k = w.shape
+    sc, dc, wv, wm, wdd = hybrid_pack_gpu(w, kd)
+    sync()
+    sp, de = O.hybrid_columns(w, kd)
+    assert (host(sc, np.int32) == sp).all() and (host(dc, np.int32) == de).all()
+    rows_w = sample_rows(o, 64, seed=4)
+    ws_ref = O.sparsify(np.ascontiguousarray(w[rows_w][:, sp]), 2, 4)[0]
+    v, i = O.compress(np.ascontiguousarray(w[rows_w][:, sp]), 2, 4)
+    assert (host(wv, np.uint16)[rows_w] == v).all()
+    assert (host(wm, np.uint8)[rows_w] == O.pack_meta_2bit(i)).all()
+    assert (host(wdd, np.uint16)[rows_w] == w[rows_w][:, de]).all()
+    wh = w.copy()
+    wh[:, sp] = O.sparsify(np.ascontiguousarray(w[:, sp]), 2, 4)[0]
+    del ws_ref
+    for t in (1, 8, 32, 64, 2048):
+        x = x_all[:t]
+        y = empty((t, o), np.float32, fill=float("nan"))
+        S.nm_hybrid_gemm(dev(x), sc, k - kd, dc, kd, wv, wm, S.NM_META_2BIT, wdd, o, y)
+        sync()
+        rows = sample_rows(t, 12, seed=t)
+        check_gemm(host(y, np.float32)[rows], O.gemm(x[rows], wh), x[rows], wh, label=f"hybrid full t={t}")
+
+
+# ------------------------------------------------------------------ edge cases ---
+
+def test_zero_sizes_and_k_zero():
+    y = empty((4, 8), np.float32, fill=5.0)
+    x = empty((4, 8), np.uint16, fill=0)
+    w = empty((8, 8), np.uint16, fill=0)
+    a = S.make_spmm_args(S.NM_ACT_DYNAMIC, 4, 8, 0, x, w, y, n=2, m=4, ldx=8, ldw=8)
+    S.nm_spmm(a)
+    sync()
+    assert (host(y, np.float32) == 0).all()
+    y.fill_(5.0)
+    a.accumulate = 1
+    S.nm_spmm(a)
+    sync()
+    assert (host(y, np.float32) == 5).all()
+    a.t = 0
+    assert S.nm_spmm(a, check=False) == S.NM_OK
