@@ -129,14 +129,18 @@ typedef enum {
   NM_ACT_DYNAMIC = 0,    /* X dense; select n:m of X inside the call, then contract     */
   NM_ACT_COMPRESSED = 1, /* X given compressed (values + meta from nm_compress)          */
   NM_W_COMPRESSED = 2,   /* W given as 2:4 compressed (values + meta); X dense           */
-  NM_W_SLIDE = 3         /* W given lowered by nm_lower_slide (2:4 over K'); X lifted on
+  NM_W_SLIDE = 3,        /* W given lowered by nm_lower_slide (2:4 over K'); X lifted on
                             the fly inside the operand loader                            */
+  NM_ACT_MASKED = 4      /* X dense plus its keep bitmask from nm_sparsify (x_meta =
+                            uint32 [t][ceil(k/32)]): the two-pass form of ACT_DYNAMIC    */
 } nm_spmm_mode;
 
 /*
  * Arguments of nm_spmm.  Y[t][o] (fp32, row stride ldy) = sum_k A[t][k] * B[o][k] with
  *   ACT_DYNAMIC:    A = S_{n:m}(x),         B = w (bf16 [o][ldw] or fp8 [o][ldw] bytes)
  *   ACT_COMPRESSED: A = decompress(x, x_meta) (x = values [t][k*n/m]), B = w as above
+ *   ACT_MASKED:     A = x with the positions whose bit in x_meta is clear zeroed; the
+ *                   mask must come from nm_sparsify with the same n, m (then A = S(x))
  *   W_COMPRESSED:   A = x (bf16 [t][ldx]),  B = decompress(w, w_meta), 2:4 over k
  *   W_SLIDE:        A = lift_ns(x),          B = decompress(w, w_meta), 2:4 over
  *                   K' = k*(2ns-2)/ns  (equals x . Wpruned^T)

@@ -16,7 +16,7 @@ import os
 __all__ = [
     "NMError", "lib", "NM_OK", "NM_EINVAL", "NM_ESHAPE", "NM_EALIGN", "NM_EUNSUPPORTED", "NM_EHIP",
     "NM_META_U8", "NM_META_2BIT", "NM_W_BF16", "NM_W_FP8E4M3", "NM_ACT_DYNAMIC", "NM_ACT_COMPRESSED",
-    "NM_W_COMPRESSED", "NM_W_SLIDE", "nm_spmm_args", "nm_status_str", "nm_version", "nm_sparsify",
+    "NM_W_COMPRESSED", "NM_W_SLIDE", "NM_ACT_MASKED", "nm_spmm_args", "nm_status_str", "nm_version", "nm_sparsify",
     "nm_compress", "nm_decompress", "nm_lower_slide", "nm_slide_lift", "nm_spmm",
     "nm_spmm_workspace_size", "nm_hybrid_pack", "nm_hybrid_pack_workspace_size", "nm_hybrid_gemm",
     "lowered_k",
@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnmsparse
 NM_OK, NM_EINVAL, NM_ESHAPE, NM_EALIGN, NM_EUNSUPPORTED, NM_EHIP = range(6)
 NM_META_U8, NM_META_2BIT = 0, 1
 NM_W_BF16, NM_W_FP8E4M3 = 0, 1
-NM_ACT_DYNAMIC, NM_ACT_COMPRESSED, NM_W_COMPRESSED, NM_W_SLIDE = range(4)
+NM_ACT_DYNAMIC, NM_ACT_COMPRESSED, NM_W_COMPRESSED, NM_W_SLIDE, NM_ACT_MASKED = range(5)
 
 _i64 = ctypes.c_int64
 _int = ctypes.c_int

@@ -199,6 +199,7 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
   nm_status st;
   switch (a->mode) {
     case NM_ACT_DYNAMIC:
+    case NM_ACT_MASKED:
     case NM_ACT_COMPRESSED: {
       if ((st = check_pattern(K, a->n, a->m))) return st;
       if (a->w_dtype != NM_W_BF16 && a->w_dtype != NM_W_FP8E4M3) return NM_EINVAL;
@@ -212,8 +213,12 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
         if ((st = check_bf16(a->w, O, K, a->ldw, true))) return st;
       }
       if (a->w_scale != nullptr && !aligned16(a->w_scale)) return NM_EALIGN;
-      if (a->mode == NM_ACT_DYNAMIC) {
+      if (a->mode == NM_ACT_DYNAMIC || a->mode == NM_ACT_MASKED) {
         if ((st = check_bf16(a->x, T, K, a->ldx, true))) return st;
+        if (a->mode == NM_ACT_MASKED) {
+          if (a->x_meta == nullptr && T > 0 && K > 0) return NM_EINVAL;
+          if (a->x_meta != nullptr && !aligned16(a->x_meta)) return NM_EALIGN;
+        }
       } else {
         if (a->x_meta_fmt != NM_META_U8 && a->x_meta_fmt != NM_META_2BIT) return NM_EINVAL;
         if (a->x_meta_fmt == NM_META_2BIT && !(a->n == 2 && a->m == 4)) return NM_EINVAL;
@@ -250,8 +255,13 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
         return hip_status(nml::launch_gemm_dense(g, s));
       }
 
-      // ACT_DYNAMIC
       g.x = (const uint16_t*)a->x; g.ldx = a->ldx;
+      if (a->mode == NM_ACT_MASKED) {
+        g.prologue = nml::PRO_MASK; g.x_mask = (const uint32_t*)a->x_meta;
+        return hip_status(nml::launch_gemm_dense(g, s));
+      }
+
+      // ACT_DYNAMIC
       if (a->n == 2 && a->m == 4 && !fp8 && a->w_scale == nullptr && have_ws) {
         // 2:4: compress X once, then the sparse matrix instruction with X as sparse operand
         uint16_t* xv = (uint16_t*)a->workspace;
