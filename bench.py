@@ -4,8 +4,8 @@
 Workload (the down-projection layer the throughput metric is quoted on): 8:16 activation
 sparsity, X 8192 x 14336 bf16 drawn Student-t(4) * 0.5, W 4096 x 14336 bf16 ~ N(0, 0.02),
 Y = S(X) . W^T in fp32.  One step = the whole hot path over one batch:
-  nm_sparsify  (per-group top-8 of 16 by magnitude -> keep bitmask)
-  nm_spmm      (ACT_MASKED: the selected X contracted with W on dense matrix cores)
+  nm_sparsify  (per-group top-8 of 16 by magnitude -> S(X), pruned entries +0)
+  nm_spmm      (ACT_MASKED with S(X): the selected X contracted with W on matrix cores)
 Inputs are resident in HBM before the timed region.  Prints ONE JSON line on stdout.
 
 --gpus N with N > 1 is refused: this build runs on a single GPU.
@@ -24,8 +24,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-PMC_FILE = os.path.join(ROOT, "profiles", "gemm_dense_mask_pmc.json")
-PMC_SOURCES = ["semi_structured_sparse_amd/csrc/gemm_dense.hip", "semi_structured_sparse_amd/csrc/nm_device.h"]
+PMC_FILE = os.path.join(ROOT, "profiles", "gemm_lds_pmc.json")
+PMC_SOURCES = ["semi_structured_sparse_amd/csrc/gemm_lds.hip", "semi_structured_sparse_amd/csrc/nm_device.h"]
 
 
 def log(*a):
@@ -127,13 +127,13 @@ def main():
     x = torch.from_numpy(x_bits.view(np.int16)).cuda()
     w = torch.from_numpy(w_bits.view(np.int16)).cuda()
     y = torch.empty((T, O_), dtype=torch.float32, device="cuda")
-    mask = torch.empty((T, (K + 31) // 32), dtype=torch.int32, device="cuda")
-    a = S.make_spmm_args(S.NM_ACT_MASKED, T, O_, K, x, w, y, n=n, m=m, x_meta=mask)
+    sx = torch.empty((T, K), dtype=torch.int16, device="cuda")
+    a = S.make_spmm_args(S.NM_ACT_MASKED, T, O_, K, sx, w, y, n=n, m=m)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        S.nm_sparsify(x, n, m, None, mask)
+        S.nm_sparsify(x, n, m, sx, None)
         if ev is not None:
             ev[1].record()
         S.nm_spmm(a)
@@ -156,7 +156,7 @@ def main():
     flops = 2.0 * T * O_ * K
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (gemm_ms * 1e-3) / 1e12
-    sel_bytes = T * K * 2 + T * ((K + 31) // 32) * 4
+    sel_bytes = T * K * 2 * 2
     log(f"step {ms_per_step:.3f} ms: select {sel_ms * 1e3:.1f} us ({sel_bytes / sel_ms / 1e6:.0f} GB/s), "
         f"product {gemm_ms * 1e3:.1f} us ({achieved:.1f} TFLOP/s)")
     traffic = measured_traffic(T)
@@ -168,7 +168,7 @@ def main():
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"8:16 activation-sparse MLP down-projection, X {T}x{K} Student-t(4)*0.5, "
                                f"W {O_}x{K} N(0,0.02), fp32 out", "tokens": T, "in_features": K,
-                   "out_features": O_, "pattern": "8:16", "route": "nm_sparsify + nm_spmm(ACT_MASKED)"},
+                   "out_features": O_, "pattern": "8:16", "route": "nm_sparsify -> S(X), nm_spmm(ACT_MASKED)"},
         "executed_tflops": round(value, 2),
         "kernels": {
             "select_us": round(sel_ms * 1e3, 2), "select_GBps": round(sel_bytes / sel_ms / 1e6, 1),

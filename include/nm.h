@@ -132,7 +132,8 @@ typedef enum {
   NM_W_SLIDE = 3,        /* W given lowered by nm_lower_slide (2:4 over K'); X lifted on
                             the fly inside the operand loader                            */
   NM_ACT_MASKED = 4      /* X dense plus its keep bitmask from nm_sparsify (x_meta =
-                            uint32 [t][ceil(k/32)]): the two-pass form of ACT_DYNAMIC    */
+                            uint32 [t][ceil(k/32)]), or X = S(X) already (x_meta NULL):
+                            the two-pass forms of ACT_DYNAMIC                            */
 } nm_spmm_mode;
 
 /*
@@ -140,7 +141,8 @@ typedef enum {
  *   ACT_DYNAMIC:    A = S_{n:m}(x),         B = w (bf16 [o][ldw] or fp8 [o][ldw] bytes)
  *   ACT_COMPRESSED: A = decompress(x, x_meta) (x = values [t][k*n/m]), B = w as above
  *   ACT_MASKED:     A = x with the positions whose bit in x_meta is clear zeroed; the
- *                   mask must come from nm_sparsify with the same n, m (then A = S(x))
+ *                   mask must come from nm_sparsify with the same n, m (then A = S(x)).
+ *                   x_meta may be NULL when x already holds S(x) (nm_sparsify's y).
  *   W_COMPRESSED:   A = x (bf16 [t][ldx]),  B = decompress(w, w_meta), 2:4 over k
  *   W_SLIDE:        A = lift_ns(x),          B = decompress(w, w_meta), 2:4 over
  *                   K' = k*(2ns-2)/ns  (equals x . Wpruned^T)

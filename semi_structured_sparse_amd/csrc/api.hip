@@ -66,16 +66,22 @@ nm_status check_pattern(int64_t k, int n, int m) {
   return NM_OK;
 }
 
-// Which activation route nm_spmm takes (overridable for A/B measurement).
-enum ActRoute { ROUTE_FUSED = 0, ROUTE_MASK = 1 };
+// Which activation route nm_spmm takes (NM_ACT_ROUTE overrides it for A/B measurement):
+//   fused: top-n selected inside the product kernel's X-tile loader;
+//   mask:  a select pass writes the keep bitmask, the product applies it to X fragments;
+//   sx:    a select pass writes S(X) to the workspace, the product streams it unchanged.
+// Measured on gfx950 at 8192 x 14336 x 4096 (8:16): sx 90 + 767 us, mask 67 + 1091 us;
+// the fused loader re-selects X once per output tile and is slowest at large T.
+enum ActRoute { ROUTE_FUSED = 0, ROUTE_MASK = 1, ROUTE_SX = 2 };
 
 ActRoute act_route(int64_t t) {
   const char* e = std::getenv("NM_ACT_ROUTE");
   if (e != nullptr) {
     if (std::strcmp(e, "fused") == 0) return ROUTE_FUSED;
     if (std::strcmp(e, "mask") == 0) return ROUTE_MASK;
+    if (std::strcmp(e, "sx") == 0) return ROUTE_SX;
   }
-  return t >= 512 ? ROUTE_MASK : ROUTE_FUSED;
+  return t >= 512 ? ROUTE_SX : ROUTE_FUSED;
 }
 
 int64_t mask_words(int64_t t, int64_t k) { return t * ((k + 31) / 32); }
@@ -179,7 +185,7 @@ int64_t nm_spmm_workspace_size(const nm_spmm_args* a) {
   if (a == nullptr || a->t < 0 || a->k < 0) return 0;
   if (a->mode == NM_ACT_DYNAMIC) {
     if (a->n == 2 && a->m == 4) return a->t * (a->k / 2) * 2 + a->t * ((a->k + 7) / 8) + 64;
-    return mask_words(a->t, a->k) * 4;
+    return a->t * a->k * 2;   // S(X) for the two-pass route (also covers the bitmask)
   }
   if (a->mode == NM_ACT_COMPRESSED) return a->t * a->k * 2;
   return 0;
@@ -215,10 +221,7 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
       if (a->w_scale != nullptr && !aligned16(a->w_scale)) return NM_EALIGN;
       if (a->mode == NM_ACT_DYNAMIC || a->mode == NM_ACT_MASKED) {
         if ((st = check_bf16(a->x, T, K, a->ldx, true))) return st;
-        if (a->mode == NM_ACT_MASKED) {
-          if (a->x_meta == nullptr && T > 0 && K > 0) return NM_EINVAL;
-          if (a->x_meta != nullptr && !aligned16(a->x_meta)) return NM_EALIGN;
-        }
+        if (a->mode == NM_ACT_MASKED && a->x_meta != nullptr && !aligned16(a->x_meta)) return NM_EALIGN;
       } else {
         if (a->x_meta_fmt != NM_META_U8 && a->x_meta_fmt != NM_META_2BIT) return NM_EINVAL;
         if (a->x_meta_fmt == NM_META_2BIT && !(a->n == 2 && a->m == 4)) return NM_EINVAL;
@@ -257,7 +260,8 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
 
       g.x = (const uint16_t*)a->x; g.ldx = a->ldx;
       if (a->mode == NM_ACT_MASKED) {
-        g.prologue = nml::PRO_MASK; g.x_mask = (const uint32_t*)a->x_meta;
+        g.prologue = a->x_meta != nullptr ? nml::PRO_MASK : nml::PRO_NONE;
+        g.x_mask = (const uint32_t*)a->x_meta;
         return hip_status(nml::launch_gemm_dense(g, s));
       }
 
@@ -277,6 +281,14 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
       }
       const ActRoute route = act_route(T);
       uint32_t* mask = a->x_mask_out;
+      if (route == ROUTE_SX && have_ws) {
+        uint16_t* sx = (uint16_t*)a->workspace;
+        hipError_t e = nml::launch_select(a->m, (const uint16_t*)a->x, T, K, a->ldx, a->n, sx, K, mask,
+                                          nullptr, nullptr, 0, s);
+        if (e != hipSuccess) return NM_EHIP;
+        g.prologue = nml::PRO_NONE; g.x = sx; g.ldx = K;
+        return hip_status(nml::launch_gemm_dense(g, s));
+      }
       if (route == ROUTE_MASK && (mask != nullptr || have_ws)) {
         if (mask == nullptr) mask = (uint32_t*)a->workspace;
         hipError_t e = nml::launch_select(a->m, (const uint16_t*)a->x, T, K, a->ldx, a->n, nullptr, 0, mask,

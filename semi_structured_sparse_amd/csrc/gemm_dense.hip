@@ -17,6 +17,9 @@
 // through double-buffered LDS tiles (row pitch 72 bf16 = 144 bytes: conflict-free
 // 16-byte fragment reads).  Workgroups are remapped so that each of the 8 XCDs (own L2)
 // works on a contiguous band of output tiles.
+#include <cstdlib>
+#include <cstring>
+
 #include "nm_device.h"
 #include "nm_launch.h"
 
@@ -324,6 +327,11 @@ hipError_t launch_m(const nml::GemmArgs& a, hipStream_t s) {
 namespace nml {
 
 hipError_t launch_gemm_dense(const GemmArgs& a, hipStream_t s) {
+  // NM_GEMM=regs / lds overrides the kernel choice (A/B measurement and tests)
+  const char* force = std::getenv("NM_GEMM");
+  const bool regs_only = force != nullptr && std::strcmp(force, "regs") == 0;
+  const bool lds_any = force != nullptr && std::strcmp(force, "lds") == 0;
+  if (!regs_only && gemm_lds_eligible(a, lds_any)) return launch_gemm_lds(a, s);
   if (a.w_fp8) {
     switch (a.prologue) {
       case PRO_NONE: return launch_m<PRO_NONE, true>(a, s);

@@ -1,0 +1,261 @@
+// Large-token dense-MFMA product with direct global->LDS staging:
+//   Y[t][o] = sum_k A~[t][k] * W[o][k]
+// where A~ is X itself (PRO_NONE: X already sparsified, or a dense layer) or X with the
+// positions whose keep bit is clear zeroed (PRO_MASK: the bitmask of the per-group top-n
+// selection -- Flexible (N:M) Activation Sparsity page, technical summary 2.A/2.C --
+// produced by a separate select pass).
+//
+// gfx950 design:
+//  * Both operands are K-contiguous rows.  A K-step moves 64 bf16 (128 bytes) of every
+//    tile row straight from global memory into LDS with global_load_lds_dwordx4: one
+//    wave instruction fills 8 whole rows (1 KiB, contiguous in LDS), so no VGPRs are
+//    spent on staging and every global access is a full 128-byte line.
+//  * LDS rows are unpadded; the 16-byte chunk c of row r lives at chunk c ^ ((r>>1)&7),
+//    which keeps the 16-lane groups of a ds_read_b128 fragment read on distinct banks.
+//  * Two LDS stages (64 KiB each for a 256x256 tile): the loads of K-step k+1 are issued
+//    a group at a time between the matrix instructions of K-step k; one barrier per
+//    K-step.  The waves raise their priority while issuing matrix instructions.
+//  * The keep mask travels with the X tile (two 32-bit words per row per K-step) and is
+//    applied to each 8-element X fragment right after its LDS read (4 VALU ops per
+//    dword, overlapping the matrix instructions).
+//  * 8 waves (2 per SIMD), each owning a 64 (o) x 128 (t) block of 16x16 accumulators
+//    (v_mfma_f32_16x16x32_bf16); workgroups are remapped so each XCD (own L2) walks a
+//    compact band of output tiles.  Measured on gfx950: LDS reads sustain ~128 B/clk per
+//    CU, so the 2 x 4 KiB fragment reads per wave per K-step and the 64 KiB of staged
+//    tiles keep the LDS about as busy as the matrix cores; the 64 x 128 wave shape and
+//    the priority hint were the fastest of the variants tried.
+// Requirements (checked by the dispatcher): K % 64 == 0, 16-byte aligned rows.  Rows
+// beyond T or O are read from the last valid row and their outputs are not stored.
+#include "nm_device.h"
+#include "nm_launch.h"
+
+namespace {
+
+using namespace nmk;
+using namespace nml;
+
+constexpr int BK = 64;                 // bf16 per K-step
+constexpr int ROWB = BK * 2;           // bytes per tile row per K-step
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// global -> LDS copy of `bytes` (4 or 16) per lane: lane i writes lds + i * bytes.  The
+// LDS address must be wave-uniform (it is passed in M0).
+__device__ __forceinline__ void g2lds16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void g2lds4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
+}
+
+// zero the halves of dword d whose bits (2q, 2q+1) of `bits` are clear
+__device__ __forceinline__ uint32_t keep_pair(uint32_t d, uint32_t bits, int q) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_sbfe((int)bits, 2 * q, 1);      // 0 or ~0
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_sbfe((int)bits, 2 * q + 1, 1);
+  return d & ((hi & 0xFFFF0000u) | (lo & 0x0000FFFFu));
+}
+
+template <int BM, int BN, int WM, int WN, int PRO>
+__global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
+    const uint16_t* __restrict__ w, int64_t ldw, const uint16_t* __restrict__ x, int64_t ldx,
+    const uint32_t* __restrict__ xmask, int64_t T, int64_t O, int64_t K, float* __restrict__ y,
+    int64_t ldy, int accumulate, int tiles_m, int tiles_n) {
+  constexpr int NW = WM * WN;
+  constexpr int SM = BM / WM, SN = BN / WN;       // wave sub-tile (o x t)
+  constexpr int FI = SM / 16, FJ = SN / 16;
+  constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
+  constexpr int MASK_BYTES = (PRO == PRO_MASK) ? BN * 8 : 16;
+  constexpr int A_GROUPS = BM / 8, B_GROUPS = BN / 8;   // 8-row load groups
+  constexpr int NGA = A_GROUPS / NW, NGB = B_GROUPS / NW;
+  static_assert(A_GROUPS % NW == 0 && B_GROUPS % NW == 0, "load groups per wave");
+  static_assert(NGA <= 2 * FI && NGB <= 2 * FI, "load groups are spread over the 2*FI MFMA steps");
+  constexpr int MASK_GROUPS = (PRO == PRO_MASK) ? BN / 32 : 0;   // 32 rows x 2 words per inst
+
+  // two stages as distinct arrays: every LDS access names its stage statically
+  __shared__ __align__(16) unsigned char sA0[A_BYTES], sB0[B_BYTES], sM0[MASK_BYTES];
+  __shared__ __align__(16) unsigned char sA1[A_BYTES], sB1[B_BYTES], sM1[MASK_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (LDS base goes to M0)
+  const int wm = wave % WM, wn = wave / WM;
+
+  // XCD-aware tile order: hardware places workgroup b on XCD b % 8; each XCD takes a
+  // contiguous range of tiles, walked t-major inside bands of GROUP o-tiles.
+  const int ntiles = tiles_m * tiles_n;
+  int lin = blockIdx.x;
+  if ((ntiles & 7) == 0) lin = (blockIdx.x & 7) * (ntiles >> 3) + (blockIdx.x >> 3);
+  constexpr int GROUP = 16;
+  const int band = lin / (GROUP * tiles_n);
+  const int band_w = min(GROUP, tiles_m - band * GROUP);
+  const int inband = lin - band * GROUP * tiles_n;
+  const int tile_m = band * GROUP + inband % band_w;
+  const int tile_n = inband / band_w;
+  const int64_t o0 = (int64_t)tile_m * BM, t0 = (int64_t)tile_n * BN;
+
+  // per-lane global source addresses of this wave's load groups (K offset added per step)
+  const int lrow = lane >> 3, lchunk = lane & 7;
+  const uint16_t* asrc[NGA];
+  const uint16_t* bsrc[NGB];
+#pragma unroll
+  for (int g = 0; g < NGA; ++g) {
+    const int r = (wave + g * NW) * 8 + lrow;
+    int64_t o = o0 + r;
+    if (o >= O) o = O - 1;
+    asrc[g] = w + o * ldw + 8 * swz(r, lchunk);
+  }
+#pragma unroll
+  for (int g = 0; g < NGB; ++g) {
+    const int r = (wave + g * NW) * 8 + lrow;
+    int64_t t = t0 + r;
+    if (t >= T) t = T - 1;
+    bsrc[g] = x + t * ldx + 8 * swz(r, lchunk);
+  }
+  const int64_t mwords = K >> 5;
+  const uint32_t* msrc = nullptr;
+  if constexpr (PRO == PRO_MASK) {
+    if (wave < MASK_GROUPS) {
+      int64_t t = t0 + wave * 32 + (lane >> 1);
+      if (t >= T) t = T - 1;
+      msrc = xmask + t * mwords + (lane & 1);
+    }
+  }
+
+  auto issue_all = [&](unsigned char* a, unsigned char* b, unsigned char* mk, int64_t k0) {
+#pragma unroll
+    for (int g = 0; g < NGA; ++g) g2lds16(asrc[g] + k0, a + (wave + g * NW) * 1024);
+#pragma unroll
+    for (int g = 0; g < NGB; ++g) g2lds16(bsrc[g] + k0, b + (wave + g * NW) * 1024);
+    if constexpr (PRO == PRO_MASK) {
+      if (wave < MASK_GROUPS) g2lds4(msrc + (k0 >> 5), mk + wave * 256);
+    }
+  };
+
+  f32x4 acc[FI][FJ];
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int fr = lane & 15, fq = lane >> 4;
+  const int nk = (int)(K / BK);
+
+  // Multiply one staged K-step; the next stage's load groups are issued one A and one
+  // B group per MFMA step, spread over the matrix-instruction stream.
+  auto compute = [&](const unsigned char* abase, const unsigned char* bbase, const unsigned char* mbase,
+                     unsigned char* na, unsigned char* nb, unsigned char* nm, int64_t nk0, bool load_next) {
+    uint2 mw[FJ];
+    if constexpr (PRO == PRO_MASK) {
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) {
+        const int r = wn * SN + j * 16 + fr;
+        mw[j] = *reinterpret_cast<const uint2*>(mbase + r * 8);
+      }
+      if (load_next && wave < MASK_GROUPS) g2lds4(msrc + (nk0 >> 5), nm + wave * 256);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int c = 4 * ks + fq;
+      bf16x8 bfr[FJ];
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) {
+        const int r = wn * SN + j * 16 + fr;
+        if constexpr (PRO == PRO_MASK) {
+          u32x4 v = *reinterpret_cast<const u32x4*>(bbase + r * ROWB + 16 * swz(r, c));
+          const uint32_t word = ks ? mw[j].y : mw[j].x;
+          const uint32_t bits = word >> (8 * fq);
+          v[0] = keep_pair(v[0], bits, 0);
+          v[1] = keep_pair(v[1], bits, 1);
+          v[2] = keep_pair(v[2], bits, 2);
+          v[3] = keep_pair(v[3], bits, 3);
+          bfr[j] = __builtin_bit_cast(bf16x8, v);
+        } else {
+          bfr[j] = *reinterpret_cast<const bf16x8*>(bbase + r * ROWB + 16 * swz(r, c));
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < FI; ++i) {
+        const int step = ks * FI + i;
+        if (load_next) {
+          if (step < NGA) g2lds16(asrc[step] + nk0, na + (wave + step * NW) * 1024);
+          if (step < NGB) g2lds16(bsrc[step] + nk0, nb + (wave + step * NW) * 1024);
+        }
+        const int r = wm * SM + i * 16 + fr;
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(abase + r * ROWB + 16 * swz(r, c));
+        __builtin_amdgcn_s_setprio(1);   // keep the matrix pipe fed ahead of the other wave's memory work
+#pragma unroll
+        for (int j = 0; j < FJ; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_s_setprio(0);
+      }
+    }
+  };
+
+  issue_all(sA0, sB0, sM0, 0);
+  __builtin_amdgcn_s_waitcnt(0);   // the staged tiles have landed in LDS
+  __syncthreads();
+  // two K-steps per trip (stage 0, then stage 1)
+  for (int kt = 0; kt < nk; kt += 2) {
+    compute(sA0, sB0, sM0, sA1, sB1, sM1, (int64_t)(kt + 1) * BK, kt + 1 < nk);
+    __builtin_amdgcn_s_waitcnt(0);   // next stage landed in LDS
+    __syncthreads();
+    if (kt + 1 < nk) {
+      compute(sA1, sB1, sM1, sA0, sB0, sM0, (int64_t)(kt + 2) * BK, kt + 2 < nk);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  }
+
+  // epilogue: lane holds 4 consecutive o for one t in each 16x16 block
+  const bool vec_ok = ((ldy & 3) == 0);
+#pragma unroll
+  for (int i = 0; i < FI; ++i) {
+    const int64_t ob = o0 + wm * SM + i * 16 + 4 * fq;
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) {
+      const int64_t t = t0 + wn * SN + j * 16 + fr;
+      if (t >= T) continue;
+      float* yp = y + t * ldy + ob;
+      if (vec_ok && ob + 4 <= O) {
+        float4 cur = accumulate ? *reinterpret_cast<float4*>(yp) : make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4*>(yp) =
+            make_float4(cur.x + acc[i][j][0], cur.y + acc[i][j][1], cur.z + acc[i][j][2], cur.w + acc[i][j][3]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (ob + r < O) yp[r] = accumulate ? yp[r] + acc[i][j][r] : acc[i][j][r];
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int PRO>
+hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
+  const int tiles_m = (int)((a.o + BM - 1) / BM), tiles_n = (int)((a.t + BN - 1) / BN);
+  const int64_t ntiles = (int64_t)tiles_m * tiles_n;
+  if (ntiles == 0) return hipSuccess;
+  auto kern = k_gemm_lds<BM, BN, WM, WN, PRO>;
+  kern<<<dim3((unsigned)ntiles), dim3(64 * WM * WN), 0, s>>>(
+      (const uint16_t*)a.w, a.ldw, a.x, a.ldx, a.x_mask, a.t, a.o, a.k, a.y, a.ldy, a.accumulate, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+namespace nml {
+
+bool gemm_lds_eligible(const GemmArgs& a, bool any_size) {
+  if (a.w_fp8 || a.w_scale != nullptr) return false;
+  if (a.prologue != PRO_NONE && a.prologue != PRO_MASK) return false;
+  if (a.k % BK != 0 || a.k == 0) return false;
+  if ((a.ldw % 8) || (a.ldx % 8)) return false;
+  // enough tiles to fill the machine with 256x256 tiles
+  return any_size || ((a.o + 255) / 256) * ((a.t + 255) / 256) >= 128;
+}
+
+hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t s) {
+  if (a.prologue == PRO_MASK) return launch_cfg<256, 256, 4, 2, PRO_MASK>(a, s);
+  return launch_cfg<256, 256, 4, 2, PRO_NONE>(a, s);
+}
+
+}  // namespace nml

@@ -34,6 +34,9 @@ struct GemmArgs {
   uint32_t* mask_out;     // PRO_SELECT: optional mask export
 };
 hipError_t launch_gemm_dense(const GemmArgs& a, hipStream_t s);
+// direct-to-LDS variant for large PRO_NONE / PRO_MASK problems with K % 64 == 0
+bool gemm_lds_eligible(const GemmArgs& a, bool any_size);
+hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t s);
 
 // 2:4 sparse-operand GEMM on the gfx950 sparse matrix instructions.  The sparse
 // operand is W (values [O][kc/2], 2-bit meta [O][ceil(kc/8)]) over a (possibly lowered)

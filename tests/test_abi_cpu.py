@@ -118,7 +118,7 @@ def test_spmm_validation():
     a = spmm_args(t=64, k=4096)
     assert S.nm_spmm_workspace_size(a) == 64 * 2048 * 2 + 64 * 512 + 64
     a = spmm_args(t=64, k=4096, n=8, m=16)
-    assert S.nm_spmm_workspace_size(a) == 64 * 128 * 4
+    assert S.nm_spmm_workspace_size(a) == 64 * 4096 * 2
 
 
 def test_hybrid_validation():

@@ -207,7 +207,7 @@ def run_act(x, w, n, m, route=None, w8=None, s8=None, workspace=True, accumulate
 
 
 @pytest.mark.parametrize("n,m", [(8, 16), (16, 32), (4, 8), (2, 4), (1, 4), (6, 8)])
-@pytest.mark.parametrize("route", ["fused", "mask"])
+@pytest.mark.parametrize("route", ["fused", "mask", "sx"])
 @pytest.mark.parametrize("t,o,k", [(300, 200, 1024), (17, 520, 1056), (513, 264, 2048)])
 def test_spmm_act_dynamic(n, m, route, t, o, k):
     print(f"spmm act n={n} m={m} route={route} t={t} o={o} k={k}", flush=True)
@@ -220,6 +220,49 @@ def test_spmm_act_dynamic(n, m, route, t, o, k):
     sx, keep = O.sparsify(x, n, m)
     assert (mask == O.pack_mask(keep)).all()
     check_gemm(y, O.gemm(sx, w), sx, w, label=f"act {n}:{m} {route}")
+
+
+@pytest.mark.parametrize("kernel", ["lds", "regs"])
+@pytest.mark.parametrize("t,o,k", [(1000, 600, 1024), (257, 300, 640), (64, 2000, 2048)])
+def test_spmm_act_masked_kernels(kernel, t, o, k):
+    """Two-pass route (nm_sparsify mask + ACT_MASKED) on both product kernels, ragged
+    tiles in T and O."""
+    print(f"masked kernel={kernel} t={t} o={o} k={k}", flush=True)
+    rng = np.random.default_rng(t + o)
+    x = synth.student_t_bf16(rng, (t, k), 4.0, 0.5)
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    xd, wdv = dev(x), dev(w)
+    mask = empty((t, k // 32), np.uint32)
+    S.nm_sparsify(xd, 8, 16, None, mask)
+    y = empty((t, o), np.float32, fill=float("nan"))
+    a = S.make_spmm_args(S.NM_ACT_MASKED, t, o, k, xd, wdv, y, n=8, m=16, x_meta=mask)
+    old = os.environ.get("NM_GEMM")
+    os.environ["NM_GEMM"] = kernel
+    try:
+        S.nm_spmm(a)
+        sync()
+    finally:
+        if old is None:
+            os.environ.pop("NM_GEMM", None)
+        else:
+            os.environ["NM_GEMM"] = old
+    sx, keep = O.sparsify(x, 8, 16)
+    assert (host(mask, np.uint32) == O.pack_mask(keep)).all()
+    check_gemm(host(y, np.float32), O.gemm(sx, w), sx, w, label=f"masked {kernel}")
+    # the same kernel with X already sparsified (no mask)
+    y2 = empty((t, o), np.float32, fill=float("nan"))
+    sxd = dev(sx)
+    a2 = S.make_spmm_args(S.NM_ACT_MASKED, t, o, k, sxd, wdv, y2, n=8, m=16, x_meta=mask)
+    os.environ["NM_GEMM"] = kernel
+    try:
+        S.nm_spmm(a2)
+        sync()
+    finally:
+        if old is None:
+            os.environ.pop("NM_GEMM", None)
+        else:
+            os.environ["NM_GEMM"] = old
+    check_gemm(host(y2, np.float32), O.gemm(sx, w), sx, w, label=f"masked presparsified {kernel}")
 
 
 def test_spmm_act_2of4_layer():
@@ -262,7 +305,7 @@ def test_spmm_act_accumulate_and_fp8():
     w = synth.normal_bf16(rng, (o, k), 0.02)
     q, s = synth.fp8_e4m3_quantize_rows(w)
     y0 = rng.standard_normal((t, o)).astype(np.float32)
-    for route in ("fused", "mask"):
+    for route in ("fused", "mask", "sx"):
         y, _ = run_act(x, None, 16, 32, route=route, w8=q, s8=s)
         sx, _ = O.sparsify(x, 16, 32)
         wdeq = O.fp8_e4m3_to_f64(q) * s[:, None].astype(np.float64)
@@ -285,7 +328,7 @@ def test_fp8_decode_all_codes():
     assert (y[0].astype(np.float64) == O.fp8_e4m3_to_f64(codes)).all()
 
 
-@pytest.mark.parametrize("route", ["fused", "mask"])
+@pytest.mark.parametrize("route", ["fused", "mask", "sx"])
 def test_spmm_act_full_size_sampled(route):
     """8:16 down-projection at 2048 and 8192 tokens; oracle on sampled output rows."""
     print(f"act full route={route}", flush=True)
