@@ -86,6 +86,41 @@ ActRoute act_route(int64_t t) {
 
 int64_t mask_words(int64_t t, int64_t k) { return t * ((k + 31) / 32); }
 
+// Token counts up to this go to the weight-streaming kernel (decode shapes).
+constexpr int64_t kSkinnyMaxT = 128;
+
+bool use_skinny(int64_t t) {
+  const char* e = std::getenv("NM_SKINNY");
+  if (e != nullptr && std::strcmp(e, "0") == 0) return false;
+  return t <= kSkinnyMaxT;
+}
+
+nm_status run_skinny(const nml::SkinnyArgs& a, hipStream_t s) {
+  if (nml::skinny_needs_zero(a)) {
+    nm_status st = zero_output(a.y, a.t, a.o, a.ldy, s);
+    if (st != NM_OK) return st;
+  }
+  return hip_status(nml::launch_skinny(a, s));
+}
+
+// Few-token product on a dense activation operand that is already S(X) (g.prologue ==
+// PRO_NONE): up to 32 tokens the weight-streaming kernel, above it the split-K tile
+// kernel (bf16 weights, K % 64 == 0).
+nm_status run_dense_few(const nml::GemmArgs& g, hipStream_t s) {
+  if (g.t > 32 && nml::gemm_lds_small_eligible(g)) {
+    if (nml::gemm_lds_small_splits(g) > 1 && !g.accumulate) {
+      nm_status st = zero_output(g.y, g.t, g.o, g.ldy, s);
+      if (st != NM_OK) return st;
+    }
+    return hip_status(nml::launch_gemm_lds_small(g, s));
+  }
+  nml::SkinnyArgs sk{};
+  sk.w = g.w; sk.ldw = g.ldw; sk.w_scale = g.w_scale; sk.w_kind = g.w_fp8 ? 1 : 0;
+  sk.x = g.x; sk.ldx = g.ldx; sk.loader = nml::XL_PLAIN; sk.t = g.t; sk.o = g.o; sk.k = g.k;
+  sk.y = g.y; sk.ldy = g.ldy; sk.accumulate = g.accumulate;
+  return run_skinny(sk, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -184,8 +219,8 @@ nm_status nm_slide_lift(const void* x, int64_t t, int64_t k, int64_t ldx, int ns
 int64_t nm_spmm_workspace_size(const nm_spmm_args* a) {
   if (a == nullptr || a->t < 0 || a->k < 0) return 0;
   if (a->mode == NM_ACT_DYNAMIC) {
-    if (a->n == 2 && a->m == 4) return a->t * (a->k / 2) * 2 + a->t * ((a->k + 7) / 8) + 64;
-    return a->t * a->k * 2;   // S(X) for the two-pass route (also covers the bitmask)
+    // S(X) for the two-pass routes; also covers the 2:4 compressed X (values + 2-bit meta)
+    return a->t * a->k * 2 + 64;
   }
   if (a->mode == NM_ACT_COMPRESSED) return a->t * a->k * 2;
   return 0;
@@ -255,6 +290,7 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
                                               a->x_meta_fmt == NM_META_2BIT, T, K, a->n, xd, K, s);
         if (e != hipSuccess) return NM_EHIP;
         g.x = xd; g.ldx = K; g.prologue = nml::PRO_NONE;
+        if (use_skinny(T)) return run_dense_few(g, s);
         return hip_status(nml::launch_gemm_dense(g, s));
       }
 
@@ -262,7 +298,18 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
       if (a->mode == NM_ACT_MASKED) {
         g.prologue = a->x_meta != nullptr ? nml::PRO_MASK : nml::PRO_NONE;
         g.x_mask = (const uint32_t*)a->x_meta;
+        if (a->x_meta == nullptr && use_skinny(T)) return run_dense_few(g, s);
         return hip_status(nml::launch_gemm_dense(g, s));
+      }
+
+      // ACT_DYNAMIC, few tokens: select into S(X), then stream the weights
+      if (use_skinny(T) && have_ws) {
+        uint16_t* sx = (uint16_t*)a->workspace;
+        hipError_t e = nml::launch_select(a->m, (const uint16_t*)a->x, T, K, a->ldx, a->n, sx, K, a->x_mask_out,
+                                          nullptr, nullptr, 0, s);
+        if (e != hipSuccess) return NM_EHIP;
+        g.x = sx; g.ldx = K; g.prologue = nml::PRO_NONE;
+        return run_dense_few(g, s);
       }
 
       // ACT_DYNAMIC
@@ -319,6 +366,14 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
       if (!span_ok(O, kc)) return NM_ESHAPE;
       if (T == 0 || O == 0) return NM_OK;
       if (K == 0) return a->accumulate ? NM_OK : zero_output(a->y, T, O, a->ldy, s);
+      if (use_skinny(T)) {
+        nml::SkinnyArgs sk{};
+        sk.w = a->w; sk.w_meta = (const uint8_t*)a->w_meta; sk.w_kind = 2;
+        sk.x = (const uint16_t*)a->x; sk.ldx = a->ldx; sk.ns = ns;
+        sk.loader = a->mode == NM_W_SLIDE ? nml::XL_LIFT : nml::XL_PLAIN;
+        sk.t = T; sk.o = O; sk.k = kc; sk.y = a->y; sk.ldy = a->ldy; sk.accumulate = a->accumulate;
+        return run_skinny(sk, s);
+      }
       nml::SparseArgs sa{};
       sa.w_vals = (const uint16_t*)a->w; sa.w_meta = (const uint8_t*)a->w_meta; sa.kc = kc;
       sa.x = (const uint16_t*)a->x; sa.ldx = a->ldx; sa.ns = ns;
@@ -387,6 +442,31 @@ nm_status nm_hybrid_gemm(const void* x, int64_t t, int64_t ldx, const int32_t* s
   if (t == 0 || o == 0) return NM_OK;
   const hipStream_t s = as_stream(stream);
   if (k_s == 0 && k_d == 0) return accumulate ? NM_OK : zero_output(y, t, o, ldy, s);
+  if (use_skinny(t)) {
+    // two weight streams (2:4 region, dense region) adding into one output
+    if (!accumulate) {
+      nm_status st = zero_output(y, t, o, ldy, s);
+      if (st != NM_OK) return st;
+    }
+    if (k_s > 0) {
+      nml::SkinnyArgs sk{};
+      sk.w = ws_values; sk.w_meta = (const uint8_t*)ws_meta; sk.w_kind = 2;
+      sk.x = (const uint16_t*)x; sk.ldx = ldx; sk.loader = gathered ? nml::XL_GATHER : nml::XL_PLAIN;
+      sk.cols = sparse_cols; sk.t = t; sk.o = o; sk.k = k_s; sk.y = y; sk.ldy = ldy; sk.accumulate = 1;
+      hipError_t e = nml::launch_skinny(sk, s);
+      if (e != hipSuccess) return NM_EHIP;
+    }
+    if (k_d > 0) {
+      nml::SkinnyArgs sk{};
+      sk.w = wd; sk.ldw = ldwd; sk.w_kind = 0;
+      sk.x = (const uint16_t*)x; sk.ldx = ldx; sk.loader = gathered ? nml::XL_GATHER : nml::XL_PLAIN;
+      sk.cols = dense_cols; sk.col_base = gathered ? 0 : k_s;
+      sk.t = t; sk.o = o; sk.k = k_d; sk.y = y; sk.ldy = ldy; sk.accumulate = 1;
+      hipError_t e = nml::launch_skinny(sk, s);
+      if (e != hipSuccess) return NM_EHIP;
+    }
+    return NM_OK;
+  }
   nml::SparseArgs sa{};
   sa.w_vals = (const uint16_t*)ws_values; sa.w_meta = (const uint8_t*)ws_meta; sa.kc = k_s;
   sa.x = (const uint16_t*)x; sa.ldx = ldx; sa.loader = gathered ? nml::XL_GATHER : nml::XL_PLAIN;

@@ -61,7 +61,7 @@ template <int BM, int BN, int WM, int WN, int PRO>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
     const uint16_t* __restrict__ w, int64_t ldw, const uint16_t* __restrict__ x, int64_t ldx,
     const uint32_t* __restrict__ xmask, int64_t T, int64_t O, int64_t K, float* __restrict__ y,
-    int64_t ldy, int accumulate, int tiles_m, int tiles_n) {
+    int64_t ldy, int accumulate, int tiles_m, int tiles_n, int64_t kslice, int atomic) {
   constexpr int NW = WM * WN;
   constexpr int SM = BM / WM, SN = BN / WN;       // wave sub-tile (o x t)
   constexpr int FI = SM / 16, FJ = SN / 16;
@@ -82,9 +82,14 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
 
   // XCD-aware tile order: hardware places workgroup b on XCD b % 8; each XCD takes a
   // contiguous range of tiles, walked t-major inside bands of GROUP o-tiles.
+  // optional split-K: block b handles reduction slice b / ntiles (partial sums added
+  // atomically into Y)
   const int ntiles = tiles_m * tiles_n;
-  int lin = blockIdx.x;
-  if ((ntiles & 7) == 0) lin = (blockIdx.x & 7) * (ntiles >> 3) + (blockIdx.x >> 3);
+  const int kpart = blockIdx.x / ntiles;
+  int lin = blockIdx.x - kpart * ntiles;
+  if ((ntiles & 7) == 0 && gridDim.x == (unsigned)ntiles) lin = (blockIdx.x & 7) * (ntiles >> 3) + (blockIdx.x >> 3);
+  const int64_t kbeg = (int64_t)kpart * kslice;
+  const int64_t kend = (kbeg + kslice < K) ? kbeg + kslice : K;
   constexpr int GROUP = 16;
   const int band = lin / (GROUP * tiles_n);
   const int band_w = min(GROUP, tiles_m - band * GROUP);
@@ -120,6 +125,14 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
       msrc = xmask + t * mwords + (lane & 1);
     }
   }
+  // the slice's K offset is folded into the source addresses
+#pragma unroll
+  for (int g = 0; g < NGA; ++g) asrc[g] += kbeg;
+#pragma unroll
+  for (int g = 0; g < NGB; ++g) bsrc[g] += kbeg;
+  if constexpr (PRO == PRO_MASK) {
+    if (msrc != nullptr) msrc += kbeg >> 5;
+  }
 
   auto issue_all = [&](unsigned char* a, unsigned char* b, unsigned char* mk, int64_t k0) {
 #pragma unroll
@@ -138,7 +151,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
     for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int fr = lane & 15, fq = lane >> 4;
-  const int nk = (int)(K / BK);
+  const int nk = (int)((kend - kbeg) / BK);
 
   // Multiply one staged K-step; the next stage's load groups are issued one A and one
   // B group per MFMA step, spread over the matrix-instruction stream.
@@ -216,7 +229,11 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
       const int64_t t = t0 + wn * SN + j * 16 + fr;
       if (t >= T) continue;
       float* yp = y + t * ldy + ob;
-      if (vec_ok && ob + 4 <= O) {
+      if (atomic) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (ob + r < O) unsafeAtomicAdd(yp + r, acc[i][j][r]);
+      } else if (vec_ok && ob + 4 <= O) {
         float4 cur = accumulate ? *reinterpret_cast<float4*>(yp) : make_float4(0.f, 0.f, 0.f, 0.f);
         *reinterpret_cast<float4*>(yp) =
             make_float4(cur.x + acc[i][j][0], cur.y + acc[i][j][1], cur.z + acc[i][j][2], cur.w + acc[i][j][3]);
@@ -230,13 +247,17 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
 }
 
 template <int BM, int BN, int WM, int WN, int PRO>
-hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
+hipError_t launch_cfg(const GemmArgs& a, hipStream_t s, int64_t splits) {
   const int tiles_m = (int)((a.o + BM - 1) / BM), tiles_n = (int)((a.t + BN - 1) / BN);
   const int64_t ntiles = (int64_t)tiles_m * tiles_n;
   if (ntiles == 0) return hipSuccess;
+  int64_t kslice = ((a.k / BK + splits - 1) / splits) * BK;
+  splits = (a.k + kslice - 1) / kslice;
+  if (ntiles * splits > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   auto kern = k_gemm_lds<BM, BN, WM, WN, PRO>;
-  kern<<<dim3((unsigned)ntiles), dim3(64 * WM * WN), 0, s>>>(
-      (const uint16_t*)a.w, a.ldw, a.x, a.ldx, a.x_mask, a.t, a.o, a.k, a.y, a.ldy, a.accumulate, tiles_m, tiles_n);
+  kern<<<dim3((unsigned)(ntiles * splits)), dim3(64 * WM * WN), 0, s>>>(
+      (const uint16_t*)a.w, a.ldw, a.x, a.ldx, a.x_mask, a.t, a.o, a.k, a.y, a.ldy, a.accumulate, tiles_m, tiles_n,
+      kslice, splits > 1 ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -254,8 +275,30 @@ bool gemm_lds_eligible(const GemmArgs& a, bool any_size) {
 }
 
 hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t s) {
-  if (a.prologue == PRO_MASK) return launch_cfg<256, 256, 4, 2, PRO_MASK>(a, s);
-  return launch_cfg<256, 256, 4, 2, PRO_NONE>(a, s);
+  if (a.prologue == PRO_MASK) return launch_cfg<256, 256, 4, 2, PRO_MASK>(a, s, 1);
+  return launch_cfg<256, 256, 4, 2, PRO_NONE>(a, s, 1);
+}
+
+// Few-token variant: 256 output rows x 64 or 128 tokens per tile, split-K so that there
+// are about 512 workgroups; partial sums go to Y with atomics (Y cleared by the caller).
+int64_t gemm_lds_small_splits(const GemmArgs& a) {
+  const int bn = a.t <= 64 ? 64 : 128;
+  const int64_t tiles = ((a.o + 255) / 256) * ((a.t + bn - 1) / bn);
+  int64_t splits = (512 + tiles - 1) / tiles;
+  const int64_t ksteps = a.k / BK;
+  if (splits > ksteps / 2) splits = ksteps / 2 > 0 ? ksteps / 2 : 1;
+  return splits < 1 ? 1 : splits;
+}
+
+bool gemm_lds_small_eligible(const GemmArgs& a) {
+  return a.prologue == PRO_NONE && !a.w_fp8 && a.w_scale == nullptr && a.k % BK == 0 && a.k > 0 &&
+         (a.ldw % 8) == 0 && (a.ldx % 8) == 0 && a.t <= 128;
+}
+
+hipError_t launch_gemm_lds_small(const GemmArgs& a, hipStream_t s) {
+  const int64_t splits = gemm_lds_small_splits(a);
+  if (a.t <= 64) return launch_cfg<256, 64, 8, 1, PRO_NONE>(a, s, splits);
+  return launch_cfg<256, 128, 4, 2, PRO_NONE>(a, s, splits);
 }
 
 }  // namespace nml

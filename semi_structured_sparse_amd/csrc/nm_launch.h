@@ -37,6 +37,10 @@ hipError_t launch_gemm_dense(const GemmArgs& a, hipStream_t s);
 // direct-to-LDS variant for large PRO_NONE / PRO_MASK problems with K % 64 == 0
 bool gemm_lds_eligible(const GemmArgs& a, bool any_size);
 hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t s);
+// few-token split-K variant (T <= 128, PRO_NONE, bf16); adds atomically when splits > 1
+bool gemm_lds_small_eligible(const GemmArgs& a);
+int64_t gemm_lds_small_splits(const GemmArgs& a);
+hipError_t launch_gemm_lds_small(const GemmArgs& a, hipStream_t s);
 
 // 2:4 sparse-operand GEMM on the gfx950 sparse matrix instructions.  The sparse
 // operand is W (values [O][kc/2], 2-bit meta [O][ceil(kc/8)]) over a (possibly lowered)
@@ -61,6 +65,29 @@ struct SparseArgs {
   int trans_out;          // 0: Y[t][o] with o = sparse-side row; 1: Y[s][d] (X sparse)
 };
 hipError_t launch_gemm_sparse(const SparseArgs& a, hipStream_t s);
+
+// Few-token streaming product (T <= 128).  w_kind: 0 bf16 [o][ldw], 1 fp8 [o][ldw] bytes
+// (+ w_scale), 2 2:4 compressed over k (values [o][k/2], 2-bit meta [o][ceil(k/8)]).
+// Adds into y with atomics when K is split; the caller clears y first when
+// skinny_needs_zero() says so.
+struct SkinnyArgs {
+  const void* w;
+  int64_t ldw;
+  const uint8_t* w_meta;
+  const float* w_scale;
+  int w_kind;
+  const uint16_t* x;
+  int64_t ldx;
+  int loader, ns;
+  const int32_t* cols;
+  int64_t col_base;
+  int64_t t, o, k;
+  float* y;
+  int64_t ldy;
+  int accumulate;
+};
+bool skinny_needs_zero(const SkinnyArgs& a);
+hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t s);
 
 hipError_t launch_hybrid_pack(const uint16_t* w, int64_t o, int64_t k, int64_t ldw, int64_t k_dense,
                               int32_t* sparse_cols, int32_t* dense_cols, uint16_t* ws_values,

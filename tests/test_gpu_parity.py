@@ -265,17 +265,79 @@ def test_spmm_act_masked_kernels(kernel, t, o, k):
     check_gemm(host(y2, np.float32), O.gemm(sx, w), sx, w, label=f"masked presparsified {kernel}")
 
 
+class env_set:
+    """Temporarily set environment variables (the library reads its route overrides
+    per call)."""
+
+    def __init__(self, **kv):
+        self.kv = kv
+        self.old = {}
+
+    def __enter__(self):
+        for k, v in self.kv.items():
+            self.old[k] = os.environ.get(k)
+            os.environ[k] = v
+
+    def __exit__(self, *exc):
+        for k, v in self.old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
 def test_spmm_act_2of4_layer():
-    """Single 2:4 activation-sparse layer (X 64x512, W 512x512): sparse matrix path
-    (compress + SMFMAC with X as the sparse operand) and the fused dense path."""
+    """Single 2:4 activation-sparse layer (X 64x512, W 512x512): the weight-streaming
+    few-token kernel, the sparse matrix path (compress + SMFMAC with X as the sparse
+    operand) and the fused dense path."""
     d = synth.layer_2of4_small()
     x, w = d["x"], d["w"]
     sx, keep = O.sparsify(x, 2, 4)
     ref = O.gemm(sx, w)
-    for ws in (True, False):
-        y, mask = run_act(x, w, 2, 4, workspace=ws)
-        assert (mask == O.pack_mask(keep)).all()
-        check_gemm(y, ref, sx, w, label=f"2:4 layer ws={ws}")
+    for skinny in ("1", "0"):
+        for ws in (True, False):
+            with env_set(NM_SKINNY=skinny):
+                y, mask = run_act(x, w, 2, 4, workspace=ws)
+            assert (mask == O.pack_mask(keep)).all()
+            check_gemm(y, ref, sx, w, label=f"2:4 layer ws={ws} skinny={skinny}")
+
+
+@pytest.mark.parametrize("skinny", ["1", "0"])
+@pytest.mark.parametrize("t", [1, 7, 16, 33, 64, 100, 128])
+@pytest.mark.parametrize("k", [1056, 1024])
+def test_few_token_kernels(skinny, t, k):
+    """Few-token shapes on the weight-streaming kernel, the split-K tile kernel (K a
+    multiple of 64) and the plain tile kernels: 8:16 activations (bf16 and fp8 weights),
+    2:4 and 6:8-lowered weights, ragged O."""
+    print(f"few-token t={t} k={k} skinny={skinny}", flush=True)
+    rng = np.random.default_rng(t)
+    o = 200
+    x = synth.student_t_bf16(rng, (t, k), 4.0, 0.5)
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    with env_set(NM_SKINNY=skinny):
+        y, _ = run_act(x, w, 8, 16)
+        sx, _ = O.sparsify(x, 8, 16)
+        check_gemm(y, O.gemm(sx, w), sx, w, label="8:16 bf16")
+        q, sc = synth.fp8_e4m3_quantize_rows(w)
+        y8, _ = run_act(x, None, 8, 16, w8=q, s8=sc)
+        wdeq = O.fp8_e4m3_to_f64(q) * sc[:, None].astype(np.float64)
+        check_gemm(y8, O.spmm_act_fp8(x, q, sc, 8, 16), sx, wdeq, label="8:16 fp8")
+        v, mt = gpu_compress_2of4(w)
+        yw = empty((t, o), np.float32, fill=float("nan"))
+        a = S.make_spmm_args(S.NM_W_COMPRESSED, t, o, k, dev(x), v, yw, w_meta=mt, w_meta_fmt=S.NM_META_2BIT)
+        S.nm_spmm(a)
+        sync()
+        ws24, _ = O.sparsify(w, 2, 4)
+        check_gemm(host(yw, np.float32), O.gemm(x, ws24), x, ws24, label="w 2:4")
+        k8 = 1024
+        x8 = np.ascontiguousarray(x[:, :k8])
+        vp, mp = slide_pack_gpu(np.ascontiguousarray(w[:, :k8]), 4)
+        ys = empty((t, o), np.float32, fill=float("nan"))
+        a = S.make_spmm_args(S.NM_W_SLIDE, t, o, k8, dev(x8), vp, ys, ns=4, w_meta=mp, w_meta_fmt=S.NM_META_2BIT)
+        S.nm_spmm(a)
+        sync()
+        pr, _ = O.sparsify(np.ascontiguousarray(w[:, :k8]), 6, 8)
+        check_gemm(host(ys, np.float32), O.gemm(x8, pr), x8, pr, label="slide 6:8")
 
 
 def test_spmm_act_compressed_2of4_and_8of16():
