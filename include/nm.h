@@ -153,9 +153,16 @@ typedef enum {
  *   w_kmajor    ACT_DYNAMIC, bf16 W only: the same weights stored K-major [k][o]
  *               (row stride o); used for single-token calls, which then read only the
  *               selected K-rows of W.
- *   workspace   device scratch; with workspace_bytes >= nm_spmm_workspace_size(args)
- *               ACT_DYNAMIC may run select and product as two passes.  Calls sharing a
- *               workspace must be ordered (same stream).
+ *   workspace   device scratch (16-byte aligned).  With workspace_bytes >=
+ *               nm_spmm_workspace_size(args): ACT_DYNAMIC may run select and product as
+ *               two passes (S(x) staged in the workspace), ACT_COMPRESSED stages the
+ *               decompressed x there (required unless n:m = 2:4 with 2BIT metadata), and
+ *               few-token calls (t <= 128) with a small o may split the reduction across
+ *               workgroups, writing fp32 partial sums there that a second kernel adds in
+ *               a fixed order.  With less, the call takes a single-pass route.  Contents
+ *               after the call are unspecified.  Calls sharing a workspace must be
+ *               ordered (same stream).
+ * Results are deterministic: the same call on the same inputs gives the same bits.
  */
 typedef struct {
   int mode;               /* nm_spmm_mode                                          */
@@ -190,7 +197,8 @@ typedef struct {
  */
 nm_status nm_spmm(const nm_spmm_args* args, void* stream);
 
-/* Bytes of workspace that let nm_spmm take its two-pass route (0 if none is used). */
+/* Bytes of workspace for nm_spmm's preferred route with these arguments (0 if it uses
+ * none).  Depends on mode, n, m, ns, t, o, k, w_dtype, w_scale, ldx and x_meta only. */
 int64_t nm_spmm_workspace_size(const nm_spmm_args* args);
 
 /*
@@ -221,15 +229,26 @@ int64_t nm_hybrid_pack_workspace_size(int64_t k);
  *                + sum_{j<K_d} x[t][dense_cols[j]]  * Wd[o][j]
  * with Ws the 2:4 compressed sparse region (sparse matrix instructions) and Wd the dense
  * region (dense matrix instructions).  [SPENSE] 2.A (input split with accumulation).
- * sparse_cols / dense_cols may both be NULL, in which case x is taken as already
- * permuted: columns [0, K_s) are the sparse region and [K_s, K_s+K_d) the dense one.
- * Requires K_s % 4 == 0.
+ * x is bf16 [t][ldx] with ldx >= K_s + K_d.  sparse_cols / dense_cols (as written by
+ * nm_hybrid_pack: a partition of [0, K_s + K_d)) may both be NULL, in which case x is
+ * taken as already permuted: columns [0, K_s) are the sparse region and [K_s, K_s+K_d)
+ * the dense one (then K_s % 8 == 0 when K_d > 0).  Column indices outside
+ * [0, K_s + K_d) are clamped into it.  ws_meta must be 2BIT.  Requires K_s % 4 == 0.
+ * workspace: device scratch (16-byte aligned) of workspace_bytes bytes.  The gathered
+ * form (column lists given) stages the column-permuted x there and requires at least
+ * t * (ceil8(K_s) + ceil8(K_d)) * 2 bytes (NM_EINVAL otherwise);
+ * nm_hybrid_gemm_workspace_size gives the amount for the preferred route.  Contents
+ * after the call are unspecified; calls sharing it must be ordered.
  */
 nm_status nm_hybrid_gemm(const void* x, int64_t t, int64_t ldx, const int32_t* sparse_cols,
                          int64_t k_s, const int32_t* dense_cols, int64_t k_d,
                          const void* ws_values, const void* ws_meta, nm_meta fmt,
                          const void* wd, int64_t ldwd, int64_t o, float* y, int64_t ldy,
-                         int accumulate, void* stream);
+                         int accumulate, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes of nm_hybrid_gemm's preferred route (gathered: column lists given). */
+int64_t nm_hybrid_gemm_workspace_size(int64_t t, int64_t k_s, int64_t k_d, int64_t o,
+                                      int gathered);
 
 #ifdef __cplusplus
 }

@@ -19,7 +19,7 @@ __all__ = [
     "NM_W_COMPRESSED", "NM_W_SLIDE", "NM_ACT_MASKED", "nm_spmm_args", "nm_status_str", "nm_version", "nm_sparsify",
     "nm_compress", "nm_decompress", "nm_lower_slide", "nm_slide_lift", "nm_spmm",
     "nm_spmm_workspace_size", "nm_hybrid_pack", "nm_hybrid_pack_workspace_size", "nm_hybrid_gemm",
-    "lowered_k",
+    "nm_hybrid_gemm_workspace_size", "lowered_k",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnmsparse.so")
@@ -87,7 +87,9 @@ def lib() -> ctypes.CDLL:
     L.nm_hybrid_pack_workspace_size.argtypes = [_i64]
     L.nm_hybrid_gemm.restype = _int
     L.nm_hybrid_gemm.argtypes = [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _int, _vp, _i64, _i64, _vp,
-                                 _i64, _int, _vp]
+                                 _i64, _int, _vp, _i64, _vp]
+    L.nm_hybrid_gemm_workspace_size.restype = _i64
+    L.nm_hybrid_gemm_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _int]
     _LIB = L
     return L
 
@@ -237,13 +239,21 @@ def nm_hybrid_pack_workspace_size(k: int) -> int:
     return int(lib().nm_hybrid_pack_workspace_size(k))
 
 
+def nm_hybrid_gemm_workspace_size(t: int, k_s: int, k_d: int, o: int, gathered: bool) -> int:
+    return int(lib().nm_hybrid_gemm_workspace_size(t, k_s, k_d, o, 1 if gathered else 0))
+
+
 def nm_hybrid_gemm(x, sparse_cols, k_s, dense_cols, k_d, ws_values, ws_meta, fmt, wd, o, y, accumulate=0,
-                   stream=None, *, t=None, ldx=None, ldwd=None, ldy=None, check=True):
+                   stream=None, *, t=None, ldx=None, ldwd=None, ldy=None, workspace=None, workspace_bytes=None,
+                   check=True):
     t = x.shape[0] if t is None else t
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
+            workspace.numel() * workspace.element_size()
     st = lib().nm_hybrid_gemm(_ptr(x), t, _ld(x) if ldx is None else ldx, _ptr(sparse_cols), k_s,
                               _ptr(dense_cols), k_d, _ptr(ws_values), _ptr(ws_meta), fmt, _ptr(wd),
                               _ld(wd) if ldwd is None else ldwd, o, _ptr(y), _ld(y) if ldy is None else ldy,
-                              accumulate, _stream(stream))
+                              accumulate, _ptr(workspace), workspace_bytes, _stream(stream))
     if check:
         _check(st, "nm_hybrid_gemm")
     return st

@@ -86,39 +86,102 @@ ActRoute act_route(int64_t t) {
 
 int64_t mask_words(int64_t t, int64_t k) { return t * ((k + 31) / 32); }
 
-// Token counts up to this go to the weight-streaming kernel (decode shapes).
-constexpr int64_t kSkinnyMaxT = 128;
+// Token counts up to this go to the few-token kernels (decode shapes).
+constexpr int64_t kFewMaxT = 128;
 
-bool use_skinny(int64_t t) {
-  const char* e = std::getenv("NM_SKINNY");
+bool use_few(int64_t t) {
+  const char* e = std::getenv("NM_FEW");   // A/B measurement override ("0": tile kernels only)
   if (e != nullptr && std::strcmp(e, "0") == 0) return false;
-  return t <= kSkinnyMaxT;
+  return t <= kFewMaxT;
 }
 
-nm_status run_skinny(const nml::SkinnyArgs& a, hipStream_t s) {
-  if (nml::skinny_needs_zero(a)) {
-    nm_status st = zero_output(a.y, a.t, a.o, a.ldy, s);
-    if (st != NM_OK) return st;
+inline int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
+
+// Scratch slice [off, bytes) of a workspace, or null / 0 when the workspace ends before off.
+inline float* ws_slice(void* ws, int64_t ws_bytes, int64_t off, int64_t* avail) {
+  if (ws == nullptr || ws_bytes <= off) {
+    *avail = 0;
+    return nullptr;
   }
-  return hip_status(nml::launch_skinny(a, s));
+  *avail = ws_bytes - off;
+  return reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + off);
 }
 
-// Few-token product on a dense activation operand that is already S(X) (g.prologue ==
-// PRO_NONE): up to 32 tokens the weight-streaming kernel, above it the split-K tile
-// kernel (bf16 weights, K % 64 == 0).
-nm_status run_dense_few(const nml::GemmArgs& g, hipStream_t s) {
-  if (g.t > 32 && nml::gemm_lds_small_eligible(g)) {
-    if (nml::gemm_lds_small_splits(g) > 1 && !g.accumulate) {
-      nm_status st = zero_output(g.y, g.t, g.o, g.ldy, s);
-      if (st != NM_OK) return st;
-    }
-    return hip_status(nml::launch_gemm_lds_small(g, s));
+// Few-token product with a dense weight on an activation operand that is already S(X)
+// (g.prologue == PRO_NONE): the weight-streaming kernel, or above 32 tokens the split-K
+// tile kernel for bf16 weights (NM_FEW_ROUTE=stream|tile overrides for A/B measurement).
+bool few_use_tile(const nml::GemmArgs& g) {
+  if (!nml::gemm_lds_small_eligible(g)) return false;
+  const char* e = std::getenv("NM_FEW_ROUTE");
+  if (e != nullptr && std::strcmp(e, "tile") == 0) return true;
+  if (e != nullptr && std::strcmp(e, "stream") == 0) return false;
+  return g.t > 32;
+}
+
+nml::FewArgs few_dense_args(const nml::GemmArgs& g) {
+  nml::FewArgs f{};
+  f.nseg = 1;
+  nml::FewSeg& sg = f.seg[0];
+  sg.w = g.w; sg.ldw = g.ldw; sg.w_kind = g.w_fp8 ? nml::WK_FP8 : nml::WK_BF16;
+  sg.x = g.x; sg.ldx = g.ldx; sg.loader = nml::XL_PLAIN; sg.ns = 2; sg.k = g.k;
+  f.w_scale = g.w_scale; f.t = g.t; f.o = g.o; f.y = g.y; f.ldy = g.ldy; f.accumulate = g.accumulate;
+  return f;
+}
+
+int64_t dense_few_part_bytes(const nml::GemmArgs& g) {
+  return few_use_tile(g) ? nml::gemm_lds_small_part_bytes(g) : nml::few_partial_bytes(few_dense_args(g));
+}
+
+nm_status run_dense_few(const nml::GemmArgs& g, float* part, int64_t part_bytes, hipStream_t s) {
+  if (few_use_tile(g)) return hip_status(nml::launch_gemm_lds_small(g, part, part_bytes, s));
+  return hip_status(nml::launch_few(few_dense_args(g), part, part_bytes, s));
+}
+
+// 2:4 (W_COMPRESSED) or lowered (W_SLIDE) weights, few tokens
+nml::FewArgs few_sparse_args(const nm_spmm_args* a, int64_t kc, int ns) {
+  nml::FewArgs f{};
+  f.nseg = 1;
+  nml::FewSeg& sg = f.seg[0];
+  sg.w = a->w; sg.w_meta = (const uint8_t*)a->w_meta; sg.w_kind = nml::WK_SP24;
+  sg.x = (const uint16_t*)a->x; sg.ldx = a->ldx; sg.ns = ns;
+  sg.loader = a->mode == NM_W_SLIDE ? nml::XL_LIFT : nml::XL_PLAIN; sg.k = kc;
+  f.t = a->t; f.o = a->o; f.y = a->y; f.ldy = a->ldy; f.accumulate = a->accumulate;
+  return f;
+}
+
+// Reduction length of the 2:4 operand of the W_* modes (K, or K' for lowered weights).
+int64_t w_mode_kc(const nm_spmm_args* a) {
+  if (a->mode == NM_W_SLIDE) return (a->k / (2 * a->ns)) * 4 * (a->ns - 1);
+  return a->k;
+}
+
+// Bytes of S(X) / decompressed-X staging at the start of nm_spmm's workspace.
+int64_t spmm_stage_bytes(const nm_spmm_args* a) {
+  if (a->mode == NM_ACT_DYNAMIC) return a->t * a->k * 2 + 64;   // also holds the 2:4 compressed X
+  if (a->mode == NM_ACT_COMPRESSED) return a->t * a->k * 2;
+  return 0;
+}
+
+// Hybrid: column-permuted X staging [t][ldp], dense region at column off1.
+inline int64_t hybrid_off1(int64_t k_s) { return (k_s + 7) / 8 * 8; }
+inline int64_t hybrid_ldp(int64_t k_s, int64_t k_d) { return hybrid_off1(k_s) + (k_d + 7) / 8 * 8; }
+
+nml::FewArgs few_hybrid_args(const uint16_t* x, int64_t ldx, int64_t dbase, int64_t t, int64_t k_s, int64_t k_d,
+                             const void* ws_values, const void* ws_meta, const void* wd, int64_t ldwd, int64_t o,
+                             float* y, int64_t ldy, int accumulate) {
+  nml::FewArgs f{};
+  if (k_s > 0) {
+    nml::FewSeg& sg = f.seg[f.nseg++];
+    sg.w = ws_values; sg.w_meta = (const uint8_t*)ws_meta; sg.w_kind = nml::WK_SP24;
+    sg.x = x; sg.ldx = ldx; sg.loader = nml::XL_PLAIN; sg.ns = 2; sg.k = k_s;
   }
-  nml::SkinnyArgs sk{};
-  sk.w = g.w; sk.ldw = g.ldw; sk.w_scale = g.w_scale; sk.w_kind = g.w_fp8 ? 1 : 0;
-  sk.x = g.x; sk.ldx = g.ldx; sk.loader = nml::XL_PLAIN; sk.t = g.t; sk.o = g.o; sk.k = g.k;
-  sk.y = g.y; sk.ldy = g.ldy; sk.accumulate = g.accumulate;
-  return run_skinny(sk, s);
+  if (k_d > 0) {
+    nml::FewSeg& sg = f.seg[f.nseg++];
+    sg.w = wd; sg.ldw = ldwd; sg.w_kind = nml::WK_BF16;
+    sg.x = x + dbase; sg.ldx = ldx; sg.loader = nml::XL_PLAIN; sg.ns = 2; sg.k = k_d;
+  }
+  f.t = t; f.o = o; f.y = y; f.ldy = ldy; f.accumulate = accumulate;
+  return f;
 }
 
 }  // namespace
@@ -217,13 +280,23 @@ nm_status nm_slide_lift(const void* x, int64_t t, int64_t k, int64_t ldx, int ns
 }
 
 int64_t nm_spmm_workspace_size(const nm_spmm_args* a) {
-  if (a == nullptr || a->t < 0 || a->k < 0) return 0;
-  if (a->mode == NM_ACT_DYNAMIC) {
-    // S(X) for the two-pass routes; also covers the 2:4 compressed X (values + 2-bit meta)
-    return a->t * a->k * 2 + 64;
+  if (a == nullptr || a->t < 0 || a->o < 0 || a->k < 0) return 0;
+  const int64_t stage = spmm_stage_bytes(a);
+  int64_t part = 0;
+  if (use_few(a->t) && a->t > 0 && a->o > 0 && a->k > 0) {
+    if (a->mode == NM_W_COMPRESSED || a->mode == NM_W_SLIDE) {
+      if (a->mode == NM_W_SLIDE && (a->ns < 2 || a->ns > 8 || a->k % (2 * a->ns))) return 0;
+      part = nml::few_partial_bytes(few_sparse_args(a, w_mode_kc(a), a->mode == NM_W_SLIDE ? a->ns : 2));
+    } else if (a->mode == NM_ACT_DYNAMIC || a->mode == NM_ACT_COMPRESSED ||
+               (a->mode == NM_ACT_MASKED && a->x_meta == nullptr)) {
+      nml::GemmArgs g{};
+      g.w = a->w; g.ldw = a->ldw; g.w_fp8 = a->w_dtype == NM_W_FP8E4M3 ? 1 : 0; g.w_scale = a->w_scale;
+      g.t = a->t; g.o = a->o; g.k = a->k; g.prologue = nml::PRO_NONE;
+      g.ldx = a->mode == NM_ACT_MASKED ? a->ldx : a->k;
+      part = dense_few_part_bytes(g);
+    }
   }
-  if (a->mode == NM_ACT_COMPRESSED) return a->t * a->k * 2;
-  return 0;
+  return part > 0 ? align256(stage) + part : stage;
 }
 
 nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
@@ -272,8 +345,11 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
       g.w = a->w; g.ldw = a->ldw; g.w_fp8 = fp8 ? 1 : 0; g.w_scale = a->w_scale;
       g.n = a->n; g.m = a->m; g.t = T; g.o = O; g.k = K;
       g.y = a->y; g.ldy = a->ldy; g.accumulate = a->accumulate;
-      const int64_t ws_need = nm_spmm_workspace_size(a);
-      const bool have_ws = a->workspace != nullptr && a->workspace_bytes >= ws_need;
+      // workspace: [S(X) or decompressed X staging][few-token partial sums]
+      const int64_t stage = spmm_stage_bytes(a);
+      const bool have_ws = a->workspace != nullptr && a->workspace_bytes >= stage;
+      int64_t part_avail = 0;
+      float* part = ws_slice(a->workspace, a->workspace_bytes, stage > 0 ? align256(stage) : 0, &part_avail);
 
       if (a->mode == NM_ACT_COMPRESSED) {
         if (a->n == 2 && a->m == 4 && a->x_meta_fmt == NM_META_2BIT && !fp8 && a->w_scale == nullptr) {
@@ -290,7 +366,7 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
                                               a->x_meta_fmt == NM_META_2BIT, T, K, a->n, xd, K, s);
         if (e != hipSuccess) return NM_EHIP;
         g.x = xd; g.ldx = K; g.prologue = nml::PRO_NONE;
-        if (use_skinny(T)) return run_dense_few(g, s);
+        if (use_few(T)) return run_dense_few(g, part, part_avail, s);
         return hip_status(nml::launch_gemm_dense(g, s));
       }
 
@@ -298,18 +374,18 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
       if (a->mode == NM_ACT_MASKED) {
         g.prologue = a->x_meta != nullptr ? nml::PRO_MASK : nml::PRO_NONE;
         g.x_mask = (const uint32_t*)a->x_meta;
-        if (a->x_meta == nullptr && use_skinny(T)) return run_dense_few(g, s);
+        if (a->x_meta == nullptr && use_few(T)) return run_dense_few(g, part, part_avail, s);
         return hip_status(nml::launch_gemm_dense(g, s));
       }
 
       // ACT_DYNAMIC, few tokens: select into S(X), then stream the weights
-      if (use_skinny(T) && have_ws) {
+      if (use_few(T) && have_ws) {
         uint16_t* sx = (uint16_t*)a->workspace;
         hipError_t e = nml::launch_select(a->m, (const uint16_t*)a->x, T, K, a->ldx, a->n, sx, K, a->x_mask_out,
                                           nullptr, nullptr, 0, s);
         if (e != hipSuccess) return NM_EHIP;
         g.x = sx; g.ldx = K; g.prologue = nml::PRO_NONE;
-        return run_dense_few(g, s);
+        return run_dense_few(g, part, part_avail, s);
       }
 
       // ACT_DYNAMIC
@@ -363,17 +439,13 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
       if ((st = check_bf16(a->x, T, K, a->ldx, true))) return st;
       if (O > 0 && kc > 0 && (a->w == nullptr || a->w_meta == nullptr)) return NM_EINVAL;
       if ((a->w && !aligned16(a->w)) || (a->w_meta && !aligned16(a->w_meta))) return NM_EALIGN;
+      if (a->workspace != nullptr && !aligned16(a->workspace)) return NM_EALIGN;
       if (!span_ok(O, kc)) return NM_ESHAPE;
       if (T == 0 || O == 0) return NM_OK;
       if (K == 0) return a->accumulate ? NM_OK : zero_output(a->y, T, O, a->ldy, s);
-      if (use_skinny(T)) {
-        nml::SkinnyArgs sk{};
-        sk.w = a->w; sk.w_meta = (const uint8_t*)a->w_meta; sk.w_kind = 2;
-        sk.x = (const uint16_t*)a->x; sk.ldx = a->ldx; sk.ns = ns;
-        sk.loader = a->mode == NM_W_SLIDE ? nml::XL_LIFT : nml::XL_PLAIN;
-        sk.t = T; sk.o = O; sk.k = kc; sk.y = a->y; sk.ldy = a->ldy; sk.accumulate = a->accumulate;
-        return run_skinny(sk, s);
-      }
+      if (use_few(T))
+        return hip_status(nml::launch_few(few_sparse_args(a, kc, ns), (float*)a->workspace,
+                                          a->workspace ? a->workspace_bytes : 0, s));
       nml::SparseArgs sa{};
       sa.w_vals = (const uint16_t*)a->w; sa.w_meta = (const uint8_t*)a->w_meta; sa.kc = kc;
       sa.x = (const uint16_t*)a->x; sa.ldx = a->ldx; sa.ns = ns;
@@ -412,17 +484,29 @@ nm_status nm_hybrid_pack(const void* w, int64_t o, int64_t k, int64_t ldw, int64
                                             (uint16_t*)wd, ldwd, workspace, as_stream(stream)));
 }
 
+int64_t nm_hybrid_gemm_workspace_size(int64_t t, int64_t k_s, int64_t k_d, int64_t o, int gathered) {
+  if (t <= 0 || o <= 0 || k_s < 0 || k_d < 0 || (k_s == 0 && k_d == 0)) return 0;
+  const int64_t stage = gathered ? t * hybrid_ldp(k_s, k_d) * 2 : 0;
+  int64_t part = 0;
+  if (use_few(t)) {
+    const int64_t ldp = gathered ? hybrid_ldp(k_s, k_d) : k_s + k_d;
+    part = nml::few_partial_bytes(few_hybrid_args(nullptr, ldp, 0, t, k_s, k_d, nullptr, nullptr, nullptr, k_d, o,
+                                                  nullptr, o, 0));
+  }
+  return part > 0 ? align256(stage) + part : stage;
+}
+
 nm_status nm_hybrid_gemm(const void* x, int64_t t, int64_t ldx, const int32_t* sparse_cols, int64_t k_s,
                          const int32_t* dense_cols, int64_t k_d, const void* ws_values, const void* ws_meta,
                          nm_meta fmt, const void* wd, int64_t ldwd, int64_t o, float* y, int64_t ldy,
-                         int accumulate, void* stream) {
+                         int accumulate, void* workspace, int64_t workspace_bytes, void* stream) {
   if (t < 0 || o < 0 || k_s < 0 || k_d < 0) return NM_ESHAPE;
   if ((k_s % 4) != 0) return NM_ESHAPE;
   if (accumulate != 0 && accumulate != 1) return NM_EINVAL;
   if (fmt != NM_META_2BIT) return (fmt == NM_META_U8) ? NM_EUNSUPPORTED : NM_EINVAL;
   const bool gathered = sparse_cols != nullptr || dense_cols != nullptr;
   if (gathered && ((k_s > 0 && sparse_cols == nullptr) || (k_d > 0 && dense_cols == nullptr))) return NM_EINVAL;
-  const int64_t kx = gathered ? 1 : k_s + k_d;      // columns of x that must exist (gathered: unknown)
+  const int64_t kx = k_s + k_d;      // columns of x (the column lists index into them)
   nm_status st;
   if (x == nullptr && t > 0) return NM_EINVAL;
   if (x != nullptr) {
@@ -439,39 +523,37 @@ nm_status nm_hybrid_gemm(const void* x, int64_t t, int64_t ldx, const int32_t* s
     if (!aligned16(y)) return NM_EALIGN;
   }
   if ((sparse_cols && !aligned16(sparse_cols)) || (dense_cols && !aligned16(dense_cols))) return NM_EALIGN;
+  if (workspace != nullptr && !aligned16(workspace)) return NM_EALIGN;
+  if (workspace_bytes < 0) return NM_EINVAL;
+  // the gathered form stages the column-permuted X in the workspace
+  const int64_t stage = gathered ? t * hybrid_ldp(k_s, k_d) * 2 : 0;
+  if (gathered && t > 0 && o > 0 && (workspace == nullptr || workspace_bytes < stage)) return NM_EINVAL;
   if (t == 0 || o == 0) return NM_OK;
   const hipStream_t s = as_stream(stream);
   if (k_s == 0 && k_d == 0) return accumulate ? NM_OK : zero_output(y, t, o, ldy, s);
-  if (use_skinny(t)) {
-    // two weight streams (2:4 region, dense region) adding into one output
-    if (!accumulate) {
-      nm_status st = zero_output(y, t, o, ldy, s);
-      if (st != NM_OK) return st;
-    }
-    if (k_s > 0) {
-      nml::SkinnyArgs sk{};
-      sk.w = ws_values; sk.w_meta = (const uint8_t*)ws_meta; sk.w_kind = 2;
-      sk.x = (const uint16_t*)x; sk.ldx = ldx; sk.loader = gathered ? nml::XL_GATHER : nml::XL_PLAIN;
-      sk.cols = sparse_cols; sk.t = t; sk.o = o; sk.k = k_s; sk.y = y; sk.ldy = ldy; sk.accumulate = 1;
-      hipError_t e = nml::launch_skinny(sk, s);
-      if (e != hipSuccess) return NM_EHIP;
-    }
-    if (k_d > 0) {
-      nml::SkinnyArgs sk{};
-      sk.w = wd; sk.ldw = ldwd; sk.w_kind = 0;
-      sk.x = (const uint16_t*)x; sk.ldx = ldx; sk.loader = gathered ? nml::XL_GATHER : nml::XL_PLAIN;
-      sk.cols = dense_cols; sk.col_base = gathered ? 0 : k_s;
-      sk.t = t; sk.o = o; sk.k = k_d; sk.y = y; sk.ldy = ldy; sk.accumulate = 1;
-      hipError_t e = nml::launch_skinny(sk, s);
-      if (e != hipSuccess) return NM_EHIP;
-    }
-    return NM_OK;
+
+  const uint16_t* xa = (const uint16_t*)x;
+  int64_t lda = ldx, dbase = k_s;
+  if (gathered) {
+    uint16_t* xp = (uint16_t*)workspace;
+    const int64_t ldp = hybrid_ldp(k_s, k_d);
+    hipError_t e = nml::launch_permute_cols((const uint16_t*)x, t, ldx, kx, sparse_cols, k_s, dense_cols, k_d,
+                                            hybrid_off1(k_s), xp, ldp, s);
+    if (e != hipSuccess) return NM_EHIP;
+    xa = xp; lda = ldp; dbase = hybrid_off1(k_s);
+  }
+  if (use_few(t)) {
+    int64_t avail = 0;
+    float* part = ws_slice(workspace, workspace_bytes, stage > 0 ? align256(stage) : 0, &avail);
+    return hip_status(nml::launch_few(few_hybrid_args(xa, lda, dbase, t, k_s, k_d, ws_values, ws_meta, wd, ldwd, o,
+                                                      y, ldy, accumulate),
+                                      part, avail, s));
   }
   nml::SparseArgs sa{};
   sa.w_vals = (const uint16_t*)ws_values; sa.w_meta = (const uint8_t*)ws_meta; sa.kc = k_s;
-  sa.x = (const uint16_t*)x; sa.ldx = ldx; sa.loader = gathered ? nml::XL_GATHER : nml::XL_PLAIN;
-  sa.cols = sparse_cols; sa.t = t; sa.o = o;
-  sa.wd = (const uint16_t*)wd; sa.ldwd = ldwd; sa.kd = k_d; sa.dcols = dense_cols;
+  sa.x = xa; sa.ldx = lda; sa.loader = nml::XL_PLAIN;
+  sa.t = t; sa.o = o;
+  sa.wd = (const uint16_t*)wd; sa.ldwd = ldwd; sa.kd = k_d; sa.dbase = dbase;
   sa.y = y; sa.ldy = ldy; sa.accumulate = accumulate; sa.trans_out = 0;
   return hip_status(nml::launch_gemm_sparse(sa, s));
 }

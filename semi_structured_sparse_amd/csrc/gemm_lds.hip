@@ -61,7 +61,7 @@ template <int BM, int BN, int WM, int WN, int PRO>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
     const uint16_t* __restrict__ w, int64_t ldw, const uint16_t* __restrict__ x, int64_t ldx,
     const uint32_t* __restrict__ xmask, int64_t T, int64_t O, int64_t K, float* __restrict__ y,
-    int64_t ldy, int accumulate, int tiles_m, int tiles_n, int64_t kslice, int atomic) {
+    int64_t ldy, int accumulate, int tiles_m, int tiles_n, int64_t kslice, float* __restrict__ part) {
   constexpr int NW = WM * WN;
   constexpr int SM = BM / WM, SN = BN / WN;       // wave sub-tile (o x t)
   constexpr int FI = SM / 16, FJ = SN / 16;
@@ -82,8 +82,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
 
   // XCD-aware tile order: hardware places workgroup b on XCD b % 8; each XCD takes a
   // contiguous range of tiles, walked t-major inside bands of GROUP o-tiles.
-  // optional split-K: block b handles reduction slice b / ntiles (partial sums added
-  // atomically into Y)
+  // optional split-K: block b handles reduction slice b / ntiles and writes its fp32
+  // partial tile to part[slice][t][o] (summed in slice order by a second kernel)
   const int ntiles = tiles_m * tiles_n;
   const int kpart = blockIdx.x / ntiles;
   int lin = blockIdx.x - kpart * ntiles;
@@ -229,10 +229,11 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
       const int64_t t = t0 + wn * SN + j * 16 + fr;
       if (t >= T) continue;
       float* yp = y + t * ldy + ob;
-      if (atomic) {
+      if (part != nullptr) {
+        float* pp = part + ((int64_t)kpart * T + t) * O + ob;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (ob + r < O) unsafeAtomicAdd(yp + r, acc[i][j][r]);
+          if (ob + r < O) pp[r] = acc[i][j][r];
       } else if (vec_ok && ob + 4 <= O) {
         float4 cur = accumulate ? *reinterpret_cast<float4*>(yp) : make_float4(0.f, 0.f, 0.f, 0.f);
         *reinterpret_cast<float4*>(yp) =
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
 }
 
 template <int BM, int BN, int WM, int WN, int PRO>
-hipError_t launch_cfg(const GemmArgs& a, hipStream_t s, int64_t splits) {
+hipError_t launch_cfg(const GemmArgs& a, hipStream_t s, int64_t splits, float* part) {
   const int tiles_m = (int)((a.o + BM - 1) / BM), tiles_n = (int)((a.t + BN - 1) / BN);
   const int64_t ntiles = (int64_t)tiles_m * tiles_n;
   if (ntiles == 0) return hipSuccess;
@@ -257,8 +258,10 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s, int64_t splits) {
   auto kern = k_gemm_lds<BM, BN, WM, WN, PRO>;
   kern<<<dim3((unsigned)(ntiles * splits)), dim3(64 * WM * WN), 0, s>>>(
       (const uint16_t*)a.w, a.ldw, a.x, a.ldx, a.x_mask, a.t, a.o, a.k, a.y, a.ldy, a.accumulate, tiles_m, tiles_n,
-      kslice, splits > 1 ? 1 : 0);
-  return hipGetLastError();
+      kslice, splits > 1 ? part : nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  return launch_reduce_parts(part, splits, nullptr, a.t, a.o, a.y, a.ldy, a.accumulate, s);
 }
 
 }  // namespace
@@ -275,13 +278,13 @@ bool gemm_lds_eligible(const GemmArgs& a, bool any_size) {
 }
 
 hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t s) {
-  if (a.prologue == PRO_MASK) return launch_cfg<256, 256, 4, 2, PRO_MASK>(a, s, 1);
-  return launch_cfg<256, 256, 4, 2, PRO_NONE>(a, s, 1);
+  if (a.prologue == PRO_MASK) return launch_cfg<256, 256, 4, 2, PRO_MASK>(a, s, 1, nullptr);
+  return launch_cfg<256, 256, 4, 2, PRO_NONE>(a, s, 1, nullptr);
 }
 
 // Few-token variant: 256 output rows x 64 or 128 tokens per tile, split-K so that there
-// are about 512 workgroups; partial sums go to Y with atomics (Y cleared by the caller).
-int64_t gemm_lds_small_splits(const GemmArgs& a) {
+// are about 512 workgroups; the slices' partial tiles are summed by a second kernel.
+static int64_t small_splits(const GemmArgs& a) {
   const int bn = a.t <= 64 ? 64 : 128;
   const int64_t tiles = ((a.o + 255) / 256) * ((a.t + bn - 1) / bn);
   int64_t splits = (512 + tiles - 1) / tiles;
@@ -295,10 +298,16 @@ bool gemm_lds_small_eligible(const GemmArgs& a) {
          (a.ldw % 8) == 0 && (a.ldx % 8) == 0 && a.t <= 128;
 }
 
-hipError_t launch_gemm_lds_small(const GemmArgs& a, hipStream_t s) {
-  const int64_t splits = gemm_lds_small_splits(a);
-  if (a.t <= 64) return launch_cfg<256, 64, 8, 1, PRO_NONE>(a, s, splits);
-  return launch_cfg<256, 128, 4, 2, PRO_NONE>(a, s, splits);
+int64_t gemm_lds_small_part_bytes(const GemmArgs& a) {
+  const int64_t splits = small_splits(a);
+  return splits > 1 ? splits * a.t * a.o * 4 : 0;
+}
+
+hipError_t launch_gemm_lds_small(const GemmArgs& a, float* part, int64_t part_bytes, hipStream_t s) {
+  int64_t splits = small_splits(a);
+  if (part == nullptr || part_bytes < splits * a.t * a.o * 4) splits = 1;
+  if (a.t <= 64) return launch_cfg<256, 64, 8, 1, PRO_NONE>(a, s, splits, part);
+  return launch_cfg<256, 128, 4, 2, PRO_NONE>(a, s, splits, part);
 }
 
 }  // namespace nml

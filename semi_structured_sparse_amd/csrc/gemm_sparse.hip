@@ -8,11 +8,10 @@
 //   XL_LIFT  : X~ = lift_N(X), never materialised  (SlideSparse page, technical summary
 //              2.B: lowered (2N-2):2N weights need the activations lifted; section 2.A
 //              gives the window geometry: X'[g*4(N-1)+4w+s] = X[g*2N+2w+s])
-//   XL_GATHER: X~[t][j] = X[t][cols[j]]            (hybrid sparse region, SpenseGPT page,
-//              technical summary 2.A/2.B: columns permuted into a contiguous region)
 // An optional second phase contracts a dense region with v_mfma_f32_16x16x32_bf16 into
-// the same accumulators (SpenseGPT input split with accumulation):
-//   Y += X[:, dcols] . Wd^T.
+// the same accumulators (SpenseGPT page, technical summary 2.A: input split with
+// accumulation): Y += X[:, dbase:dbase+kd] . Wd^T, X holding the permuted columns
+// (sparse region first, dense region at column dbase).
 //
 // Operand layouts (verified on gfx950): for the sparse instruction, lane l holds row
 // l%16 of the sparse operand for dense reduction positions [16*(l/16), +16) as 8
@@ -47,8 +46,8 @@ __device__ __forceinline__ uint32_t ld_u16(const uint16_t* p) { return *p; }
 // 32 consecutive reduction positions [kk, kk+32) of X~ row t into 16 dwords.
 template <int LOADER>
 __device__ __forceinline__ void load_x32(const uint16_t* __restrict__ x, int64_t ldx, int64_t t,
-                                         int64_t kk, int64_t kc, int ns, const int32_t* __restrict__ cols,
-                                         int64_t col_base, uint32_t (&r)[16]) {
+                                         int64_t kk, int64_t kc, int ns, int64_t col_base,
+                                         uint32_t (&r)[16]) {
   const uint16_t* rp = x + t * ldx;
   if constexpr (LOADER == XL_PLAIN) {
 #pragma unroll
@@ -83,23 +82,15 @@ __device__ __forceinline__ void load_x32(const uint16_t* __restrict__ x, int64_t
         r[2 * wq] = 0; r[2 * wq + 1] = 0;
       }
     }
-  } else {  // XL_GATHER
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int64_t k0 = kk + 2 * q;
-      const uint32_t lo = (k0 < kc) ? ld_u16(rp + cols[k0]) : 0u;
-      const uint32_t hi = (k0 + 1 < kc) ? ld_u16(rp + cols[k0 + 1]) : 0u;
-      r[q] = lo | (hi << 16);
-    }
   }
 }
 
 template <int BO, int BT, int WO, int WT, int LOADER>
 __global__ __launch_bounds__(64 * WO * WT) void k_gemm_sparse(
     const uint16_t* __restrict__ wv, const uint8_t* __restrict__ wm, int64_t kc,
-    const uint16_t* __restrict__ x, int64_t ldx, int ns, const int32_t* __restrict__ cols,
+    const uint16_t* __restrict__ x, int64_t ldx, int ns,
     int64_t T, int64_t O, const uint16_t* __restrict__ wd, int64_t ldwd, int64_t kd,
-    const int32_t* __restrict__ dcols, float* __restrict__ y, int64_t ldy, int accumulate,
+    int64_t dbase, float* __restrict__ y, int64_t ldy, int accumulate,
     int trans_out, int tiles_o, int tiles_t) {
   constexpr int NTH = 64 * WO * WT;
   constexpr int RPP = NTH / 2;
@@ -178,7 +169,7 @@ __global__ __launch_bounds__(64 * WO * WT) void k_gemm_sparse(
         const int64_t t = t0 + lrow + p * RPP;
         const int64_t kk = k0 + 32 * lhalf;
         if (t < T && kk < kc) {
-          load_x32<LOADER>(x, ldx, t, kk, kc, ns, cols, 0, rb[p]);
+          load_x32<LOADER>(x, ldx, t, kk, kc, ns, 0, rb[p]);
         } else {
 #pragma unroll
           for (int q = 0; q < 16; ++q) rb[p][q] = 0;
@@ -275,8 +266,7 @@ __global__ __launch_bounds__(64 * WO * WT) void k_gemm_sparse(
         const int64_t t = t0 + lrow + p * RPP;
         const int64_t kk = k0 + 32 * lhalf;
         if (t < T && kk < kd) {
-          if (dcols != nullptr) load_x32<XL_GATHER>(x, ldx, t, kk, kd, ns, dcols, 0, rb[p]);
-          else load_x32<XL_PLAIN>(x, ldx, t, kk, kd, ns, nullptr, kc, rb[p]);
+          load_x32<XL_PLAIN>(x, ldx, t, kk, kd, ns, dbase, rb[p]);
         } else {
 #pragma unroll
           for (int q = 0; q < 16; ++q) rb[p][q] = 0;
@@ -373,7 +363,7 @@ hipError_t launch_cfg(const nml::SparseArgs& a, hipStream_t s) {
     attr_set = true;
   }
   kern<<<dim3((unsigned)ntiles), dim3(64 * WO * WT), lds, s>>>(
-      a.w_vals, a.w_meta, a.kc, a.x, a.ldx, a.ns, a.cols, a.t, a.o, a.wd, a.ldwd, a.kd, a.dcols,
+      a.w_vals, a.w_meta, a.kc, a.x, a.ldx, a.ns, a.t, a.o, a.wd, a.ldwd, a.kd, a.dbase,
       a.y, a.ldy, a.accumulate, a.trans_out, tiles_o, tiles_t);
   return hipGetLastError();
 }
@@ -393,7 +383,6 @@ hipError_t launch_gemm_sparse(const SparseArgs& a, hipStream_t s) {
   switch (a.loader) {
     case XL_PLAIN: return launch_pick<XL_PLAIN>(a, s);
     case XL_LIFT: return launch_pick<XL_LIFT>(a, s);
-    case XL_GATHER: return launch_pick<XL_GATHER>(a, s);
   }
   return hipErrorInvalidValue;
 }

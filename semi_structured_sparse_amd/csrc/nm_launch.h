@@ -37,15 +37,17 @@ hipError_t launch_gemm_dense(const GemmArgs& a, hipStream_t s);
 // direct-to-LDS variant for large PRO_NONE / PRO_MASK problems with K % 64 == 0
 bool gemm_lds_eligible(const GemmArgs& a, bool any_size);
 hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t s);
-// few-token split-K variant (T <= 128, PRO_NONE, bf16); adds atomically when splits > 1
+// few-token split-K variant (T <= 128, PRO_NONE, bf16): with part (scratch of at least
+// gemm_lds_small_part_bytes(a) bytes) the K slices write fp32 partial tiles that a second
+// kernel sums in slice order; without it, one slice.
 bool gemm_lds_small_eligible(const GemmArgs& a);
-int64_t gemm_lds_small_splits(const GemmArgs& a);
-hipError_t launch_gemm_lds_small(const GemmArgs& a, hipStream_t s);
+int64_t gemm_lds_small_part_bytes(const GemmArgs& a);
+hipError_t launch_gemm_lds_small(const GemmArgs& a, float* part, int64_t part_bytes, hipStream_t s);
 
 // 2:4 sparse-operand GEMM on the gfx950 sparse matrix instructions.  The sparse
 // operand is W (values [O][kc/2], 2-bit meta [O][ceil(kc/8)]) over a (possibly lowered)
-// reduction length kc; the dense operand is X, read through one of three loaders.
-enum XLoader { XL_PLAIN = 0, XL_LIFT = 1, XL_GATHER = 2 };
+// reduction length kc; the dense operand is X, read plainly or lifted.
+enum XLoader { XL_PLAIN = 0, XL_LIFT = 1 };
 struct SparseArgs {
   const uint16_t* w_vals;
   const uint8_t* w_meta;  // 2-bit
@@ -53,12 +55,11 @@ struct SparseArgs {
   const uint16_t* x;
   int64_t ldx;
   int loader, ns;
-  const int32_t* cols;    // XL_GATHER: x column of each reduction index
   int64_t t, o;
   // optional dense second phase (hybrid): Y += Xd . Wd^T
   const uint16_t* wd;
   int64_t ldwd, kd;
-  const int32_t* dcols;   // x column of each dense reduction index (null: kc + j)
+  int64_t dbase;          // x column of the first dense reduction index (multiple of 8)
   float* y;
   int64_t ldy;
   int accumulate;
@@ -66,28 +67,41 @@ struct SparseArgs {
 };
 hipError_t launch_gemm_sparse(const SparseArgs& a, hipStream_t s);
 
-// Few-token streaming product (T <= 128).  w_kind: 0 bf16 [o][ldw], 1 fp8 [o][ldw] bytes
-// (+ w_scale), 2 2:4 compressed over k (values [o][k/2], 2-bit meta [o][ceil(k/8)]).
-// Adds into y with atomics when K is split; the caller clears y first when
-// skinny_needs_zero() says so.
-struct SkinnyArgs {
-  const void* w;
+// Few-token streaming product (T <= 128): one or two weight segments summed into one
+// accumulator, then scaled (w_scale, per output row) and written or added to y.
+enum WKind { WK_BF16 = 0, WK_FP8 = 1, WK_SP24 = 2 };
+struct FewSeg {
+  const void* w;          // WK_BF16 [o][ldw] bf16, WK_FP8 [o][ldw] bytes, WK_SP24 values [o][k/2]
   int64_t ldw;
-  const uint8_t* w_meta;
-  const float* w_scale;
+  const uint8_t* w_meta;  // WK_SP24: 2-bit metadata [o][ceil(k/8)]
   int w_kind;
-  const uint16_t* x;
+  const uint16_t* x;      // X rows of this segment (first column of the segment)
   int64_t ldx;
-  int loader, ns;
-  const int32_t* cols;
-  int64_t col_base;
-  int64_t t, o, k;
+  int loader, ns;         // XL_PLAIN or XL_LIFT (lowered (2ns-2):2ns weights)
+  int64_t k;              // reduction length in X~ coordinates (lifted for XL_LIFT)
+};
+struct FewArgs {
+  FewSeg seg[2];
+  int nseg;
+  const float* w_scale;   // [o] or null
+  int64_t t, o;
   float* y;
   int64_t ldy;
   int accumulate;
 };
-bool skinny_needs_zero(const SkinnyArgs& a);
-hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t s);
+// Scratch bytes of fp32 partial sums the preferred launch uses (0: single pass).
+int64_t few_partial_bytes(const FewArgs& a);
+// part: scratch of part_bytes bytes or null; with less than few_partial_bytes(a) the
+// product runs as a single pass (fewer workgroups when o is small).
+hipError_t launch_few(const FewArgs& a, float* part, int64_t part_bytes, hipStream_t s);
+// y[t][o] (=|+=) w_scale[o] * sum_{s < splits} part[s][t][o]   (part rows have stride o)
+hipError_t launch_reduce_parts(const float* part, int64_t splits, const float* w_scale, int64_t t, int64_t o,
+                               float* y, int64_t ldy, int accumulate, hipStream_t s);
+// xo[t][j] = x[t][c0[j]] (j < k0), xo[t][off1 + j] = x[t][c1[j]] (j < k1); indices
+// clamped to [0, kx)
+hipError_t launch_permute_cols(const uint16_t* x, int64_t t, int64_t ldx, int64_t kx, const int32_t* c0, int64_t k0,
+                               const int32_t* c1, int64_t k1, int64_t off1, uint16_t* xo, int64_t ldo,
+                               hipStream_t s);
 
 hipError_t launch_hybrid_pack(const uint16_t* w, int64_t o, int64_t k, int64_t ldw, int64_t k_dense,
                               int32_t* sparse_cols, int32_t* dense_cols, uint16_t* ws_values,

@@ -119,6 +119,15 @@ def test_spmm_validation():
     assert S.nm_spmm_workspace_size(a) >= 64 * 2048 * 2 + 64 * 512
     a = spmm_args(t=64, k=4096, n=8, m=16)
     assert S.nm_spmm_workspace_size(a) >= 64 * 4096 * 2
+    # few tokens, few output rows: the reduction is split across workgroups and the
+    # partial sums need scratch; many output rows need none
+    a = spmm_args(mode=S.NM_W_COMPRESSED, t=4, o=64, k=4096, w_meta=P, w_meta_fmt=S.NM_META_2BIT)
+    assert S.nm_spmm_workspace_size(a) >= 2 * 4 * 64 * 4
+    a = spmm_args(mode=S.NM_W_COMPRESSED, t=4, o=8192, k=4096, w_meta=P, w_meta_fmt=S.NM_META_2BIT, ldy=8192)
+    assert S.nm_spmm_workspace_size(a) == 0
+    a = spmm_args(mode=S.NM_W_COMPRESSED, t=4, o=8, k=16, w_meta=P, w_meta_fmt=S.NM_META_2BIT,
+                  workspace=MIS, workspace_bytes=1 << 20)
+    assert f(a) == S.NM_EALIGN
 
 
 def test_hybrid_validation():
@@ -129,6 +138,17 @@ def test_hybrid_validation():
     assert g(P, None, 12, None, 4, Q, Q, S.NM_META_2BIT, Q, 8, P, t=4, ldx=16, ldwd=8, ldy=8) == S.NM_EALIGN
     assert g(P, P, 8, P, 8, None, Q, S.NM_META_2BIT, Q, 8, P, t=4, ldx=16, ldwd=8, ldy=8) == S.NM_EINVAL
     assert g(P, P, 8, P, 8, Q, Q, S.NM_META_2BIT, Q, 8, None, t=4, ldx=16, ldwd=8, ldy=8) == S.NM_EINVAL
+    # gathered form: the permuted-X staging must fit in the workspace
+    assert g(P, P, 8, P, 8, Q, Q, S.NM_META_2BIT, Q, 8, P, t=4, ldx=16, ldwd=8, ldy=8) == S.NM_EINVAL
+    assert g(P, P, 8, P, 8, Q, Q, S.NM_META_2BIT, Q, 8, P, t=4, ldx=16, ldwd=8, ldy=8, workspace=Q,
+             workspace_bytes=4 * 16 * 2 - 1) == S.NM_EINVAL
+    assert g(P, P, 8, P, 8, Q, Q, S.NM_META_2BIT, Q, 8, P, t=4, ldx=16, ldwd=8, ldy=8, workspace=MIS,
+             workspace_bytes=1 << 20) == S.NM_EALIGN
+    assert g(P, P, 8, P, 8, Q, Q, S.NM_META_2BIT, Q, 8, P, t=4, ldx=8, ldwd=8, ldy=8, workspace=Q,
+             workspace_bytes=1 << 20) == S.NM_ESHAPE                                      # ldx < k_s + k_d
+    assert S.nm_hybrid_gemm_workspace_size(4, 8, 8, 8, True) >= 4 * 16 * 2
+    assert S.nm_hybrid_gemm_workspace_size(4, 8, 8, 14336, False) == 0
+    assert S.nm_hybrid_gemm_workspace_size(0, 8, 8, 8, True) == 0
     p = lambda *a, **kw: S.nm_hybrid_pack(*a, check=False, stream=0, **kw)  # noqa: E731
     assert S.nm_hybrid_pack_workspace_size(4096) >= 4096 * 12
     assert p(P, 20, P, P, Q, Q, S.NM_META_2BIT, Q, P, o=8, k=16, ldw=16, ldwd=16, workspace_bytes=1 << 20) == S.NM_ESHAPE

@@ -294,50 +294,109 @@ def test_spmm_act_2of4_layer():
     x, w = d["x"], d["w"]
     sx, keep = O.sparsify(x, 2, 4)
     ref = O.gemm(sx, w)
-    for skinny in ("1", "0"):
+    for few in ("1", "0"):
         for ws in (True, False):
-            with env_set(NM_SKINNY=skinny):
+            with env_set(NM_FEW=few):
                 y, mask = run_act(x, w, 2, 4, workspace=ws)
             assert (mask == O.pack_mask(keep)).all()
-            check_gemm(y, ref, sx, w, label=f"2:4 layer ws={ws} skinny={skinny}")
+            check_gemm(y, ref, sx, w, label=f"2:4 layer ws={ws} few={few}")
 
 
-@pytest.mark.parametrize("skinny", ["1", "0"])
+# route overrides of the few-token dispatch: weight-streaming kernel, split-K tile kernel
+# (bf16 weights, K % 64 == 0; others fall back to streaming), or the large-T tile kernels
+FEW_ROUTES = {"stream": {"NM_FEW_ROUTE": "stream"}, "tile": {"NM_FEW_ROUTE": "tile"}, "off": {"NM_FEW": "0"}}
+
+
+def run_w(mode, x, v, mt, o, k, ns=2, workspace=True, accumulate=0, y0=None):
+    t = x.shape[0]
+    y = dev(y0.astype(np.float32)) if y0 is not None else empty((t, o), np.float32, fill=float("nan"))
+    a = S.make_spmm_args(mode, t, o, k, dev(x), v, y, ns=ns, w_meta=mt, w_meta_fmt=S.NM_META_2BIT,
+                         accumulate=accumulate)
+    ws = None
+    if workspace:
+        nb = S.nm_spmm_workspace_size(a)
+        ws = empty((max(nb, 16),), np.uint8)
+        a.workspace, a.workspace_bytes = ws.data_ptr(), nb
+    S.nm_spmm(a)
+    sync()
+    return host(y, np.float32)
+
+
+@pytest.mark.parametrize("route", list(FEW_ROUTES))
 @pytest.mark.parametrize("t", [1, 7, 16, 33, 64, 100, 128])
 @pytest.mark.parametrize("k", [1056, 1024])
-def test_few_token_kernels(skinny, t, k):
-    """Few-token shapes on the weight-streaming kernel, the split-K tile kernel (K a
-    multiple of 64) and the plain tile kernels: 8:16 activations (bf16 and fp8 weights),
-    2:4 and 6:8-lowered weights, ragged O."""
-    print(f"few-token t={t} k={k} skinny={skinny}", flush=True)
+def test_few_token_kernels(route, t, k):
+    """Few-token shapes on each route: 8:16 activations (bf16 and fp8 weights), 2:4 and
+    6:8-lowered weights, ragged O (200 rows: the reduction is also split across
+    workgroups and summed by the second pass), with and without a workspace."""
+    print(f"few-token t={t} k={k} route={route}", flush=True)
     rng = np.random.default_rng(t)
     o = 200
     x = synth.student_t_bf16(rng, (t, k), 4.0, 0.5)
     w = synth.normal_bf16(rng, (o, k), 0.02)
-    with env_set(NM_SKINNY=skinny):
-        y, _ = run_act(x, w, 8, 16)
+    with env_set(**FEW_ROUTES[route]):
         sx, _ = O.sparsify(x, 8, 16)
-        check_gemm(y, O.gemm(sx, w), sx, w, label="8:16 bf16")
+        for ws in (True, False):
+            y, _ = run_act(x, w, 8, 16, workspace=ws)
+            check_gemm(y, O.gemm(sx, w), sx, w, label=f"8:16 bf16 ws={ws}")
         q, sc = synth.fp8_e4m3_quantize_rows(w)
         y8, _ = run_act(x, None, 8, 16, w8=q, s8=sc)
         wdeq = O.fp8_e4m3_to_f64(q) * sc[:, None].astype(np.float64)
         check_gemm(y8, O.spmm_act_fp8(x, q, sc, 8, 16), sx, wdeq, label="8:16 fp8")
         v, mt = gpu_compress_2of4(w)
-        yw = empty((t, o), np.float32, fill=float("nan"))
-        a = S.make_spmm_args(S.NM_W_COMPRESSED, t, o, k, dev(x), v, yw, w_meta=mt, w_meta_fmt=S.NM_META_2BIT)
-        S.nm_spmm(a)
-        sync()
         ws24, _ = O.sparsify(w, 2, 4)
-        check_gemm(host(yw, np.float32), O.gemm(x, ws24), x, ws24, label="w 2:4")
+        for ws in (True, False):
+            yw = run_w(S.NM_W_COMPRESSED, x, v, mt, o, k, workspace=ws)
+            check_gemm(yw, O.gemm(x, ws24), x, ws24, label=f"w 2:4 ws={ws}")
         k8 = 1024
         x8 = np.ascontiguousarray(x[:, :k8])
         vp, mp = slide_pack_gpu(np.ascontiguousarray(w[:, :k8]), 4)
-        ys = empty((t, o), np.float32, fill=float("nan"))
-        a = S.make_spmm_args(S.NM_W_SLIDE, t, o, k8, dev(x8), vp, ys, ns=4, w_meta=mp, w_meta_fmt=S.NM_META_2BIT)
-        S.nm_spmm(a)
-        sync()
+        ys = run_w(S.NM_W_SLIDE, x8, vp, mp, o, k8, ns=4)
         pr, _ = O.sparsify(np.ascontiguousarray(w[:, :k8]), 6, 8)
-        check_gemm(host(ys, np.float32), O.gemm(x8, pr), x8, pr, label="slide 6:8")
+        check_gemm(ys, O.gemm(x8, pr), x8, pr, label="slide 6:8")
+
+
+@pytest.mark.parametrize("wpb,splits", [("4", "0"), ("8", "0"), ("16", "0"), ("16", "3"), ("4", "7")])
+@pytest.mark.parametrize("t", [1, 20, 70])
+def test_few_token_partition_overrides(wpb, splits, t):
+    """The weight-streaming kernel under forced in-workgroup wave counts and cross-
+    workgroup splits (every partition of the reduction must give the same result up to
+    rounding), with accumulation into a nonzero Y; then bitwise determinism of a repeat
+    call.  O = 64 (few row blocks), K = 4096."""
+    print(f"few-token partition wpb={wpb} splits={splits} t={t}", flush=True)
+    rng = np.random.default_rng(7 * t + int(wpb))
+    o, k = 64, 4096
+    x = synth.student_t_bf16(rng, (t, k), 4.0, 0.5)
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    y0 = rng.standard_normal((t, o)).astype(np.float32)
+    env = {"NM_FEW_ROUTE": "stream", "NM_FEW_WPB": wpb}
+    if splits != "0":
+        env["NM_FEW_SPLITS"] = splits
+    with env_set(**env):
+        sx, _ = O.sparsify(x, 8, 16)
+        y, _ = run_act(x, w, 8, 16, accumulate=1, y0=y0)
+        check_gemm(y - y0, O.gemm(sx, w), sx, w, label="8:16 accumulate")
+        y_again, _ = run_act(x, w, 8, 16, accumulate=1, y0=y0)
+        assert (y.view(np.uint32) == y_again.view(np.uint32)).all(), "repeat call differs"
+        q, sc = synth.fp8_e4m3_quantize_rows(w)
+        y8, _ = run_act(x, None, 8, 16, w8=q, s8=sc)
+        wdeq = O.fp8_e4m3_to_f64(q) * sc[:, None].astype(np.float64)
+        check_gemm(y8, O.spmm_act_fp8(x, q, sc, 8, 16), sx, wdeq, label="8:16 fp8")
+        v, mt = gpu_compress_2of4(w)
+        ws24, _ = O.sparsify(w, 2, 4)
+        yw = run_w(S.NM_W_COMPRESSED, x, v, mt, o, k, accumulate=1, y0=y0)
+        check_gemm(yw - y0, O.gemm(x, ws24), x, ws24, label="w 2:4 accumulate")
+        vp, mp = slide_pack_gpu(w, 4)
+        ys = run_w(S.NM_W_SLIDE, x, vp, mp, o, k, ns=4)
+        pr, _ = O.sparsify(w, 6, 8)
+        check_gemm(ys, O.gemm(x, pr), x, pr, label="slide 6:8")
+        sc_, dc_, wv, wm, wdd = hybrid_pack_gpu(w, 1024)
+        sync()
+        sp, de, hv, hi, hwd = O.hybrid_pack(w, 1024)
+        wh = w.copy()
+        wh[:, sp] = O.decompress(hv, hi, 2, 4, k - 1024)
+        yh = run_hybrid(x, sc_, k - 1024, dc_, 1024, wv, wm, wdd, o)
+        check_gemm(yh, O.hybrid_gemm(x, sp, de, hv, hi, hwd), x, wh, label="hybrid")
 
 
 def test_spmm_act_compressed_2of4_and_8of16():
@@ -524,6 +583,17 @@ def hybrid_pack_gpu(w, kd, fmt=S.NM_META_2BIT):
     return sc, dc, wv, wm, wdd
 
 
+def run_hybrid(x, sc, ks, dc, kd, wv, wm, wdd, o, ldwd=None, accumulate=0):
+    t = x.shape[0]
+    y = empty((t, o), np.float32, fill=float("nan"))
+    nb = S.nm_hybrid_gemm_workspace_size(t, ks, kd, o, sc is not None or dc is not None)
+    ws = empty((max(nb, 16),), np.uint8)
+    S.nm_hybrid_gemm(dev(x), sc, ks, dc, kd, wv, wm, S.NM_META_2BIT, wdd, o, y, accumulate, ldwd=ldwd,
+                     workspace=ws, workspace_bytes=nb)
+    sync()
+    return host(y, np.float32)
+
+
 @pytest.mark.parametrize("o,k,kd", [(100, 256, 64), (64, 128, 0), (48, 96, 96), (300, 512, 128)])
 def test_hybrid_pack_and_gemm(o, k, kd):
     rng = np.random.default_rng(o + k + kd)
@@ -540,15 +610,14 @@ def test_hybrid_pack_and_gemm(o, k, kd):
     if kd:
         assert (host(dc, np.int32)[:kd] == de).all()
         assert (host(wdd, np.uint16)[:, :kd] == wd).all()
-    y = empty((130, o), np.float32, fill=float("nan"))
-    S.nm_hybrid_gemm(dev(x), sc if ks else None, ks, dc if kd else None, kd, wv, wm, S.NM_META_2BIT,
-                     wdd if kd else None, o, y, ldwd=max(kd, 8))
-    sync()
-    ref = O.hybrid_gemm(x, sp, de, v, i, wd)
     wh = w.copy()
     if ks:
         wh[:, sp] = O.decompress(v, i, 2, 4, ks)
-    check_gemm(host(y, np.float32), ref, x, wh, label="hybrid")
+    for t in (130, 5, 40):
+        xt = np.ascontiguousarray(x[:t])
+        y = run_hybrid(xt, sc if ks else None, ks, dc if kd else None, kd, wv, wm, wdd if kd else None, o,
+                       ldwd=max(kd, 8))
+        check_gemm(y, O.hybrid_gemm(xt, sp, de, v, i, wd), xt, wh, label=f"hybrid t={t}")
 
 
 def test_hybrid_prepermuted_input():
@@ -561,12 +630,16 @@ def test_hybrid_prepermuted_input():
     sync()
     sp, de, v, i, wd = O.hybrid_pack(w, kd)
     xp = np.ascontiguousarray(np.concatenate([x[:, sp], x[:, de]], axis=1))
-    y = empty((70, o), np.float32, fill=float("nan"))
-    S.nm_hybrid_gemm(dev(xp), None, k - kd, None, kd, wv, wm, S.NM_META_2BIT, wdd, o, y, ldwd=max(kd, 8))
-    sync()
     wh = w.copy()
     wh[:, sp] = O.decompress(v, i, 2, 4, k - kd)
-    check_gemm(host(y, np.float32), O.hybrid_gemm(x, sp, de, v, i, wd), x, wh, label="hybrid prepermuted")
+    for t in (70, 3):
+        y = run_hybrid(np.ascontiguousarray(xp[:t]), None, k - kd, None, kd, wv, wm, wdd, o, ldwd=max(kd, 8))
+        check_gemm(y, O.hybrid_gemm(x[:t], sp, de, v, i, wd), x[:t], wh, label=f"hybrid prepermuted t={t}")
+    # the gathered form needs its staging workspace
+    y = empty((3, o), np.float32)
+    st = S.nm_hybrid_gemm(dev(x[:3]), sc, k - kd, dc, kd, wv, wm, S.NM_META_2BIT, wdd, o, y, ldwd=max(kd, 8),
+                          check=False)
+    assert st == S.NM_EINVAL
 
 
 def test_hybrid_full_size_sampled():
@@ -589,11 +662,9 @@ def test_hybrid_full_size_sampled():
     del ws_ref
     for t in (1, 8, 32, 64, 2048):
         x = x_all[:t]
-        y = empty((t, o), np.float32, fill=float("nan"))
-        S.nm_hybrid_gemm(dev(x), sc, k - kd, dc, kd, wv, wm, S.NM_META_2BIT, wdd, o, y)
-        sync()
+        y = run_hybrid(x, sc, k - kd, dc, kd, wv, wm, wdd, o)
         rows = sample_rows(t, 12, seed=t)
-        check_gemm(host(y, np.float32)[rows], O.gemm(x[rows], wh), x[rows], wh, label=f"hybrid full t={t}")
+        check_gemm(y[rows], O.gemm(x[rows], wh), x[rows], wh, label=f"hybrid full t={t}")
 
 
 # ------------------------------------------------------------------ edge cases ---
