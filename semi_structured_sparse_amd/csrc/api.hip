@@ -108,14 +108,13 @@ inline float* ws_slice(void* ws, int64_t ws_bytes, int64_t off, int64_t* avail) 
 }
 
 // Few-token product with a dense weight on an activation operand that is already S(X)
-// (g.prologue == PRO_NONE): the weight-streaming kernel, or above 32 tokens the split-K
-// tile kernel for bf16 weights (NM_FEW_ROUTE=stream|tile overrides for A/B measurement).
+// (g.prologue == PRO_NONE): the weight-streaming kernel.  The split-K tile kernel is kept
+// as an A/B alternative (NM_FEW_ROUTE=tile, bf16 weights): measured on gfx950 at
+// 4096 x 14336 it is slower at 64 tokens (50 vs 41 us) and level at 128.
 bool few_use_tile(const nml::GemmArgs& g) {
   if (!nml::gemm_lds_small_eligible(g)) return false;
   const char* e = std::getenv("NM_FEW_ROUTE");
-  if (e != nullptr && std::strcmp(e, "tile") == 0) return true;
-  if (e != nullptr && std::strcmp(e, "stream") == 0) return false;
-  return g.t > 32;
+  return e != nullptr && std::strcmp(e, "tile") == 0;
 }
 
 nml::FewArgs few_dense_args(const nml::GemmArgs& g) {

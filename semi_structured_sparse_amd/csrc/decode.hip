@@ -43,30 +43,29 @@ __device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t q, uint32_t& lo, uint32
 }
 
 // 8 consecutive reduction positions [k, k+8) of an X~ row (rp = start of the row), zero
-// beyond kend.  k is in X~ coordinates (lifted index space for XL_LIFT).
-template <int XL>
-__device__ __forceinline__ u32x4 load_x8(const uint16_t* __restrict__ rp, int64_t k, int64_t kend, int ns,
-                                         bool row_ok) {
+// beyond kend.  k is in X~ coordinates (lifted index space for XL_LIFT, where window
+// w of group g -- 4 lifted positions -- holds original positions g*2NS + 2w + [0, 4)).
+// CHECKED = false: the caller guarantees [k, k+8) < kend (no bounds tests, no branches).
+template <int XL, int NS, bool CHECKED>
+__device__ __forceinline__ u32x4 load_x8(const uint16_t* __restrict__ rp, int k, int kend) {
   u32x4 r = {0u, 0u, 0u, 0u};
-  if (!row_ok) return r;
   if constexpr (XL == XL_PLAIN) {
-    if (k + 8 <= kend) return *reinterpret_cast<const u32x4*>(rp + k);
+    if (!CHECKED || k + 8 <= kend) return *reinterpret_cast<const u32x4*>(rp + k);
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       if (k + e < kend) r[e >> 1] |= (uint32_t)rp[k + e] << (16 * (e & 1));
     return r;
   } else {
-    // two windows of 4 lifted positions, each 4 consecutive original positions
-    const int wpg = ns - 1;
+    constexpr uint32_t WPG = NS - 1;   // windows per group (compile-time divisor)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int64_t kp = k + 4 * h;
-      if (kp < kend) {
-        const int64_t win = kp >> 2;
-        const int64_t g = win / wpg;
-        const int64_t w = win - g * wpg;
+      const int kp = k + 4 * h;
+      if (!CHECKED || kp < kend) {
+        const uint32_t win = (uint32_t)kp >> 2;
+        const uint32_t g = win / WPG;
+        const uint32_t w = win - g * WPG;
         // 4-byte aligned only: two dword loads
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(rp + g * 2 * ns + 2 * w);
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(rp + g * (2 * NS) + 2 * w);
         r[2 * h] = src[0];
         r[2 * h + 1] = src[1];
       }
@@ -79,200 +78,505 @@ __device__ __forceinline__ u32x4 load_x8(const uint16_t* __restrict__ rp, int64_
 // dense-equivalent)
 template <int WK> struct Chunk { static constexpr int K = (WK == WK_SP24) ? 64 : 32; };
 
-// chunks per pipelined batch: two batches of weight + X fragments live in registers,
-// within 128 VGPRs for 1-2 token blocks (up to 16 waves per workgroup) and 256 above
-constexpr int unroll_for(int tb, int wk) {
-  return wk == WK_SP24 ? (tb == 1 ? 2 : 1) : (tb == 1 ? 4 : tb <= 4 ? 2 : 1);
+// 16-row weight tiles per wave: each X fragment feeds RW matrix instructions, so the X
+// bytes a wave pulls through L1 per weight byte drop from TB to TB/RW (2 TB/RW for 2:4).
+constexpr int rw_for(int tb, int wk) { return tb == 1 ? 1 : tb == 2 ? 2 : tb == 4 ? 4 : 2; }
+
+// chunks per pipelined batch: two batches of weight + X fragments live in registers
+// next to the accumulators, within 128 VGPRs for 1-2 token blocks (up to 16 waves per
+// workgroup) and 256 above
+constexpr int unroll_for(int tb, int rw, int wk) {
+  const int per_chunk = rw * (wk == WK_SP24 ? 5 : 4) + tb * (wk == WK_SP24 ? 8 : 4);
+  const int budget = (tb <= 2 ? 128 : 256) - 48 - 4 * rw * tb - 2 * tb;
+  const int u = budget / (2 * per_chunk);
+  return u < 1 ? 1 : (u > 4 ? 4 : u);
 }
 
-// Stream reduction positions [k0, k1) of one segment for the lane's weight row o_ld into
-// acc (lane holds Y^T rows 4*fq + r of the 16-row block for tokens 16*j + fr).
-template <int TB, int WK, int XL>
-__device__ __forceinline__ void stream_seg(f32x4 (&acc)[TB], const FewSeg& sg, int64_t o_ld, int64_t T,
-                                           int64_t k0, int64_t k1, int lane) {
+// Stream reduction positions [k0, k1) of one segment for the lane's weight rows into acc
+// (lane holds Y^T rows 16*i + 4*fq + r of the block for tokens 16*j + fr).
+//
+// Whole chunks go through a branch-free software pipeline: every load is issued
+// unconditionally (token rows past T read row T-1; their outputs are never stored, and a
+// matrix instruction's output column depends only on its own input column), so the
+// compiler can count outstanding loads exactly and wait only for the batch it is about
+// to multiply.  The ragged end of the part is handled chunk by chunk with checked loads.
+template <int TB, int RW, int WK, int XL, int NS>
+__device__ __forceinline__ void stream_seg(f32x4 (&acc)[RW][TB], const FewSeg& sg, const int64_t (&orow)[RW],
+                                           int64_t T, int k0, int k1, int lane) {
   constexpr int CK = Chunk<WK>::K;
-  constexpr int UNROLL = unroll_for(TB, WK);
+  constexpr int UNROLL = unroll_for(TB, RW, WK);
   const int fr = lane & 15, fq = lane >> 4;
 
   const uint16_t* xrow[TB];
-  bool xok[TB];
 #pragma unroll
   for (int j = 0; j < TB; ++j) {
     const int64_t t = 16 * j + fr;
-    xok[j] = t < T;
-    xrow[j] = sg.x + (xok[j] ? t : 0) * sg.ldx;
+    xrow[j] = sg.x + (t < T ? t : T - 1) * sg.ldx;
   }
-  const int64_t kcv = sg.k / 2;               // compressed row length (2:4)
-  const int64_t mstride = (sg.k + 7) >> 3;    // 2-bit metadata bytes per row
-  const bool vec_sp = (kcv & 7) == 0;         // 16-byte aligned compressed rows
+  const int kcv = (int)(sg.k / 2);            // compressed row length (2:4)
+  const int mstride = (int)((sg.k + 7) >> 3); // 2-bit metadata bytes per row
+  const uint8_t* wrow[RW];                    // start of each weight row (bytes)
+  const uint8_t* mrow[RW];
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    if constexpr (WK == WK_BF16) wrow[i] = reinterpret_cast<const uint8_t*>(sg.w) + orow[i] * sg.ldw * 2;
+    else if constexpr (WK == WK_FP8) wrow[i] = reinterpret_cast<const uint8_t*>(sg.w) + orow[i] * sg.ldw;
+    else wrow[i] = reinterpret_cast<const uint8_t*>(sg.w) + orow[i] * (int64_t)kcv * 2;
+    mrow[i] = (WK == WK_SP24) ? sg.w_meta + orow[i] * (int64_t)mstride : nullptr;
+  }
 
   struct Batch {
-    u32x4 w[UNROLL];
-    uint32_t m[UNROLL];
+    u32x4 w[UNROLL][RW];
+    uint32_t m[UNROLL][RW];
     u32x4 xl[UNROLL][TB];
     u32x4 xh[UNROLL][TB];
   };
-  auto fetch = [&](Batch& bt, int64_t kc) {
+  // unchecked loads of chunk k (the whole chunk lies inside the part)
+  auto load_chunk = [&](Batch& bt, int u, int k) {
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int64_t k = kc + (int64_t)u * CK;
-      bt.m[u] = 0;
+    for (int i = 0; i < RW; ++i) {
       if constexpr (WK == WK_BF16) {
-        const int64_t kk = k + 8 * fq;
-        const uint16_t* rp = reinterpret_cast<const uint16_t*>(sg.w) + o_ld * sg.ldw;
-        if (kk + 8 <= k1) {
-          bt.w[u] = *reinterpret_cast<const u32x4*>(rp + kk);
-        } else {
-          u32x4 v = {0u, 0u, 0u, 0u};
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (kk + e < k1) v[e >> 1] |= (uint32_t)rp[kk + e] << (16 * (e & 1));
-          bt.w[u] = v;
-        }
+        bt.w[u][i] = *reinterpret_cast<const u32x4*>(wrow[i] + 2 * (k + 8 * fq));
       } else if constexpr (WK == WK_FP8) {
-        const int64_t kk = k + 8 * fq;
-        const uint8_t* rp = reinterpret_cast<const uint8_t*>(sg.w) + o_ld * sg.ldw;
-        uint2 q;
-        if (kk + 8 <= k1) {
-          q = *reinterpret_cast<const uint2*>(rp + kk);
-        } else {
-          uint32_t qq[2] = {0u, 0u};
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (kk + e < k1) qq[e >> 2] |= (uint32_t)rp[kk + e] << (8 * (e & 3));
-          q = make_uint2(qq[0], qq[1]);
-        }
-        bt.w[u] = u32x4{q.x, q.y, 0u, 0u};   // widened to bf16 at use
+        const uint2 q = *reinterpret_cast<const uint2*>(wrow[i] + k + 8 * fq);
+        bt.w[u][i] = u32x4{q.x, q.y, 0u, 0u};   // widened to bf16 at use
       } else {
-        // 2:4 compressed: 8 values covering dense positions [k + 16 fq, +16)
-        const int64_t v0 = k / 2 + 8 * fq;
-        const uint16_t* vp = reinterpret_cast<const uint16_t*>(sg.w) + o_ld * kcv + v0;
-        const uint8_t* mp = sg.w_meta + o_ld * mstride + (v0 >> 2);
-        if (vec_sp && v0 + 8 <= kcv && k + 16 * fq + 16 <= k1) {
-          bt.w[u] = *reinterpret_cast<const u32x4*>(vp);
-          bt.m[u] = (uint32_t)mp[0] | ((uint32_t)mp[1] << 8);
-        } else {
-          u32x4 v = {0u, 0u, 0u, 0u};
-          uint32_t m = 0;
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (k + 16 * fq + 2 * e < k1 && v0 + e < kcv) v[e >> 1] |= (uint32_t)vp[e] << (16 * (e & 1));
-#pragma unroll
-          for (int bq = 0; bq < 2; ++bq)
-            if ((v0 >> 2) + bq < mstride) m |= (uint32_t)mp[bq] << (8 * bq);
-          bt.w[u] = v;
-          bt.m[u] = m;
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < TB; ++j) {
-        bt.xl[u][j] = load_x8<XL>(xrow[j], k + 8 * fq, k1, sg.ns, xok[j]);
-        if constexpr (WK == WK_SP24) bt.xh[u][j] = load_x8<XL>(xrow[j], k + 32 + 8 * fq, k1, sg.ns, xok[j]);
+        const int v0 = k / 2 + 8 * fq;
+        bt.w[u][i] = *reinterpret_cast<const u32x4*>(wrow[i] + 2 * v0);
+        bt.m[u][i] = *reinterpret_cast<const uint16_t*>(mrow[i] + (v0 >> 2));   // v0 % 8 == 0
       }
     }
-  };
-  auto consume = [&](const Batch& bt, int64_t kc) {
 #pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int64_t k = kc + (int64_t)u * CK;
-      if (k >= k1) break;
-      u32x4 wv = bt.w[u];
+    for (int j = 0; j < TB; ++j) {
+      bt.xl[u][j] = load_x8<XL, NS, false>(xrow[j], k + 8 * fq, k + CK);
+      if constexpr (WK == WK_SP24) bt.xh[u][j] = load_x8<XL, NS, false>(xrow[j], k + 32 + 8 * fq, k + CK);
+    }
+  };
+  // checked loads of chunk k (any part of it may lie beyond k1)
+  auto load_chunk_checked = [&](Batch& bt, int u, int k) {
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      bt.m[u][i] = 0;
+      if constexpr (WK == WK_BF16) {
+        const int kk = k + 8 * fq;
+        const uint16_t* rp = reinterpret_cast<const uint16_t*>(wrow[i]);
+        u32x4 v = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (kk + e < k1) v[e >> 1] |= (uint32_t)rp[kk + e] << (16 * (e & 1));
+        bt.w[u][i] = v;
+      } else if constexpr (WK == WK_FP8) {
+        const int kk = k + 8 * fq;
+        const uint8_t* rp = wrow[i];
+        uint32_t qq[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (kk + e < k1) qq[e >> 2] |= (uint32_t)rp[kk + e] << (8 * (e & 3));
+        bt.w[u][i] = u32x4{qq[0], qq[1], 0u, 0u};
+      } else {
+        const int v0 = k / 2 + 8 * fq;
+        const uint16_t* vp = reinterpret_cast<const uint16_t*>(wrow[i]) + v0;
+        const uint8_t* mp = mrow[i] + (v0 >> 2);
+        u32x4 v = {0u, 0u, 0u, 0u};
+        uint32_t m = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (k + 16 * fq + 2 * e < k1 && v0 + e < kcv) v[e >> 1] |= (uint32_t)vp[e] << (16 * (e & 1));
+#pragma unroll
+        for (int bq = 0; bq < 2; ++bq)
+          if ((v0 >> 2) + bq < mstride) m |= (uint32_t)mp[bq] << (8 * bq);
+        bt.w[u][i] = v;
+        bt.m[u][i] = m;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      bt.xl[u][j] = load_x8<XL, NS, true>(xrow[j], k + 8 * fq, k1);
+      if constexpr (WK == WK_SP24) bt.xh[u][j] = load_x8<XL, NS, true>(xrow[j], k + 32 + 8 * fq, k1);
+    }
+  };
+  auto mma = [&](const Batch& bt, int u) {
+    bf16x8 af[RW];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      u32x4 wv = bt.w[u][i];
       if constexpr (WK == WK_FP8) {
         uint32_t c0, c1, c2, c3;
         fp8x4_to_bf16x4(wv[0], c0, c1);
         fp8x4_to_bf16x4(wv[1], c2, c3);
         wv = u32x4{c0, c1, c2, c3};
       }
-      const bf16x8 af = __builtin_bit_cast(bf16x8, wv);
+      af[i] = __builtin_bit_cast(bf16x8, wv);
+    }
 #pragma unroll
-      for (int j = 0; j < TB; ++j) {
-        if constexpr (WK == WK_SP24) {
-          const u32x4 lo = bt.xl[u][j], hi = bt.xh[u][j];
-          const u32x8 bb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          acc[j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af, __builtin_bit_cast(bf16x16, bb), acc[j],
-                                                             (int)bt.m[u], 0, 0);
-        } else {
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8, bt.xl[u][j]), acc[j], 0, 0, 0);
-        }
+    for (int j = 0; j < TB; ++j) {
+      if constexpr (WK == WK_SP24) {
+        const u32x4 lo = bt.xl[u][j], hi = bt.xh[u][j];
+        const u32x8 bb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const bf16x16 bv = __builtin_bit_cast(bf16x16, bb);
+#pragma unroll
+        for (int i = 0; i < RW; ++i)
+          acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af[i], bv, acc[i][j], (int)bt.m[u][i], 0, 0);
+      } else {
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, bt.xl[u][j]);
+#pragma unroll
+        for (int i = 0; i < RW; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bv, acc[i][j], 0, 0, 0);
       }
     }
   };
+  // the scheduling barrier keeps the next batch's loads ahead of this batch's matrix
+  // instructions (under register pressure the scheduler would otherwise sink them)
+  auto fetch = [&](Batch& bt, int kc) {
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) load_chunk(bt, u, kc + u * CK);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto consume = [&](const Batch& bt) {
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) mma(bt, u);
+  };
 
-  constexpr int64_t STEP = (int64_t)CK * UNROLL;
-  Batch b0, b1;
-  int64_t kc = k0;
-  fetch(b0, kc);
-  while (true) {
-    const int64_t kn = kc + STEP;
-    if (kn < k1) fetch(b1, kn);
-    consume(b0, kc);
-    if (kn >= k1) break;
-    const int64_t kn2 = kn + STEP;
-    if (kn2 < k1) fetch(b0, kn2);
-    consume(b1, kn);
-    if (kn2 >= k1) break;
-    kc = kn2;
+  // whole-chunk loads need 16-byte aligned compressed rows for 2:4 weights
+  const bool aligned = WK != WK_SP24 || (kcv & 7) == 0;
+  constexpr int STEP = CK * UNROLL;
+  const int nb = aligned ? (k1 - k0) / STEP : 0;   // batches of whole chunks
+  if (nb > 0) {
+    Batch b0, b1;
+    int b = 0;
+    fetch(b0, k0);
+    while (b + 2 < nb) {
+      fetch(b1, k0 + (b + 1) * STEP);
+      consume(b0);
+      fetch(b0, k0 + (b + 2) * STEP);
+      consume(b1);
+      b += 2;
+    }
+    if (b + 2 == nb) {
+      fetch(b1, k0 + (b + 1) * STEP);
+      consume(b0);
+      consume(b1);
+    } else {
+      consume(b0);
+    }
+  }
+  for (int k = k0 + nb * STEP; k < k1; k += CK) {   // ragged end, one chunk at a time
+    Batch bt;
+    load_chunk_checked(bt, 0, k);
+    mma(bt, 0);
   }
 }
 
 // the part [k0, k1) of a segment of length k handled by wave part p of P (chunk aligned)
 template <int WK>
-__device__ __forceinline__ void part_range(int64_t k, int64_t p, int64_t P, int64_t& k0, int64_t& k1) {
+__device__ __forceinline__ void part_range(int64_t k, int64_t p, int64_t P, int& k0, int& k1) {
   constexpr int CK = Chunk<WK>::K;
   const int64_t c = (k + CK - 1) / CK;
-  k0 = (p * c / P) * CK;
-  k1 = ((p + 1) * c / P) * CK;
-  if (k1 > k) k1 = k;
+  const int64_t a = (p * c / P) * CK;
+  int64_t b = ((p + 1) * c / P) * CK;
+  if (b > k) b = k;
+  k0 = (int)a;
+  k1 = (int)b;
 }
 
 template <int TB> struct MaxThreads { static constexpr int V = TB >= 4 ? 512 : 1024; };
 
-template <int TB, int WK0, int XL0, int WK1>
+template <int TB, int RW, int WK0, int XL0, int NS, int WK1>
 __global__ __launch_bounds__(MaxThreads<TB>::V) void k_few(FewSeg s0, FewSeg s1, const float* __restrict__ wscale,
                                                           int64_t T, int64_t O, float* __restrict__ y, int64_t ldy,
                                                           int accumulate, float* __restrict__ part, int splits) {
   extern __shared__ __align__(16) float red[];   // [waves][16 * TB * 16]
+  constexpr int RB = 16 * RW;                    // output rows per workgroup
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wpb = blockDim.x >> 6;
   const int fr = lane & 15, fq = lane >> 4;
-  const int64_t nob = (O + 15) / 16;
+  const int64_t nob = (O + RB - 1) / RB;
   const int64_t ob = blockIdx.x % nob;
   const int split = (int)(blockIdx.x / nob);
-  const int64_t o_row = ob * 16 + fr;            // the weight row this lane loads
-  const int64_t o_ld = o_row < O ? o_row : O - 1;
+  int64_t orow[RW];                               // the weight rows this lane loads
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    const int64_t o = ob * RB + 16 * i + fr;
+    orow[i] = o < O ? o : O - 1;
+  }
   const int64_t P = (int64_t)splits * wpb, p = (int64_t)split * wpb + wave;
 
-  f32x4 acc[TB];
+  f32x4 acc[RW][TB];
 #pragma unroll
-  for (int j = 0; j < TB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < RW; ++i)
+#pragma unroll
+    for (int j = 0; j < TB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   {
-    int64_t k0, k1;
+    int k0, k1;
     part_range<WK0>(s0.k, p, P, k0, k1);
-    if (k0 < k1) stream_seg<TB, WK0, XL0>(acc, s0, o_ld, T, k0, k1, lane);
+    if (k0 < k1) stream_seg<TB, RW, WK0, XL0, NS>(acc, s0, orow, T, k0, k1, lane);
   }
   if constexpr (WK1 != WK_NONE) {
-    int64_t k0, k1;
+    int k0, k1;
     part_range<WK1>(s1.k, p, P, k0, k1);
-    if (k0 < k1) stream_seg<TB, WK1, XL_PLAIN>(acc, s1, o_ld, T, k0, k1, lane);
+    if (k0 < k1) stream_seg<TB, RW, WK1, XL_PLAIN, 0>(acc, s1, orow, T, k0, k1, lane);
   }
 
-  // sum the waves' tiles in wave order; element e = t * 16 + (o - 16 ob)
+  // sum the waves' tiles in wave order, one 16-row tile at a time; element
+  // e = t * 16 + (o - RB ob - 16 i)
   constexpr int PER = TB * 256;
   float* mine = red + wave * PER;
 #pragma unroll
-  for (int j = 0; j < TB; ++j) *reinterpret_cast<f32x4*>(mine + (16 * j + fr) * 16 + 4 * fq) = acc[j];
+  for (int i = 0; i < RW; ++i) {
+    if (i > 0) __syncthreads();   // the previous tile's sums have been read
+#pragma unroll
+    for (int j = 0; j < TB; ++j) *reinterpret_cast<f32x4*>(mine + (16 * j + fr) * 16 + 4 * fq) = acc[i][j];
+    __syncthreads();
+    for (int e = threadIdx.x; e < PER; e += blockDim.x) {
+      float sum = 0.f;
+      for (int w = 0; w < wpb; ++w) sum += red[w * PER + e];
+      const int64_t t = e >> 4, o = ob * RB + 16 * i + (e & 15);
+      if (t >= T || o >= O) continue;
+      if (part != nullptr) {
+        part[((int64_t)split * T + t) * O + o] = sum;
+      } else {
+        float v = wscale != nullptr ? sum * wscale[o] : sum;
+        if (accumulate) v += y[t * ldy + o];
+        y[t * ldy + o] = v;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Direct-to-LDS variant for 1-2 token blocks (T <= 32).  Loading 16-byte weight
+// fragments into registers makes every load instruction touch 16 rows (64 bytes each),
+// and together with the X fragments that saturates the L1 address path; measured on
+// gfx950, streaming the weights with global_load_lds instead (8 lanes per 128-byte row
+// segment, 8 rows per instruction) recovers most of the HBM bandwidth.  Each wave owns a
+// private ring of four LDS stages, each one 128-byte segment of its 16-row tiles (+ the
+// 2:4 metadata); stage s+3 is requested while stage s is multiplied.  Pieces are stored
+// XOR-swizzled (piece j of row r at j ^ ((r>>1)&7)) so the reads back into the matrix
+// operand layout are conflict-free.  X fragments stay in registers, one stage ahead.
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void g2lds16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void g2lds4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
+}
+__device__ __forceinline__ int dswz(int r) { return (r >> 1) & 7; }
+
+template <int TB> struct Dma {
+  static constexpr int WPB = TB == 1 ? 16 : 8;   // waves per workgroup (LDS budget)
+  static constexpr int RW = TB == 1 ? 1 : 2;     // 16-row tiles per wave (= rw_for)
+};
+template <int WK> struct DmaFmt {
+  static constexpr int U = WK == WK_FP8 ? 4 : 2;    // chunks per stage: one 128-byte row segment
+  static constexpr int BPE = WK == WK_BF16 ? 2 : 1; // weight bytes per reduction position
+};
+constexpr int dma_stage_bytes(int rw, int wk) { return rw * (2048 + (wk == WK_SP24 ? 256 : 0)); }
+
+template <int TB, int RW, int WK, int XL, int NS>
+__device__ __forceinline__ void stream_dma(f32x4 (&acc)[RW][TB], const FewSeg& sg, int64_t rbase, int64_t O,
+                                           int64_t T, int k0, int k1, int lane, unsigned char* R0,
+                                           unsigned char* R1, unsigned char* R2, unsigned char* R3) {
+  constexpr int CK = Chunk<WK>::K;
+  constexpr int U = DmaFmt<WK>::U;
+  constexpr int BPE = DmaFmt<WK>::BPE;
+  constexpr int SK = U * CK;   // reduction positions per stage (128 bytes of every weight row)
+  const int fr = lane & 15, fq = lane >> 4;
+  const int kcv = (int)(sg.k / 2);
+  const int mstride = (int)((sg.k + 7) >> 3);
+  auto row_ptr = [&](int64_t o) -> const uint8_t* {
+    o = o < O ? o : O - 1;
+    if constexpr (WK == WK_BF16) return reinterpret_cast<const uint8_t*>(sg.w) + o * sg.ldw * 2;
+    else if constexpr (WK == WK_FP8) return reinterpret_cast<const uint8_t*>(sg.w) + o * sg.ldw;
+    else return reinterpret_cast<const uint8_t*>(sg.w) + o * (int64_t)kcv * 2;
+  };
+  // DMA sources: tile i, half h -> row 8h + lane/8, logical piece (lane&7) ^ swizzle
+  const uint8_t* dsrc[RW][2];
+  const uint8_t* msrc[RW];
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 8 * h + (lane >> 3);
+      dsrc[i][h] = row_ptr(rbase + 16 * i + r) + 16 * ((lane & 7) ^ dswz(r));
+    }
+    if constexpr (WK == WK_SP24) {
+      int64_t o = rbase + 16 * i + (lane >> 2);
+      o = o < O ? o : O - 1;
+      msrc[i] = sg.w_meta + o * (int64_t)mstride + 4 * (lane & 3);
+    }
+  }
+  const uint16_t* xrow[TB];
+#pragma unroll
+  for (int j = 0; j < TB; ++j) {
+    const int64_t t = 16 * j + fr;
+    xrow[j] = sg.x + (t < T ? t : T - 1) * sg.ldx;
+  }
+
+  auto issue_w = [&](unsigned char* R, int st) {
+    const int kpos = k0 + st * SK;
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      g2lds16(dsrc[i][0] + (int64_t)kpos * BPE, R + i * 2048);
+      g2lds16(dsrc[i][1] + (int64_t)kpos * BPE, R + i * 2048 + 1024);
+      if constexpr (WK == WK_SP24) g2lds4(msrc[i] + (kpos >> 3), R + RW * 2048 + i * 256);
+    }
+  };
+  struct XB {
+    u32x4 xl[U][TB];
+    u32x4 xh[U][TB];
+  };
+  auto load_x = [&](XB& xb, int st) {
+    const int kpos = k0 + st * SK;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int j = 0; j < TB; ++j) {
+        xb.xl[u][j] = load_x8<XL, NS, false>(xrow[j], kpos + u * CK + 8 * fq, 0);
+        if constexpr (WK == WK_SP24) xb.xh[u][j] = load_x8<XL, NS, false>(xrow[j], kpos + u * CK + 32 + 8 * fq, 0);
+      }
+  };
+  auto compute = [&](const unsigned char* R, const XB& xb) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      bf16x8 af[RW];
+      int meta[RW];
+#pragma unroll
+      for (int i = 0; i < RW; ++i) {
+        const unsigned char* tile = R + i * 2048 + (fr >> 3) * 1024 + (fr & 7) * 128;
+        if constexpr (WK == WK_FP8) {
+          const int pc = 2 * u + (fq >> 1);
+          const uint2 q = *reinterpret_cast<const uint2*>(tile + 16 * (pc ^ dswz(fr)) + 8 * (fq & 1));
+          uint32_t c0, c1, c2, c3;
+          fp8x4_to_bf16x4(q.x, c0, c1);
+          fp8x4_to_bf16x4(q.y, c2, c3);
+          af[i] = __builtin_bit_cast(bf16x8, u32x4{c0, c1, c2, c3});
+        } else {
+          const int pc = 4 * u + fq;
+          af[i] = *reinterpret_cast<const bf16x8*>(tile + 16 * (pc ^ dswz(fr)));
+        }
+        if constexpr (WK == WK_SP24)
+          meta[i] = *reinterpret_cast<const uint16_t*>(R + RW * 2048 + i * 256 + fr * 16 + 8 * u + 2 * fq);
+      }
+#pragma unroll
+      for (int j = 0; j < TB; ++j) {
+        if constexpr (WK == WK_SP24) {
+          const u32x4 lo = xb.xl[u][j], hi = xb.xh[u][j];
+          const u32x8 bb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const bf16x16 bv = __builtin_bit_cast(bf16x16, bb);
+#pragma unroll
+          for (int i = 0; i < RW; ++i)
+            acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af[i], bv, acc[i][j], meta[i], 0, 0);
+        } else {
+          const bf16x8 bv = __builtin_bit_cast(bf16x8, xb.xl[u][j]);
+#pragma unroll
+          for (int i = 0; i < RW; ++i)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bv, acc[i][j], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // whole stages need 16-byte aligned compressed rows and 4-byte aligned metadata rows
+  const bool aligned = WK != WK_SP24 || ((kcv & 7) == 0 && (mstride & 3) == 0);
+  const int ns = aligned ? (k1 - k0) / SK : 0;
+  if (ns > 0) {
+    issue_w(R0, 0);
+    if (ns > 1) issue_w(R1, 1);
+    if (ns > 2) issue_w(R2, 2);
+    XB xa, xb;
+    load_x(xa, 0);
+    for (int st = 0; st < ns; st += 4) {
+      if (st + 3 < ns) issue_w(R3, st + 3);
+      if (st + 1 < ns) load_x(xb, st + 1);
+      compute(R0, xa);
+      if (st + 1 >= ns) break;
+      if (st + 4 < ns) issue_w(R0, st + 4);
+      if (st + 2 < ns) load_x(xa, st + 2);
+      compute(R1, xb);
+      if (st + 2 >= ns) break;
+      if (st + 5 < ns) issue_w(R1, st + 5);
+      if (st + 3 < ns) load_x(xb, st + 3);
+      compute(R2, xa);
+      if (st + 3 >= ns) break;
+      if (st + 6 < ns) issue_w(R2, st + 6);
+      if (st + 4 < ns) load_x(xa, st + 4);
+      compute(R3, xb);
+    }
+  }
+  // ragged end (and unaligned compressed rows): register loads, chunk by chunk
+  const int kt = k0 + ns * SK;
+  if (kt < k1) {
+    int64_t orow[RW];
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const int64_t o = rbase + 16 * i + fr;
+      orow[i] = o < O ? o : O - 1;
+    }
+    stream_seg<TB, RW, WK, XL, NS>(acc, sg, orow, T, kt, k1, lane);
+  }
+}
+
+template <int TB, int WK0, int XL0, int NS, int WK1>
+__global__ __launch_bounds__(64 * Dma<TB>::WPB) void k_fewd(FewSeg s0, FewSeg s1, const float* __restrict__ wscale,
+                                                           int64_t T, int64_t O, float* __restrict__ y, int64_t ldy,
+                                                           int accumulate, float* __restrict__ part, int splits) {
+  constexpr int RW = Dma<TB>::RW, WPB = Dma<TB>::WPB;
+  constexpr int STAGE = dma_stage_bytes(RW, WK0);   // the first segment's kind is the larger one
+  static_assert(WK1 == WK_NONE || dma_stage_bytes(RW, WK1) <= STAGE, "stage size");
+  static_assert(STAGE >= TB * 1024, "reduction buffer reuses stage 0");
+  __shared__ __align__(16) unsigned char r0[WPB * STAGE], r1[WPB * STAGE], r2[WPB * STAGE], r3[WPB * STAGE];
+  constexpr int RB = 16 * RW;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wpb = blockDim.x >> 6;
+  const int fr = lane & 15, fq = lane >> 4;
+  const int64_t nob = (O + RB - 1) / RB;
+  const int64_t ob = blockIdx.x % nob;
+  const int split = (int)(blockIdx.x / nob);
+  const int64_t P = (int64_t)splits * wpb, p = (int64_t)split * wpb + wave;
+  f32x4 acc[RW][TB];
+#pragma unroll
+  for (int i = 0; i < RW; ++i)
+#pragma unroll
+    for (int j = 0; j < TB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  unsigned char* w0 = r0 + wave * STAGE;
+  unsigned char* w1 = r1 + wave * STAGE;
+  unsigned char* w2 = r2 + wave * STAGE;
+  unsigned char* w3 = r3 + wave * STAGE;
+  {
+    int k0, k1;
+    part_range<WK0>(s0.k, p, P, k0, k1);
+    if (k0 < k1) stream_dma<TB, RW, WK0, XL0, NS>(acc, s0, ob * RB, O, T, k0, k1, lane, w0, w1, w2, w3);
+  }
+  if constexpr (WK1 != WK_NONE) {
+    int k0, k1;
+    part_range<WK1>(s1.k, p, P, k0, k1);
+    if (k0 < k1) stream_dma<TB, RW, WK1, XL_PLAIN, 0>(acc, s1, ob * RB, O, T, k0, k1, lane, w0, w1, w2, w3);
+  }
+  // sum the waves' tiles in wave order through stage 0's memory (one 16 x 16 token block
+  // at a time); element e = t_local * 16 + (o - RB ob - 16 i)
   __syncthreads();
-  for (int e = threadIdx.x; e < PER; e += blockDim.x) {
-    float sum = 0.f;
-    for (int w = 0; w < wpb; ++w) sum += red[w * PER + e];
-    const int64_t t = e >> 4, o = ob * 16 + (e & 15);
-    if (t >= T || o >= O) continue;
-    if (part != nullptr) {
-      part[((int64_t)split * T + t) * O + o] = sum;
-    } else {
-      float v = wscale != nullptr ? sum * wscale[o] : sum;
-      if (accumulate) v += y[t * ldy + o];
-      y[t * ldy + o] = v;
+  float* red = reinterpret_cast<float*>(r0);
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      if (i + j > 0) __syncthreads();
+      *reinterpret_cast<f32x4*>(red + wave * 256 + fr * 16 + 4 * fq) = acc[i][j];
+      __syncthreads();
+      for (int e = threadIdx.x; e < 256; e += blockDim.x) {
+        float sum = 0.f;
+        for (int w = 0; w < wpb; ++w) sum += red[w * 256 + e];
+        const int64_t t = 16 * j + (e >> 4), o = ob * RB + 16 * i + (e & 15);
+        if (t >= T || o >= O) continue;
+        if (part != nullptr) {
+          part[((int64_t)split * T + t) * O + o] = sum;
+        } else {
+          float v = wscale != nullptr ? sum * wscale[o] : sum;
+          if (accumulate) v += y[t * ldy + o];
+          y[t * ldy + o] = v;
+        }
+      }
     }
   }
 }
@@ -311,7 +615,7 @@ __global__ void k_permute_cols(const uint16_t* __restrict__ x, int64_t T, int64_
 }
 
 struct Plan {
-  int tb, wpb;
+  int tb, rw, wpb;
   int64_t splits;
 };
 
@@ -323,14 +627,18 @@ int env_int(const char* name) {   // A/B measurement overrides
 Plan make_plan(const FewArgs& a, bool allow_split) {
   Plan p;
   p.tb = a.t <= 16 ? 1 : a.t <= 32 ? 2 : a.t <= 64 ? 4 : 8;
-  const int max_wpb = p.tb >= 4 ? 8 : 16;
-  const int64_t nob = (a.o + 15) / 16;
+  p.rw = rw_for(p.tb, a.seg[0].w_kind);
+  // waves per workgroup: LDS rings bound the direct-to-LDS kernels (16 waves for one token
+  // block, 8 for two); 4 measured best for the register kernel at four token blocks
+  const int max_wpb = p.tb == 1 ? 16 : p.tb == 4 ? 4 : 8;
   int64_t chunks = 0;   // chunks of the longest segment
   for (int i = 0; i < a.nseg; ++i) {
     const int ck = a.seg[i].w_kind == WK_SP24 ? 64 : 32;
     const int64_t c = (a.seg[i].k + ck - 1) / ck;
     chunks = c > chunks ? c : chunks;
   }
+  const int ew = env_int("NM_FEW_WPB"), es = env_int("NM_FEW_SPLITS");
+  const int64_t nob = (a.o + 16 * p.rw - 1) / (16 * p.rw);
   // about one workgroup of max_wpb waves per CU (256 CUs); many row blocks -> fewer waves
   // per block, few row blocks -> the reduction is also split across workgroups
   int wpb = max_wpb;
@@ -343,40 +651,60 @@ Plan make_plan(const FewArgs& a, bool allow_split) {
   // keep at least two chunks per wave part
   if (splits > 1 && splits * wpb * 2 > chunks) splits = chunks / (2 * wpb) > 1 ? chunks / (2 * wpb) : 1;
   while (wpb > 4 && splits * wpb * 2 > chunks) wpb /= 2;
-  const int ew = env_int("NM_FEW_WPB"), es = env_int("NM_FEW_SPLITS");
-  if (ew == 4 || ew == 8 || (ew == 16 && max_wpb == 16)) wpb = ew;
+  if (ew == 4 || (ew == 8 && p.tb != 4) || (ew == 16 && max_wpb == 16)) wpb = ew;
   if (es > 0 && allow_split) splits = es;
   p.wpb = wpb;
   p.splits = splits;
   return p;
 }
 
-template <int TB, int WK0, int XL0, int WK1>
+template <int TB, int WK0, int XL0, int NS, int WK1>
 hipError_t launch_k(const FewArgs& a, const Plan& p, float* part, hipStream_t s) {
-  auto kern = k_few<TB, WK0, XL0, WK1>;
-  const int64_t nob = (a.o + 15) / 16;
+  constexpr int RW = rw_for(TB, WK0);
+  const int64_t nob = (a.o + 16 * RW - 1) / (16 * RW);
   const int64_t blocks = nob * p.splits;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  const size_t lds = (size_t)p.wpb * TB * 1024;
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
   const FewSeg s1 = a.nseg > 1 ? a.seg[1] : FewSeg{};
-  kern<<<dim3((unsigned)blocks), dim3(64 * p.wpb), lds, s>>>(a.seg[0], s1, a.w_scale, a.t, a.o, a.y, a.ldy,
-                                                             a.accumulate, p.splits > 1 ? part : nullptr,
-                                                             (int)p.splits);
+  float* pp = p.splits > 1 ? part : nullptr;
+  if constexpr (TB <= 2) {
+    static_assert(RW == Dma<TB>::RW, "row tiles");
+    if (p.wpb > Dma<TB>::WPB) return hipErrorInvalidConfiguration;
+    k_fewd<TB, WK0, XL0, NS, WK1><<<dim3((unsigned)blocks), dim3(64 * p.wpb), 0, s>>>(
+        a.seg[0], s1, a.w_scale, a.t, a.o, a.y, a.ldy, a.accumulate, pp, (int)p.splits);
+  } else {
+    auto kern = k_few<TB, RW, WK0, XL0, NS, WK1>;
+    const size_t lds = (size_t)p.wpb * TB * 1024;
+    if (lds > 65536) {
+      hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    kern<<<dim3((unsigned)blocks), dim3(64 * p.wpb), lds, s>>>(a.seg[0], s1, a.w_scale, a.t, a.o, a.y, a.ldy,
+                                                               a.accumulate, pp, (int)p.splits);
+  }
   return hipGetLastError();
 }
 
-template <int WK0, int XL0, int WK1>
+template <int WK0, int XL0, int NS, int WK1>
 hipError_t launch_tb(const FewArgs& a, const Plan& p, float* part, hipStream_t s) {
   switch (p.tb) {
-    case 1: return launch_k<1, WK0, XL0, WK1>(a, p, part, s);
-    case 2: return launch_k<2, WK0, XL0, WK1>(a, p, part, s);
-    case 4: return launch_k<4, WK0, XL0, WK1>(a, p, part, s);
-    default: return launch_k<8, WK0, XL0, WK1>(a, p, part, s);
+    case 1: return launch_k<1, WK0, XL0, NS, WK1>(a, p, part, s);
+    case 2: return launch_k<2, WK0, XL0, NS, WK1>(a, p, part, s);
+    case 4: return launch_k<4, WK0, XL0, NS, WK1>(a, p, part, s);
+    default: return launch_k<8, WK0, XL0, NS, WK1>(a, p, part, s);
   }
+}
+
+hipError_t launch_lift(const FewArgs& a, const Plan& p, float* part, hipStream_t s) {
+  switch (a.seg[0].ns) {
+    case 2: return launch_tb<WK_SP24, XL_LIFT, 2, WK_NONE>(a, p, part, s);
+    case 3: return launch_tb<WK_SP24, XL_LIFT, 3, WK_NONE>(a, p, part, s);
+    case 4: return launch_tb<WK_SP24, XL_LIFT, 4, WK_NONE>(a, p, part, s);
+    case 5: return launch_tb<WK_SP24, XL_LIFT, 5, WK_NONE>(a, p, part, s);
+    case 6: return launch_tb<WK_SP24, XL_LIFT, 6, WK_NONE>(a, p, part, s);
+    case 7: return launch_tb<WK_SP24, XL_LIFT, 7, WK_NONE>(a, p, part, s);
+    case 8: return launch_tb<WK_SP24, XL_LIFT, 8, WK_NONE>(a, p, part, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -391,6 +719,8 @@ int64_t few_partial_bytes(const FewArgs& a) {
 
 hipError_t launch_few(const FewArgs& a, float* part, int64_t part_bytes, hipStream_t s) {
   if (a.t > 128 || a.nseg < 1 || a.nseg > 2) return hipErrorInvalidValue;
+  for (int i = 0; i < a.nseg; ++i)   // reduction indices are 32-bit inside the kernel
+    if (a.seg[i].k > 0x3FFFFFFF) return hipErrorInvalidValue;
   if (a.t == 0 || a.o == 0) return hipSuccess;
   Plan p = make_plan(a, part != nullptr);
   if (p.splits > 1 && part_bytes < p.splits * a.t * a.o * 4) p = make_plan(a, false);
@@ -398,15 +728,15 @@ hipError_t launch_few(const FewArgs& a, float* part, int64_t part_bytes, hipStre
   hipError_t e = hipErrorInvalidValue;
   if (a.nseg == 2) {
     if (s0.w_kind == WK_SP24 && s0.loader == XL_PLAIN && a.seg[1].w_kind == WK_BF16 && a.seg[1].loader == XL_PLAIN)
-      e = launch_tb<WK_SP24, XL_PLAIN, WK_BF16>(a, p, part, s);
+      e = launch_tb<WK_SP24, XL_PLAIN, 0, WK_BF16>(a, p, part, s);
   } else if (s0.w_kind == WK_BF16 && s0.loader == XL_PLAIN) {
-    e = launch_tb<WK_BF16, XL_PLAIN, WK_NONE>(a, p, part, s);
+    e = launch_tb<WK_BF16, XL_PLAIN, 0, WK_NONE>(a, p, part, s);
   } else if (s0.w_kind == WK_FP8 && s0.loader == XL_PLAIN) {
-    e = launch_tb<WK_FP8, XL_PLAIN, WK_NONE>(a, p, part, s);
+    e = launch_tb<WK_FP8, XL_PLAIN, 0, WK_NONE>(a, p, part, s);
   } else if (s0.w_kind == WK_SP24 && s0.loader == XL_PLAIN) {
-    e = launch_tb<WK_SP24, XL_PLAIN, WK_NONE>(a, p, part, s);
+    e = launch_tb<WK_SP24, XL_PLAIN, 0, WK_NONE>(a, p, part, s);
   } else if (s0.w_kind == WK_SP24 && s0.loader == XL_LIFT) {
-    e = launch_tb<WK_SP24, XL_LIFT, WK_NONE>(a, p, part, s);
+    e = launch_lift(a, p, part, s);
   }
   if (e != hipSuccess || p.splits == 1) return e;
   return launch_reduce_parts(part, p.splits, a.w_scale, a.t, a.o, a.y, a.ldy, a.accumulate, s);
