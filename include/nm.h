@@ -151,8 +151,9 @@ typedef enum {
  * Optional fields (may be NULL / 0):
  *   x_mask_out  ACT_DYNAMIC only: receives the selection bitmask of x [t][ceil(k/32)]
  *   w_kmajor    ACT_DYNAMIC, bf16 W only: the same weights stored K-major [k][o]
- *               (row stride o); used for single-token calls, which then read only the
- *               selected K-rows of W.
+ *               (row stride o, 16-byte aligned).  Single-token calls (t == 1) with
+ *               o % 8 == 0, no w_scale and a workspace of nm_spmm_workspace_size bytes
+ *               then read only the selected K-rows of W (n/m of its bytes).
  *   workspace   device scratch (16-byte aligned).  With workspace_bytes >=
  *               nm_spmm_workspace_size(args): ACT_DYNAMIC may run select and product as
  *               two passes (S(x) staged in the workspace), ACT_COMPRESSED stages the

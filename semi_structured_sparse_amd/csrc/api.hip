@@ -278,8 +278,15 @@ nm_status nm_slide_lift(const void* x, int64_t t, int64_t k, int64_t ldx, int ns
   return hip_status(nml::launch_lift(ns, (const uint16_t*)x, t, k, ldx, (uint16_t*)x_out, ldo, as_stream(stream)));
 }
 
+// Single-token route over K-major weights (reads only the selected K-rows).
+bool gather1_route(const nm_spmm_args* a) {
+  return a->mode == NM_ACT_DYNAMIC && a->t == 1 && a->w_kmajor != nullptr && a->w_dtype == NM_W_BF16 &&
+         a->w_scale == nullptr && a->o > 0 && a->k > 0 && (a->o % 8) == 0 && supported_m(a->m);
+}
+
 int64_t nm_spmm_workspace_size(const nm_spmm_args* a) {
   if (a == nullptr || a->t < 0 || a->o < 0 || a->k < 0) return 0;
+  if (gather1_route(a)) return nml::gather1_part_bytes(a->k, a->o, a->m);
   const int64_t stage = spmm_stage_bytes(a);
   int64_t part = 0;
   if (use_few(a->t) && a->t > 0 && a->o > 0 && a->k > 0) {
@@ -337,6 +344,7 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
       }
       if (a->x_mask_out != nullptr && !aligned16(a->x_mask_out)) return NM_EALIGN;
       if (a->workspace != nullptr && !aligned16(a->workspace)) return NM_EALIGN;
+      if (a->w_kmajor != nullptr && !aligned16(a->w_kmajor)) return NM_EALIGN;
       if (T == 0 || O == 0) return NM_OK;
       if (K == 0) return a->accumulate ? NM_OK : zero_output(a->y, T, O, a->ldy, s);
 
@@ -377,6 +385,14 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
         return hip_status(nml::launch_gemm_dense(g, s));
       }
 
+      // ACT_DYNAMIC, one token with K-major weights: select and gather the kept K-rows
+      if (gather1_route(a)) {
+        const int64_t need = nml::gather1_part_bytes(K, O, a->m);
+        if (a->workspace != nullptr && a->workspace_bytes >= need)
+          return hip_status(nml::launch_gather1(a->m, (const uint16_t*)a->x, K, a->n, (const uint16_t*)a->w_kmajor, O,
+                                                a->y, a->accumulate, a->x_mask_out, (float*)a->workspace,
+                                                a->workspace_bytes, s));
+      }
       // ACT_DYNAMIC, few tokens: select into S(X), then stream the weights
       if (use_few(T) && have_ws) {
         uint16_t* sx = (uint16_t*)a->workspace;

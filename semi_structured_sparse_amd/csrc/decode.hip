@@ -435,7 +435,10 @@ __device__ __forceinline__ void stream_dma(f32x4 (&acc)[RW][TB], const FewSeg& s
         if constexpr (WK == WK_SP24) xb.xh[u][j] = load_x8<XL, NS, false>(xrow[j], kpos + u * CK + 32 + 8 * fq, 0);
       }
   };
+  // the scheduling barriers keep each stage's LDS reads after its own wait (the
+  // scheduler would otherwise hoist later stages' reads and force a full drain)
   auto compute = [&](const unsigned char* R, const XB& xb) {
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       bf16x8 af[RW];
@@ -474,6 +477,7 @@ __device__ __forceinline__ void stream_dma(f32x4 (&acc)[RW][TB], const FewSeg& s
         }
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // whole stages need 16-byte aligned compressed rows and 4-byte aligned metadata rows
@@ -485,7 +489,25 @@ __device__ __forceinline__ void stream_dma(f32x4 (&acc)[RW][TB], const FewSeg& s
     if (ns > 2) issue_w(R2, 2);
     XB xa, xb;
     load_x(xa, 0);
-    for (int st = 0; st < ns; st += 4) {
+    int st = 0;
+    // steady state: every step has a stage to prefetch (straight-line, so the compiler
+    // waits exactly for the stage it reads)
+    for (; st + 7 <= ns; st += 4) {
+      issue_w(R3, st + 3);
+      load_x(xb, st + 1);
+      compute(R0, xa);
+      issue_w(R0, st + 4);
+      load_x(xa, st + 2);
+      compute(R1, xb);
+      issue_w(R1, st + 5);
+      load_x(xb, st + 3);
+      compute(R2, xa);
+      issue_w(R2, st + 6);
+      load_x(xa, st + 4);
+      compute(R3, xb);
+    }
+    // the last stages (fewer than seven), prefetching only what exists
+    for (; st < ns; st += 4) {
       if (st + 3 < ns) issue_w(R3, st + 3);
       if (st + 1 < ns) load_x(xb, st + 1);
       compute(R0, xa);
@@ -581,13 +603,193 @@ __global__ __launch_bounds__(64 * Dma<TB>::WPB) void k_fewd(FewSeg s0, FewSeg s1
   }
 }
 
-__global__ void k_reduce_parts(const float* __restrict__ part, int64_t splits, const float* __restrict__ wscale,
-                               int64_t T, int64_t O, float* __restrict__ y, int64_t ldy, int accumulate) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= T * O) return;
+// ---------------------------------------------------------------------------------
+// Single token with K-major weights Wk [K][O]:  y[o] = sum_{k kept} x[k] * Wk[k][o].
+// With one token the selection keeps n of every m inputs, so only those K-rows of the
+// weights are read (n/m of the bytes) -- each a contiguous run of the output dimension.
+// Workgroup (k-span, o-chunk): select the span's groups of x in registers (top-n by
+// magnitude, ties to the lower index: the same rule as the select kernel), list the kept
+// (k, x[k]) in LDS in ascending k (exactly n per group, so every slot is known), then
+// stream those rows' o-chunk with 16-byte loads, 8 rows in flight per thread, and write
+// the span's fp32 partial sums; a second kernel adds the spans in order.
+constexpr int G1_THREADS = 512;
+constexpr int G1_MAX_SPAN = 2048;
+
+template <int M>
+__global__ __launch_bounds__(G1_THREADS) void k_gather1(const uint16_t* __restrict__ x, int64_t K, int n,
+                                                       const uint16_t* __restrict__ wk, int64_t O, int kspan,
+                                                       int ochunk, int nochunk, float* __restrict__ part,
+                                                       uint32_t* __restrict__ mask_out) {
+  __shared__ int sk[G1_MAX_SPAN];
+  __shared__ float sv[G1_MAX_SPAN];
+  __shared__ uint32_t mw[G1_MAX_SPAN / 32];
+  __shared__ __align__(16) float red[G1_THREADS * 8];
+  const int tid = threadIdx.x;
+  const int oc = (int)(blockIdx.x % nochunk);
+  const int ks = (int)(blockIdx.x / nochunk);
+  const int64_t k0 = (int64_t)ks * kspan;
+  const int span = (int)((k0 + kspan <= K) ? kspan : K - k0);
+  const int groups = span / M;
+  const bool want_mask = mask_out != nullptr && oc == 0;
+  if (want_mask)
+    for (int w = tid; w < (span + 31) / 32; w += G1_THREADS) mw[w] = 0u;
+  __syncthreads();
+  for (int g = tid; g < groups; g += G1_THREADS) {
+    uint32_t d[M / 2];
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(x + k0 + (int64_t)g * M);
+#pragma unroll
+    for (int q = 0; q < M / 2; ++q) d[q] = src[q];
+    const uint32_t bits = topn_bits<M>(d, n);
+    int slot = g * n;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      if ((bits >> i) & 1u) {
+        const uint32_t b = (d[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+        sk[slot] = (int)(k0 + (int64_t)g * M + i);
+        sv[slot] = __uint_as_float(b << 16);
+        ++slot;
+      }
+    }
+    if (want_mask) atomicOr(&mw[(g * M) >> 5], (M == 32 ? bits : bits << ((g * M) & 31)));
+  }
+  __syncthreads();
+  if (want_mask)
+    for (int w = tid; w < (span + 31) / 32; w += G1_THREADS) mask_out[(k0 >> 5) + w] = mw[w];
+
+  const int lanes_o = ochunk / 8;                 // threads across the o-chunk
+  const int nkl = G1_THREADS / lanes_o;           // threads along the kept list
+  const int kl = tid / lanes_o, lo = tid % lanes_o;
+  const int64_t o0 = (int64_t)oc * ochunk + 8 * lo;
+  const int nsel = groups * n;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (o0 < O) {
+    // software pipeline: batch b+1 (8 kept rows) is requested before batch b is used
+    const uint16_t* wcol = wk + o0;
+    struct B8 {
+      u32x4 w[8];
+      float v[8];
+    };
+    auto fetch = [&](B8& bt, int e) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int ee = e + q * nkl;
+        bt.w[q] = *reinterpret_cast<const u32x4*>(wcol + (int64_t)sk[ee] * O);
+        bt.v[q] = sv[ee];
+      }
+    };
+    auto use = [&](const B8& bt) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          acc[2 * c] += bt.v[q] * __uint_as_float(bt.w[q][c] << 16);
+          acc[2 * c + 1] += bt.v[q] * __uint_as_float(bt.w[q][c] & 0xFFFF0000u);
+        }
+    };
+    const int stride = 8 * nkl;
+    const int nb = (nsel - kl + stride - 1) / stride > 0 ? (nsel - kl) / stride : 0;   // whole batches
+    int e = kl;
+    if (nb > 0) {
+      B8 b0, b1;
+      int b = 0;
+      fetch(b0, e);
+      while (b + 2 < nb) {
+        fetch(b1, e + stride);
+        use(b0);
+        fetch(b0, e + 2 * stride);
+        use(b1);
+        b += 2;
+        e += 2 * stride;
+      }
+      if (b + 2 == nb) {
+        fetch(b1, e + stride);
+        use(b0);
+        use(b1);
+        e += 2 * stride;
+      } else {
+        use(b0);
+        e += stride;
+      }
+    }
+    for (; e < nsel; e += nkl) {
+      const u32x4 wv = *reinterpret_cast<const u32x4*>(wcol + (int64_t)sk[e] * O);
+      const float v = sv[e];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        acc[2 * c] += v * __uint_as_float(wv[c] << 16);
+        acc[2 * c + 1] += v * __uint_as_float(wv[c] & 0xFFFF0000u);
+      }
+    }
+  }
+  // add the list lanes in order, write the span's partial sums
+#pragma unroll
+  for (int q = 0; q < 8; ++q) red[kl * ochunk + 8 * lo + q] = acc[q];
+  __syncthreads();
+  for (int i = tid; i < ochunk; i += G1_THREADS) {
+    const int64_t o = (int64_t)oc * ochunk + i;
+    if (o >= O) continue;
+    float sum = 0.f;
+    for (int l = 0; l < nkl; ++l) sum += red[l * ochunk + i];
+    part[(int64_t)ks * O + o] = sum;
+  }
+}
+
+struct G1Plan {
+  int kspan, ochunk, nochunk;
+  int64_t nks;
+};
+
+G1Plan g1_plan(int64_t k, int64_t o, int m) {
+  G1Plan p;
+  int oc = 64;
+  while (oc < 1024 && oc < o) oc *= 2;
+  p.ochunk = oc;
+  p.nochunk = (int)((o + oc - 1) / oc);
+  const int64_t target = (256 + p.nochunk - 1) / p.nochunk;   // about one workgroup per CU
+  int64_t span = (k + target - 1) / target;
+  const int unit = m > 32 ? m : 32;                           // whole mask words and groups
+  span = (span + unit - 1) / unit * unit;
+  if (span > G1_MAX_SPAN) span = G1_MAX_SPAN;
+  if (span < unit) span = unit;
+  p.kspan = (int)span;
+  p.nks = (k + span - 1) / span;
+  return p;
+}
+
+// y = w_scale * sum of the partial tiles, accumulated or stored.  A workgroup owns 64
+// consecutive outputs; its 4 thread lanes per output take every 4th partial (unrolled,
+// so many loads are in flight) and the 4 lane sums are added in lane order.  Fixed
+// order throughout: results do not depend on timing.
+constexpr int RP_OUT = 64, RP_LANES = 4;
+
+__global__ __launch_bounds__(RP_OUT * RP_LANES) void k_reduce_parts(const float* __restrict__ part, int64_t splits,
+                                                                   const float* __restrict__ wscale, int64_t T,
+                                                                   int64_t O, float* __restrict__ y, int64_t ldy,
+                                                                   int accumulate) {
+  __shared__ float sums[RP_LANES][RP_OUT];
+  const int lo = threadIdx.x % RP_OUT, sl = threadIdx.x / RP_OUT;
+  const int64_t n = T * O;
+  const int64_t i = (int64_t)blockIdx.x * RP_OUT + lo;
+  float acc = 0.f;
+  if (i < n) {
+    const float* p = part + i;
+    int64_t sp = sl;
+    for (; sp + 7 * RP_LANES < splits; sp += 8 * RP_LANES) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = p[(sp + q * RP_LANES) * n];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc += v[q];
+    }
+    for (; sp < splits; sp += RP_LANES) acc += p[sp * n];
+  }
+  sums[sl][lo] = acc;
+  __syncthreads();
+  if (sl != 0 || i >= n) return;
+  float sum = sums[0][lo];
+#pragma unroll
+  for (int l = 1; l < RP_LANES; ++l) sum += sums[l][lo];
   const int64_t t = i / O, o = i - t * O;
-  float sum = 0.f;
-  for (int64_t sp = 0; sp < splits; ++sp) sum += part[sp * T * O + i];
   float v = wscale != nullptr ? sum * wscale[o] : sum;
   if (accumulate) v += y[t * ldy + o];
   y[t * ldy + o] = v;
@@ -651,7 +853,7 @@ Plan make_plan(const FewArgs& a, bool allow_split) {
   // keep at least two chunks per wave part
   if (splits > 1 && splits * wpb * 2 > chunks) splits = chunks / (2 * wpb) > 1 ? chunks / (2 * wpb) : 1;
   while (wpb > 4 && splits * wpb * 2 > chunks) wpb /= 2;
-  if (ew == 4 || (ew == 8 && p.tb != 4) || (ew == 16 && max_wpb == 16)) wpb = ew;
+  if (ew == 4 || ew == 8 || (ew == 16 && max_wpb == 16)) wpb = ew;
   if (es > 0 && allow_split) splits = es;
   p.wpb = wpb;
   p.splits = splits;
@@ -742,12 +944,36 @@ hipError_t launch_few(const FewArgs& a, float* part, int64_t part_bytes, hipStre
   return launch_reduce_parts(part, p.splits, a.w_scale, a.t, a.o, a.y, a.ldy, a.accumulate, s);
 }
 
+int64_t gather1_part_bytes(int64_t k, int64_t o, int m) {
+  if (k <= 0 || o <= 0) return 0;
+  return g1_plan(k, o, m).nks * o * 4;
+}
+
+hipError_t launch_gather1(int m, const uint16_t* x, int64_t k, int n, const uint16_t* wk, int64_t o, float* y,
+                          int accumulate, uint32_t* mask_out, float* part, int64_t part_bytes, hipStream_t s) {
+  const G1Plan p = g1_plan(k, o, m);
+  if (part == nullptr || part_bytes < p.nks * o * 4 || (o % 8) != 0) return hipErrorInvalidValue;
+  const int64_t blocks = p.nks * p.nochunk;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const dim3 g((unsigned)blocks), b(G1_THREADS);
+  switch (m) {
+    case 4: k_gather1<4><<<g, b, 0, s>>>(x, k, n, wk, o, p.kspan, p.ochunk, p.nochunk, part, mask_out); break;
+    case 8: k_gather1<8><<<g, b, 0, s>>>(x, k, n, wk, o, p.kspan, p.ochunk, p.nochunk, part, mask_out); break;
+    case 16: k_gather1<16><<<g, b, 0, s>>>(x, k, n, wk, o, p.kspan, p.ochunk, p.nochunk, part, mask_out); break;
+    case 32: k_gather1<32><<<g, b, 0, s>>>(x, k, n, wk, o, p.kspan, p.ochunk, p.nochunk, part, mask_out); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_reduce_parts(part, p.nks, nullptr, 1, o, y, o, accumulate, s);   // one row: ldy unused
+}
+
 hipError_t launch_reduce_parts(const float* part, int64_t splits, const float* w_scale, int64_t t, int64_t o,
                                float* y, int64_t ldy, int accumulate, hipStream_t s) {
   const int64_t n = t * o;
   if (n == 0) return hipSuccess;
-  k_reduce_parts<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(part, splits, w_scale, t, o, y, ldy,
-                                                                        accumulate);
+  k_reduce_parts<<<dim3((unsigned)((n + RP_OUT - 1) / RP_OUT)), dim3(RP_OUT * RP_LANES), 0, s>>>(
+      part, splits, w_scale, t, o, y, ldy, accumulate);
   return hipGetLastError();
 }
 

@@ -94,6 +94,11 @@ int64_t few_partial_bytes(const FewArgs& a);
 // part: scratch of part_bytes bytes or null; with less than few_partial_bytes(a) the
 // product runs as a single pass (fewer workgroups when o is small).
 hipError_t launch_few(const FewArgs& a, float* part, int64_t part_bytes, hipStream_t s);
+// Single token, K-major weights wk [k][o] (row stride o, o % 8 == 0): y[0][o] (=|+=)
+// sum over the n:m-selected k of x[k] * wk[k][o]; part: scratch of gather1_part_bytes.
+int64_t gather1_part_bytes(int64_t k, int64_t o, int m);
+hipError_t launch_gather1(int m, const uint16_t* x, int64_t k, int n, const uint16_t* wk, int64_t o, float* y,
+                          int accumulate, uint32_t* mask_out, float* part, int64_t part_bytes, hipStream_t s);
 // y[t][o] (=|+=) w_scale[o] * sum_{s < splits} part[s][t][o]   (part rows have stride o)
 hipError_t launch_reduce_parts(const float* part, int64_t splits, const float* w_scale, int64_t t, int64_t o,
                                float* y, int64_t ldy, int accumulate, hipStream_t s);

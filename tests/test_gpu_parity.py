@@ -399,6 +399,59 @@ def test_few_token_partition_overrides(wpb, splits, t):
         check_gemm(yh, O.hybrid_gemm(x, sp, de, hv, hi, hwd), x, wh, label="hybrid")
 
 
+@pytest.mark.parametrize("n,m", [(8, 16), (16, 32), (2, 4), (4, 8), (1, 4), (31, 32)])
+@pytest.mark.parametrize("k,o", [(1056, 264), (4128, 1024), (96, 8)])
+def test_single_token_kmajor_gather(n, m, k, o):
+    """One token with K-major weights: only the kept K-rows are read.  Result, mask and
+    accumulation against the oracle; the route needs o % 8 == 0 and a workspace."""
+    if k % m:
+        pytest.skip("k not a multiple of m")
+    print(f"gather n={n} m={m} k={k} o={o}", flush=True)
+    rng = np.random.default_rng(k + o + m)
+    x = synth.student_t_bf16(rng, (1, k), 4.0, 0.5)
+    x[0, :4] = np.array([0x3F80, 0x3F80, 0xBF80, 0x0000], np.uint16)     # ties
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    wk = dev(np.ascontiguousarray(w.T))
+    sx, keep = O.sparsify(x, n, m)
+    ref = O.gemm(sx, w)
+    y0 = rng.standard_normal((1, o)).astype(np.float32)
+    for acc in (0, 1):
+        y = dev(y0) if acc else empty((1, o), np.float32, fill=float("nan"))
+        mask = empty((1, (k + 31) // 32), np.uint32, fill=-1)
+        a = S.make_spmm_args(S.NM_ACT_DYNAMIC, 1, o, k, dev(x), dev(w), y, n=n, m=m, w_kmajor=wk,
+                             x_mask_out=mask, accumulate=acc)
+        nb = S.nm_spmm_workspace_size(a)
+        assert nb > 0 and nb < 1 << 24          # partial sums only
+        ws = empty((nb,), np.uint8)
+        a.workspace, a.workspace_bytes = ws.data_ptr(), nb
+        S.nm_spmm(a)
+        sync()
+        got = host(y, np.float32)
+        check_gemm(got - (y0 if acc else 0), ref, sx, w, label=f"gather acc={acc}")
+        assert (host(mask, np.uint32) == O.pack_mask(keep)).all()
+        if acc == 0:   # repeat: bitwise identical
+            S.nm_spmm(a)
+            sync()
+            assert (host(y, np.float32).view(np.uint32) == got.view(np.uint32)).all()
+
+
+def test_single_token_kmajor_full_size():
+    """8:16 down-projection, one token, K-major weights 14336 x 4096."""
+    d = synth.mlp_down_8of16(t_max=1)
+    x, w = d["x"], d["w"]
+    o, k = w.shape
+    wk = dev(np.ascontiguousarray(w.T))
+    y = empty((1, o), np.float32, fill=float("nan"))
+    a = S.make_spmm_args(S.NM_ACT_DYNAMIC, 1, o, k, dev(x), dev(w), y, n=8, m=16, w_kmajor=wk)
+    nb = S.nm_spmm_workspace_size(a)
+    ws = empty((nb,), np.uint8)
+    a.workspace, a.workspace_bytes = ws.data_ptr(), nb
+    S.nm_spmm(a)
+    sync()
+    sx, _ = O.sparsify(x, 8, 16)
+    check_gemm(host(y, np.float32), O.gemm(sx, w), sx, w, label="gather full")
+
+
 def test_spmm_act_compressed_2of4_and_8of16():
     rng = np.random.default_rng(9)
     for n, m, fmt in [(2, 4, 1), (8, 16, 0), (2, 4, 0)]:
