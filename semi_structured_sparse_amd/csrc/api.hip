@@ -154,6 +154,17 @@ int64_t w_mode_kc(const nm_spmm_args* a) {
   return a->k;
 }
 
+// Large-token ACT_DYNAMIC with fp8 weights: the weights are widened once to bf16 in the
+// workspace (after the S(X) staging) for the direct-to-LDS product kernel.
+int64_t fp8_widen_bytes(const nm_spmm_args* a) {
+  if (a->mode != NM_ACT_DYNAMIC || a->w_dtype != NM_W_FP8E4M3 || use_few(a->t)) return 0;
+  if (a->k % 64 != 0 || a->t < 512) return 0;
+  return a->o * a->k * 2;
+}
+
+// Row stride of a materialised lifted X (16-byte rows).
+inline int64_t lift_ld(int64_t kp) { return (kp + 7) / 8 * 8; }
+
 // Bytes of S(X) / decompressed-X staging at the start of nm_spmm's workspace.
 int64_t spmm_stage_bytes(const nm_spmm_args* a) {
   if (a->mode == NM_ACT_DYNAMIC) return a->t * a->k * 2 + 64;   // also holds the 2:4 compressed X
@@ -302,7 +313,11 @@ int64_t nm_spmm_workspace_size(const nm_spmm_args* a) {
       part = dense_few_part_bytes(g);
     }
   }
-  return part > 0 ? align256(stage) + part : stage;
+  if (part > 0) return align256(stage) + part;
+  if (a->mode == NM_W_SLIDE && !use_few(a->t) && a->t > 0 && a->ns >= 2 && a->ns <= 8 && a->k % (2 * a->ns) == 0)
+    return a->t * lift_ld(w_mode_kc(a)) * 2;   // lifted X for the large-token product
+  const int64_t widen = fp8_widen_bytes(a);
+  return widen > 0 ? align256(stage) + widen : stage;
 }
 
 nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
@@ -425,6 +440,13 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
                                           nullptr, nullptr, 0, s);
         if (e != hipSuccess) return NM_EHIP;
         g.prologue = nml::PRO_NONE; g.x = sx; g.ldx = K;
+        const int64_t widen = fp8_widen_bytes(a), woff = align256(stage);
+        if (widen > 0 && a->workspace_bytes >= woff + widen) {
+          uint16_t* wb = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(a->workspace) + woff);
+          e = nml::launch_widen_fp8((const uint8_t*)a->w, a->ldw, O, K, wb, s);
+          if (e != hipSuccess) return NM_EHIP;
+          g.w = wb; g.ldw = K; g.w_fp8 = 0;   // w_scale stays: applied in the epilogue
+        }
         return hip_status(nml::launch_gemm_dense(g, s));
       }
       if (route == ROUTE_MASK && (mask != nullptr || have_ws)) {
@@ -466,6 +488,13 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
       sa.x = (const uint16_t*)a->x; sa.ldx = a->ldx; sa.ns = ns;
       sa.loader = a->mode == NM_W_SLIDE ? nml::XL_LIFT : nml::XL_PLAIN;
       sa.t = T; sa.o = O; sa.y = a->y; sa.ldy = a->ldy; sa.accumulate = a->accumulate; sa.trans_out = 0;
+      if (a->mode == NM_W_SLIDE && a->workspace != nullptr && a->workspace_bytes >= T * lift_ld(kc) * 2) {
+        // materialise lift(X) once so the product kernel reads X with 16-byte loads
+        uint16_t* xl = (uint16_t*)a->workspace;
+        hipError_t e = nml::launch_lift(ns, (const uint16_t*)a->x, T, K, a->ldx, xl, lift_ld(kc), s);
+        if (e != hipSuccess) return NM_EHIP;
+        sa.x = xl; sa.ldx = lift_ld(kc); sa.loader = nml::XL_PLAIN;
+      }
       return hip_status(nml::launch_gemm_sparse(sa, s));
     }
     default:

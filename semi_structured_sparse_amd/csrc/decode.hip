@@ -34,14 +34,6 @@ using namespace nml;
 
 constexpr int WK_NONE = -1;
 
-__device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t q, uint32_t& lo, uint32_t& hi) {
-  typedef float f2 __attribute__((ext_vector_type(2)));
-  const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)q, false);
-  const f2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)q, true);
-  lo = __builtin_amdgcn_perm(__float_as_uint(a.y), __float_as_uint(a.x), 0x07060302u);
-  hi = __builtin_amdgcn_perm(__float_as_uint(b.y), __float_as_uint(b.x), 0x07060302u);
-}
-
 // 8 consecutive reduction positions [k, k+8) of an X~ row (rp = start of the row), zero
 // beyond kend.  k is in X~ coordinates (lifted index space for XL_LIFT, where window
 // w of group g -- 4 lifted positions -- holds original positions g*2NS + 2w + [0, 4)).

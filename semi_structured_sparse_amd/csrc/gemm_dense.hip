@@ -31,16 +31,6 @@ using namespace nml;
 constexpr int BK = 64;
 constexpr int PITCH = BK + 8;   // LDS row pitch in bf16
 
-// fp8 e4m3fn (OCP) x4 in a dword -> 4 bf16 in two dwords.  Every e4m3 value is exact in
-// bf16, so taking the high half of the fp32 conversion loses nothing.
-__device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t q, uint32_t& lo, uint32_t& hi) {
-  typedef float f2 __attribute__((ext_vector_type(2)));
-  const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)q, false);
-  const f2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)q, true);
-  lo = __builtin_amdgcn_perm(__float_as_uint(a.y), __float_as_uint(a.x), 0x07060302u);
-  hi = __builtin_amdgcn_perm(__float_as_uint(b.y), __float_as_uint(b.x), 0x07060302u);
-}
-
 // Load 8 bf16 (one 16-byte chunk) of a row at column kk, zero beyond K.
 __device__ __forceinline__ uint4 load_chunk_bf16(const uint16_t* rowp, int64_t kk, int64_t K) {
   if (kk + 8 <= K) return *reinterpret_cast<const uint4*>(rowp + kk);

@@ -61,7 +61,8 @@ template <int BM, int BN, int WM, int WN, int PRO>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
     const uint16_t* __restrict__ w, int64_t ldw, const uint16_t* __restrict__ x, int64_t ldx,
     const uint32_t* __restrict__ xmask, int64_t T, int64_t O, int64_t K, float* __restrict__ y,
-    int64_t ldy, int accumulate, int tiles_m, int tiles_n, int64_t kslice, float* __restrict__ part) {
+    int64_t ldy, int accumulate, int tiles_m, int tiles_n, int64_t kslice, float* __restrict__ part,
+    const float* __restrict__ wscale) {
   constexpr int NW = WM * WN;
   constexpr int SM = BM / WM, SN = BN / WN;       // wave sub-tile (o x t)
   constexpr int FI = SM / 16, FJ = SN / 16;
@@ -219,11 +220,20 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
     }
   }
 
-  // epilogue: lane holds 4 consecutive o for one t in each 16x16 block
+  // epilogue: lane holds 4 consecutive o for one t in each 16x16 block (per-row weight
+  // scale applied to the finished sums; split-K partials are scaled by the reduction)
   const bool vec_ok = ((ldy & 3) == 0);
 #pragma unroll
   for (int i = 0; i < FI; ++i) {
     const int64_t ob = o0 + wm * SM + i * 16 + 4 * fq;
+    if (wscale != nullptr && part == nullptr) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float sc = (ob + r < O) ? wscale[ob + r] : 0.f;
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) acc[i][j][r] *= sc;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < FJ; ++j) {
       const int64_t t = t0 + wn * SN + j * 16 + fr;
@@ -258,10 +268,10 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s, int64_t splits, float* p
   auto kern = k_gemm_lds<BM, BN, WM, WN, PRO>;
   kern<<<dim3((unsigned)(ntiles * splits)), dim3(64 * WM * WN), 0, s>>>(
       (const uint16_t*)a.w, a.ldw, a.x, a.ldx, a.x_mask, a.t, a.o, a.k, a.y, a.ldy, a.accumulate, tiles_m, tiles_n,
-      kslice, splits > 1 ? part : nullptr);
+      kslice, splits > 1 ? part : nullptr, a.w_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  return launch_reduce_parts(part, splits, nullptr, a.t, a.o, a.y, a.ldy, a.accumulate, s);
+  return launch_reduce_parts(part, splits, a.w_scale, a.t, a.o, a.y, a.ldy, a.accumulate, s);
 }
 
 }  // namespace
@@ -269,7 +279,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s, int64_t splits, float* p
 namespace nml {
 
 bool gemm_lds_eligible(const GemmArgs& a, bool any_size) {
-  if (a.w_fp8 || a.w_scale != nullptr) return false;
+  if (a.w_fp8) return false;
   if (a.prologue != PRO_NONE && a.prologue != PRO_MASK) return false;
   if (a.k % BK != 0 || a.k == 0) return false;
   if ((a.ldw % 8) || (a.ldx % 8)) return false;
@@ -278,8 +288,37 @@ bool gemm_lds_eligible(const GemmArgs& a, bool any_size) {
 }
 
 hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t s) {
-  if (a.prologue == PRO_MASK) return launch_cfg<256, 256, 4, 2, PRO_MASK>(a, s, 1, nullptr);
+  // fewer 256 x 256 tiles than CUs: 256 x 128 tiles (twice as many workgroups)
+  const bool half = ((a.o + 255) / 256) * ((a.t + 255) / 256) < 256;
+  if (a.prologue == PRO_MASK) {
+    if (half) return launch_cfg<256, 128, 4, 2, PRO_MASK>(a, s, 1, nullptr);
+    return launch_cfg<256, 256, 4, 2, PRO_MASK>(a, s, 1, nullptr);
+  }
+  if (half) return launch_cfg<256, 128, 4, 2, PRO_NONE>(a, s, 1, nullptr);
   return launch_cfg<256, 256, 4, 2, PRO_NONE>(a, s, 1, nullptr);
+}
+
+// fp8 weights for the large-token product: widened once to bf16 (exact), then the
+// direct-to-LDS kernel with the per-row scale in its epilogue.
+__global__ void k_widen_fp8(const uint8_t* __restrict__ w8, int64_t ldw, int64_t O, int64_t K,
+                            uint16_t* __restrict__ wb) {
+  const int64_t per_row = K / 8;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= O * per_row) return;
+  const int64_t o = i / per_row, c = i - o * per_row;
+  const uint2 q = *reinterpret_cast<const uint2*>(w8 + o * ldw + 8 * c);
+  uint32_t c0, c1, c2, c3;
+  fp8x4_to_bf16x4(q.x, c0, c1);
+  fp8x4_to_bf16x4(q.y, c2, c3);
+  *reinterpret_cast<uint4*>(wb + o * K + 8 * c) = make_uint4(c0, c1, c2, c3);
+}
+
+hipError_t launch_widen_fp8(const uint8_t* w8, int64_t ldw, int64_t o, int64_t k, uint16_t* wb, hipStream_t s) {
+  if (k % 8) return hipErrorInvalidValue;
+  const int64_t n = o * (k / 8);
+  if (n == 0) return hipSuccess;
+  k_widen_fp8<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(w8, ldw, o, k, wb);
+  return hipGetLastError();
 }
 
 // Few-token variant: 256 output rows x 64 or 128 tokens per tile, split-K so that there
@@ -294,7 +333,7 @@ static int64_t small_splits(const GemmArgs& a) {
 }
 
 bool gemm_lds_small_eligible(const GemmArgs& a) {
-  return a.prologue == PRO_NONE && !a.w_fp8 && a.w_scale == nullptr && a.k % BK == 0 && a.k > 0 &&
+  return a.prologue == PRO_NONE && !a.w_fp8 && a.k % BK == 0 && a.k > 0 &&
          (a.ldw % 8) == 0 && (a.ldx % 8) == 0 && a.t <= 128;
 }
 

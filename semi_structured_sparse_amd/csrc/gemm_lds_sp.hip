@@ -1,0 +1,260 @@
+// Large-token product with a 2:4 sparse weight operand, staged direct-to-LDS:
+//   Y[t][o] (=|+=) sum_k X[t][k] * W24[o][k]  (+ sum_j X[t][dbase + j] * Wd[o][j])
+//
+// W24 is 2:4 along the reduction (values [O][kc/2], 2-bit positions [O][kc/8]) -- plain
+// 2:4 weights, or (2N-2):2N weights lowered to overlapping 2:4 windows whose activations
+// were lifted beforehand (SlideSparse page, technical summary 2.A/2.B).  The optional
+// dense second phase is the hybrid format's dense region, accumulated into the same
+// accumulators (SpenseGPT page, technical summary 2.A).
+//
+// gfx950 design, after the dense direct-to-LDS kernel:
+//  * 256 x 256 output tile, 8 waves of 64 (o) x 128 (t); two LDS stages, each a distinct
+//    static array (so the compiler tracks the DMA into each one separately).
+//  * One sparse K-step covers 64 reduction positions: per weight row 64 bytes of
+//    compressed values (global_load_lds_dwordx4, 4 lanes per row) and 8 bytes of 2-bit
+//    positions (global_load_lds_dword, 2 lanes per row); per token row 128 bytes of X
+//    (8 lanes per row).  Pieces are XOR-swizzled per row so the fragment reads are
+//    conflict-free.
+//  * v_smfmac_f32_16x16x64_bf16: lane l holds weight row l%16 as 8 compressed values for
+//    positions [16(l/16), +16) plus its 16-bit index word, and token l%16 at positions
+//    8(l/16)+[0,8) and 32+8(l/16)+[0,8).
+//  * Dense phase: 128 bytes per weight row per K-step, two v_mfma_f32_16x16x32_bf16.
+// Requirements (checked by the caller): kc % 64 == 0 and kd % 64 == 0, 16-byte aligned
+// rows (kc % 32 == 0 makes the value and position rows aligned), X and Wd ld % 8 == 0.
+#include "nm_device.h"
+#include "nm_launch.h"
+
+namespace {
+
+using namespace nmk;
+using namespace nml;
+
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ void g2lds16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void g2lds4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
+}
+
+constexpr int BM = 256, BN = 256, WM = 4, WN = 2, NW = WM * WN;
+constexpr int SM = BM / WM, SN = BN / WN, FI = SM / 16, FJ = SN / 16;
+constexpr int A_BYTES = BM * 128;          // dense W rows (sparse phase: values + positions)
+constexpr int SV_BYTES = BM * 64;          // compressed values per sparse step
+constexpr int B_BYTES = BN * 128;          // X rows
+constexpr int GROUP = 16;
+
+__device__ __forceinline__ int swz8(int r, int c) { return c ^ ((r >> 1) & 7); }   // 8 pieces per row
+__device__ __forceinline__ int swz4(int r, int c) { return c ^ ((r >> 2) & 3); }   // 4 pieces per row
+
+__global__ __launch_bounds__(64 * NW) void k_gemm_lds_sp(
+    const uint16_t* __restrict__ wv, const uint8_t* __restrict__ wm, int64_t kc, const uint16_t* __restrict__ x,
+    int64_t ldx, const uint16_t* __restrict__ wd, int64_t ldwd, int64_t kd, int64_t dbase, int64_t T, int64_t O,
+    float* __restrict__ y, int64_t ldy, int accumulate, int tiles_m, int tiles_n) {
+  __shared__ __align__(16) unsigned char sA0[A_BYTES], sB0[B_BYTES];
+  __shared__ __align__(16) unsigned char sA1[A_BYTES], sB1[B_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wmi = wave % WM, wni = wave / WM;
+
+  // XCD-aware tile order (workgroup b runs on XCD b % 8), bands of GROUP o-tiles
+  const int ntiles = tiles_m * tiles_n;
+  int lin = blockIdx.x;
+  if ((ntiles & 7) == 0) lin = (blockIdx.x & 7) * (ntiles >> 3) + (blockIdx.x >> 3);
+  const int band = lin / (GROUP * tiles_n);
+  const int band_w = min(GROUP, tiles_m - band * GROUP);
+  const int inband = lin - band * GROUP * tiles_n;
+  const int tile_m = band * GROUP + inband % band_w, tile_n = inband / band_w;
+  const int64_t o0 = (int64_t)tile_m * BM, t0 = (int64_t)tile_n * BN;
+
+  const int64_t kcv = kc / 2, mstride = kc / 8;
+  const int nks = (int)(kc / 64), nkd = (int)(kd / 64), nk = nks + nkd;
+
+  f32x4 acc[FI][FJ];
+#pragma unroll
+  for (int i = 0; i < FI; ++i)
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int fr = lane & 15, fg = lane >> 4;
+
+  // X rows: groups of 8 rows (8 lanes x 16 bytes per row), 4 per wave
+  const uint16_t* xsrc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = (wave + q * NW) * 8 + (lane >> 3);
+    int64_t t = t0 + r;
+    t = t < T ? t : T - 1;
+    xsrc[q] = x + t * ldx + 8 * swz8(r, lane & 7);
+  }
+
+  // ----------------------------------------------------------- sparse phase ---
+  if (nks > 0) {
+    // compressed values: groups of 16 rows (4 lanes x 16 bytes per row), 2 per wave;
+    // positions: 32 rows per wave (2 lanes x 4 bytes per row)
+    const uint8_t* vsrc[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int r = (wave + q * NW) * 16 + (lane >> 2);
+      int64_t o = o0 + r;
+      o = o < O ? o : O - 1;
+      vsrc[q] = reinterpret_cast<const uint8_t*>(wv) + o * kcv * 2 + 16 * swz4(r, lane & 3);
+    }
+    const uint8_t* msrc;
+    {
+      const int r = wave * 32 + (lane >> 1);
+      int64_t o = o0 + r;
+      o = o < O ? o : O - 1;
+      msrc = wm + o * mstride + 4 * (lane & 1);
+    }
+    auto issue = [&](unsigned char* a, unsigned char* b, int s) {
+      const int64_t k0 = (int64_t)s * 64;   // dense positions; also the byte offset of the values
+#pragma unroll
+      for (int q = 0; q < 2; ++q) g2lds16(vsrc[q] + k0, a + (wave + q * NW) * 1024);
+      g2lds4(msrc + (k0 >> 3), a + SV_BYTES + wave * 256);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) g2lds16(xsrc[q] + k0, b + (wave + q * NW) * 1024);
+    };
+    auto compute = [&](const unsigned char* a, const unsigned char* b) {
+      bf16x8 af[FI];
+      int idx[FI];
+#pragma unroll
+      for (int i = 0; i < FI; ++i) {
+        const int r = wmi * SM + i * 16 + fr;
+        af[i] = *reinterpret_cast<const bf16x8*>(a + r * 64 + 16 * swz4(r, fg));
+        idx[i] = *reinterpret_cast<const uint16_t*>(a + SV_BYTES + r * 8 + 2 * fg);
+      }
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) {
+        const int c = wni * SN + j * 16 + fr;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(b + c * 128 + 16 * swz8(c, fg));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(b + c * 128 + 16 * swz8(c, 4 + fg));
+        const u32x8 bb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const bf16x16 bv = __builtin_bit_cast(bf16x16, bb);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int i = 0; i < FI; ++i)
+          acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af[i], bv, acc[i][j], idx[i], 0, 0);
+        __builtin_amdgcn_s_setprio(0);
+      }
+    };
+    issue(sA0, sB0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // two steps per trip (stage 0, then stage 1); the next step's loads go out first
+    for (int s = 0; s < nks; s += 2) {
+      if (s + 1 < nks) issue(sA1, sB1, s + 1);
+      compute(sA0, sB0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (s + 1 < nks) {
+        if (s + 2 < nks) issue(sA0, sB0, s + 2);
+        compute(sA1, sB1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+    }
+  }
+
+  // ------------------------------------------------------------ dense phase ---
+  if (nkd > 0) {
+    // dense weight rows: groups of 8 rows (8 lanes x 16 bytes per row), 4 per wave
+    const uint16_t* dsrc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = (wave + q * NW) * 8 + (lane >> 3);
+      int64_t o = o0 + r;
+      o = o < O ? o : O - 1;
+      dsrc[q] = wd + o * ldwd + 8 * swz8(r, lane & 7);
+    }
+    auto issue = [&](unsigned char* a, unsigned char* b, int s) {
+      const int64_t j0 = (int64_t)s * 64;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) g2lds16(dsrc[q] + j0, a + (wave + q * NW) * 1024);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) g2lds16(xsrc[q] + dbase + j0, b + (wave + q * NW) * 1024);
+    };
+    auto compute = [&](const unsigned char* a, const unsigned char* b) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 bfr[FJ];
+#pragma unroll
+        for (int j = 0; j < FJ; ++j) {
+          const int c = wni * SN + j * 16 + fr;
+          bfr[j] = *reinterpret_cast<const bf16x8*>(b + c * 128 + 16 * swz8(c, 4 * ks + fg));
+        }
+#pragma unroll
+        for (int i = 0; i < FI; ++i) {
+          const int r = wmi * SM + i * 16 + fr;
+          const bf16x8 af = *reinterpret_cast<const bf16x8*>(a + r * 128 + 16 * swz8(r, 4 * ks + fg));
+          __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+          for (int j = 0; j < FJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
+          __builtin_amdgcn_s_setprio(0);
+        }
+      }
+    };
+    issue(sA0, sB0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int s = 0; s < nkd; s += 2) {
+      if (s + 1 < nkd) issue(sA1, sB1, s + 1);
+      compute(sA0, sB0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (s + 1 < nkd) {
+        if (s + 2 < nkd) issue(sA0, sB0, s + 2);
+        compute(sA1, sB1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+    }
+  }
+
+  // epilogue: lane holds 4 consecutive o for one t in each 16x16 block
+  const bool vec_ok = ((ldy & 3) == 0);
+#pragma unroll
+  for (int i = 0; i < FI; ++i) {
+    const int64_t ob = o0 + wmi * SM + i * 16 + 4 * fg;
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) {
+      const int64_t t = t0 + wni * SN + j * 16 + fr;
+      if (t >= T) continue;
+      float* yp = y + t * ldy + ob;
+      if (vec_ok && ob + 4 <= O) {
+        float4 cur = accumulate ? *reinterpret_cast<float4*>(yp) : make_float4(0.f, 0.f, 0.f, 0.f);
+        *reinterpret_cast<float4*>(yp) =
+            make_float4(cur.x + acc[i][j][0], cur.y + acc[i][j][1], cur.z + acc[i][j][2], cur.w + acc[i][j][3]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (ob + r < O) yp[r] = accumulate ? yp[r] + acc[i][j][r] : acc[i][j][r];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+namespace nml {
+
+bool gemm_lds_sp_eligible(const SparseArgs& a, bool any_size) {
+  if (a.loader != XL_PLAIN || a.trans_out) return false;
+  if (a.kc % 64 != 0 || a.kd % 64 != 0 || (a.kc == 0 && a.kd == 0)) return false;
+  if ((a.ldx % 8) != 0 || (a.kd > 0 && ((a.ldwd % 8) != 0 || (a.dbase % 8) != 0))) return false;
+  // enough 256 x 256 tiles to fill the machine
+  return any_size || ((a.o + BM - 1) / BM) * ((a.t + BN - 1) / BN) >= 128;
+}
+
+hipError_t launch_gemm_lds_sp(const SparseArgs& a, hipStream_t s) {
+  const int tiles_m = (int)((a.o + BM - 1) / BM), tiles_n = (int)((a.t + BN - 1) / BN);
+  const int64_t ntiles = (int64_t)tiles_m * tiles_n;
+  if (ntiles == 0) return hipSuccess;
+  if (ntiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  k_gemm_lds_sp<<<dim3((unsigned)ntiles), dim3(64 * NW), 0, s>>>(
+      a.w_vals, a.w_meta, a.kc, a.x, a.ldx, a.wd, a.ldwd, a.kd, a.dbase, a.t, a.o, a.y, a.ldy, a.accumulate,
+      tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace nml

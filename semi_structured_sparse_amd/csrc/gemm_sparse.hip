@@ -19,6 +19,9 @@
 // of 4); the dense operand's lane l holds column l%16 at reduction positions
 // 8*(l/16)+[0,8) and 32+8*(l/16)+[0,8).  The accumulator layout equals the dense
 // 16x16 instruction's, so both phases share it.
+#include <cstdlib>
+#include <cstring>
+
 #include "nm_device.h"
 #include "nm_launch.h"
 
@@ -380,6 +383,11 @@ hipError_t launch_pick(const nml::SparseArgs& a, hipStream_t s) {
 namespace nml {
 
 hipError_t launch_gemm_sparse(const SparseArgs& a, hipStream_t s) {
+  // NM_GEMM=regs / lds overrides the kernel choice (A/B measurement and tests)
+  const char* force = std::getenv("NM_GEMM");
+  const bool regs_only = force != nullptr && std::strcmp(force, "regs") == 0;
+  const bool lds_any = force != nullptr && std::strcmp(force, "lds") == 0;
+  if (!regs_only && gemm_lds_sp_eligible(a, lds_any)) return launch_gemm_lds_sp(a, s);
   switch (a.loader) {
     case XL_PLAIN: return launch_pick<XL_PLAIN>(a, s);
     case XL_LIFT: return launch_pick<XL_LIFT>(a, s);

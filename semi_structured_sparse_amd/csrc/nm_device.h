@@ -71,4 +71,14 @@ __device__ __forceinline__ uint32_t mask_pair(uint32_t d, uint32_t two_bits) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// Four OCP e4m3fn codes (one per byte of q) -> four bf16, exactly (every e4m3 value is a
+// bf16 value): hardware decode to fp32, then the high halves.  lo = codes 0,1; hi = 2,3.
+__device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t q, uint32_t& lo, uint32_t& hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)q, false);
+  const f2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)q, true);
+  lo = __builtin_amdgcn_perm(__float_as_uint(a.y), __float_as_uint(a.x), 0x07060302u);
+  hi = __builtin_amdgcn_perm(__float_as_uint(b.y), __float_as_uint(b.x), 0x07060302u);
+}
+
 }  // namespace nmk

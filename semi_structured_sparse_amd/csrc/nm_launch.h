@@ -37,6 +37,8 @@ hipError_t launch_gemm_dense(const GemmArgs& a, hipStream_t s);
 // direct-to-LDS variant for large PRO_NONE / PRO_MASK problems with K % 64 == 0
 bool gemm_lds_eligible(const GemmArgs& a, bool any_size);
 hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t s);
+// fp8 e4m3fn weights [o][ldw] bytes -> bf16 [o][k] (exact), k % 8 == 0
+hipError_t launch_widen_fp8(const uint8_t* w8, int64_t ldw, int64_t o, int64_t k, uint16_t* wb, hipStream_t s);
 // few-token split-K variant (T <= 128, PRO_NONE, bf16): with part (scratch of at least
 // gemm_lds_small_part_bytes(a) bytes) the K slices write fp32 partial tiles that a second
 // kernel sums in slice order; without it, one slice.
@@ -66,6 +68,9 @@ struct SparseArgs {
   int trans_out;          // 0: Y[t][o] with o = sparse-side row; 1: Y[s][d] (X sparse)
 };
 hipError_t launch_gemm_sparse(const SparseArgs& a, hipStream_t s);
+// direct-to-LDS variant for large problems (plain loader, kc % 64 == 0, kd % 64 == 0)
+bool gemm_lds_sp_eligible(const SparseArgs& a, bool any_size);
+hipError_t launch_gemm_lds_sp(const SparseArgs& a, hipStream_t s);
 
 // Few-token streaming product (T <= 128): one or two weight segments summed into one
 // accumulator, then scaled (w_scale, per output row) and written or added to y.

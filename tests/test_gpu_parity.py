@@ -489,6 +489,27 @@ def test_spmm_act_accumulate_and_fp8():
         check_gemm(y2 - y0, O.gemm(sx, w), sx, w, label=f"accumulate {route}")
 
 
+@pytest.mark.parametrize("t,o,k", [(600, 300, 1024), (520, 136, 1056)])
+def test_spmm_act_fp8_large_tokens(t, o, k):
+    """fp8 weights at prefill sizes: widened once to bf16 in the workspace (K % 64 == 0)
+    or multiplied by the fp8-loading kernel (otherwise); scale, accumulate."""
+    print(f"fp8 large t={t} o={o} k={k}", flush=True)
+    rng = np.random.default_rng(t + k)
+    x = synth.student_t_bf16(rng, (t, k), 4.0, 1.0)
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    q, sc = synth.fp8_e4m3_quantize_rows(w)
+    wdeq = O.fp8_e4m3_to_f64(q) * sc[:, None].astype(np.float64)
+    y0 = rng.standard_normal((t, o)).astype(np.float32)
+    for n, m in ((16, 32), (8, 16)):
+        sx, keep = O.sparsify(x, n, m)
+        ref = O.spmm_act_fp8(x, q, sc, n, m)
+        y, mask = run_act(x, None, n, m, w8=q, s8=sc)
+        assert (mask == O.pack_mask(keep)).all()
+        check_gemm(y, ref, sx, wdeq, label=f"fp8 {n}:{m}")
+        y2, _ = run_act(x, None, n, m, w8=q, s8=sc, accumulate=1, y0=y0)
+        check_gemm(y2 - y0, ref, sx, wdeq, label=f"fp8 {n}:{m} accumulate")
+
+
 def test_fp8_decode_all_codes():
     """Every finite e4m3 code through the fp8 weight loader equals the oracle's decode."""
     codes = np.arange(256, dtype=np.uint8)
@@ -619,6 +640,45 @@ def test_spmm_w_slide_full_size_sampled():
         sync()
         rows = sample_rows(t, 16, seed=t)
         check_gemm(host(y, np.float32)[rows], O.gemm(x[rows], pruned), x[rows], pruned, label=f"slide full t={t}")
+
+
+@pytest.mark.parametrize("kernel", ["lds", "regs"])
+@pytest.mark.parametrize("t,o", [(300, 264), (130, 520)])
+def test_sparse_weight_product_kernels(kernel, t, o):
+    """Large-token 2:4-weight products on both kernels (direct-to-LDS and register
+    staged): plain 2:4, lowered 6:8 / 4:6 / 8:10 (X lifted into the workspace first) and
+    the hybrid format with its dense second phase; ragged T and O."""
+    print(f"sparse kernels kernel={kernel} t={t} o={o}", flush=True)
+    rng = np.random.default_rng(t + o)
+    with env_set(NM_GEMM=kernel):
+        k = 1024
+        x = synth.normal_bf16(rng, (t, k))
+        w = synth.normal_bf16(rng, (o, k), 0.02)
+        v, mt = gpu_compress_2of4(w)
+        ws24, _ = O.sparsify(w, 2, 4)
+        for ws in (True, False):
+            y = run_w(S.NM_W_COMPRESSED, x, v, mt, o, k, workspace=ws)
+            check_gemm(y, O.gemm(x, ws24), x, ws24, label=f"2:4 {kernel}")
+        for ns, kk in ((4, 2048), (3, 1536), (5, 2560)):
+            xs = synth.normal_bf16(rng, (t, kk))
+            wsl = synth.normal_bf16(rng, (o, kk), 0.02)
+            vv, ii = O.compress(wsl, 2 * ns - 2, 2 * ns)
+            kp = O.lowered_k(kk, ns)
+            vp = empty((o, kp // 2), np.uint16)
+            mp = empty((o, (kp + 7) // 8), np.uint8)
+            S.nm_lower_slide(dev(vv), dev(ii), o, kk, ns, vp, mp, S.NM_META_2BIT)
+            pr, _ = O.sparsify(wsl, 2 * ns - 2, 2 * ns)
+            for ws in (True, False):
+                y = run_w(S.NM_W_SLIDE, xs, vp, mp, o, kk, ns=ns, workspace=ws)
+                check_gemm(y, O.gemm(xs, pr), xs, pr, label=f"slide ns={ns} ws={ws} {kernel}")
+        kd = 256
+        sc, dc, wv, wm, wdd = hybrid_pack_gpu(w, kd)
+        sync()
+        sp, de, hv, hi, hwd = O.hybrid_pack(w, kd)
+        wh = w.copy()
+        wh[:, sp] = O.decompress(hv, hi, 2, 4, k - kd)
+        yh = run_hybrid(x, sc, k - kd, dc, kd, wv, wm, wdd, o)
+        check_gemm(yh, O.hybrid_gemm(x, sp, de, hv, hi, hwd), x, wh, label=f"hybrid {kernel}")
 
 
 # ----------------------------------------------------------------------- hybrid ---
