@@ -87,6 +87,164 @@ def cpu_baseline(x_bits, w_bits, n, m, budget_s=12.0):
                       f"(numpy fp64 select + matmul), {total_t:.1f} s"}
 
 
+def gpu_time_us(torch, fn, graph, iters=10, warm=3):
+    """Mean time per call.  graph=True: 20 calls captured in a HIP graph and replayed (the
+    GPU time of short few-token calls without host launch overhead); else events around
+    back-to-back calls."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if not graph:
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters * 1e3
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        fn()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=st):
+            for _ in range(20):
+                fn()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(3):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 60 * 1e3
+
+
+def measure_rows(torch, S, synth, np):
+    """Every workload row of the method's measurement table: time, dense-equivalent and
+    executed TFLOP/s, algorithmic bytes and GB/s, and the fraction of the roofline that
+    bounds the row (HBM for few tokens, bf16 matrix peak for many)."""
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(
+        np.int16 if a.dtype == np.uint16 else (np.int32 if a.dtype == np.int32 else np.uint8))).cuda()
+    f32 = lambda *sh: torch.empty(sh, dtype=torch.float32, device="cuda")
+    buf = lambda nb, dt=torch.uint8: torch.empty((max(int(nb), 16),), dtype=dt, device="cuda")
+    rows = []
+
+    def add(cfg, t, path, us, f_dense, f_exec, nbytes):
+        r = {"cfg": cfg, "tokens": t, "path": path, "us": round(us, 2),
+             "dense_equiv_tflops": round(f_dense / us / 1e6, 2), "executed_tflops": round(f_exec / us / 1e6, 2),
+             "algorithmic_bytes": int(nbytes), "GBps": round(nbytes / us / 1e3, 1)}
+        if t <= 128:
+            r.update(bound="hbm", frac=round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4))
+        else:
+            r.update(bound="mfma", frac=round(f_exec / us / 1e6 / PEAK_BF16_TFLOPS, 4))
+        rows.append(r)
+        log(f"  {cfg:5s} T={t:5d} {path:34s} {us:9.1f} us  {r['executed_tflops']:8.1f} TF/s exec  "
+            f"{r['GBps']:7.0f} GB/s  {r['bound']} {100 * r['frac']:.1f}%")
+
+    def spmm(a, ws_holder):
+        nb = S.nm_spmm_workspace_size(a)
+        ws_holder.append(buf(nb))
+        a.workspace, a.workspace_bytes = ws_holder[-1].data_ptr(), nb
+        return lambda: S.nm_spmm(a)
+
+    keep = []
+    # cfg1: 2:4 activations, 64 x 512 x 512
+    d = synth.layer_2of4_small()
+    x1, w1 = dev(d["x"]), dev(d["w"])
+    y = f32(64, 512)
+    fn = spmm(S.make_spmm_args(S.NM_ACT_DYNAMIC, 64, 512, 512, x1, w1, y, n=2, m=4), keep)
+    add("cfg1", 64, "2:4 act (select + product)", gpu_time_us(torch, fn, True), 2.0 * 64 * 512 * 512,
+        2.0 * 64 * 512 * 512, 64 * 512 * 2 + 512 * 512 * 2 + 64 * 512 * 4)
+    # cfg2: 8:16 activations, down-projection 4096 x 14336
+    d = synth.mlp_down_8of16(t_max=8192)
+    x2, w2 = dev(d["x"]), dev(d["w"])
+    O2, K2 = 4096, 14336
+    wk2 = dev(np.ascontiguousarray(d["w"].T))
+    y = f32(1, O2)
+    fn = spmm(S.make_spmm_args(S.NM_ACT_DYNAMIC, 1, O2, K2, x2[:1], w2, y, n=8, m=16, w_kmajor=wk2), keep)
+    add("cfg2", 1, "8:16 act, K-major gather", gpu_time_us(torch, fn, True), 2.0 * O2 * K2, 2.0 * O2 * K2 / 2,
+        K2 // 2 * O2 * 2 + K2 * 2 + O2 * 4)
+    del wk2
+    for t in (1, 16, 128, 2048, 8192):
+        y = f32(t, O2)
+        fn = spmm(S.make_spmm_args(S.NM_ACT_DYNAMIC, t, O2, K2, x2[:t], w2, y, n=8, m=16), keep)
+        f = 2.0 * t * O2 * K2
+        add("cfg2", t, "8:16 act (select + product)", gpu_time_us(torch, fn, t <= 128), f, f,
+            t * K2 * 2 + O2 * K2 * 2 + t * O2 * 4)
+    del x2, w2
+    # cfg3: 6:8 weights lowered to 2:4, 4096 x 4096, lifted activations
+    d = synth.slide_6of8_layer(t_max=4096)
+    w3, x3 = dev(d["w"]), dev(d["x"])
+    v = torch.empty((4096, 3072), dtype=torch.int16, device="cuda")
+    i8 = torch.empty((4096, 3072), dtype=torch.uint8, device="cuda")
+    S.nm_compress(w3, 6, 8, v, i8, S.NM_META_U8)
+    vp = torch.empty((4096, 3072), dtype=torch.int16, device="cuda")
+    mp = torch.empty((4096, 768), dtype=torch.uint8, device="cuda")
+    S.nm_lower_slide(v, i8, 4096, 4096, 4, vp, mp, S.NM_META_2BIT)
+    for t in (1, 16, 128, 4096):
+        y = f32(t, 4096)
+        fn = spmm(S.make_spmm_args(S.NM_W_SLIDE, t, 4096, 4096, x3[:t], vp, y, ns=4, w_meta=mp,
+                                   w_meta_fmt=S.NM_META_2BIT), keep)
+        add("cfg3", t, "6:8 W lowered to 2:4, lifted X", gpu_time_us(torch, fn, t <= 128), 2.0 * t * 4096 * 4096,
+            2.0 * t * 4096 * 3072, 4096 * 3072 * 2 + 4096 * 768 + t * 4096 * 2 + t * 4096 * 4)
+    del w3, x3, v, i8, vp, mp
+    # cfg4: hybrid, 14336 x 4096, 25% dense columns
+    d = synth.hybrid_up_layer(t_max=2048)
+    w4, x4 = dev(d["w"]), dev(d["x"])
+    o4, k4 = d["w"].shape
+    kd = d["k_dense"]
+    ks = k4 - kd
+    sc = torch.empty((ks,), dtype=torch.int32, device="cuda")
+    dc = torch.empty((kd,), dtype=torch.int32, device="cuda")
+    wv = torch.empty((o4, ks // 2), dtype=torch.int16, device="cuda")
+    wm = torch.empty((o4, ks // 8), dtype=torch.uint8, device="cuda")
+    wd = torch.empty((o4, kd), dtype=torch.int16, device="cuda")
+    S.nm_hybrid_pack(w4, kd, sc, dc, wv, wm, S.NM_META_2BIT, wd, buf(S.nm_hybrid_pack_workspace_size(k4)))
+    for t in (1, 8, 32, 64, 2048):
+        y = f32(t, o4)
+        nb = S.nm_hybrid_gemm_workspace_size(t, ks, kd, o4, True)
+        wsb = buf(nb)
+        xs = x4[:t]
+        fn = lambda: S.nm_hybrid_gemm(xs, sc, ks, dc, kd, wv, wm, S.NM_META_2BIT, wd, o4, y, workspace=wsb,
+                                      workspace_bytes=nb)
+        add("cfg4", t, "hybrid 2:4 + 25% dense columns", gpu_time_us(torch, fn, t <= 128), 2.0 * t * o4 * k4,
+            2.0 * t * o4 * (kd + ks / 2), o4 * ks + o4 * ks // 8 + o4 * kd * 2 + t * k4 * 2 + t * o4 * 4)
+    del w4, x4, sc, dc, wv, wm, wd
+    # cfg5: one 8B-shaped layer, 16:32 and 8:16, bf16 and fp8 weights, T = 64 and 8192
+    lay = synth.transformer_layer(t_max=8192, with_fp8=True)
+    names = list(synth.TRANSFORMER_SHAPES)
+    wdev = {nm: dev(lay["w"][nm]) for nm in names}
+    w8dev = {nm: (dev(lay["w8"][nm]), torch.from_numpy(lay["s8"][nm]).cuda()) for nm in names}
+    xdev = {st: dev(v) for st, v in lay["x"].items()}
+    del lay
+    for t in (64, 8192):
+        for n, m in ((16, 32), (8, 16)):
+            for kind in ("bf16", "fp8"):
+                tot_us = tot_f = tot_b = 0.0
+                for nm in names:
+                    o_, k_, st = synth.TRANSFORMER_SHAPES[nm]
+                    y = f32(t, o_)
+                    xin = xdev[st][:t]
+                    if kind == "bf16":
+                        a = S.make_spmm_args(S.NM_ACT_DYNAMIC, t, o_, k_, xin, wdev[nm], y, n=n, m=m)
+                        wb = o_ * k_ * 2
+                    else:
+                        q, s8 = w8dev[nm]
+                        a = S.make_spmm_args(S.NM_ACT_DYNAMIC, t, o_, k_, xin, q, y, n=n, m=m,
+                                             w_dtype=S.NM_W_FP8E4M3, w_scale=s8)
+                        wb = o_ * k_ + o_ * 4
+                    fn = spmm(a, keep)
+                    tot_us += gpu_time_us(torch, fn, t <= 128, iters=5, warm=2)
+                    tot_f += 2.0 * t * o_ * k_
+                    tot_b += wb + t * k_ * 2 + t * o_ * 4
+                    keep.clear()
+                add("cfg5", t, f"layer {n}:{m} act, {kind} W", tot_us, tot_f, tot_f, tot_b)
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,7 +252,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--shapes", action="store_true", help="also time the decode token counts (stderr + JSON)")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip the per-workload rows (all five workloads at their token counts)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB five times (counter calibration)")
     args = ap.parse_args()
@@ -178,29 +337,9 @@ def main():
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
     }
 
-    if args.shapes:
-        shapes = {}
-        for tt in (1, 16, 128, 2048):
-            ys = torch.empty((tt, O_), dtype=torch.float32, device="cuda")
-            ad = S.make_spmm_args(S.NM_ACT_DYNAMIC, tt, O_, K, x[:tt], w, ys, n=n, m=m)
-            nb = S.nm_spmm_workspace_size(ad)
-            wsb = torch.empty((max(nb, 16),), dtype=torch.uint8, device="cuda")
-            ad.workspace, ad.workspace_bytes = wsb.data_ptr(), nb
-            for _ in range(3):
-                S.nm_spmm(ad)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            it = 20
-            e0.record()
-            for _ in range(it):
-                S.nm_spmm(ad)
-            e1.record()
-            torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) / it * 1e3
-            byts = tt * K * 2 + O_ * K * 2 + tt * O_ * 4
-            shapes[str(tt)] = {"us": round(us, 2), "TFLOPs": round(2.0 * tt * O_ * K / us / 1e6, 2),
-                               "GBps": round(byts / us / 1e3, 1)}
-            log(f"T={tt}: {us:.1f} us, {2.0 * tt * O_ * K / us / 1e6:.2f} TFLOP/s, {byts / us / 1e3:.0f} GB/s")
-        result["shapes"] = shapes
+    if not args.no_rows:
+        log("per-workload rows:")
+        result["rows"] = measure_rows(torch, S, synth, np)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x_bits, w_bits, n, m)

@@ -263,6 +263,16 @@ def test_spmm_act_masked_kernels(kernel, t, o, k):
         else:
             os.environ["NM_GEMM"] = old
     check_gemm(host(y2, np.float32), O.gemm(sx, w), sx, w, label=f"masked presparsified {kernel}")
+    # x already S(X), no mask: the plain product
+    y3 = empty((t, o), np.float32, fill=float("nan"))
+    a3 = S.make_spmm_args(S.NM_ACT_MASKED, t, o, k, sxd, wdv, y3, n=8, m=16)
+    nb = S.nm_spmm_workspace_size(a3)
+    ws3 = empty((max(nb, 16),), np.uint8)
+    a3.workspace, a3.workspace_bytes = ws3.data_ptr(), nb
+    with env_set(NM_GEMM=kernel):
+        S.nm_spmm(a3)
+        sync()
+    check_gemm(host(y3, np.float32), O.gemm(sx, w), sx, w, label=f"S(X) no mask {kernel}")
 
 
 class env_set:
