@@ -108,13 +108,17 @@ inline float* ws_slice(void* ws, int64_t ws_bytes, int64_t off, int64_t* avail) 
 }
 
 // Few-token product with a dense weight on an activation operand that is already S(X)
-// (g.prologue == PRO_NONE): the weight-streaming kernel.  The split-K tile kernel is kept
-// as an A/B alternative (NM_FEW_ROUTE=tile, bf16 weights): measured on gfx950 at
-// 4096 x 14336 it is slower at 64 tokens (50 vs 41 us) and level at 128.
+// (g.prologue == PRO_NONE).  Up to 32 tokens the weight-streaming kernel; above that the
+// split-K tile kernel, whose workgroups share each X slice through LDS across 128 weight
+// rows.  Measured on gfx950 (bf16 W, 33-128 tokens): 4096 x 14336 at 128 tokens 40 vs
+// 73 us, 14336 x 4096 at 64 tokens 32 vs 46 us; for weights under 2048 rows the
+// streaming kernel stays ahead.  NM_FEW_ROUTE=stream|tile forces either for A/B.
 bool few_use_tile(const nml::GemmArgs& g) {
   if (!nml::gemm_lds_small_eligible(g)) return false;
   const char* e = std::getenv("NM_FEW_ROUTE");
-  return e != nullptr && std::strcmp(e, "tile") == 0;
+  if (e != nullptr && std::strcmp(e, "tile") == 0) return true;
+  if (e != nullptr && std::strcmp(e, "stream") == 0) return false;
+  return g.t > 32 && g.o >= 2048;
 }
 
 nml::FewArgs few_dense_args(const nml::GemmArgs& g) {

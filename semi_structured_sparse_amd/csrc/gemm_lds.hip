@@ -35,6 +35,8 @@ using namespace nmk;
 using namespace nml;
 
 constexpr int BK = 64;                 // bf16 per K-step
+// s_waitcnt immediate for lgkmcnt(0) alone (vmcnt and expcnt at their maxima)
+constexpr int kWaitLgkm0 = 0xC07F;
 constexpr int ROWB = BK * 2;           // bytes per tile row per K-step
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -154,10 +156,22 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
   const int fr = lane & 15, fq = lane >> 4;
   const int nk = (int)((kend - kbeg) / BK);
 
-  // Multiply one staged K-step; the next stage's load groups are issued one A and one
-  // B group per MFMA step, spread over the matrix-instruction stream.
+  // Multiply one staged K-step (two 32-wide halves, FI row steps each).  Fragments are
+  // read one step ahead: the A fragment of the next row step, and during the first half
+  // the B fragments of the second, so no matrix instruction waits on the LDS read issued
+  // just before it.  The next stage's load groups are issued one A and one B group per
+  // row step.  Scheduling barriers keep the compiler from sinking the early reads below
+  // the matrix instructions.
+  auto read_a = [&](const unsigned char* abase, int ks, int i) {
+    const int r = wm * SM + i * 16 + fr;
+    return *reinterpret_cast<const u32x4*>(abase + r * ROWB + 16 * swz(r, 4 * ks + fq));
+  };
+  auto read_b = [&](const unsigned char* bbase, int ks, int j) {
+    const int r = wn * SN + j * 16 + fr;
+    return *reinterpret_cast<const u32x4*>(bbase + r * ROWB + 16 * swz(r, 4 * ks + fq));
+  };
   auto compute = [&](const unsigned char* abase, const unsigned char* bbase, const unsigned char* mbase,
-                     unsigned char* na, unsigned char* nb, unsigned char* nm, int64_t nk0, bool load_next) {
+                     unsigned char* na, unsigned char* nb, unsigned char* nm, int64_t nk0) {
     uint2 mw[FJ];
     if constexpr (PRO == PRO_MASK) {
 #pragma unroll
@@ -165,42 +179,58 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
         const int r = wn * SN + j * 16 + fr;
         mw[j] = *reinterpret_cast<const uint2*>(mbase + r * 8);
       }
-      if (load_next && wave < MASK_GROUPS) g2lds4(msrc + (nk0 >> 5), nm + wave * 256);
+      if (wave < MASK_GROUPS) g2lds4(msrc + (nk0 >> 5), nm + wave * 256);
     }
+    // the next stage's loads go out first: the first matrix step waits for every LDS read
+    // anyway, and no LDS read issued later has to wait behind a load still in flight
+#pragma unroll
+    for (int g = 0; g < NGA; ++g) g2lds16(asrc[g] + nk0, na + (wave + g * NW) * 1024);
+#pragma unroll
+    for (int g = 0; g < NGB; ++g) g2lds16(bsrc[g] + nk0, nb + (wave + g * NW) * 1024);
+    u32x4 b0[FJ], b1[FJ];
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) b0[j] = read_b(bbase, 0, j);
+    u32x4 acur = read_a(abase, 0, 0), anxt;
+    constexpr int BPS = (FJ + FI - 1) / FI;   // second-half B fragments read per row step
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int c = 4 * ks + fq;
       bf16x8 bfr[FJ];
 #pragma unroll
       for (int j = 0; j < FJ; ++j) {
-        const int r = wn * SN + j * 16 + fr;
+        u32x4 v = ks ? b1[j] : b0[j];
         if constexpr (PRO == PRO_MASK) {
-          u32x4 v = *reinterpret_cast<const u32x4*>(bbase + r * ROWB + 16 * swz(r, c));
           const uint32_t word = ks ? mw[j].y : mw[j].x;
           const uint32_t bits = word >> (8 * fq);
           v[0] = keep_pair(v[0], bits, 0);
           v[1] = keep_pair(v[1], bits, 1);
           v[2] = keep_pair(v[2], bits, 2);
           v[3] = keep_pair(v[3], bits, 3);
-          bfr[j] = __builtin_bit_cast(bf16x8, v);
-        } else {
-          bfr[j] = *reinterpret_cast<const bf16x8*>(bbase + r * ROWB + 16 * swz(r, c));
         }
+        bfr[j] = __builtin_bit_cast(bf16x8, v);
       }
 #pragma unroll
       for (int i = 0; i < FI; ++i) {
-        const int step = ks * FI + i;
-        if (load_next) {
-          if (step < NGA) g2lds16(asrc[step] + nk0, na + (wave + step * NW) * 1024);
-          if (step < NGB) g2lds16(bsrc[step] + nk0, nb + (wave + step * NW) * 1024);
+        // Wait for the reads issued one step ago before issuing this step's: while a
+        // direct-to-LDS load is in flight the compiler can only wait for all LDS reads,
+        // so a wait placed after the new reads would also wait for them.
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + 1 < FI) anxt = read_a(abase, ks, i + 1);
+        else if (ks == 0) anxt = read_a(abase, 1, 0);
+        if (ks == 0) {
+#pragma unroll
+          for (int q = 0; q < BPS; ++q)
+            if (i * BPS + q < FJ) b1[i * BPS + q] = read_b(bbase, 1, i * BPS + q);
         }
-        const int r = wm * SM + i * 16 + fr;
-        const bf16x8 af = *reinterpret_cast<const bf16x8*>(abase + r * ROWB + 16 * swz(r, c));
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 af = __builtin_bit_cast(bf16x8, acur);
         __builtin_amdgcn_s_setprio(1);   // keep the matrix pipe fed ahead of the other wave's memory work
 #pragma unroll
         for (int j = 0; j < FJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
         __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+        acur = anxt;
       }
     }
   };
@@ -208,13 +238,15 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
   issue_all(sA0, sB0, sM0, 0);
   __builtin_amdgcn_s_waitcnt(0);   // the staged tiles have landed in LDS
   __syncthreads();
-  // two K-steps per trip (stage 0, then stage 1)
+  // Two K-steps per trip (stage 0, then stage 1), each loading the step after it into
+  // the other stage.  The last step reloads step 0 into the idle stage instead (never
+  // read), so every step runs the same branch-free code.
   for (int kt = 0; kt < nk; kt += 2) {
-    compute(sA0, sB0, sM0, sA1, sB1, sM1, (int64_t)(kt + 1) * BK, kt + 1 < nk);
+    compute(sA0, sB0, sM0, sA1, sB1, sM1, kt + 1 < nk ? (int64_t)(kt + 1) * BK : 0);
     __builtin_amdgcn_s_waitcnt(0);   // next stage landed in LDS
     __syncthreads();
     if (kt + 1 < nk) {
-      compute(sA1, sB1, sM1, sA0, sB0, sM0, (int64_t)(kt + 2) * BK, kt + 2 < nk);
+      compute(sA1, sB1, sM1, sA0, sB0, sM0, kt + 2 < nk ? (int64_t)(kt + 2) * BK : 0);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
@@ -321,14 +353,38 @@ hipError_t launch_widen_fp8(const uint8_t* w8, int64_t ldw, int64_t o, int64_t k
   return hipGetLastError();
 }
 
-// Few-token variant: 256 output rows x 64 or 128 tokens per tile, split-K so that there
-// are about 512 workgroups; the slices' partial tiles are summed by a second kernel.
+// Few-token variant: 128 output rows x 64 or 128 tokens per tile, split-K so that the
+// grid has as many workgroups as fit one per CU (the splits' fp32 partial tiles are
+// summed in slice order by a second kernel).  Measured on gfx950 for 33-128 tokens: one
+// workgroup per CU beats two (twice the partial-sum traffic) and beats 256-row tiles
+// (fewer tiles, so more splits).  NM_TILE_BM=256, NM_TILE_WAVES=4 and NM_TILE_WG=<n>
+// (target workgroups) select the other shapes for A/B measurement.
+struct SmallCfg {
+  int bm, bn, waves;
+  int64_t target;
+};
+
+static int env_int(const char* name, int dflt) {
+  const char* e = std::getenv(name);
+  return e != nullptr ? std::atoi(e) : dflt;
+}
+
+static SmallCfg small_cfg(const GemmArgs& a) {
+  SmallCfg c;
+  c.bn = a.t <= 64 ? 64 : 128;
+  c.bm = env_int("NM_TILE_BM", 128) == 256 ? 256 : 128;
+  c.waves = env_int("NM_TILE_WAVES", 8) == 4 ? 4 : 8;
+  c.target = env_int("NM_TILE_WG", 256);
+  if (c.target < 1) c.target = 1;
+  return c;
+}
+
 static int64_t small_splits(const GemmArgs& a) {
-  const int bn = a.t <= 64 ? 64 : 128;
-  const int64_t tiles = ((a.o + 255) / 256) * ((a.t + bn - 1) / bn);
-  int64_t splits = (512 + tiles - 1) / tiles;
+  const SmallCfg c = small_cfg(a);
+  const int64_t tiles = ((a.o + c.bm - 1) / c.bm) * ((a.t + c.bn - 1) / c.bn);
+  int64_t splits = c.target / tiles;
   const int64_t ksteps = a.k / BK;
-  if (splits > ksteps / 2) splits = ksteps / 2 > 0 ? ksteps / 2 : 1;
+  if (splits > ksteps / 2) splits = ksteps / 2;
   return splits < 1 ? 1 : splits;
 }
 
@@ -345,8 +401,17 @@ int64_t gemm_lds_small_part_bytes(const GemmArgs& a) {
 hipError_t launch_gemm_lds_small(const GemmArgs& a, float* part, int64_t part_bytes, hipStream_t s) {
   int64_t splits = small_splits(a);
   if (part == nullptr || part_bytes < splits * a.t * a.o * 4) splits = 1;
-  if (a.t <= 64) return launch_cfg<256, 64, 8, 1, PRO_NONE>(a, s, splits, part);
-  return launch_cfg<256, 128, 4, 2, PRO_NONE>(a, s, splits, part);
+  const SmallCfg c = small_cfg(a);
+  if (c.bm == 256) {
+    if (a.t <= 64) return launch_cfg<256, 64, 8, 1, PRO_NONE>(a, s, splits, part);
+    return launch_cfg<256, 128, 4, 2, PRO_NONE>(a, s, splits, part);
+  }
+  if (a.t <= 64) {
+    if (c.waves == 4) return launch_cfg<128, 64, 2, 2, PRO_NONE>(a, s, splits, part);
+    return launch_cfg<128, 64, 4, 2, PRO_NONE>(a, s, splits, part);
+  }
+  if (c.waves == 4) return launch_cfg<128, 128, 2, 2, PRO_NONE>(a, s, splits, part);
+  return launch_cfg<128, 128, 4, 2, PRO_NONE>(a, s, splits, part);
 }
 
 }  // namespace nml

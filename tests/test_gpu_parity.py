@@ -313,8 +313,12 @@ def test_spmm_act_2of4_layer():
 
 
 # route overrides of the few-token dispatch: weight-streaming kernel, split-K tile kernel
-# (bf16 weights, K % 64 == 0; others fall back to streaming), or the large-T tile kernels
-FEW_ROUTES = {"stream": {"NM_FEW_ROUTE": "stream"}, "tile": {"NM_FEW_ROUTE": "tile"}, "off": {"NM_FEW": "0"}}
+# (bf16 weights, K % 64 == 0; others fall back to streaming) in its default 128-row shape,
+# its 256-row and 4-wave shapes and a forced workgroup count, or the large-T tile kernels
+FEW_ROUTES = {"stream": {"NM_FEW_ROUTE": "stream"}, "tile": {"NM_FEW_ROUTE": "tile"},
+              "tile256": {"NM_FEW_ROUTE": "tile", "NM_TILE_BM": "256"},
+              "tile4w": {"NM_FEW_ROUTE": "tile", "NM_TILE_WAVES": "4", "NM_TILE_WG": "37"},
+              "off": {"NM_FEW": "0"}}
 
 
 def run_w(mode, x, v, mt, o, k, ns=2, workspace=True, accumulate=0, y0=None):
@@ -546,6 +550,21 @@ def test_spmm_act_full_size_sampled(route):
         sx, keep = O.sparsify(x[rows], 8, 16)
         assert (mask[rows] == O.pack_mask(keep)).all()
         check_gemm(y[rows], O.gemm(sx, w), sx, w, label=f"full t={t}")
+
+
+@pytest.mark.parametrize("t", [1, 16, 33, 64, 128])
+def test_spmm_act_decode_full_size_sampled(t):
+    """8:16 down-projection (W 4096 x 14336) at decode token counts on the default routes
+    (select + streaming kernel up to 32 tokens, select + split-K tile kernel above);
+    oracle on sampled output rows."""
+    print(f"act decode full t={t}", flush=True)
+    d = synth.mlp_down_8of16(t_max=128)
+    x, w = d["x"][:t], d["w"]
+    y, mask = run_act(x, w, 8, 16)
+    rows = sample_rows(t, 12, seed=t)
+    sx, keep = O.sparsify(x[rows], 8, 16)
+    assert (mask[rows] == O.pack_mask(keep)).all()
+    check_gemm(y[rows], O.gemm(sx, w), sx, w, label=f"decode full t={t}")
 
 
 # ------------------------------------------------------------------- weight 2:4 ---
