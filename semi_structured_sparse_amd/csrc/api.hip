@@ -158,16 +158,56 @@ int64_t w_mode_kc(const nm_spmm_args* a) {
   return a->k;
 }
 
-// Large-token ACT_DYNAMIC with fp8 weights: the weights are widened once to bf16 in the
+// Row stride of a materialised lifted X (16-byte rows).
+inline int64_t lift_ld(int64_t kp) { return (kp + 7) / 8 * 8; }
+
+// Few-token products with a 2:4 weight operand (plain, lowered or hybrid): the split-K
+// tile kernel, whose workgroups share each X slice through LDS across 128 weight rows,
+// when its shape rules hold (plain loader: lowered weights read a lifted copy of X), above
+// 32 tokens for weights of at least 2048 rows and above 16 tokens from 8192 rows; the
+// streaming kernel otherwise.  Measured on gfx950: 6:8 lowered 4096 x 4096 at 128 tokens
+// 30 vs 58 us, 14336 x 4096 at 16 tokens 40 vs 56 us; 2:4 14336 x 4096 at 33 tokens 31 vs
+// 38 us.  NM_FEW_ROUTE=stream|tile forces either for A/B measurement.
+bool sp_few_tile(const nml::SparseArgs& sa) {
+  if (!nml::gemm_lds_sp_eligible(sa, true)) return false;
+  const char* e = std::getenv("NM_FEW_ROUTE");
+  if (e != nullptr && std::strcmp(e, "tile") == 0) return true;
+  if (e != nullptr && std::strcmp(e, "stream") == 0) return false;
+  return (sa.t > 32 && sa.o >= 2048) || (sa.t > 16 && sa.o >= 8192);
+}
+
+// The W_* modes as a tile-kernel call; lowered weights read X lifted into a buffer of
+// row stride lift_ld(kc) (pointer filled in by the caller).
+nml::SparseArgs w_mode_sparse_args(const nm_spmm_args* a, int64_t kc, int ns) {
+  nml::SparseArgs sa{};
+  sa.w_vals = (const uint16_t*)a->w; sa.w_meta = (const uint8_t*)a->w_meta; sa.kc = kc;
+  sa.x = (const uint16_t*)a->x; sa.ldx = a->ldx; sa.ns = ns;
+  sa.loader = nml::XL_PLAIN;
+  if (a->mode == NM_W_SLIDE) sa.ldx = lift_ld(kc);
+  sa.t = a->t; sa.o = a->o; sa.y = a->y; sa.ldy = a->ldy; sa.accumulate = a->accumulate; sa.trans_out = 0;
+  return sa;
+}
+
+// Workspace bytes of the few-token tile route of the W_* modes: [lifted X][partials].
+int64_t w_mode_tile_bytes(const nm_spmm_args* a, int64_t kc, int ns) {
+  const nml::SparseArgs sa = w_mode_sparse_args(a, kc, ns);
+  if (!sp_few_tile(sa)) return 0;
+  const int64_t lift = a->mode == NM_W_SLIDE ? align256(a->t * lift_ld(kc) * 2) : 0;
+  return lift + nml::gemm_lds_sp_small_part_bytes(sa);
+}
+
+// Large-token ACT_DYNAMIC with fp8 weights: bytes of a bf16 copy of the weights in the
 // workspace (after the S(X) staging) for the direct-to-LDS product kernel.
+// Only when the codes cannot go to LDS directly (rows not 16-byte multiples), or when
+// NM_FP8_WIDEN=1 asks for it (A/B measurement).
 int64_t fp8_widen_bytes(const nm_spmm_args* a) {
   if (a->mode != NM_ACT_DYNAMIC || a->w_dtype != NM_W_FP8E4M3 || use_few(a->t)) return 0;
   if (a->k % 64 != 0 || a->t < 512) return 0;
+  const char* e = std::getenv("NM_FP8_WIDEN");
+  const bool force = e != nullptr && std::strcmp(e, "1") == 0;
+  if (!force && a->ldw % 16 == 0) return 0;
   return a->o * a->k * 2;
 }
-
-// Row stride of a materialised lifted X (16-byte rows).
-inline int64_t lift_ld(int64_t kp) { return (kp + 7) / 8 * 8; }
 
 // Bytes of S(X) / decompressed-X staging at the start of nm_spmm's workspace.
 int64_t spmm_stage_bytes(const nm_spmm_args* a) {
@@ -196,6 +236,18 @@ nml::FewArgs few_hybrid_args(const uint16_t* x, int64_t ldx, int64_t dbase, int6
   }
   f.t = t; f.o = o; f.y = y; f.ldy = ldy; f.accumulate = accumulate;
   return f;
+}
+
+nml::SparseArgs hybrid_sparse_args(const uint16_t* x, int64_t ldx, int64_t dbase, int64_t t, int64_t k_s,
+                                   int64_t k_d, const void* ws_values, const void* ws_meta, const void* wd,
+                                   int64_t ldwd, int64_t o, float* y, int64_t ldy, int accumulate) {
+  nml::SparseArgs sa{};
+  sa.w_vals = (const uint16_t*)ws_values; sa.w_meta = (const uint8_t*)ws_meta; sa.kc = k_s;
+  sa.x = x; sa.ldx = ldx; sa.loader = nml::XL_PLAIN;
+  sa.t = t; sa.o = o;
+  sa.wd = (const uint16_t*)wd; sa.ldwd = ldwd; sa.kd = k_d; sa.dbase = dbase;
+  sa.y = y; sa.ldy = ldy; sa.accumulate = accumulate; sa.trans_out = 0;
+  return sa;
 }
 
 }  // namespace
@@ -307,7 +359,10 @@ int64_t nm_spmm_workspace_size(const nm_spmm_args* a) {
   if (use_few(a->t) && a->t > 0 && a->o > 0 && a->k > 0) {
     if (a->mode == NM_W_COMPRESSED || a->mode == NM_W_SLIDE) {
       if (a->mode == NM_W_SLIDE && (a->ns < 2 || a->ns > 8 || a->k % (2 * a->ns))) return 0;
-      part = nml::few_partial_bytes(few_sparse_args(a, w_mode_kc(a), a->mode == NM_W_SLIDE ? a->ns : 2));
+      const int ns = a->mode == NM_W_SLIDE ? a->ns : 2;
+      const int64_t tile = w_mode_tile_bytes(a, w_mode_kc(a), ns);
+      if (tile > 0) return tile;
+      part = nml::few_partial_bytes(few_sparse_args(a, w_mode_kc(a), ns));
     } else if (a->mode == NM_ACT_DYNAMIC || a->mode == NM_ACT_COMPRESSED ||
                (a->mode == NM_ACT_MASKED && a->x_meta == nullptr)) {
       nml::GemmArgs g{};
@@ -484,9 +539,24 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
       if (!span_ok(O, kc)) return NM_ESHAPE;
       if (T == 0 || O == 0) return NM_OK;
       if (K == 0) return a->accumulate ? NM_OK : zero_output(a->y, T, O, a->ldy, s);
-      if (use_few(T))
+      if (use_few(T)) {
+        const int64_t tile = w_mode_tile_bytes(a, kc, ns);
+        if (tile > 0 && a->workspace != nullptr && a->workspace_bytes >= tile) {
+          nml::SparseArgs sa = w_mode_sparse_args(a, kc, ns);
+          int64_t off = 0;
+          if (a->mode == NM_W_SLIDE) {
+            uint16_t* xl = (uint16_t*)a->workspace;
+            hipError_t e = nml::launch_lift(ns, (const uint16_t*)a->x, T, K, a->ldx, xl, lift_ld(kc), s);
+            if (e != hipSuccess) return NM_EHIP;
+            sa.x = xl;
+            off = align256(T * lift_ld(kc) * 2);
+          }
+          return hip_status(nml::launch_gemm_lds_sp_small(
+              sa, reinterpret_cast<float*>(reinterpret_cast<char*>(a->workspace) + off), a->workspace_bytes - off, s));
+        }
         return hip_status(nml::launch_few(few_sparse_args(a, kc, ns), (float*)a->workspace,
                                           a->workspace ? a->workspace_bytes : 0, s));
+      }
       nml::SparseArgs sa{};
       sa.w_vals = (const uint16_t*)a->w; sa.w_meta = (const uint8_t*)a->w_meta; sa.kc = kc;
       sa.x = (const uint16_t*)a->x; sa.ldx = a->ldx; sa.ns = ns;
@@ -538,8 +608,11 @@ int64_t nm_hybrid_gemm_workspace_size(int64_t t, int64_t k_s, int64_t k_d, int64
   int64_t part = 0;
   if (use_few(t)) {
     const int64_t ldp = gathered ? hybrid_ldp(k_s, k_d) : k_s + k_d;
-    part = nml::few_partial_bytes(few_hybrid_args(nullptr, ldp, 0, t, k_s, k_d, nullptr, nullptr, nullptr, k_d, o,
-                                                  nullptr, o, 0));
+    const nml::SparseArgs sa = hybrid_sparse_args(nullptr, ldp, gathered ? hybrid_off1(k_s) : k_s, t, k_s, k_d,
+                                                  nullptr, nullptr, nullptr, k_d, o, nullptr, o, 0);
+    part = sp_few_tile(sa) ? nml::gemm_lds_sp_small_part_bytes(sa)
+                           : nml::few_partial_bytes(few_hybrid_args(nullptr, ldp, 0, t, k_s, k_d, nullptr, nullptr,
+                                                                    nullptr, k_d, o, nullptr, o, 0));
   }
   return part > 0 ? align256(stage) + part : stage;
 }
@@ -590,19 +663,17 @@ nm_status nm_hybrid_gemm(const void* x, int64_t t, int64_t ldx, const int32_t* s
     if (e != hipSuccess) return NM_EHIP;
     xa = xp; lda = ldp; dbase = hybrid_off1(k_s);
   }
+  const nml::SparseArgs sa = hybrid_sparse_args(xa, lda, dbase, t, k_s, k_d, ws_values, ws_meta, wd, ldwd, o, y,
+                                                ldy, accumulate);
   if (use_few(t)) {
     int64_t avail = 0;
     float* part = ws_slice(workspace, workspace_bytes, stage > 0 ? align256(stage) : 0, &avail);
+    if (sp_few_tile(sa) && avail >= nml::gemm_lds_sp_small_part_bytes(sa))
+      return hip_status(nml::launch_gemm_lds_sp_small(sa, part, avail, s));
     return hip_status(nml::launch_few(few_hybrid_args(xa, lda, dbase, t, k_s, k_d, ws_values, ws_meta, wd, ldwd, o,
                                                       y, ldy, accumulate),
                                       part, avail, s));
   }
-  nml::SparseArgs sa{};
-  sa.w_vals = (const uint16_t*)ws_values; sa.w_meta = (const uint8_t*)ws_meta; sa.kc = k_s;
-  sa.x = xa; sa.ldx = lda; sa.loader = nml::XL_PLAIN;
-  sa.t = t; sa.o = o;
-  sa.wd = (const uint16_t*)wd; sa.ldwd = ldwd; sa.kd = k_d; sa.dbase = dbase;
-  sa.y = y; sa.ldy = ldy; sa.accumulate = accumulate; sa.trans_out = 0;
   return hip_status(nml::launch_gemm_sparse(sa, s));
 }
 

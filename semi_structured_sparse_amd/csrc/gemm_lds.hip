@@ -41,7 +41,8 @@ constexpr int ROWB = BK * 2;           // bytes per tile row per K-step
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }    // 8 pieces per row
+__device__ __forceinline__ int swz4(int r, int c) { return c ^ ((r >> 2) & 3); }   // 4 pieces per row
 
 // global -> LDS copy of `bytes` (4 or 16) per lane: lane i writes lds + i * bytes.  The
 // LDS address must be wave-uniform (it is passed in M0).
@@ -59,18 +60,20 @@ __device__ __forceinline__ uint32_t keep_pair(uint32_t d, uint32_t bits, int q) 
   return d & ((hi & 0xFFFF0000u) | (lo & 0x0000FFFFu));
 }
 
-template <int BM, int BN, int WM, int WN, int PRO>
+template <int BM, int BN, int WM, int WN, int PRO, bool W8>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
-    const uint16_t* __restrict__ w, int64_t ldw, const uint16_t* __restrict__ x, int64_t ldx,
+    const unsigned char* __restrict__ w, int64_t ldw, const uint16_t* __restrict__ x, int64_t ldx,
     const uint32_t* __restrict__ xmask, int64_t T, int64_t O, int64_t K, float* __restrict__ y,
     int64_t ldy, int accumulate, int tiles_m, int tiles_n, int64_t kslice, float* __restrict__ part,
     const float* __restrict__ wscale) {
   constexpr int NW = WM * WN;
   constexpr int SM = BM / WM, SN = BN / WN;       // wave sub-tile (o x t)
   constexpr int FI = SM / 16, FJ = SN / 16;
-  constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
+  // W rows per K-step: 128 bytes of bf16, or 64 bytes of fp8 codes (4 pieces per row)
+  constexpr int AROWB = W8 ? 64 : ROWB, A_RPG = W8 ? 16 : 8;   // bytes per row, rows per load group
+  constexpr int A_BYTES = BM * AROWB, B_BYTES = BN * ROWB;
   constexpr int MASK_BYTES = (PRO == PRO_MASK) ? BN * 8 : 16;
-  constexpr int A_GROUPS = BM / 8, B_GROUPS = BN / 8;   // 8-row load groups
+  constexpr int A_GROUPS = BM / A_RPG, B_GROUPS = BN / 8;   // load groups (1 KiB each)
   constexpr int NGA = A_GROUPS / NW, NGB = B_GROUPS / NW;
   static_assert(A_GROUPS % NW == 0 && B_GROUPS % NW == 0, "load groups per wave");
   static_assert(NGA <= 2 * FI && NGB <= 2 * FI, "load groups are spread over the 2*FI MFMA steps");
@@ -103,14 +106,15 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
 
   // per-lane global source addresses of this wave's load groups (K offset added per step)
   const int lrow = lane >> 3, lchunk = lane & 7;
-  const uint16_t* asrc[NGA];
+  const unsigned char* asrc[NGA];
   const uint16_t* bsrc[NGB];
+  constexpr int WBYTES = W8 ? 1 : 2;   // bytes per weight element
 #pragma unroll
   for (int g = 0; g < NGA; ++g) {
-    const int r = (wave + g * NW) * 8 + lrow;
+    const int r = (wave + g * NW) * A_RPG + (W8 ? (lane >> 2) : lrow);
     int64_t o = o0 + r;
     if (o >= O) o = O - 1;
-    asrc[g] = w + o * ldw + 8 * swz(r, lchunk);
+    asrc[g] = w + (o * ldw) * WBYTES + 16 * (W8 ? swz4(r, lane & 3) : swz(r, lchunk));
   }
 #pragma unroll
   for (int g = 0; g < NGB; ++g) {
@@ -130,7 +134,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
   }
   // the slice's K offset is folded into the source addresses
 #pragma unroll
-  for (int g = 0; g < NGA; ++g) asrc[g] += kbeg;
+  for (int g = 0; g < NGA; ++g) asrc[g] += kbeg * WBYTES;
 #pragma unroll
   for (int g = 0; g < NGB; ++g) bsrc[g] += kbeg;
   if constexpr (PRO == PRO_MASK) {
@@ -139,7 +143,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
 
   auto issue_all = [&](unsigned char* a, unsigned char* b, unsigned char* mk, int64_t k0) {
 #pragma unroll
-    for (int g = 0; g < NGA; ++g) g2lds16(asrc[g] + k0, a + (wave + g * NW) * 1024);
+    for (int g = 0; g < NGA; ++g) g2lds16(asrc[g] + k0 * WBYTES, a + (wave + g * NW) * 1024);
 #pragma unroll
     for (int g = 0; g < NGB; ++g) g2lds16(bsrc[g] + k0, b + (wave + g * NW) * 1024);
     if constexpr (PRO == PRO_MASK) {
@@ -162,9 +166,25 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
   // just before it.  The next stage's load groups are issued one A and one B group per
   // row step.  Scheduling barriers keep the compiler from sinking the early reads below
   // the matrix instructions.
+  // A fragment: 8 bf16 (16 bytes), or 8 fp8 codes (8 bytes, widened when used)
   auto read_a = [&](const unsigned char* abase, int ks, int i) {
     const int r = wm * SM + i * 16 + fr;
-    return *reinterpret_cast<const u32x4*>(abase + r * ROWB + 16 * swz(r, 4 * ks + fq));
+    if constexpr (W8) {
+      const uint2 q = *reinterpret_cast<const uint2*>(abase + r * 64 + 16 * swz4(r, 2 * ks + (fq >> 1)) + 8 * (fq & 1));
+      return u32x4{q.x, q.y, 0u, 0u};
+    } else {
+      return *reinterpret_cast<const u32x4*>(abase + r * ROWB + 16 * swz(r, 4 * ks + fq));
+    }
+  };
+  auto a_frag = [&](u32x4 v) {
+    if constexpr (W8) {
+      uint32_t c0, c1, c2, c3;
+      fp8x4_to_bf16x4(v[0], c0, c1);
+      fp8x4_to_bf16x4(v[1], c2, c3);
+      return __builtin_bit_cast(bf16x8, u32x4{c0, c1, c2, c3});
+    } else {
+      return __builtin_bit_cast(bf16x8, v);
+    }
   };
   auto read_b = [&](const unsigned char* bbase, int ks, int j) {
     const int r = wn * SN + j * 16 + fr;
@@ -184,7 +204,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
     // the next stage's loads go out first: the first matrix step waits for every LDS read
     // anyway, and no LDS read issued later has to wait behind a load still in flight
 #pragma unroll
-    for (int g = 0; g < NGA; ++g) g2lds16(asrc[g] + nk0, na + (wave + g * NW) * 1024);
+    for (int g = 0; g < NGA; ++g) g2lds16(asrc[g] + nk0 * WBYTES, na + (wave + g * NW) * 1024);
 #pragma unroll
     for (int g = 0; g < NGB; ++g) g2lds16(bsrc[g] + nk0, nb + (wave + g * NW) * 1024);
     u32x4 b0[FJ], b1[FJ];
@@ -223,7 +243,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
             if (i * BPS + q < FJ) b1[i * BPS + q] = read_b(bbase, 1, i * BPS + q);
         }
         __builtin_amdgcn_sched_barrier(0);
-        const bf16x8 af = __builtin_bit_cast(bf16x8, acur);
+        const bf16x8 af = a_frag(acur);
         __builtin_amdgcn_s_setprio(1);   // keep the matrix pipe fed ahead of the other wave's memory work
 #pragma unroll
         for (int j = 0; j < FJ; ++j)
@@ -289,7 +309,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
   }
 }
 
-template <int BM, int BN, int WM, int WN, int PRO>
+template <int BM, int BN, int WM, int WN, int PRO, bool W8 = false>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s, int64_t splits, float* part) {
   const int tiles_m = (int)((a.o + BM - 1) / BM), tiles_n = (int)((a.t + BN - 1) / BN);
   const int64_t ntiles = (int64_t)tiles_m * tiles_n;
@@ -297,9 +317,9 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s, int64_t splits, float* p
   int64_t kslice = ((a.k / BK + splits - 1) / splits) * BK;
   splits = (a.k + kslice - 1) / kslice;
   if (ntiles * splits > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  auto kern = k_gemm_lds<BM, BN, WM, WN, PRO>;
+  auto kern = k_gemm_lds<BM, BN, WM, WN, PRO, W8>;
   kern<<<dim3((unsigned)(ntiles * splits)), dim3(64 * WM * WN), 0, s>>>(
-      (const uint16_t*)a.w, a.ldw, a.x, a.ldx, a.x_mask, a.t, a.o, a.k, a.y, a.ldy, a.accumulate, tiles_m, tiles_n,
+      (const unsigned char*)a.w, a.ldw, a.x, a.ldx, a.x_mask, a.t, a.o, a.k, a.y, a.ldy, a.accumulate, tiles_m, tiles_n,
       kslice, splits > 1 ? part : nullptr, a.w_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
@@ -310,11 +330,17 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s, int64_t splits, float* p
 
 namespace nml {
 
+// fp8 weights: rows of codes straight into LDS (ldw a multiple of 16 bytes), widened to
+// bf16 per fragment; with the plain prologue only.
+static bool w_rows_ok(const GemmArgs& a) {
+  if (a.w_fp8) return a.prologue == PRO_NONE && (a.ldw % 16) == 0;
+  return (a.ldw % 8) == 0;
+}
+
 bool gemm_lds_eligible(const GemmArgs& a, bool any_size) {
-  if (a.w_fp8) return false;
   if (a.prologue != PRO_NONE && a.prologue != PRO_MASK) return false;
   if (a.k % BK != 0 || a.k == 0) return false;
-  if ((a.ldw % 8) || (a.ldx % 8)) return false;
+  if (!w_rows_ok(a) || (a.ldx % 8)) return false;
   // enough tiles to fill the machine with 256x256 tiles
   return any_size || ((a.o + 255) / 256) * ((a.t + 255) / 256) >= 128;
 }
@@ -326,12 +352,16 @@ hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t s) {
     if (half) return launch_cfg<256, 128, 4, 2, PRO_MASK>(a, s, 1, nullptr);
     return launch_cfg<256, 256, 4, 2, PRO_MASK>(a, s, 1, nullptr);
   }
+  if (a.w_fp8) {
+    if (half) return launch_cfg<256, 128, 4, 2, PRO_NONE, true>(a, s, 1, nullptr);
+    return launch_cfg<256, 256, 4, 2, PRO_NONE, true>(a, s, 1, nullptr);
+  }
   if (half) return launch_cfg<256, 128, 4, 2, PRO_NONE>(a, s, 1, nullptr);
   return launch_cfg<256, 256, 4, 2, PRO_NONE>(a, s, 1, nullptr);
 }
 
-// fp8 weights for the large-token product: widened once to bf16 (exact), then the
-// direct-to-LDS kernel with the per-row scale in its epilogue.
+// fp8 weights widened once to bf16 (exact), for the kernels that read bf16 weights only
+// (kept as an A/B alternative to the fp8 direct-to-LDS variant).
 __global__ void k_widen_fp8(const uint8_t* __restrict__ w8, int64_t ldw, int64_t O, int64_t K,
                             uint16_t* __restrict__ wb) {
   const int64_t per_row = K / 8;
@@ -372,7 +402,7 @@ static int env_int(const char* name, int dflt) {
 static SmallCfg small_cfg(const GemmArgs& a) {
   SmallCfg c;
   c.bn = a.t <= 64 ? 64 : 128;
-  c.bm = env_int("NM_TILE_BM", 128) == 256 ? 256 : 128;
+  c.bm = (env_int("NM_TILE_BM", 128) == 256 && !a.w_fp8) ? 256 : 128;
   c.waves = env_int("NM_TILE_WAVES", 8) == 4 ? 4 : 8;
   c.target = env_int("NM_TILE_WG", 256);
   if (c.target < 1) c.target = 1;
@@ -389,8 +419,7 @@ static int64_t small_splits(const GemmArgs& a) {
 }
 
 bool gemm_lds_small_eligible(const GemmArgs& a) {
-  return a.prologue == PRO_NONE && !a.w_fp8 && a.k % BK == 0 && a.k > 0 &&
-         (a.ldw % 8) == 0 && (a.ldx % 8) == 0 && a.t <= 128;
+  return a.prologue == PRO_NONE && a.k % BK == 0 && a.k > 0 && w_rows_ok(a) && (a.ldx % 8) == 0 && a.t <= 128;
 }
 
 int64_t gemm_lds_small_part_bytes(const GemmArgs& a) {
@@ -402,6 +431,10 @@ hipError_t launch_gemm_lds_small(const GemmArgs& a, float* part, int64_t part_by
   int64_t splits = small_splits(a);
   if (part == nullptr || part_bytes < splits * a.t * a.o * 4) splits = 1;
   const SmallCfg c = small_cfg(a);
+  if (a.w_fp8) {
+    if (a.t <= 64) return launch_cfg<128, 64, 4, 2, PRO_NONE, true>(a, s, splits, part);
+    return launch_cfg<128, 128, 4, 2, PRO_NONE, true>(a, s, splits, part);
+  }
   if (c.bm == 256) {
     if (a.t <= 64) return launch_cfg<256, 64, 8, 1, PRO_NONE>(a, s, splits, part);
     return launch_cfg<256, 128, 4, 2, PRO_NONE>(a, s, splits, part);

@@ -10,6 +10,10 @@
 // gfx950 design, after the dense direct-to-LDS kernel:
 //  * 256 x 256 output tile, 8 waves of 64 (o) x 128 (t); two LDS stages, each a distinct
 //    static array (so the compiler tracks the DMA into each one separately).
+//  * Few tokens (33-128): 128 x 64 or 128 x 128 tiles and a reduction split across
+//    workgroups (one per CU); each split writes its fp32 partial tile, and a second
+//    kernel sums the splits in a fixed order.  The sparse and dense steps form one
+//    reduction sequence that the splits cut into contiguous ranges.
 //  * One sparse K-step covers 64 reduction positions: per weight row 64 bytes of
 //    compressed values (global_load_lds_dwordx4, 4 lanes per row) and 8 bytes of 2-bit
 //    positions (global_load_lds_dword, 2 lanes per row); per token row 128 bytes of X
@@ -37,30 +41,40 @@ __device__ __forceinline__ void g2lds4(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
 }
 
-constexpr int BM = 256, BN = 256, WM = 4, WN = 2, NW = WM * WN;
-constexpr int SM = BM / WM, SN = BN / WN, FI = SM / 16, FJ = SN / 16;
-constexpr int A_BYTES = BM * 128;          // dense W rows (sparse phase: values + positions)
-constexpr int SV_BYTES = BM * 64;          // compressed values per sparse step
-constexpr int B_BYTES = BN * 128;          // X rows
 constexpr int GROUP = 16;
 
 __device__ __forceinline__ int swz8(int r, int c) { return c ^ ((r >> 1) & 7); }   // 8 pieces per row
 __device__ __forceinline__ int swz4(int r, int c) { return c ^ ((r >> 2) & 3); }   // 4 pieces per row
 
-__global__ __launch_bounds__(64 * NW) void k_gemm_lds_sp(
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
     const uint16_t* __restrict__ wv, const uint8_t* __restrict__ wm, int64_t kc, const uint16_t* __restrict__ x,
     int64_t ldx, const uint16_t* __restrict__ wd, int64_t ldwd, int64_t kd, int64_t dbase, int64_t T, int64_t O,
-    float* __restrict__ y, int64_t ldy, int accumulate, int tiles_m, int tiles_n) {
+    float* __restrict__ y, int64_t ldy, int accumulate, int tiles_m, int tiles_n, int steps_per_split,
+    float* __restrict__ part) {
+  constexpr int NW = WM * WN;
+  constexpr int SM = BM / WM, SN = BN / WN, FI = SM / 16, FJ = SN / 16;
+  constexpr int A_BYTES = BM * 128;          // dense W rows (sparse phase: values + positions)
+  constexpr int SV_BYTES = BM * 64;          // compressed values per sparse step
+  constexpr int B_BYTES = BN * 128;          // X rows
+  constexpr int NV = BM / 16 / NW;           // value load groups (16 rows) per wave
+  constexpr int NMW = BM / 32;               // waves that load positions (32 rows each)
+  constexpr int NX = BN / 8 / NW;            // X load groups (8 rows) per wave
+  constexpr int ND = BM / 8 / NW;            // dense weight load groups (8 rows) per wave
+  static_assert(NV >= 1 && NX >= 1 && ND >= 1 && NMW <= NW && BM % (16 * NW) == 0 && BN % (8 * NW) == 0,
+                "load groups per wave");
   __shared__ __align__(16) unsigned char sA0[A_BYTES], sB0[B_BYTES];
   __shared__ __align__(16) unsigned char sA1[A_BYTES], sB1[B_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wmi = wave % WM, wni = wave / WM;
 
-  // XCD-aware tile order (workgroup b runs on XCD b % 8), bands of GROUP o-tiles
+  // XCD-aware tile order (workgroup b runs on XCD b % 8), bands of GROUP o-tiles; with a
+  // split reduction, block b takes split b / ntiles of tile b % ntiles
   const int ntiles = tiles_m * tiles_n;
-  int lin = blockIdx.x;
-  if ((ntiles & 7) == 0) lin = (blockIdx.x & 7) * (ntiles >> 3) + (blockIdx.x >> 3);
+  const int kpart = blockIdx.x / ntiles;
+  int lin = blockIdx.x - kpart * ntiles;
+  if ((ntiles & 7) == 0 && gridDim.x == (unsigned)ntiles) lin = (blockIdx.x & 7) * (ntiles >> 3) + (blockIdx.x >> 3);
   const int band = lin / (GROUP * tiles_n);
   const int band_w = min(GROUP, tiles_m - band * GROUP);
   const int inband = lin - band * GROUP * tiles_n;
@@ -68,7 +82,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_lds_sp(
   const int64_t o0 = (int64_t)tile_m * BM, t0 = (int64_t)tile_n * BN;
 
   const int64_t kcv = kc / 2, mstride = kc / 8;
-  const int nks = (int)(kc / 64), nkd = (int)(kd / 64), nk = nks + nkd;
+  // this split's range [sb, se) of the step sequence (sparse steps, then dense steps)
+  const int nks_all = (int)(kc / 64), nk_all = nks_all + (int)(kd / 64);
+  const int sb = kpart * steps_per_split;
+  const int se = min(nk_all, sb + steps_per_split);
+  const int ks0 = min(sb, nks_all), ks1 = min(se, nks_all);          // sparse steps [ks0, ks1)
+  const int kd0 = max(sb, nks_all) - nks_all, kd1 = max(se, nks_all) - nks_all;   // dense [kd0, kd1)
+  const int nks = ks1 - ks0, nkd = kd1 - kd0;
 
   f32x4 acc[FI][FJ];
 #pragma unroll
@@ -77,10 +97,10 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_lds_sp(
     for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int fr = lane & 15, fg = lane >> 4;
 
-  // X rows: groups of 8 rows (8 lanes x 16 bytes per row), 4 per wave
-  const uint16_t* xsrc[4];
+  // X rows: groups of 8 rows (8 lanes x 16 bytes per row), NX per wave
+  const uint16_t* xsrc[NX];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < NX; ++q) {
     const int r = (wave + q * NW) * 8 + (lane >> 3);
     int64_t t = t0 + r;
     t = t < T ? t : T - 1;
@@ -89,11 +109,11 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_lds_sp(
 
   // ----------------------------------------------------------- sparse phase ---
   if (nks > 0) {
-    // compressed values: groups of 16 rows (4 lanes x 16 bytes per row), 2 per wave;
-    // positions: 32 rows per wave (2 lanes x 4 bytes per row)
-    const uint8_t* vsrc[2];
+    // compressed values: groups of 16 rows (4 lanes x 16 bytes per row), NV per wave;
+    // positions: 32 rows per loading wave (2 lanes x 4 bytes per row)
+    const uint8_t* vsrc[NV];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < NV; ++q) {
       const int r = (wave + q * NW) * 16 + (lane >> 2);
       int64_t o = o0 + r;
       o = o < O ? o : O - 1;
@@ -101,18 +121,18 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_lds_sp(
     }
     const uint8_t* msrc;
     {
-      const int r = wave * 32 + (lane >> 1);
+      const int r = (wave < NMW ? wave : 0) * 32 + (lane >> 1);
       int64_t o = o0 + r;
       o = o < O ? o : O - 1;
       msrc = wm + o * mstride + 4 * (lane & 1);
     }
     auto issue = [&](unsigned char* a, unsigned char* b, int s) {
-      const int64_t k0 = (int64_t)s * 64;   // dense positions; also the byte offset of the values
+      const int64_t k0 = (int64_t)(ks0 + s) * 64;   // dense positions; also the byte offset of the values
 #pragma unroll
-      for (int q = 0; q < 2; ++q) g2lds16(vsrc[q] + k0, a + (wave + q * NW) * 1024);
-      g2lds4(msrc + (k0 >> 3), a + SV_BYTES + wave * 256);
+      for (int q = 0; q < NV; ++q) g2lds16(vsrc[q] + k0, a + (wave + q * NW) * 1024);
+      if (wave < NMW) g2lds4(msrc + (k0 >> 3), a + SV_BYTES + wave * 256);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) g2lds16(xsrc[q] + k0, b + (wave + q * NW) * 1024);
+      for (int q = 0; q < NX; ++q) g2lds16(xsrc[q] + k0, b + (wave + q * NW) * 1024);
     };
     auto compute = [&](const unsigned char* a, const unsigned char* b) {
       bf16x8 af[FI];
@@ -157,21 +177,21 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_lds_sp(
 
   // ------------------------------------------------------------ dense phase ---
   if (nkd > 0) {
-    // dense weight rows: groups of 8 rows (8 lanes x 16 bytes per row), 4 per wave
-    const uint16_t* dsrc[4];
+    // dense weight rows: groups of 8 rows (8 lanes x 16 bytes per row), ND per wave
+    const uint16_t* dsrc[ND];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < ND; ++q) {
       const int r = (wave + q * NW) * 8 + (lane >> 3);
       int64_t o = o0 + r;
       o = o < O ? o : O - 1;
       dsrc[q] = wd + o * ldwd + 8 * swz8(r, lane & 7);
     }
     auto issue = [&](unsigned char* a, unsigned char* b, int s) {
-      const int64_t j0 = (int64_t)s * 64;
+      const int64_t j0 = (int64_t)(kd0 + s) * 64;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) g2lds16(dsrc[q] + j0, a + (wave + q * NW) * 1024);
+      for (int q = 0; q < ND; ++q) g2lds16(dsrc[q] + j0, a + (wave + q * NW) * 1024);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) g2lds16(xsrc[q] + dbase + j0, b + (wave + q * NW) * 1024);
+      for (int q = 0; q < NX; ++q) g2lds16(xsrc[q] + dbase + j0, b + (wave + q * NW) * 1024);
     };
     auto compute = [&](const unsigned char* a, const unsigned char* b) {
 #pragma unroll
@@ -221,7 +241,12 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_lds_sp(
       const int64_t t = t0 + wni * SN + j * 16 + fr;
       if (t >= T) continue;
       float* yp = y + t * ldy + ob;
-      if (vec_ok && ob + 4 <= O) {
+      if (part != nullptr) {
+        float* pp = part + ((int64_t)kpart * T + t) * O + ob;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (ob + r < O) pp[r] = acc[i][j][r];
+      } else if (vec_ok && ob + 4 <= O) {
         float4 cur = accumulate ? *reinterpret_cast<float4*>(yp) : make_float4(0.f, 0.f, 0.f, 0.f);
         *reinterpret_cast<float4*>(yp) =
             make_float4(cur.x + acc[i][j][0], cur.y + acc[i][j][1], cur.z + acc[i][j][2], cur.w + acc[i][j][3]);
@@ -234,6 +259,34 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_lds_sp(
   }
 }
 
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_sp_cfg(const SparseArgs& a, hipStream_t s, int64_t splits, float* part) {
+  const int tiles_m = (int)((a.o + BM - 1) / BM), tiles_n = (int)((a.t + BN - 1) / BN);
+  const int64_t ntiles = (int64_t)tiles_m * tiles_n;
+  if (ntiles == 0) return hipSuccess;
+  const int64_t nk = a.kc / 64 + a.kd / 64;
+  if (splits < 1 || part == nullptr) splits = 1;
+  const int64_t per = (nk + splits - 1) / splits;
+  splits = per > 0 ? (nk + per - 1) / per : 1;
+  if (ntiles * splits > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  k_gemm_lds_sp<BM, BN, WM, WN><<<dim3((unsigned)(ntiles * splits)), dim3(64 * WM * WN), 0, s>>>(
+      a.w_vals, a.w_meta, a.kc, a.x, a.ldx, a.wd, a.ldwd, a.kd, a.dbase, a.t, a.o, a.y, a.ldy, a.accumulate,
+      tiles_m, tiles_n, (int)(per > 0 ? per : 1), splits > 1 ? part : nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  return launch_reduce_parts(part, splits, nullptr, a.t, a.o, a.y, a.ldy, a.accumulate, s);
+}
+
+// Few-token split: 128-row tiles, as many workgroups as fit one per CU.
+int64_t sp_small_splits(const SparseArgs& a) {
+  const int bn = a.t <= 64 ? 64 : 128;
+  const int64_t tiles = ((a.o + 127) / 128) * ((a.t + bn - 1) / bn);
+  const int64_t nk = a.kc / 64 + a.kd / 64;
+  int64_t splits = 256 / tiles;
+  if (splits > nk / 2) splits = nk / 2;
+  return splits < 1 ? 1 : splits;
+}
+
 }  // namespace
 
 namespace nml {
@@ -243,18 +296,23 @@ bool gemm_lds_sp_eligible(const SparseArgs& a, bool any_size) {
   if (a.kc % 64 != 0 || a.kd % 64 != 0 || (a.kc == 0 && a.kd == 0)) return false;
   if ((a.ldx % 8) != 0 || (a.kd > 0 && ((a.ldwd % 8) != 0 || (a.dbase % 8) != 0))) return false;
   // enough 256 x 256 tiles to fill the machine
-  return any_size || ((a.o + BM - 1) / BM) * ((a.t + BN - 1) / BN) >= 128;
+  return any_size || ((a.o + 255) / 256) * ((a.t + 255) / 256) >= 128;
 }
 
 hipError_t launch_gemm_lds_sp(const SparseArgs& a, hipStream_t s) {
-  const int tiles_m = (int)((a.o + BM - 1) / BM), tiles_n = (int)((a.t + BN - 1) / BN);
-  const int64_t ntiles = (int64_t)tiles_m * tiles_n;
-  if (ntiles == 0) return hipSuccess;
-  if (ntiles > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  k_gemm_lds_sp<<<dim3((unsigned)ntiles), dim3(64 * NW), 0, s>>>(
-      a.w_vals, a.w_meta, a.kc, a.x, a.ldx, a.wd, a.ldwd, a.kd, a.dbase, a.t, a.o, a.y, a.ldy, a.accumulate,
-      tiles_m, tiles_n);
-  return hipGetLastError();
+  return launch_sp_cfg<256, 256, 4, 2>(a, s, 1, nullptr);
+}
+
+int64_t gemm_lds_sp_small_part_bytes(const SparseArgs& a) {
+  const int64_t splits = sp_small_splits(a);
+  return splits > 1 ? splits * a.t * a.o * 4 : 0;
+}
+
+hipError_t launch_gemm_lds_sp_small(const SparseArgs& a, float* part, int64_t part_bytes, hipStream_t s) {
+  int64_t splits = sp_small_splits(a);
+  if (part == nullptr || part_bytes < splits * a.t * a.o * 4) splits = 1;
+  if (a.t <= 64) return launch_sp_cfg<128, 64, 4, 2>(a, s, splits, part);
+  return launch_sp_cfg<128, 128, 4, 2>(a, s, splits, part);
 }
 
 }  // namespace nml

@@ -71,6 +71,11 @@ hipError_t launch_gemm_sparse(const SparseArgs& a, hipStream_t s);
 // direct-to-LDS variant for large problems (plain loader, kc % 64 == 0, kd % 64 == 0)
 bool gemm_lds_sp_eligible(const SparseArgs& a, bool any_size);
 hipError_t launch_gemm_lds_sp(const SparseArgs& a, hipStream_t s);
+// few-token split variant (same eligibility with any_size): with part (scratch of at least
+// gemm_lds_sp_small_part_bytes(a) bytes) the splits write fp32 partial tiles that a second
+// kernel sums in split order; without it, one split.
+int64_t gemm_lds_sp_small_part_bytes(const SparseArgs& a);
+hipError_t launch_gemm_lds_sp_small(const SparseArgs& a, float* part, int64_t part_bytes, hipStream_t s);
 
 // Few-token streaming product (T <= 128): one or two weight segments summed into one
 // accumulator, then scaled (w_scale, per output row) and written or added to y.

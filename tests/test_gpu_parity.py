@@ -503,25 +503,28 @@ def test_spmm_act_accumulate_and_fp8():
         check_gemm(y2 - y0, O.gemm(sx, w), sx, w, label=f"accumulate {route}")
 
 
-@pytest.mark.parametrize("t,o,k", [(600, 300, 1024), (520, 136, 1056)])
-def test_spmm_act_fp8_large_tokens(t, o, k):
-    """fp8 weights at prefill sizes: widened once to bf16 in the workspace (K % 64 == 0)
-    or multiplied by the fp8-loading kernel (otherwise); scale, accumulate."""
-    print(f"fp8 large t={t} o={o} k={k}", flush=True)
+@pytest.mark.parametrize("widen", ["0", "1"])
+@pytest.mark.parametrize("t,o,k", [(600, 300, 1024), (520, 136, 1056), (1030, 520, 2048)])
+def test_spmm_act_fp8_large_tokens(t, o, k, widen):
+    """fp8 weights at prefill sizes (K % 64 == 0): codes staged straight into LDS and
+    widened per fragment, or (NM_FP8_WIDEN=1) widened once to bf16 in the workspace;
+    otherwise the register-staged fp8 kernel.  Scale, accumulate, ragged tiles."""
+    print(f"fp8 large t={t} o={o} k={k} widen={widen}", flush=True)
     rng = np.random.default_rng(t + k)
     x = synth.student_t_bf16(rng, (t, k), 4.0, 1.0)
     w = synth.normal_bf16(rng, (o, k), 0.02)
     q, sc = synth.fp8_e4m3_quantize_rows(w)
     wdeq = O.fp8_e4m3_to_f64(q) * sc[:, None].astype(np.float64)
     y0 = rng.standard_normal((t, o)).astype(np.float32)
-    for n, m in ((16, 32), (8, 16)):
-        sx, keep = O.sparsify(x, n, m)
-        ref = O.spmm_act_fp8(x, q, sc, n, m)
-        y, mask = run_act(x, None, n, m, w8=q, s8=sc)
-        assert (mask == O.pack_mask(keep)).all()
-        check_gemm(y, ref, sx, wdeq, label=f"fp8 {n}:{m}")
-        y2, _ = run_act(x, None, n, m, w8=q, s8=sc, accumulate=1, y0=y0)
-        check_gemm(y2 - y0, ref, sx, wdeq, label=f"fp8 {n}:{m} accumulate")
+    with env_set(NM_FP8_WIDEN=widen):
+        for n, m in ((16, 32), (8, 16)):
+            sx, keep = O.sparsify(x, n, m)
+            ref = O.spmm_act_fp8(x, q, sc, n, m)
+            y, mask = run_act(x, None, n, m, w8=q, s8=sc)
+            assert (mask == O.pack_mask(keep)).all()
+            check_gemm(y, ref, sx, wdeq, label=f"fp8 {n}:{m}")
+            y2, _ = run_act(x, None, n, m, w8=q, s8=sc, accumulate=1, y0=y0)
+            check_gemm(y2 - y0, ref, sx, wdeq, label=f"fp8 {n}:{m} accumulate")
 
 
 def test_fp8_decode_all_codes():
@@ -565,6 +568,22 @@ def test_spmm_act_decode_full_size_sampled(t):
     sx, keep = O.sparsify(x[rows], 8, 16)
     assert (mask[rows] == O.pack_mask(keep)).all()
     check_gemm(y[rows], O.gemm(sx, w), sx, w, label=f"decode full t={t}")
+
+
+@pytest.mark.parametrize("t", [16, 64, 128])
+def test_spmm_act_fp8_decode_full_size_sampled(t):
+    """fp8 weights (per-row scales) on the 8:16 down-projection (W 4096 x 14336) at decode
+    token counts; oracle on sampled output rows."""
+    print(f"fp8 decode full t={t}", flush=True)
+    d = synth.mlp_down_8of16(t_max=128)
+    x, w = d["x"][:t], d["w"]
+    q, sc = synth.fp8_e4m3_quantize_rows(w)
+    y, mask = run_act(x, None, 8, 16, w8=q, s8=sc)
+    rows = sample_rows(t, 8, seed=t)
+    sx, keep = O.sparsify(x[rows], 8, 16)
+    assert (mask[rows] == O.pack_mask(keep)).all()
+    wdeq = O.fp8_e4m3_to_f64(q) * sc[:, None].astype(np.float64)
+    check_gemm(y[rows], O.spmm_act_fp8(x[rows], q, sc, 8, 16), sx, wdeq, label=f"fp8 decode full t={t}")
 
 
 # ------------------------------------------------------------------- weight 2:4 ---
@@ -671,15 +690,21 @@ def test_spmm_w_slide_full_size_sampled():
         check_gemm(host(y, np.float32)[rows], O.gemm(x[rows], pruned), x[rows], pruned, label=f"slide full t={t}")
 
 
-@pytest.mark.parametrize("kernel", ["lds", "regs"])
-@pytest.mark.parametrize("t,o", [(300, 264), (130, 520)])
+SPARSE_KERNELS = {"lds": {"NM_GEMM": "lds"}, "regs": {"NM_GEMM": "regs"},
+                  "tile": {"NM_FEW_ROUTE": "tile"}, "stream": {"NM_FEW_ROUTE": "stream"}}
+
+
+@pytest.mark.parametrize("kernel,t,o", [("lds", 300, 264), ("lds", 130, 520), ("regs", 300, 264),
+                                        ("regs", 130, 520), ("tile", 33, 264), ("tile", 64, 520),
+                                        ("tile", 100, 264), ("tile", 128, 130), ("stream", 100, 264)])
 def test_sparse_weight_product_kernels(kernel, t, o):
-    """Large-token 2:4-weight products on both kernels (direct-to-LDS and register
-    staged): plain 2:4, lowered 6:8 / 4:6 / 8:10 (X lifted into the workspace first) and
-    the hybrid format with its dense second phase; ragged T and O."""
+    """2:4-weight products on each kernel: large-token direct-to-LDS and register-staged
+    tiles, the few-token split-K tile kernel and the few-token streaming kernel.  Plain
+    2:4, lowered 6:8 / 4:6 / 8:10 (X lifted into the workspace first where the kernel
+    needs it) and the hybrid format with its dense second phase; ragged T and O."""
     print(f"sparse kernels kernel={kernel} t={t} o={o}", flush=True)
     rng = np.random.default_rng(t + o)
-    with env_set(NM_GEMM=kernel):
+    with env_set(**SPARSE_KERNELS[kernel]):
         k = 1024
         x = synth.normal_bf16(rng, (t, k))
         w = synth.normal_bf16(rng, (o, k), 0.02)
