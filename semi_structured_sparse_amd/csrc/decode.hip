@@ -787,6 +787,57 @@ __global__ __launch_bounds__(RP_OUT * RP_LANES) void k_reduce_parts(const float*
   y[t * ldy + o] = v;
 }
 
+// Few splits over many outputs (the split-K tile kernels): each thread owns 4 consecutive
+// outputs and adds the splits' float4 partials in split order, four loads in flight.
+constexpr int RP4_THREADS = 256;
+
+__global__ __launch_bounds__(RP4_THREADS) void k_reduce_parts4(const float* __restrict__ part, int64_t splits,
+                                                               const float* __restrict__ wscale, int64_t T,
+                                                               int64_t O, float* __restrict__ y, int64_t ldy,
+                                                               int accumulate) {
+  const int64_t n = T * O;
+  const int64_t i = ((int64_t)blockIdx.x * RP4_THREADS + threadIdx.x) * 4;
+  if (i >= n) return;
+  const float* p = part + i;
+  float4 acc = *reinterpret_cast<const float4*>(p);
+  int64_t sp = 1;
+  for (; sp + 3 < splits; sp += 4) {
+    float4 v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const float4*>(p + (sp + q) * n);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc.x += v[q].x;
+      acc.y += v[q].y;
+      acc.z += v[q].z;
+      acc.w += v[q].w;
+    }
+  }
+  for (; sp < splits; ++sp) {
+    const float4 v = *reinterpret_cast<const float4*>(p + sp * n);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  const int64_t t = i / O, o = i - t * O;   // O % 4 == 0: the 4 outputs share a row
+  if (wscale != nullptr) {
+    acc.x *= wscale[o];
+    acc.y *= wscale[o + 1];
+    acc.z *= wscale[o + 2];
+    acc.w *= wscale[o + 3];
+  }
+  float4* yp = reinterpret_cast<float4*>(y + t * ldy + o);
+  if (accumulate) {
+    const float4 c = *yp;
+    acc.x += c.x;
+    acc.y += c.y;
+    acc.z += c.z;
+    acc.w += c.w;
+  }
+  *yp = acc;
+}
+
 // X[:, c0] then X[:, c1] side by side: xo[t][j] = x[t][c0[j]] (j < k0),
 // xo[t][off1 + j] = x[t][c1[j]] (j < k1).  Column indices are clamped to [0, kx).
 __global__ void k_permute_cols(const uint16_t* __restrict__ x, int64_t T, int64_t ldx, int64_t kx,
@@ -964,6 +1015,13 @@ hipError_t launch_reduce_parts(const float* part, int64_t splits, const float* w
                                float* y, int64_t ldy, int accumulate, hipStream_t s) {
   const int64_t n = t * o;
   if (n == 0) return hipSuccess;
+  // y is 16-byte aligned (checked at the boundary); float4 rows need o and ldy % 4 == 0
+  if (splits >= 1 && splits <= 16 && o % 4 == 0 && ldy % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0 &&
+      (reinterpret_cast<uintptr_t>(part) & 15) == 0) {
+    k_reduce_parts4<<<dim3((unsigned)((n / 4 + RP4_THREADS - 1) / RP4_THREADS)), dim3(RP4_THREADS), 0, s>>>(
+        part, splits, w_scale, t, o, y, ldy, accumulate);
+    return hipGetLastError();
+  }
   k_reduce_parts<<<dim3((unsigned)((n + RP_OUT - 1) / RP_OUT)), dim3(RP_OUT * RP_LANES), 0, s>>>(
       part, splits, w_scale, t, o, y, ldy, accumulate);
   return hipGetLastError();

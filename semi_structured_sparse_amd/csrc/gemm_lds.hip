@@ -35,8 +35,10 @@ using namespace nmk;
 using namespace nml;
 
 constexpr int BK = 64;                 // bf16 per K-step
-// s_waitcnt immediate for lgkmcnt(0) alone (vmcnt and expcnt at their maxima)
+// s_waitcnt immediates: lgkmcnt(0) alone (vmcnt and expcnt at their maxima), and
+// vmcnt(n) alone (vmcnt split over bits 3:0 and 15:14)
 constexpr int kWaitLgkm0 = 0xC07F;
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int ROWB = BK * 2;           // bytes per tile row per K-step
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -60,7 +62,7 @@ __device__ __forceinline__ uint32_t keep_pair(uint32_t d, uint32_t bits, int q) 
   return d & ((hi & 0xFFFF0000u) | (lo & 0x0000FFFFu));
 }
 
-template <int BM, int BN, int WM, int WN, int PRO, bool W8>
+template <int BM, int BN, int WM, int WN, int PRO, bool W8, int NST>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
     const unsigned char* __restrict__ w, int64_t ldw, const uint16_t* __restrict__ x, int64_t ldx,
     const uint32_t* __restrict__ xmask, int64_t T, int64_t O, int64_t K, float* __restrict__ y,
@@ -79,9 +81,13 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
   static_assert(NGA <= 2 * FI && NGB <= 2 * FI, "load groups are spread over the 2*FI MFMA steps");
   constexpr int MASK_GROUPS = (PRO == PRO_MASK) ? BN / 32 : 0;   // 32 rows x 2 words per inst
 
-  // two stages as distinct arrays: every LDS access names its stage statically
+  // NST (2 or 4) stages as distinct arrays: every LDS access names its stage statically,
+  // so the compiler tracks the loads into each stage separately
+  static_assert(NST == 2 || (NST == 4 && PRO == PRO_NONE), "four stages take the plain prologue only");
+  constexpr int A_X = NST == 4 ? A_BYTES : 16, B_X = NST == 4 ? B_BYTES : 16;
   __shared__ __align__(16) unsigned char sA0[A_BYTES], sB0[B_BYTES], sM0[MASK_BYTES];
   __shared__ __align__(16) unsigned char sA1[A_BYTES], sB1[B_BYTES], sM1[MASK_BYTES];
+  __shared__ __align__(16) unsigned char sA2[A_X], sB2[B_X], sA3[A_X], sB3[B_X];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (LDS base goes to M0)
   const int wm = wave % WM, wn = wave / WM;
@@ -163,9 +169,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
   // Multiply one staged K-step (two 32-wide halves, FI row steps each).  Fragments are
   // read one step ahead: the A fragment of the next row step, and during the first half
   // the B fragments of the second, so no matrix instruction waits on the LDS read issued
-  // just before it.  The next stage's load groups are issued one A and one B group per
-  // row step.  Scheduling barriers keep the compiler from sinking the early reads below
-  // the matrix instructions.
+  // just before it.  Scheduling barriers keep the compiler from sinking the early reads
+  // below the matrix instructions.
   // A fragment: 8 bf16 (16 bytes), or 8 fp8 codes (8 bytes, widened when used)
   auto read_a = [&](const unsigned char* abase, int ks, int i) {
     const int r = wm * SM + i * 16 + fr;
@@ -190,8 +195,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
     const int r = wn * SN + j * 16 + fr;
     return *reinterpret_cast<const u32x4*>(bbase + r * ROWB + 16 * swz(r, 4 * ks + fq));
   };
-  auto compute = [&](const unsigned char* abase, const unsigned char* bbase, const unsigned char* mbase,
-                     unsigned char* na, unsigned char* nb, unsigned char* nm, int64_t nk0) {
+  auto compute = [&](const unsigned char* abase, const unsigned char* bbase, const unsigned char* mbase) {
     uint2 mw[FJ];
     if constexpr (PRO == PRO_MASK) {
 #pragma unroll
@@ -199,14 +203,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
         const int r = wn * SN + j * 16 + fr;
         mw[j] = *reinterpret_cast<const uint2*>(mbase + r * 8);
       }
-      if (wave < MASK_GROUPS) g2lds4(msrc + (nk0 >> 5), nm + wave * 256);
     }
-    // the next stage's loads go out first: the first matrix step waits for every LDS read
-    // anyway, and no LDS read issued later has to wait behind a load still in flight
-#pragma unroll
-    for (int g = 0; g < NGA; ++g) g2lds16(asrc[g] + nk0 * WBYTES, na + (wave + g * NW) * 1024);
-#pragma unroll
-    for (int g = 0; g < NGB; ++g) g2lds16(bsrc[g] + nk0, nb + (wave + g * NW) * 1024);
     u32x4 b0[FJ], b1[FJ];
 #pragma unroll
     for (int j = 0; j < FJ; ++j) b0[j] = read_b(bbase, 0, j);
@@ -255,20 +252,64 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
     }
   };
 
-  issue_all(sA0, sB0, sM0, 0);
-  __builtin_amdgcn_s_waitcnt(0);   // the staged tiles have landed in LDS
-  __syncthreads();
-  // Two K-steps per trip (stage 0, then stage 1), each loading the step after it into
-  // the other stage.  The last step reloads step 0 into the idle stage instead (never
-  // read), so every step runs the same branch-free code.
-  for (int kt = 0; kt < nk; kt += 2) {
-    compute(sA0, sB0, sM0, sA1, sB1, sM1, kt + 1 < nk ? (int64_t)(kt + 1) * BK : 0);
-    __builtin_amdgcn_s_waitcnt(0);   // next stage landed in LDS
+  if constexpr (NST == 2) {
+    issue_all(sA0, sB0, sM0, 0);
+    __builtin_amdgcn_s_waitcnt(0);   // the staged tiles have landed in LDS
     __syncthreads();
-    if (kt + 1 < nk) {
-      compute(sA1, sB1, sM1, sA0, sB0, sM0, kt + 2 < nk ? (int64_t)(kt + 2) * BK : 0);
-      __builtin_amdgcn_s_waitcnt(0);
+    // Two K-steps per trip (stage 0, then stage 1).  Each step first issues the loads of
+    // the step after it into the other stage (the first matrix step waits for every LDS
+    // read anyway, so no later LDS read waits behind them); the last step reloads step 0
+    // into the idle stage instead (never read), so every step runs the same code.
+    for (int kt = 0; kt < nk; kt += 2) {
+      issue_all(sA1, sB1, sM1, kt + 1 < nk ? (int64_t)(kt + 1) * BK : 0);
+      compute(sA0, sB0, sM0);
+      __builtin_amdgcn_s_waitcnt(0);   // next stage landed in LDS
       __syncthreads();
+      if (kt + 1 < nk) {
+        issue_all(sA0, sB0, sM0, kt + 2 < nk ? (int64_t)(kt + 2) * BK : 0);
+        compute(sA1, sB1, sM1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+    }
+  } else {
+    // Four stages, three K-steps in flight (few-token shapes are bound by how many bytes
+    // each CU keeps in flight).  Before step k each wave waits until its loads of step k
+    // have landed (the loads of the up to two later steps may still be in flight), then
+    // the barrier makes every wave's loads visible and retires the reads of step k - 1,
+    // whose stage then takes the loads of step k + 3.
+    constexpr int L = NGA + NGB;   // load instructions per wave per step
+    // The barrier is the bare instruction: __syncthreads() would also wait for every load
+    // still in flight.  LDS is coherent within the workgroup, so the per-wave wait before
+    // it is all the loads need; the empty asm statements keep the compiler from moving
+    // memory accesses across it.
+    auto wait_step = [&](int k) {
+      if (k + 2 < nk) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * L));
+      else if (k + 1 < nk) __builtin_amdgcn_s_waitcnt(vmcnt_imm(L));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    // The first trip (kt = -4) only issues steps 0-2, through the same instructions as
+    // every later trip, so the compiler's tracking of which stage each load writes stays
+    // exact around the loop (a separate prologue makes it wait for all loads).
+    for (int kt = -4; kt < nk; kt += 4) {
+      if (kt >= 0) wait_step(kt);
+      if (kt + 3 >= 0 && kt + 3 < nk) issue_all(sA3, sB3, sM0, (int64_t)(kt + 3) * BK);
+      if (kt >= 0) compute(sA0, sB0, sM0);
+      if (kt + 1 >= nk) break;
+      if (kt + 1 >= 0) wait_step(kt + 1);
+      if (kt + 4 < nk) issue_all(sA0, sB0, sM0, (int64_t)(kt + 4) * BK);
+      if (kt + 1 >= 0) compute(sA1, sB1, sM0);
+      if (kt + 2 >= nk) break;
+      if (kt + 2 >= 0) wait_step(kt + 2);
+      if (kt + 5 < nk) issue_all(sA1, sB1, sM0, (int64_t)(kt + 5) * BK);
+      if (kt + 2 >= 0) compute(sA2, sB2, sM0);
+      if (kt + 3 >= nk) break;
+      if (kt + 3 >= 0) wait_step(kt + 3);
+      if (kt + 6 < nk) issue_all(sA2, sB2, sM0, (int64_t)(kt + 6) * BK);
+      if (kt + 3 >= 0) compute(sA3, sB3, sM0);
     }
   }
 
@@ -309,7 +350,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
   }
 }
 
-template <int BM, int BN, int WM, int WN, int PRO, bool W8 = false>
+template <int BM, int BN, int WM, int WN, int PRO, bool W8 = false, int NST = 2>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s, int64_t splits, float* part) {
   const int tiles_m = (int)((a.o + BM - 1) / BM), tiles_n = (int)((a.t + BN - 1) / BN);
   const int64_t ntiles = (int64_t)tiles_m * tiles_n;
@@ -317,7 +358,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s, int64_t splits, float* p
   int64_t kslice = ((a.k / BK + splits - 1) / splits) * BK;
   splits = (a.k + kslice - 1) / kslice;
   if (ntiles * splits > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  auto kern = k_gemm_lds<BM, BN, WM, WN, PRO, W8>;
+  auto kern = k_gemm_lds<BM, BN, WM, WN, PRO, W8, NST>;
   kern<<<dim3((unsigned)(ntiles * splits)), dim3(64 * WM * WN), 0, s>>>(
       (const unsigned char*)a.w, a.ldw, a.x, a.ldx, a.x_mask, a.t, a.o, a.k, a.y, a.ldy, a.accumulate, tiles_m, tiles_n,
       kslice, splits > 1 ? part : nullptr, a.w_scale);
@@ -329,6 +370,11 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s, int64_t splits, float* p
 }  // namespace
 
 namespace nml {
+
+static int env_int(const char* name, int dflt) {
+  const char* e = std::getenv(name);
+  return e != nullptr ? std::atoi(e) : dflt;
+}
 
 // fp8 weights: rows of codes straight into LDS (ldw a multiple of 16 bytes), widened to
 // bf16 per fragment; with the plain prologue only.
@@ -387,17 +433,13 @@ hipError_t launch_widen_fp8(const uint8_t* w8, int64_t ldw, int64_t o, int64_t k
 // grid has as many workgroups as fit one per CU (the splits' fp32 partial tiles are
 // summed in slice order by a second kernel).  Measured on gfx950 for 33-128 tokens: one
 // workgroup per CU beats two (twice the partial-sum traffic) and beats 256-row tiles
-// (fewer tiles, so more splits).  NM_TILE_BM=256, NM_TILE_WAVES=4 and NM_TILE_WG=<n>
-// (target workgroups) select the other shapes for A/B measurement.
+// (fewer tiles, so more splits); four LDS stages (three K-steps in flight) measured level
+// with two.  NM_TILE_BM=256, NM_TILE_WAVES=4, NM_TILE_STAGES=4 and NM_TILE_WG=<n> (target
+// workgroups) select the other shapes for A/B measurement.
 struct SmallCfg {
   int bm, bn, waves;
   int64_t target;
 };
-
-static int env_int(const char* name, int dflt) {
-  const char* e = std::getenv(name);
-  return e != nullptr ? std::atoi(e) : dflt;
-}
 
 static SmallCfg small_cfg(const GemmArgs& a) {
   SmallCfg c;
@@ -431,8 +473,13 @@ hipError_t launch_gemm_lds_small(const GemmArgs& a, float* part, int64_t part_by
   int64_t splits = small_splits(a);
   if (part == nullptr || part_bytes < splits * a.t * a.o * 4) splits = 1;
   const SmallCfg c = small_cfg(a);
+  const bool st4 = env_int("NM_TILE_STAGES", 2) == 4;
   if (a.w_fp8) {
-    if (a.t <= 64) return launch_cfg<128, 64, 4, 2, PRO_NONE, true>(a, s, splits, part);
+    if (a.t <= 64) {
+      if (st4) return launch_cfg<128, 64, 4, 2, PRO_NONE, true, 4>(a, s, splits, part);
+      return launch_cfg<128, 64, 4, 2, PRO_NONE, true>(a, s, splits, part);
+    }
+    if (st4) return launch_cfg<128, 128, 4, 2, PRO_NONE, true, 4>(a, s, splits, part);
     return launch_cfg<128, 128, 4, 2, PRO_NONE, true>(a, s, splits, part);
   }
   if (c.bm == 256) {
@@ -441,9 +488,11 @@ hipError_t launch_gemm_lds_small(const GemmArgs& a, float* part, int64_t part_by
   }
   if (a.t <= 64) {
     if (c.waves == 4) return launch_cfg<128, 64, 2, 2, PRO_NONE>(a, s, splits, part);
+    if (st4) return launch_cfg<128, 64, 4, 2, PRO_NONE, false, 4>(a, s, splits, part);
     return launch_cfg<128, 64, 4, 2, PRO_NONE>(a, s, splits, part);
   }
   if (c.waves == 4) return launch_cfg<128, 128, 2, 2, PRO_NONE>(a, s, splits, part);
+  if (st4) return launch_cfg<128, 128, 4, 2, PRO_NONE, false, 4>(a, s, splits, part);
   return launch_cfg<128, 128, 4, 2, PRO_NONE>(a, s, splits, part);
 }
 

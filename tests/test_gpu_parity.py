@@ -313,11 +313,12 @@ def test_spmm_act_2of4_layer():
 
 
 # route overrides of the few-token dispatch: weight-streaming kernel, split-K tile kernel
-# (bf16 weights, K % 64 == 0; others fall back to streaming) in its default 128-row shape,
-# its 256-row and 4-wave shapes and a forced workgroup count, or the large-T tile kernels
+# (K % 64 == 0; others fall back to streaming) in its default 128-row shape, its 256-row,
+# 4-wave and 4-stage shapes and forced workgroup counts, or the large-T tile kernels
 FEW_ROUTES = {"stream": {"NM_FEW_ROUTE": "stream"}, "tile": {"NM_FEW_ROUTE": "tile"},
               "tile256": {"NM_FEW_ROUTE": "tile", "NM_TILE_BM": "256"},
               "tile4w": {"NM_FEW_ROUTE": "tile", "NM_TILE_WAVES": "4", "NM_TILE_WG": "37"},
+              "tile4st": {"NM_FEW_ROUTE": "tile", "NM_TILE_STAGES": "4", "NM_TILE_WG": "100"},
               "off": {"NM_FEW": "0"}}
 
 
