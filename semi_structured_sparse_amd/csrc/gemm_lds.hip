@@ -67,7 +67,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
     const unsigned char* __restrict__ w, int64_t ldw, const uint16_t* __restrict__ x, int64_t ldx,
     const uint32_t* __restrict__ xmask, int64_t T, int64_t O, int64_t K, float* __restrict__ y,
     int64_t ldy, int accumulate, int tiles_m, int tiles_n, int64_t kslice, float* __restrict__ part,
-    const float* __restrict__ wscale) {
+    const float* __restrict__ wscale, int group) {
   constexpr int NW = WM * WN;
   constexpr int SM = BM / WM, SN = BN / WN;       // wave sub-tile (o x t)
   constexpr int FI = SM / 16, FJ = SN / 16;
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
   const int wm = wave % WM, wn = wave / WM;
 
   // XCD-aware tile order: hardware places workgroup b on XCD b % 8; each XCD takes a
-  // contiguous range of tiles, walked t-major inside bands of GROUP o-tiles.
+  // contiguous range of tiles, walked t-major inside bands of `group` o-tiles.
   // optional split-K: block b handles reduction slice b / ntiles and writes its fp32
   // partial tile to part[slice][t][o] (summed in slice order by a second kernel)
   const int ntiles = tiles_m * tiles_n;
@@ -102,11 +102,10 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
   if ((ntiles & 7) == 0 && gridDim.x == (unsigned)ntiles) lin = (blockIdx.x & 7) * (ntiles >> 3) + (blockIdx.x >> 3);
   const int64_t kbeg = (int64_t)kpart * kslice;
   const int64_t kend = (kbeg + kslice < K) ? kbeg + kslice : K;
-  constexpr int GROUP = 16;
-  const int band = lin / (GROUP * tiles_n);
-  const int band_w = min(GROUP, tiles_m - band * GROUP);
-  const int inband = lin - band * GROUP * tiles_n;
-  const int tile_m = band * GROUP + inband % band_w;
+  const int band = lin / (group * tiles_n);
+  const int band_w = min(group, tiles_m - band * group);
+  const int inband = lin - band * group * tiles_n;
+  const int tile_m = band * group + inband % band_w;
   const int tile_n = inband / band_w;
   const int64_t o0 = (int64_t)tile_m * BM, t0 = (int64_t)tile_n * BN;
 
@@ -350,6 +349,23 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
   }
 }
 
+static int env_int(const char* name, int dflt) {
+  const char* e = std::getenv(name);
+  return e != nullptr ? std::atoi(e) : dflt;
+}
+
+// o-tiles per band of the XCD-aware tile order.  An XCD runs 32 tiles at a time (one per
+// CU); a band g o-tiles wide makes that set g o-tiles x 32/g t-tiles, whose K-step
+// footprint g*BM + (32/g)*BN rows is smallest near g = sqrt(32 BN / BM).  Measured on
+// gfx950 at 8192 x 14336 x 4096: bands of 8 (or 4) o-tiles 711 us, of 16 736-820 us
+// (every XCD then streamed all of W twice: 2.1 GB of L2 fills per launch).
+// NM_GEMM_GROUP=<g> overrides for A/B measurement.
+static int group_for(int tiles_m, int bm, int bn) {
+  int g = env_int("NM_GEMM_GROUP", bn >= bm ? 8 : 4);
+  if (g < 1) g = 1;
+  return g < tiles_m ? g : tiles_m;
+}
+
 template <int BM, int BN, int WM, int WN, int PRO, bool W8 = false, int NST = 2>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s, int64_t splits, float* part) {
   const int tiles_m = (int)((a.o + BM - 1) / BM), tiles_n = (int)((a.t + BN - 1) / BN);
@@ -361,7 +377,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s, int64_t splits, float* p
   auto kern = k_gemm_lds<BM, BN, WM, WN, PRO, W8, NST>;
   kern<<<dim3((unsigned)(ntiles * splits)), dim3(64 * WM * WN), 0, s>>>(
       (const unsigned char*)a.w, a.ldw, a.x, a.ldx, a.x_mask, a.t, a.o, a.k, a.y, a.ldy, a.accumulate, tiles_m, tiles_n,
-      kslice, splits > 1 ? part : nullptr, a.w_scale);
+      kslice, splits > 1 ? part : nullptr, a.w_scale, group_for(tiles_m, BM, BN));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   return launch_reduce_parts(part, splits, a.w_scale, a.t, a.o, a.y, a.ldy, a.accumulate, s);
@@ -371,10 +387,6 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s, int64_t splits, float* p
 
 namespace nml {
 
-static int env_int(const char* name, int dflt) {
-  const char* e = std::getenv(name);
-  return e != nullptr ? std::atoi(e) : dflt;
-}
 
 // fp8 weights: rows of codes straight into LDS (ldw a multiple of 16 bytes), widened to
 // bf16 per fragment; with the plain prologue only.

@@ -25,6 +25,8 @@
 //  * Dense phase: 128 bytes per weight row per K-step, two v_mfma_f32_16x16x32_bf16.
 // Requirements (checked by the caller): kc % 64 == 0 and kd % 64 == 0, 16-byte aligned
 // rows (kc % 32 == 0 makes the value and position rows aligned), X and Wd ld % 8 == 0.
+#include <cstdlib>
+
 #include "nm_device.h"
 #include "nm_launch.h"
 
@@ -41,8 +43,6 @@ __device__ __forceinline__ void g2lds4(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
 }
 
-constexpr int GROUP = 16;
-
 __device__ __forceinline__ int swz8(int r, int c) { return c ^ ((r >> 1) & 7); }   // 8 pieces per row
 __device__ __forceinline__ int swz4(int r, int c) { return c ^ ((r >> 2) & 3); }   // 4 pieces per row
 
@@ -51,7 +51,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
     const uint16_t* __restrict__ wv, const uint8_t* __restrict__ wm, int64_t kc, const uint16_t* __restrict__ x,
     int64_t ldx, const uint16_t* __restrict__ wd, int64_t ldwd, int64_t kd, int64_t dbase, int64_t T, int64_t O,
     float* __restrict__ y, int64_t ldy, int accumulate, int tiles_m, int tiles_n, int steps_per_split,
-    float* __restrict__ part) {
+    float* __restrict__ part, int group) {
   constexpr int NW = WM * WN;
   constexpr int SM = BM / WM, SN = BN / WN, FI = SM / 16, FJ = SN / 16;
   constexpr int A_BYTES = BM * 128;          // dense W rows (sparse phase: values + positions)
@@ -69,16 +69,16 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wmi = wave % WM, wni = wave / WM;
 
-  // XCD-aware tile order (workgroup b runs on XCD b % 8), bands of GROUP o-tiles; with a
+  // XCD-aware tile order (workgroup b runs on XCD b % 8), bands of `group` o-tiles; with a
   // split reduction, block b takes split b / ntiles of tile b % ntiles
   const int ntiles = tiles_m * tiles_n;
   const int kpart = blockIdx.x / ntiles;
   int lin = blockIdx.x - kpart * ntiles;
   if ((ntiles & 7) == 0 && gridDim.x == (unsigned)ntiles) lin = (blockIdx.x & 7) * (ntiles >> 3) + (blockIdx.x >> 3);
-  const int band = lin / (GROUP * tiles_n);
-  const int band_w = min(GROUP, tiles_m - band * GROUP);
-  const int inband = lin - band * GROUP * tiles_n;
-  const int tile_m = band * GROUP + inband % band_w, tile_n = inband / band_w;
+  const int band = lin / (group * tiles_n);
+  const int band_w = min(group, tiles_m - band * group);
+  const int inband = lin - band * group * tiles_n;
+  const int tile_m = band * group + inband % band_w, tile_n = inband / band_w;
   const int64_t o0 = (int64_t)tile_m * BM, t0 = (int64_t)tile_n * BN;
 
   const int64_t kcv = kc / 2, mstride = kc / 8;
@@ -259,6 +259,16 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
   }
 }
 
+// o-tiles per band of the XCD-aware tile order: an XCD runs 32 tiles at a time, and a
+// band g o-tiles wide keeps their K-step footprint g*BM + (32/g)*BN rows near its minimum
+// (as for the dense direct-to-LDS kernel).  NM_GEMM_GROUP=<g> overrides for A/B.
+static int group_for(int tiles_m, int bm, int bn) {
+  const char* e = std::getenv("NM_GEMM_GROUP");
+  int g = e != nullptr ? std::atoi(e) : (bn >= bm ? 8 : 4);
+  if (g < 1) g = 1;
+  return g < tiles_m ? g : tiles_m;
+}
+
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_sp_cfg(const SparseArgs& a, hipStream_t s, int64_t splits, float* part) {
   const int tiles_m = (int)((a.o + BM - 1) / BM), tiles_n = (int)((a.t + BN - 1) / BN);
@@ -271,7 +281,7 @@ hipError_t launch_sp_cfg(const SparseArgs& a, hipStream_t s, int64_t splits, flo
   if (ntiles * splits > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   k_gemm_lds_sp<BM, BN, WM, WN><<<dim3((unsigned)(ntiles * splits)), dim3(64 * WM * WN), 0, s>>>(
       a.w_vals, a.w_meta, a.kc, a.x, a.ldx, a.wd, a.ldwd, a.kd, a.dbase, a.t, a.o, a.y, a.ldy, a.accumulate,
-      tiles_m, tiles_n, (int)(per > 0 ? per : 1), splits > 1 ? part : nullptr);
+      tiles_m, tiles_n, (int)(per > 0 ? per : 1), splits > 1 ? part : nullptr, group_for(tiles_m, BM, BN));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   return launch_reduce_parts(part, splits, nullptr, a.t, a.o, a.y, a.ldy, a.accumulate, s);
