@@ -87,15 +87,28 @@ def cpu_baseline(x_bits, w_bits, n, m, budget_s=12.0):
                       f"(numpy fp64 select + matmul), {total_t:.1f} s"}
 
 
-def gpu_time_us(torch, fn, graph, iters=10, warm=3):
+def gpu_time_us(torch, fn, graph, iters=10, warm=3, settle_ms=30.0):
     """Mean time per call.  graph=True: 20 calls captured in a HIP graph and replayed (the
     GPU time of short few-token calls without host launch overhead); else events around
-    back-to-back calls."""
+    back-to-back calls, after at least `settle_ms` of back-to-back warmup calls (the clock
+    settles under sustained matrix work) and over at least 10 ms of calls."""
     for _ in range(warm):
         fn()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     if not graph:
+        spent, n, per = 0.0, 1, 1.0
+        while spent < settle_ms:
+            e0.record()
+            for _ in range(n):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            spent += ms
+            per = max(ms / n, 1e-3)
+            n = min(2 * n, 64)
+        iters = max(iters, int(10.0 / per) + 1)
         e0.record()
         for _ in range(iters):
             fn()
@@ -248,8 +261,10 @@ def measure_rows(torch, S, synth, np):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # defaults reach the sustained clock: under back-to-back matrix work the chip's power
+    # control lowers the clock for the first ~25 steps (product kernel 720 -> 980 -> 700 us)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true",
