@@ -26,6 +26,7 @@
 // Requirements (checked by the caller): kc % 64 == 0 and kd % 64 == 0, 16-byte aligned
 // rows (kc % 32 == 0 makes the value and position rows aligned), X and Wd ld % 8 == 0.
 #include <cstdlib>
+#include <cstring>
 
 #include "nm_device.h"
 #include "nm_launch.h"
@@ -42,6 +43,9 @@ __device__ __forceinline__ void g2lds16(const void* g, void* lds) {
 __device__ __forceinline__ void g2lds4(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
 }
+
+// s_waitcnt immediate for lgkmcnt(0) alone (vmcnt and expcnt at their maxima)
+constexpr int kWaitLgkm0 = 0xC07F;
 
 __device__ __forceinline__ int swz8(int r, int c) { return c ^ ((r >> 1) & 7); }   // 8 pieces per row
 __device__ __forceinline__ int swz4(int r, int c) { return c ^ ((r >> 2) & 3); }   // 4 pieces per row
@@ -134,6 +138,15 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
 #pragma unroll
       for (int q = 0; q < NX; ++q) g2lds16(xsrc[q] + k0, b + (wave + q * NW) * 1024);
     };
+    // The B fragment of column block j + 1 is read while block j is multiplied; the wait
+    // for it sits before the next reads (while a direct-to-LDS load is in flight the
+    // compiler can only wait for all LDS reads, so a wait after them would stall on them).
+    auto read_bv = [&](const unsigned char* b, int j) {
+      const int c = wni * SN + j * 16 + fr;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(b + c * 128 + 16 * swz8(c, fg));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(b + c * 128 + 16 * swz8(c, 4 + fg));
+      return u32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
     auto compute = [&](const unsigned char* a, const unsigned char* b) {
       bf16x8 af[FI];
       int idx[FI];
@@ -143,18 +156,21 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
         af[i] = *reinterpret_cast<const bf16x8*>(a + r * 64 + 16 * swz4(r, fg));
         idx[i] = *reinterpret_cast<const uint16_t*>(a + SV_BYTES + r * 8 + 2 * fg);
       }
+      u32x8 bcur = read_bv(b, 0), bnxt;
 #pragma unroll
       for (int j = 0; j < FJ; ++j) {
-        const int c = wni * SN + j * 16 + fr;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(b + c * 128 + 16 * swz8(c, fg));
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(b + c * 128 + 16 * swz8(c, 4 + fg));
-        const u32x8 bb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        const bf16x16 bv = __builtin_bit_cast(bf16x16, bb);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (j + 1 < FJ) bnxt = read_bv(b, j + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x16 bv = __builtin_bit_cast(bf16x16, bcur);
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int i = 0; i < FI; ++i)
           acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af[i], bv, acc[i][j], idx[i], 0, 0);
         __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+        bcur = bnxt;
       }
     };
     issue(sA0, sB0, 0);
@@ -193,6 +209,11 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
 #pragma unroll
       for (int q = 0; q < NX; ++q) g2lds16(xsrc[q] + dbase + j0, b + (wave + q * NW) * 1024);
     };
+    // A fragments one row step ahead, waits before the next reads (as in the sparse phase)
+    auto read_ad = [&](const unsigned char* a, int ks, int i) {
+      const int r = wmi * SM + i * 16 + fr;
+      return *reinterpret_cast<const bf16x8*>(a + r * 128 + 16 * swz8(r, 4 * ks + fg));
+    };
     auto compute = [&](const unsigned char* a, const unsigned char* b) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -202,15 +223,20 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
           const int c = wni * SN + j * 16 + fr;
           bfr[j] = *reinterpret_cast<const bf16x8*>(b + c * 128 + 16 * swz8(c, 4 * ks + fg));
         }
+        bf16x8 acur = read_ad(a, ks, 0), anxt;
 #pragma unroll
         for (int i = 0; i < FI; ++i) {
-          const int r = wmi * SM + i * 16 + fr;
-          const bf16x8 af = *reinterpret_cast<const bf16x8*>(a + r * 128 + 16 * swz8(r, 4 * ks + fg));
+          __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+          __builtin_amdgcn_sched_barrier(0);
+          if (i + 1 < FI) anxt = read_ad(a, ks, i + 1);
+          __builtin_amdgcn_sched_barrier(0);
           __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int j = 0; j < FJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bfr[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(acur, bfr[j], acc[i][j], 0, 0, 0);
           __builtin_amdgcn_s_setprio(0);
+          __builtin_amdgcn_sched_barrier(0);
+          acur = anxt;
         }
       }
     };
@@ -310,7 +336,11 @@ bool gemm_lds_sp_eligible(const SparseArgs& a, bool any_size) {
 }
 
 hipError_t launch_gemm_lds_sp(const SparseArgs& a, hipStream_t s) {
-  return launch_sp_cfg<256, 256, 4, 2>(a, s, 1, nullptr);
+  // waves of 128 (o) x 64 (t): the dense X operand, read by WM waves, is the larger LDS
+  // read stream, so WM = 2 beats 4 (measured 1-4% on gfx950); NM_SP_WAVES=4x2 for A/B
+  const char* e = std::getenv("NM_SP_WAVES");
+  if (e != nullptr && std::strcmp(e, "4x2") == 0) return launch_sp_cfg<256, 256, 4, 2>(a, s, 1, nullptr);
+  return launch_sp_cfg<256, 256, 2, 4>(a, s, 1, nullptr);
 }
 
 int64_t gemm_lds_sp_small_part_bytes(const SparseArgs& a) {

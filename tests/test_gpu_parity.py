@@ -691,11 +691,12 @@ def test_spmm_w_slide_full_size_sampled():
         check_gemm(host(y, np.float32)[rows], O.gemm(x[rows], pruned), x[rows], pruned, label=f"slide full t={t}")
 
 
-SPARSE_KERNELS = {"lds": {"NM_GEMM": "lds"}, "regs": {"NM_GEMM": "regs"},
+SPARSE_KERNELS = {"lds": {"NM_GEMM": "lds"}, "lds4x2": {"NM_GEMM": "lds", "NM_SP_WAVES": "4x2"},
+                  "regs": {"NM_GEMM": "regs"},
                   "tile": {"NM_FEW_ROUTE": "tile"}, "stream": {"NM_FEW_ROUTE": "stream"}}
 
 
-@pytest.mark.parametrize("kernel,t,o", [("lds", 300, 264), ("lds", 130, 520), ("regs", 300, 264),
+@pytest.mark.parametrize("kernel,t,o", [("lds", 300, 264), ("lds", 130, 520), ("lds4x2", 300, 264), ("regs", 300, 264),
                                         ("regs", 130, 520), ("tile", 33, 264), ("tile", 64, 520),
                                         ("tile", 100, 264), ("tile", 128, 130), ("stream", 100, 264)])
 def test_sparse_weight_product_kernels(kernel, t, o):
