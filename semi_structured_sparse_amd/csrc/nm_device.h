@@ -40,6 +40,51 @@ __device__ __forceinline__ void sort_desc(uint32_t (&c)[M]) {
   }
 }
 
+// Descending sort by Batcher's odd-even merge network (5 / 19 / 63 / 191 comparators for
+// M = 4 / 8 / 16 / 32, against 6 / 24 / 80 / 240 for the bitonic network above).  When
+// only one output is used the compiler drops the comparators it does not depend on.
+template <int M>
+__device__ __forceinline__ void sort_desc_oem(uint32_t (&c)[M]) {
+#pragma unroll
+  for (int p = 1; p < M; p <<= 1) {
+#pragma unroll
+    for (int k = p; k >= 1; k >>= 1) {
+#pragma unroll
+      for (int j = k % p; j + k < M; j += 2 * k) {
+#pragma unroll
+        for (int i = 0; i < k; ++i) {
+          const int a = i + j, b = i + j + k;
+          if (b < M && a / (2 * p) == b / (2 * p)) {
+            const uint32_t x = c[a], y = c[b];
+            c[a] = x > y ? x : y;
+            c[b] = x > y ? y : x;
+          }
+        }
+      }
+    }
+  }
+}
+
+// Keep bits for a compile-time n: only the n-th largest key is needed.
+template <int M, int N>
+__device__ __forceinline__ uint32_t topn_bits_n(const uint32_t (&d)[M / 2]) {
+  static_assert(N >= 1 && N <= M, "1 <= n <= m");
+  uint32_t c[M], s[M];
+#pragma unroll
+  for (int q = 0; q < M / 2; ++q) {
+    c[2 * q] = ((d[q] << 16) & 0x7FFF0000u) | (0xFFFFu - 2 * q);
+    c[2 * q + 1] = (d[q] & 0x7FFF0000u) | (0xFFFFu - 2 * q - 1);
+  }
+#pragma unroll
+  for (int i = 0; i < M; ++i) s[i] = c[i];
+  sort_desc_oem<M>(s);
+  const uint32_t tau = s[N - 1];
+  uint32_t bits = 0;
+#pragma unroll
+  for (int i = 0; i < M; ++i) bits |= (c[i] >= tau ? 1u : 0u) << i;
+  return bits;
+}
+
 // d: the group as packed dwords (element 2q in the low half of d[q]).  Returns the keep
 // bits (bit i set iff element i is kept), exactly n bits set for 1 <= n <= M.
 template <int M>

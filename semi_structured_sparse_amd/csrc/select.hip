@@ -70,7 +70,8 @@ __device__ __forceinline__ void copy_u8(uint8_t* dst, const uint8_t* lds, int co
   }
 }
 
-template <int M>
+// NT: n as a compile-time constant (the half-density patterns), or 0 for any n.
+template <int M, int NT>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void k_select(
     const uint16_t* __restrict__ x, int64_t rows, int64_t k, int64_t ldx, int n,
     uint16_t* __restrict__ y, int64_t ldy, uint32_t* __restrict__ mask,
@@ -98,7 +99,11 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_select(
 #pragma unroll
     for (int q = 0; q < M / 2; ++q) d[q] = 0;
   }
-  const uint32_t keep = valid ? topn_bits<M>(d, n) : 0u;
+  uint32_t keep = 0u;
+  if (valid) {
+    if constexpr (NT > 0) keep = topn_bits_n<M, NT>(d);
+    else keep = topn_bits<M>(d, n);
+  }
 
   if (y != nullptr && valid) {
     uint32_t o[M / 2];
@@ -195,13 +200,19 @@ hipError_t launch_select(int m, const uint16_t* x, int64_t rows, int64_t k, int6
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)blocks), block(64 * kWavesPerBlock);
+#define NM_SELECT(MM)                                                                              \
+  if (n == (MM) / 2)                                                                               \
+    k_select<MM, (MM) / 2><<<grid, block, 0, s>>>(x, rows, k, ldx, n, y, ldy, mask, values, meta, meta_2bit); \
+  else                                                                                             \
+    k_select<MM, 0><<<grid, block, 0, s>>>(x, rows, k, ldx, n, y, ldy, mask, values, meta, meta_2bit);
   switch (m) {
-    case 4: k_select<4><<<grid, block, 0, s>>>(x, rows, k, ldx, n, y, ldy, mask, values, meta, meta_2bit); break;
-    case 8: k_select<8><<<grid, block, 0, s>>>(x, rows, k, ldx, n, y, ldy, mask, values, meta, meta_2bit); break;
-    case 16: k_select<16><<<grid, block, 0, s>>>(x, rows, k, ldx, n, y, ldy, mask, values, meta, meta_2bit); break;
-    case 32: k_select<32><<<grid, block, 0, s>>>(x, rows, k, ldx, n, y, ldy, mask, values, meta, meta_2bit); break;
+    case 4: NM_SELECT(4) break;
+    case 8: NM_SELECT(8) break;
+    case 16: NM_SELECT(16) break;
+    case 32: NM_SELECT(32) break;
     default: return hipErrorInvalidValue;
   }
+#undef NM_SELECT
   return hipGetLastError();
 }
 
