@@ -135,21 +135,58 @@ def gpu_time_us(torch, fn, graph, iters=10, warm=3, settle_ms=30.0):
     return e0.elapsed_time(e1) / 60 * 1e3
 
 
+def gpu_time_rot_us(torch, fns):
+    """Mean GPU time per call of a graph that cycles through `fns` (calls on distinct
+    copies of the weights, so that no weight stays in the 256 MB Infinity Cache between
+    its uses): max(20, len(fns)) calls per graph, three replays timed."""
+    n = max(20, len(fns))
+    for f in fns[:3]:
+        f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        fns[0]()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=st):
+            for i in range(n):
+                fns[i % len(fns)]()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (3 * n) * 1e3
+
+
+ROT_BYTES = 600e6   # weight copies cycled per few-token row: well past the 256 MB cache
+
+
+def n_copies(wbytes):
+    return max(3, int(ROT_BYTES // max(wbytes, 1)) + 1)
+
+
 def measure_rows(torch, S, synth, np):
     """Every workload row of the method's measurement table: time, dense-equivalent and
     executed TFLOP/s, algorithmic bytes and GB/s, and the fraction of the roofline that
-    bounds the row (HBM for few tokens, bf16 matrix peak for many)."""
+    bounds the row (HBM for few tokens, bf16 matrix peak for many).  Few-token rows cycle
+    through enough copies of their weights that each call reads its weights from HBM."""
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(
         np.int16 if a.dtype == np.uint16 else (np.int32 if a.dtype == np.int32 else np.uint8))).cuda()
     f32 = lambda *sh: torch.empty(sh, dtype=torch.float32, device="cuda")
     buf = lambda nb, dt=torch.uint8: torch.empty((max(int(nb), 16),), dtype=dt, device="cuda")
     rows = []
 
-    def add(cfg, t, path, us, f_dense, f_exec, nbytes):
+    def add(cfg, t, path, us, f_dense, f_exec, nbytes, bound=None):
         r = {"cfg": cfg, "tokens": t, "path": path, "us": round(us, 2),
              "dense_equiv_tflops": round(f_dense / us / 1e6, 2), "executed_tflops": round(f_exec / us / 1e6, 2),
              "algorithmic_bytes": int(nbytes), "GBps": round(nbytes / us / 1e3, 1)}
-        if t <= 128:
+        if bound == "hbm" or (bound is None and t <= 128):
             r.update(bound="hbm", frac=round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4))
         else:
             r.update(bound="mfma", frac=round(f_exec / us / 1e6 / PEAK_BF16_TFLOPS, 4))
@@ -162,6 +199,18 @@ def measure_rows(torch, S, synth, np):
         ws_holder.append(buf(nb))
         a.workspace, a.workspace_bytes = ws_holder[-1].data_ptr(), nb
         return lambda: S.nm_spmm(a)
+
+    def rot_spmm(make_args, weights, wbytes, ws_holder):
+        """One call per weight copy (tuples of tensors, first the originals), sharing one
+        workspace; make_args(*copy) builds the call's arguments."""
+        cps = [weights] + [tuple(w.clone() for w in weights) for _ in range(n_copies(wbytes) - 1)]
+        ws_holder.append(cps)
+        args = [make_args(*c) for c in cps]
+        nb = max(S.nm_spmm_workspace_size(a) for a in args)
+        ws_holder.append(buf(nb))
+        for a in args:
+            a.workspace, a.workspace_bytes = ws_holder[-1].data_ptr(), nb
+        return [(lambda a=a: S.nm_spmm(a)) for a in args]
 
     keep = []
     # cfg1: 2:4 activations, 64 x 512 x 512
@@ -177,16 +226,37 @@ def measure_rows(torch, S, synth, np):
     O2, K2 = 4096, 14336
     wk2 = dev(np.ascontiguousarray(d["w"].T))
     y = f32(1, O2)
-    fn = spmm(S.make_spmm_args(S.NM_ACT_DYNAMIC, 1, O2, K2, x2[:1], w2, y, n=8, m=16, w_kmajor=wk2), keep)
-    add("cfg2", 1, "8:16 act, K-major gather", gpu_time_us(torch, fn, True), 2.0 * O2 * K2, 2.0 * O2 * K2 / 2,
+    fns = rot_spmm(lambda wk: S.make_spmm_args(S.NM_ACT_DYNAMIC, 1, O2, K2, x2[:1], w2, y, n=8, m=16, w_kmajor=wk),
+                   (wk2,), O2 * K2 * 2, keep)
+    add("cfg2", 1, "8:16 act, K-major gather", gpu_time_rot_us(torch, fns), 2.0 * O2 * K2, 2.0 * O2 * K2 / 2,
         K2 // 2 * O2 * 2 + K2 * 2 + O2 * 4)
+    keep.clear()
     del wk2
+    # the select kernel alone at 8192 tokens: S(X) + mask, and values + u8 index + mask
+    t = 8192
+    sxb = torch.empty((t, K2), dtype=torch.int16, device="cuda")
+    mk = torch.empty((t, K2 // 32), dtype=torch.int32, device="cuda")
+    vv = torch.empty((t, K2 // 2), dtype=torch.int16, device="cuda")
+    ix = torch.empty((t, K2 // 2), dtype=torch.uint8, device="cuda")
+    fn = lambda: S.nm_sparsify(x2, 8, 16, sxb, mk, check=False)
+    add("cfg2", t, "select alone: S(X) + mask", gpu_time_us(torch, fn, False), 0.0, 0.0,
+        t * K2 * 2 + t * K2 * 2 + t * K2 // 8, bound="hbm")
+    fn = lambda: S.nm_compress(x2, 8, 16, vv, ix, S.NM_META_U8, mask=mk, check=False)
+    add("cfg2", t, "select alone: values + u8 idx + mask", gpu_time_us(torch, fn, False), 0.0, 0.0,
+        t * K2 * 2 + t * K2 // 2 * 3 + t * K2 // 8, bound="hbm")
+    del sxb, mk, vv, ix
     for t in (1, 16, 128, 2048, 8192):
         y = f32(t, O2)
-        fn = spmm(S.make_spmm_args(S.NM_ACT_DYNAMIC, t, O2, K2, x2[:t], w2, y, n=8, m=16), keep)
         f = 2.0 * t * O2 * K2
-        add("cfg2", t, "8:16 act (select + product)", gpu_time_us(torch, fn, t <= 128), f, f,
-            t * K2 * 2 + O2 * K2 * 2 + t * O2 * 4)
+        if t <= 128:
+            fns = rot_spmm(lambda w: S.make_spmm_args(S.NM_ACT_DYNAMIC, t, O2, K2, x2[:t], w, y, n=8, m=16),
+                           (w2,), O2 * K2 * 2, keep)
+            us = gpu_time_rot_us(torch, fns)
+        else:
+            us = gpu_time_us(torch, spmm(S.make_spmm_args(S.NM_ACT_DYNAMIC, t, O2, K2, x2[:t], w2, y, n=8, m=16),
+                                         keep), False)
+        add("cfg2", t, "8:16 act (select + product)", us, f, f, t * K2 * 2 + O2 * K2 * 2 + t * O2 * 4)
+        keep.clear()
     del x2, w2
     # cfg3: 6:8 weights lowered to 2:4, 4096 x 4096, lifted activations
     d = synth.slide_6of8_layer(t_max=4096)
@@ -199,10 +269,15 @@ def measure_rows(torch, S, synth, np):
     S.nm_lower_slide(v, i8, 4096, 4096, 4, vp, mp, S.NM_META_2BIT)
     for t in (1, 16, 128, 4096):
         y = f32(t, 4096)
-        fn = spmm(S.make_spmm_args(S.NM_W_SLIDE, t, 4096, 4096, x3[:t], vp, y, ns=4, w_meta=mp,
-                                   w_meta_fmt=S.NM_META_2BIT), keep)
-        add("cfg3", t, "6:8 W lowered to 2:4, lifted X", gpu_time_us(torch, fn, t <= 128), 2.0 * t * 4096 * 4096,
+        mk3 = lambda v_, m_: S.make_spmm_args(S.NM_W_SLIDE, t, 4096, 4096, x3[:t], v_, y, ns=4, w_meta=m_,
+                                              w_meta_fmt=S.NM_META_2BIT)
+        if t <= 128:
+            us = gpu_time_rot_us(torch, rot_spmm(mk3, (vp, mp), 4096 * 3072 * 2 + 4096 * 768, keep))
+        else:
+            us = gpu_time_us(torch, spmm(mk3(vp, mp), keep), False)
+        add("cfg3", t, "6:8 W lowered to 2:4, lifted X", us, 2.0 * t * 4096 * 4096,
             2.0 * t * 4096 * 3072, 4096 * 3072 * 2 + 4096 * 768 + t * 4096 * 2 + t * 4096 * 4)
+        keep.clear()
     del w3, x3, v, i8, vp, mp
     # cfg4: hybrid, 14336 x 4096, 25% dense columns
     d = synth.hybrid_up_layer(t_max=2048)
@@ -216,15 +291,22 @@ def measure_rows(torch, S, synth, np):
     wm = torch.empty((o4, ks // 8), dtype=torch.uint8, device="cuda")
     wd = torch.empty((o4, kd), dtype=torch.int16, device="cuda")
     S.nm_hybrid_pack(w4, kd, sc, dc, wv, wm, S.NM_META_2BIT, wd, buf(S.nm_hybrid_pack_workspace_size(k4)))
+    wb4 = o4 * ks + o4 * ks // 8 + o4 * kd * 2
     for t in (1, 8, 32, 64, 2048):
         y = f32(t, o4)
         nb = S.nm_hybrid_gemm_workspace_size(t, ks, kd, o4, True)
         wsb = buf(nb)
         xs = x4[:t]
-        fn = lambda: S.nm_hybrid_gemm(xs, sc, ks, dc, kd, wv, wm, S.NM_META_2BIT, wd, o4, y, workspace=wsb,
-                                      workspace_bytes=nb)
-        add("cfg4", t, "hybrid 2:4 + 25% dense columns", gpu_time_us(torch, fn, t <= 128), 2.0 * t * o4 * k4,
-            2.0 * t * o4 * (kd + ks / 2), o4 * ks + o4 * ks // 8 + o4 * kd * 2 + t * k4 * 2 + t * o4 * 4)
+        call = lambda wv_, wm_, wd_: (lambda: S.nm_hybrid_gemm(xs, sc, ks, dc, kd, wv_, wm_, S.NM_META_2BIT, wd_, o4,
+                                                               y, workspace=wsb, workspace_bytes=nb))
+        if t <= 128:
+            cps = [(wv, wm, wd)] + [(wv.clone(), wm.clone(), wd.clone()) for _ in range(n_copies(wb4) - 1)]
+            us = gpu_time_rot_us(torch, [call(*c) for c in cps])
+            del cps
+        else:
+            us = gpu_time_us(torch, call(wv, wm, wd), False)
+        add("cfg4", t, "hybrid 2:4 + 25% dense columns", us, 2.0 * t * o4 * k4,
+            2.0 * t * o4 * (kd + ks / 2), wb4 + t * k4 * 2 + t * o4 * 4)
     del w4, x4, sc, dc, wv, wm, wd
     # cfg5: one 8B-shaped layer, 16:32 and 8:16, bf16 and fp8 weights, T = 64 and 8192
     lay = synth.transformer_layer(t_max=8192, with_fp8=True)
@@ -242,15 +324,18 @@ def measure_rows(torch, S, synth, np):
                     y = f32(t, o_)
                     xin = xdev[st][:t]
                     if kind == "bf16":
-                        a = S.make_spmm_args(S.NM_ACT_DYNAMIC, t, o_, k_, xin, wdev[nm], y, n=n, m=m)
+                        mk5 = lambda w_: S.make_spmm_args(S.NM_ACT_DYNAMIC, t, o_, k_, xin, w_, y, n=n, m=m)
+                        wts = (wdev[nm],)
                         wb = o_ * k_ * 2
                     else:
-                        q, s8 = w8dev[nm]
-                        a = S.make_spmm_args(S.NM_ACT_DYNAMIC, t, o_, k_, xin, q, y, n=n, m=m,
-                                             w_dtype=S.NM_W_FP8E4M3, w_scale=s8)
+                        mk5 = lambda q_, s_: S.make_spmm_args(S.NM_ACT_DYNAMIC, t, o_, k_, xin, q_, y, n=n, m=m,
+                                                              w_dtype=S.NM_W_FP8E4M3, w_scale=s_)
+                        wts = w8dev[nm]
                         wb = o_ * k_ + o_ * 4
-                    fn = spmm(a, keep)
-                    tot_us += gpu_time_us(torch, fn, t <= 128, iters=5, warm=2)
+                    if t <= 128:
+                        tot_us += gpu_time_rot_us(torch, rot_spmm(mk5, wts, wb, keep))
+                    else:
+                        tot_us += gpu_time_us(torch, spmm(mk5(*wts), keep), False, iters=5, warm=2)
                     tot_f += 2.0 * t * o_ * k_
                     tot_b += wb + t * k_ * 2 + t * o_ * 4
                     keep.clear()
