@@ -171,6 +171,25 @@ def n_copies(wbytes):
     return max(3, int(ROT_BYTES // max(wbytes, 1)) + 1)
 
 
+def measure_ceilings(torch, S):
+    """Achievable ceilings on this machine: a plain streaming read over distinct buffers
+    (cold in the 256 MB Infinity Cache) and over one buffer read again, and the bf16
+    matrix-instruction rate on register operands, each after the clock has settled."""
+    nb = 117440512
+    bufs = [torch.empty((nb // 4,), dtype=torch.int32, device="cuda").fill_(b) for b in range(6)]
+    sink = torch.empty((S.nm_probe_sink_bytes() // 4,), dtype=torch.int32, device="cuda")
+    cold = gpu_time_rot_us(torch, [(lambda b=b: S.nm_probe_read(b, nb, sink, check=False)) for b in bufs])
+    warm = gpu_time_us(torch, lambda: S.nm_probe_read(bufs[0], nb, sink, check=False), False)
+    del bufs
+    iters = 2000
+    mf = gpu_time_us(torch, lambda: S.nm_probe_mfma(iters, sink, check=False), False)
+    res = {"hbm_read_cold_GBps": round(nb / cold / 1e3, 1), "hbm_read_warm_GBps": round(nb / warm / 1e3, 1),
+           "mfma_bf16_TFLOPs": round(S.nm_probe_mfma_flops(iters) / mf / 1e6, 1)}
+    log(f"ceilings: streaming read {res['hbm_read_cold_GBps']:.0f} GB/s cold, {res['hbm_read_warm_GBps']:.0f} GB/s "
+        f"re-read; bf16 matrix instructions {res['mfma_bf16_TFLOPs']:.0f} TFLOP/s")
+    return res
+
+
 def measure_rows(torch, S, synth, np):
     """Every workload row of the method's measurement table: time, dense-equivalent and
     executed TFLOP/s, algorithmic bytes and GB/s, and the fraction of the roofline that
@@ -438,6 +457,7 @@ def main():
     }
 
     if not args.no_rows:
+        result["ceilings"] = measure_ceilings(torch, S)
         log("per-workload rows:")
         result["rows"] = measure_rows(torch, S, synth, np)
 

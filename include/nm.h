@@ -251,6 +251,22 @@ nm_status nm_hybrid_gemm(const void* x, int64_t t, int64_t ldx, const int32_t* s
 int64_t nm_hybrid_gemm_workspace_size(int64_t t, int64_t k_s, int64_t k_d, int64_t o,
                                       int gathered);
 
+/*
+ * Measurement helpers (not part of the method): the achievable ceilings on the machine at
+ * hand, reported beside the nominal peaks.
+ *   nm_probe_sink_bytes   bytes of the device sink both probes write (one value per thread).
+ *   nm_probe_read         one streaming read of `bytes` (a multiple of 16) at buf, 16-byte
+ *                         loads at a grid stride; buf and sink 16-byte aligned.
+ *   nm_probe_mfma         `iters` rounds of 16 independent bf16 16x16x32 matrix instructions
+ *                         per wave on register operands; nm_probe_mfma_flops(iters) gives the
+ *                         FLOPs one launch performs.
+ * Both only enqueue work on `stream`; time them with events on that stream.
+ */
+int64_t nm_probe_sink_bytes(void);
+nm_status nm_probe_read(const void* buf, int64_t bytes, void* sink, void* stream);
+int64_t nm_probe_mfma_flops(int64_t iters);
+nm_status nm_probe_mfma(int64_t iters, void* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,6 +17,7 @@ __all__ = [
     "NMError", "lib", "NM_OK", "NM_EINVAL", "NM_ESHAPE", "NM_EALIGN", "NM_EUNSUPPORTED", "NM_EHIP",
     "NM_META_U8", "NM_META_2BIT", "NM_W_BF16", "NM_W_FP8E4M3", "NM_ACT_DYNAMIC", "NM_ACT_COMPRESSED",
     "NM_W_COMPRESSED", "NM_W_SLIDE", "NM_ACT_MASKED", "nm_spmm_args", "nm_status_str", "nm_version", "nm_sparsify",
+    "nm_probe_sink_bytes", "nm_probe_read", "nm_probe_mfma_flops", "nm_probe_mfma",
     "nm_compress", "nm_decompress", "nm_lower_slide", "nm_slide_lift", "nm_spmm",
     "nm_spmm_workspace_size", "nm_hybrid_pack", "nm_hybrid_pack_workspace_size", "nm_hybrid_gemm",
     "nm_hybrid_gemm_workspace_size", "lowered_k",
@@ -90,6 +91,14 @@ def lib() -> ctypes.CDLL:
                                  _i64, _int, _vp, _i64, _vp]
     L.nm_hybrid_gemm_workspace_size.restype = _i64
     L.nm_hybrid_gemm_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _int]
+    L.nm_probe_sink_bytes.restype = _i64
+    L.nm_probe_sink_bytes.argtypes = []
+    L.nm_probe_read.restype = _int
+    L.nm_probe_read.argtypes = [_vp, _i64, _vp, _vp]
+    L.nm_probe_mfma_flops.restype = _i64
+    L.nm_probe_mfma_flops.argtypes = [_i64]
+    L.nm_probe_mfma.restype = _int
+    L.nm_probe_mfma.argtypes = [_i64, _vp, _vp]
     _LIB = L
     return L
 
@@ -258,3 +267,26 @@ def nm_hybrid_gemm(x, sparse_cols, k_s, dense_cols, k_d, ws_values, ws_meta, fmt
         _check(st, "nm_hybrid_gemm")
     return st
 
+
+# ------------------------------------------------------------ measurement helpers ---
+
+def nm_probe_sink_bytes():
+    return lib().nm_probe_sink_bytes()
+
+
+def nm_probe_read(buf, nbytes, sink, stream=None, *, check=True):
+    st = lib().nm_probe_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream))
+    if check:
+        _check(st, "nm_probe_read")
+    return st
+
+
+def nm_probe_mfma_flops(iters):
+    return lib().nm_probe_mfma_flops(iters)
+
+
+def nm_probe_mfma(iters, sink, stream=None, *, check=True):
+    st = lib().nm_probe_mfma(iters, _ptr(sink), _stream(stream))
+    if check:
+        _check(st, "nm_probe_mfma")
+    return st

@@ -164,3 +164,18 @@ def test_binding_lowered_k_matches_oracle():
         for k in (2 * ns, 2 * ns * 7, 4096 - 4096 % (2 * ns)):
             assert S.lowered_k(k, ns) == O.lowered_k(k, ns)
 
+
+
+def test_probe_helpers_host_side():
+    """Measurement helpers: sizes are host arithmetic; bad arguments are rejected before
+    any GPU call."""
+    assert S.nm_probe_sink_bytes() >= 2048 * 256 * 4
+    assert S.nm_probe_mfma_flops(10) == 1024 * 4 * 16 * 10 * 16 * 16 * 32 * 2
+    assert S.nm_probe_mfma_flops(-1) == 0
+    assert S.nm_probe_read(None, -16, None, check=False, stream=0) == S.NM_ESHAPE
+    assert S.nm_probe_read(None, 24, None, check=False, stream=0) == S.NM_ESHAPE
+    assert S.nm_probe_read(None, 32, None, check=False, stream=0) == S.NM_EINVAL
+    assert S.nm_probe_read(16 * 1024 + 4, 32, 16 * 1024, check=False, stream=0) == S.NM_EALIGN
+    assert S.nm_probe_mfma(-1, 16 * 1024, check=False, stream=0) == S.NM_ESHAPE
+    assert S.nm_probe_mfma(1, None, check=False, stream=0) == S.NM_EINVAL
+    assert S.nm_probe_mfma(1, 16 * 1024 + 8, check=False, stream=0) == S.NM_EALIGN

@@ -853,3 +853,32 @@ def test_zero_sizes_and_k_zero():
     assert (host(y, np.float32) == 5).all()
     a.t = 0
     assert S.nm_spmm(a, check=False) == S.NM_OK
+
+
+# ------------------------------------------------------------ measurement probes ---
+
+@pytest.mark.gpu
+def test_measurement_probes():
+    """The read probe XORs what each thread loads (one 16-byte element per thread when the
+    buffer holds exactly one per thread); the matrix probe's sums scale with its round
+    count (small integers, exact in fp32)."""
+    print("probes", flush=True)
+    import torch
+    nth = 2048 * 256
+    rng = np.random.default_rng(11)
+    words = rng.integers(0, 2**32, size=(nth, 4), dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).cuda()
+    sink = torch.zeros((S.nm_probe_sink_bytes() // 4,), dtype=torch.int32, device="cuda")
+    S.nm_probe_read(buf, nth * 16, sink)
+    sync()
+    got = sink[:nth].cpu().numpy().view(np.uint32)
+    assert (got == (words[:, 0] ^ words[:, 1] ^ words[:, 2] ^ words[:, 3])).all()
+    outs = []
+    for iters in (0, 3, 6):
+        fs = torch.full((S.nm_probe_sink_bytes() // 4,), float("nan"), dtype=torch.float32, device="cuda")
+        S.nm_probe_mfma(iters, fs)
+        sync()
+        outs.append(fs[:1024 * 256].cpu().numpy())
+    assert (outs[0] == 0).all()
+    assert np.isfinite(outs[1]).all() and (outs[1] > 0).all()
+    assert (outs[2] == 2 * outs[1]).all()
