@@ -9,21 +9,23 @@
 //  * Both operands are K-contiguous rows.  A K-step moves 64 bf16 (128 bytes) of every
 //    tile row straight from global memory into LDS with global_load_lds_dwordx4: one
 //    wave instruction fills 8 whole rows (1 KiB, contiguous in LDS), so no VGPRs are
-//    spent on staging and every global access is a full 128-byte line.
-//  * LDS rows are unpadded; the 16-byte chunk c of row r lives at chunk c ^ ((r>>1)&7),
-//    which keeps the 16-lane groups of a ds_read_b128 fragment read on distinct banks.
-//  * Two LDS stages (64 KiB each for a 256x256 tile): the loads of K-step k+1 are issued
-//    a group at a time between the matrix instructions of K-step k; one barrier per
-//    K-step.  The waves raise their priority while issuing matrix instructions.
+//    spent on staging and every global access is a full 128-byte line.  fp8 weights
+//    move 64-byte rows of codes and are widened per fragment.
+//  * LDS rows are unpadded; the 16-byte chunk c of row r lives at chunk c ^ ((r>>1)&7)
+//    (c ^ ((r>>2)&3) for 64-byte rows), which keeps the 16-lane groups of a ds_read_b128
+//    fragment read on distinct banks.
+//  * Two LDS stages (64 KiB each for a 256x256 tile): each K-step first issues the loads
+//    of the next step into the other stage, then multiplies; one barrier per K-step.
+//    Fragments are read one matrix step ahead.  Measured on gfx950 (8192 x 14336 x 4096):
+//    without the per-step loads the same loop runs at 2.1 PFLOP/s; 32-wide K-steps with
+//    four stages (three steps in flight) were 13% slower than this (twice the barriers).
 //  * The keep mask travels with the X tile (two 32-bit words per row per K-step) and is
-//    applied to each 8-element X fragment right after its LDS read (4 VALU ops per
-//    dword, overlapping the matrix instructions).
+//    applied to each 8-element X fragment right after its LDS read.
 //  * 8 waves (2 per SIMD), each owning a 64 (o) x 128 (t) block of 16x16 accumulators
-//    (v_mfma_f32_16x16x32_bf16); workgroups are remapped so each XCD (own L2) walks a
-//    compact band of output tiles.  Measured on gfx950: LDS reads sustain ~128 B/clk per
-//    CU, so the 2 x 4 KiB fragment reads per wave per K-step and the 64 KiB of staged
-//    tiles keep the LDS about as busy as the matrix cores; the 64 x 128 wave shape and
-//    the priority hint were the fastest of the variants tried.
+//    (v_mfma_f32_16x16x32_bf16); 4 waves of 128 x 128 (one per SIMD) were 15% slower.
+//    Workgroups are remapped so each XCD (own L2) runs a near-square block of tiles.
+//  * The few-token shapes (128-row tiles, split K) reuse the kernel with four stages as
+//    an option (three K-steps in flight, per-wave counted waits and a bare barrier).
 // Requirements (checked by the dispatcher): K % 64 == 0, 16-byte aligned rows.  Rows
 // beyond T or O are read from the last valid row and their outputs are not stored.
 #include "nm_device.h"
@@ -39,12 +41,13 @@ constexpr int BK = 64;                 // bf16 per K-step
 // vmcnt(n) alone (vmcnt split over bits 3:0 and 15:14)
 constexpr int kWaitLgkm0 = 0xC07F;
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-constexpr int ROWB = BK * 2;           // bytes per tile row per K-step
 
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }    // 8 pieces per row
 __device__ __forceinline__ int swz4(int r, int c) { return c ^ ((r >> 2) & 3); }   // 4 pieces per row
+template <int PC>
+__device__ __forceinline__ int pswz(int r, int c) { return PC == 8 ? swz(r, c) : swz4(r, c); }
 
 // global -> LDS copy of `bytes` (4 or 16) per lane: lane i writes lds + i * bytes.  The
 // LDS address must be wave-uniform (it is passed in M0).
@@ -62,7 +65,7 @@ __device__ __forceinline__ uint32_t keep_pair(uint32_t d, uint32_t bits, int q) 
   return d & ((hi & 0xFFFF0000u) | (lo & 0x0000FFFFu));
 }
 
-template <int BM, int BN, int WM, int WN, int PRO, bool W8, int NST>
+template <int BM, int BN, int WM, int WN, int PRO, bool W8, int NST, int KH>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
     const unsigned char* __restrict__ w, int64_t ldw, const uint16_t* __restrict__ x, int64_t ldx,
     const uint32_t* __restrict__ xmask, int64_t T, int64_t O, int64_t K, float* __restrict__ y,
@@ -71,14 +74,17 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
   constexpr int NW = WM * WN;
   constexpr int SM = BM / WM, SN = BN / WN;       // wave sub-tile (o x t)
   constexpr int FI = SM / 16, FJ = SN / 16;
-  // W rows per K-step: 128 bytes of bf16, or 64 bytes of fp8 codes (4 pieces per row)
-  constexpr int AROWB = W8 ? 64 : ROWB, A_RPG = W8 ? 16 : 8;   // bytes per row, rows per load group
-  constexpr int A_BYTES = BM * AROWB, B_BYTES = BN * ROWB;
+  // A K-step is KH halves of 32 positions.  Rows per step: X 64*KH bytes (8 or 4 pieces of
+  // 16 bytes); W the same in bf16, or 32*KH bytes of fp8 codes.  A load group is 1 KiB.
+  static_assert(KH == 2 || (KH == 1 && !W8 && PRO == PRO_NONE), "32-position steps: bf16, plain prologue");
+  constexpr int SBK = 32 * KH;
+  constexpr int XROWB = 2 * SBK, XPC = XROWB / 16, X_RPG = 64 / XPC;
+  constexpr int AROWB = W8 ? SBK : XROWB, APC = AROWB / 16, A_RPG = 64 / APC;
+  constexpr int A_BYTES = BM * AROWB, B_BYTES = BN * XROWB;
   constexpr int MASK_BYTES = (PRO == PRO_MASK) ? BN * 8 : 16;
-  constexpr int A_GROUPS = BM / A_RPG, B_GROUPS = BN / 8;   // load groups (1 KiB each)
+  constexpr int A_GROUPS = BM / A_RPG, B_GROUPS = BN / X_RPG;
   constexpr int NGA = A_GROUPS / NW, NGB = B_GROUPS / NW;
   static_assert(A_GROUPS % NW == 0 && B_GROUPS % NW == 0, "load groups per wave");
-  static_assert(NGA <= 2 * FI && NGB <= 2 * FI, "load groups are spread over the 2*FI MFMA steps");
   constexpr int MASK_GROUPS = (PRO == PRO_MASK) ? BN / 32 : 0;   // 32 rows x 2 words per inst
 
   // NST (2 or 4) stages as distinct arrays: every LDS access names its stage statically,
@@ -110,23 +116,22 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
   const int64_t o0 = (int64_t)tile_m * BM, t0 = (int64_t)tile_n * BN;
 
   // per-lane global source addresses of this wave's load groups (K offset added per step)
-  const int lrow = lane >> 3, lchunk = lane & 7;
   const unsigned char* asrc[NGA];
   const uint16_t* bsrc[NGB];
   constexpr int WBYTES = W8 ? 1 : 2;   // bytes per weight element
 #pragma unroll
   for (int g = 0; g < NGA; ++g) {
-    const int r = (wave + g * NW) * A_RPG + (W8 ? (lane >> 2) : lrow);
+    const int r = (wave + g * NW) * A_RPG + lane / APC;
     int64_t o = o0 + r;
     if (o >= O) o = O - 1;
-    asrc[g] = w + (o * ldw) * WBYTES + 16 * (W8 ? swz4(r, lane & 3) : swz(r, lchunk));
+    asrc[g] = w + (o * ldw) * WBYTES + 16 * pswz<APC>(r, lane % APC);
   }
 #pragma unroll
   for (int g = 0; g < NGB; ++g) {
-    const int r = (wave + g * NW) * 8 + lrow;
+    const int r = (wave + g * NW) * X_RPG + lane / XPC;
     int64_t t = t0 + r;
     if (t >= T) t = T - 1;
-    bsrc[g] = x + t * ldx + 8 * swz(r, lchunk);
+    bsrc[g] = x + t * ldx + 8 * pswz<XPC>(r, lane % XPC);
   }
   const int64_t mwords = K >> 5;
   const uint32_t* msrc = nullptr;
@@ -163,7 +168,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
     for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int fr = lane & 15, fq = lane >> 4;
-  const int nk = (int)((kend - kbeg) / BK);
+  const int nk = (int)((kend - kbeg) / SBK);
 
   // Multiply one staged K-step (two 32-wide halves, FI row steps each).  Fragments are
   // read one step ahead: the A fragment of the next row step, and during the first half
@@ -177,7 +182,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
       const uint2 q = *reinterpret_cast<const uint2*>(abase + r * 64 + 16 * swz4(r, 2 * ks + (fq >> 1)) + 8 * (fq & 1));
       return u32x4{q.x, q.y, 0u, 0u};
     } else {
-      return *reinterpret_cast<const u32x4*>(abase + r * ROWB + 16 * swz(r, 4 * ks + fq));
+      return *reinterpret_cast<const u32x4*>(abase + r * AROWB + 16 * pswz<APC>(r, 4 * ks + fq));
     }
   };
   auto a_frag = [&](u32x4 v) {
@@ -192,7 +197,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
   };
   auto read_b = [&](const unsigned char* bbase, int ks, int j) {
     const int r = wn * SN + j * 16 + fr;
-    return *reinterpret_cast<const u32x4*>(bbase + r * ROWB + 16 * swz(r, 4 * ks + fq));
+    return *reinterpret_cast<const u32x4*>(bbase + r * XROWB + 16 * pswz<XPC>(r, 4 * ks + fq));
   };
   auto compute = [&](const unsigned char* abase, const unsigned char* bbase, const unsigned char* mbase) {
     uint2 mw[FJ];
@@ -209,7 +214,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
     u32x4 acur = read_a(abase, 0, 0), anxt;
     constexpr int BPS = (FJ + FI - 1) / FI;   // second-half B fragments read per row step
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < KH; ++ks) {
       bf16x8 bfr[FJ];
 #pragma unroll
       for (int j = 0; j < FJ; ++j) {
@@ -232,8 +237,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         __builtin_amdgcn_sched_barrier(0);
         if (i + 1 < FI) anxt = read_a(abase, ks, i + 1);
-        else if (ks == 0) anxt = read_a(abase, 1, 0);
-        if (ks == 0) {
+        else if (ks + 1 < KH) anxt = read_a(abase, ks + 1, 0);
+        if (ks + 1 < KH) {
 #pragma unroll
           for (int q = 0; q < BPS; ++q)
             if (i * BPS + q < FJ) b1[i * BPS + q] = read_b(bbase, 1, i * BPS + q);
@@ -260,12 +265,12 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
     // read anyway, so no later LDS read waits behind them); the last step reloads step 0
     // into the idle stage instead (never read), so every step runs the same code.
     for (int kt = 0; kt < nk; kt += 2) {
-      issue_all(sA1, sB1, sM1, kt + 1 < nk ? (int64_t)(kt + 1) * BK : 0);
+      issue_all(sA1, sB1, sM1, kt + 1 < nk ? (int64_t)(kt + 1) * SBK : 0);
       compute(sA0, sB0, sM0);
       __builtin_amdgcn_s_waitcnt(0);   // next stage landed in LDS
       __syncthreads();
       if (kt + 1 < nk) {
-        issue_all(sA0, sB0, sM0, kt + 2 < nk ? (int64_t)(kt + 2) * BK : 0);
+        issue_all(sA0, sB0, sM0, kt + 2 < nk ? (int64_t)(kt + 2) * SBK : 0);
         compute(sA1, sB1, sM1);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -290,25 +295,66 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
     };
+    auto wait_n = [&](int pending) {   // pending: load instructions allowed in flight
+      if (pending == 2 * L) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * L));
+      else if (pending == L) __builtin_amdgcn_s_waitcnt(vmcnt_imm(L));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    if (nk % 4 == 0 && nk >= 8) {
+      // Steady trips issue unconditionally, so the compiler's count of loads in flight
+      // into each stage stays exact and it adds no waits of its own; the last trip
+      // (which issues only step nk - 1) is written out after the loop.
+      issue_all(sA0, sB0, sM0, 0);
+      issue_all(sA1, sB1, sM0, SBK);
+      issue_all(sA2, sB2, sM0, 2 * SBK);
+      int kt = 0;
+      for (; kt + 8 <= nk; kt += 4) {
+        wait_n(2 * L);
+        issue_all(sA3, sB3, sM0, (int64_t)(kt + 3) * SBK);
+        compute(sA0, sB0, sM0);
+        wait_n(2 * L);
+        issue_all(sA0, sB0, sM0, (int64_t)(kt + 4) * SBK);
+        compute(sA1, sB1, sM0);
+        wait_n(2 * L);
+        issue_all(sA1, sB1, sM0, (int64_t)(kt + 5) * SBK);
+        compute(sA2, sB2, sM0);
+        wait_n(2 * L);
+        issue_all(sA2, sB2, sM0, (int64_t)(kt + 6) * SBK);
+        compute(sA3, sB3, sM0);
+      }
+      wait_n(2 * L);
+      issue_all(sA3, sB3, sM0, (int64_t)(kt + 3) * SBK);
+      compute(sA0, sB0, sM0);
+      wait_n(2 * L);
+      compute(sA1, sB1, sM0);
+      wait_n(L);
+      compute(sA2, sB2, sM0);
+      wait_n(0);
+      compute(sA3, sB3, sM0);
+    } else {
     // The first trip (kt = -4) only issues steps 0-2, through the same instructions as
     // every later trip, so the compiler's tracking of which stage each load writes stays
     // exact around the loop (a separate prologue makes it wait for all loads).
     for (int kt = -4; kt < nk; kt += 4) {
       if (kt >= 0) wait_step(kt);
-      if (kt + 3 >= 0 && kt + 3 < nk) issue_all(sA3, sB3, sM0, (int64_t)(kt + 3) * BK);
+      if (kt + 3 >= 0 && kt + 3 < nk) issue_all(sA3, sB3, sM0, (int64_t)(kt + 3) * SBK);
       if (kt >= 0) compute(sA0, sB0, sM0);
       if (kt + 1 >= nk) break;
       if (kt + 1 >= 0) wait_step(kt + 1);
-      if (kt + 4 < nk) issue_all(sA0, sB0, sM0, (int64_t)(kt + 4) * BK);
+      if (kt + 4 < nk) issue_all(sA0, sB0, sM0, (int64_t)(kt + 4) * SBK);
       if (kt + 1 >= 0) compute(sA1, sB1, sM0);
       if (kt + 2 >= nk) break;
       if (kt + 2 >= 0) wait_step(kt + 2);
-      if (kt + 5 < nk) issue_all(sA1, sB1, sM0, (int64_t)(kt + 5) * BK);
+      if (kt + 5 < nk) issue_all(sA1, sB1, sM0, (int64_t)(kt + 5) * SBK);
       if (kt + 2 >= 0) compute(sA2, sB2, sM0);
       if (kt + 3 >= nk) break;
       if (kt + 3 >= 0) wait_step(kt + 3);
-      if (kt + 6 < nk) issue_all(sA2, sB2, sM0, (int64_t)(kt + 6) * BK);
+      if (kt + 6 < nk) issue_all(sA2, sB2, sM0, (int64_t)(kt + 6) * SBK);
       if (kt + 3 >= 0) compute(sA3, sB3, sM0);
+    }
     }
   }
 
@@ -366,7 +412,7 @@ static int group_for(int tiles_m, int bm, int bn) {
   return g < tiles_m ? g : tiles_m;
 }
 
-template <int BM, int BN, int WM, int WN, int PRO, bool W8 = false, int NST = 2>
+template <int BM, int BN, int WM, int WN, int PRO, bool W8 = false, int NST = 2, int KH = 2>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s, int64_t splits, float* part) {
   const int tiles_m = (int)((a.o + BM - 1) / BM), tiles_n = (int)((a.t + BN - 1) / BN);
   const int64_t ntiles = (int64_t)tiles_m * tiles_n;
@@ -374,7 +420,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s, int64_t splits, float* p
   int64_t kslice = ((a.k / BK + splits - 1) / splits) * BK;
   splits = (a.k + kslice - 1) / kslice;
   if (ntiles * splits > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  auto kern = k_gemm_lds<BM, BN, WM, WN, PRO, W8, NST>;
+  auto kern = k_gemm_lds<BM, BN, WM, WN, PRO, W8, NST, KH>;
   kern<<<dim3((unsigned)(ntiles * splits)), dim3(64 * WM * WN), 0, s>>>(
       (const unsigned char*)a.w, a.ldw, a.x, a.ldx, a.x_mask, a.t, a.o, a.k, a.y, a.ldy, a.accumulate, tiles_m, tiles_n,
       kslice, splits > 1 ? part : nullptr, a.w_scale, group_for(tiles_m, BM, BN));
