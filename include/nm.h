@@ -157,12 +157,13 @@ typedef enum {
  *   workspace   device scratch (16-byte aligned).  With workspace_bytes >=
  *               nm_spmm_workspace_size(args): ACT_DYNAMIC may run select and product as
  *               two passes (S(x) staged in the workspace), ACT_COMPRESSED stages the
- *               decompressed x there (required unless n:m = 2:4 with 2BIT metadata), and
- *               few-token calls (t <= 128) with a small o may split the reduction across
- *               workgroups, writing fp32 partial sums there that a second kernel adds in
- *               a fixed order.  With less, the call takes a single-pass route.  Contents
- *               after the call are unspecified.  Calls sharing a workspace must be
- *               ordered (same stream).
+ *               decompressed x there (required unless n:m = 2:4 with 2BIT metadata),
+ *               W_SLIDE calls above 16-32 tokens stage the lifted x there, and few-token
+ *               calls (t <= 128) may split the reduction across workgroups, writing fp32
+ *               partial sums there that a second kernel adds in a fixed order (the
+ *               split-K tile route for 33-128 tokens needs this).  With less, the call
+ *               takes a route that needs none (slower).  Contents after the call are
+ *               unspecified.  Calls sharing a workspace must be ordered (same stream).
  * Results are deterministic: the same call on the same inputs gives the same bits.
  */
 typedef struct {

@@ -21,7 +21,7 @@ import numpy as np
 __all__ = [
     "bf16_bits_from_f32", "f32_from_bf16_bits", "normal_bf16", "student_t_bf16",
     "fp8_e4m3_quantize_rows", "sha256", "layer_2of4_small", "mlp_down_8of16",
-    "slide_6of8_layer", "hybrid_up_layer", "transformer_layer",
+    "slide_6of8_layer", "hybrid_up_layer", "transformer_layer", "device_normal_bf16",
 ]
 
 
@@ -66,6 +66,18 @@ def fp8_e4m3_quantize_rows(w_bits: np.ndarray):
     s[s == 0] = np.float32(1.0)
     q = torch.from_numpy((w / s[:, None]).astype(np.float32)).to(torch.float8_e4m3fn)
     return q.view(torch.uint8).numpy().copy(), s
+
+
+def device_normal_bf16(torch, shape, seed: int, std: float = 1.0):
+    """N(0, std) drawn on the GPU from a seeded generator and rounded to bf16 (nearest
+    even), returned as a device int16 tensor of bf16 bit patterns.  For inputs too large
+    to draw on the host; tests copy the rows they check back to the host."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    x = torch.randn(shape, generator=g, device="cuda", dtype=torch.float32)
+    if std != 1.0:
+        x *= std
+    return x.to(torch.bfloat16).view(torch.int16)
 
 
 def sha256(*arrays) -> str:

@@ -855,6 +855,33 @@ def test_zero_sizes_and_k_zero():
     assert S.nm_spmm(a, check=False) == S.NM_OK
 
 
+def test_large_offsets_sampled():
+    """Operands past 2^31 bytes: X 70000 x 16384 bf16 (2.3 GB, drawn on the GPU from a
+    seeded generator), 8:16 activations into O = 256 through select, S(X) staged in a
+    2.3 GB workspace and the direct-to-LDS product.  Mask and outputs on sampled rows,
+    including rows whose byte offset is past 2^31 and the last row."""
+    import torch
+    print("large offsets t=70000 k=16384 o=256", flush=True)
+    t, k, o = 70000, 16384, 256
+    xd = synth.device_normal_bf16(torch, (t, k), seed=12)
+    w = synth.normal_bf16(np.random.default_rng(13), (o, k), 0.02)
+    y = empty((t, o), np.float32, fill=float("nan"))
+    mask = empty((t, k // 32), np.uint32, fill=-1)
+    a = S.make_spmm_args(S.NM_ACT_DYNAMIC, t, o, k, xd, dev(w), y, n=8, m=16, x_mask_out=mask)
+    nb = S.nm_spmm_workspace_size(a)
+    assert nb >= t * k * 2
+    ws = empty((nb,), np.uint8)
+    a.workspace, a.workspace_bytes = ws.data_ptr(), nb
+    S.nm_spmm(a)
+    sync()
+    rows = np.array(sorted(set(sample_rows(t, 10, seed=3).tolist()) | {65535, 65536, 69999}))
+    xr = xd[torch.from_numpy(rows).cuda()].cpu().numpy().view(np.uint16)
+    sx, keep = O.sparsify(xr, 8, 16)
+    assert (host(mask, np.uint32)[rows] == O.pack_mask(keep)).all()
+    check_gemm(host(y, np.float32)[rows], O.gemm(sx, w), sx, w, label="large offsets")
+    del ws, xd
+
+
 # ------------------------------------------------------------ measurement probes ---
 
 @pytest.mark.gpu
