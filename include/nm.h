@@ -35,10 +35,13 @@
  *    caller's next synchronisation.  No call throws; all are thread-safe and stateless.
  *  - Alignment: every device pointer must be 16-byte aligned and every bf16 leading
  *    dimension a multiple of 8 elements (nm_sparsify / nm_compress / nm_decompress with
- *    m = 4 accept a multiple of 4, nm_slide_lift any); fp8 weights need a leading
- *    dimension that is a multiple of 16 bytes (NM_EALIGN otherwise).  fp32 outputs take
- *    any leading dimension >= O.
- *  - Supported patterns: m in {4, 8, 16, 32}, 1 <= n <= m, K % m == 0.
+ *    m = 4 accept a multiple of 4, with m in {6, 10, 12, 14} a multiple of 2,
+ *    nm_slide_lift any); fp8 weights need a leading dimension that is a multiple of 16
+ *    bytes (NM_EALIGN otherwise).  fp32 outputs take any leading dimension >= O.
+ *  - Supported patterns: m in {4, 8, 16, 32}, 1 <= n <= m, K % m == 0.  nm_sparsify,
+ *    nm_compress and nm_decompress also take m in {6, 10, 12, 14} (the group widths of
+ *    the (2N-2):2N weight family, [SLIDE] 2.A) without a bitmask, since such groups
+ *    straddle the 32-bit mask words (NM_EUNSUPPORTED with a mask).
  *  - Sizes are int64_t; rows, K, T, O >= 0 (zero-size calls return NM_OK and launch
  *    nothing, except that nm_spmm / nm_hybrid_gemm with K == 0 still write Y = 0 (or
  *    leave it unchanged when accumulating)).

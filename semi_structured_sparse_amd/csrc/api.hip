@@ -15,6 +15,8 @@ constexpr int kVersion = 100;  // 0.1.0
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool supported_m(int m) { return m == 4 || m == 8 || m == 16 || m == 32; }
+// group widths the select / compact / scatter kernels also take (no bitmask)
+inline bool select_only_m(int m) { return m == 6 || m == 10 || m == 12 || m == 14; }
 
 inline bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   if (a < 0 || b < 0) return false;
@@ -57,11 +59,22 @@ nm_status check_bf16(const void* p, int64_t rows, int64_t k, int64_t ld, bool re
 
 // Row alignment the group kernels need: one group of m bf16 per lane, loaded in one
 // piece of min(16, 2m) bytes.
-inline int group_ld_mult(int m) { return m < 8 ? m : 8; }
+inline int group_ld_mult(int m) { return select_only_m(m) ? 2 : (m < 8 ? m : 8); }
+
 
 nm_status check_pattern(int64_t k, int n, int m) {
   if (!supported_m(m)) return (m >= 1 && n >= 1 && n <= m) ? NM_EUNSUPPORTED : NM_EINVAL;
   if (n < 1 || n > m) return NM_EINVAL;
+  if (k < 0 || (k % m) != 0) return NM_ESHAPE;
+  return NM_OK;
+}
+
+// check_pattern for the select-family calls: also the (2N-2):2N widths, when no bitmask
+// is requested
+nm_status check_select_pattern(int64_t k, int n, int m, bool mask) {
+  if (!select_only_m(m)) return check_pattern(k, n, m);
+  if (n < 1 || n > m) return NM_EINVAL;
+  if (mask) return NM_EUNSUPPORTED;
   if (k < 0 || (k % m) != 0) return NM_ESHAPE;
   return NM_OK;
 }
@@ -270,7 +283,7 @@ int nm_version(void) { return kVersion; }
 
 nm_status nm_sparsify(const void* x, int64_t rows, int64_t k, int64_t ldx, int n, int m, void* y,
                       int64_t ldy, uint32_t* mask, void* stream) {
-  nm_status st = check_pattern(k, n, m);
+  nm_status st = check_select_pattern(k, n, m, mask != nullptr);
   if (st) return st;
   if (rows < 0) return NM_ESHAPE;
   if (y == nullptr && mask == nullptr) return NM_EINVAL;
@@ -284,7 +297,7 @@ nm_status nm_sparsify(const void* x, int64_t rows, int64_t k, int64_t ldx, int n
 
 nm_status nm_compress(const void* x, int64_t rows, int64_t k, int64_t ldx, int n, int m, void* values,
                       void* meta, nm_meta fmt, uint32_t* mask, void* stream) {
-  nm_status st = check_pattern(k, n, m);
+  nm_status st = check_select_pattern(k, n, m, mask != nullptr);
   if (st) return st;
   if (rows < 0) return NM_ESHAPE;
   if (fmt != NM_META_U8 && fmt != NM_META_2BIT) return NM_EINVAL;
@@ -302,7 +315,7 @@ nm_status nm_compress(const void* x, int64_t rows, int64_t k, int64_t ldx, int n
 
 nm_status nm_decompress(const void* values, const void* meta, nm_meta fmt, int64_t rows, int64_t k, int n,
                         int m, void* y, int64_t ldy, void* stream) {
-  nm_status st = check_pattern(k, n, m);
+  nm_status st = check_select_pattern(k, n, m, false);
   if (st) return st;
   if (rows < 0) return NM_ESHAPE;
   if (fmt != NM_META_U8 && fmt != NM_META_2BIT) return NM_EINVAL;

@@ -85,6 +85,30 @@ __device__ __forceinline__ uint32_t topn_bits_n(const uint32_t (&d)[M / 2]) {
   return bits;
 }
 
+// Groups whose width is not a power of two (m = 6, 10, 12, 14: the (2N-2):2N family):
+// the keys are padded with zeros to P = the next power of two.  Every real key is at
+// least 0xFFFF - i > 0, so the pads sort last and the n-th largest key is unchanged.
+template <int M, int P>
+__device__ __forceinline__ uint32_t topn_bits_pad(const uint32_t (&d)[M / 2], int n) {
+  static_assert(M % 2 == 0 && M <= P && (P & (P - 1)) == 0, "even width, power-of-two pad");
+  uint32_t c[M], s[P];
+#pragma unroll
+  for (int q = 0; q < M / 2; ++q) {
+    c[2 * q] = ((d[q] << 16) & 0x7FFF0000u) | (0xFFFFu - 2 * q);
+    c[2 * q + 1] = (d[q] & 0x7FFF0000u) | (0xFFFFu - 2 * q - 1);
+  }
+#pragma unroll
+  for (int i = 0; i < P; ++i) s[i] = i < M ? c[i] : 0u;
+  sort_desc_oem<P>(s);
+  uint32_t tau = s[0];
+#pragma unroll
+  for (int j = 1; j < M; ++j) tau = (j == n - 1) ? s[j] : tau;
+  uint32_t bits = 0;
+#pragma unroll
+  for (int i = 0; i < M; ++i) bits |= (c[i] >= tau ? 1u : 0u) << i;
+  return bits;
+}
+
 // d: the group as packed dwords (element 2q in the low half of d[q]).  Returns the keep
 // bits (bit i set iff element i is kept), exactly n bits set for 1 <= n <= M.
 template <int M>

@@ -21,9 +21,16 @@ using namespace nmk;
 constexpr int kWavesPerBlock = 4;
 constexpr int kMaxN = 32;
 
+// widths that are not a multiple of 8 (other than 4) move dword by dword
+template <int M>
+constexpr bool kDwordGroups = (M % 8) != 0 && M != 4;
+
 template <int M>
 __device__ __forceinline__ void load_group(const uint16_t* p, uint32_t (&d)[M / 2]) {
-  if constexpr (M == 4) {
+  if constexpr (kDwordGroups<M>) {
+#pragma unroll
+    for (int q = 0; q < M / 2; ++q) d[q] = reinterpret_cast<const uint32_t*>(p)[q];
+  } else if constexpr (M == 4) {
     const uint2 v = *reinterpret_cast<const uint2*>(p);
     d[0] = v.x; d[1] = v.y;
   } else {
@@ -37,7 +44,10 @@ __device__ __forceinline__ void load_group(const uint16_t* p, uint32_t (&d)[M / 
 
 template <int M>
 __device__ __forceinline__ void store_group(uint16_t* p, const uint32_t (&d)[M / 2]) {
-  if constexpr (M == 4) {
+  if constexpr (kDwordGroups<M>) {
+#pragma unroll
+    for (int q = 0; q < M / 2; ++q) reinterpret_cast<uint32_t*>(p)[q] = d[q];
+  } else if constexpr (M == 4) {
     *reinterpret_cast<uint2*>(p) = make_uint2(d[0], d[1]);
   } else {
 #pragma unroll
@@ -101,7 +111,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_select(
   }
   uint32_t keep = 0u;
   if (valid) {
-    if constexpr (NT > 0) keep = topn_bits_n<M, NT>(d);
+    if constexpr (kDwordGroups<M>) keep = topn_bits_pad<M, (M <= 8 ? 8 : 16)>(d, n);
+    else if constexpr (NT > 0) keep = topn_bits_n<M, NT>(d);
     else keep = topn_bits<M>(d, n);
   }
 
@@ -112,7 +123,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_select(
     store_group<M>(y + row * ldy + g * M, o);
   }
 
-  if (mask != nullptr) {
+  if constexpr (32 % M == 0) if (mask != nullptr) {
     uint32_t w = keep << ((uint32_t)(g * M) & 31u);
     if constexpr (M < 32) {
 #pragma unroll
@@ -177,7 +188,7 @@ __global__ __launch_bounds__(256) void k_decompress(
       const int64_t slot = g * n + j;
       pos = (meta[row * ((k + 7) >> 3) + (slot >> 2)] >> (2 * (slot & 3))) & 3u;
     } else {
-      pos = meta[row * kc + g * n + j] & (uint32_t)(M - 1);
+      pos = (uint32_t)meta[row * kc + g * n + j] % (uint32_t)M;
     }
 #pragma unroll
     for (int i = 0; i < M; ++i) {
@@ -210,6 +221,10 @@ hipError_t launch_select(int m, const uint16_t* x, int64_t rows, int64_t k, int6
     case 8: NM_SELECT(8) break;
     case 16: NM_SELECT(16) break;
     case 32: NM_SELECT(32) break;
+    case 6: k_select<6, 0><<<grid, block, 0, s>>>(x, rows, k, ldx, n, y, ldy, nullptr, values, meta, meta_2bit); break;
+    case 10: k_select<10, 0><<<grid, block, 0, s>>>(x, rows, k, ldx, n, y, ldy, nullptr, values, meta, meta_2bit); break;
+    case 12: k_select<12, 0><<<grid, block, 0, s>>>(x, rows, k, ldx, n, y, ldy, nullptr, values, meta, meta_2bit); break;
+    case 14: k_select<14, 0><<<grid, block, 0, s>>>(x, rows, k, ldx, n, y, ldy, nullptr, values, meta, meta_2bit); break;
     default: return hipErrorInvalidValue;
   }
 #undef NM_SELECT
@@ -228,6 +243,10 @@ hipError_t launch_decompress(int m, const uint16_t* values, const uint8_t* meta,
     case 8: k_decompress<8><<<grid, block, 0, s>>>(values, meta, meta_2bit, rows, k, n, y, ldy); break;
     case 16: k_decompress<16><<<grid, block, 0, s>>>(values, meta, meta_2bit, rows, k, n, y, ldy); break;
     case 32: k_decompress<32><<<grid, block, 0, s>>>(values, meta, meta_2bit, rows, k, n, y, ldy); break;
+    case 6: k_decompress<6><<<grid, block, 0, s>>>(values, meta, meta_2bit, rows, k, n, y, ldy); break;
+    case 10: k_decompress<10><<<grid, block, 0, s>>>(values, meta, meta_2bit, rows, k, n, y, ldy); break;
+    case 12: k_decompress<12><<<grid, block, 0, s>>>(values, meta, meta_2bit, rows, k, n, y, ldy); break;
+    case 14: k_decompress<14><<<grid, block, 0, s>>>(values, meta, meta_2bit, rows, k, n, y, ldy); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -50,7 +50,12 @@ def test_sparsify_validation():
     assert st(f, None, 2, 4, y=Q, rows=4, k=8, ldx=8, ldy=8) == S.NM_EINVAL                   # null x
     assert st(f, P, 0, 4, y=Q, rows=4, k=8, ldx=8, ldy=8) == S.NM_EINVAL                      # n < 1
     assert st(f, P, 5, 4, y=Q, rows=4, k=8, ldx=8, ldy=8) == S.NM_EINVAL                      # n > m
-    assert st(f, P, 2, 6, y=Q, rows=4, k=12, ldx=16, ldy=16) == S.NM_EUNSUPPORTED             # m = 6
+    assert st(f, P, 2, 7, y=Q, rows=4, k=14, ldx=16, ldy=16) == S.NM_EUNSUPPORTED             # m = 7
+    assert st(f, P, 2, 6, y=Q, mask=Q, rows=4, k=12, ldx=16, ldy=16) == S.NM_EUNSUPPORTED     # m = 6 mask
+    assert st(f, P, 2, 6, y=Q, rows=4, k=10, ldx=16, ldy=16) == S.NM_ESHAPE                   # k % 6
+    assert st(f, P, 2, 6, y=Q, rows=4, k=12, ldx=13, ldy=16) == S.NM_EALIGN                   # ld odd (m=6)
+    assert st(f, P, 7, 6, y=Q, rows=4, k=12, ldx=16, ldy=16) == S.NM_EINVAL                   # n > m (m=6)
+    assert st(f, P, 4, 10, y=Q, mask=Q, rows=4, k=20, ldx=20, ldy=20) == S.NM_EUNSUPPORTED    # m = 10 mask
     assert st(f, P, 2, 4, y=Q, rows=4, k=10, ldx=16, ldy=16) == S.NM_ESHAPE                   # k % m
     assert st(f, P, 2, 4, y=Q, rows=4, k=16, ldx=8, ldy=16) == S.NM_ESHAPE                    # ldx < k
     assert st(f, P, 2, 4, y=Q, rows=-1, k=16, ldx=16, ldy=16) == S.NM_ESHAPE                  # rows < 0

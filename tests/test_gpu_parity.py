@@ -86,6 +86,42 @@ def test_select_bitexact(n, m, rows, groups, pad):
         assert (host(vals2, np.uint16) == v_ref).all()
 
 
+# group widths of the (2N-2):2N weight family: no bitmask (groups straddle mask words)
+SELECT_WIDE_CASES = [(4, 6), (1, 6), (6, 6), (8, 10), (3, 10), (10, 12), (6, 12), (12, 14), (7, 14), (13, 14)]
+
+
+@pytest.mark.parametrize("n,m", SELECT_WIDE_CASES)
+@pytest.mark.parametrize("rows,groups,pad", [(37, 131, 0), (5, 3, 2), (70, 64, 6)])
+def test_select_bitexact_family_widths(n, m, rows, groups, pad):
+    """S(X), values + u8 index and the scatter back, for m in {6, 10, 12, 14}; the
+    bitmask is refused for these widths."""
+    print(f"select wide n={n} m={m} rows={rows} groups={groups} pad={pad}", flush=True)
+    rng = np.random.default_rng(2000 * m + n + rows)
+    k = groups * m
+    x = synth.student_t_bf16(rng, (rows, k), 4.0, 0.5)
+    x[: min(4, rows)] = special_rows(k, rng)[: min(4, rows)]
+    ld = k + pad
+    xd = dev(x, ld)
+    y = empty((rows, ld), np.uint16, fill=-1)
+    S.nm_sparsify(xd, n, m, y, None, k=k)
+    kc = k * n // m
+    vals = empty((rows, kc), np.uint16, fill=-1)
+    idx = empty((rows, kc), np.uint8, fill=255)
+    S.nm_compress(xd, n, m, vals, idx, S.NM_META_U8, None, k=k)
+    back = empty((rows, k), np.uint16, fill=-1)
+    S.nm_decompress(vals, idx, S.NM_META_U8, rows, k, n, m, back)
+    sync()
+    s_ref, _ = O.sparsify(x, n, m)
+    v_ref, i_ref = O.compress(x, n, m)
+    assert (host(y, np.uint16)[:, :k] == s_ref).all()
+    assert (host(y, np.uint16)[:, k:] == 0xFFFF).all()
+    assert (host(vals, np.uint16) == v_ref).all()
+    assert (host(idx, np.uint8) == i_ref).all()
+    assert (host(back, np.uint16) == s_ref).all()
+    mk = empty((rows, (k + 31) // 32), np.uint32)
+    assert S.nm_sparsify(xd, n, m, y, mk, k=k, check=False) == S.NM_EUNSUPPORTED
+
+
 @pytest.mark.parametrize("n,m", [(8, 16), (16, 32), (2, 4)])
 def test_select_full_size_sampled(n, m):
     """Down-projection activations at full size (8192 x 14336); oracle on sampled rows."""
@@ -647,19 +683,25 @@ def test_spmm_w_slide(ns, t):
     check_gemm(host(y, np.float32), O.gemm(x, pruned), x, pruned, label=f"slide ns={ns}")
 
 
-@pytest.mark.parametrize("ns", [3, 5])
+@pytest.mark.parametrize("ns", [3, 5, 6, 7])
 def test_spmm_w_slide_odd_family(ns):
-    """4:6 and 8:10 weights: compressed on the host (the GPU select covers m in
-    {4, 8, 16, 32}), lowered and multiplied on the GPU."""
+    """4:6, 8:10, 10:12 and 12:14 weights end to end on the GPU: compressed by the
+    library (bit-exact against the oracle), lowered and multiplied."""
     rng = np.random.default_rng(ns)
     t, o, k = 70, 136, 2 * ns * 24
     x = synth.normal_bf16(rng, (t, k))
     w = synth.normal_bf16(rng, (o, k), 0.02)
-    v, i = O.compress(w, 2 * ns - 2, 2 * ns)
+    v_ref, i_ref = O.compress(w, 2 * ns - 2, 2 * ns)
+    v = empty(v_ref.shape, np.uint16)
+    i = empty(i_ref.shape, np.uint8)
+    S.nm_compress(dev(w), 2 * ns - 2, 2 * ns, v, i, S.NM_META_U8, None)
+    sync()
+    assert (host(v, np.uint16) == v_ref).all()
+    assert (host(i, np.uint8) == i_ref).all()
     kp = O.lowered_k(k, ns)
     vp = empty((o, kp // 2), np.uint16)
     mp = empty((o, (kp + 7) // 8), np.uint8)
-    S.nm_lower_slide(dev(v), dev(i), o, k, ns, vp, mp, S.NM_META_2BIT)
+    S.nm_lower_slide(v, i, o, k, ns, vp, mp, S.NM_META_2BIT)
     y = empty((t, o), np.float32, fill=float("nan"))
     a = S.make_spmm_args(S.NM_W_SLIDE, t, o, k, dev(x), vp, y, ns=ns, w_meta=mp, w_meta_fmt=S.NM_META_2BIT)
     S.nm_spmm(a)
