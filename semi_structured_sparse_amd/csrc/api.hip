@@ -209,6 +209,27 @@ int64_t w_mode_tile_bytes(const nm_spmm_args* a, int64_t kc, int ns) {
   return lift + nml::gemm_lds_sp_small_part_bytes(sa);
 }
 
+// Large-token 2:4-family products on the direct-to-LDS kernel read a K-blocked copy of the
+// weight positions (o * kc / 8 bytes) from the workspace at byte offset `off` when the
+// workspace holds it (NM_META_BLOCK=0 keeps the row-major positions, for A/B measurement).
+bool meta_block_wanted(const nml::SparseArgs& sa) {
+  const char* e = std::getenv("NM_META_BLOCK");
+  if (e != nullptr && std::strcmp(e, "0") == 0) return false;
+  return sa.kc > 0 && sa.w_meta != nullptr && nml::gemm_sparse_uses_lds(sa);
+}
+int64_t meta_block_ws(const nml::SparseArgs& sa) {
+  const char* e = std::getenv("NM_META_BLOCK");
+  if ((e != nullptr && std::strcmp(e, "0") == 0) || sa.kc <= 0 || !nml::gemm_sparse_uses_lds(sa)) return 0;
+  return nml::meta_block_bytes(sa.o, sa.kc);
+}
+nm_status use_meta_block(nml::SparseArgs& sa, void* ws, int64_t ws_bytes, int64_t off, hipStream_t s) {
+  if (ws == nullptr || !meta_block_wanted(sa) || ws_bytes < off + nml::meta_block_bytes(sa.o, sa.kc)) return NM_OK;
+  uint8_t* blk = reinterpret_cast<uint8_t*>(ws) + off;
+  if (nml::launch_meta_block(sa.w_meta, sa.o, sa.kc, blk, s) != hipSuccess) return NM_EHIP;
+  sa.w_meta_blk = blk;
+  return NM_OK;
+}
+
 // Large-token ACT_DYNAMIC with fp8 weights: bytes of a bf16 copy of the weights in the
 // workspace (after the S(X) staging) for the direct-to-LDS product kernel.
 // Only when the codes cannot go to LDS directly (rows not 16-byte multiples), or when
@@ -386,8 +407,16 @@ int64_t nm_spmm_workspace_size(const nm_spmm_args* a) {
     }
   }
   if (part > 0) return align256(stage) + part;
-  if (a->mode == NM_W_SLIDE && !use_few(a->t) && a->t > 0 && a->ns >= 2 && a->ns <= 8 && a->k % (2 * a->ns) == 0)
-    return a->t * lift_ld(w_mode_kc(a)) * 2;   // lifted X for the large-token product
+  if ((a->mode == NM_W_SLIDE || a->mode == NM_W_COMPRESSED) && !use_few(a->t) && a->t > 0 && a->o > 0) {
+    // large-token product: [lifted X (lowered weights)][K-blocked positions]
+    if (a->mode == NM_W_SLIDE && (a->ns < 2 || a->ns > 8 || a->k % (2 * a->ns))) return 0;
+    if (a->mode == NM_W_COMPRESSED && a->k % 4) return 0;
+    const int64_t kc = w_mode_kc(a);
+    const int64_t lift = a->mode == NM_W_SLIDE ? align256(a->t * lift_ld(kc) * 2) : 0;
+    nml::SparseArgs sa = w_mode_sparse_args(a, kc, a->mode == NM_W_SLIDE ? a->ns : 2);
+    const int64_t mb = meta_block_ws(sa);
+    return mb > 0 ? lift + mb : lift;
+  }
   const int64_t widen = fp8_widen_bytes(a);
   return widen > 0 ? align256(stage) + widen : stage;
 }
@@ -575,13 +604,16 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
       sa.x = (const uint16_t*)a->x; sa.ldx = a->ldx; sa.ns = ns;
       sa.loader = a->mode == NM_W_SLIDE ? nml::XL_LIFT : nml::XL_PLAIN;
       sa.t = T; sa.o = O; sa.y = a->y; sa.ldy = a->ldy; sa.accumulate = a->accumulate; sa.trans_out = 0;
+      int64_t off = 0;
       if (a->mode == NM_W_SLIDE && a->workspace != nullptr && a->workspace_bytes >= T * lift_ld(kc) * 2) {
         // materialise lift(X) once so the product kernel reads X with 16-byte loads
         uint16_t* xl = (uint16_t*)a->workspace;
         hipError_t e = nml::launch_lift(ns, (const uint16_t*)a->x, T, K, a->ldx, xl, lift_ld(kc), s);
         if (e != hipSuccess) return NM_EHIP;
         sa.x = xl; sa.ldx = lift_ld(kc); sa.loader = nml::XL_PLAIN;
+        off = align256(T * lift_ld(kc) * 2);
       }
+      if ((st = use_meta_block(sa, a->workspace, a->workspace_bytes, off, s))) return st;
       return hip_status(nml::launch_gemm_sparse(sa, s));
     }
     default:
@@ -627,7 +659,16 @@ int64_t nm_hybrid_gemm_workspace_size(int64_t t, int64_t k_s, int64_t k_d, int64
                            : nml::few_partial_bytes(few_hybrid_args(nullptr, ldp, 0, t, k_s, k_d, nullptr, nullptr,
                                                                     nullptr, k_d, o, nullptr, o, 0));
   }
-  return part > 0 ? align256(stage) + part : stage;
+  if (part > 0) return align256(stage) + part;
+  if (!use_few(t) && k_s > 0) {
+    // large-token product: [permuted X][K-blocked positions]
+    const int64_t ldp = gathered ? hybrid_ldp(k_s, k_d) : k_s + k_d;
+    const nml::SparseArgs sa = hybrid_sparse_args(nullptr, ldp, gathered ? hybrid_off1(k_s) : k_s, t, k_s, k_d,
+                                                  nullptr, nullptr, nullptr, k_d, o, nullptr, o, 0);
+    const int64_t mb = meta_block_ws(sa);
+    if (mb > 0) return align256(stage) + mb;
+  }
+  return stage;
 }
 
 nm_status nm_hybrid_gemm(const void* x, int64_t t, int64_t ldx, const int32_t* sparse_cols, int64_t k_s,
@@ -676,8 +717,8 @@ nm_status nm_hybrid_gemm(const void* x, int64_t t, int64_t ldx, const int32_t* s
     if (e != hipSuccess) return NM_EHIP;
     xa = xp; lda = ldp; dbase = hybrid_off1(k_s);
   }
-  const nml::SparseArgs sa = hybrid_sparse_args(xa, lda, dbase, t, k_s, k_d, ws_values, ws_meta, wd, ldwd, o, y,
-                                                ldy, accumulate);
+  nml::SparseArgs sa = hybrid_sparse_args(xa, lda, dbase, t, k_s, k_d, ws_values, ws_meta, wd, ldwd, o, y, ldy,
+                                          accumulate);
   if (use_few(t)) {
     int64_t avail = 0;
     float* part = ws_slice(workspace, workspace_bytes, stage > 0 ? align256(stage) : 0, &avail);
@@ -687,6 +728,7 @@ nm_status nm_hybrid_gemm(const void* x, int64_t t, int64_t ldx, const int32_t* s
                                                       y, ldy, accumulate),
                                       part, avail, s));
   }
+  if ((st = use_meta_block(sa, workspace, workspace_bytes, stage > 0 ? align256(stage) : 0, s))) return st;
   return hip_status(nml::launch_gemm_sparse(sa, s));
 }
 

@@ -382,12 +382,16 @@ hipError_t launch_pick(const nml::SparseArgs& a, hipStream_t s) {
 
 namespace nml {
 
-hipError_t launch_gemm_sparse(const SparseArgs& a, hipStream_t s) {
+bool gemm_sparse_uses_lds(const SparseArgs& a) {
   // NM_GEMM=regs / lds overrides the kernel choice (A/B measurement and tests)
   const char* force = std::getenv("NM_GEMM");
   const bool regs_only = force != nullptr && std::strcmp(force, "regs") == 0;
   const bool lds_any = force != nullptr && std::strcmp(force, "lds") == 0;
-  if (!regs_only && gemm_lds_sp_eligible(a, lds_any)) return launch_gemm_lds_sp(a, s);
+  return !regs_only && gemm_lds_sp_eligible(a, lds_any);
+}
+
+hipError_t launch_gemm_sparse(const SparseArgs& a, hipStream_t s) {
+  if (gemm_sparse_uses_lds(a)) return launch_gemm_lds_sp(a, s);
   switch (a.loader) {
     case XL_PLAIN: return launch_pick<XL_PLAIN>(a, s);
     case XL_LIFT: return launch_pick<XL_LIFT>(a, s);

@@ -66,8 +66,17 @@ struct SparseArgs {
   int64_t ldy;
   int accumulate;
   int trans_out;          // 0: Y[t][o] with o = sparse-side row; 1: Y[s][d] (X sparse)
+  // optional K-blocked copy of w_meta, [kc/64][o][8 bytes] (launch_meta_block), read by
+  // the direct-to-LDS kernel in place of w_meta; the other kernels ignore it
+  const uint8_t* w_meta_blk;
 };
 hipError_t launch_gemm_sparse(const SparseArgs& a, hipStream_t s);
+// whether launch_gemm_sparse hands this call to the direct-to-LDS kernel
+bool gemm_sparse_uses_lds(const SparseArgs& a);
+// 2-bit positions [o][kc/8] -> K-blocked [kc/64][o][8 bytes] (kc % 64 == 0): one K-step's
+// positions for consecutive rows are contiguous, so a tile loads them as whole lines
+int64_t meta_block_bytes(int64_t o, int64_t kc);
+hipError_t launch_meta_block(const uint8_t* meta, int64_t o, int64_t kc, uint8_t* out, hipStream_t s);
 // direct-to-LDS variant for large problems (plain loader, kc % 64 == 0, kd % 64 == 0)
 bool gemm_lds_sp_eligible(const SparseArgs& a, bool any_size);
 hipError_t launch_gemm_lds_sp(const SparseArgs& a, hipStream_t s);

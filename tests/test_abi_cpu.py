@@ -130,6 +130,14 @@ def test_spmm_validation():
     assert S.nm_spmm_workspace_size(a) >= 2 * 4 * 64 * 4
     a = spmm_args(mode=S.NM_W_COMPRESSED, t=4, o=8192, k=4096, w_meta=P, w_meta_fmt=S.NM_META_2BIT, ldy=8192)
     assert S.nm_spmm_workspace_size(a) == 0
+    # large tokens: the K-blocked copy of the weight positions (2:4), after the lifted X
+    # (6:8 lowered to 2:4 over K' = 1.5 K)
+    a = spmm_args(mode=S.NM_W_COMPRESSED, t=4096, o=4096, k=6144, w_meta=P, w_meta_fmt=S.NM_META_2BIT, ldx=6144,
+                  ldy=4096)
+    assert S.nm_spmm_workspace_size(a) >= 4096 * 6144 // 8
+    a = spmm_args(mode=S.NM_W_SLIDE, ns=4, t=4096, o=4096, k=4096, w_meta=P, w_meta_fmt=S.NM_META_2BIT, ldx=4096,
+                  ldy=4096)
+    assert S.nm_spmm_workspace_size(a) >= 4096 * 6144 * 2 + 4096 * 6144 // 8
     a = spmm_args(mode=S.NM_W_COMPRESSED, t=4, o=8, k=16, w_meta=P, w_meta_fmt=S.NM_META_2BIT,
                   workspace=MIS, workspace_bytes=1 << 20)
     assert f(a) == S.NM_EALIGN
@@ -154,6 +162,9 @@ def test_hybrid_validation():
     assert S.nm_hybrid_gemm_workspace_size(4, 8, 8, 8, True) >= 4 * 16 * 2
     assert S.nm_hybrid_gemm_workspace_size(4, 8, 8, 14336, False) == 0
     assert S.nm_hybrid_gemm_workspace_size(0, 8, 8, 8, True) == 0
+    # large-token hybrid: permuted X, then the K-blocked copy of the 2:4 positions
+    assert S.nm_hybrid_gemm_workspace_size(2048, 3072, 1024, 14336, True) >= 2048 * 4096 * 2 + 14336 * 3072 // 8
+    assert S.nm_hybrid_gemm_workspace_size(2048, 3072, 1024, 14336, False) >= 14336 * 3072 // 8
     p = lambda *a, **kw: S.nm_hybrid_pack(*a, check=False, stream=0, **kw)  # noqa: E731
     assert S.nm_hybrid_pack_workspace_size(4096) >= 4096 * 12
     assert p(P, 20, P, P, Q, Q, S.NM_META_2BIT, Q, P, o=8, k=16, ldw=16, ldwd=16, workspace_bytes=1 << 20) == S.NM_ESHAPE

@@ -723,22 +723,31 @@ def test_spmm_w_slide_full_size_sampled():
     vp_ref, ip_ref = O.slide_lower(v, i, k, 4)
     assert (host(vp, np.uint16)[rows_w] == vp_ref).all()
     assert (host(mp, np.uint8)[rows_w] == O.pack_meta_2bit(ip_ref)).all()
-    for t in (1, 16, 128, 4096):
+    # with the workspace the size query asks for (the measured configuration: X lifted once,
+    # positions K-blocked, direct-to-LDS product at 4096 tokens), and without one
+    for t, ws in ((1, True), (16, True), (128, True), (4096, True), (4096, False)):
         x = x_all[:t]
         y = empty((t, o), np.float32, fill=float("nan"))
         a = S.make_spmm_args(S.NM_W_SLIDE, t, o, k, dev(x), vp, y, ns=4, w_meta=mp, w_meta_fmt=S.NM_META_2BIT)
+        if ws:
+            nb = S.nm_spmm_workspace_size(a)
+            wsb = empty((max(nb, 16),), np.uint8)
+            a.workspace, a.workspace_bytes = wsb.data_ptr(), nb
         S.nm_spmm(a)
         sync()
         rows = sample_rows(t, 16, seed=t)
-        check_gemm(host(y, np.float32)[rows], O.gemm(x[rows], pruned), x[rows], pruned, label=f"slide full t={t}")
+        check_gemm(host(y, np.float32)[rows], O.gemm(x[rows], pruned), x[rows], pruned,
+                   label=f"slide full t={t} ws={ws}")
 
 
 SPARSE_KERNELS = {"lds": {"NM_GEMM": "lds"}, "lds4x2": {"NM_GEMM": "lds", "NM_SP_WAVES": "4x2"},
+                  "lds_rowmeta": {"NM_GEMM": "lds", "NM_META_BLOCK": "0"},
                   "regs": {"NM_GEMM": "regs"},
                   "tile": {"NM_FEW_ROUTE": "tile"}, "stream": {"NM_FEW_ROUTE": "stream"}}
 
 
-@pytest.mark.parametrize("kernel,t,o", [("lds", 300, 264), ("lds", 130, 520), ("lds4x2", 300, 264), ("regs", 300, 264),
+@pytest.mark.parametrize("kernel,t,o", [("lds", 300, 264), ("lds", 130, 520), ("lds4x2", 300, 264),
+                                        ("lds_rowmeta", 300, 264), ("regs", 300, 264),
                                         ("regs", 130, 520), ("tile", 33, 264), ("tile", 64, 520),
                                         ("tile", 100, 264), ("tile", 128, 130), ("stream", 100, 264)])
 def test_sparse_weight_product_kernels(kernel, t, o):
@@ -803,6 +812,40 @@ def run_hybrid(x, sc, ks, dc, kd, wv, wm, wdd, o, ldwd=None, accumulate=0):
                      workspace=ws, workspace_bytes=nb)
     sync()
     return host(y, np.float32)
+
+
+@pytest.mark.parametrize("t,o,kc", [(300, 264, 1088), (257, 130, 64), (512, 520, 2112)])
+def test_blocked_positions_match_row_major(t, o, kc):
+    """The large-token 2:4 product reads the weight positions from a K-blocked copy in the
+    workspace; with NM_META_BLOCK=0 it reads them row-major.  Only the source of the same
+    bytes differs, so the two outputs agree bit for bit; both match the oracle.  Ragged
+    step counts (17, 1, 33 K-steps of 64) and row counts; plain 2:4 and the hybrid format."""
+    print(f"blocked positions t={t} o={o} kc={kc}", flush=True)
+    rng = np.random.default_rng(t + o + kc)
+    x = synth.normal_bf16(rng, (t, kc))
+    w = synth.normal_bf16(rng, (o, kc), 0.02)
+    v, mt = gpu_compress_2of4(w)
+    ws24, _ = O.sparsify(w, 2, 4)
+    with env_set(NM_GEMM="lds"):
+        y_blk = run_w(S.NM_W_COMPRESSED, x, v, mt, o, kc)
+        with env_set(NM_META_BLOCK="0"):
+            y_row = run_w(S.NM_W_COMPRESSED, x, v, mt, o, kc)
+    assert np.array_equal(y_blk.view(np.uint32), y_row.view(np.uint32)), "blocked vs row-major positions"
+    check_gemm(y_blk, O.gemm(x, ws24), x, ws24, label="2:4 blocked positions")
+    kd = 64
+    xh = synth.normal_bf16(rng, (t, kc + kd))
+    wh0 = synth.normal_bf16(rng, (o, kc + kd), 0.02)
+    sc, dc, wv, wm, wdd = hybrid_pack_gpu(wh0, kd)
+    sync()
+    sp, de, hv, hi, hwd = O.hybrid_pack(wh0, kd)
+    wh = wh0.copy()
+    wh[:, sp] = O.decompress(hv, hi, 2, 4, kc)
+    with env_set(NM_GEMM="lds"):
+        yh_blk = run_hybrid(xh, sc, kc, dc, kd, wv, wm, wdd, o)
+        with env_set(NM_META_BLOCK="0"):
+            yh_row = run_hybrid(xh, sc, kc, dc, kd, wv, wm, wdd, o)
+    assert np.array_equal(yh_blk.view(np.uint32), yh_row.view(np.uint32)), "hybrid blocked vs row-major"
+    check_gemm(yh_blk, O.hybrid_gemm(xh, sp, de, hv, hi, hwd), xh, wh, label="hybrid blocked positions")
 
 
 @pytest.mark.parametrize("o,k,kd", [(100, 256, 64), (64, 128, 0), (48, 96, 96), (300, 512, 128)])
