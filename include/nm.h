@@ -161,7 +161,9 @@ typedef enum {
  *               nm_spmm_workspace_size(args): ACT_DYNAMIC may run select and product as
  *               two passes (S(x) staged in the workspace), ACT_COMPRESSED stages the
  *               decompressed x there (required unless n:m = 2:4 with 2BIT metadata),
- *               W_SLIDE calls above 16-32 tokens stage the lifted x there, and few-token
+ *               W_SLIDE calls above 16-32 tokens stage the lifted x there, W_* calls
+ *               above 128 tokens also place a K-blocked copy of the 2-bit positions
+ *               there (o * kc / 8 bytes: fewer, larger loads per tile), and few-token
  *               calls (t <= 128) may split the reduction across workgroups, writing fp32
  *               partial sums there that a second kernel adds in a fixed order (the
  *               split-K tile route for 33-128 tokens needs this).  With less, the call
@@ -241,7 +243,8 @@ int64_t nm_hybrid_pack_workspace_size(int64_t k);
  * [0, K_s + K_d) are clamped into it.  ws_meta must be 2BIT.  Requires K_s % 4 == 0.
  * workspace: device scratch (16-byte aligned) of workspace_bytes bytes.  The gathered
  * form (column lists given) stages the column-permuted x there and requires at least
- * t * (ceil8(K_s) + ceil8(K_d)) * 2 bytes (NM_EINVAL otherwise);
+ * t * (ceil8(K_s) + ceil8(K_d)) * 2 bytes (NM_EINVAL otherwise); above 128 tokens the
+ * preferred route also places a K-blocked copy of ws_meta after it (o * K_s / 8 bytes).
  * nm_hybrid_gemm_workspace_size gives the amount for the preferred route.  Contents
  * after the call are unspecified; calls sharing it must be ordered.
  */
