@@ -17,7 +17,8 @@ Sources (cited by page title and section)
 [FLEX]  "Motivating Next-Gen Accelerators with Flexible (N:M) Activation Sparsity via
         Benchmarking Lightweight Post-Training Sparsification Approaches"
         - technical summary section 1 (configuration counts 6 and 12,870; metadata cost),
-          section 2.A (ACT score = activation magnitude), section 2.C (patterns 2:4, 4:8,
+          section 2.A (ACT score = activation magnitude; WT and Amber-Pruner scores from
+          weight magnitudes), section 2.C (patterns 2:4, 4:8,
           8:16, 16:32 along the reduction dimension).
 [SLIDE] "SlideSparse: Fast and Flexible (2N-2):2N Structured Sparsity"
         - technical summary section 2.A (N-1 overlapping windows of width 4, stride 2,
@@ -59,7 +60,8 @@ __all__ = [
     "pack_meta_2bit", "unpack_meta_2bit", "decompress", "slide_windows",
     "slide_lower", "slide_scatter_back", "lift", "column_sq_norms", "hybrid_columns",
     "hybrid_pack", "gemm", "spmm_act", "spmm_slide", "hybrid_gemm", "fp8_e4m3_to_f64",
-    "spmm_act_fp8", "lowered_k",
+    "spmm_act_fp8", "lowered_k", "SCORE_ACT_WEIGHTED", "SCORE_WEIGHT", "selection_scores",
+    "select_keep_scored", "sparsify_scored",
 ]
 
 
@@ -112,6 +114,61 @@ def sparsify(bits: np.ndarray, n: int, m: int):
     """S(X): kept values copied bit for bit, pruned values +0.0.  Returns (S bits, keep)."""
     keep = select_keep(bits, n, m)
     return np.where(keep, bits, np.uint16(0)).astype(np.uint16), keep
+
+
+SCORE_ACT_WEIGHTED = 0   # score = |x_k| * c_k   (activation weighted by weight magnitude)
+SCORE_WEIGHT = 1         # score = c_k           (weight magnitude alone)
+
+
+def selection_scores(bits: np.ndarray, col_score: np.ndarray, mode: int) -> np.ndarray:
+    """Per-element selection scores of the alternative strategies.  [FLEX] 2.A lists,
+    besides ACT, a weight-magnitude score (WT) and Amber-Pruner, which weights the
+    activation importance by the magnitude of the corresponding weights.
+
+    col_score: fp32 [K], c_k >= 0 finite: a per-input-channel weight magnitude supplied by
+    the caller (the pages do not fix the statistic or its outlier handling).
+      mode SCORE_ACT_WEIGHTED: s = fp32(|x|) * c_k, one fp32 multiply (round to nearest
+                               even, subnormals kept), as the GPU computes it;
+      mode SCORE_WEIGHT:       s = c_k for every row.
+    x must be finite.  Returns fp32 [R][K]."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    c = np.asarray(col_score, dtype=np.float32)
+    if c.shape != (bits.shape[1],):
+        raise ValueError("col_score must have one entry per column")
+    if mode == SCORE_WEIGHT:
+        return np.broadcast_to(c, bits.shape).copy()
+    if mode != SCORE_ACT_WEIGHTED:
+        raise ValueError("unknown score mode")
+    mag = ((bits & np.uint16(0x7FFF)).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    return (mag * c[None, :]).astype(np.float32)
+
+
+def select_keep_scored(bits: np.ndarray, col_score: np.ndarray, n: int, m: int, mode: int,
+                       row_chunk: int = 256) -> np.ndarray:
+    """Keep mask of the per-group top-n by selection score (selection_scores): the same
+    rank rule as select_keep with the score in place of the magnitude,
+        rank_i = #{j : s_j > s_i} + #{j < i : s_j == s_i},  keep iff rank_i < n."""
+    if not (1 <= n <= m):
+        raise ValueError("need 1 <= n <= m")
+    score = selection_scores(bits, col_score, mode)
+    r, k = score.shape
+    if k % m:
+        raise ValueError("K must be a multiple of m")
+    keep = np.empty((r, k), dtype=bool)
+    lower = np.tril(np.ones((m, m), dtype=bool), k=-1)
+    for r0 in range(0, r, row_chunk):
+        sc = score[r0:r0 + row_chunk].reshape(-1, k // m, m)
+        si = sc[..., :, None]
+        sj = sc[..., None, :]
+        rank = (sj > si).sum(-1) + ((sj == si) & lower).sum(-1)
+        keep[r0:r0 + row_chunk] = (rank < n).reshape(-1, k)
+    return keep
+
+
+def sparsify_scored(bits: np.ndarray, col_score: np.ndarray, n: int, m: int, mode: int):
+    """S(X) under a scored selection: kept values bit for bit, pruned +0.0."""
+    keep = select_keep_scored(bits, col_score, n, m, mode)
+    return np.where(keep, np.asarray(bits, dtype=np.uint16), np.uint16(0)).astype(np.uint16), keep
 
 
 def pack_mask(keep: np.ndarray) -> np.ndarray:

@@ -387,3 +387,99 @@ def test_fp8_layer_equals_scaled_bf16_layer():
     wdeq = O.fp8_e4m3_to_f64(q) * s[:, None].astype(np.float64)
     sx, _ = O.sparsify(x, 8, 16)
     assert np.allclose(y8, O.bf16_to_f64(sx) @ wdeq.T, rtol=1e-12, atol=1e-14)
+
+
+# ----------------------------------------------------------- scored selection ---
+
+def f32_round(v):
+    """Round a Python float (fp64, here always the exact product) to fp32, ties to even,
+    subnormals kept: the C conversion behind struct, independent of numpy."""
+    return struct.unpack("<f", struct.pack("<f", v))[0]
+
+
+@pytest.mark.parametrize("m", [4, 8, 16, 32])
+def test_scored_unit_scale_is_act(m):
+    """c = 1 for every column: |x| * 1 is |x| exactly, so the weighted score ranks like
+    the ACT magnitude (ties included) and the masks agree."""
+    rng = np.random.default_rng(m)
+    x = rng.choice(np.array(ALPHABET + [0x3E80, 0x4100], dtype=np.uint16), size=(40, 4 * m))
+    x[:20] = synth.student_t_bf16(rng, (20, 4 * m), 4.0, 0.5)
+    ones = np.ones(4 * m, np.float32)
+    for n in sorted({1, m // 4 or 1, m // 2, m - 1, m}):
+        assert (O.select_keep_scored(x, ones, n, m, O.SCORE_ACT_WEIGHTED) == O.select_keep(x, n, m)).all()
+    # any power-of-two scale common to all columns ranks the same way
+    assert (O.select_keep_scored(x, ones * 0.125, m // 2, m, O.SCORE_ACT_WEIGHTED)
+            == O.select_keep(x, m // 2, m)).all()
+
+
+@pytest.mark.parametrize("m,n", [(4, 2), (8, 3), (8, 4), (16, 8)])
+def test_scored_bruteforce_rounded_products(m, n):
+    """Each score is the exact product |x| * c (exact in fp64 for bf16 x fp32) rounded
+    once to fp32; the kept set is the first n-subset of largest score sum (brute force).
+    Tiny values put some products in the fp32 subnormal range; repeated column scales
+    and repeated |x| force ties, which rounding can also create."""
+    rng = np.random.default_rng(100 * m + n)
+    rows = 24
+    x = synth.student_t_bf16(rng, (rows, 2 * m), 4.0, 0.5)
+    x[3] = x[3, 0]                                        # one row of equal magnitudes
+    x[4, :m] = 0x0080                                     # bf16 min normal (2^-126)
+    x[5] = rng.choice(np.array([0x3F80, 0xBF80, 0x3F81, 0x3F7F], dtype=np.uint16), size=2 * m)
+    c = rng.uniform(0.25, 4.0, size=2 * m).astype(np.float32)
+    c[1::3] = c[0]                                        # repeated scales
+    c[m // 2] = np.float32(2.0 ** -20)                    # products below the normal range
+    c[m - 1] = np.float32(1.0 + 2.0 ** -23)               # rounding-sensitive scale
+    keep = O.select_keep_scored(x, c, n, m, O.SCORE_ACT_WEIGHTED)
+    if m >= 16:
+        rows = 8
+    for r in range(rows):
+        for g in range(2):
+            scores = [f32_round(abs(value_of(x[r, g * m + i])) * float(c[g * m + i])) for i in range(m)]
+            assert list(keep[r, g * m:(g + 1) * m]) == brute_keep(scores, n), (r, g)
+
+
+def test_scored_weight_mode_ignores_x():
+    """WT: the score is the column's weight magnitude alone, so every row keeps the same
+    positions: per group the n largest c_k, ties to the lower index (brute force)."""
+    rng = np.random.default_rng(7)
+    m, n = 16, 8
+    x = synth.student_t_bf16(rng, (9, 3 * m), 4.0, 0.5)
+    c = rng.choice(np.array([0.5, 1.0, 1.5, 3.0], np.float32), size=3 * m)
+    keep = O.select_keep_scored(x, c, n, m, O.SCORE_WEIGHT)
+    for g in range(3):
+        ref = brute_keep([float(v) for v in c[g * m:(g + 1) * m]], n)
+        for r in range(x.shape[0]):
+            assert list(keep[r, g * m:(g + 1) * m]) == ref
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_scored_invariants(mode):
+    """Exactly n kept per group; every kept score beats every pruned one under (score
+    descending, index ascending); S(X) copies kept bits and zeroes the rest."""
+    rng = np.random.default_rng(11 + mode)
+    m, n = 16, 8
+    x = synth.student_t_bf16(rng, (50, 8 * m), 4.0, 0.5)
+    c = (np.abs(rng.standard_normal(8 * m)) + 0.01).astype(np.float32)
+    y, keep = O.sparsify_scored(x, c, n, m, mode)
+    s = O.selection_scores(x, c, mode)
+    assert (keep.reshape(50, 8, m).sum(-1) == n).all()
+    for r in range(50):
+        for g in range(8):
+            sl = slice(g * m, (g + 1) * m)
+            kept = [i for i in range(m) if keep[r, sl][i]]
+            pruned = [i for i in range(m) if not keep[r, sl][i]]
+            for i in kept:
+                for j in pruned:
+                    assert (s[r, sl][i] > s[r, sl][j]) or (s[r, sl][i] == s[r, sl][j] and i < j)
+    assert (y[keep] == x[keep]).all() and (y[~keep] == 0).all()
+
+
+def test_scored_rounding_makes_ties():
+    """The score is one rounded fp32 product: 1 * (1 + 2^-7 + 2^-23) and
+    (1 + 2^-7) * (1 + 2^-23) differ by 2^-30 exactly but are the same fp32 number, so
+    with n = 1 the lower index wins (an exact-arithmetic score would keep index 1)."""
+    x = np.array([[0x3F80, 0x3F81, 0x3F00, 0x3F00]], np.uint16)          # 1, 1 + 2^-7, .5, .5
+    c = np.array([1 + 2.0 ** -7 + 2.0 ** -23, 1 + 2.0 ** -23, 1.0, 1.0], np.float32)
+    assert float(c[0]) == 1 + 2.0 ** -7 + 2.0 ** -23 and float(c[1]) == 1 + 2.0 ** -23
+    exact = [abs(value_of(x[0, i])) * float(c[i]) for i in range(4)]
+    assert exact[1] > exact[0] and f32_round(exact[1]) == f32_round(exact[0])
+    assert list(O.select_keep_scored(x, c, 1, 4, O.SCORE_ACT_WEIGHTED)[0]) == [True, False, False, False]
