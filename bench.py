@@ -263,6 +263,12 @@ def measure_rows(torch, S, synth, np):
     fn = lambda: S.nm_compress(x2, 8, 16, vv, ix, S.NM_META_U8, mask=mk, check=False)
     add("cfg2", t, "select alone: values + u8 idx + mask", gpu_time_us(torch, fn, False), 0.0, 0.0,
         t * K2 * 2 + t * K2 // 2 * 3 + t * K2 // 8, bound="hbm")
+    # scored selection: activations weighted by the fp32 L2 norm of each weight column
+    cs = w2.view(torch.bfloat16).float().pow(2).sum(0).sqrt().contiguous()
+    fn = lambda: S.nm_sparsify_scored(x2, 8, 16, cs, S.NM_SCORE_ACT_WEIGHTED, sxb, mk, check=False)
+    add("cfg2", t, "select alone, |x| * weight-column norm: S(X) + mask", gpu_time_us(torch, fn, False), 0.0, 0.0,
+        t * K2 * 2 + t * K2 * 2 + t * K2 // 8 + K2 * 4, bound="hbm")
+    del cs
     del sxb, mk, vv, ix
     for t in (1, 16, 128, 2048, 8192):
         y = f32(t, O2)

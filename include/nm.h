@@ -83,6 +83,30 @@ int nm_version(void);
 nm_status nm_sparsify(const void* x, int64_t rows, int64_t k, int64_t ldx, int n, int m,
                       void* y, int64_t ldy, uint32_t* mask, void* stream);
 
+typedef enum {
+  NM_SCORE_ACT_WEIGHTED = 0,   /* score = |x[k]| * col_score[k]  (activation weighted by    */
+                               /*         the magnitude of the weights it multiplies)       */
+  NM_SCORE_WEIGHT = 1          /* score = col_score[k]           (weight magnitude alone)   */
+} nm_score;
+
+/*
+ * nm_sparsify_scored -- S(X) under an alternative selection score: per group of m along
+ * K keep the n largest scores, ties to the lower index.  [FLEX] 2.A lists, besides ACT,
+ * a weight-magnitude score (WT) and Amber-Pruner, which weights activation importance by
+ * the magnitude of the corresponding weights; the pages give neither statistic, so the
+ * per-column magnitude is the caller's (e.g. the L2 norm of each column of W, after any
+ * outlier clipping).  The score is one fp32 multiply, rounded to nearest even with
+ * subnormals kept: score = fp32(|x|) * col_score[k].
+ *   x          bf16 [rows][ldx], finite
+ *   col_score  fp32 [k], device, 16-byte aligned, every entry finite and >= 0
+ *   mode       an nm_score value (NM_EINVAL otherwise)
+ *   y, mask    as for nm_sparsify (at least one non-NULL)
+ * m in {4, 8, 16, 32} (other widths: NM_EUNSUPPORTED).  Results are bit-exact.
+ */
+nm_status nm_sparsify_scored(const void* x, int64_t rows, int64_t k, int64_t ldx, int n, int m,
+                             const float* col_score, nm_score mode, void* y, int64_t ldy,
+                             uint32_t* mask, void* stream);
+
 /*
  * nm_compress -- select and compact in one pass, straight from the dense input.
  * [FLEX] 1 (values plus index metadata), [SLIDE] 2.C (load-time compression).

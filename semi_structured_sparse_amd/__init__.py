@@ -17,6 +17,7 @@ __all__ = [
     "NMError", "lib", "NM_OK", "NM_EINVAL", "NM_ESHAPE", "NM_EALIGN", "NM_EUNSUPPORTED", "NM_EHIP",
     "NM_META_U8", "NM_META_2BIT", "NM_W_BF16", "NM_W_FP8E4M3", "NM_ACT_DYNAMIC", "NM_ACT_COMPRESSED",
     "NM_W_COMPRESSED", "NM_W_SLIDE", "NM_ACT_MASKED", "nm_spmm_args", "nm_status_str", "nm_version", "nm_sparsify",
+    "nm_sparsify_scored", "NM_SCORE_ACT_WEIGHTED", "NM_SCORE_WEIGHT",
     "nm_probe_sink_bytes", "nm_probe_read", "nm_probe_mfma_flops", "nm_probe_mfma",
     "nm_compress", "nm_decompress", "nm_lower_slide", "nm_slide_lift", "nm_spmm",
     "nm_spmm_workspace_size", "nm_hybrid_pack", "nm_hybrid_pack_workspace_size", "nm_hybrid_gemm",
@@ -28,6 +29,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnmsparse
 NM_OK, NM_EINVAL, NM_ESHAPE, NM_EALIGN, NM_EUNSUPPORTED, NM_EHIP = range(6)
 NM_META_U8, NM_META_2BIT = 0, 1
 NM_W_BF16, NM_W_FP8E4M3 = 0, 1
+NM_SCORE_ACT_WEIGHTED, NM_SCORE_WEIGHT = 0, 1
 NM_ACT_DYNAMIC, NM_ACT_COMPRESSED, NM_W_COMPRESSED, NM_W_SLIDE, NM_ACT_MASKED = range(5)
 
 _i64 = ctypes.c_int64
@@ -70,6 +72,8 @@ def lib() -> ctypes.CDLL:
     L.nm_version.argtypes = []
     L.nm_sparsify.restype = _int
     L.nm_sparsify.argtypes = [_vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _vp]
+    L.nm_sparsify_scored.restype = _int
+    L.nm_sparsify_scored.argtypes = [_vp, _i64, _i64, _i64, _int, _int, _vp, _int, _vp, _i64, _vp, _vp]
     L.nm_compress.restype = _int
     L.nm_compress.argtypes = [_vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _int, _vp, _vp]
     L.nm_decompress.restype = _int
@@ -158,6 +162,17 @@ def nm_sparsify(x, n, m, y=None, mask=None, stream=None, *, rows=None, k=None, l
                            _ld(y) if ldy is None else ldy, _ptr(mask), _stream(stream))
     if check:
         _check(st, "nm_sparsify")
+    return st
+
+
+def nm_sparsify_scored(x, n, m, col_score, mode=NM_SCORE_ACT_WEIGHTED, y=None, mask=None, stream=None, *,
+                       rows=None, k=None, ldx=None, ldy=None, check=True):
+    rows = x.shape[0] if rows is None else rows
+    k = x.shape[1] if k is None else k
+    st = lib().nm_sparsify_scored(_ptr(x), rows, k, _ld(x) if ldx is None else ldx, n, m, _ptr(col_score), mode,
+                                  _ptr(y), _ld(y) if ldy is None else ldy, _ptr(mask), _stream(stream))
+    if check:
+        _check(st, "nm_sparsify_scored")
     return st
 
 

@@ -316,6 +316,26 @@ nm_status nm_sparsify(const void* x, int64_t rows, int64_t k, int64_t ldx, int n
                                        nullptr, nullptr, 0, as_stream(stream)));
 }
 
+nm_status nm_sparsify_scored(const void* x, int64_t rows, int64_t k, int64_t ldx, int n, int m,
+                             const float* col_score, nm_score mode, void* y, int64_t ldy, uint32_t* mask,
+                             void* stream) {
+  if (m != 4 && m != 8 && m != 16 && m != 32)
+    return (m >= 1 && n >= 1 && n <= m) ? NM_EUNSUPPORTED : NM_EINVAL;
+  nm_status st = check_pattern(k, n, m);
+  if (st) return st;
+  if (rows < 0) return NM_ESHAPE;
+  if (mode != NM_SCORE_ACT_WEIGHTED && mode != NM_SCORE_WEIGHT) return NM_EINVAL;
+  if (y == nullptr && mask == nullptr) return NM_EINVAL;
+  if (col_score == nullptr && k > 0) return NM_EINVAL;
+  if ((st = check_bf16(x, rows, k, ldx, true, group_ld_mult(m)))) return st;
+  if ((st = check_bf16(y, rows, k, ldy, false, group_ld_mult(m)))) return st;
+  if ((mask != nullptr && !aligned16(mask)) || (col_score != nullptr && !aligned16(col_score))) return NM_EALIGN;
+  if (rows == 0 || k == 0) return NM_OK;
+  return hip_status(nml::launch_select_scored(m, (const uint16_t*)x, rows, k, ldx, n, col_score,
+                                              mode == NM_SCORE_ACT_WEIGHTED ? 1 : 0, (uint16_t*)y, ldy, mask,
+                                              as_stream(stream)));
+}
+
 nm_status nm_compress(const void* x, int64_t rows, int64_t k, int64_t ldx, int n, int m, void* values,
                       void* meta, nm_meta fmt, uint32_t* mask, void* stream) {
   nm_status st = check_select_pattern(k, n, m, mask != nullptr);

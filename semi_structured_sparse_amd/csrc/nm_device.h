@@ -43,8 +43,8 @@ __device__ __forceinline__ void sort_desc(uint32_t (&c)[M]) {
 // Descending sort by Batcher's odd-even merge network (5 / 19 / 63 / 191 comparators for
 // M = 4 / 8 / 16 / 32, against 6 / 24 / 80 / 240 for the bitonic network above).  When
 // only one output is used the compiler drops the comparators it does not depend on.
-template <int M>
-__device__ __forceinline__ void sort_desc_oem(uint32_t (&c)[M]) {
+template <int M, typename T>
+__device__ __forceinline__ void sort_desc_oem(T (&c)[M]) {
 #pragma unroll
   for (int p = 1; p < M; p <<= 1) {
 #pragma unroll
@@ -55,7 +55,7 @@ __device__ __forceinline__ void sort_desc_oem(uint32_t (&c)[M]) {
         for (int i = 0; i < k; ++i) {
           const int a = i + j, b = i + j + k;
           if (b < M && a / (2 * p) == b / (2 * p)) {
-            const uint32_t x = c[a], y = c[b];
+            const T x = c[a], y = c[b];
             c[a] = x > y ? x : y;
             c[b] = x > y ? y : x;
           }
@@ -128,6 +128,33 @@ __device__ __forceinline__ uint32_t topn_bits(const uint32_t (&d)[M / 2], int n)
   uint32_t bits = 0;
 #pragma unroll
   for (int i = 0; i < M; ++i) bits |= (c[i] >= tau ? 1u : 0u) << i;
+  return bits;
+}
+
+// Scored top-n (the weight-magnitude and activation-times-weight-magnitude scores):
+// score_i = fp32(|x_i|) * c_i (one multiply, round to nearest even) or c_i alone, with
+// c_i >= 0 finite and x finite, so scores are non-negative floats whose bit patterns
+// order like their values.  A 64-bit key (score bits << 32) | (0xFFFFFFFF - i) is unique
+// per element and orders ties to the lower index; keep <=> key >= the n-th largest key.
+template <int M>
+__device__ __forceinline__ uint32_t topn_bits_scored(const uint32_t (&d)[M / 2], const float (&c)[M], int n,
+                                                     bool use_x) {
+  uint64_t key[M], s[M];
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    const uint32_t h = (i & 1) ? (d[i >> 1] >> 16) : (d[i >> 1] & 0xFFFFu);
+    const float mag = __uint_as_float((h & 0x7FFFu) << 16);
+    const float sc = use_x ? mag * c[i] : c[i];
+    key[i] = ((uint64_t)__float_as_uint(sc) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
+    s[i] = key[i];
+  }
+  sort_desc_oem<M>(s);
+  uint64_t tau = s[0];
+#pragma unroll
+  for (int j = 1; j < M; ++j) tau = (j == n - 1) ? s[j] : tau;
+  uint32_t bits = 0;
+#pragma unroll
+  for (int i = 0; i < M; ++i) bits |= (key[i] >= tau ? 1u : 0u) << i;
   return bits;
 }
 

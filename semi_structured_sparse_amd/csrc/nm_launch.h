@@ -5,6 +5,11 @@
 
 namespace nml {
 
+// scored top-n (m in {4, 8, 16, 32}): score = fp32(|x|) * col_score[k] (use_x) or
+// col_score[k] alone; outputs S(X) and/or the bitmask
+hipError_t launch_select_scored(int m, const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, int n,
+                                const float* col_score, int use_x, uint16_t* y, int64_t ldy, uint32_t* mask,
+                                hipStream_t s);
 hipError_t launch_select(int m, const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, int n,
                          uint16_t* y, int64_t ldy, uint32_t* mask, uint16_t* values,
                          uint8_t* meta, int meta_2bit, hipStream_t s);

@@ -198,9 +198,83 @@ __global__ __launch_bounds__(256) void k_decompress(
   store_group<M>(y + row * ldy + g * M, out);
 }
 
+// Scored selection: the top-n of each group by score (topn_bits_scored) instead of by
+// magnitude; outputs S(X) and/or the bitmask.  Lane l owns group g0 + l as in k_select
+// and reads the group's M column scores with 16-byte loads (col_score is shared by all
+// rows, so it stays in cache).
+template <int M>
+__global__ __launch_bounds__(64 * kWavesPerBlock) void k_select_scored(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t k, int64_t ldx, int n,
+    const float* __restrict__ col_score, int use_x, uint16_t* __restrict__ y, int64_t ldy,
+    uint32_t* __restrict__ mask) {
+  static_assert(M >= 4 && 32 % M == 0, "power-of-two widths 4..32");
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int64_t G = k / M;
+  const int64_t strips_per_row = (G + 63) >> 6;
+  const int64_t strip = (int64_t)blockIdx.x * kWavesPerBlock + wave;
+  const bool strip_ok = strip < rows * strips_per_row;
+  const int64_t row = strip_ok ? strip / strips_per_row : 0;
+  const int64_t g0 = strip_ok ? (strip - row * strips_per_row) * 64 : 0;
+  const int64_t g = g0 + lane;
+  const bool valid = strip_ok && g < G;
+
+  uint32_t d[M / 2];
+  float c[M];
+  if (valid) {
+    load_group<M>(x + row * ldx + g * M, d);
+#pragma unroll
+    for (int q = 0; q < M / 4; ++q) {
+      const float4 v = reinterpret_cast<const float4*>(col_score + g * M)[q];
+      c[4 * q] = v.x; c[4 * q + 1] = v.y; c[4 * q + 2] = v.z; c[4 * q + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < M / 2; ++q) d[q] = 0;
+#pragma unroll
+    for (int i = 0; i < M; ++i) c[i] = 0.f;
+  }
+  const uint32_t keep = valid ? topn_bits_scored<M>(d, c, n, use_x != 0) : 0u;
+
+  if (y != nullptr && valid) {
+    uint32_t o[M / 2];
+#pragma unroll
+    for (int q = 0; q < M / 2; ++q) o[q] = mask_pair(d[q], keep >> (2 * q));
+    store_group<M>(y + row * ldy + g * M, o);
+  }
+  if (mask != nullptr) {
+    uint32_t w = keep << ((uint32_t)(g * M) & 31u);
+    if constexpr (M < 32) {
+#pragma unroll
+      for (int off = 1; off < 32 / M; off <<= 1) w |= __shfl_xor(w, off, 64);
+    }
+    const int64_t words = (k + 31) >> 5;
+    if (valid && (lane % (32 / M)) == 0) mask[row * words + ((g * M) >> 5)] = w;
+  }
+}
+
 }  // namespace
 
 namespace nml {
+
+hipError_t launch_select_scored(int m, const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, int n,
+                                const float* col_score, int use_x, uint16_t* y, int64_t ldy, uint32_t* mask,
+                                hipStream_t s) {
+  const int64_t G = k / m;
+  const int64_t strips = rows * ((G + 63) / 64);
+  const int64_t blocks = (strips + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  dim3 grid((unsigned)blocks), block(64 * kWavesPerBlock);
+  switch (m) {
+    case 4: k_select_scored<4><<<grid, block, 0, s>>>(x, rows, k, ldx, n, col_score, use_x, y, ldy, mask); break;
+    case 8: k_select_scored<8><<<grid, block, 0, s>>>(x, rows, k, ldx, n, col_score, use_x, y, ldy, mask); break;
+    case 16: k_select_scored<16><<<grid, block, 0, s>>>(x, rows, k, ldx, n, col_score, use_x, y, ldy, mask); break;
+    case 32: k_select_scored<32><<<grid, block, 0, s>>>(x, rows, k, ldx, n, col_score, use_x, y, ldy, mask); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_select(int m, const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, int n,
                          uint16_t* y, int64_t ldy, uint32_t* mask, uint16_t* values,

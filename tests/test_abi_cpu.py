@@ -143,6 +143,22 @@ def test_spmm_validation():
     assert f(a) == S.NM_EALIGN
 
 
+def test_sparsify_scored_validation():
+    f = lambda *a, **kw: S.nm_sparsify_scored(*a, check=False, stream=0, **kw)  # noqa: E731
+    x = dict(rows=4, k=16, ldx=16, ldy=16)
+    assert f(P, 3, 6, Q, 0, P, None, rows=4, k=12, ldx=16, ldy=16) == S.NM_EUNSUPPORTED    # width 6
+    assert f(P, 0, 4, Q, 0, P, None, **x) == S.NM_EINVAL                                  # n < 1
+    assert f(P, 5, 4, Q, 0, P, None, **x) == S.NM_EINVAL                                  # n > m
+    assert f(P, 2, 4, Q, 2, P, None, **x) == S.NM_EINVAL                                  # mode
+    assert f(P, 2, 4, Q, 0, None, None, **x) == S.NM_EINVAL                               # no output
+    assert f(P, 2, 4, None, 0, P, None, **x) == S.NM_EINVAL                               # no scores
+    assert f(P, 2, 4, MIS, 0, P, None, **x) == S.NM_EALIGN                                # scores aligned
+    assert f(P, 2, 4, Q, 0, None, MIS, **x) == S.NM_EALIGN                                # mask aligned
+    assert f(P, 2, 8, Q, 0, P, None, rows=4, k=12, ldx=16, ldy=16) == S.NM_ESHAPE          # k % m
+    assert f(P, 2, 4, Q, 0, P, None, rows=4, k=16, ldx=8, ldy=16) == S.NM_ESHAPE           # ldx < k
+    assert f(P, 2, 4, Q, 0, P, None, rows=0, k=16, ldx=16, ldy=16) == S.NM_OK             # empty: no-op
+
+
 def test_hybrid_validation():
     g = lambda *a, **kw: S.nm_hybrid_gemm(*a, check=False, stream=0, **kw)  # noqa: E731
     assert g(P, P, 6, P, 2, Q, Q, S.NM_META_2BIT, Q, 8, P, t=4, ldx=16, ldwd=8, ldy=8) == S.NM_ESHAPE  # k_s % 4

@@ -147,6 +147,67 @@ def test_select_full_size_sampled(n, m):
     assert (pop.reshape(t, -1, m).sum(-1) == n).all()
 
 
+def scored_columns(rng, k, tiny=False):
+    """Per-column fp32 weight magnitudes: L2 norms of a random W's columns, with repeated
+    values, zeros and (tiny) subnormal-range products mixed in."""
+    w = synth.normal_bf16(rng, (64, k), 0.02)
+    c = np.sqrt((O.bf16_to_f64(w) ** 2).sum(0)).astype(np.float32)
+    c[1::5] = c[0]
+    c[3::17] = 0.0
+    if tiny:
+        c[::3] = np.float32(2.0 ** -110)
+    return c
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("n,m", [(2, 4), (1, 4), (4, 8), (3, 8), (8, 16), (5, 16), (16, 32), (1, 32)])
+@pytest.mark.parametrize("rows,groups,pad", [(37, 131, 0), (5, 3, 8), (70, 64, 16)])
+def test_select_scored_bitexact(mode, n, m, rows, groups, pad):
+    """Scored selection (weight magnitude alone, or activation weighted by it): S(X) and
+    the bitmask bit for bit against the oracle, with ties in x and in the column scores,
+    zero scores, products in the fp32 subnormal range and padded rows."""
+    print(f"select scored mode={mode} n={n} m={m} rows={rows} groups={groups} pad={pad}", flush=True)
+    rng = np.random.default_rng(3000 * m + 10 * n + rows + mode)
+    k = groups * m
+    x = synth.student_t_bf16(rng, (rows, k), 4.0, 0.5)
+    x[: min(4, rows)] = special_rows(k, rng)[: min(4, rows)]
+    x[~np.isfinite(O.bf16_to_f64(x))] = 0x3F80                 # scores need finite x (no inf, NaN)
+    if rows > 5:
+        x[5] = 0x0100                                           # tiny |x|: subnormal products
+    c = scored_columns(rng, k, tiny=(rows == 37))
+    ld = k + pad
+    y = empty((rows, ld), np.uint16, fill=-1)
+    words = (k + 31) // 32
+    mask = empty((rows, words), np.uint32, fill=-1)
+    S.nm_sparsify_scored(dev(x, ld), n, m, dev(c), mode, y, mask, k=k)
+    sync()
+    s_ref, keep = O.sparsify_scored(x, c, n, m, mode)
+    assert (host(y, np.uint16)[:, :k] == s_ref).all()
+    assert (host(y, np.uint16)[:, k:] == 0xFFFF).all()
+    assert (host(mask, np.uint32) == O.pack_mask(keep)).all()
+
+
+def test_select_scored_full_size_sampled():
+    """Down-projection activations at full size (8192 x 14336), column scores = fp32 L2
+    norms of the layer's W columns (activation weighted by weight magnitude); oracle on
+    sampled rows, exactly n kept per group on every row."""
+    print("select scored full", flush=True)
+    d = synth.mlp_down_8of16(t_max=8192)
+    x, w = d["x"], d["w"]
+    t, k = x.shape
+    c = np.sqrt((O.bf16_to_f64(w) ** 2).sum(0)).astype(np.float32)
+    y = empty((t, k), np.uint16)
+    mask = empty((t, (k + 31) // 32), np.uint32)
+    S.nm_sparsify_scored(dev(x), 8, 16, dev(c), S.NM_SCORE_ACT_WEIGHTED, y, mask)
+    sync()
+    rows = sample_rows(t, 40)
+    s_ref, keep = O.sparsify_scored(x[rows], c, 8, 16, O.SCORE_ACT_WEIGHTED)
+    assert (host(y, np.uint16)[rows] == s_ref).all()
+    assert (host(mask, np.uint32)[rows] == O.pack_mask(keep)).all()
+    pop = np.unpackbits(host(mask, np.uint32).view(np.uint8), axis=1, bitorder="little")
+    assert (pop.reshape(t, -1, 16).sum(-1) == 8).all()
+
+
 def test_select_deterministic():
     rng = np.random.default_rng(5)
     x = synth.student_t_bf16(rng, (256, 4096), 4.0, 1.0)
