@@ -134,27 +134,44 @@ __device__ __forceinline__ uint32_t topn_bits(const uint32_t (&d)[M / 2], int n)
 // Scored top-n (the weight-magnitude and activation-times-weight-magnitude scores):
 // score_i = fp32(|x_i|) * c_i (one multiply, round to nearest even) or c_i alone, with
 // c_i >= 0 finite and x finite, so scores are non-negative floats whose bit patterns
-// order like their values.  A 64-bit key (score bits << 32) | (0xFFFFFFFF - i) is unique
-// per element and orders ties to the lower index; keep <=> key >= the n-th largest key.
-template <int M>
+// order like their values.  The odd-even merge network on the 32-bit patterns gives the
+// n-th largest score tau; then every score above tau is kept, and of the scores equal to
+// tau the lowest-index ones, as many as n minus the count above tau (ties to the lower
+// index).  NT > 0: n = NT known at compile time (only the comparators that tau depends
+// on survive); NT = 0: n at run time.
+template <int M, int NT>
 __device__ __forceinline__ uint32_t topn_bits_scored(const uint32_t (&d)[M / 2], const float (&c)[M], int n,
                                                      bool use_x) {
-  uint64_t key[M], s[M];
+  uint32_t sc[M], s[M];
 #pragma unroll
   for (int i = 0; i < M; ++i) {
     const uint32_t h = (i & 1) ? (d[i >> 1] >> 16) : (d[i >> 1] & 0xFFFFu);
     const float mag = __uint_as_float((h & 0x7FFFu) << 16);
-    const float sc = use_x ? mag * c[i] : c[i];
-    key[i] = ((uint64_t)__float_as_uint(sc) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)i);
-    s[i] = key[i];
+    sc[i] = __float_as_uint(use_x ? mag * c[i] : c[i]);
+    s[i] = sc[i];
   }
   sort_desc_oem<M>(s);
-  uint64_t tau = s[0];
+  uint32_t tau;
+  if constexpr (NT > 0) {
+    tau = s[NT - 1];
+    n = NT;
+  } else {
+    tau = s[0];
 #pragma unroll
-  for (int j = 1; j < M; ++j) tau = (j == n - 1) ? s[j] : tau;
+    for (int j = 1; j < M; ++j) tau = (j == n - 1) ? s[j] : tau;
+  }
+  int above = 0;
+#pragma unroll
+  for (int i = 0; i < M; ++i) above += sc[i] > tau ? 1 : 0;
+  int ties_left = n - above;   // >= 1: tau is the n-th largest
   uint32_t bits = 0;
 #pragma unroll
-  for (int i = 0; i < M; ++i) bits |= (key[i] >= tau ? 1u : 0u) << i;
+  for (int i = 0; i < M; ++i) {
+    const bool eq = sc[i] == tau;
+    const bool keep = sc[i] > tau || (eq && ties_left > 0);
+    ties_left -= eq ? 1 : 0;
+    bits |= (keep ? 1u : 0u) << i;
+  }
   return bits;
 }
 

@@ -202,7 +202,7 @@ __global__ __launch_bounds__(256) void k_decompress(
 // magnitude; outputs S(X) and/or the bitmask.  Lane l owns group g0 + l as in k_select
 // and reads the group's M column scores with 16-byte loads (col_score is shared by all
 // rows, so it stays in cache).
-template <int M>
+template <int M, int NT>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void k_select_scored(
     const uint16_t* __restrict__ x, int64_t rows, int64_t k, int64_t ldx, int n,
     const float* __restrict__ col_score, int use_x, uint16_t* __restrict__ y, int64_t ldy,
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_select_scored(
 #pragma unroll
     for (int i = 0; i < M; ++i) c[i] = 0.f;
   }
-  const uint32_t keep = valid ? topn_bits_scored<M>(d, c, n, use_x != 0) : 0u;
+  const uint32_t keep = valid ? topn_bits_scored<M, NT>(d, c, n, use_x != 0) : 0u;
 
   if (y != nullptr && valid) {
     uint32_t o[M / 2];
@@ -266,13 +266,19 @@ hipError_t launch_select_scored(int m, const uint16_t* x, int64_t rows, int64_t 
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)blocks), block(64 * kWavesPerBlock);
+#define NM_SCORED(MM)                                                                              \
+  if (n == (MM) / 2)                                                                               \
+    k_select_scored<MM, (MM) / 2><<<grid, block, 0, s>>>(x, rows, k, ldx, n, col_score, use_x, y, ldy, mask); \
+  else                                                                                             \
+    k_select_scored<MM, 0><<<grid, block, 0, s>>>(x, rows, k, ldx, n, col_score, use_x, y, ldy, mask);
   switch (m) {
-    case 4: k_select_scored<4><<<grid, block, 0, s>>>(x, rows, k, ldx, n, col_score, use_x, y, ldy, mask); break;
-    case 8: k_select_scored<8><<<grid, block, 0, s>>>(x, rows, k, ldx, n, col_score, use_x, y, ldy, mask); break;
-    case 16: k_select_scored<16><<<grid, block, 0, s>>>(x, rows, k, ldx, n, col_score, use_x, y, ldy, mask); break;
-    case 32: k_select_scored<32><<<grid, block, 0, s>>>(x, rows, k, ldx, n, col_score, use_x, y, ldy, mask); break;
+    case 4: NM_SCORED(4) break;
+    case 8: NM_SCORED(8) break;
+    case 16: NM_SCORED(16) break;
+    case 32: NM_SCORED(32) break;
     default: return hipErrorInvalidValue;
   }
+#undef NM_SCORED
   return hipGetLastError();
 }
 
