@@ -365,6 +365,40 @@ def measure_rows(torch, S, synth, np):
                     tot_b += wb + t * k_ * 2 + t * o_ * 4
                     keep.clear()
                 add("cfg5", t, f"layer {n}:{m} act, {kind} W", tot_us, tot_f, tot_f, tot_b)
+    # the same layer with the linears that share an input concatenated along the output
+    # dimension (q|k|v: 6144 x 4096, gate|up: 28672 x 4096): four calls instead of seven,
+    # one selection per input stream, identical outputs
+    groups = (("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "up")), ("down", ("down",)))
+    wcat = {g: torch.cat([wdev[nm] for nm in parts], 0).contiguous() for g, parts in groups}
+    w8cat = {g: (torch.cat([w8dev[nm][0] for nm in parts], 0).contiguous(),
+                 torch.cat([w8dev[nm][1] for nm in parts], 0).contiguous()) for g, parts in groups}
+    del wdev, w8dev
+    for t in (64, 8192):
+        for n, m in ((16, 32), (8, 16)):
+            for kind in ("bf16", "fp8"):
+                tot_us = tot_f = tot_b = 0.0
+                for g, parts in groups:
+                    o_ = sum(synth.TRANSFORMER_SHAPES[nm][0] for nm in parts)
+                    _, k_, st = synth.TRANSFORMER_SHAPES[parts[0]]
+                    y = f32(t, o_)
+                    xin = xdev[st][:t]
+                    if kind == "bf16":
+                        mk5 = lambda w_: S.make_spmm_args(S.NM_ACT_DYNAMIC, t, o_, k_, xin, w_, y, n=n, m=m)
+                        wts = (wcat[g],)
+                        wb = o_ * k_ * 2
+                    else:
+                        mk5 = lambda q_, s_: S.make_spmm_args(S.NM_ACT_DYNAMIC, t, o_, k_, xin, q_, y, n=n, m=m,
+                                                              w_dtype=S.NM_W_FP8E4M3, w_scale=s_)
+                        wts = w8cat[g]
+                        wb = o_ * k_ + o_ * 4
+                    if t <= 128:
+                        tot_us += gpu_time_rot_us(torch, rot_spmm(mk5, wts, wb, keep))
+                    else:
+                        tot_us += gpu_time_us(torch, spmm(mk5(*wts), keep), False, iters=5, warm=2)
+                    tot_f += 2.0 * t * o_ * k_
+                    tot_b += wb + t * k_ * 2 + t * o_ * 4
+                    keep.clear()
+                add("cfg5", t, f"layer {n}:{m} act, {kind} W, fused qkv + gate|up", tot_us, tot_f, tot_f, tot_b)
     return rows
 
 

@@ -638,6 +638,58 @@ def test_fp8_decode_all_codes():
     assert (y[0].astype(np.float64) == O.fp8_e4m3_to_f64(codes)).all()
 
 
+LAYER_GROUPS = {"q": ("q",), "k": ("k",), "v": ("v",), "o": ("o",), "gate": ("gate",), "up": ("up",),
+                "down": ("down",), "qkv": ("q", "k", "v"), "gate_up": ("gate", "up")}
+
+
+@pytest.fixture(scope="module")
+def layer8b():
+    return synth.transformer_layer(t_max=8192, with_fp8=True)
+
+
+@pytest.mark.parametrize("t", [64, 8192])
+@pytest.mark.parametrize("group", list(LAYER_GROUPS))
+def test_layer_full_size_sampled(layer8b, group, t):
+    """The 8B-shaped layer's linears at full size, each alone and with the linears that
+    share an input concatenated along the output dimension (q|k|v 6144 x 4096, gate|up
+    28672 x 4096), as the layer measurement runs them: 16:32 and 8:16 activations, bf16
+    and fp8 weights, workspace from the size query; oracle on sampled output rows."""
+    import torch
+
+    parts = LAYER_GROUPS[group]
+    print(f"layer {group} t={t}", flush=True)
+    st = synth.TRANSFORMER_SHAPES[parts[0]][2]
+    x = layer8b["x"][st][:t]
+    w = np.concatenate([layer8b["w"][p] for p in parts], 0)
+    w8 = np.concatenate([layer8b["w8"][p] for p in parts], 0)
+    s8 = np.concatenate([layer8b["s8"][p] for p in parts], 0)
+    o, k = w.shape
+    rows = sample_rows(t, 6, seed=t + o)
+    xd = dev(x)
+    wdeq = O.fp8_e4m3_to_f64(w8) * s8[:, None].astype(np.float64)
+    for (n, m) in ((16, 32), (8, 16)):
+        sx, keep = O.sparsify(x[rows], n, m)
+        for kind in ("bf16", "fp8"):
+            y = torch.full((t, o), float("nan"), dtype=torch.float32, device="cuda")
+            if kind == "bf16":
+                a = S.make_spmm_args(S.NM_ACT_DYNAMIC, t, o, k, xd, dev(w), y, n=n, m=m)
+            else:
+                a = S.make_spmm_args(S.NM_ACT_DYNAMIC, t, o, k, xd, dev(w8), y, n=n, m=m,
+                                     w_dtype=S.NM_W_FP8E4M3, w_scale=dev(s8))
+            nb = S.nm_spmm_workspace_size(a)
+            ws = empty((max(nb, 16),), np.uint8)
+            a.workspace, a.workspace_bytes = ws.data_ptr(), nb
+            S.nm_spmm(a)
+            sync()
+            yr = y[torch.from_numpy(rows).cuda()].cpu().numpy()
+            if kind == "bf16":
+                check_gemm(yr, O.gemm(sx, w), sx, w, label=f"layer {group} t={t} {n}:{m} bf16")
+            else:
+                check_gemm(yr, O.spmm_act_fp8(x[rows], w8, s8, n, m), sx, wdeq,
+                           label=f"layer {group} t={t} {n}:{m} fp8")
+            del y, ws, a
+
+
 @pytest.mark.parametrize("route", ["fused", "mask", "sx"])
 def test_spmm_act_full_size_sampled(route):
     """8:16 down-projection at 2048 and 8192 tokens; oracle on sampled output rows."""
