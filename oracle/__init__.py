@@ -61,7 +61,8 @@ __all__ = [
     "slide_lower", "slide_scatter_back", "lift", "column_sq_norms", "hybrid_columns",
     "hybrid_pack", "gemm", "spmm_act", "spmm_slide", "hybrid_gemm", "fp8_e4m3_to_f64",
     "spmm_act_fp8", "lowered_k", "SCORE_ACT_WEIGHTED", "SCORE_WEIGHT", "selection_scores",
-    "select_keep_scored", "sparsify_scored",
+    "select_keep_scored", "sparsify_scored", "spense_glu_scores", "spense_order", "spense_order_tail",
+    "spense_pack", "outsplit_gemm",
 ]
 
 
@@ -350,6 +351,79 @@ def hybrid_pack(w_bits: np.ndarray, k_dense: int):
         v = np.zeros((w_bits.shape[0], 0), np.uint16)
         i = np.zeros((w_bits.shape[0], 0), np.uint8)
     return sparse, dense, v, i, wd
+
+
+# -------------------------------------------------------------- Spense GLU (MLP) ---
+# [SPENSE] 2.A: output-split for the gate and up projections (rows split between a 2:4
+# GEMM and a dense GEMM), input-split for the down projection; 2.B: the intermediate
+# indices of a GLU MLP can be permuted without changing its result, so the dense ones are
+# chosen by a score and moved into one contiguous block.
+
+def spense_glu_scores(w_gate, w_up, w_down, hs_in, hs_mid) -> np.ndarray:
+    """Loss-aware importance of each intermediate index i ([SPENSE] 2.B, the "+" strategy):
+    the Wanda-style score |W_ij| * sqrt(H_jj) summed over the three projections that touch
+    index i.  Reading (the page gives the per-weight score and says it is aggregated over
+    gate, up and down, nothing more):
+        g_i = sum_j |W_gate[i][j]| * hs_in[j]     (j ascending)
+        u_i = sum_j |W_up[i][j]|   * hs_in[j]     (j ascending)
+        d_i = sum_o |W_down[o][i]|                (o ascending)
+        S_i = (g_i + u_i) + hs_mid[i] * d_i
+    in fp64, every product and sum rounded once in that order; hs_in / hs_mid are the
+    square roots of the input Hessian diagonals (X^T X over calibration tokens), given by
+    the caller.  w_*: bf16 bits, gate/up [I][H], down [H][I]."""
+    g = np.abs(bf16_to_f64(w_gate)) * np.asarray(hs_in, np.float64)[None, :]
+    u = np.abs(bf16_to_f64(w_up)) * np.asarray(hs_in, np.float64)[None, :]
+    d = np.abs(bf16_to_f64(w_down))
+    gs = np.cumsum(g, axis=1)[:, -1] if g.shape[1] else np.zeros(g.shape[0])   # left-to-right
+    us = np.cumsum(u, axis=1)[:, -1] if u.shape[1] else np.zeros(u.shape[0])
+    ds = np.cumsum(d, axis=0)[-1] if d.shape[0] else np.zeros(d.shape[1])
+    return (gs + us) + np.asarray(hs_mid, np.float64) * ds
+
+
+def spense_order(scores: np.ndarray, n_dense: int) -> np.ndarray:
+    """Permutation of the intermediate indices: the n_dense largest scores (ties to the
+    lower index) are dense; sparse indices first, then dense ones, each ascending."""
+    i_n = len(scores)
+    order = sorted(range(i_n), key=lambda j: (-scores[j], j))
+    dense = sorted(order[:n_dense])
+    is_dense = np.zeros(i_n, dtype=bool)
+    is_dense[dense] = True
+    return np.array([j for j in range(i_n) if not is_dense[j]] + dense, dtype=np.int32)
+
+
+def spense_order_tail(i_n: int, n_dense: int) -> np.ndarray:
+    """The simple strategy ([SPENSE] 2.B): the last n_dense indices stay dense (identity)."""
+    return np.arange(i_n, dtype=np.int32)
+
+
+def spense_pack(w_bits, perm, n_sparse: int, axis: int):
+    """Split a weight along `axis` by the permutation: axis 0 (output-split) takes rows
+    perm[:n_sparse] as the 2:4 region (pruned and compressed along K) and rows
+    perm[n_sparse:] as the dense region; axis 1 (input-split) does the same with columns.
+    Returns (W_s values, W_s idx, W_d)."""
+    w = np.asarray(w_bits, dtype=np.uint16)
+    perm = np.asarray(perm, dtype=np.int64)
+    if axis == 0:
+        ws, wd = w[perm[:n_sparse]], w[perm[n_sparse:]]
+    else:
+        ws, wd = w[:, perm[:n_sparse]], w[:, perm[n_sparse:]]
+    ws, wd = np.ascontiguousarray(ws), np.ascontiguousarray(wd)
+    if ws.size:
+        v, i = compress(ws, 2, 4)
+    else:
+        v = np.zeros((ws.shape[0], ws.shape[1] // 2), np.uint16)
+        i = np.zeros((ws.shape[0], ws.shape[1] // 2), np.uint8)
+    return v, i, wd
+
+
+def outsplit_gemm(x_bits, ws_vals, ws_idx, wd_bits, k: int) -> np.ndarray:
+    """[SPENSE] 2.A output split: Y = [X . W_s^T, X . W_d^T] (W_s 2:4 compressed rows)."""
+    parts = []
+    if ws_vals.shape[0]:
+        parts.append(gemm(x_bits, decompress(ws_vals, ws_idx, 2, 4, k)))
+    if wd_bits.shape[0]:
+        parts.append(gemm(x_bits, wd_bits))
+    return np.concatenate(parts, axis=1)
 
 
 # ---------------------------------------------------------------------------- GEMM ---

@@ -483,3 +483,96 @@ def test_scored_rounding_makes_ties():
     exact = [abs(value_of(x[0, i])) * float(c[i]) for i in range(4)]
     assert exact[1] > exact[0] and f32_round(exact[1]) == f32_round(exact[0])
     assert list(O.select_keep_scored(x, c, 1, 4, O.SCORE_ACT_WEIGHTED)[0]) == [True, False, False, False]
+
+
+# ------------------------------------------------------------------ Spense GLU ---
+
+def test_spense_scores_exact_small_integers():
+    """Integer-valued weights and Hessian roots keep every sum exact in fp64, so the
+    scores equal the rational formula: sum_j |Wg_ij| h_j + sum_j |Wu_ij| h_j + m_i sum_o |Wd_oi|."""
+    rng = np.random.default_rng(3)
+    i_n, h = 12, 8
+    ints = np.array([-3, -2, -1, 0, 1, 2, 3, 4], dtype=np.float32)
+    wg = arr(rng.choice(ints, (i_n, h)).tolist())
+    wu = arr(rng.choice(ints, (i_n, h)).tolist())
+    wd = arr(rng.choice(ints, (h, i_n)).tolist())
+    hs_in = rng.choice([0.5, 1.0, 2.0, 3.0], h)
+    hs_mid = rng.choice([0.25, 1.0, 5.0], i_n)
+    got = O.spense_glu_scores(wg, wu, wd, hs_in, hs_mid)
+    for i in range(i_n):
+        ref = sum(abs(Fraction(value_of(wg[i, j]))) * Fraction(hs_in[j]) for j in range(h))
+        ref += sum(abs(Fraction(value_of(wu[i, j]))) * Fraction(hs_in[j]) for j in range(h))
+        ref += Fraction(hs_mid[i]) * sum(abs(Fraction(value_of(wd[o, i]))) for o in range(h))
+        assert Fraction(got[i]) == ref
+
+
+def test_spense_scores_fixed_order():
+    """The sums run left to right in fp64: 1 + 2^-53 + 2^-53 gives 1 (each small term is
+    lost to round-to-even), where an exact or pairwise sum would give 1 + 2^-52."""
+    tiny = 2.0 ** -53
+    wg = arr([[1.0, tiny, tiny]])
+    zero = arr([[0.0, 0.0, 0.0]])
+    got = O.spense_glu_scores(wg, zero, arr([[0.0], [0.0], [0.0]]), np.ones(3), np.ones(1))
+    assert got[0] == 1.0 and 1.0 + 2 * tiny != 1.0
+
+
+def test_spense_order_ties_and_layout():
+    scores = np.array([2.0, 5.0, 5.0, 1.0, 5.0, 0.0])
+    perm = O.spense_order(scores, 2)
+    # dense: the two largest, 5.0 at indices 1 and 2 (index 4 loses the tie); sparse first
+    assert list(perm) == [0, 3, 4, 5, 1, 2]
+    assert list(O.spense_order(scores, 0)) == list(range(6))
+    assert sorted(O.spense_order(scores, 6)) == list(range(6)) and list(O.spense_order(scores, 6)) == list(range(6))
+    assert list(O.spense_order_tail(6, 2)) == list(range(6))
+
+
+def _silu(v):
+    return v / (1.0 + np.exp(-v))
+
+
+def test_spense_glu_permutation_invariance():
+    """A GLU MLP gives the same output when gate/up rows and down columns are permuted
+    together.  Spense MLP = down input-split over silu(gate) * up, each from the output-
+    split products in permuted order; it equals the plain MLP on the weights with the
+    same 2:4 pruning applied to the sparse rows of gate/up and sparse columns of down."""
+    rng = np.random.default_rng(21)
+    t, h, i_n, n_dense = 5, 32, 48, 12
+    x = synth.normal_bf16(rng, (t, h))
+    wg = synth.normal_bf16(rng, (i_n, h), 0.02)
+    wu = synth.normal_bf16(rng, (i_n, h), 0.02)
+    wd = synth.normal_bf16(rng, (h, i_n), 0.02)
+    scores = O.spense_glu_scores(wg, wu, wd, np.abs(rng.standard_normal(h)), np.abs(rng.standard_normal(i_n)))
+    perm = O.spense_order(scores, n_dense)
+    ns = i_n - n_dense
+    gv, gi, gd = O.spense_pack(wg, perm, ns, 0)
+    uv, ui, ud = O.spense_pack(wu, perm, ns, 0)
+    dv, di, dd = O.spense_pack(wd, perm, ns, 1)
+    a = _silu(O.outsplit_gemm(x, gv, gi, gd, h)) * O.outsplit_gemm(x, uv, ui, ud, h)   # permuted order
+    y = a[:, :ns] @ O.bf16_to_f64(O.decompress(dv, di, 2, 4, ns)).T + a[:, ns:] @ O.bf16_to_f64(dd).T
+    # plain MLP on the equivalently pruned weights, original index order
+    wg_e, wu_e, wd_e = wg.copy(), wu.copy(), wd.copy()
+    sp = perm[:ns]
+    wg_e[sp] = O.sparsify(wg[sp], 2, 4)[0]
+    wu_e[sp] = O.sparsify(wu[sp], 2, 4)[0]
+    wd_e[:, sp] = O.sparsify(np.ascontiguousarray(wd[:, sp]), 2, 4)[0]
+    xf = O.bf16_to_f64(x)
+    ref = (_silu(xf @ O.bf16_to_f64(wg_e).T) * (xf @ O.bf16_to_f64(wu_e).T)) @ O.bf16_to_f64(wd_e).T
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-15)
+    # a permutation that does not keep gate/up rows and down columns together changes it
+    bad = O.bf16_to_f64(O.decompress(dv, di, 2, 4, ns))[:, ::-1]
+    y_bad = a[:, :ns] @ bad.T + a[:, ns:] @ O.bf16_to_f64(dd).T
+    assert not np.allclose(y_bad, ref, rtol=1e-6)
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+def test_spense_pack_regions(axis):
+    rng = np.random.default_rng(5 + axis)
+    w = synth.normal_bf16(rng, (24, 40), 0.02)
+    n = w.shape[axis]
+    perm = rng.permutation(n).astype(np.int32)
+    ns = 16
+    v, i, wd = O.spense_pack(w, perm, ns, axis)
+    ws = w[perm[:ns]] if axis == 0 else np.ascontiguousarray(w[:, perm[:ns]])
+    kk = ws.shape[1]
+    assert (O.decompress(v, i, 2, 4, kk) == O.sparsify(ws, 2, 4)[0]).all()
+    assert (wd == (w[perm[ns:]] if axis == 0 else w[:, perm[ns:]])).all()
