@@ -283,6 +283,77 @@ int64_t nm_hybrid_gemm_workspace_size(int64_t t, int64_t k_s, int64_t k_d, int64
                                       int gathered);
 
 /*
+ * Spense layout of a GLU MLP ([SPENSE] 2.A, 2.B).  The intermediate indices of
+ * down(act(gate x) * up x) can be permuted without changing the result, so the indices
+ * kept dense are moved into one block at the end: gate and up are split by output rows
+ * (output-split: a 2:4 product and a dense product write disjoint column ranges of y),
+ * down by input columns (input-split: nm_hybrid_gemm with the column lists NULL, since
+ * the GLU output already comes in the permuted order).
+ */
+typedef enum {
+  NM_SPENSE_LOSS = 0,   /* dense = the n_dense indices of largest loss-aware score      */
+  NM_SPENSE_TAIL = 1    /* dense = the last n_dense indices (identity permutation)      */
+} nm_spense_strategy;
+
+/*
+ * nm_spense_glu_order -- which intermediate indices stay dense, and the permutation.
+ * [SPENSE] 2.B: the loss-aware score of index i sums the per-weight score
+ * |W_ij| * sqrt(H_jj) over the three projections:
+ *   S_i = (sum_j |Wg[i][j]| hs_in[j] + sum_j |Wu[i][j]| hs_in[j]) + hs_mid[i] * sum_o |Wd[o][i]|
+ * in fp64, each sum in ascending index order, every product and sum rounded once.
+ *   w_gate, w_up  bf16 [inter][ld_gu] (row i = intermediate index i), w_down bf16 [hidden][ld_d]
+ *   hs_in         fp64 [hidden]: square roots of the MLP input's Hessian diagonal (X^T X)
+ *   hs_mid        fp64 [inter]:  the same for the down projection's input
+ *                 (weights and hs_* are not read for NM_SPENSE_TAIL and may be NULL)
+ *   perm          int32 [inter] out: sparse indices ascending, then the n_dense dense ones
+ *                 ascending (ties in the score go to the lower index)
+ *   scores        fp64 [inter] out, or NULL (then the scores live in the workspace)
+ *   workspace     >= nm_spense_glu_order_workspace_size(inter) bytes
+ * Offline step (once per weight set).  Deterministic.
+ */
+nm_status nm_spense_glu_order(const void* w_gate, const void* w_up, int64_t ld_gu, const void* w_down,
+                              int64_t ld_d, int64_t hidden, int64_t inter, const double* hs_in,
+                              const double* hs_mid, int64_t n_dense, nm_spense_strategy strategy,
+                              int32_t* perm, double* scores, void* workspace, int64_t workspace_bytes,
+                              void* stream);
+int64_t nm_spense_glu_order_workspace_size(int64_t inter);
+
+/*
+ * nm_spense_pack -- split W [o][k] by a permutation into a 2:4 region and a dense region.
+ * [SPENSE] 2.A.
+ *   axis 0 (output-split, gate / up): rows perm[0:n_sparse] are pruned 2:4 along k and
+ *          compressed (values [n_sparse][k/2], meta); rows perm[n_sparse:o] go to
+ *          wd [o - n_sparse][ldwd] (ldwd >= k).  k % 4 == 0.
+ *   axis 1 (input-split, down): columns perm[0:n_sparse] are pruned 2:4 in that order
+ *          (values [o][n_sparse/2], meta); columns perm[n_sparse:k] go to wd [o][ldwd]
+ *          (ldwd >= k - n_sparse).  n_sparse % 4 == 0.
+ * Meta is U8 or 2BIT as in nm_compress.  perm entries outside the axis are clamped into
+ * it.  The workspace takes nm_spense_pack_workspace_size(o, k, axis, n_sparse) bytes
+ * (axis 0: a gathered copy of the sparse rows).  Offline step.
+ */
+nm_status nm_spense_pack(const void* w, int64_t o, int64_t k, int64_t ldw, int axis, const int32_t* perm,
+                         int64_t n_sparse, void* ws_values, void* ws_meta, nm_meta fmt, void* wd,
+                         int64_t ldwd, void* workspace, int64_t workspace_bytes, void* stream);
+int64_t nm_spense_pack_workspace_size(int64_t o, int64_t k, int axis, int64_t n_sparse);
+
+/*
+ * nm_spense_outsplit_gemm -- output-split product ([SPENSE] 2.A):
+ *   y[:, 0:o_s]        (=|+=) x . W_s^T   (W_s: 2:4 rows as packed by nm_spense_pack axis 0,
+ *                                          2BIT meta)
+ *   y[:, o_s:o_s+o_d]  (=|+=) x . W_d^T   (dense rows wd [o_d][ldwd])
+ * x bf16 [t][ldx]; k % 4 == 0; ldy >= o_s + o_d; o_s % 4 == 0 when both parts are
+ * present (the dense part starts at y + o_s).  The two parts run as the corresponding
+ * nm_spmm calls (W_COMPRESSED and the plain product), in order on `stream`, sharing the
+ * workspace: nm_spense_outsplit_workspace_size(t, k, o_s, o_d) bytes for the preferred
+ * routes.
+ */
+nm_status nm_spense_outsplit_gemm(const void* x, int64_t t, int64_t k, int64_t ldx, const void* ws_values,
+                                  const void* ws_meta, int64_t o_s, const void* wd, int64_t ldwd, int64_t o_d,
+                                  float* y, int64_t ldy, int accumulate, void* workspace,
+                                  int64_t workspace_bytes, void* stream);
+int64_t nm_spense_outsplit_workspace_size(int64_t t, int64_t k, int64_t o_s, int64_t o_d);
+
+/*
  * Measurement helpers (not part of the method): the achievable ceilings on the machine at
  * hand, reported beside the nominal peaks.
  *   nm_probe_sink_bytes   bytes of the device sink both probes write (one value per thread).

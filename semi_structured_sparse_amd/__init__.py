@@ -21,7 +21,9 @@ __all__ = [
     "nm_probe_sink_bytes", "nm_probe_read", "nm_probe_mfma_flops", "nm_probe_mfma",
     "nm_compress", "nm_decompress", "nm_lower_slide", "nm_slide_lift", "nm_spmm",
     "nm_spmm_workspace_size", "nm_hybrid_pack", "nm_hybrid_pack_workspace_size", "nm_hybrid_gemm",
-    "nm_hybrid_gemm_workspace_size", "lowered_k",
+    "nm_hybrid_gemm_workspace_size", "lowered_k", "NM_SPENSE_LOSS", "NM_SPENSE_TAIL", "nm_spense_glu_order",
+    "nm_spense_glu_order_workspace_size", "nm_spense_pack", "nm_spense_pack_workspace_size",
+    "nm_spense_outsplit_gemm", "nm_spense_outsplit_workspace_size",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnmsparse.so")
@@ -30,6 +32,7 @@ NM_OK, NM_EINVAL, NM_ESHAPE, NM_EALIGN, NM_EUNSUPPORTED, NM_EHIP = range(6)
 NM_META_U8, NM_META_2BIT = 0, 1
 NM_W_BF16, NM_W_FP8E4M3 = 0, 1
 NM_SCORE_ACT_WEIGHTED, NM_SCORE_WEIGHT = 0, 1
+NM_SPENSE_LOSS, NM_SPENSE_TAIL = 0, 1
 NM_ACT_DYNAMIC, NM_ACT_COMPRESSED, NM_W_COMPRESSED, NM_W_SLIDE, NM_ACT_MASKED = range(5)
 
 _i64 = ctypes.c_int64
@@ -95,6 +98,20 @@ def lib() -> ctypes.CDLL:
                                  _i64, _int, _vp, _i64, _vp]
     L.nm_hybrid_gemm_workspace_size.restype = _i64
     L.nm_hybrid_gemm_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _int]
+    L.nm_spense_glu_order.restype = _int
+    L.nm_spense_glu_order.argtypes = [_vp, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _int, _vp, _vp, _vp,
+                                      _i64, _vp]
+    L.nm_spense_glu_order_workspace_size.restype = _i64
+    L.nm_spense_glu_order_workspace_size.argtypes = [_i64]
+    L.nm_spense_pack.restype = _int
+    L.nm_spense_pack.argtypes = [_vp, _i64, _i64, _i64, _int, _vp, _i64, _vp, _vp, _int, _vp, _i64, _vp, _i64, _vp]
+    L.nm_spense_pack_workspace_size.restype = _i64
+    L.nm_spense_pack_workspace_size.argtypes = [_i64, _i64, _int, _i64]
+    L.nm_spense_outsplit_gemm.restype = _int
+    L.nm_spense_outsplit_gemm.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _int,
+                                          _vp, _i64, _vp]
+    L.nm_spense_outsplit_workspace_size.restype = _i64
+    L.nm_spense_outsplit_workspace_size.argtypes = [_i64, _i64, _i64, _i64]
     L.nm_probe_sink_bytes.restype = _i64
     L.nm_probe_sink_bytes.argtypes = []
     L.nm_probe_read.restype = _int
@@ -265,6 +282,65 @@ def nm_hybrid_pack_workspace_size(k: int) -> int:
 
 def nm_hybrid_gemm_workspace_size(t: int, k_s: int, k_d: int, o: int, gathered: bool) -> int:
     return int(lib().nm_hybrid_gemm_workspace_size(t, k_s, k_d, o, 1 if gathered else 0))
+
+
+def nm_spense_glu_order(w_gate, w_up, w_down, hs_in, hs_mid, n_dense, strategy, perm, workspace, scores=None,
+                        stream=None, *, hidden=None, inter=None, ld_gu=None, ld_d=None, workspace_bytes=None,
+                        check=True):
+    inter = (w_gate.shape[0] if w_gate is not None else perm.shape[0]) if inter is None else inter
+    hidden = (w_gate.shape[1] if w_gate is not None else 0) if hidden is None else hidden
+    wsb = (workspace.numel() * workspace.element_size()) if workspace_bytes is None else workspace_bytes
+    st = lib().nm_spense_glu_order(_ptr(w_gate), _ptr(w_up), (_ld(w_gate) if w_gate is not None else 0)
+                                   if ld_gu is None else ld_gu, _ptr(w_down),
+                                   (_ld(w_down) if w_down is not None else 0) if ld_d is None else ld_d, hidden,
+                                   inter, _ptr(hs_in), _ptr(hs_mid), n_dense, strategy, _ptr(perm), _ptr(scores),
+                                   _ptr(workspace), wsb, _stream(stream))
+    if check:
+        _check(st, "nm_spense_glu_order")
+    return st
+
+
+def nm_spense_glu_order_workspace_size(inter: int) -> int:
+    return int(lib().nm_spense_glu_order_workspace_size(inter))
+
+
+def nm_spense_pack(w, axis, perm, n_sparse, ws_values, ws_meta, fmt, wd, workspace=None, stream=None, *, o=None,
+                   k=None, ldw=None, ldwd=None, workspace_bytes=None, check=True):
+    o = w.shape[0] if o is None else o
+    k = w.shape[1] if k is None else k
+    wsb = (workspace.numel() * workspace.element_size() if workspace is not None else 0) \
+        if workspace_bytes is None else workspace_bytes
+    st = lib().nm_spense_pack(_ptr(w), o, k, _ld(w) if ldw is None else ldw, axis, _ptr(perm), n_sparse,
+                              _ptr(ws_values), _ptr(ws_meta), fmt, _ptr(wd),
+                              (_ld(wd) if wd is not None else 0) if ldwd is None else ldwd, _ptr(workspace), wsb,
+                              _stream(stream))
+    if check:
+        _check(st, "nm_spense_pack")
+    return st
+
+
+def nm_spense_pack_workspace_size(o: int, k: int, axis: int, n_sparse: int) -> int:
+    return int(lib().nm_spense_pack_workspace_size(o, k, axis, n_sparse))
+
+
+def nm_spense_outsplit_gemm(x, ws_values, ws_meta, o_s, wd, o_d, y, accumulate=0, workspace=None, stream=None, *,
+                            t=None, k=None, ldx=None, ldwd=None, ldy=None, workspace_bytes=None, check=True):
+    t = x.shape[0] if t is None else t
+    k = x.shape[1] if k is None else k
+    wsb = (workspace.numel() * workspace.element_size() if workspace is not None else 0) \
+        if workspace_bytes is None else workspace_bytes
+    st = lib().nm_spense_outsplit_gemm(_ptr(x), t, k, _ld(x) if ldx is None else ldx, _ptr(ws_values),
+                                       _ptr(ws_meta), o_s, _ptr(wd),
+                                       (_ld(wd) if wd is not None else 0) if ldwd is None else ldwd, o_d, _ptr(y),
+                                       _ld(y) if ldy is None else ldy, accumulate, _ptr(workspace), wsb,
+                                       _stream(stream))
+    if check:
+        _check(st, "nm_spense_outsplit_gemm")
+    return st
+
+
+def nm_spense_outsplit_workspace_size(t: int, k: int, o_s: int, o_d: int) -> int:
+    return int(lib().nm_spense_outsplit_workspace_size(t, k, o_s, o_d))
 
 
 def nm_hybrid_gemm(x, sparse_cols, k_s, dense_cols, k_d, ws_values, ws_meta, fmt, wd, o, y, accumulate=0,

@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libnmsparse.so")
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["api.hip", "select.hip", "slide.hip", "gemm_dense.hip", "gemm_lds.hip", "gemm_sparse.hip",
-           "gemm_lds_sp.hip", "hybrid_pack.hip", "decode.hip", "probe.hip"]
+           "gemm_lds_sp.hip", "hybrid_pack.hip", "spense.hip", "decode.hip", "probe.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
          # packed fp32 VALU forms stay off (code generation choice for this toolchain)
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -641,6 +641,152 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
   }
 }
 
+// ------------------------------------------------------------- Spense GLU layout ---
+
+int64_t nm_spense_glu_order_workspace_size(int64_t inter) {
+  return inter <= 0 ? 0 : align256(inter * 8) + inter * 4;
+}
+
+nm_status nm_spense_glu_order(const void* w_gate, const void* w_up, int64_t ld_gu, const void* w_down, int64_t ld_d,
+                              int64_t hidden, int64_t inter, const double* hs_in, const double* hs_mid,
+                              int64_t n_dense, nm_spense_strategy strategy, int32_t* perm, double* scores,
+                              void* workspace, int64_t workspace_bytes, void* stream) {
+  if (hidden < 0 || inter < 0 || inter > 0x7FFFFFFF || n_dense < 0 || n_dense > inter) return NM_ESHAPE;
+  if (strategy != NM_SPENSE_LOSS && strategy != NM_SPENSE_TAIL) return NM_EINVAL;
+  if (inter > 0 && (perm == nullptr || workspace == nullptr ||
+                    workspace_bytes < nm_spense_glu_order_workspace_size(inter)))
+    return NM_EINVAL;
+  nm_status st;
+  if (strategy == NM_SPENSE_LOSS) {
+    if ((st = check_bf16(w_gate, inter, hidden, ld_gu, true))) return st;
+    if ((st = check_bf16(w_up, inter, hidden, ld_gu, true))) return st;
+    if ((st = check_bf16(w_down, hidden, inter, ld_d, true))) return st;
+    if ((hs_in == nullptr && hidden > 0) || (hs_mid == nullptr && inter > 0)) return NM_EINVAL;
+    if ((hs_in && !aligned16(hs_in)) || (hs_mid && !aligned16(hs_mid))) return NM_EALIGN;
+  }
+  if ((perm && !aligned16(perm)) || (scores && !aligned16(scores)) || (workspace && !aligned16(workspace)))
+    return NM_EALIGN;
+  if (inter == 0) return NM_OK;
+  const hipStream_t s = as_stream(stream);
+  double* sc = scores != nullptr ? scores : reinterpret_cast<double*>(workspace);
+  int32_t* flag = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(workspace) + align256(inter * 8));
+  hipError_t e;
+  if (strategy == NM_SPENSE_LOSS) {
+    e = nml::launch_glu_scores((const uint16_t*)w_gate, (const uint16_t*)w_up, ld_gu, (const uint16_t*)w_down, ld_d,
+                               hidden, inter, hs_in, hs_mid, sc, s);
+    if (e == hipSuccess) e = nml::launch_rank_flags(sc, inter, n_dense, flag, s);
+  } else {
+    e = nml::launch_tail_flags(inter, n_dense, flag, s);
+  }
+  if (e == hipSuccess) e = nml::launch_flag_lists(flag, inter, n_dense, perm, perm + (inter - n_dense), s);
+  return hip_status(e);
+}
+
+int64_t nm_spense_pack_workspace_size(int64_t o, int64_t k, int axis, int64_t n_sparse) {
+  if (axis != 0 || o <= 0 || k <= 0 || n_sparse <= 0) return 0;
+  return n_sparse * ((k + 7) / 8 * 8) * 2;   // the gathered sparse rows
+}
+
+nm_status nm_spense_pack(const void* w, int64_t o, int64_t k, int64_t ldw, int axis, const int32_t* perm,
+                         int64_t n_sparse, void* ws_values, void* ws_meta, nm_meta fmt, void* wd, int64_t ldwd,
+                         void* workspace, int64_t workspace_bytes, void* stream) {
+  if (axis != 0 && axis != 1) return NM_EINVAL;
+  if (fmt != NM_META_U8 && fmt != NM_META_2BIT) return NM_EINVAL;
+  if (o < 0 || k < 0) return NM_ESHAPE;
+  const int64_t n = axis == 0 ? o : k;
+  if (n_sparse < 0 || n_sparse > n || n > 0x7FFFFFFF) return NM_ESHAPE;
+  const int64_t kc = axis == 0 ? k : n_sparse;                  // reduction length of the 2:4 region
+  const int64_t srows = axis == 0 ? n_sparse : o;               // rows of the 2:4 region
+  const int64_t drows = axis == 0 ? o - n_sparse : o, dcols = axis == 0 ? k : k - n_sparse;
+  if (srows > 0 && kc > 0 && (kc % 4) != 0) return NM_ESHAPE;
+  nm_status st;
+  if ((st = check_bf16(w, o, k, ldw, true))) return st;
+  if (n > 0 && perm == nullptr) return NM_EINVAL;
+  if (srows > 0 && kc > 0 && (ws_values == nullptr || ws_meta == nullptr)) return NM_EINVAL;
+  if ((st = check_bf16(wd, drows, dcols, ldwd, true))) return st;
+  if ((perm && !aligned16(perm)) || (ws_values && !aligned16(ws_values)) || (ws_meta && !aligned16(ws_meta)) ||
+      (workspace && !aligned16(workspace)))
+    return NM_EALIGN;
+  const int64_t need = nm_spense_pack_workspace_size(o, k, axis, n_sparse);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return NM_EINVAL;
+  if (o == 0 || k == 0) return NM_OK;
+  const hipStream_t s = as_stream(stream);
+  const int m2 = fmt == NM_META_2BIT ? 1 : 0;
+  hipError_t e = hipSuccess;
+  if (axis == 0) {
+    // output-split: gather the sparse rows, compress them 2:4 along K; gather the dense rows
+    if (n_sparse > 0) {
+      uint16_t* g = reinterpret_cast<uint16_t*>(workspace);
+      const int64_t ldg = (k + 7) / 8 * 8;
+      e = nml::launch_gather_rows((const uint16_t*)w, ldw, o, k, perm, n_sparse, g, ldg, s);
+      if (e == hipSuccess)
+        e = nml::launch_select(4, g, n_sparse, k, ldg, 2, nullptr, 0, nullptr, (uint16_t*)ws_values,
+                               (uint8_t*)ws_meta, m2, s);
+    }
+    if (e == hipSuccess && drows > 0)
+      e = nml::launch_gather_rows((const uint16_t*)w, ldw, o, k, perm + n_sparse, drows, (uint16_t*)wd, ldwd, s);
+  } else {
+    // input-split: 2:4 over the columns perm[0:n_sparse], dense columns perm[n_sparse:k]
+    e = nml::launch_pack_cols((const uint16_t*)w, o, ldw, k, perm, n_sparse, (uint16_t*)ws_values,
+                              (uint8_t*)ws_meta, m2, s);
+    if (e == hipSuccess)
+      e = nml::launch_gather_cols((const uint16_t*)w, o, ldw, k, perm + n_sparse, dcols, (uint16_t*)wd, ldwd, s);
+  }
+  return hip_status(e);
+}
+
+// the two parts of an output-split call as nm_spmm calls
+static nm_spmm_args outsplit_part(int sparse, const void* x, int64_t t, int64_t k, int64_t ldx, const void* w,
+                                  const void* meta, int64_t o, int64_t ldw, float* y, int64_t ldy, int accumulate) {
+  nm_spmm_args a{};
+  a.mode = sparse ? NM_W_COMPRESSED : NM_ACT_MASKED;
+  a.n = sparse ? 2 : 4; a.m = 4; a.ns = 2;
+  a.t = t; a.o = o; a.k = k;
+  a.x = x; a.ldx = ldx;
+  a.w = w; a.ldw = ldw; a.w_dtype = NM_W_BF16;
+  a.w_meta = meta; a.w_meta_fmt = NM_META_2BIT;
+  a.y = y; a.ldy = ldy; a.accumulate = accumulate;
+  return a;
+}
+
+int64_t nm_spense_outsplit_workspace_size(int64_t t, int64_t k, int64_t o_s, int64_t o_d) {
+  if (t <= 0 || k <= 0 || o_s < 0 || o_d < 0) return 0;
+  int64_t nb = 0;
+  if (o_s > 0) {
+    const nm_spmm_args a = outsplit_part(1, nullptr, t, k, k, nullptr, nullptr, o_s, k / 2, nullptr, o_s + o_d, 0);
+    nb = nm_spmm_workspace_size(&a);
+  }
+  if (o_d > 0) {
+    const nm_spmm_args b = outsplit_part(0, nullptr, t, k, k, nullptr, nullptr, o_d, k, nullptr, o_s + o_d, 0);
+    const int64_t nd = nm_spmm_workspace_size(&b);
+    nb = nd > nb ? nd : nb;
+  }
+  return nb;
+}
+
+nm_status nm_spense_outsplit_gemm(const void* x, int64_t t, int64_t k, int64_t ldx, const void* ws_values,
+                                  const void* ws_meta, int64_t o_s, const void* wd, int64_t ldwd, int64_t o_d,
+                                  float* y, int64_t ldy, int accumulate, void* workspace, int64_t workspace_bytes,
+                                  void* stream) {
+  if (t < 0 || k < 0 || o_s < 0 || o_d < 0) return NM_ESHAPE;
+  if (k % 4) return NM_ESHAPE;
+  if (ldy < o_s + o_d) return NM_ESHAPE;
+  if (o_s > 0 && o_d > 0 && (o_s % 4) != 0) return NM_EALIGN;   // the dense part starts at y + o_s
+  nm_status st = NM_OK;
+  if (o_s > 0) {
+    nm_spmm_args a = outsplit_part(1, x, t, k, ldx, ws_values, ws_meta, o_s, k / 2, y, ldy, accumulate);
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    if ((st = nm_spmm(&a, stream))) return st;
+  }
+  if (o_d > 0) {
+    nm_spmm_args b = outsplit_part(0, x, t, k, ldx, wd, nullptr, o_d, ldwd, y != nullptr ? y + o_s : nullptr, ldy,
+                                   accumulate);
+    b.workspace = workspace; b.workspace_bytes = workspace_bytes;
+    st = nm_spmm(&b, stream);
+  }
+  return st;
+}
+
 int64_t nm_hybrid_pack_workspace_size(int64_t k) { return k <= 0 ? 0 : k * 12 + 64; }
 
 nm_status nm_hybrid_pack(const void* w, int64_t o, int64_t k, int64_t ldw, int64_t k_dense, int32_t* sparse_cols,

@@ -82,9 +82,15 @@ __global__ __launch_bounds__(1024) void k_col_lists(const int32_t* __restrict__ 
   }
 }
 
+// Column index from a list, clamped into [0, ncols) (lists may come from the caller).
+__device__ __forceinline__ int64_t col_at(const int32_t* cols, int64_t j, int64_t ncols) {
+  const int64_t c = cols[j];
+  return c < 0 ? 0 : (c >= ncols ? ncols - 1 : c);
+}
+
 // One thread packs two consecutive 4-groups of the sparse region of one row.
 __global__ __launch_bounds__(256) void k_pack_ws(const uint16_t* __restrict__ w, int64_t o, int64_t ldw,
-                                                 const int32_t* __restrict__ sparse_cols, int64_t ks,
+                                                 int64_t ncols, const int32_t* __restrict__ sparse_cols, int64_t ks,
                                                  uint16_t* __restrict__ vals, uint8_t* __restrict__ meta,
                                                  int meta_2bit) {
   const int64_t G = ks / 4, pairs = (G + 1) / 2;
@@ -98,8 +104,8 @@ __global__ __launch_bounds__(256) void k_pack_ws(const uint16_t* __restrict__ w,
     const int64_t g = 2 * gp + h;
     if (g >= G) break;
     uint32_t d[2];
-    const uint32_t e0 = rp[sparse_cols[4 * g]], e1 = rp[sparse_cols[4 * g + 1]];
-    const uint32_t e2 = rp[sparse_cols[4 * g + 2]], e3 = rp[sparse_cols[4 * g + 3]];
+    const uint32_t e0 = rp[col_at(sparse_cols, 4 * g, ncols)], e1 = rp[col_at(sparse_cols, 4 * g + 1, ncols)];
+    const uint32_t e2 = rp[col_at(sparse_cols, 4 * g + 2, ncols)], e3 = rp[col_at(sparse_cols, 4 * g + 3, ncols)];
     d[0] = e0 | (e1 << 16);
     d[1] = e2 | (e3 << 16);
     const uint32_t keep = topn_bits<4>(d, 2);
@@ -121,12 +127,12 @@ __global__ __launch_bounds__(256) void k_pack_ws(const uint16_t* __restrict__ w,
 }
 
 __global__ __launch_bounds__(256) void k_gather_wd(const uint16_t* __restrict__ w, int64_t o, int64_t ldw,
-                                                   const int32_t* __restrict__ dense_cols, int64_t kd,
+                                                   int64_t ncols, const int32_t* __restrict__ dense_cols, int64_t kd,
                                                    uint16_t* __restrict__ wd, int64_t ldwd) {
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (tid >= o * kd) return;
   const int64_t row = tid / kd, j = tid - row * kd;
-  wd[row * ldwd + j] = w[row * ldw + dense_cols[j]];
+  wd[row * ldwd + j] = w[row * ldw + col_at(dense_cols, j, ncols)];
 }
 
 inline unsigned blocks_for(int64_t n, int b) { return (unsigned)((n + b - 1) / b); }
@@ -134,6 +140,34 @@ inline unsigned blocks_for(int64_t n, int b) { return (unsigned)((n + b - 1) / b
 }  // namespace
 
 namespace nml {
+
+hipError_t launch_rank_flags(const double* scores, int64_t n, int64_t n_top, int32_t* flag, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  k_col_rank<<<blocks_for(n, 256), 256, 0, s>>>(scores, n, n_top, flag);
+  return hipGetLastError();
+}
+
+hipError_t launch_flag_lists(const int32_t* flag, int64_t n, int64_t n_flagged, int32_t* unflagged,
+                             int32_t* flagged, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  k_col_lists<<<1, 1024, 0, s>>>(flag, n, n_flagged, unflagged, flagged);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_cols(const uint16_t* w, int64_t o, int64_t ldw, int64_t ncols, const int32_t* cols,
+                            int64_t ks, uint16_t* vals, uint8_t* meta, int meta_2bit, hipStream_t s) {
+  if (ks <= 0 || o <= 0 || ncols <= 0) return hipSuccess;
+  k_pack_ws<<<blocks_for(o * ((ks / 4 + 1) / 2), 256), 256, 0, s>>>(w, o, ldw, ncols, cols, ks, vals, meta,
+                                                                      meta_2bit);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_cols(const uint16_t* w, int64_t o, int64_t ldw, int64_t ncols, const int32_t* cols,
+                              int64_t kd, uint16_t* wd, int64_t ldwd, hipStream_t s) {
+  if (kd <= 0 || o <= 0 || ncols <= 0) return hipSuccess;
+  k_gather_wd<<<blocks_for(o * kd, 256), 256, 0, s>>>(w, o, ldw, ncols, cols, kd, wd, ldwd);
+  return hipGetLastError();
+}
 
 hipError_t launch_hybrid_pack(const uint16_t* w, int64_t o, int64_t k, int64_t ldw, int64_t k_dense,
                               int32_t* sparse_cols, int32_t* dense_cols, uint16_t* ws_values,
@@ -147,10 +181,10 @@ hipError_t launch_hybrid_pack(const uint16_t* w, int64_t o, int64_t k, int64_t l
   k_col_lists<<<1, 1024, 0, s>>>(flag, k, k_dense, sparse_cols, dense_cols);
   const int64_t ks = k - k_dense;
   if (ks > 0 && o > 0)
-    k_pack_ws<<<blocks_for(o * ((ks / 4 + 1) / 2), 256), 256, 0, s>>>(w, o, ldw, sparse_cols, ks,
+    k_pack_ws<<<blocks_for(o * ((ks / 4 + 1) / 2), 256), 256, 0, s>>>(w, o, ldw, k, sparse_cols, ks,
                                                                         ws_values, ws_meta, meta_2bit);
   if (k_dense > 0 && o > 0)
-    k_gather_wd<<<blocks_for(o * k_dense, 256), 256, 0, s>>>(w, o, ldw, dense_cols, k_dense, wd, ldwd);
+    k_gather_wd<<<blocks_for(o * k_dense, 256), 256, 0, s>>>(w, o, ldw, k, dense_cols, k_dense, wd, ldwd);
   return hipGetLastError();
 }
 

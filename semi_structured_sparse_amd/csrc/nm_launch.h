@@ -82,6 +82,27 @@ bool gemm_sparse_uses_lds(const SparseArgs& a);
 // positions for consecutive rows are contiguous, so a tile loads them as whole lines
 int64_t meta_block_bytes(int64_t o, int64_t kc);
 hipError_t launch_meta_block(const uint8_t* meta, int64_t o, int64_t kc, uint8_t* out, hipStream_t s);
+
+// Ranking and packing pieces of the hybrid packer, shared with the Spense GLU packer:
+// flag[i] = 1 for the n_top largest scores (ties to the lower index; NaN scores must be
+// mapped below every real score by the caller); the unflagged / flagged index lists in
+// ascending order (one workgroup); 2:4 compression of the columns `cols` of each row; and
+// the gather of the columns `cols`.  Column indices are clamped into [0, ncols).
+hipError_t launch_rank_flags(const double* scores, int64_t n, int64_t n_top, int32_t* flag, hipStream_t s);
+hipError_t launch_flag_lists(const int32_t* flag, int64_t n, int64_t n_flagged, int32_t* unflagged,
+                             int32_t* flagged, hipStream_t s);
+hipError_t launch_pack_cols(const uint16_t* w, int64_t o, int64_t ldw, int64_t ncols, const int32_t* cols,
+                            int64_t ks, uint16_t* vals, uint8_t* meta, int meta_2bit, hipStream_t s);
+hipError_t launch_gather_cols(const uint16_t* w, int64_t o, int64_t ldw, int64_t ncols, const int32_t* cols,
+                              int64_t kd, uint16_t* wd, int64_t ldwd, hipStream_t s);
+
+// Spense GLU: per-intermediate-index scores, tail flags, and a row gather
+hipError_t launch_glu_scores(const uint16_t* wg, const uint16_t* wu, int64_t ld_gu, const uint16_t* wdn,
+                             int64_t ld_d, int64_t hidden, int64_t inter, const double* hs_in,
+                             const double* hs_mid, double* scores, hipStream_t s);
+hipError_t launch_tail_flags(int64_t n, int64_t n_tail, int32_t* flag, hipStream_t s);
+hipError_t launch_gather_rows(const uint16_t* w, int64_t ldw, int64_t o, int64_t k, const int32_t* rows,
+                              int64_t count, uint16_t* out, int64_t ldo, hipStream_t s);
 // direct-to-LDS variant for large problems (plain loader, kc % 64 == 0, kd % 64 == 0)
 bool gemm_lds_sp_eligible(const SparseArgs& a, bool any_size);
 hipError_t launch_gemm_lds_sp(const SparseArgs& a, hipStream_t s);

@@ -159,6 +159,44 @@ def test_sparsify_scored_validation():
     assert f(P, 2, 4, Q, 0, P, None, rows=0, k=16, ldx=16, ldy=16) == S.NM_OK             # empty: no-op
 
 
+def test_spense_validation():
+    g = lambda *a, **kw: S.nm_spense_glu_order(*a, check=False, stream=0, **kw)  # noqa: E731
+    dims = dict(hidden=16, inter=32, ld_gu=16, ld_d=32, workspace_bytes=1 << 20)
+    assert g(P, P, Q, Q, Q, 4, 2, P, Q, **dims) == S.NM_EINVAL                     # strategy
+    assert g(P, P, Q, Q, Q, 40, 0, P, Q, **dims) == S.NM_ESHAPE                    # n_dense > inter
+    assert g(P, P, Q, Q, Q, 4, 0, None, Q, **dims) == S.NM_EINVAL                  # no perm
+    assert g(P, P, Q, Q, Q, 4, 0, P, None, **dims) == S.NM_EINVAL                  # no workspace
+    assert g(P, P, Q, Q, Q, 4, 0, P, Q, hidden=16, inter=32, ld_gu=16, ld_d=32,
+             workspace_bytes=100) == S.NM_EINVAL                                    # workspace too small
+    assert g(None, P, Q, Q, Q, 4, 0, P, Q, **dims) == S.NM_EINVAL                  # loss scores need weights
+    assert g(P, P, Q, None, Q, 4, 0, P, Q, **dims) == S.NM_EINVAL                  # ... and hs_in
+    assert g(P, P, Q, Q, Q, 4, 0, MIS, Q, **dims) == S.NM_EALIGN
+    assert g(None, None, None, None, None, 0, S.NM_SPENSE_TAIL, P, Q, hidden=0, inter=0, ld_gu=0, ld_d=0,
+             workspace_bytes=0) == S.NM_OK                                          # empty
+    assert S.nm_spense_glu_order_workspace_size(14336) >= 14336 * 12
+    k = lambda *a, **kw: S.nm_spense_pack(*a, check=False, stream=0, **kw)  # noqa: E731
+    pk = dict(o=16, k=32, ldw=32, ldwd=32, workspace_bytes=1 << 20)
+    assert k(P, 2, Q, 8, P, Q, S.NM_META_2BIT, P, Q, **pk) == S.NM_EINVAL          # axis
+    assert k(P, 0, Q, 8, P, Q, 7, P, Q, **pk) == S.NM_EINVAL                       # meta format
+    assert k(P, 0, Q, 20, P, Q, S.NM_META_2BIT, P, Q, **pk) == S.NM_ESHAPE         # n_sparse > o
+    assert k(P, 1, Q, 6, P, Q, S.NM_META_2BIT, P, Q, **pk) == S.NM_ESHAPE          # n_sparse % 4 (columns)
+    assert k(P, 0, Q, 8, P, Q, S.NM_META_2BIT, P, Q, o=16, k=30, ldw=32, ldwd=32,
+             workspace_bytes=1 << 20) == S.NM_ESHAPE                                # k % 4 (rows)
+    assert k(P, 0, None, 8, P, Q, S.NM_META_2BIT, P, Q, **pk) == S.NM_EINVAL       # no perm
+    assert k(P, 0, Q, 8, P, Q, S.NM_META_2BIT, P, None, o=16, k=32, ldw=32, ldwd=32,
+             workspace_bytes=0) == S.NM_EINVAL                                      # rows need the workspace
+    assert k(P, 0, MIS, 8, P, Q, S.NM_META_2BIT, P, Q, **pk) == S.NM_EALIGN
+    assert S.nm_spense_pack_workspace_size(16, 32, 0, 8) >= 8 * 32 * 2
+    assert S.nm_spense_pack_workspace_size(16, 32, 1, 8) == 0
+    f = lambda *a, **kw: S.nm_spense_outsplit_gemm(*a, check=False, stream=0, **kw)  # noqa: E731
+    od = dict(t=4, k=32, ldx=32, ldwd=32, ldy=64)
+    assert f(P, Q, Q, 32, Q, 32, P, **dict(od, k=30)) == S.NM_ESHAPE                # k % 4
+    assert f(P, Q, Q, 32, Q, 40, P, **od) == S.NM_ESHAPE                            # ldy < o_s + o_d
+    assert f(P, Q, Q, 30, Q, 32, P, **dict(od, ldy=64)) == S.NM_EALIGN              # o_s % 4
+    assert f(P, Q, Q, 32, Q, 32, P, **dict(od, t=0)) == S.NM_OK                     # empty
+    assert S.nm_spense_outsplit_workspace_size(64, 4096, 21504, 7168) > 0
+
+
 def test_hybrid_validation():
     g = lambda *a, **kw: S.nm_hybrid_gemm(*a, check=False, stream=0, **kw)  # noqa: E731
     assert g(P, P, 6, P, 2, Q, Q, S.NM_META_2BIT, Q, 8, P, t=4, ldx=16, ldwd=8, ldy=8) == S.NM_ESHAPE  # k_s % 4

@@ -1034,6 +1034,152 @@ def test_hybrid_full_size_sampled():
         check_gemm(y[rows], O.gemm(x[rows], wh), x[rows], wh, label=f"hybrid full t={t}")
 
 
+# ------------------------------------------------------------------ Spense GLU ---
+
+def spense_order_gpu(wg, wu, wd, hs_in, hs_mid, n_dense, strategy):
+    import torch
+
+    i_n, h = wg.shape
+    perm = torch.empty((i_n,), dtype=torch.int32, device="cuda")
+    scores = torch.empty((i_n,), dtype=torch.float64, device="cuda")
+    ws = empty((max(S.nm_spense_glu_order_workspace_size(i_n), 16),), np.uint8)
+    S.nm_spense_glu_order(dev(wg), dev(wu), dev(wd), torch.from_numpy(hs_in).cuda(),
+                          torch.from_numpy(hs_mid).cuda(), n_dense, strategy, perm, ws, scores=scores)
+    sync()
+    return perm.cpu().numpy(), scores.cpu().numpy()
+
+
+@pytest.mark.parametrize("i_n,h,n_dense", [(200, 64, 50), (40, 24, 0), (64, 8, 64), (136, 40, 33)])
+def test_spense_glu_order(i_n, h, n_dense):
+    """Loss-aware scores bit for bit (fp64, fixed order) and the permutation exactly, with
+    forced score ties (repeated rows); the tail strategy gives the identity."""
+    print(f"spense order i={i_n} h={h} dense={n_dense}", flush=True)
+    rng = np.random.default_rng(i_n + h)
+    wg = synth.normal_bf16(rng, (i_n, h), 0.02)
+    wu = synth.normal_bf16(rng, (i_n, h), 0.02)
+    wd = synth.normal_bf16(rng, (h, i_n), 0.02)
+    wg[5], wu[5], wd[:, 5] = wg[3], wu[3], wd[:, 3]               # equal scores at 3 and 5
+    hs_in = np.abs(rng.standard_normal(h)) + 0.1
+    hs_mid = np.abs(rng.standard_normal(i_n)) + 0.1
+    hs_mid[5] = hs_mid[3]
+    perm, scores = spense_order_gpu(wg, wu, wd, hs_in, hs_mid, n_dense, S.NM_SPENSE_LOSS)
+    ref = O.spense_glu_scores(wg, wu, wd, hs_in, hs_mid)
+    assert scores[3] == scores[5]
+    assert (scores.view(np.uint64) == ref.view(np.uint64)).all()
+    assert (perm == O.spense_order(ref, n_dense)).all()
+    perm_t, _ = spense_order_gpu(wg, wu, wd, hs_in, hs_mid, n_dense, S.NM_SPENSE_TAIL)
+    assert (perm_t == O.spense_order_tail(i_n, n_dense)).all()
+
+
+def test_spense_glu_order_full_size():
+    """The 8B-shaped layer's MLP (gate/up 14336 x 4096, down 4096 x 14336), Hessian roots
+    from the layer's input streams, 25% dense: scores bit for bit, permutation exactly."""
+    print("spense order full", flush=True)
+    lay = synth.transformer_layer(t_max=256, names=("gate", "up", "down"))
+    wg, wu, wd = lay["w"]["gate"], lay["w"]["up"], lay["w"]["down"]
+    hs_in = np.sqrt((O.bf16_to_f64(lay["x"]["mlp_in"]) ** 2).sum(0))
+    hs_mid = np.sqrt((O.bf16_to_f64(lay["x"]["down_in"]) ** 2).sum(0))
+    n_dense = wg.shape[0] // 4
+    perm, scores = spense_order_gpu(wg, wu, wd, hs_in, hs_mid, n_dense, S.NM_SPENSE_LOSS)
+    ref = O.spense_glu_scores(wg, wu, wd, hs_in, hs_mid)
+    assert (scores.view(np.uint64) == ref.view(np.uint64)).all()
+    assert (perm == O.spense_order(ref, n_dense)).all()
+
+
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("axis,o,k,ns", [(0, 100, 64, 60), (0, 48, 40, 0), (0, 40, 32, 40), (1, 24, 96, 64),
+                                         (1, 130, 40, 0), (1, 20, 48, 48)])
+def test_spense_pack(fmt, axis, o, k, ns):
+    """Split by a random permutation: the 2:4 region's values and positions and the dense
+    region bit for bit, rows (output-split) and columns (input-split)."""
+    print(f"spense pack axis={axis} o={o} k={k} ns={ns} fmt={fmt}", flush=True)
+    import torch
+
+    rng = np.random.default_rng(o + k + ns + axis)
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    n = o if axis == 0 else k
+    perm = rng.permutation(n).astype(np.int32)
+    v_ref, i_ref, wd_ref = O.spense_pack(w, perm, ns, axis)
+    srows, kc = (ns, k) if axis == 0 else (o, ns)
+    vals = empty((max(srows, 1), max(kc // 2, 1)), np.uint16, fill=-1)
+    meta = empty((max(srows, 1), max((kc + 7) // 8 if fmt else kc // 2, 1)), np.uint8, fill=255)
+    drows, dcols = wd_ref.shape
+    ldwd = max((dcols + 7) // 8 * 8, 8)
+    wdd = empty((max(drows, 1), ldwd), np.uint16, fill=-1)
+    nb = S.nm_spense_pack_workspace_size(o, k, axis, ns)
+    ws = empty((max(nb, 16),), np.uint8)
+    S.nm_spense_pack(dev(w), axis, torch.from_numpy(perm).cuda(), ns, vals, meta, fmt, wdd, ws,
+                     ldwd=ldwd, workspace_bytes=nb)
+    sync()
+    if srows and kc:
+        assert (host(vals, np.uint16)[:srows, :kc // 2] == v_ref).all()
+        got_meta = host(meta, np.uint8)[:srows]
+        assert (got_meta[:, :(kc + 7) // 8] == O.pack_meta_2bit(i_ref)).all() if fmt else \
+            (got_meta[:, :kc // 2] == i_ref).all()
+    if drows and dcols:
+        assert (host(wdd, np.uint16)[:drows, :dcols] == wd_ref).all()
+
+
+@pytest.mark.parametrize("t", [1, 17, 64, 130, 600])
+@pytest.mark.parametrize("o_s,o_d", [(264, 88), (0, 96), (128, 0), (2048, 512)])
+def test_spense_outsplit_gemm(t, o_s, o_d):
+    """Output-split product: y[:, :o_s] from the 2:4 rows, y[:, o_s:] from the dense rows,
+    on every route (few tokens to large T), overwrite and accumulate."""
+    print(f"spense outsplit t={t} o_s={o_s} o_d={o_d}", flush=True)
+    import torch
+
+    rng = np.random.default_rng(t + o_s + o_d)
+    k = 1024
+    o = o_s + o_d
+    x = synth.student_t_bf16(rng, (t, k), 4.0, 0.5)
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    perm = rng.permutation(o).astype(np.int32)
+    v_ref, i_ref, wd_ref = O.spense_pack(w, perm, o_s, 0)
+    ref = O.outsplit_gemm(x, v_ref, i_ref, wd_ref, k)
+    w_eff = np.concatenate([O.decompress(v_ref, i_ref, 2, 4, k), wd_ref], 0) if o_s else wd_ref
+    vals = empty((max(o_s, 1), k // 2), np.uint16)
+    meta = empty((max(o_s, 1), k // 8), np.uint8)
+    wdd = empty((max(o_d, 1), k), np.uint16)
+    nb = S.nm_spense_pack_workspace_size(o, k, 0, o_s)
+    ws = empty((max(nb, 16),), np.uint8)
+    S.nm_spense_pack(dev(w), 0, torch.from_numpy(perm).cuda(), o_s, vals, meta, S.NM_META_2BIT, wdd, ws,
+                     workspace_bytes=nb)
+    y0 = rng.standard_normal((t, o)).astype(np.float32)
+    for acc in (0, 1):
+        y = dev(y0) if acc else empty((t, o), np.float32, fill=float("nan"))
+        nb = S.nm_spense_outsplit_workspace_size(t, k, o_s, o_d)
+        ws2 = empty((max(nb, 16),), np.uint8)
+        S.nm_spense_outsplit_gemm(dev(x), vals, meta, o_s, wdd, o_d, y, acc, ws2, workspace_bytes=nb)
+        sync()
+        out = host(y, np.float32).astype(np.float64) - (y0 if acc else 0)
+        check_gemm(out, ref, x, w_eff, label=f"outsplit acc={acc}")
+
+
+def test_spense_down_input_split_prepermuted():
+    """Down projection of the Spense MLP: columns packed by the permutation (input-split),
+    product on an input that is already in the permuted order (no column lists)."""
+    print("spense down", flush=True)
+    import torch
+
+    rng = np.random.default_rng(77)
+    t, o, i_n, n_dense = 300, 520, 1024, 256
+    w = synth.normal_bf16(rng, (o, i_n), 0.02)
+    perm = rng.permutation(i_n).astype(np.int32)
+    ns = i_n - n_dense
+    v_ref, i_ref, wd_ref = O.spense_pack(w, perm, ns, 1)
+    a = synth.student_t_bf16(rng, (t, i_n), 4.0, 0.5)             # GLU output, permuted order
+    vals = empty((o, ns // 2), np.uint16)
+    meta = empty((o, ns // 8), np.uint8)
+    wdd = empty((o, n_dense), np.uint16)
+    S.nm_spense_pack(dev(w), 1, torch.from_numpy(perm).cuda(), ns, vals, meta, S.NM_META_2BIT, wdd)
+    sync()
+    for tt in (1, 64, t):
+        y = run_hybrid(a[:tt], None, ns, None, n_dense, vals, meta, wdd, o)
+        ref = O.gemm(a[:tt, :ns], O.decompress(v_ref, i_ref, 2, 4, ns)) + O.gemm(a[:tt, ns:], wd_ref)
+        w_eff = np.concatenate([O.decompress(v_ref, i_ref, 2, 4, ns), wd_ref], 1)
+        check_gemm(y, ref, a[:tt], w_eff, label=f"spense down t={tt}")
+
+
 # ------------------------------------------------------------------ edge cases ---
 
 def test_zero_sizes_and_k_zero():
