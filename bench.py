@@ -399,6 +399,56 @@ def measure_rows(torch, S, synth, np):
                     tot_b += wb + t * k_ * 2 + t * o_ * 4
                     keep.clear()
                 add("cfg5", t, f"layer {n}:{m} act, {kind} W, fused qkv + gate|up", tot_us, tot_f, tot_f, tot_b)
+    # Spense MLP of the same layer: 25% of the intermediate indices dense, chosen by the
+    # loss-aware score (Hessian roots from the layer's input streams) and moved to the end;
+    # gate|up as one output-split call (rows [gate_s, up_s, gate_d, up_d]), down as an
+    # input-split call on its input in the permuted order.  Packing is offline (untimed);
+    # the GLU's elementwise product between the two calls is not part of the timed path.
+    i_n, hd = 14336, 4096
+    wgu, wdn = wcat["gate_up"], wcat["down"]
+    hs_in = xdev["mlp_in"].view(torch.bfloat16).double().pow(2).sum(0).sqrt().contiguous()
+    hs_mid = xdev["down_in"].view(torch.bfloat16).double().pow(2).sum(0).sqrt().contiguous()
+    n_dense = i_n // 4
+    ns = i_n - n_dense
+    perm = torch.empty((i_n,), dtype=torch.int32, device="cuda")
+    S.nm_spense_glu_order(wgu[:i_n], wgu[i_n:], wdn, hs_in, hs_mid, n_dense, S.NM_SPENSE_LOSS, perm,
+                          buf(S.nm_spense_glu_order_workspace_size(i_n)))
+    perm_gu = torch.cat([perm[:ns], perm[:ns] + i_n, perm[ns:], perm[ns:] + i_n]).to(torch.int32).contiguous()
+    o_s, o_d = 2 * ns, 2 * n_dense
+    gv = torch.empty((o_s, hd // 2), dtype=torch.int16, device="cuda")
+    gm = torch.empty((o_s, hd // 8), dtype=torch.uint8, device="cuda")
+    gd = torch.empty((o_d, hd), dtype=torch.int16, device="cuda")
+    S.nm_spense_pack(wgu, 0, perm_gu, o_s, gv, gm, S.NM_META_2BIT, gd,
+                     buf(S.nm_spense_pack_workspace_size(2 * i_n, hd, 0, o_s)))
+    dv = torch.empty((hd, ns // 2), dtype=torch.int16, device="cuda")
+    dm = torch.empty((hd, ns // 8), dtype=torch.uint8, device="cuda")
+    dd = torch.empty((hd, n_dense), dtype=torch.int16, device="cuda")
+    S.nm_spense_pack(wdn, 1, perm, ns, dv, dm, S.NM_META_2BIT, dd)
+    torch.cuda.synchronize()
+    del wcat, w8cat
+    wbytes = o_s * hd + o_s * hd // 8 + o_d * hd * 2 + hd * ns + hd * ns // 8 + hd * n_dense * 2
+    packed = (gv, gm, gd, dv, dm, dd)
+    for t in (1, 64, 2048):
+        xg, a_in = xdev["mlp_in"][:t], xdev["down_in"][:t]   # down's input: the permuted GLU output's shape
+        ygu, yd = f32(t, 2 * i_n), f32(t, hd)
+        cps = [packed] + ([tuple(z.clone() for z in packed) for _ in range(n_copies(wbytes) - 1)] if t <= 128 else [])
+        keep.append(cps)
+        nb1 = S.nm_spense_outsplit_workspace_size(t, hd, o_s, o_d)
+        nb2 = S.nm_hybrid_gemm_workspace_size(t, ns, n_dense, hd, False)
+        ws = buf(max(nb1, nb2))
+        keep.append(ws)
+
+        def mlp(c, xg=xg, a_in=a_in, ygu=ygu, yd=yd, ws=ws, nb1=nb1, nb2=nb2):
+            S.nm_spense_outsplit_gemm(xg, c[0], c[1], o_s, c[2], o_d, ygu, 0, ws, workspace_bytes=nb1, check=False)
+            S.nm_hybrid_gemm(a_in, None, ns, None, n_dense, c[3], c[4], S.NM_META_2BIT, c[5], hd, yd, 0,
+                             workspace=ws, workspace_bytes=nb2, check=False)
+        fns = [(lambda c=c: mlp(c)) for c in cps]
+        us = gpu_time_rot_us(torch, fns) if t <= 128 else gpu_time_us(torch, fns[0], False)
+        f_dense = 2.0 * t * (2 * i_n * hd + hd * i_n)
+        f_exec = 2.0 * t * (o_s * hd / 2 + o_d * hd + hd * ns / 2 + hd * n_dense)
+        nbytes = wbytes + t * hd * 2 + t * 2 * i_n * 4 + t * i_n * 2 + t * hd * 4
+        add("spense", t, "MLP: gate|up output-split + down input-split, 25% dense", us, f_dense, f_exec, nbytes)
+        keep.clear()
     return rows
 
 
