@@ -62,7 +62,7 @@ __all__ = [
     "hybrid_pack", "gemm", "spmm_act", "spmm_slide", "hybrid_gemm", "fp8_e4m3_to_f64",
     "spmm_act_fp8", "lowered_k", "SCORE_ACT_WEIGHTED", "SCORE_WEIGHT", "selection_scores",
     "select_keep_scored", "sparsify_scored", "spense_glu_scores", "spense_order", "spense_order_tail",
-    "spense_pack", "outsplit_gemm",
+    "spense_pack", "outsplit_gemm", "e4m3_encode", "quantize_tokens", "f32_from_bf16", "spmm_w8a8_slide",
 ]
 
 
@@ -473,6 +473,69 @@ def fp8_e4m3_to_f64(q: np.ndarray) -> np.ndarray:
     sub = s * mant * 2.0 ** -9
     out = np.where(e == 0, sub, normal)
     return np.where((e == 15) & (mant == 7), np.nan, out)
+
+
+E4M3_MAX = 448.0
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    """Values with |v| <= 448 -> OCP E4M3FN codes, round to nearest, ties to even.
+    Normal range (|v| >= 2^-6): v = 2^e (1 + f), f rounded to 3 bits (a carry moves to the
+    next exponent); below it the subnormal step 2^-9 (q = round(|v| / 2^-9), and q = 8 is the
+    smallest normal, code 0x08).  Zero encodes as 0x00 (+0) or 0x80 (-0)."""
+    v = np.asarray(v, dtype=np.float64)
+    if np.any(np.abs(v) > E4M3_MAX) or np.any(np.isnan(v)):
+        raise ValueError("e4m3_encode needs finite |v| <= 448")
+    a = np.abs(v)
+    sign = np.where(np.signbit(v), 0x80, 0).astype(np.int64)
+    mant, ex = np.frexp(a)                      # a = mant * 2^ex, mant in [0.5, 1)
+    e = ex - 1                                  # a = (2 mant) * 2^e, 2 mant in [1, 2)
+    f8 = np.rint((2.0 * mant - 1.0) * 8.0)      # 3 fraction bits, ties to even (exact in fp64)
+    carry = f8 == 8.0
+    e = np.where(carry, e + 1, e)
+    f8 = np.where(carry, 0.0, f8)
+    normal = ((e + 7) << 3).astype(np.int64) + f8.astype(np.int64)
+    sub = np.rint(a * 2.0 ** 9).astype(np.int64)   # 0..8; 8 is code 0x08, the smallest normal
+    code = np.where(a >= 2.0 ** -6, normal, sub)
+    return (code | sign).astype(np.uint8)
+
+
+def quantize_tokens(x_bits: np.ndarray):
+    """Per-token fp8 quantization of bf16 activations (the online step of the SlideSparse
+    page, technical summary 2.B, which fuses it with the lift; the page gives no scheme).
+    Reading: symmetric absmax scaling to the e4m3 range, per row t:
+        amax_t = max_k |x_tk|;  r_t = fp32(448 / amax_t);  s_t = fp32(amax_t / 448)
+        q_tk  = e4m3_encode(clamp(fp32(x_tk * r_t), -448, 448))
+    with r_t = s_t = 1 for an all-zero row; every fp32 operation rounds to nearest even.
+    Returns (codes uint8 [T][K], scales fp32 [T]); x ~= dec(q) * s."""
+    x = f32_from_bf16(x_bits)
+    amax = np.abs(x).max(axis=1) if x.shape[1] else np.zeros(x.shape[0], np.float32)
+    zero = amax == 0
+    safe = np.where(zero, np.float32(1.0), amax).astype(np.float32)
+    r = np.where(zero, np.float32(1.0), np.float32(E4M3_MAX) / safe).astype(np.float32)
+    s = np.where(zero, np.float32(1.0), safe / np.float32(E4M3_MAX)).astype(np.float32)
+    v = (x * r[:, None]).astype(np.float32)
+    v = np.clip(v, np.float32(-E4M3_MAX), np.float32(E4M3_MAX))
+    return e4m3_encode(v), s
+
+
+def f32_from_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> fp32 values (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def spmm_w8a8_slide(x_bits, w8_vals, w_idx, w_scale, k: int, ns: int) -> np.ndarray:
+    """fp8 weights and fp8 activations (the SlideSparse page's serving precision, technical
+    summary 2.B-2.C): X quantized per token, lifted ((2N-2):2N weights lowered to 2:4 over
+    K' = K (2N-2)/N; ns = 2 means plain 2:4, no lift), multiplied against the 2:4 weight
+    codes W' (values [O][K'/2] + in-window positions), then both scales applied:
+        Y[t][o] = s_t * s_o * sum_k' dec(lift(q)[t][k']) * dec(W'[o][k'])"""
+    q, s_t = quantize_tokens(x_bits)
+    qx = lift(q, ns) if ns > 2 else q
+    kp = qx.shape[1]
+    wd = decompress(np.asarray(w8_vals, np.uint8).astype(np.uint16), w_idx, 2, 4, kp)
+    acc = fp8_e4m3_to_f64(qx) @ fp8_e4m3_to_f64(wd.astype(np.uint8)).T
+    return acc * s_t.astype(np.float64)[:, None] * np.asarray(w_scale, np.float64)[None, :]
 
 
 def spmm_act_fp8(x_bits: np.ndarray, w8: np.ndarray, scale: np.ndarray, n: int, m: int) -> np.ndarray:

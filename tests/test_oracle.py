@@ -576,3 +576,75 @@ def test_spense_pack_regions(axis):
     kk = ws.shape[1]
     assert (O.decompress(v, i, 2, 4, kk) == O.sparsify(ws, 2, 4)[0]).all()
     assert (wd == (w[perm[ns:]] if axis == 0 else w[:, perm[ns:]])).all()
+
+
+# ------------------------------------------------------------- fp8 activations ---
+
+def test_e4m3_encode_against_torch():
+    """The encoder written from the format definition agrees with torch's fp32 ->
+    float8_e4m3fn conversion: every finite code value, every midpoint between neighbouring
+    codes (ties to even), and random values across the normal and subnormal ranges."""
+    import torch
+
+    codes = np.array([c for c in range(256) if not np.isnan(O.fp8_e4m3_to_f64(np.uint8(c)))], np.uint8)
+    vals = O.fp8_e4m3_to_f64(codes)
+    assert (O.e4m3_encode(vals) == codes).all()
+    pos = np.sort(np.unique(np.abs(vals)))
+    mids = (pos[:-1] + pos[1:]) / 2
+    rng = np.random.default_rng(8)
+    rnd = np.concatenate([rng.uniform(-448, 448, 4000), rng.uniform(-2 ** -6, 2 ** -6, 2000),
+                          rng.uniform(-1, 1, 2000) * 2.0 ** -10])
+    for v in (np.concatenate([mids, -mids]), rnd):
+        v32 = v.astype(np.float32)
+        ref = torch.from_numpy(v32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert (O.e4m3_encode(v32.astype(np.float64)) == ref).all()
+
+
+def test_quantize_tokens_properties():
+    """Each row's largest magnitude maps to +-448 exactly; every value is reproduced by
+    dec(q) * s within half an e4m3 step (relative 2^-4 in the normal range, 2^-10 s below
+    it); the scale is amax / 448 in fp32; an all-zero row gets scale 1 and zero codes."""
+    rng = np.random.default_rng(9)
+    x = synth.student_t_bf16(rng, (40, 512), 4.0, 0.5)
+    x[7] = 0
+    q, s = O.quantize_tokens(x)
+    xf = O.bf16_to_f64(x)
+    amax = np.abs(xf).max(1)
+    for t in range(40):
+        if amax[t] == 0:
+            assert s[t] == 1.0 and (q[t] == 0).all()
+            continue
+        assert s[t] == np.float32(np.float32(amax[t]) / np.float32(448.0))
+        j = int(np.argmax(np.abs(xf[t])))
+        assert q[t, j] in (0x7E, 0xFE)
+        d = O.fp8_e4m3_to_f64(q[t]) * float(s[t])
+        err = np.abs(d - xf[t])
+        small = np.abs(xf[t]) < 2.0 ** -6 * float(s[t])
+        assert (err[~small] <= 2.0 ** -4 * np.abs(xf[t][~small]) * (1 + 1e-6)).all()
+        assert (err[small] <= 2.0 ** -10 * float(s[t]) * (1 + 1e-6)).all()
+
+
+@pytest.mark.parametrize("ns", [2, 4])
+def test_w8a8_slide_is_the_dequantized_dense_product(ns):
+    """Lifting X and lowering W preserve the product, so the fp8 result must equal the
+    dense product of the dequantized tokens with the weight codes scattered back to their
+    original positions -- a route that never lifts."""
+    rng = np.random.default_rng(10 + ns)
+    t, o, k = 9, 12, 64
+    x = synth.student_t_bf16(rng, (t, k), 4.0, 0.5)
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    if ns == 2:
+        vals, idx = O.compress(w, 2, 4)
+        w8, ws = synth.fp8_e4m3_quantize_rows(vals)
+        wd = O.decompress(w8.astype(np.uint16), idx, 2, 4, k).astype(np.uint8)
+    else:
+        v, i = O.compress(w, 6, 8)
+        vp, ip = O.slide_lower(v, i, k, ns)
+        w8, ws = synth.fp8_e4m3_quantize_rows(vp)
+        idx = ip
+        wd = O.slide_scatter_back(w8.astype(np.uint16), ip, k, ns).astype(np.uint8)
+    got = O.spmm_w8a8_slide(x, w8, idx, ws, k, ns)
+    q, st = O.quantize_tokens(x)
+    ref = (O.fp8_e4m3_to_f64(q) * st[:, None].astype(np.float64)) @ \
+        (O.fp8_e4m3_to_f64(wd) * ws[:, None].astype(np.float64)).T
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-15)
