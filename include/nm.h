@@ -144,6 +144,19 @@ nm_status nm_lower_slide(const void* values, const uint8_t* idx, int64_t rows, i
                          int ns, void* values_out, void* meta_out, nm_meta fmt, void* stream);
 
 /*
+ * nm_quant_lift -- per-token fp8 quantization of the activations fused with the lift
+ * ([SLIDE] 2.B; the page gives no quantization scheme).  Per row t:
+ *   amax = max_k |x[t][k]|,  r = fp32(448 / amax),  xs[t] = fp32(amax / 448)  (1, 1 if amax = 0)
+ *   q[k] = e4m3fn(clamp(fp32(x[t][k] * r), -448, 448)), round to nearest even (OCP E4M3FN)
+ * written lifted: xq[t][g*4(N-1) + 4w + s] = q[g*2N + 2w + s] (N = ns; ns = 2: no lift),
+ * uint8 codes [t][ldq] with ldq >= K' = k(2N-2)/N and ldq % 16 == 0 (codes past K' are
+ * zero); xs fp32 [t].  x must be finite.  nm_spmm does this itself for fp8 weights in
+ * the W_* modes; this call exists for inspection and tests.
+ */
+nm_status nm_quant_lift(const void* x, int64_t t, int64_t k, int64_t ldx, int ns, void* xq, int64_t ldq,
+                        float* xs, void* stream);
+
+/*
  * nm_slide_lift -- explicit activation lifting, X' [t][ldo] over K' = k*(2N-2)/N:
  * X'[t][g*4(N-1) + 4w + s] = X[t][g*2N + 2w + s].  [SLIDE] 2.B.  nm_spmm performs the
  * same lifting inside its operand loader; this call exists for inspection and tests.
@@ -173,6 +186,12 @@ typedef enum {
  *   W_COMPRESSED:   A = x (bf16 [t][ldx]),  B = decompress(w, w_meta), 2:4 over k
  *   W_SLIDE:        A = lift_ns(x),          B = decompress(w, w_meta), 2:4 over
  *                   K' = k*(2ns-2)/ns  (equals x . Wpruned^T)
+ *   W_* with w_dtype NM_W_FP8E4M3 (w: e4m3 codes [o][K'/2], w_scale required): x is
+ *                   quantized per token to e4m3 and lifted first (nm_quant_lift), and
+ *                   Y = xs[t] * (sum_k' dec(xq[t][k']) * dec(W'[o][k'])) * w_scale[o], on the
+ *                   fp8 sparse matrix instruction ([SLIDE]: FP8 serving).  Requires
+ *                   K' % 128 == 0 (NM_EUNSUPPORTED otherwise) and a workspace of
+ *                   nm_spmm_workspace_size bytes (NM_EINVAL otherwise).
  * then, when w_scale != NULL (fp8 weights), Y[t][o] *= w_scale[o]; finally Y = result
  * (accumulate == 0) or Y += result (accumulate == 1).
  * Optional fields (may be NULL / 0):
@@ -206,7 +225,7 @@ typedef struct {
   int x_meta_fmt;         /* nm_meta                                               */
   const void* w;          /* see mode                                              */
   int64_t ldw;            /* elements (bf16) or bytes (fp8); ignored for W_* modes */
-  int w_dtype;            /* nm_wdtype (ACT_* modes)                               */
+  int w_dtype;            /* nm_wdtype (fp8 in W_* modes: fp8 x fp8, see above)     */
   const void* w_meta;     /* W_* metadata                                          */
   int w_meta_fmt;         /* nm_meta                                               */
   const float* w_scale;   /* fp32 [o] per-row scale (required for fp8, else NULL)  */

@@ -23,7 +23,7 @@ __all__ = [
     "nm_spmm_workspace_size", "nm_hybrid_pack", "nm_hybrid_pack_workspace_size", "nm_hybrid_gemm",
     "nm_hybrid_gemm_workspace_size", "lowered_k", "NM_SPENSE_LOSS", "NM_SPENSE_TAIL", "nm_spense_glu_order",
     "nm_spense_glu_order_workspace_size", "nm_spense_pack", "nm_spense_pack_workspace_size",
-    "nm_spense_outsplit_gemm", "nm_spense_outsplit_workspace_size",
+    "nm_spense_outsplit_gemm", "nm_spense_outsplit_workspace_size", "nm_quant_lift",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnmsparse.so")
@@ -98,6 +98,8 @@ def lib() -> ctypes.CDLL:
                                  _i64, _int, _vp, _i64, _vp]
     L.nm_hybrid_gemm_workspace_size.restype = _i64
     L.nm_hybrid_gemm_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _int]
+    L.nm_quant_lift.restype = _int
+    L.nm_quant_lift.argtypes = [_vp, _i64, _i64, _i64, _int, _vp, _i64, _vp, _vp]
     L.nm_spense_glu_order.restype = _int
     L.nm_spense_glu_order.argtypes = [_vp, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _int, _vp, _vp, _vp,
                                       _i64, _vp]
@@ -282,6 +284,16 @@ def nm_hybrid_pack_workspace_size(k: int) -> int:
 
 def nm_hybrid_gemm_workspace_size(t: int, k_s: int, k_d: int, o: int, gathered: bool) -> int:
     return int(lib().nm_hybrid_gemm_workspace_size(t, k_s, k_d, o, 1 if gathered else 0))
+
+
+def nm_quant_lift(x, ns, xq, xs, stream=None, *, t=None, k=None, ldx=None, ldq=None, check=True):
+    t = x.shape[0] if t is None else t
+    k = x.shape[1] if k is None else k
+    st = lib().nm_quant_lift(_ptr(x), t, k, _ld(x) if ldx is None else ldx, ns, _ptr(xq),
+                             _ld(xq) if ldq is None else ldq, _ptr(xs), _stream(stream))
+    if check:
+        _check(st, "nm_quant_lift")
+    return st
 
 
 def nm_spense_glu_order(w_gate, w_up, w_down, hs_in, hs_mid, n_dense, strategy, perm, workspace, scores=None,

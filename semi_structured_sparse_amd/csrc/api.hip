@@ -225,9 +225,55 @@ int64_t meta_block_ws(const nml::SparseArgs& sa) {
 nm_status use_meta_block(nml::SparseArgs& sa, void* ws, int64_t ws_bytes, int64_t off, hipStream_t s) {
   if (ws == nullptr || !meta_block_wanted(sa) || ws_bytes < off + nml::meta_block_bytes(sa.o, sa.kc)) return NM_OK;
   uint8_t* blk = reinterpret_cast<uint8_t*>(ws) + off;
-  if (nml::launch_meta_block(sa.w_meta, sa.o, sa.kc, blk, s) != hipSuccess) return NM_EHIP;
+  if (nml::launch_meta_block(sa.w_meta, sa.o, sa.kc, sa.f8 ? 16 : 8, blk, s) != hipSuccess) return NM_EHIP;
   sa.w_meta_blk = blk;
   return NM_OK;
+}
+
+// fp8 x fp8 route of the W_* modes with fp8 weights: workspace [token codes][token
+// scales][K-blocked positions][partial sums (few tokens)].  kc % 128 == 0.
+struct W8A8Layout {
+  int64_t xq, xs, meta, part, total;
+};
+W8A8Layout w8a8_layout(int64_t t, int64_t o, int64_t kc, const nml::SparseArgs* sa_small) {
+  W8A8Layout L{};
+  L.xq = 0;
+  L.xs = align256(t * kc);
+  L.meta = L.xs + align256(t * 4);
+  L.part = L.meta + align256(nml::meta_block_bytes(o, kc));
+  const int64_t pb = (sa_small != nullptr && use_few(t)) ? nml::gemm_lds_sp_small_part_bytes(*sa_small) : 0;
+  L.total = L.part + pb;
+  return L;
+}
+nml::SparseArgs w8a8_args(const nm_spmm_args* a, int64_t kc, const uint8_t* xq, const float* xs) {
+  nml::SparseArgs sa{};
+  sa.w_vals = (const uint16_t*)a->w; sa.w_meta = (const uint8_t*)a->w_meta; sa.kc = kc;
+  sa.x = (const uint16_t*)xq; sa.ldx = kc; sa.loader = nml::XL_PLAIN; sa.ns = 2;
+  sa.t = a->t; sa.o = a->o; sa.y = a->y; sa.ldy = a->ldy; sa.accumulate = a->accumulate; sa.trans_out = 0;
+  sa.f8 = 1; sa.x_scale = xs; sa.w_scale = a->w_scale;
+  return sa;
+}
+int64_t w8a8_ws_bytes(const nm_spmm_args* a, int64_t kc) {
+  const nml::SparseArgs sa = w8a8_args(a, kc, nullptr, nullptr);
+  return w8a8_layout(a->t, a->o, kc, &sa).total;
+}
+nm_status w8a8_product(const nm_spmm_args* a, int64_t kc, int ns, hipStream_t s) {
+  const nml::SparseArgs probe = w8a8_args(a, kc, nullptr, nullptr);
+  const W8A8Layout L = w8a8_layout(a->t, a->o, kc, &probe);
+  if (a->workspace == nullptr || a->workspace_bytes < L.total) return NM_EINVAL;
+  char* ws = reinterpret_cast<char*>(a->workspace);
+  uint8_t* xq = reinterpret_cast<uint8_t*>(ws + L.xq);
+  float* xs = reinterpret_cast<float*>(ws + L.xs);
+  hipError_t e = nml::launch_quant_lift(a->mode == NM_W_SLIDE ? ns : 2, (const uint16_t*)a->x, a->t, a->k,
+                                        a->ldx, xq, kc, xs, s);
+  if (e != hipSuccess) return NM_EHIP;
+  nml::SparseArgs sa = w8a8_args(a, kc, xq, xs);
+  uint8_t* blk = reinterpret_cast<uint8_t*>(ws + L.meta);
+  if (nml::launch_meta_block(sa.w_meta, sa.o, kc, 16, blk, s) != hipSuccess) return NM_EHIP;
+  sa.w_meta_blk = blk;
+  if (use_few(a->t))
+    return hip_status(nml::launch_gemm_lds_sp_small(sa, reinterpret_cast<float*>(ws + L.part), L.total - L.part, s));
+  return hip_status(nml::launch_gemm_lds_sp(sa, s));
 }
 
 // Large-token ACT_DYNAMIC with fp8 weights: bytes of a bf16 copy of the weights in the
@@ -399,6 +445,22 @@ nm_status nm_slide_lift(const void* x, int64_t t, int64_t k, int64_t ldx, int ns
   return hip_status(nml::launch_lift(ns, (const uint16_t*)x, t, k, ldx, (uint16_t*)x_out, ldo, as_stream(stream)));
 }
 
+nm_status nm_quant_lift(const void* x, int64_t t, int64_t k, int64_t ldx, int ns, void* xq, int64_t ldq, float* xs,
+                        void* stream) {
+  if (ns < 2 || ns > 8) return (ns > 8) ? NM_EUNSUPPORTED : NM_EINVAL;
+  if (t < 0 || k < 0 || (k % (2 * ns)) != 0) return NM_ESHAPE;
+  const int64_t kp = (k / (2 * ns)) * 4 * (ns - 1);
+  nm_status st;
+  if ((st = check_bf16(x, t, k, ldx, true, 1))) return st;
+  if (ldq < kp || !span_ok(t, ldq)) return NM_ESHAPE;
+  if ((ldq % 16) != 0) return NM_EALIGN;
+  if (t > 0 && (xq == nullptr || xs == nullptr)) return NM_EINVAL;
+  if ((xq && !aligned16(xq)) || (xs && !aligned16(xs))) return NM_EALIGN;
+  if (t == 0) return NM_OK;
+  return hip_status(nml::launch_quant_lift(ns, (const uint16_t*)x, t, k, ldx, (uint8_t*)xq, ldq, xs,
+                                           as_stream(stream)));
+}
+
 // Single-token route over K-major weights (reads only the selected K-rows).
 bool gather1_route(const nm_spmm_args* a) {
   return a->mode == NM_ACT_DYNAMIC && a->t == 1 && a->w_kmajor != nullptr && a->w_dtype == NM_W_BF16 &&
@@ -407,6 +469,11 @@ bool gather1_route(const nm_spmm_args* a) {
 
 int64_t nm_spmm_workspace_size(const nm_spmm_args* a) {
   if (a == nullptr || a->t < 0 || a->o < 0 || a->k < 0) return 0;
+  if ((a->mode == NM_W_COMPRESSED || a->mode == NM_W_SLIDE) && a->w_dtype == NM_W_FP8E4M3) {
+    if (a->mode == NM_W_SLIDE && (a->ns < 2 || a->ns > 8 || a->k % (2 * a->ns))) return 0;
+    const int64_t kc = w_mode_kc(a);
+    return (a->t > 0 && a->o > 0 && kc > 0 && kc % 128 == 0) ? w8a8_ws_bytes(a, kc) : 0;
+  }
   if (gather1_route(a)) return nml::gather1_part_bytes(a->k, a->o, a->m);
   const int64_t stage = spmm_stage_bytes(a);
   int64_t part = 0;
@@ -594,11 +661,22 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
         return NM_ESHAPE;
       }
       if (a->w_meta_fmt != NM_META_2BIT) return NM_EUNSUPPORTED;
+      if (a->w_dtype != NM_W_BF16 && a->w_dtype != NM_W_FP8E4M3) return NM_EINVAL;
       if ((st = check_bf16(a->x, T, K, a->ldx, true))) return st;
       if (O > 0 && kc > 0 && (a->w == nullptr || a->w_meta == nullptr)) return NM_EINVAL;
       if ((a->w && !aligned16(a->w)) || (a->w_meta && !aligned16(a->w_meta))) return NM_EALIGN;
       if (a->workspace != nullptr && !aligned16(a->workspace)) return NM_EALIGN;
       if (!span_ok(O, kc)) return NM_ESHAPE;
+      if (a->w_dtype == NM_W_FP8E4M3) {
+        // fp8 weights: the activations are quantized per token to e4m3 and lifted in one
+        // pass, and the product runs on the fp8 sparse matrix instruction
+        if (a->w_scale == nullptr && O > 0) return NM_EINVAL;
+        if (a->w_scale != nullptr && !aligned16(a->w_scale)) return NM_EALIGN;
+        if (kc % 128 != 0) return NM_EUNSUPPORTED;
+        if (T == 0 || O == 0) return NM_OK;
+        if (K == 0) return a->accumulate ? NM_OK : zero_output(a->y, T, O, a->ldy, s);
+        return w8a8_product(a, kc, ns, s);
+      }
       if (T == 0 || O == 0) return NM_OK;
       if (K == 0) return a->accumulate ? NM_OK : zero_output(a->y, T, O, a->ldy, s);
       if (use_few(T)) {

@@ -57,22 +57,26 @@ constexpr int kWaitLgkm0 = 0xC07F;
 __device__ __forceinline__ int swz8(int r, int c) { return c ^ ((r >> 1) & 7); }   // 8 pieces per row
 __device__ __forceinline__ int swz4(int r, int c) { return c ^ ((r >> 2) & 3); }   // 4 pieces per row
 
-template <int BM, int BN, int WM, int WN, bool MB>
+template <int BM, int BN, int WM, int WN, bool MB, bool F8>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
     const uint16_t* __restrict__ wv, const uint8_t* __restrict__ wm, int64_t kc, const uint16_t* __restrict__ x,
     int64_t ldx, const uint16_t* __restrict__ wd, int64_t ldwd, int64_t kd, int64_t dbase, int64_t T, int64_t O,
     float* __restrict__ y, int64_t ldy, int accumulate, int tiles_m, int tiles_n, int steps_per_split,
-    float* __restrict__ part, int group) {
+    float* __restrict__ part, int group, const float* __restrict__ xscale, const float* __restrict__ wscale) {
+  // F8: e4m3 codes for both operands, K-steps of 128 positions: the value and X bytes per
+  // row per step stay 64 and 128, the positions grow to 16 bytes per row per step, and the
+  // matrix instruction is v_smfmac_f32_16x16x128_fp8_fp8 (same operand placement by byte)
+  constexpr int STEPK = F8 ? 128 : 64;       // reduction positions per sparse step
+  constexpr int MU = F8 ? 16 : 8;            // position bytes per row per sparse step
   constexpr int NW = WM * WN;
   constexpr int SM = BM / WM, SN = BN / WN, FI = SM / 16, FJ = SN / 16;
   constexpr int A_BYTES = BM * 128;          // dense W rows (sparse phase: values + positions)
   constexpr int SV_BYTES = BM * 64;          // compressed values per sparse step
   constexpr int B_BYTES = BN * 128;          // X rows
   constexpr int NV = BM / 16 / NW;           // value load groups (16 rows) per wave
-  constexpr int NMW = BM / 32;               // waves that load positions (32 rows each)
   constexpr int NX = BN / 8 / NW;            // X load groups (8 rows) per wave
   constexpr int ND = BM / 8 / NW;            // dense weight load groups (8 rows) per wave
-  static_assert(NV >= 1 && NX >= 1 && ND >= 1 && NMW <= NW && BM % (16 * NW) == 0 && BN % (8 * NW) == 0,
+  static_assert(NV >= 1 && NX >= 1 && ND >= 1 && BM % (16 * NW) == 0 && BN % (8 * NW) == 0,
                 "load groups per wave");
   __shared__ __align__(16) unsigned char sA0[A_BYTES], sB0[B_BYTES];
   __shared__ __align__(16) unsigned char sA1[A_BYTES], sB1[B_BYTES];
@@ -92,9 +96,9 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
   const int tile_m = band * group + inband % band_w, tile_n = inband / band_w;
   const int64_t o0 = (int64_t)tile_m * BM, t0 = (int64_t)tile_n * BN;
 
-  const int64_t kcv = kc / 2, mstride = kc / 8;
+  const int64_t vrow = F8 ? kc / 2 : kc, mstride = kc / 8;   // value / position bytes per row
   // this split's range [sb, se) of the step sequence (sparse steps, then dense steps)
-  const int nks_all = (int)(kc / 64), nk_all = nks_all + (int)(kd / 64);
+  const int nks_all = (int)(kc / STEPK), nk_all = nks_all + (int)(kd / 64);
   const int sb = kpart * steps_per_split;
   const int se = min(nk_all, sb + steps_per_split);
   const int ks0 = min(sb, nks_all), ks1 = min(se, nks_all);          // sparse steps [ks0, ks1)
@@ -108,14 +112,16 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
     for (int j = 0; j < FJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int fr = lane & 15, fg = lane >> 4;
 
-  // X rows: groups of 8 rows (8 lanes x 16 bytes per row), NX per wave
-  const uint16_t* xsrc[NX];
+  // X rows: groups of 8 rows (8 lanes x 16 bytes per row), NX per wave; 128 bytes per
+  // step (64 bf16 or 128 fp8 codes); ldx in elements (bytes for fp8)
+  const unsigned char* xsrc[NX];
+  const int64_t ldxb = F8 ? ldx : 2 * ldx;
 #pragma unroll
   for (int q = 0; q < NX; ++q) {
     const int r = (wave + q * NW) * 8 + (lane >> 3);
     int64_t t = t0 + r;
     t = t < T ? t : T - 1;
-    xsrc[q] = x + t * ldx + 8 * swz8(r, lane & 7);
+    xsrc[q] = reinterpret_cast<const unsigned char*>(x) + t * ldxb + 16 * swz8(r, lane & 7);
   }
 
   // ----------------------------------------------------------- sparse phase ---
@@ -128,25 +134,31 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
       const int r = (wave + q * NW) * 16 + (lane >> 2);
       int64_t o = o0 + r;
       o = o < O ? o : O - 1;
-      vsrc[q] = reinterpret_cast<const uint8_t*>(wv) + o * kcv * 2 + 16 * swz4(r, lane & 3);
+      vsrc[q] = reinterpret_cast<const uint8_t*>(wv) + o * vrow + 16 * swz4(r, lane & 3);
     }
-    // positions of step s for row o: wm + o * mstride + 8 s (row-major) or
-    // wm + (s * O + o) * 8 (K-blocked)
+    // positions of step s for row o: wm + o * mstride + MU s (row-major) or
+    // wm + (s * O + o) * MU (K-blocked); bf16: 2 lanes of 4 bytes per row (32 rows per
+    // loading wave), fp8: one lane of 16 bytes per row (64 rows per loading wave)
+    constexpr int MROWS = F8 ? 64 : 32, NMWAVES = BM / MROWS;
+    static_assert(NMWAVES <= NW, "position load waves");
     const uint8_t* msrc;
-    const int64_t mstep = MB ? O * 8 : 8;
+    const int64_t mstep = MB ? O * MU : MU;
     {
-      const int r = (wave < NMW ? wave : 0) * 32 + (lane >> 1);
+      const int r = (wave < NMWAVES ? wave : 0) * MROWS + (F8 ? lane : (lane >> 1));
       int64_t o = o0 + r;
       o = o < O ? o : O - 1;
-      msrc = wm + o * (MB ? 8 : mstride) + 4 * (lane & 1);
+      msrc = wm + o * (MB ? MU : mstride) + (F8 ? 0 : 4 * (lane & 1));
     }
     auto issue = [&](unsigned char* a, unsigned char* b, int s) {
-      const int64_t k0 = (int64_t)(ks0 + s) * 64;   // dense positions; also the byte offset of the values
+      const int64_t v0 = (int64_t)(ks0 + s) * 64;   // value bytes per row per step: 64
 #pragma unroll
-      for (int q = 0; q < NV; ++q) g2lds16(vsrc[q] + k0, a + (wave + q * NW) * 1024);
-      if (wave < NMW) g2lds4(msrc + (ks0 + s) * mstep, a + SV_BYTES + wave * 256);
+      for (int q = 0; q < NV; ++q) g2lds16(vsrc[q] + v0, a + (wave + q * NW) * 1024);
+      if (wave < NMWAVES) {
+        if constexpr (F8) g2lds16(msrc + (ks0 + s) * mstep, a + SV_BYTES + wave * 1024);
+        else g2lds4(msrc + (ks0 + s) * mstep, a + SV_BYTES + wave * 256);
+      }
 #pragma unroll
-      for (int q = 0; q < NX; ++q) g2lds16(xsrc[q] + k0, b + (wave + q * NW) * 1024);
+      for (int q = 0; q < NX; ++q) g2lds16(xsrc[q] + (int64_t)(ks0 + s) * 128, b + (wave + q * NW) * 1024);
     };
     // The B fragment of column block j + 1 is read while block j is multiplied; the wait
     // for it sits before the next reads (while a direct-to-LDS load is in flight the
@@ -164,7 +176,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
       for (int i = 0; i < FI; ++i) {
         const int r = wmi * SM + i * 16 + fr;
         af[i] = *reinterpret_cast<const bf16x8*>(a + r * 64 + 16 * swz4(r, fg));
-        idx[i] = *reinterpret_cast<const uint16_t*>(a + SV_BYTES + r * 8 + 2 * fg);
+        if constexpr (F8) idx[i] = *reinterpret_cast<const int*>(a + SV_BYTES + r * 16 + 4 * fg);
+        else idx[i] = *reinterpret_cast<const uint16_t*>(a + SV_BYTES + r * 8 + 2 * fg);
       }
       u32x8 bcur = read_bv(b, 0), bnxt;
 #pragma unroll
@@ -173,11 +186,19 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
         __builtin_amdgcn_sched_barrier(0);
         if (j + 1 < FJ) bnxt = read_bv(b, j + 1);
         __builtin_amdgcn_sched_barrier(0);
-        const bf16x16 bv = __builtin_bit_cast(bf16x16, bcur);
         __builtin_amdgcn_s_setprio(1);
+        if constexpr (F8) {
+          const i32x8 bv = __builtin_bit_cast(i32x8, bcur);
 #pragma unroll
-        for (int i = 0; i < FI; ++i)
-          acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af[i], bv, acc[i][j], idx[i], 0, 0);
+          for (int i = 0; i < FI; ++i)
+            acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(__builtin_bit_cast(i32x4, af[i]), bv,
+                                                                       acc[i][j], idx[i], 0, 0);
+        } else {
+          const bf16x16 bv = __builtin_bit_cast(bf16x16, bcur);
+#pragma unroll
+          for (int i = 0; i < FI; ++i)
+            acc[i][j] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(af[i], bv, acc[i][j], idx[i], 0, 0);
+        }
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
         bcur = bnxt;
@@ -217,7 +238,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
 #pragma unroll
       for (int q = 0; q < ND; ++q) g2lds16(dsrc[q] + j0, a + (wave + q * NW) * 1024);
 #pragma unroll
-      for (int q = 0; q < NX; ++q) g2lds16(xsrc[q] + dbase + j0, b + (wave + q * NW) * 1024);
+      for (int q = 0; q < NX; ++q) g2lds16(xsrc[q] + 2 * (dbase + j0), b + (wave + q * NW) * 1024);
     };
     // A fragments one row step ahead, waits before the next reads (as in the sparse phase)
     auto read_ad = [&](const unsigned char* a, int ks, int i) {
@@ -267,15 +288,26 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
     }
   }
 
-  // epilogue: lane holds 4 consecutive o for one t in each 16x16 block
+  // epilogue: lane holds 4 consecutive o for one t in each 16x16 block; fp8 sums take
+  // the token scale, then the row scale: y = (sum * s_t) * s_o
   const bool vec_ok = ((ldy & 3) == 0);
 #pragma unroll
   for (int i = 0; i < FI; ++i) {
     const int64_t ob = o0 + wmi * SM + i * 16 + 4 * fg;
+    float wsr[4] = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (F8) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wsr[r] = wscale[ob + r < O ? ob + r : O - 1];
+    }
 #pragma unroll
     for (int j = 0; j < FJ; ++j) {
       const int64_t t = t0 + wni * SN + j * 16 + fr;
       if (t >= T) continue;
+      if constexpr (F8) {
+        const float st = xscale[t];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = (acc[i][j][r] * st) * wsr[r];
+      }
       float* yp = y + t * ldy + ob;
       if (part != nullptr) {
         float* pp = part + ((int64_t)kpart * T + t) * O + ob;
@@ -307,24 +339,25 @@ static int group_for(int tiles_m, int bm, int bn) {
 
 // K-blocked positions: a workgroup moves a block of 128 rows x 16 steps (8 bytes per row
 // and step) through LDS, reading each row's 128 bytes and writing each step's 1 KB run.
+template <typename U>
 __global__ __launch_bounds__(256) void k_meta_block(const uint8_t* __restrict__ meta, int64_t o, int64_t nsteps,
                                                     uint8_t* __restrict__ out) {
-  __shared__ uint2 tile[16][128 + 1];
+  __shared__ U tile[16][128 + 1];
   const int tid = threadIdx.x;
   const int64_t r0 = (int64_t)blockIdx.x * 128, s0 = (int64_t)blockIdx.y * 16;
-  const int64_t rowb = nsteps * 8;
+  const int64_t rowb = nsteps * (int64_t)sizeof(U);
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     const int rr = p * 16 + (tid >> 4), c = tid & 15;
     const int64_t row = r0 + rr, st = s0 + c;
-    if (row < o && st < nsteps) tile[c][rr] = *reinterpret_cast<const uint2*>(meta + row * rowb + st * 8);
+    if (row < o && st < nsteps) tile[c][rr] = *reinterpret_cast<const U*>(meta + row * rowb + st * (int64_t)sizeof(U));
   }
   __syncthreads();
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     const int c = p * 2 + (tid >> 7), rr = tid & 127;
     const int64_t row = r0 + rr, st = s0 + c;
-    if (row < o && st < nsteps) *reinterpret_cast<uint2*>(out + (st * o + row) * 8) = tile[c][rr];
+    if (row < o && st < nsteps) *reinterpret_cast<U*>(out + (st * o + row) * (int64_t)sizeof(U)) = tile[c][rr];
   }
 }
 
@@ -333,7 +366,7 @@ hipError_t launch_sp_cfg(const SparseArgs& a, hipStream_t s, int64_t splits, flo
   const int tiles_m = (int)((a.o + BM - 1) / BM), tiles_n = (int)((a.t + BN - 1) / BN);
   const int64_t ntiles = (int64_t)tiles_m * tiles_n;
   if (ntiles == 0) return hipSuccess;
-  const int64_t nk = a.kc / 64 + a.kd / 64;
+  const int64_t nk = a.kc / (a.f8 ? 128 : 64) + a.kd / 64;
   if (splits < 1 || part == nullptr) splits = 1;
   const int64_t per = (nk + splits - 1) / splits;
   splits = per > 0 ? (nk + per - 1) / per : 1;
@@ -341,14 +374,18 @@ hipError_t launch_sp_cfg(const SparseArgs& a, hipStream_t s, int64_t splits, flo
   const dim3 grid((unsigned)(ntiles * splits)), block(64 * WM * WN);
   const int steps = (int)(per > 0 ? per : 1), group = group_for(tiles_m, BM, BN);
   float* pp = splits > 1 ? part : nullptr;
-  if (a.w_meta_blk != nullptr)
-    k_gemm_lds_sp<BM, BN, WM, WN, true><<<grid, block, 0, s>>>(
-        a.w_vals, a.w_meta_blk, a.kc, a.x, a.ldx, a.wd, a.ldwd, a.kd, a.dbase, a.t, a.o, a.y, a.ldy, a.accumulate,
-        tiles_m, tiles_n, steps, pp, group);
-  else
-    k_gemm_lds_sp<BM, BN, WM, WN, false><<<grid, block, 0, s>>>(
-        a.w_vals, a.w_meta, a.kc, a.x, a.ldx, a.wd, a.ldwd, a.kd, a.dbase, a.t, a.o, a.y, a.ldy, a.accumulate,
-        tiles_m, tiles_n, steps, pp, group);
+#define NM_SP_LAUNCH(MBV, F8V, META)                                                                    \
+  k_gemm_lds_sp<BM, BN, WM, WN, MBV, F8V><<<grid, block, 0, s>>>(                                       \
+      a.w_vals, META, a.kc, a.x, a.ldx, a.wd, a.ldwd, a.kd, a.dbase, a.t, a.o, a.y, a.ldy, a.accumulate, \
+      tiles_m, tiles_n, steps, pp, group, a.x_scale, a.w_scale)
+  if (a.f8) {
+    if (a.w_meta_blk != nullptr) NM_SP_LAUNCH(true, true, a.w_meta_blk);
+    else NM_SP_LAUNCH(false, true, a.w_meta);
+  } else {
+    if (a.w_meta_blk != nullptr) NM_SP_LAUNCH(true, false, a.w_meta_blk);
+    else NM_SP_LAUNCH(false, false, a.w_meta);
+  }
+#undef NM_SP_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   return launch_reduce_parts(part, splits, nullptr, a.t, a.o, a.y, a.ldy, a.accumulate, s);
@@ -358,7 +395,7 @@ hipError_t launch_sp_cfg(const SparseArgs& a, hipStream_t s, int64_t splits, flo
 int64_t sp_small_splits(const SparseArgs& a) {
   const int bn = a.t <= 64 ? 64 : 128;
   const int64_t tiles = ((a.o + 127) / 128) * ((a.t + bn - 1) / bn);
-  const int64_t nk = a.kc / 64 + a.kd / 64;
+  const int64_t nk = a.kc / (a.f8 ? 128 : 64) + a.kd / 64;
   int64_t splits = 256 / tiles;
   if (splits > nk / 2) splits = nk / 2;
   return splits < 1 ? 1 : splits;
@@ -371,6 +408,8 @@ namespace nml {
 bool gemm_lds_sp_eligible(const SparseArgs& a, bool any_size) {
   if (a.loader != XL_PLAIN || a.trans_out) return false;
   if (a.kc % 64 != 0 || a.kd % 64 != 0 || (a.kc == 0 && a.kd == 0)) return false;
+  if (a.f8 && (a.kc % 128 != 0 || a.kd != 0 || (a.ldx % 16) != 0 || a.x_scale == nullptr || a.w_scale == nullptr))
+    return false;
   if ((a.ldx % 8) != 0 || (a.kd > 0 && ((a.ldwd % 8) != 0 || (a.dbase % 8) != 0))) return false;
   // enough 256 x 256 tiles to fill the machine
   return any_size || ((a.o + 255) / 256) * ((a.t + 255) / 256) >= 128;
@@ -378,12 +417,14 @@ bool gemm_lds_sp_eligible(const SparseArgs& a, bool any_size) {
 
 int64_t meta_block_bytes(int64_t o, int64_t kc) { return o * (kc / 8); }
 
-hipError_t launch_meta_block(const uint8_t* meta, int64_t o, int64_t kc, uint8_t* out, hipStream_t s) {
-  const int64_t nsteps = kc / 64;
+hipError_t launch_meta_block(const uint8_t* meta, int64_t o, int64_t kc, int unit, uint8_t* out, hipStream_t s) {
+  if (unit != 8 && unit != 16) return hipErrorInvalidValue;
+  const int64_t nsteps = kc / (8 * unit);
   if (o <= 0 || nsteps <= 0) return hipSuccess;
   const int64_t gx = (o + 127) / 128, gy = (nsteps + 15) / 16;
   if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidConfiguration;
-  k_meta_block<<<dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s>>>(meta, o, nsteps, out);
+  if (unit == 8) k_meta_block<uint2><<<dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s>>>(meta, o, nsteps, out);
+  else k_meta_block<uint4><<<dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s>>>(meta, o, nsteps, out);
   return hipGetLastError();
 }
 

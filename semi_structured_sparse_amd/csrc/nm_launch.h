@@ -17,6 +17,10 @@ hipError_t launch_decompress(int m, const uint16_t* values, const uint8_t* meta,
                              int64_t rows, int64_t k, int n, uint16_t* y, int64_t ldy, hipStream_t s);
 hipError_t launch_lower_slide(int ns, const uint16_t* values, const uint8_t* idx, int64_t rows,
                               int64_t k, uint16_t* vout, uint8_t* mout, int meta_2bit, hipStream_t s);
+// per-token fp8 quantization fused with the lift (ns = 2: no lift): codes xq [t][ldq]
+// (lifted length K (2ns-2)/ns, zero up to ldq; ldq % 4 == 0), scales xs [t]
+hipError_t launch_quant_lift(int ns, const uint16_t* x, int64_t t, int64_t k, int64_t ldx, uint8_t* xq,
+                             int64_t ldq, float* xs, hipStream_t s);
 hipError_t launch_lift(int ns, const uint16_t* x, int64_t t, int64_t k, int64_t ldx, uint16_t* xo,
                        int64_t ldo, hipStream_t s);
 
@@ -74,14 +78,21 @@ struct SparseArgs {
   // optional K-blocked copy of w_meta, [kc/64][o][8 bytes] (launch_meta_block), read by
   // the direct-to-LDS kernel in place of w_meta; the other kernels ignore it
   const uint8_t* w_meta_blk;
+  // fp8 x fp8 (direct-to-LDS kernel only): w_vals are e4m3 codes [o][kc/2], x holds e4m3
+  // codes [t][ldx bytes] (quantized per token, lifted), y = x_scale[t] * w_scale[o] * sum;
+  // K-steps of 128 positions (kc % 128 == 0), blocked positions [kc/128][o][16 bytes]
+  int f8;
+  const float* x_scale;
+  const float* w_scale;
 };
 hipError_t launch_gemm_sparse(const SparseArgs& a, hipStream_t s);
 // whether launch_gemm_sparse hands this call to the direct-to-LDS kernel
 bool gemm_sparse_uses_lds(const SparseArgs& a);
 // 2-bit positions [o][kc/8] -> K-blocked [kc/64][o][8 bytes] (kc % 64 == 0): one K-step's
 // positions for consecutive rows are contiguous, so a tile loads them as whole lines
+// (unit = bytes of positions per row per K-step: 8 for bf16 steps of 64, 16 for fp8 steps of 128)
 int64_t meta_block_bytes(int64_t o, int64_t kc);
-hipError_t launch_meta_block(const uint8_t* meta, int64_t o, int64_t kc, uint8_t* out, hipStream_t s);
+hipError_t launch_meta_block(const uint8_t* meta, int64_t o, int64_t kc, int unit, uint8_t* out, hipStream_t s);
 
 // Ranking and packing pieces of the hybrid packer, shared with the Spense GLU packer:
 // flag[i] = 1 for the n_top largest scores (ties to the lower index; NaN scores must be

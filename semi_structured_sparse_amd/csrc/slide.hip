@@ -96,9 +96,93 @@ __global__ __launch_bounds__(256) void k_lift(const uint16_t* __restrict__ x, in
     for (int s = 0; s < 4; ++s) dst[4 * w + s] = src[2 * w + s];
 }
 
+// e4m3fn code of v (|v| <= 448, finite), round to nearest, ties to even: in the normal
+// range the 23 fraction bits are rounded to 3 (a carry moves to the next exponent), below
+// 2^-6 the value is rounded to a multiple of the subnormal step 2^-9 (q = 8 is code 0x08,
+// the smallest normal).
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const uint32_t a = b & 0x7FFFFFFFu;
+  if (__uint_as_float(a) >= 0x1p-6f) {
+    int e = (int)(a >> 23) - 127;
+    uint32_t m3 = (a >> 20) & 7u;
+    const uint32_t rem = a & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) ++m3;
+    if (m3 == 8u) { m3 = 0u; ++e; }
+    return sign | ((uint32_t)(e + 7) << 3) | m3;
+  }
+  return sign | (uint32_t)rintf(__uint_as_float(a) * 512.0f);
+}
+
+// Per-token fp8 quantization fused with the lift (SlideSparse page, technical summary
+// 2.B: the online step quantizes the activations and expands them for the lowered
+// weights in one pass).  One workgroup per token row: the row's magnitude maximum (on
+// the 15-bit patterns, which order like |x|), then r = fp32(448 / amax) and
+// s = fp32(amax / 448) (1 for an all-zero row), then every value x -> e4m3(clamp(x * r)),
+// written in lifted order: out[g 4(NS-1) + 4w + s] = q[g 2NS + 2w + s] (NS = 2: no lift).
+// Codes past the lifted length, up to ldq, are written as zero.
+template <int NS>
+__global__ __launch_bounds__(256) void k_quant_lift(const uint16_t* __restrict__ x, int64_t k, int64_t ldx,
+                                                    uint8_t* __restrict__ xq, int64_t ldq, float* __restrict__ xs) {
+  constexpr int W = NS - 1;
+  __shared__ uint32_t red[4];
+  const int64_t row = blockIdx.x;
+  const uint16_t* xr = x + row * ldx;
+  uint8_t* qr = xq + row * ldq;
+  const int tid = threadIdx.x;
+  uint32_t mk = 0;
+  for (int64_t i = tid; i < k; i += 256) {
+    const uint32_t key = xr[i] & 0x7FFFu;
+    mk = key > mk ? key : mk;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)mk, off, 64);
+    mk = o > mk ? o : mk;
+  }
+  if ((tid & 63) == 0) red[tid >> 6] = mk;
+  __syncthreads();
+  mk = red[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) mk = red[w] > mk ? red[w] : mk;
+  const float amax = __uint_as_float(mk << 16);
+  const float r = mk == 0 ? 1.0f : 448.0f / amax;
+  if (tid == 0) xs[row] = mk == 0 ? 1.0f : amax / 448.0f;
+  const int64_t G = k / (2 * NS);
+  for (int64_t g = tid; g < G; g += 256) {
+    uint32_t q[2 * NS];
+#pragma unroll
+    for (int i = 0; i < 2 * NS; ++i) {
+      const float v = __uint_as_float((uint32_t)xr[g * 2 * NS + i] << 16) * r;
+      q[i] = e4m3_rne(fminf(fmaxf(v, -448.0f), 448.0f));
+    }
+    // 4 (NS - 1) lifted codes = NS - 1 dwords, one per window
+    uint32_t* dst = reinterpret_cast<uint32_t*>(qr + g * 4 * W);
+#pragma unroll
+    for (int w = 0; w < W; ++w)
+      dst[w] = q[2 * w] | (q[2 * w + 1] << 8) | (q[2 * w + 2] << 16) | (q[2 * w + 3] << 24);
+  }
+  for (int64_t i = G * 4 * W + tid; i < ldq; i += 256) qr[i] = 0;
+}
+
 }  // namespace
 
 namespace nml {
+
+hipError_t launch_quant_lift(int ns, const uint16_t* x, int64_t t, int64_t k, int64_t ldx, uint8_t* xq,
+                             int64_t ldq, float* xs, hipStream_t s) {
+  if (t <= 0) return hipSuccess;
+  if (t > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  dim3 grid((unsigned)t), block(256);
+  switch (ns) {
+#define NM_CASE(NSV) case NSV: k_quant_lift<NSV><<<grid, block, 0, s>>>(x, k, ldx, xq, ldq, xs); break;
+    NM_CASE(2) NM_CASE(3) NM_CASE(4) NM_CASE(5) NM_CASE(6) NM_CASE(7) NM_CASE(8)
+#undef NM_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_lower_slide(int ns, const uint16_t* values, const uint8_t* idx, int64_t rows,
                               int64_t k, uint16_t* vout, uint8_t* mout, int meta_2bit, hipStream_t s) {

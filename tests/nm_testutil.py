@@ -61,3 +61,15 @@ def sample_rows(t, count=48, seed=0):
     r = set(rng.choice(t, size=min(count, t), replace=False).tolist())
     r.update({0, t - 1})
     return np.array(sorted(r))
+
+
+def check_gemm_vals(y, y_ref, a_vals, b_vals, label=""):
+    """check_gemm with both operands given as fp64 values (e.g. dequantized fp8 codes)."""
+    y = np.asarray(y, dtype=np.float64)
+    bound = np.abs(np.asarray(a_vals, np.float64)) @ np.abs(np.asarray(b_vals, np.float64)).T
+    err = np.abs(y - y_ref)
+    rel = np.linalg.norm(y - y_ref) / max(np.linalg.norm(y_ref), 1e-300)
+    worst = (err - ELT_REL * bound - ELT_ABS).max() if err.size else -1
+    assert rel <= REL_FRO, f"{label} relative Frobenius error {rel:.3e}"
+    assert worst <= 0, f"{label} per-element bound exceeded by {worst:.3e}"
+    return rel

@@ -159,6 +159,24 @@ def test_sparsify_scored_validation():
     assert f(P, 2, 4, Q, 0, P, None, rows=0, k=16, ldx=16, ldy=16) == S.NM_OK             # empty: no-op
 
 
+def test_w8a8_validation():
+    q = lambda *a, **kw: S.nm_quant_lift(*a, check=False, stream=0, **kw)  # noqa: E731
+    assert q(P, 1, Q, P, t=4, k=16, ldx=16, ldq=32) == S.NM_EINVAL                 # ns < 2
+    assert q(P, 9, Q, P, t=4, k=18, ldx=18, ldq=32) == S.NM_EUNSUPPORTED           # ns > 8
+    assert q(P, 4, Q, P, t=4, k=12, ldx=16, ldq=32) == S.NM_ESHAPE                 # k % 2ns
+    assert q(P, 4, Q, P, t=4, k=16, ldx=16, ldq=16) == S.NM_ESHAPE                 # ldq < K' (24)
+    assert q(P, 4, Q, P, t=4, k=16, ldx=16, ldq=40) == S.NM_EALIGN                 # ldq % 16
+    assert q(P, 4, None, P, t=4, k=16, ldx=16, ldq=32) == S.NM_EINVAL              # no codes
+    assert q(P, 4, Q, P, t=0, k=16, ldx=16, ldq=32) == S.NM_OK                     # empty
+    f = lambda a: S.nm_spmm(a, check=False, stream=0)  # noqa: E731
+    w8 = dict(mode=S.NM_W_SLIDE, ns=4, w_dtype=S.NM_W_FP8E4M3, w_meta=P, w_meta_fmt=S.NM_META_2BIT)
+    assert f(spmm_args(k=256, ldx=256, w_scale=None, **w8)) == S.NM_EINVAL         # fp8 needs scales
+    assert f(spmm_args(k=64, ldx=64, w_scale=P, **w8)) == S.NM_EUNSUPPORTED         # K' = 96 not % 128
+    assert f(spmm_args(k=256, ldx=256, w_scale=P, **w8)) == S.NM_EINVAL             # needs the workspace
+    a = spmm_args(t=4096, o=4096, k=4096, ldx=4096, ldy=4096, w_scale=P, **w8)
+    assert S.nm_spmm_workspace_size(a) >= 4096 * 6144 + 4096 * 4 + 4096 * 6144 // 8
+
+
 def test_spense_validation():
     g = lambda *a, **kw: S.nm_spense_glu_order(*a, check=False, stream=0, **kw)  # noqa: E731
     dims = dict(hidden=16, inter=32, ld_gu=16, ld_d=32, workspace_bytes=1 << 20)

@@ -12,7 +12,7 @@ import pytest
 
 import oracle as O
 import synth
-from nm_testutil import check_gemm, dev, empty, host, sample_rows
+from nm_testutil import check_gemm, dev, empty, host, sample_rows, check_gemm_vals
 
 pytestmark = pytest.mark.gpu
 
@@ -1032,6 +1032,114 @@ def test_hybrid_full_size_sampled():
         y = run_hybrid(x, sc, k - kd, dc, kd, wv, wm, wdd, o)
         rows = sample_rows(t, 12, seed=t)
         check_gemm(y[rows], O.gemm(x[rows], wh), x[rows], wh, label=f"hybrid full t={t}")
+
+
+# --------------------------------------------------------- fp8 x fp8 (W8A8) ---
+
+@pytest.mark.parametrize("ns,t,k,pad", [(4, 37, 1024, 0), (2, 5, 256, 16), (3, 64, 96, 32), (4, 1, 64, 48)])
+def test_quant_lift_bitexact(ns, t, k, pad):
+    """Per-token e4m3 codes (lifted) and scales bit for bit against the oracle: Student-t
+    rows, an all-zero row, tiny values (subnormal codes), ties of the largest magnitude."""
+    print(f"quant lift ns={ns} t={t} k={k} pad={pad}", flush=True)
+    import torch
+
+    rng = np.random.default_rng(ns * 100 + t + k)
+    x = synth.student_t_bf16(rng, (t, k), 4.0, 0.5)
+    if t > 3:
+        x[1] = 0
+        x[2] = rng.choice(np.array([0x0001, 0x8002, 0x0100, 0x3F80, 0xBF80], np.uint16), size=k)
+        x[3, : k // 2] = x[3, 0]
+    kp = O.lowered_k(k, ns) if ns > 2 else k
+    ldq = (kp + 15) // 16 * 16 + pad
+    xq = torch.full((t, ldq), 0x55, dtype=torch.uint8, device="cuda")
+    xs = torch.empty((t,), dtype=torch.float32, device="cuda")
+    S.nm_quant_lift(dev(x), ns, xq, xs)
+    sync()
+    q, s_ref = O.quantize_tokens(x)
+    q_ref = O.lift(q, ns).astype(np.uint8) if ns > 2 else q
+    got = xq.cpu().numpy()
+    assert (got[:, :kp] == q_ref).all()
+    assert (got[:, kp:] == 0).all()
+    assert (xs.cpu().numpy().view(np.uint32) == s_ref.view(np.uint32)).all()
+
+
+def w8a8_weights(rng, o, k, ns):
+    """fp8 weights of the lowered 2:4 form: a random bf16 W pruned (2N-2):2N (2:4 for
+    N = 2), lowered by the oracle, the kept values quantized per row (input format)."""
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    if ns == 2:
+        vals, idx = O.compress(w, 2, 4)
+    else:
+        v, i = O.compress(w, 2 * ns - 2, 2 * ns)
+        vals, idx = O.slide_lower(v, i, k, ns)
+    w8, ws = synth.fp8_e4m3_quantize_rows(vals)
+    return w8, idx, ws
+
+
+def run_w8a8(x, w8, idx, ws, o, k, ns, accumulate=0, y0=None, rows=None):
+    import torch
+
+    t = x.shape[0]
+    mode = S.NM_W_SLIDE if ns > 2 else S.NM_W_COMPRESSED
+    y = dev(y0.astype(np.float32)) if y0 is not None else empty((t, o), np.float32, fill=float("nan"))
+    a = S.make_spmm_args(mode, t, o, k, dev(x), dev(w8), y, ns=ns, w_dtype=S.NM_W_FP8E4M3, w_scale=dev(ws),
+                         w_meta=dev(O.pack_meta_2bit(idx)), w_meta_fmt=S.NM_META_2BIT, accumulate=accumulate)
+    nb = S.nm_spmm_workspace_size(a)
+    wsb = empty((max(nb, 16),), np.uint8)
+    a.workspace, a.workspace_bytes = wsb.data_ptr(), nb
+    S.nm_spmm(a)
+    sync()
+    if rows is None:
+        return host(y, np.float32)
+    return y[torch.from_numpy(rows).cuda()].cpu().numpy()
+
+
+def w8a8_operands(x, w8, idx, ws, k, ns):
+    q, s_t = O.quantize_tokens(x)
+    qx = O.lift(q, ns).astype(np.uint8) if ns > 2 else q
+    kp = qx.shape[1]
+    wd = O.decompress(w8.astype(np.uint16), idx, 2, 4, kp).astype(np.uint8)
+    return (O.fp8_e4m3_to_f64(qx) * s_t[:, None].astype(np.float64),
+            O.fp8_e4m3_to_f64(wd) * ws[:, None].astype(np.float64))
+
+
+@pytest.mark.parametrize("ns", [2, 4])
+@pytest.mark.parametrize("t,o", [(1, 264), (17, 520), (64, 264), (128, 130), (200, 264), (600, 520)])
+def test_spmm_w8a8(ns, t, o):
+    """fp8 weights and per-token fp8 activations on the fp8 sparse matrix instruction:
+    plain 2:4 and 6:8 lowered (activations lifted in the quantizing pass), every token
+    route (split reduction for few tokens, 256 x 256 tiles above), ragged O, accumulate."""
+    print(f"w8a8 ns={ns} t={t} o={o}", flush=True)
+    rng = np.random.default_rng(ns * 1000 + t + o)
+    k = 1024
+    x = synth.student_t_bf16(rng, (t, k), 4.0, 0.5)
+    w8, idx, ws = w8a8_weights(rng, o, k, ns)
+    ref = O.spmm_w8a8_slide(x, w8, idx, ws, k, ns)
+    a_v, b_v = w8a8_operands(x, w8, idx, ws, k, ns)
+    y = run_w8a8(x, w8, idx, ws, o, k, ns)
+    check_gemm_vals(y, ref, a_v, b_v, label=f"w8a8 ns={ns}")
+    y0 = rng.standard_normal((t, o)).astype(np.float32)
+    y2 = run_w8a8(x, w8, idx, ws, o, k, ns, accumulate=1, y0=y0)
+    check_gemm_vals(y2.astype(np.float64) - y0, ref, a_v, b_v, label=f"w8a8 ns={ns} accumulate")
+
+
+def test_spmm_w8a8_full_size_sampled():
+    """6:8 weights 4096 x 4096 lowered to 2:4 over K' = 6144, fp8 weights and activations,
+    T in {1, 128, 4096}; oracle on sampled output rows."""
+    print("w8a8 full", flush=True)
+    d = synth.slide_6of8_layer(t_max=4096)
+    x_all, w = d["x"], d["w"]
+    o, k = w.shape
+    v, i = O.compress(w, 6, 8)
+    vals, idx = O.slide_lower(v, i, k, 4)
+    w8, ws = synth.fp8_e4m3_quantize_rows(vals)
+    for t in (1, 128, 4096):
+        x = x_all[:t]
+        rows = sample_rows(t, 12, seed=t)
+        y = run_w8a8(x, w8, idx, ws, o, k, 4, rows=rows)
+        ref = O.spmm_w8a8_slide(x[rows], w8, idx, ws, k, 4)
+        a_v, b_v = w8a8_operands(x[rows], w8, idx, ws, k, 4)
+        check_gemm_vals(y, ref, a_v, b_v, label=f"w8a8 full t={t}")
 
 
 # ------------------------------------------------------------------ Spense GLU ---
