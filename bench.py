@@ -23,6 +23,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 matrix peak
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PMC_FILE = os.path.join(ROOT, "profiles", "gemm_lds_pmc.json")
 PMC_SOURCES = ["semi_structured_sparse_amd/csrc/gemm_lds.hip", "semi_structured_sparse_amd/csrc/nm_device.h"]
@@ -201,14 +202,14 @@ def measure_rows(torch, S, synth, np):
     buf = lambda nb, dt=torch.uint8: torch.empty((max(int(nb), 16),), dtype=dt, device="cuda")
     rows = []
 
-    def add(cfg, t, path, us, f_dense, f_exec, nbytes, bound=None):
+    def add(cfg, t, path, us, f_dense, f_exec, nbytes, bound=None, peak=PEAK_BF16_TFLOPS):
         r = {"cfg": cfg, "tokens": t, "path": path, "us": round(us, 2),
              "dense_equiv_tflops": round(f_dense / us / 1e6, 2), "executed_tflops": round(f_exec / us / 1e6, 2),
              "algorithmic_bytes": int(nbytes), "GBps": round(nbytes / us / 1e3, 1)}
         if bound == "hbm" or (bound is None and t <= 128):
             r.update(bound="hbm", frac=round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4))
         else:
-            r.update(bound="mfma", frac=round(f_exec / us / 1e6 / PEAK_BF16_TFLOPS, 4))
+            r.update(bound="mfma", frac=round(f_exec / us / 1e6 / peak, 4))
         rows.append(r)
         log(f"  {cfg:5s} T={t:5d} {path:34s} {us:9.1f} us  {r['executed_tflops']:8.1f} TF/s exec  "
             f"{r['GBps']:7.0f} GB/s  {r['bound']} {100 * r['frac']:.1f}%")
@@ -303,6 +304,25 @@ def measure_rows(torch, S, synth, np):
         add("cfg3", t, "6:8 W lowered to 2:4, lifted X", us, 2.0 * t * 4096 * 4096,
             2.0 * t * 4096 * 3072, 4096 * 3072 * 2 + 4096 * 768 + t * 4096 * 2 + t * 4096 * 4)
         keep.clear()
+    # the same layer with fp8 weights (per-row codes, the input format) and activations
+    # quantized per token to fp8 inside the call (fused with the lift), on the fp8 sparse
+    # matrix instruction; prefill measured against the fp8 dense peak
+    q8, s8 = synth.fp8_e4m3_quantize_rows(vp.cpu().numpy().view(np.uint16))
+    q8d, s8d = dev(q8), torch.from_numpy(s8).cuda()
+    wb8 = 4096 * 3072 + 4096 * 768 + 4096 * 4
+    for t in (1, 16, 128, 4096):
+        y = f32(t, 4096)
+        mk8 = lambda q_, s_, m_: S.make_spmm_args(S.NM_W_SLIDE, t, 4096, 4096, x3[:t], q_, y, ns=4,
+                                                  w_dtype=S.NM_W_FP8E4M3, w_scale=s_, w_meta=m_,
+                                                  w_meta_fmt=S.NM_META_2BIT)
+        if t <= 128:
+            us = gpu_time_rot_us(torch, rot_spmm(mk8, (q8d, s8d, mp), wb8, keep))
+        else:
+            us = gpu_time_us(torch, spmm(mk8(q8d, s8d, mp), keep), False)
+        add("cfg3", t, "6:8 lowered, fp8 W + per-token fp8 X", us, 2.0 * t * 4096 * 4096, 2.0 * t * 4096 * 3072,
+            wb8 + t * 4096 * 2 + t * 4096 * 4, peak=PEAK_FP8_TFLOPS)
+        keep.clear()
+    del q8d, s8d
     del w3, x3, v, i8, vp, mp
     # cfg4: hybrid, 14336 x 4096, 25% dense columns
     d = synth.hybrid_up_layer(t_max=2048)

@@ -268,11 +268,13 @@ nm_status w8a8_product(const nm_spmm_args* a, int64_t kc, int ns, hipStream_t s)
                                         a->ldx, xq, kc, xs, s);
   if (e != hipSuccess) return NM_EHIP;
   nml::SparseArgs sa = w8a8_args(a, kc, xq, xs);
+  // few tokens: the split tile kernel reads the row-major positions (a blocked copy would
+  // cost a launch of about the product's own length); above that the blocked copy pays
+  if (use_few(a->t))
+    return hip_status(nml::launch_gemm_lds_sp_small(sa, reinterpret_cast<float*>(ws + L.part), L.total - L.part, s));
   uint8_t* blk = reinterpret_cast<uint8_t*>(ws + L.meta);
   if (nml::launch_meta_block(sa.w_meta, sa.o, kc, 16, blk, s) != hipSuccess) return NM_EHIP;
   sa.w_meta_blk = blk;
-  if (use_few(a->t))
-    return hip_status(nml::launch_gemm_lds_sp_small(sa, reinterpret_cast<float*>(ws + L.part), L.total - L.part, s));
   return hip_status(nml::launch_gemm_lds_sp(sa, s));
 }
 

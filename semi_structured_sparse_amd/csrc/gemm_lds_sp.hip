@@ -337,25 +337,28 @@ static int group_for(int tiles_m, int bm, int bn) {
   return g < tiles_m ? g : tiles_m;
 }
 
-// K-blocked positions: a workgroup moves a block of 128 rows x 16 steps (8 bytes per row
-// and step) through LDS, reading each row's 128 bytes and writing each step's 1 KB run.
+// K-blocked positions ([steps][rows][unit], unit = 8 or 16 bytes per row and step): a
+// workgroup moves a block of 32 rows x 16 steps through LDS (small blocks: the copy is a
+// few MB and needs many workgroups in flight to run at memory speed).
 template <typename U>
 __global__ __launch_bounds__(256) void k_meta_block(const uint8_t* __restrict__ meta, int64_t o, int64_t nsteps,
                                                     uint8_t* __restrict__ out) {
-  __shared__ U tile[16][128 + 1];
+  // a block of 32 rows x 16 steps: each row's 16 units are read as one run, each step's
+  // 32 rows written as one run
+  __shared__ U tile[16][32 + 1];
   const int tid = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.x * 128, s0 = (int64_t)blockIdx.y * 16;
+  const int64_t r0 = (int64_t)blockIdx.x * 32, s0 = (int64_t)blockIdx.y * 16;
   const int64_t rowb = nsteps * (int64_t)sizeof(U);
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
+  for (int p = 0; p < 2; ++p) {
     const int rr = p * 16 + (tid >> 4), c = tid & 15;
     const int64_t row = r0 + rr, st = s0 + c;
     if (row < o && st < nsteps) tile[c][rr] = *reinterpret_cast<const U*>(meta + row * rowb + st * (int64_t)sizeof(U));
   }
   __syncthreads();
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    const int c = p * 2 + (tid >> 7), rr = tid & 127;
+  for (int p = 0; p < 2; ++p) {
+    const int c = p * 8 + (tid >> 5), rr = tid & 31;
     const int64_t row = r0 + rr, st = s0 + c;
     if (row < o && st < nsteps) *reinterpret_cast<U*>(out + (st * o + row) * (int64_t)sizeof(U)) = tile[c][rr];
   }
@@ -421,7 +424,7 @@ hipError_t launch_meta_block(const uint8_t* meta, int64_t o, int64_t kc, int uni
   if (unit != 8 && unit != 16) return hipErrorInvalidValue;
   const int64_t nsteps = kc / (8 * unit);
   if (o <= 0 || nsteps <= 0) return hipSuccess;
-  const int64_t gx = (o + 127) / 128, gy = (nsteps + 15) / 16;
+  const int64_t gx = (o + 31) / 32, gy = (nsteps + 15) / 16;
   if (gx > 0x7FFFFFFF || gy > 65535) return hipErrorInvalidConfiguration;
   if (unit == 8) k_meta_block<uint2><<<dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s>>>(meta, o, nsteps, out);
   else k_meta_block<uint4><<<dim3((unsigned)gx, (unsigned)gy), dim3(256), 0, s>>>(meta, o, nsteps, out);

@@ -122,9 +122,11 @@ __device__ __forceinline__ uint32_t e4m3_rne(float v) {
 // s = fp32(amax / 448) (1 for an all-zero row), then every value x -> e4m3(clamp(x * r)),
 // written in lifted order: out[g 4(NS-1) + 4w + s] = q[g 2NS + 2w + s] (NS = 2: no lift).
 // Codes past the lifted length, up to ldq, are written as zero.
-template <int NS>
+template <int NS, bool VEC>
 __global__ __launch_bounds__(256) void k_quant_lift(const uint16_t* __restrict__ x, int64_t k, int64_t ldx,
                                                     uint8_t* __restrict__ xq, int64_t ldq, float* __restrict__ xs) {
+  // VEC (k % 8 == 0, 16-byte aligned rows): the maximum pass reads 8 values per load and
+  // NS = 4 groups (8 values) are single 16-byte loads; otherwise values move one by one
   constexpr int W = NS - 1;
   __shared__ uint32_t red[4];
   const int64_t row = blockIdx.x;
@@ -132,9 +134,22 @@ __global__ __launch_bounds__(256) void k_quant_lift(const uint16_t* __restrict__
   uint8_t* qr = xq + row * ldq;
   const int tid = threadIdx.x;
   uint32_t mk = 0;
-  for (int64_t i = tid; i < k; i += 256) {
-    const uint32_t key = xr[i] & 0x7FFFu;
-    mk = key > mk ? key : mk;
+  if constexpr (VEC) {
+    for (int64_t i = (int64_t)tid * 8; i < k; i += 256 * 8) {
+      const uint4 v = *reinterpret_cast<const uint4*>(xr + i);
+      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = d[j] & 0x7FFFu, hi = (d[j] >> 16) & 0x7FFFu;
+        mk = lo > mk ? lo : mk;
+        mk = hi > mk ? hi : mk;
+      }
+    }
+  } else {
+    for (int64_t i = tid; i < k; i += 256) {
+      const uint32_t key = xr[i] & 0x7FFFu;
+      mk = key > mk ? key : mk;
+    }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
@@ -151,10 +166,20 @@ __global__ __launch_bounds__(256) void k_quant_lift(const uint16_t* __restrict__
   if (tid == 0) xs[row] = mk == 0 ? 1.0f : amax / 448.0f;
   const int64_t G = k / (2 * NS);
   for (int64_t g = tid; g < G; g += 256) {
+    uint32_t v16[2 * NS];
+    if constexpr (VEC && NS == 4) {
+      const uint4 v = *reinterpret_cast<const uint4*>(xr + g * 8);
+      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { v16[2 * j] = d[j] & 0xFFFFu; v16[2 * j + 1] = d[j] >> 16; }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2 * NS; ++i) v16[i] = xr[g * 2 * NS + i];
+    }
     uint32_t q[2 * NS];
 #pragma unroll
     for (int i = 0; i < 2 * NS; ++i) {
-      const float v = __uint_as_float((uint32_t)xr[g * 2 * NS + i] << 16) * r;
+      const float v = __uint_as_float(v16[i] << 16) * r;
       q[i] = e4m3_rne(fminf(fmaxf(v, -448.0f), 448.0f));
     }
     // 4 (NS - 1) lifted codes = NS - 1 dwords, one per window
@@ -175,8 +200,13 @@ hipError_t launch_quant_lift(int ns, const uint16_t* x, int64_t t, int64_t k, in
   if (t <= 0) return hipSuccess;
   if (t > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)t), block(256);
+  const bool vec = (k % 8) == 0 && (ldx % 8) == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
   switch (ns) {
-#define NM_CASE(NSV) case NSV: k_quant_lift<NSV><<<grid, block, 0, s>>>(x, k, ldx, xq, ldq, xs); break;
+#define NM_CASE(NSV)                                                                           \
+  case NSV:                                                                                    \
+    if (vec) k_quant_lift<NSV, true><<<grid, block, 0, s>>>(x, k, ldx, xq, ldq, xs);           \
+    else k_quant_lift<NSV, false><<<grid, block, 0, s>>>(x, k, ldx, xq, ldq, xs);              \
+    break;
     NM_CASE(2) NM_CASE(3) NM_CASE(4) NM_CASE(5) NM_CASE(6) NM_CASE(7) NM_CASE(8)
 #undef NM_CASE
     default: return hipErrorInvalidValue;
