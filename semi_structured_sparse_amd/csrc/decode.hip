@@ -23,6 +23,8 @@
 //    scratch buffer and a second kernel sums them in split order.  Either way the
 //    summation order is fixed, so results are bit-for-bit reproducible.
 #include <cstdlib>
+#include <cstring>
+#include <type_traits>
 
 #include "nm_device.h"
 #include "nm_launch.h"
@@ -353,6 +355,8 @@ __device__ __forceinline__ void g2lds4(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
 }
 __device__ __forceinline__ int dswz(int r) { return (r >> 1) & 7; }
+// s_waitcnt immediate: vmcnt(n) alone (bits 3:0 and 15:14; expcnt and lgkmcnt at their maxima)
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <int TB> struct Dma {
   static constexpr int WPB = TB == 1 ? 16 : 8;   // waves per workgroup (LDS budget)
@@ -364,10 +368,15 @@ template <int WK> struct DmaFmt {
 };
 constexpr int dma_stage_bytes(int rw, int wk) { return rw * (2048 + (wk == WK_SP24 ? 256 : 0)); }
 
-template <int TB, int RW, int WK, int XL, int NS>
+// XS: the segment's X row (T == 1) is staged in LDS at xs.  `pre` runs before the first
+// weight stages are requested and `mid(n)` after them, n = the requests this wave issued
+// in between (every wave calls this, also with an empty part, so that `mid` may hold a
+// workgroup barrier).
+template <int TB, int RW, int WK, int XL, int NS, bool XS, typename Pre, typename Mid>
 __device__ __forceinline__ void stream_dma(f32x4 (&acc)[RW][TB], const FewSeg& sg, int64_t rbase, int64_t O,
                                            int64_t T, int k0, int k1, int lane, unsigned char* R0,
-                                           unsigned char* R1, unsigned char* R2, unsigned char* R3) {
+                                           unsigned char* R1, unsigned char* R2, unsigned char* R3,
+                                           const uint16_t* xs, Pre&& pre, Mid&& mid) {
   constexpr int CK = Chunk<WK>::K;
   constexpr int U = DmaFmt<WK>::U;
   constexpr int BPE = DmaFmt<WK>::BPE;
@@ -401,7 +410,7 @@ __device__ __forceinline__ void stream_dma(f32x4 (&acc)[RW][TB], const FewSeg& s
 #pragma unroll
   for (int j = 0; j < TB; ++j) {
     const int64_t t = 16 * j + fr;
-    xrow[j] = sg.x + (t < T ? t : T - 1) * sg.ldx;
+    xrow[j] = XS ? xs : sg.x + (t < T ? t : T - 1) * sg.ldx;
   }
 
   auto issue_w = [&](unsigned char* R, int st) {
@@ -427,6 +436,20 @@ __device__ __forceinline__ void stream_dma(f32x4 (&acc)[RW][TB], const FewSeg& s
         if constexpr (WK == WK_SP24) xb.xh[u][j] = load_x8<XL, NS, false>(xrow[j], kpos + u * CK + 32 + 8 * fq, 0);
       }
   };
+  // XS: the stage about to be read has landed once at most `later` stages' requests
+  // (issued after it) are still in flight.  Without XS the waits for the X registers,
+  // which are requested after their stage's weights, order the LDS reads; with X in LDS
+  // nothing would, and the compiler does not order LDS reads after direct-to-LDS loads
+  // on every path, so the waits are explicit.
+  constexpr int OPS = 2 * RW + (WK == WK_SP24 ? RW : 0);   // requests per stage
+  auto stage_ready = [&](auto later) {
+    if constexpr (XS) {
+      constexpr int n = decltype(later)::value * OPS;
+      __builtin_amdgcn_s_waitcnt(vm_wait(n));
+    }
+  };
+  using L3 = std::integral_constant<int, 3>;
+  using L0 = std::integral_constant<int, 0>;
   // the scheduling barriers keep each stage's LDS reads after its own wait (the
   // scheduler would otherwise hoist later stages' reads and force a full drain)
   auto compute = [&](const unsigned char* R, const XB& xb) {
@@ -474,11 +497,15 @@ __device__ __forceinline__ void stream_dma(f32x4 (&acc)[RW][TB], const FewSeg& s
 
   // whole stages need 16-byte aligned compressed rows and 4-byte aligned metadata rows
   const bool aligned = WK != WK_SP24 || ((kcv & 7) == 0 && (mstride & 3) == 0);
-  const int ns = aligned ? (k1 - k0) / SK : 0;
+  const int ns = (aligned && k0 < k1) ? (k1 - k0) / SK : 0;
+  pre();
   if (ns > 0) {
     issue_w(R0, 0);
     if (ns > 1) issue_w(R1, 1);
     if (ns > 2) issue_w(R2, 2);
+  }
+  mid((ns < 3 ? ns : 3) * OPS);
+  if (ns > 0) {
     XB xa, xb;
     load_x(xa, 0);
     int st = 0;
@@ -487,39 +514,47 @@ __device__ __forceinline__ void stream_dma(f32x4 (&acc)[RW][TB], const FewSeg& s
     for (; st + 7 <= ns; st += 4) {
       issue_w(R3, st + 3);
       load_x(xb, st + 1);
+      stage_ready(L3{});
       compute(R0, xa);
       issue_w(R0, st + 4);
       load_x(xa, st + 2);
+      stage_ready(L3{});
       compute(R1, xb);
       issue_w(R1, st + 5);
       load_x(xb, st + 3);
+      stage_ready(L3{});
       compute(R2, xa);
       issue_w(R2, st + 6);
       load_x(xa, st + 4);
+      stage_ready(L3{});
       compute(R3, xb);
     }
     // the last stages (fewer than seven), prefetching only what exists
     for (; st < ns; st += 4) {
       if (st + 3 < ns) issue_w(R3, st + 3);
       if (st + 1 < ns) load_x(xb, st + 1);
+      stage_ready(L0{});
       compute(R0, xa);
       if (st + 1 >= ns) break;
       if (st + 4 < ns) issue_w(R0, st + 4);
       if (st + 2 < ns) load_x(xa, st + 2);
+      stage_ready(L0{});
       compute(R1, xb);
       if (st + 2 >= ns) break;
       if (st + 5 < ns) issue_w(R1, st + 5);
       if (st + 3 < ns) load_x(xb, st + 3);
+      stage_ready(L0{});
       compute(R2, xa);
       if (st + 3 >= ns) break;
       if (st + 6 < ns) issue_w(R2, st + 6);
       if (st + 4 < ns) load_x(xa, st + 4);
+      stage_ready(L0{});
       compute(R3, xb);
     }
   }
   // ragged end (and unaligned compressed rows): register loads, chunk by chunk
   const int kt = k0 + ns * SK;
-  if (kt < k1) {
+  if (k0 < k1 && kt < k1) {
     int64_t orow[RW];
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
@@ -530,10 +565,30 @@ __device__ __forceinline__ void stream_dma(f32x4 (&acc)[RW][TB], const FewSeg& s
   }
 }
 
-template <int TB, int WK0, int XL0, int NS, int WK1>
+// Request an X row of n elements (n % 8 == 0, 16-byte aligned) into LDS by direct-to-LDS
+// loads, 1 KiB (512 elements) per request, requests spread over the waves; lanes past the
+// row end re-read its last 16 bytes into the tail of the last KiB (LDS holds whole KiB).
+__device__ __forceinline__ void stage_row_dma(const uint16_t* __restrict__ src, int n, uint16_t* dst, int wave,
+                                              int wpb, int lane) {
+  const int nch = (n + 511) >> 9;
+  for (int c = wave; c < nch; c += wpb) {
+    int e = c * 512 + lane * 8;
+    e = e <= n - 8 ? e : n - 8;
+    g2lds16(src + e, dst + c * 512);
+  }
+}
+
+// XS (one token): each segment's X row -- xn0 and xn1 elements, the second at the next
+// KiB -- is requested into dynamic LDS before the first weight stages, so its (mostly L2)
+// latency overlaps theirs, and the fragments are read from there.  Register loads of X
+// between the direct-to-LDS weight loads made the compiler drain every request in flight
+// before each use; LDS reads need only the explicit per-stage waits.  Same values, same
+// arithmetic: bit-identical results.
+template <int TB, int WK0, int XL0, int NS, int WK1, bool XS>
 __global__ __launch_bounds__(64 * Dma<TB>::WPB) void k_fewd(FewSeg s0, FewSeg s1, const float* __restrict__ wscale,
                                                            int64_t T, int64_t O, float* __restrict__ y, int64_t ldy,
-                                                           int accumulate, float* __restrict__ part, int splits) {
+                                                           int accumulate, float* __restrict__ part, int splits,
+                                                           int xn0, int xn1) {
   constexpr int RW = Dma<TB>::RW, WPB = Dma<TB>::WPB;
   constexpr int STAGE = dma_stage_bytes(RW, WK0);   // the first segment's kind is the larger one
   static_assert(WK1 == WK_NONE || dma_stage_bytes(RW, WK1) <= STAGE, "stage size");
@@ -557,15 +612,40 @@ __global__ __launch_bounds__(64 * Dma<TB>::WPB) void k_fewd(FewSeg s0, FewSeg s1
   unsigned char* w1 = r1 + wave * STAGE;
   unsigned char* w2 = r2 + wave * STAGE;
   unsigned char* w3 = r3 + wave * STAGE;
+  extern __shared__ __align__(16) uint16_t xs_lds[];
+  const int off1 = ((xn0 + 511) >> 9) << 9;   // whole KiB per staged row
   {
     int k0, k1;
     part_range<WK0>(s0.k, p, P, k0, k1);
-    if (k0 < k1) stream_dma<TB, RW, WK0, XL0, NS>(acc, s0, ob * RB, O, T, k0, k1, lane, w0, w1, w2, w3);
+    auto pre = [&]() {
+      if constexpr (XS) {
+        stage_row_dma(s0.x, xn0, xs_lds, wave, wpb, lane);
+        if constexpr (WK1 != WK_NONE) stage_row_dma(s1.x, xn1, xs_lds + off1, wave, wpb, lane);
+      }
+    };
+    // this wave's X requests have landed once only the n weight requests issued after
+    // them are in flight; then the barrier makes every wave's X visible
+    auto mid = [&](int n) {
+      if constexpr (XS) {
+        switch (n) {   // 0 to 3 stages of 2 or 3 requests
+          case 9: __builtin_amdgcn_s_waitcnt(vm_wait(9)); break;
+          case 6: __builtin_amdgcn_s_waitcnt(vm_wait(6)); break;
+          case 4: __builtin_amdgcn_s_waitcnt(vm_wait(4)); break;
+          case 3: __builtin_amdgcn_s_waitcnt(vm_wait(3)); break;
+          case 2: __builtin_amdgcn_s_waitcnt(vm_wait(2)); break;
+          default: __builtin_amdgcn_s_waitcnt(vm_wait(0)); break;
+        }
+        __builtin_amdgcn_s_barrier();
+      }
+    };
+    stream_dma<TB, RW, WK0, XL0, NS, XS>(acc, s0, ob * RB, O, T, k0, k1, lane, w0, w1, w2, w3, xs_lds, pre, mid);
   }
   if constexpr (WK1 != WK_NONE) {
     int k0, k1;
     part_range<WK1>(s1.k, p, P, k0, k1);
-    if (k0 < k1) stream_dma<TB, RW, WK1, XL_PLAIN, 0>(acc, s1, ob * RB, O, T, k0, k1, lane, w0, w1, w2, w3);
+    if (k0 < k1)
+      stream_dma<TB, RW, WK1, XL_PLAIN, 0, XS>(acc, s1, ob * RB, O, T, k0, k1, lane, w0, w1, w2, w3, xs_lds + off1,
+                                               []() {}, [](int) {});
   }
   // sum the waves' tiles in wave order through stage 0's memory (one 16 x 16 token block
   // at a time); element e = t_local * 16 + (o - RB ob - 16 i)
@@ -917,8 +997,30 @@ hipError_t launch_k(const FewArgs& a, const Plan& p, float* part, hipStream_t s)
   if constexpr (TB <= 2) {
     static_assert(RW == Dma<TB>::RW, "row tiles");
     if (p.wpb > Dma<TB>::WPB) return hipErrorInvalidConfiguration;
-    k_fewd<TB, WK0, XL0, NS, WK1><<<dim3((unsigned)blocks), dim3(64 * p.wpb), 0, s>>>(
-        a.seg[0], s1, a.w_scale, a.t, a.o, a.y, a.ldy, a.accumulate, pp, (int)p.splits);
+    if constexpr (TB == 1) {
+      // one token: stage the X rows in LDS next to the weight rings when they fit
+      // (NM_FEWD_XLDS=0 keeps the register loads, for A/B measurement)
+      // rows of whole 16-byte pieces from 16-byte aligned starts, staged in whole KiB
+      const int64_t xn0 = XL0 == XL_LIFT ? a.seg[0].k / (4 * (NS - 1)) * (2 * NS) : a.seg[0].k;
+      const int64_t xn1 = a.nseg > 1 ? a.seg[1].k : 0;
+      const int64_t xbytes = (((xn0 + 511) >> 9) + ((xn1 + 511) >> 9)) * 1024;
+      const int64_t ring = 4LL * Dma<TB>::WPB * dma_stage_bytes(RW, WK0);
+      auto piece_ok = [](const uint16_t* x, int64_t n) {
+        return n == 0 || (n >= 8 && (n % 8) == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0);
+      };
+      const bool rows_ok = piece_ok(a.seg[0].x, xn0) && (a.nseg < 2 || piece_ok(a.seg[1].x, xn1)) && xn0 > 0;
+      const char* e = std::getenv("NM_FEWD_XLDS");
+      if (a.t == 1 && rows_ok && ring + xbytes <= 163840 && !(e != nullptr && std::strcmp(e, "0") == 0)) {
+        auto kern = k_fewd<TB, WK0, XL0, NS, WK1, true>;
+        hipError_t ae = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)xbytes);
+        if (ae != hipSuccess) return ae;
+        kern<<<dim3((unsigned)blocks), dim3(64 * p.wpb), (size_t)xbytes, s>>>(
+            a.seg[0], s1, a.w_scale, a.t, a.o, a.y, a.ldy, a.accumulate, pp, (int)p.splits, (int)xn0, (int)xn1);
+        return hipGetLastError();
+      }
+    }
+    k_fewd<TB, WK0, XL0, NS, WK1, false><<<dim3((unsigned)blocks), dim3(64 * p.wpb), 0, s>>>(
+        a.seg[0], s1, a.w_scale, a.t, a.o, a.y, a.ldy, a.accumulate, pp, (int)p.splits, 0, 0);
   } else {
     auto kern = k_few<TB, RW, WK0, XL0, NS, WK1>;
     const size_t lds = (size_t)p.wpb * TB * 1024;

@@ -1361,3 +1361,57 @@ def test_measurement_probes():
     assert (outs[0] == 0).all()
     assert np.isfinite(outs[1]).all() and (outs[1] > 0).all()
     assert (outs[2] == 2 * outs[1]).all()
+
+
+@pytest.mark.parametrize("o", [200, 4096])
+def test_one_token_staged_x_bitexact(o):
+    """One token on the weight-streaming kernel: X rows staged in LDS give the same bits as
+    X read from global memory (NM_FEWD_XLDS=0), and match the oracle, for dense bf16 and
+    fp8 weights (8:16 activations, ragged K), plain 2:4, lowered 6:8 and 4:6, and the
+    two-segment hybrid; o = 200 also splits the reduction across workgroups."""
+    print(f"one-token staged X o={o}", flush=True)
+    rng = np.random.default_rng(o + 3)
+    runs = []
+
+    def both(label, fn):
+        with env_set(NM_FEW_ROUTE="stream"):
+            y_lds = fn()
+            with env_set(NM_FEWD_XLDS="0"):
+                y_glb = fn()
+        assert np.array_equal(y_lds.view(np.uint32), y_glb.view(np.uint32)), f"{label}: staged vs global X"
+        runs.append(label)
+        return y_lds
+
+    k = 1056
+    x = synth.student_t_bf16(rng, (1, k), 4.0, 0.5)
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    sx, _ = O.sparsify(x, 8, 16)
+    y = both("8:16 bf16", lambda: run_act(x, w, 8, 16)[0])
+    check_gemm(y, O.gemm(sx, w), sx, w, label="8:16 bf16 staged")
+    q, sc = synth.fp8_e4m3_quantize_rows(w)
+    y = both("8:16 fp8", lambda: run_act(x, None, 8, 16, w8=q, s8=sc)[0])
+    wdeq = O.fp8_e4m3_to_f64(q) * sc[:, None].astype(np.float64)
+    check_gemm(y, O.spmm_act_fp8(x, q, sc, 8, 16), sx, wdeq, label="8:16 fp8 staged")
+    v, mt = gpu_compress_2of4(w)
+    ws24, _ = O.sparsify(w, 2, 4)
+    y = both("w 2:4", lambda: run_w(S.NM_W_COMPRESSED, x, v, mt, o, k))
+    check_gemm(y, O.gemm(x, ws24), x, ws24, label="w 2:4 staged")
+    for ns in (4, 3):
+        kk = 1008   # a multiple of 2 ns for both
+        xs_ = np.ascontiguousarray(x[:, :kk])
+        ws_ = np.ascontiguousarray(w[:, :kk])
+        vp, mp = slide_pack_gpu(ws_, ns)
+        pr, _ = O.sparsify(ws_, 2 * ns - 2, 2 * ns)
+        y = both(f"slide ns={ns}", lambda: run_w(S.NM_W_SLIDE, xs_, vp, mp, o, kk, ns=ns))
+        check_gemm(y, O.gemm(xs_, pr), xs_, pr, label=f"slide ns={ns} staged")
+    kh, kd = 1024, 256
+    xh = np.ascontiguousarray(x[:, :kh])
+    wh0 = np.ascontiguousarray(w[:, :kh])
+    sc_, dc_, wv, wm, wdd = hybrid_pack_gpu(wh0, kd)
+    sync()
+    sp, de, hv, hi, hwd = O.hybrid_pack(wh0, kd)
+    whh = wh0.copy()
+    whh[:, sp] = O.decompress(hv, hi, 2, 4, kh - kd)
+    y = both("hybrid", lambda: run_hybrid(xh, sc_, kh - kd, dc_, kd, wv, wm, wdd, o, ldwd=kd))
+    check_gemm(y, O.hybrid_gemm(xh, sp, de, hv, hi, hwd), xh, whh, label="hybrid staged")
+    assert len(runs) == 6
