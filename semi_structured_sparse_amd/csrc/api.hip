@@ -598,6 +598,17 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
                                                 a->y, a->accumulate, a->x_mask_out, (float*)a->workspace,
                                                 a->workspace_bytes, s));
       }
+      // ACT_DYNAMIC, one token, no mask asked for, n = m/2: the weight-streaming kernel
+      // selects inside the X row it stages, with no separate select pass
+      if (T == 1 && have_ws && a->x_mask_out == nullptr && 2 * a->n == a->m) {
+        nml::GemmArgs g1 = g;
+        g1.x = (const uint16_t*)a->x; g1.ldx = a->ldx; g1.prologue = nml::PRO_NONE;
+        if (!few_use_tile(g1)) {
+          nml::FewArgs f = few_dense_args(g1);
+          f.sel_m = a->m;
+          if (nml::few_select_in_kernel(f)) return hip_status(nml::launch_few(f, part, part_avail, s));
+        }
+      }
       // ACT_DYNAMIC, few tokens: select into S(X), then stream the weights
       if (use_few(T) && have_ws) {
         uint16_t* sx = (uint16_t*)a->workspace;

@@ -561,7 +561,14 @@ __device__ __forceinline__ void stream_dma(f32x4 (&acc)[RW][TB], const FewSeg& s
       const int64_t o = rbase + 16 * i + fr;
       orow[i] = o < O ? o : O - 1;
     }
-    stream_seg<TB, RW, WK, XL, NS>(acc, sg, orow, T, kt, k1, lane);
+    if constexpr (XS) {
+      // the staged row (selected in place when the kernel selects): one token, row 0
+      FewSeg sl = sg;
+      sl.x = xs;
+      stream_seg<TB, RW, WK, XL, NS>(acc, sl, orow, T, kt, k1, lane);
+    } else {
+      stream_seg<TB, RW, WK, XL, NS>(acc, sg, orow, T, kt, k1, lane);
+    }
   }
 }
 
@@ -584,7 +591,10 @@ __device__ __forceinline__ void stage_row_dma(const uint16_t* __restrict__ src, 
 // between the direct-to-LDS weight loads made the compiler drain every request in flight
 // before each use; LDS reads need only the explicit per-stage waits.  Same values, same
 // arithmetic: bit-identical results.
-template <int TB, int WK0, int XL0, int NS, int WK1, bool XS>
+// SELM > 0 (with XS, one plain segment): the staged row is X itself; after it lands every
+// workgroup keeps the SELM/2 largest magnitudes of each SELM-group in place (the select
+// pass's ranking, ties to the lower index) before the first multiply.
+template <int TB, int WK0, int XL0, int NS, int WK1, bool XS, int SELM = 0>
 __global__ __launch_bounds__(64 * Dma<TB>::WPB) void k_fewd(FewSeg s0, FewSeg s1, const float* __restrict__ wscale,
                                                            int64_t T, int64_t O, float* __restrict__ y, int64_t ldy,
                                                            int accumulate, float* __restrict__ part, int splits,
@@ -636,6 +646,25 @@ __global__ __launch_bounds__(64 * Dma<TB>::WPB) void k_fewd(FewSeg s0, FewSeg s1
           default: __builtin_amdgcn_s_waitcnt(vm_wait(0)); break;
         }
         __builtin_amdgcn_s_barrier();
+        if constexpr (SELM > 0) {
+          // the groups are whole (xn0 % SELM == 0); LDS writes done before the barrier,
+          // weight requests left in flight
+          for (int g = threadIdx.x; g < xn0 / SELM; g += blockDim.x) {
+            uint32_t* gp = reinterpret_cast<uint32_t*>(xs_lds + g * SELM);
+            uint32_t d[SELM / 2];
+#pragma unroll
+            for (int q = 0; q < SELM / 2; ++q) d[q] = gp[q];
+            const uint32_t keep = topn_bits_n<SELM, SELM / 2>(d);
+#pragma unroll
+            for (int q = 0; q < SELM / 2; ++q) {
+              const uint32_t lo = ((keep >> (2 * q)) & 1u) ? 0x0000FFFFu : 0u;
+              const uint32_t hi = ((keep >> (2 * q + 1)) & 1u) ? 0xFFFF0000u : 0u;
+              gp[q] = d[q] & (lo | hi);
+            }
+          }
+          __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes done
+          __builtin_amdgcn_s_barrier();
+        }
       }
     };
     stream_dma<TB, RW, WK0, XL0, NS, XS>(acc, s0, ob * RB, O, T, k0, k1, lane, w0, w1, w2, w3, xs_lds, pre, mid);
@@ -1012,6 +1041,18 @@ hipError_t launch_k(const FewArgs& a, const Plan& p, float* part, hipStream_t s)
       const char* e = std::getenv("NM_FEWD_XLDS");
       if (a.t == 1 && rows_ok && ring + xbytes <= 163840 && !(e != nullptr && std::strcmp(e, "0") == 0)) {
         auto kern = k_fewd<TB, WK0, XL0, NS, WK1, true>;
+        if constexpr (XL0 == XL_PLAIN && WK1 == WK_NONE && (WK0 == WK_BF16 || WK0 == WK_FP8)) {
+          switch (a.sel_m) {
+            case 0: break;
+            case 4: kern = k_fewd<TB, WK0, XL0, NS, WK1, true, 4>; break;
+            case 8: kern = k_fewd<TB, WK0, XL0, NS, WK1, true, 8>; break;
+            case 16: kern = k_fewd<TB, WK0, XL0, NS, WK1, true, 16>; break;
+            case 32: kern = k_fewd<TB, WK0, XL0, NS, WK1, true, 32>; break;
+            default: return hipErrorInvalidValue;
+          }
+        } else if (a.sel_m != 0) {
+          return hipErrorInvalidValue;
+        }
         hipError_t ae = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)xbytes);
         if (ae != hipSuccess) return ae;
         kern<<<dim3((unsigned)blocks), dim3(64 * p.wpb), (size_t)xbytes, s>>>(
@@ -1019,6 +1060,7 @@ hipError_t launch_k(const FewArgs& a, const Plan& p, float* part, hipStream_t s)
         return hipGetLastError();
       }
     }
+    if (a.sel_m != 0) return hipErrorInvalidValue;   // selection needs the staged row
     k_fewd<TB, WK0, XL0, NS, WK1, false><<<dim3((unsigned)blocks), dim3(64 * p.wpb), 0, s>>>(
         a.seg[0], s1, a.w_scale, a.t, a.o, a.y, a.ldy, a.accumulate, pp, (int)p.splits, 0, 0);
   } else {
@@ -1028,6 +1070,7 @@ hipError_t launch_k(const FewArgs& a, const Plan& p, float* part, hipStream_t s)
       hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
     }
+    if (a.sel_m != 0) return hipErrorInvalidValue;
     kern<<<dim3((unsigned)blocks), dim3(64 * p.wpb), lds, s>>>(a.seg[0], s1, a.w_scale, a.t, a.o, a.y, a.ldy,
                                                                a.accumulate, pp, (int)p.splits);
   }
@@ -1067,11 +1110,30 @@ int64_t few_partial_bytes(const FewArgs& a) {
   return p.splits > 1 ? p.splits * a.t * a.o * 4 : 0;
 }
 
+bool few_select_in_kernel(const FewArgs& a) {
+  const char* e = std::getenv("NM_FEW_SELECT");
+  if (e != nullptr && std::strcmp(e, "0") == 0) return false;
+  const char* ex = std::getenv("NM_FEWD_XLDS");
+  if (ex != nullptr && std::strcmp(ex, "0") == 0) return false;
+  if (a.t != 1 || a.nseg != 1 || a.o <= 0) return false;
+  const int m = a.sel_m;
+  if (m != 4 && m != 8 && m != 16 && m != 32) return false;
+  const FewSeg& sg = a.seg[0];
+  if (sg.loader != XL_PLAIN || (sg.w_kind != WK_BF16 && sg.w_kind != WK_FP8)) return false;
+  const int64_t n = sg.k;
+  if (n < 8 || n % 8 != 0 || n % m != 0 || (reinterpret_cast<uintptr_t>(sg.x) & 15) != 0) return false;
+  // the staged row beside the weight ring (one token block: dense stages of 2 KiB)
+  const int64_t ring = 4LL * Dma<1>::WPB * dma_stage_bytes(1, sg.w_kind);
+  if (ring + ((n + 511) >> 9) * 1024 > 163840) return false;
+  return make_plan(a, true).tb == 1;
+}
+
 hipError_t launch_few(const FewArgs& a, float* part, int64_t part_bytes, hipStream_t s) {
   if (a.t > 128 || a.nseg < 1 || a.nseg > 2) return hipErrorInvalidValue;
   for (int i = 0; i < a.nseg; ++i)   // reduction indices are 32-bit inside the kernel
     if (a.seg[i].k > 0x3FFFFFFF) return hipErrorInvalidValue;
   if (a.t == 0 || a.o == 0) return hipSuccess;
+  if (a.sel_m != 0 && !few_select_in_kernel(a)) return hipErrorInvalidValue;
   Plan p = make_plan(a, part != nullptr);
   if (p.splits > 1 && part_bytes < p.splits * a.t * a.o * 4) p = make_plan(a, false);
   const FewSeg& s0 = a.seg[0];

@@ -144,7 +144,12 @@ struct FewArgs {
   float* y;
   int64_t ldy;
   int accumulate;
+  int sel_m;              // > 0: seg[0].x is X itself; keep the m/2 largest of every m (see below)
 };
+// One token, one plain dense segment (bf16 or fp8 W), m in {4, 8, 16, 32}: whether
+// launch_few applies the n = m/2 selection to the X row inside the product (the row
+// staged in LDS), so that no separate select pass is needed.  NM_FEW_SELECT=0: never.
+bool few_select_in_kernel(const FewArgs& a);
 // Scratch bytes of fp32 partial sums the preferred launch uses (0: single pass).
 int64_t few_partial_bytes(const FewArgs& a);
 // part: scratch of part_bytes bytes or null; with less than few_partial_bytes(a) the

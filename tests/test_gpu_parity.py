@@ -272,7 +272,7 @@ def test_lift_bitexact(ns):
 
 # -------------------------------------------------------------- activation spmm ---
 
-def run_act(x, w, n, m, route=None, w8=None, s8=None, workspace=True, accumulate=0, y0=None):
+def run_act(x, w, n, m, route=None, w8=None, s8=None, workspace=True, accumulate=0, y0=None, want_mask=True):
     t, k = x.shape
     o = w.shape[0] if w is not None else w8.shape[0]
     xd = dev(x)
@@ -281,7 +281,7 @@ def run_act(x, w, n, m, route=None, w8=None, s8=None, workspace=True, accumulate
     else:
         wd_, dtype, sd = dev(w), S.NM_W_BF16, None
     y = dev(y0.astype(np.float32)) if y0 is not None else empty((t, o), np.float32, fill=float("nan"))
-    mask = empty((t, (k + 31) // 32), np.uint32, fill=-1)
+    mask = empty((t, (k + 31) // 32), np.uint32, fill=-1) if want_mask else None
     a = S.make_spmm_args(S.NM_ACT_DYNAMIC, t, o, k, xd, wd_, y, n=n, m=m, w_dtype=dtype, w_scale=sd,
                          x_mask_out=mask, accumulate=accumulate)
     ws = None
@@ -300,7 +300,7 @@ def run_act(x, w, n, m, route=None, w8=None, s8=None, workspace=True, accumulate
             os.environ.pop("NM_ACT_ROUTE", None)
         else:
             os.environ["NM_ACT_ROUTE"] = old
-    return host(y, np.float32), host(mask, np.uint32)
+    return host(y, np.float32), (host(mask, np.uint32) if mask is not None else None)
 
 
 @pytest.mark.parametrize("n,m", [(8, 16), (16, 32), (4, 8), (2, 4), (1, 4), (6, 8)])
@@ -1415,3 +1415,35 @@ def test_one_token_staged_x_bitexact(o):
     y = both("hybrid", lambda: run_hybrid(xh, sc_, kh - kd, dc_, kd, wv, wm, wdd, o, ldwd=kd))
     check_gemm(y, O.hybrid_gemm(xh, sp, de, hv, hi, hwd), xh, whh, label="hybrid staged")
     assert len(runs) == 6
+
+
+@pytest.mark.parametrize("o", [200, 4096])
+@pytest.mark.parametrize("m", [4, 8, 16, 32])
+def test_one_token_select_in_kernel(m, o):
+    """One token, n = m/2, no mask asked for: the weight-streaming kernel selects inside
+    the X row it stages in LDS.  Same bits as the separate select pass followed by the
+    product (NM_FEW_SELECT=0), and within tolerance of the oracle, for bf16 and fp8
+    weights; one row is Student-t, the other has many equal magnitudes (ties to the
+    lower index)."""
+    print(f"one-token select in kernel m={m} o={o}", flush=True)
+    rng = np.random.default_rng(m * 100 + o)
+    k = 1056 if m <= 16 else 1024
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    q, sc = synth.fp8_e4m3_quantize_rows(w)
+    wdeq = O.fp8_e4m3_to_f64(q) * sc[:, None].astype(np.float64)
+    xt = synth.student_t_bf16(rng, (1, k), 4.0, 0.5)
+    # magnitudes from a few values and both signs: many ties inside each group
+    vals = np.array([0x3F80, 0x4000, 0xBF80, 0xC000, 0x3F00, 0x0000, 0x8000], dtype=np.uint16)
+    xtie = vals[rng.integers(0, len(vals), size=(1, k))].astype(np.uint16)
+    for label, x in (("student-t", xt), ("ties", xtie)):
+        sx, _ = O.sparsify(x, m // 2, m)
+        with env_set(NM_FEW_ROUTE="stream"):
+            y_in = run_act(x, w, m // 2, m, want_mask=False)[0]
+            y8_in = run_act(x, None, m // 2, m, w8=q, s8=sc, want_mask=False)[0]
+            with env_set(NM_FEW_SELECT="0"):
+                y_sep = run_act(x, w, m // 2, m, want_mask=False)[0]
+                y8_sep = run_act(x, None, m // 2, m, w8=q, s8=sc, want_mask=False)[0]
+        assert np.array_equal(y_in.view(np.uint32), y_sep.view(np.uint32)), f"{label} bf16: in-kernel vs separate"
+        assert np.array_equal(y8_in.view(np.uint32), y8_sep.view(np.uint32)), f"{label} fp8: in-kernel vs separate"
+        check_gemm(y_in, O.gemm(sx, w), sx, w, label=f"{label} {m // 2}:{m} bf16 in-kernel select")
+        check_gemm(y8_in, O.spmm_act_fp8(x, q, sc, m // 2, m), sx, wdeq, label=f"{label} {m // 2}:{m} fp8")
