@@ -1447,3 +1447,15 @@ def test_one_token_select_in_kernel(m, o):
         assert np.array_equal(y8_in.view(np.uint32), y8_sep.view(np.uint32)), f"{label} fp8: in-kernel vs separate"
         check_gemm(y_in, O.gemm(sx, w), sx, w, label=f"{label} {m // 2}:{m} bf16 in-kernel select")
         check_gemm(y8_in, O.spmm_act_fp8(x, q, sc, m // 2, m), sx, wdeq, label=f"{label} {m // 2}:{m} fp8")
+    # accumulate into a nonzero y, both weight types
+    y0 = rng.standard_normal((1, o)).astype(np.float32)
+    with env_set(NM_FEW_ROUTE="stream"):
+        ya = run_act(xt, w, m // 2, m, accumulate=1, y0=y0, want_mask=False)[0]
+        ya8 = run_act(xt, None, m // 2, m, w8=q, s8=sc, accumulate=1, y0=y0, want_mask=False)[0]
+        with env_set(NM_FEW_SELECT="0"):
+            yb = run_act(xt, w, m // 2, m, accumulate=1, y0=y0, want_mask=False)[0]
+            yb8 = run_act(xt, None, m // 2, m, w8=q, s8=sc, accumulate=1, y0=y0, want_mask=False)[0]
+    assert np.array_equal(ya.view(np.uint32), yb.view(np.uint32)), "accumulate bf16: in-kernel vs separate"
+    assert np.array_equal(ya8.view(np.uint32), yb8.view(np.uint32)), "accumulate fp8: in-kernel vs separate"
+    sxt, _ = O.sparsify(xt, m // 2, m)
+    check_gemm(ya.astype(np.float64) - y0, O.gemm(sxt, w), sxt, w, label=f"{m // 2}:{m} in-kernel select accumulate")
