@@ -1459,3 +1459,63 @@ def test_one_token_select_in_kernel(m, o):
     assert np.array_equal(ya8.view(np.uint32), yb8.view(np.uint32)), "accumulate fp8: in-kernel vs separate"
     sxt, _ = O.sparsify(xt, m // 2, m)
     check_gemm(ya.astype(np.float64) - y0, O.gemm(sxt, w), sxt, w, label=f"{m // 2}:{m} in-kernel select accumulate")
+
+
+def test_one_token_graph_replays():
+    """One-token calls captured in a graph (X staged in LDS, selection inside the product;
+    staged 2:4 weights; the hybrid with its permute): three replays, with eager calls and
+    a synchronization between them, each bit-identical to the eager result."""
+    print("one-token graph replays", flush=True)
+    import torch
+    rng = np.random.default_rng(77)
+    o, k = 512, 1024
+    x = synth.student_t_bf16(rng, (1, k), 4.0, 0.5)
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    xd, wd_ = dev(x), dev(w)
+    calls = []
+    ya = empty((1, o), np.float32)
+    a = S.make_spmm_args(S.NM_ACT_DYNAMIC, 1, o, k, xd, wd_, ya, n=8, m=16)
+    wsa = empty((max(S.nm_spmm_workspace_size(a), 16),), np.uint8)
+    a.workspace, a.workspace_bytes = wsa.data_ptr(), S.nm_spmm_workspace_size(a)
+    calls.append(("8:16 act", lambda: S.nm_spmm(a), ya))
+    v, mt = gpu_compress_2of4(w)
+    yw = empty((1, o), np.float32)
+    b = S.make_spmm_args(S.NM_W_COMPRESSED, 1, o, k, xd, v, yw, w_meta=mt, w_meta_fmt=S.NM_META_2BIT)
+    wsb = empty((max(S.nm_spmm_workspace_size(b), 16),), np.uint8)
+    b.workspace, b.workspace_bytes = wsb.data_ptr(), S.nm_spmm_workspace_size(b)
+    calls.append(("w 2:4", lambda: S.nm_spmm(b), yw))
+    kd = 256
+    sc_, dc_, wv, wm, wdd = hybrid_pack_gpu(w, kd)
+    yh = empty((1, o), np.float32)
+    nbh = S.nm_hybrid_gemm_workspace_size(1, k - kd, kd, o, True)
+    wsh = empty((max(nbh, 16),), np.uint8)
+    calls.append(("hybrid", lambda: S.nm_hybrid_gemm(xd, sc_, k - kd, dc_, kd, wv, wm, S.NM_META_2BIT, wdd, o, yh,
+                                                     ldwd=kd, workspace=wsh, workspace_bytes=nbh), yh))
+    with env_set(NM_FEW_ROUTE="stream"):
+        eager = []
+        for _, fn, y in calls:
+            fn()
+            sync()
+            eager.append(host(y, np.float32).copy())
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(st):
+            for _, fn, _ in calls:
+                fn()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=st):
+            for _, fn, _ in calls:
+                fn()
+        torch.cuda.synchronize()
+        for rep in range(3):
+            for _, _, y in calls:
+                y.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            for (label, _, y), ref in zip(calls, eager):
+                assert np.array_equal(host(y, np.float32).view(np.uint32), ref.view(np.uint32)), f"{label} replay {rep}"
+            for _, fn, _ in calls:   # eager work between the replays
+                fn()
+            sync()
+        del g
