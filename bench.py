@@ -55,37 +55,39 @@ def measured_traffic(tokens):
     return d.get("bytes_per_launch")
 
 
-def cpu_baseline(x_bits, w_bits, n, m, budget_s=12.0):
-    """The oracle, as it stands, on a bounded sample of token rows of the same layer."""
-    import numpy as np
-
+def cpu_baseline(x_bits, w_bits, n, m, budget_s=15.0):
+    """The oracle, as it stands, on a bounded sample of token rows of the same layer: its
+    selection (numpy, single-threaded element-wise work) and its plain C product (one fp32
+    accumulator per output, ascending k, one thread), called once on the whole sample.
+    BLAS thread pools are held at one thread around the call."""
     import oracle as O
 
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # noqa: BLE001
-        cores = int(os.environ.get("OMP_NUM_THREADS", "1"))
-    rows = 32
-    t0 = time.perf_counter()
-    O.spmm_act(x_bits[:rows], w_bits, n, m)
-    dt = time.perf_counter() - t0
-    total_rows, total_t = rows, dt
-    # grow the sample until about budget_s of CPU work has been timed
-    while total_t < budget_s and total_rows < x_bits.shape[0]:
-        r = int(min(max(rows * 2, 32), x_bits.shape[0] - total_rows, 4096))
-        if r <= 0:
-            break
-        t0 = time.perf_counter()
-        O.spmm_act(x_bits[total_rows:total_rows + r], w_bits, n, m)
-        total_t += time.perf_counter() - t0
-        total_rows += r
-        rows = r
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # noqa: BLE001
+        threadpool_limits = None
     o, k = w_bits.shape
-    flops = 2.0 * total_rows * o * k
-    return {"value": round(flops / total_t / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{total_rows} of {x_bits.shape[0]} token rows of the same 8:16 layer "
-                      f"(numpy fp64 select + matmul), {total_t:.1f} s"}
+
+    def run(rows):
+        if threadpool_limits is not None:
+            with threadpool_limits(limits=1):
+                t0 = time.perf_counter()
+                O.spmm_act(x_bits[:rows], w_bits, n, m)
+                return time.perf_counter() - t0
+        t0 = time.perf_counter()
+        O.spmm_act(x_bits[:rows], w_bits, n, m)
+        return time.perf_counter() - t0
+
+    # two small calls size the sample (a fixed part, the weights' conversion, and a part per
+    # row), then one call of about budget_s is timed
+    t8, t24 = run(8), run(24)
+    per_row = max((t24 - t8) / 16, 1e-4)
+    rows = int(max(8, min(x_bits.shape[0], (budget_s - max(t8 - 8 * per_row, 0.0)) / per_row)))
+    total_t = run(rows)
+    flops = 2.0 * rows * o * k
+    return {"value": round(flops / total_t / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} of {x_bits.shape[0]} token rows, 8:16 select + fp32 C product, 1 thread, "
+                      f"{total_t:.1f} s"}
 
 
 def gpu_time_us(torch, fn, graph, iters=10, warm=3, settle_ms=30.0):
@@ -176,6 +178,7 @@ def measure_ceilings(torch, S):
     """Achievable ceilings on this machine: a plain streaming read over distinct buffers
     (cold in the 256 MB Infinity Cache) and over one buffer read again, and the bf16
     matrix-instruction rate on register operands, each after the clock has settled."""
+    from semi_structured_sparse_amd import probe as S  # noqa: N811  (measurement helpers)
     nb = 117440512
     bufs = [torch.empty((nb // 4,), dtype=torch.int32, device="cuda").fill_(b) for b in range(6)]
     sink = torch.empty((S.nm_probe_sink_bytes() // 4,), dtype=torch.int32, device="cuda")
@@ -200,19 +203,19 @@ def measure_rows(torch, S, synth, np):
         np.int16 if a.dtype == np.uint16 else (np.int32 if a.dtype == np.int32 else np.uint8))).cuda()
     f32 = lambda *sh: torch.empty(sh, dtype=torch.float32, device="cuda")
     buf = lambda nb, dt=torch.uint8: torch.empty((max(int(nb), 16),), dtype=dt, device="cuda")
-    rows = []
+    rows = {}
 
-    def add(cfg, t, path, us, f_dense, f_exec, nbytes, bound=None, peak=PEAK_BF16_TFLOPS):
-        r = {"cfg": cfg, "tokens": t, "path": path, "us": round(us, 2),
-             "dense_equiv_tflops": round(f_dense / us / 1e6, 2), "executed_tflops": round(f_exec / us / 1e6, 2),
-             "algorithmic_bytes": int(nbytes), "GBps": round(nbytes / us / 1e3, 1)}
+    def add(cfg, t, path, us, f_dense, f_exec, nbytes, bound=None, peak=PEAK_BF16_TFLOPS, key=None):
+        """Log the row in full (stderr); keep [us, % of the bounding roof, roof] under a short
+        key for the JSON line: roof "h" = 8 TB/s HBM, "m" = bf16 matrix peak, "m8" = fp8."""
+        gbps = nbytes / us / 1e3
         if bound == "hbm" or (bound is None and t <= 128):
-            r.update(bound="hbm", frac=round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4))
+            roof, frac = "h", gbps / PEAK_HBM_GBS
         else:
-            r.update(bound="mfma", frac=round(f_exec / us / 1e6 / peak, 4))
-        rows.append(r)
-        log(f"  {cfg:5s} T={t:5d} {path:34s} {us:9.1f} us  {r['executed_tflops']:8.1f} TF/s exec  "
-            f"{r['GBps']:7.0f} GB/s  {r['bound']} {100 * r['frac']:.1f}%")
+            roof, frac = ("m8" if peak == PEAK_FP8_TFLOPS else "m"), f_exec / us / 1e6 / peak
+        rows[key or f"{cfg}.{t}"] = [round(us, 1), round(100 * frac, 1), roof]
+        log(f"  {cfg:5s} T={t:5d} {path:34s} {us:9.1f} us  {f_dense / us / 1e6:8.1f} TF/s dense-eq  "
+            f"{f_exec / us / 1e6:8.1f} TF/s exec  {gbps:7.0f} GB/s  {roof} {100 * frac:.1f}%  [{key or cfg}]")
 
     def spmm(a, ws_holder):
         nb = S.nm_spmm_workspace_size(a)
@@ -239,7 +242,7 @@ def measure_rows(torch, S, synth, np):
     y = f32(64, 512)
     fn = spmm(S.make_spmm_args(S.NM_ACT_DYNAMIC, 64, 512, 512, x1, w1, y, n=2, m=4), keep)
     add("cfg1", 64, "2:4 act (select + product)", gpu_time_us(torch, fn, True), 2.0 * 64 * 512 * 512,
-        2.0 * 64 * 512 * 512, 64 * 512 * 2 + 512 * 512 * 2 + 64 * 512 * 4)
+        2.0 * 64 * 512 * 512, 64 * 512 * 2 + 512 * 512 * 2 + 64 * 512 * 4, key="c1.64")
     # cfg2: 8:16 activations, down-projection 4096 x 14336
     d = synth.mlp_down_8of16(t_max=8192)
     x2, w2 = dev(d["x"]), dev(d["w"])
@@ -249,7 +252,7 @@ def measure_rows(torch, S, synth, np):
     fns = rot_spmm(lambda wk: S.make_spmm_args(S.NM_ACT_DYNAMIC, 1, O2, K2, x2[:1], w2, y, n=8, m=16, w_kmajor=wk),
                    (wk2,), O2 * K2 * 2, keep)
     add("cfg2", 1, "8:16 act, K-major gather", gpu_time_rot_us(torch, fns), 2.0 * O2 * K2, 2.0 * O2 * K2 / 2,
-        K2 // 2 * O2 * 2 + K2 * 2 + O2 * 4)
+        K2 // 2 * O2 * 2 + K2 * 2 + O2 * 4, key="c2.1g")
     keep.clear()
     del wk2
     # the select kernel alone at 8192 tokens: S(X) + mask, and values + u8 index + mask
@@ -260,15 +263,15 @@ def measure_rows(torch, S, synth, np):
     ix = torch.empty((t, K2 // 2), dtype=torch.uint8, device="cuda")
     fn = lambda: S.nm_sparsify(x2, 8, 16, sxb, mk, check=False)
     add("cfg2", t, "select alone: S(X) + mask", gpu_time_us(torch, fn, False), 0.0, 0.0,
-        t * K2 * 2 + t * K2 * 2 + t * K2 // 8, bound="hbm")
+        t * K2 * 2 + t * K2 * 2 + t * K2 // 8, bound="hbm", key="c2.sel")
     fn = lambda: S.nm_compress(x2, 8, 16, vv, ix, S.NM_META_U8, mask=mk, check=False)
     add("cfg2", t, "select alone: values + u8 idx + mask", gpu_time_us(torch, fn, False), 0.0, 0.0,
-        t * K2 * 2 + t * K2 // 2 * 3 + t * K2 // 8, bound="hbm")
+        t * K2 * 2 + t * K2 // 2 * 3 + t * K2 // 8, bound="hbm", key="c2.cmp")
     # scored selection: activations weighted by the fp32 L2 norm of each weight column
     cs = w2.view(torch.bfloat16).float().pow(2).sum(0).sqrt().contiguous()
     fn = lambda: S.nm_sparsify_scored(x2, 8, 16, cs, S.NM_SCORE_ACT_WEIGHTED, sxb, mk, check=False)
     add("cfg2", t, "select alone, |x| * weight-column norm: S(X) + mask", gpu_time_us(torch, fn, False), 0.0, 0.0,
-        t * K2 * 2 + t * K2 * 2 + t * K2 // 8 + K2 * 4, bound="hbm")
+        t * K2 * 2 + t * K2 * 2 + t * K2 // 8 + K2 * 4, bound="hbm", key="c2.selsc")
     del cs
     del sxb, mk, vv, ix
     for t in (1, 16, 128, 2048, 8192):
@@ -281,7 +284,7 @@ def measure_rows(torch, S, synth, np):
         else:
             us = gpu_time_us(torch, spmm(S.make_spmm_args(S.NM_ACT_DYNAMIC, t, O2, K2, x2[:t], w2, y, n=8, m=16),
                                          keep), False)
-        add("cfg2", t, "8:16 act (select + product)", us, f, f, t * K2 * 2 + O2 * K2 * 2 + t * O2 * 4)
+        add("cfg2", t, "8:16 act (select + product)", us, f, f, t * K2 * 2 + O2 * K2 * 2 + t * O2 * 4, key=f"c2.{t}")
         keep.clear()
     del x2, w2
     # cfg3: 6:8 weights lowered to 2:4, 4096 x 4096, lifted activations
@@ -302,7 +305,7 @@ def measure_rows(torch, S, synth, np):
         else:
             us = gpu_time_us(torch, spmm(mk3(vp, mp), keep), False)
         add("cfg3", t, "6:8 W lowered to 2:4, lifted X", us, 2.0 * t * 4096 * 4096,
-            2.0 * t * 4096 * 3072, 4096 * 3072 * 2 + 4096 * 768 + t * 4096 * 2 + t * 4096 * 4)
+            2.0 * t * 4096 * 3072, 4096 * 3072 * 2 + 4096 * 768 + t * 4096 * 2 + t * 4096 * 4, key=f"c3.{t}")
         keep.clear()
     # the same layer with fp8 weights (per-row codes, the input format) and activations
     # quantized per token to fp8 inside the call (fused with the lift), on the fp8 sparse
@@ -320,7 +323,7 @@ def measure_rows(torch, S, synth, np):
         else:
             us = gpu_time_us(torch, spmm(mk8(q8d, s8d, mp), keep), False)
         add("cfg3", t, "6:8 lowered, fp8 W + per-token fp8 X", us, 2.0 * t * 4096 * 4096, 2.0 * t * 4096 * 3072,
-            wb8 + t * 4096 * 2 + t * 4096 * 4, peak=PEAK_FP8_TFLOPS)
+            wb8 + t * 4096 * 2 + t * 4096 * 4, peak=PEAK_FP8_TFLOPS, key=f"c3.{t}f8")
         keep.clear()
     del q8d, s8d
     del w3, x3, v, i8, vp, mp
@@ -351,7 +354,7 @@ def measure_rows(torch, S, synth, np):
         else:
             us = gpu_time_us(torch, call(wv, wm, wd), False)
         add("cfg4", t, "hybrid 2:4 + 25% dense columns", us, 2.0 * t * o4 * k4,
-            2.0 * t * o4 * (kd + ks / 2), wb4 + t * k4 * 2 + t * o4 * 4)
+            2.0 * t * o4 * (kd + ks / 2), wb4 + t * k4 * 2 + t * o4 * 4, key=f"c4.{t}")
     del w4, x4, sc, dc, wv, wm, wd
     # cfg5: one 8B-shaped layer, 16:32 and 8:16, bf16 and fp8 weights, T = 64 and 8192
     lay = synth.transformer_layer(t_max=8192, with_fp8=True)
@@ -384,7 +387,8 @@ def measure_rows(torch, S, synth, np):
                     tot_f += 2.0 * t * o_ * k_
                     tot_b += wb + t * k_ * 2 + t * o_ * 4
                     keep.clear()
-                add("cfg5", t, f"layer {n}:{m} act, {kind} W", tot_us, tot_f, tot_f, tot_b)
+                add("cfg5", t, f"layer {n}:{m} act, {kind} W", tot_us, tot_f, tot_f, tot_b,
+                    key=f"c5.{t}.{n}of{m}{'f8' if kind == 'fp8' else ''}")
     # the same layer with the linears that share an input concatenated along the output
     # dimension (q|k|v: 6144 x 4096, gate|up: 28672 x 4096): four calls instead of seven,
     # one selection per input stream, identical outputs
@@ -418,7 +422,8 @@ def measure_rows(torch, S, synth, np):
                     tot_f += 2.0 * t * o_ * k_
                     tot_b += wb + t * k_ * 2 + t * o_ * 4
                     keep.clear()
-                add("cfg5", t, f"layer {n}:{m} act, {kind} W, fused qkv + gate|up", tot_us, tot_f, tot_f, tot_b)
+                add("cfg5", t, f"layer {n}:{m} act, {kind} W, fused qkv + gate|up", tot_us, tot_f, tot_f, tot_b,
+                    key=f"c5.{t}.{n}of{m}{'f8' if kind == 'fp8' else ''}.cat")
     # Spense MLP of the same layer: 25% of the intermediate indices dense, chosen by the
     # loss-aware score (Hessian roots from the layer's input streams) and moved to the end;
     # gate|up as one output-split call (rows [gate_s, up_s, gate_d, up_d]), down as an
@@ -467,7 +472,8 @@ def measure_rows(torch, S, synth, np):
         f_dense = 2.0 * t * (2 * i_n * hd + hd * i_n)
         f_exec = 2.0 * t * (o_s * hd / 2 + o_d * hd + hd * ns / 2 + hd * n_dense)
         nbytes = wbytes + t * hd * 2 + t * 2 * i_n * 4 + t * i_n * 2 + t * hd * 4
-        add("spense", t, "MLP: gate|up output-split + down input-split, 25% dense", us, f_dense, f_exec, nbytes)
+        add("spense", t, "MLP: gate|up output-split + down input-split, 25% dense", us, f_dense, f_exec, nbytes,
+            key=f"sp.{t}")
         keep.clear()
     return rows
 
@@ -507,6 +513,14 @@ def main():
         print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "launches": 5}))
         return
     S.lib()
+    extra = {}
+    if not args.no_rows:
+        # the per-workload rows and the machine ceilings run first: the headline steps are
+        # then timed on a GPU whose clock has settled under sustained work
+        extra["ceilings"] = measure_ceilings(torch, S)
+        log("per-workload rows:")
+        extra["rows"] = measure_rows(torch, S, synth, np)
+        torch.cuda.synchronize()
     n, m = 8, 16
     d = synth.mlp_down_8of16(t_max=args.tokens)
     x_bits, w_bits = d["x"], d["w"]
@@ -554,26 +568,18 @@ def main():
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"8:16 activation-sparse MLP down-projection, X {T}x{K} Student-t(4)*0.5, "
-                               f"W {O_}x{K} N(0,0.02), fp32 out", "tokens": T, "in_features": K,
-                   "out_features": O_, "pattern": "8:16", "route": "nm_sparsify -> S(X), nm_spmm(ACT_MASKED)"},
+        "config": {"workload": f"8:16 act-sparse down-proj X {T}x{K} t(4)*0.5, W {O_}x{K} N(0,.02), fp32 out",
+                   "tokens": T, "in_features": K, "out_features": O_, "pattern": "8:16"},
         "executed_tflops": round(value, 2),
-        "kernels": {
-            "select_us": round(sel_ms * 1e3, 2), "select_GBps": round(sel_bytes / sel_ms / 1e6, 1),
-            "select_frac_hbm": round(sel_bytes / sel_ms / 1e6 / PEAK_HBM_GBS, 4),
-            "product_us": round(gemm_ms * 1e3, 2)},
+        "kernels": {"select_us": round(sel_ms * 1e3, 1), "select_frac_hbm": round(sel_bytes / sel_ms / 1e6 / PEAK_HBM_GBS, 3),
+                    "product_us": round(gemm_ms * 1e3, 1)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
     }
-
-    if not args.no_rows:
-        result["ceilings"] = measure_ceilings(torch, S)
-        log("per-workload rows:")
-        result["rows"] = measure_rows(torch, S, synth, np)
-
+    result.update(extra)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x_bits, w_bits, n, m)
-    print(json.dumps(result), flush=True)
+    print(json.dumps(result, separators=(",", ":")), flush=True)
 
 
 if __name__ == "__main__":

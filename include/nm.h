@@ -120,8 +120,10 @@ nm_status nm_compress(const void* x, int64_t rows, int64_t k, int64_t ldx, int n
 
 /*
  * nm_decompress -- inverse of nm_compress: scatter values to their positions, +0.0
- * elsewhere.  y bf16 [rows][ldy].  Metadata entries must be valid positions (< m,
- * strictly ascending within a group); other metadata is a caller error with an
+ * elsewhere.  [SLIDE] 2.C: the packed form (values plus index metadata) is produced once
+ * at load time and expanded again only where a dense operand is needed; [FLEX] 1 (values
+ * plus index metadata).  y bf16 [rows][ldy].  Metadata entries must be valid positions
+ * (< m, strictly ascending within a group); other metadata is a caller error with an
  * unspecified (but in-bounds) result.
  */
 nm_status nm_decompress(const void* values, const void* meta, nm_meta fmt, int64_t rows,
@@ -163,6 +165,62 @@ nm_status nm_quant_lift(const void* x, int64_t t, int64_t k, int64_t ldx, int ns
  */
 nm_status nm_slide_lift(const void* x, int64_t t, int64_t k, int64_t ldx, int ns,
                         void* x_out, int64_t ldo, void* stream);
+
+/*
+ * Route hints of nm_spmm (nm_spmm_args.route) and nm_hybrid_gemm (its `route` argument).
+ * A hint chooses WHICH kernels compute a call, never WHAT is computed: every route gives
+ * the same bitmask bit for bit and products within the same tolerance of the same
+ * definition.  NM_ROUTE_AUTO (0) lets the library choose by shape; the other bits exist
+ * so that every kernel can be tested and measured on any shape.  A hint that does not
+ * apply to a call, or whose kernel does not take the shape, is ignored (the report below
+ * says what ran).
+ */
+enum {
+  NM_ROUTE_AUTO = 0,
+  NM_ROUTE_ACT_FUSED = 1u << 0,     /* ACT_DYNAMIC above the few-token sizes: top-n selected
+                                       inside the product's X-tile loader                   */
+  NM_ROUTE_ACT_MASK = 1u << 1,      /* ... a select pass writes the bitmask to the
+                                       workspace, the product applies it to X fragments     */
+  NM_ROUTE_ACT_SX = 1u << 2,        /* ... a select pass writes S(X) to the workspace, the
+                                       product streams it                                   */
+  NM_ROUTE_NO_FEW = 1u << 3,        /* never the few-token (t <= 128) kernels               */
+  NM_ROUTE_FEW_STREAM = 1u << 4,    /* few tokens: the weight-streaming kernels             */
+  NM_ROUTE_FEW_TILE = 1u << 5,      /* few tokens: the split-K tile kernels where they apply*/
+  NM_ROUTE_NO_META_BLOCK = 1u << 6, /* large-token 2:4 products read the row-major 2-bit
+                                       positions (no K-blocked copy in the workspace)       */
+  NM_ROUTE_FP8_WIDEN = 1u << 7,     /* large-token fp8 weights widened to bf16 in the
+                                       workspace first                                      */
+  NM_ROUTE_NO_XLDS = 1u << 8,       /* one token: X fragments in registers, not staged in LDS*/
+  NM_ROUTE_NO_FEW_SELECT = 1u << 9, /* one token: a separate select pass rather than the
+                                       selection inside the product's staged X row          */
+  NM_ROUTE_TILE_LDS = 1u << 10,     /* tile products: the direct-to-LDS kernels at any size */
+  NM_ROUTE_TILE_REGS = 1u << 11     /* tile products: the register-staged kernels           */
+};
+
+/*
+ * Report of the kernels a call enqueued (bits OR-ed into *route_taken when the caller
+ * passes a host pointer; the call never clears it).
+ */
+enum {
+  NM_TAKEN_SELECT = 1u << 0,        /* a separate select / compress pass                    */
+  NM_TAKEN_FEW_STREAM = 1u << 1,    /* a few-token weight-streaming kernel                  */
+  NM_TAKEN_FEW_XLDS = 1u << 2,      /* ... with the X row staged in LDS                     */
+  NM_TAKEN_FEW_SELECT = 1u << 3,    /* ... selecting inside the staged X row                */
+  NM_TAKEN_TILE_SPLIT = 1u << 4,    /* a split-K tile kernel for few tokens                 */
+  NM_TAKEN_REDUCE = 1u << 5,        /* a pass adding partial sums in a fixed order          */
+  NM_TAKEN_TILE_LDS = 1u << 6,      /* a direct-to-LDS tile kernel                          */
+  NM_TAKEN_TILE_REGS = 1u << 7,     /* a register-staged tile kernel                        */
+  NM_TAKEN_FUSED_SELECT = 1u << 8,  /* selection inside a tile kernel's X loader            */
+  NM_TAKEN_MASK = 1u << 9,          /* a product applying a bitmask to X                    */
+  NM_TAKEN_GATHER1 = 1u << 10,      /* the single-token K-major gather                      */
+  NM_TAKEN_LIFT = 1u << 11,         /* X lifted into the workspace                          */
+  NM_TAKEN_META_BLOCK = 1u << 12,   /* 2-bit positions K-blocked into the workspace         */
+  NM_TAKEN_PERMUTE = 1u << 13,      /* hybrid columns of X permuted into the workspace      */
+  NM_TAKEN_QUANT = 1u << 14,        /* per-token fp8 quantization (and lift) pass           */
+  NM_TAKEN_WIDEN = 1u << 15,        /* fp8 weights widened to bf16 in the workspace         */
+  NM_TAKEN_DECOMPRESS = 1u << 16,   /* compressed X expanded into the workspace             */
+  NM_TAKEN_SPARSE_MMA = 1u << 17    /* a product on the sparse matrix instructions          */
+};
 
 /* Operating modes of nm_spmm. */
 typedef enum {
@@ -212,6 +270,14 @@ typedef enum {
  *               split-K tile route for 33-128 tokens needs this).  With less, the call
  *               takes a route that needs none (slower).  Contents after the call are
  *               unspecified.  Calls sharing a workspace must be ordered (same stream).
+ *   route       NM_ROUTE_* hint bits (0: the library chooses by shape)
+ *   few_wpb     few-token streaming kernels: waves per workgroup (4, 8 or 16; 0 = chosen)
+ *   few_splits  few-token streaming kernels: reduction splits across workgroups (0 = chosen)
+ *   tile_wg     split-K tile kernels: target workgroup count (0 = one per CU)
+ *   route_taken host pointer or NULL: receives NM_TAKEN_* bits (OR-ed in) of the kernels
+ *               the call enqueued
+ *   The route fields change which kernels run and the workspace the size query asks for,
+ *   never the result beyond the stated tolerance.
  * Results are deterministic: the same call on the same inputs gives the same bits.
  */
 typedef struct {
@@ -236,6 +302,11 @@ typedef struct {
   uint32_t* x_mask_out;   /* optional                                              */
   void* workspace;        /* optional                                              */
   int64_t workspace_bytes;
+  uint32_t route;         /* NM_ROUTE_* hints (0 = the library's choice)           */
+  int32_t few_wpb;        /* tuning of the chosen kernels (0 = the library's)      */
+  int32_t few_splits;
+  int32_t tile_wg;
+  uint32_t* route_taken;  /* optional host pointer: NM_TAKEN_* bits of what ran    */
 } nm_spmm_args;
 
 /*
@@ -248,7 +319,8 @@ typedef struct {
 nm_status nm_spmm(const nm_spmm_args* args, void* stream);
 
 /* Bytes of workspace for nm_spmm's preferred route with these arguments (0 if it uses
- * none).  Depends on mode, n, m, ns, t, o, k, w_dtype, w_scale, ldx and x_meta only. */
+ * none).  Depends on mode, n, m, ns, t, o, k, w_dtype, w_scale, ldx, x_meta and the route
+ * fields only. */
 int64_t nm_spmm_workspace_size(const nm_spmm_args* args);
 
 /*
@@ -290,16 +362,20 @@ int64_t nm_hybrid_pack_workspace_size(int64_t k);
  * preferred route also places a K-blocked copy of ws_meta after it (o * K_s / 8 bytes).
  * nm_hybrid_gemm_workspace_size gives the amount for the preferred route.  Contents
  * after the call are unspecified; calls sharing it must be ordered.
+ * route: NM_ROUTE_* hints (0 = the library's choice; the ACT_* and fp8 bits do not apply);
+ * route_taken: host pointer or NULL, receives NM_TAKEN_* bits as for nm_spmm.
  */
 nm_status nm_hybrid_gemm(const void* x, int64_t t, int64_t ldx, const int32_t* sparse_cols,
                          int64_t k_s, const int32_t* dense_cols, int64_t k_d,
                          const void* ws_values, const void* ws_meta, nm_meta fmt,
                          const void* wd, int64_t ldwd, int64_t o, float* y, int64_t ldy,
-                         int accumulate, void* workspace, int64_t workspace_bytes, void* stream);
+                         int accumulate, void* workspace, int64_t workspace_bytes,
+                         uint32_t route, uint32_t* route_taken, void* stream);
 
-/* Workspace bytes of nm_hybrid_gemm's preferred route (gathered: column lists given). */
+/* Workspace bytes of nm_hybrid_gemm's preferred route (gathered: column lists given) under
+ * the route hints `route`. */
 int64_t nm_hybrid_gemm_workspace_size(int64_t t, int64_t k_s, int64_t k_d, int64_t o,
-                                      int gathered);
+                                      int gathered, uint32_t route);
 
 /*
  * Spense layout of a GLU MLP ([SPENSE] 2.A, 2.B).  The intermediate indices of
@@ -371,22 +447,6 @@ nm_status nm_spense_outsplit_gemm(const void* x, int64_t t, int64_t k, int64_t l
                                   float* y, int64_t ldy, int accumulate, void* workspace,
                                   int64_t workspace_bytes, void* stream);
 int64_t nm_spense_outsplit_workspace_size(int64_t t, int64_t k, int64_t o_s, int64_t o_d);
-
-/*
- * Measurement helpers (not part of the method): the achievable ceilings on the machine at
- * hand, reported beside the nominal peaks.
- *   nm_probe_sink_bytes   bytes of the device sink both probes write (one value per thread).
- *   nm_probe_read         one streaming read of `bytes` (a multiple of 16) at buf, 16-byte
- *                         loads at a grid stride; buf and sink 16-byte aligned.
- *   nm_probe_mfma         `iters` rounds of 16 independent bf16 16x16x32 matrix instructions
- *                         per wave on register operands; nm_probe_mfma_flops(iters) gives the
- *                         FLOPs one launch performs.
- * Both only enqueue work on `stream`; time them with events on that stream.
- */
-int64_t nm_probe_sink_bytes(void);
-nm_status nm_probe_read(const void* buf, int64_t bytes, void* sink, void* stream);
-int64_t nm_probe_mfma_flops(int64_t iters);
-nm_status nm_probe_mfma(int64_t iters, void* sink, void* stream);
 
 #ifdef __cplusplus
 }

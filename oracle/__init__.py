@@ -8,8 +8,12 @@ descriptions, plain and unblocked, so that a reader can check each step by eye.
 Conventions
 -----------
 * bf16 tensors are numpy ``uint16`` arrays of bit patterns, row-major, K fastest.
-* Floating-point results are computed in fp64 (every bf16 x bf16 product is exact in
-  fp64; the only rounding is the fp64 summation, far below the GPU's fp32 rounding).
+* Matrix products follow the workloads' "fp32 accumulate": ``gemm`` and the products
+  built on it run the plain single-threaded C loop of ``gemm_f32.c`` -- one fp32
+  accumulator per output, products added in ascending k, every sum rounded to nearest
+  even (bf16 x bf16 and bf16 x e4m3 products are exact in fp32).  ``gemm_f64`` is the
+  library fp64 product of the same operands, used only for error bounds and whole-output
+  projection checks, never as the parity reference.
 * "Group" = m contiguous elements along K; group g of a row covers k in [g*m, g*m+m).
 
 Sources (cited by page title and section)
@@ -52,6 +56,9 @@ Readings where the pages are silent (each is listed in the design notes):
 """
 from __future__ import annotations
 
+import ctypes
+import os
+import subprocess
 
 import numpy as np
 
@@ -59,7 +66,7 @@ __all__ = [
     "magnitude_key", "bf16_to_f64", "select_keep", "sparsify", "pack_mask", "compress",
     "pack_meta_2bit", "unpack_meta_2bit", "decompress", "slide_windows",
     "slide_lower", "slide_scatter_back", "lift", "column_sq_norms", "hybrid_columns",
-    "hybrid_pack", "gemm", "spmm_act", "spmm_slide", "hybrid_gemm", "fp8_e4m3_to_f64",
+    "hybrid_pack", "gemm", "gemm_f64", "gemm_f32_values", "build_c", "spmm_act", "spmm_slide", "hybrid_gemm", "fp8_e4m3_to_f64",
     "spmm_act_fp8", "lowered_k", "SCORE_ACT_WEIGHTED", "SCORE_WEIGHT", "selection_scores",
     "select_keep_scored", "sparsify_scored", "spense_glu_scores", "spense_order", "spense_order_tail",
     "spense_pack", "outsplit_gemm", "e4m3_encode", "quantize_tokens", "f32_from_bf16", "spmm_w8a8_slide",
@@ -428,8 +435,63 @@ def outsplit_gemm(x_bits, ws_vals, ws_idx, wd_bits, k: int) -> np.ndarray:
 
 # ---------------------------------------------------------------------------- GEMM ---
 
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_C_SRC = os.path.join(_HERE, "gemm_f32.c")
+_C_LIB = os.path.join(_HERE, "liboracle.so")
+# plain C, no fused multiply-add contraction, no fast-math reassociation
+_C_FLAGS = ["-O3", "-fPIC", "-shared", "-std=c99", "-ffp-contract=off", "-fno-fast-math"]
+_clib_handle = None
+
+
+def build_c() -> str:
+    """Compile the oracle's C part (gemm_f32.c) into oracle/liboracle.so with gcc."""
+    tmp = _C_LIB + ".tmp"
+    subprocess.run(["gcc", *_C_FLAGS, _C_SRC, "-o", tmp], check=True)
+    os.replace(tmp, _C_LIB)
+    return _C_LIB
+
+
+def _clib():
+    global _clib_handle
+    if _clib_handle is None:
+        if not os.path.exists(_C_LIB) or os.path.getmtime(_C_LIB) < os.path.getmtime(_C_SRC):
+            build_c()
+        lib = ctypes.CDLL(_C_LIB)
+        lib.oracle_gemm_f32.restype = None
+        lib.oracle_gemm_f32.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                        ctypes.c_int64, ctypes.c_void_p]
+        _clib_handle = lib
+    return _clib_handle
+
+
+def gemm_f32_values(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """y[t][o] = fp32 sum over ascending k of a[t][k] * b[o][k], one accumulator per output
+    starting at +0, every sum rounded to nearest even (gemm_f32.c).  a: fp32 [T][K],
+    b: fp32 [O][K] holding values whose pairwise products are exact in fp32 (bf16, e4m3).
+    Returns fp32 [T][O]."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    b = np.asarray(b, dtype=np.float32)
+    t, k = a.shape
+    o = b.shape[0]
+    if b.shape[1] != k:
+        raise ValueError("operands disagree on K")
+    bk = np.ascontiguousarray(b.T)            # K-major: one k's weights contiguous
+    y = np.empty((t, o), dtype=np.float32)
+    if t and o:
+        _clib().oracle_gemm_f32(a.ctypes.data, t, k, bk.ctypes.data, o, y.ctypes.data)
+    return y
+
+
 def gemm(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
-    """Y[t][o] = sum_k a[t][k] * b[o][k] in fp64 (library matrix product)."""
+    """Y[t][o] = sum over ascending k of a[t][k] * b[o][k], accumulated in fp32 (the
+    layer's "fp32 accumulate"; gemm_f32_values).  bf16 operands; returns the fp32 results
+    as fp64 values."""
+    return gemm_f32_values(f32_from_bf16(a_bits), f32_from_bf16(b_bits)).astype(np.float64)
+
+
+def gemm_f64(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
+    """The same product in fp64 (library matrix product): error bounds and projection
+    checks only."""
     return bf16_to_f64(a_bits) @ bf16_to_f64(b_bits).T
 
 
@@ -449,15 +511,16 @@ def spmm_slide(x_bits: np.ndarray, vals_p: np.ndarray, idx_p: np.ndarray, ns: in
 
 def hybrid_gemm(x_bits, sparse_cols, dense_cols, ws_vals, ws_idx, wd_bits) -> np.ndarray:
     """[SPENSE] 2.A input split: Y = X_s . W_s^T + X_d . W_d^T, where X_s / X_d are the
-    columns of X in the sparse / dense region order and W_s is 2:4 compressed."""
+    columns of X in the sparse / dense region order and W_s is 2:4 compressed.  One fp32
+    accumulator per output runs over the sparse region, then the dense region."""
     ks = len(sparse_cols)
-    y = np.zeros((x_bits.shape[0], wd_bits.shape[0] if wd_bits.size else ws_vals.shape[0]))
-    if ks:
-        ws = decompress(ws_vals, ws_idx, 2, 4, ks)
-        y = y + gemm(np.ascontiguousarray(x_bits[:, sparse_cols]), ws)
-    if len(dense_cols):
-        y = y + gemm(np.ascontiguousarray(x_bits[:, dense_cols]), wd_bits)
-    return y
+    o = wd_bits.shape[0] if wd_bits.size else ws_vals.shape[0]
+    a_parts = [np.asarray(x_bits)[:, np.asarray(sparse_cols, np.int64)],
+               np.asarray(x_bits)[:, np.asarray(dense_cols, np.int64)]]
+    b_parts = [decompress(ws_vals, ws_idx, 2, 4, ks) if ks else np.zeros((o, 0), np.uint16),
+               np.asarray(wd_bits, np.uint16).reshape(o, len(dense_cols))]
+    # one accumulator per output: the sparse region's products first, then the dense region's
+    return gemm(np.concatenate(a_parts, axis=1), np.concatenate(b_parts, axis=1))
 
 
 # ----------------------------------------------------------------------------- fp8 ---
@@ -529,17 +592,23 @@ def spmm_w8a8_slide(x_bits, w8_vals, w_idx, w_scale, k: int, ns: int) -> np.ndar
     summary 2.B-2.C): X quantized per token, lifted ((2N-2):2N weights lowered to 2:4 over
     K' = K (2N-2)/N; ns = 2 means plain 2:4, no lift), multiplied against the 2:4 weight
     codes W' (values [O][K'/2] + in-window positions), then both scales applied:
-        Y[t][o] = s_t * s_o * sum_k' dec(lift(q)[t][k']) * dec(W'[o][k'])"""
+        Y[t][o] = fp32(fp32(s_t * sum_k' dec(lift(q)[t][k']) * dec(W'[o][k'])) * s_o)
+    with the sum accumulated in fp32 in ascending k'."""
     q, s_t = quantize_tokens(x_bits)
     qx = lift(q, ns) if ns > 2 else q
     kp = qx.shape[1]
     wd = decompress(np.asarray(w8_vals, np.uint8).astype(np.uint16), w_idx, 2, 4, kp)
-    acc = fp8_e4m3_to_f64(qx) @ fp8_e4m3_to_f64(wd.astype(np.uint8)).T
-    return acc * s_t.astype(np.float64)[:, None] * np.asarray(w_scale, np.float64)[None, :]
+    # e4m3 x e4m3 products are exact in fp32; fp32 accumulation, then the two scales
+    acc = gemm_f32_values(fp8_e4m3_to_f64(qx).astype(np.float32),
+                          fp8_e4m3_to_f64(wd.astype(np.uint8)).astype(np.float32))
+    y = (acc * s_t.astype(np.float32)[:, None]).astype(np.float32)
+    return (y * np.asarray(w_scale, np.float32)[None, :]).astype(np.float32).astype(np.float64)
 
 
 def spmm_act_fp8(x_bits: np.ndarray, w8: np.ndarray, scale: np.ndarray, n: int, m: int) -> np.ndarray:
-    """Y[t][o] = scale[o] * sum_k S(X)[t][k] * dec(W8[o][k]); scale applied after the sum."""
+    """Y[t][o] = fp32(scale[o] * sum_k S(X)[t][k] * dec(W8[o][k])): the sum accumulated in
+    fp32 in ascending k, the scale applied once after it."""
     s, _ = sparsify(x_bits, n, m)
-    acc = bf16_to_f64(s) @ fp8_e4m3_to_f64(w8).T
-    return acc * np.asarray(scale, dtype=np.float64)[None, :]
+    # bf16 x e4m3 products are exact in fp32; fp32 accumulation, then one scale multiply
+    acc = gemm_f32_values(f32_from_bf16(s), fp8_e4m3_to_f64(w8).astype(np.float32))
+    return (acc * np.asarray(scale, dtype=np.float32)[None, :]).astype(np.float32).astype(np.float64)

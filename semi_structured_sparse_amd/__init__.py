@@ -17,8 +17,8 @@ __all__ = [
     "NMError", "lib", "NM_OK", "NM_EINVAL", "NM_ESHAPE", "NM_EALIGN", "NM_EUNSUPPORTED", "NM_EHIP",
     "NM_META_U8", "NM_META_2BIT", "NM_W_BF16", "NM_W_FP8E4M3", "NM_ACT_DYNAMIC", "NM_ACT_COMPRESSED",
     "NM_W_COMPRESSED", "NM_W_SLIDE", "NM_ACT_MASKED", "nm_spmm_args", "nm_status_str", "nm_version", "nm_sparsify",
-    "nm_sparsify_scored", "NM_SCORE_ACT_WEIGHTED", "NM_SCORE_WEIGHT",
-    "nm_probe_sink_bytes", "nm_probe_read", "nm_probe_mfma_flops", "nm_probe_mfma",
+    "nm_sparsify_scored", "NM_SCORE_ACT_WEIGHTED", "NM_SCORE_WEIGHT", "route_taken", "ROUTE", "TAKEN",
+    "route_bits", "taken_names", "make_spmm_args",
     "nm_compress", "nm_decompress", "nm_lower_slide", "nm_slide_lift", "nm_spmm",
     "nm_spmm_workspace_size", "nm_hybrid_pack", "nm_hybrid_pack_workspace_size", "nm_hybrid_gemm",
     "nm_hybrid_gemm_workspace_size", "lowered_k", "NM_SPENSE_LOSS", "NM_SPENSE_TAIL", "nm_spense_glu_order",
@@ -35,6 +35,29 @@ NM_SCORE_ACT_WEIGHTED, NM_SCORE_WEIGHT = 0, 1
 NM_SPENSE_LOSS, NM_SPENSE_TAIL = 0, 1
 NM_ACT_DYNAMIC, NM_ACT_COMPRESSED, NM_W_COMPRESSED, NM_W_SLIDE, NM_ACT_MASKED = range(5)
 
+# route hints (NM_ROUTE_*) and the report of what ran (NM_TAKEN_*), by lower-case name
+ROUTE = {name: 1 << i for i, name in enumerate(
+    ["act_fused", "act_mask", "act_sx", "no_few", "few_stream", "few_tile", "no_meta_block", "fp8_widen",
+     "no_xlds", "no_few_select", "tile_lds", "tile_regs"])}
+TAKEN = {name: 1 << i for i, name in enumerate(
+    ["select", "few_stream", "few_xlds", "few_select", "tile_split", "reduce", "tile_lds", "tile_regs",
+     "fused_select", "mask", "gather1", "lift", "meta_block", "permute", "quant", "widen", "decompress",
+     "sparse_mma"])}
+
+
+def route_bits(*names) -> int:
+    """OR of the NM_ROUTE_* bits named (e.g. route_bits("few_stream", "no_xlds"))."""
+    bits = 0
+    for nm in names:
+        bits |= ROUTE[nm]
+    return bits
+
+
+def taken_names(bits: int) -> set:
+    """The NM_TAKEN_* names set in a route report."""
+    return {nm for nm, b in TAKEN.items() if bits & b}
+
+
 _i64 = ctypes.c_int64
 _int = ctypes.c_int
 _vp = ctypes.c_void_p
@@ -49,6 +72,8 @@ class nm_spmm_args(ctypes.Structure):
         ("w_scale", _vp), ("w_kmajor", _vp),
         ("y", _vp), ("ldy", _i64), ("accumulate", _int),
         ("x_mask_out", _vp), ("workspace", _vp), ("workspace_bytes", _i64),
+        ("route", ctypes.c_uint32), ("few_wpb", ctypes.c_int32), ("few_splits", ctypes.c_int32),
+        ("tile_wg", ctypes.c_int32), ("route_taken", _vp),
     ]
 
 
@@ -95,9 +120,9 @@ def lib() -> ctypes.CDLL:
     L.nm_hybrid_pack_workspace_size.argtypes = [_i64]
     L.nm_hybrid_gemm.restype = _int
     L.nm_hybrid_gemm.argtypes = [_vp, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _int, _vp, _i64, _i64, _vp,
-                                 _i64, _int, _vp, _i64, _vp]
+                                 _i64, _int, _vp, _i64, ctypes.c_uint32, _vp, _vp]
     L.nm_hybrid_gemm_workspace_size.restype = _i64
-    L.nm_hybrid_gemm_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _int]
+    L.nm_hybrid_gemm_workspace_size.argtypes = [_i64, _i64, _i64, _i64, _int, ctypes.c_uint32]
     L.nm_quant_lift.restype = _int
     L.nm_quant_lift.argtypes = [_vp, _i64, _i64, _i64, _int, _vp, _i64, _vp, _vp]
     L.nm_spense_glu_order.restype = _int
@@ -114,14 +139,6 @@ def lib() -> ctypes.CDLL:
                                           _vp, _i64, _vp]
     L.nm_spense_outsplit_workspace_size.restype = _i64
     L.nm_spense_outsplit_workspace_size.argtypes = [_i64, _i64, _i64, _i64]
-    L.nm_probe_sink_bytes.restype = _i64
-    L.nm_probe_sink_bytes.argtypes = []
-    L.nm_probe_read.restype = _int
-    L.nm_probe_read.argtypes = [_vp, _i64, _vp, _vp]
-    L.nm_probe_mfma_flops.restype = _i64
-    L.nm_probe_mfma_flops.argtypes = [_i64]
-    L.nm_probe_mfma.restype = _int
-    L.nm_probe_mfma.argtypes = [_i64, _vp, _vp]
     _LIB = L
     return L
 
@@ -245,11 +262,16 @@ def nm_spmm_workspace_size(args: nm_spmm_args) -> int:
 
 def make_spmm_args(mode, t, o, k, x, w, y, *, n=2, m=4, ns=2, ldx=None, x_meta=None, x_meta_fmt=NM_META_U8,
                    ldw=None, w_dtype=NM_W_BF16, w_meta=None, w_meta_fmt=NM_META_2BIT, w_scale=None,
-                   w_kmajor=None, ldy=None, accumulate=0, x_mask_out=None, workspace=None, workspace_bytes=0):
+                   w_kmajor=None, ldy=None, accumulate=0, x_mask_out=None, workspace=None, workspace_bytes=0,
+                   route=0, few_wpb=0, few_splits=0, tile_wg=0):
     """Fill an nm_spmm_args from tensors (pointers and leading dimensions only).  The
     returned struct keeps references to the tensors so that their memory stays allocated
-    while the struct is alive (it holds raw device pointers)."""
+    while the struct is alive (it holds raw device pointers), and carries a report cell
+    that route_taken(args) reads after a call."""
     a = nm_spmm_args()
+    a._taken = ctypes.c_uint32(0)
+    a.route, a.few_wpb, a.few_splits, a.tile_wg = route, few_wpb, few_splits, tile_wg
+    a.route_taken = ctypes.addressof(a._taken)
     a._tensors = [v for v in (x, w, y, x_meta, w_meta, w_scale, w_kmajor, x_mask_out, workspace)
                   if v is not None and not isinstance(v, int)]
     a.mode, a.n, a.m, a.ns = mode, n, m, ns
@@ -282,8 +304,13 @@ def nm_hybrid_pack_workspace_size(k: int) -> int:
     return int(lib().nm_hybrid_pack_workspace_size(k))
 
 
-def nm_hybrid_gemm_workspace_size(t: int, k_s: int, k_d: int, o: int, gathered: bool) -> int:
-    return int(lib().nm_hybrid_gemm_workspace_size(t, k_s, k_d, o, 1 if gathered else 0))
+def route_taken(args: nm_spmm_args) -> int:
+    """NM_TAKEN_* bits reported by the calls made with args (made by make_spmm_args)."""
+    return int(args._taken.value)
+
+
+def nm_hybrid_gemm_workspace_size(t: int, k_s: int, k_d: int, o: int, gathered: bool, route: int = 0) -> int:
+    return int(lib().nm_hybrid_gemm_workspace_size(t, k_s, k_d, o, 1 if gathered else 0, route))
 
 
 def nm_quant_lift(x, ns, xq, xs, stream=None, *, t=None, k=None, ldx=None, ldq=None, check=True):
@@ -357,7 +384,8 @@ def nm_spense_outsplit_workspace_size(t: int, k: int, o_s: int, o_d: int) -> int
 
 def nm_hybrid_gemm(x, sparse_cols, k_s, dense_cols, k_d, ws_values, ws_meta, fmt, wd, o, y, accumulate=0,
                    stream=None, *, t=None, ldx=None, ldwd=None, ldy=None, workspace=None, workspace_bytes=None,
-                   check=True):
+                   route=0, taken=None, check=True):
+    """taken: optional ctypes.c_uint32 that receives the NM_TAKEN_* report."""
     t = x.shape[0] if t is None else t
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
@@ -365,31 +393,8 @@ def nm_hybrid_gemm(x, sparse_cols, k_s, dense_cols, k_d, ws_values, ws_meta, fmt
     st = lib().nm_hybrid_gemm(_ptr(x), t, _ld(x) if ldx is None else ldx, _ptr(sparse_cols), k_s,
                               _ptr(dense_cols), k_d, _ptr(ws_values), _ptr(ws_meta), fmt, _ptr(wd),
                               _ld(wd) if ldwd is None else ldwd, o, _ptr(y), _ld(y) if ldy is None else ldy,
-                              accumulate, _ptr(workspace), workspace_bytes, _stream(stream))
+                              accumulate, _ptr(workspace), workspace_bytes, route,
+                              ctypes.addressof(taken) if taken is not None else None, _stream(stream))
     if check:
         _check(st, "nm_hybrid_gemm")
-    return st
-
-
-# ------------------------------------------------------------ measurement helpers ---
-
-def nm_probe_sink_bytes():
-    return lib().nm_probe_sink_bytes()
-
-
-def nm_probe_read(buf, nbytes, sink, stream=None, *, check=True):
-    st = lib().nm_probe_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream))
-    if check:
-        _check(st, "nm_probe_read")
-    return st
-
-
-def nm_probe_mfma_flops(iters):
-    return lib().nm_probe_mfma_flops(iters)
-
-
-def nm_probe_mfma(iters, sink, stream=None, *, check=True):
-    st = lib().nm_probe_mfma(iters, _ptr(sink), _stream(stream))
-    if check:
-        _check(st, "nm_probe_mfma")
     return st

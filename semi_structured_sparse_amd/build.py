@@ -12,7 +12,10 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libnmsparse.so")
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["api.hip", "select.hip", "slide.hip", "gemm_dense.hip", "gemm_lds.hip", "gemm_sparse.hip",
-           "gemm_lds_sp.hip", "hybrid_pack.hip", "spense.hip", "decode.hip", "probe.hip"]
+           "gemm_lds_sp.hip", "hybrid_pack.hip", "spense.hip", "decode.hip"]
+# measurement helpers live in a library of their own (not exported by libnmsparse)
+PROBE_SOURCES = ["probe.hip"]
+PROBE_OUT = os.path.join(PKG, "libnmprobe.so")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
          # packed fp32 VALU forms stay off (code generation choice for this toolchain)
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -46,11 +49,13 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
             print(out)
         return obj
 
+    psrcs = [s for s in PROBE_SOURCES if os.path.exists(os.path.join(CSRC, s))]
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(compile_one, srcs))
-    tmp = OUT + ".tmp"
-    _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, OUT)
+        objs = list(ex.map(compile_one, srcs + psrcs))
+    for out, sel in ((OUT, objs[:len(srcs)]), (PROBE_OUT, objs[len(srcs):])):
+        tmp = out + ".tmp"
+        _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *sel])
+        os.replace(tmp, out)
     return OUT
 
 

@@ -3,9 +3,6 @@
 // caller's stream.  See include/nm.h for the contract of each call.
 #include <hip/hip_runtime.h>
 
-#include <cstdlib>
-#include <cstring>
-
 #include "nm.h"
 #include "nm_launch.h"
 
@@ -79,7 +76,17 @@ nm_status check_select_pattern(int64_t k, int n, int m, bool mask) {
   return NM_OK;
 }
 
-// Which activation route nm_spmm takes (NM_ACT_ROUTE overrides it for A/B measurement):
+// The route hints of a call (nm.h); the size queries pass report = false so that they
+// never write the caller's report.
+nml::Route route_of(const nm_spmm_args* a, bool report) {
+  nml::Route r{};
+  r.flags = a->route;
+  r.few_wpb = a->few_wpb; r.few_splits = a->few_splits; r.tile_wg = a->tile_wg;
+  r.taken = report ? a->route_taken : nullptr;
+  return r;
+}
+
+// Which activation route nm_spmm takes (the NM_ROUTE_ACT_* hints choose one):
 //   fused: top-n selected inside the product kernel's X-tile loader;
 //   mask:  a select pass writes the keep bitmask, the product applies it to X fragments;
 //   sx:    a select pass writes S(X) to the workspace, the product streams it unchanged.
@@ -87,13 +94,10 @@ nm_status check_select_pattern(int64_t k, int n, int m, bool mask) {
 // the fused loader re-selects X once per output tile and is slowest at large T.
 enum ActRoute { ROUTE_FUSED = 0, ROUTE_MASK = 1, ROUTE_SX = 2 };
 
-ActRoute act_route(int64_t t) {
-  const char* e = std::getenv("NM_ACT_ROUTE");
-  if (e != nullptr) {
-    if (std::strcmp(e, "fused") == 0) return ROUTE_FUSED;
-    if (std::strcmp(e, "mask") == 0) return ROUTE_MASK;
-    if (std::strcmp(e, "sx") == 0) return ROUTE_SX;
-  }
+ActRoute act_route(int64_t t, const nml::Route& r) {
+  if (r.has(NM_ROUTE_ACT_FUSED)) return ROUTE_FUSED;
+  if (r.has(NM_ROUTE_ACT_MASK)) return ROUTE_MASK;
+  if (r.has(NM_ROUTE_ACT_SX)) return ROUTE_SX;
   return t >= 512 ? ROUTE_SX : ROUTE_FUSED;
 }
 
@@ -102,11 +106,7 @@ int64_t mask_words(int64_t t, int64_t k) { return t * ((k + 31) / 32); }
 // Token counts up to this go to the few-token kernels (decode shapes).
 constexpr int64_t kFewMaxT = 128;
 
-bool use_few(int64_t t) {
-  const char* e = std::getenv("NM_FEW");   // A/B measurement override ("0": tile kernels only)
-  if (e != nullptr && std::strcmp(e, "0") == 0) return false;
-  return t <= kFewMaxT;
-}
+bool use_few(int64_t t, const nml::Route& r) { return t <= kFewMaxT && !r.has(NM_ROUTE_NO_FEW); }
 
 inline int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
 
@@ -125,12 +125,11 @@ inline float* ws_slice(void* ws, int64_t ws_bytes, int64_t off, int64_t* avail) 
 // split-K tile kernel, whose workgroups share each X slice through LDS across 128 weight
 // rows.  Measured on gfx950 (bf16 W, 33-128 tokens): 4096 x 14336 at 128 tokens 40 vs
 // 73 us, 14336 x 4096 at 64 tokens 32 vs 46 us; for weights under 2048 rows the
-// streaming kernel stays ahead.  NM_FEW_ROUTE=stream|tile forces either for A/B.
+// streaming kernel stays ahead.  The NM_ROUTE_FEW_STREAM / NM_ROUTE_FEW_TILE hints force either.
 bool few_use_tile(const nml::GemmArgs& g) {
   if (!nml::gemm_lds_small_eligible(g)) return false;
-  const char* e = std::getenv("NM_FEW_ROUTE");
-  if (e != nullptr && std::strcmp(e, "tile") == 0) return true;
-  if (e != nullptr && std::strcmp(e, "stream") == 0) return false;
+  if (g.route.has(NM_ROUTE_FEW_TILE)) return true;
+  if (g.route.has(NM_ROUTE_FEW_STREAM)) return false;
   return g.t > 32 && g.o >= 2048;
 }
 
@@ -141,6 +140,7 @@ nml::FewArgs few_dense_args(const nml::GemmArgs& g) {
   sg.w = g.w; sg.ldw = g.ldw; sg.w_kind = g.w_fp8 ? nml::WK_FP8 : nml::WK_BF16;
   sg.x = g.x; sg.ldx = g.ldx; sg.loader = nml::XL_PLAIN; sg.ns = 2; sg.k = g.k;
   f.w_scale = g.w_scale; f.t = g.t; f.o = g.o; f.y = g.y; f.ldy = g.ldy; f.accumulate = g.accumulate;
+  f.route = g.route;
   return f;
 }
 
@@ -162,6 +162,7 @@ nml::FewArgs few_sparse_args(const nm_spmm_args* a, int64_t kc, int ns) {
   sg.x = (const uint16_t*)a->x; sg.ldx = a->ldx; sg.ns = ns;
   sg.loader = a->mode == NM_W_SLIDE ? nml::XL_LIFT : nml::XL_PLAIN; sg.k = kc;
   f.t = a->t; f.o = a->o; f.y = a->y; f.ldy = a->ldy; f.accumulate = a->accumulate;
+  f.route = route_of(a, true);
   return f;
 }
 
@@ -180,19 +181,19 @@ inline int64_t lift_ld(int64_t kp) { return (kp + 7) / 8 * 8; }
 // 32 tokens for weights of at least 2048 rows and above 16 tokens from 8192 rows; the
 // streaming kernel otherwise.  Measured on gfx950: 6:8 lowered 4096 x 4096 at 128 tokens
 // 30 vs 58 us, 14336 x 4096 at 16 tokens 40 vs 56 us; 2:4 14336 x 4096 at 33 tokens 31 vs
-// 38 us.  NM_FEW_ROUTE=stream|tile forces either for A/B measurement.
+// 38 us.  The NM_ROUTE_FEW_STREAM / NM_ROUTE_FEW_TILE hints force either.
 bool sp_few_tile(const nml::SparseArgs& sa) {
   if (!nml::gemm_lds_sp_eligible(sa, true)) return false;
-  const char* e = std::getenv("NM_FEW_ROUTE");
-  if (e != nullptr && std::strcmp(e, "tile") == 0) return true;
-  if (e != nullptr && std::strcmp(e, "stream") == 0) return false;
+  if (sa.route.has(NM_ROUTE_FEW_TILE)) return true;
+  if (sa.route.has(NM_ROUTE_FEW_STREAM)) return false;
   return (sa.t > 32 && sa.o >= 2048) || (sa.t > 16 && sa.o >= 8192);
 }
 
 // The W_* modes as a tile-kernel call; lowered weights read X lifted into a buffer of
 // row stride lift_ld(kc) (pointer filled in by the caller).
-nml::SparseArgs w_mode_sparse_args(const nm_spmm_args* a, int64_t kc, int ns) {
+nml::SparseArgs w_mode_sparse_args(const nm_spmm_args* a, int64_t kc, int ns, bool report) {
   nml::SparseArgs sa{};
+  sa.route = route_of(a, report);
   sa.w_vals = (const uint16_t*)a->w; sa.w_meta = (const uint8_t*)a->w_meta; sa.kc = kc;
   sa.x = (const uint16_t*)a->x; sa.ldx = a->ldx; sa.ns = ns;
   sa.loader = nml::XL_PLAIN;
@@ -203,7 +204,7 @@ nml::SparseArgs w_mode_sparse_args(const nm_spmm_args* a, int64_t kc, int ns) {
 
 // Workspace bytes of the few-token tile route of the W_* modes: [lifted X][partials].
 int64_t w_mode_tile_bytes(const nm_spmm_args* a, int64_t kc, int ns) {
-  const nml::SparseArgs sa = w_mode_sparse_args(a, kc, ns);
+  const nml::SparseArgs sa = w_mode_sparse_args(a, kc, ns, false);
   if (!sp_few_tile(sa)) return 0;
   const int64_t lift = a->mode == NM_W_SLIDE ? align256(a->t * lift_ld(kc) * 2) : 0;
   return lift + nml::gemm_lds_sp_small_part_bytes(sa);
@@ -211,15 +212,13 @@ int64_t w_mode_tile_bytes(const nm_spmm_args* a, int64_t kc, int ns) {
 
 // Large-token 2:4-family products on the direct-to-LDS kernel read a K-blocked copy of the
 // weight positions (o * kc / 8 bytes) from the workspace at byte offset `off` when the
-// workspace holds it (NM_META_BLOCK=0 keeps the row-major positions, for A/B measurement).
+// workspace holds it (the NM_ROUTE_NO_META_BLOCK hint keeps the row-major positions).
 bool meta_block_wanted(const nml::SparseArgs& sa) {
-  const char* e = std::getenv("NM_META_BLOCK");
-  if (e != nullptr && std::strcmp(e, "0") == 0) return false;
+  if (sa.route.has(NM_ROUTE_NO_META_BLOCK)) return false;
   return sa.kc > 0 && sa.w_meta != nullptr && nml::gemm_sparse_uses_lds(sa);
 }
 int64_t meta_block_ws(const nml::SparseArgs& sa) {
-  const char* e = std::getenv("NM_META_BLOCK");
-  if ((e != nullptr && std::strcmp(e, "0") == 0) || sa.kc <= 0 || !nml::gemm_sparse_uses_lds(sa)) return 0;
+  if (sa.route.has(NM_ROUTE_NO_META_BLOCK) || sa.kc <= 0 || !nml::gemm_sparse_uses_lds(sa)) return 0;
   return nml::meta_block_bytes(sa.o, sa.kc);
 }
 nm_status use_meta_block(nml::SparseArgs& sa, void* ws, int64_t ws_bytes, int64_t off, hipStream_t s) {
@@ -227,6 +226,7 @@ nm_status use_meta_block(nml::SparseArgs& sa, void* ws, int64_t ws_bytes, int64_
   uint8_t* blk = reinterpret_cast<uint8_t*>(ws) + off;
   if (nml::launch_meta_block(sa.w_meta, sa.o, sa.kc, sa.f8 ? 16 : 8, blk, s) != hipSuccess) return NM_EHIP;
   sa.w_meta_blk = blk;
+  sa.route.note(NM_TAKEN_META_BLOCK);
   return NM_OK;
 }
 
@@ -235,18 +235,19 @@ nm_status use_meta_block(nml::SparseArgs& sa, void* ws, int64_t ws_bytes, int64_
 struct W8A8Layout {
   int64_t xq, xs, meta, part, total;
 };
-W8A8Layout w8a8_layout(int64_t t, int64_t o, int64_t kc, const nml::SparseArgs* sa_small) {
+W8A8Layout w8a8_layout(int64_t t, int64_t o, int64_t kc, const nml::SparseArgs* sa_small, const nml::Route& r) {
   W8A8Layout L{};
   L.xq = 0;
   L.xs = align256(t * kc);
   L.meta = L.xs + align256(t * 4);
   L.part = L.meta + align256(nml::meta_block_bytes(o, kc));
-  const int64_t pb = (sa_small != nullptr && use_few(t)) ? nml::gemm_lds_sp_small_part_bytes(*sa_small) : 0;
+  const int64_t pb = (sa_small != nullptr && use_few(t, r)) ? nml::gemm_lds_sp_small_part_bytes(*sa_small) : 0;
   L.total = L.part + pb;
   return L;
 }
-nml::SparseArgs w8a8_args(const nm_spmm_args* a, int64_t kc, const uint8_t* xq, const float* xs) {
+nml::SparseArgs w8a8_args(const nm_spmm_args* a, int64_t kc, const uint8_t* xq, const float* xs, bool report) {
   nml::SparseArgs sa{};
+  sa.route = route_of(a, report);
   sa.w_vals = (const uint16_t*)a->w; sa.w_meta = (const uint8_t*)a->w_meta; sa.kc = kc;
   sa.x = (const uint16_t*)xq; sa.ldx = kc; sa.loader = nml::XL_PLAIN; sa.ns = 2;
   sa.t = a->t; sa.o = a->o; sa.y = a->y; sa.ldy = a->ldy; sa.accumulate = a->accumulate; sa.trans_out = 0;
@@ -254,12 +255,12 @@ nml::SparseArgs w8a8_args(const nm_spmm_args* a, int64_t kc, const uint8_t* xq, 
   return sa;
 }
 int64_t w8a8_ws_bytes(const nm_spmm_args* a, int64_t kc) {
-  const nml::SparseArgs sa = w8a8_args(a, kc, nullptr, nullptr);
-  return w8a8_layout(a->t, a->o, kc, &sa).total;
+  const nml::SparseArgs sa = w8a8_args(a, kc, nullptr, nullptr, false);
+  return w8a8_layout(a->t, a->o, kc, &sa, sa.route).total;
 }
 nm_status w8a8_product(const nm_spmm_args* a, int64_t kc, int ns, hipStream_t s) {
-  const nml::SparseArgs probe = w8a8_args(a, kc, nullptr, nullptr);
-  const W8A8Layout L = w8a8_layout(a->t, a->o, kc, &probe);
+  const nml::SparseArgs probe = w8a8_args(a, kc, nullptr, nullptr, false);
+  const W8A8Layout L = w8a8_layout(a->t, a->o, kc, &probe, probe.route);
   if (a->workspace == nullptr || a->workspace_bytes < L.total) return NM_EINVAL;
   char* ws = reinterpret_cast<char*>(a->workspace);
   uint8_t* xq = reinterpret_cast<uint8_t*>(ws + L.xq);
@@ -267,27 +268,28 @@ nm_status w8a8_product(const nm_spmm_args* a, int64_t kc, int ns, hipStream_t s)
   hipError_t e = nml::launch_quant_lift(a->mode == NM_W_SLIDE ? ns : 2, (const uint16_t*)a->x, a->t, a->k,
                                         a->ldx, xq, kc, xs, s);
   if (e != hipSuccess) return NM_EHIP;
-  nml::SparseArgs sa = w8a8_args(a, kc, xq, xs);
+  nml::SparseArgs sa = w8a8_args(a, kc, xq, xs, true);
+  sa.route.note(NM_TAKEN_QUANT | (a->mode == NM_W_SLIDE && ns > 2 ? NM_TAKEN_LIFT : 0u));
   // few tokens: the split tile kernel reads the row-major positions (a blocked copy would
   // cost a launch of about the product's own length); above that the blocked copy pays
-  if (use_few(a->t))
+  if (use_few(a->t, sa.route))
     return hip_status(nml::launch_gemm_lds_sp_small(sa, reinterpret_cast<float*>(ws + L.part), L.total - L.part, s));
   uint8_t* blk = reinterpret_cast<uint8_t*>(ws + L.meta);
   if (nml::launch_meta_block(sa.w_meta, sa.o, kc, 16, blk, s) != hipSuccess) return NM_EHIP;
   sa.w_meta_blk = blk;
+  sa.route.note(NM_TAKEN_META_BLOCK);
   return hip_status(nml::launch_gemm_lds_sp(sa, s));
 }
 
 // Large-token ACT_DYNAMIC with fp8 weights: bytes of a bf16 copy of the weights in the
 // workspace (after the S(X) staging) for the direct-to-LDS product kernel.
-// Only when the codes cannot go to LDS directly (rows not 16-byte multiples), or when
-// NM_FP8_WIDEN=1 asks for it (A/B measurement).
+// Only when the codes cannot go to LDS directly (rows not 16-byte multiples), or under
+// the NM_ROUTE_FP8_WIDEN hint.
 int64_t fp8_widen_bytes(const nm_spmm_args* a) {
-  if (a->mode != NM_ACT_DYNAMIC || a->w_dtype != NM_W_FP8E4M3 || use_few(a->t)) return 0;
+  const nml::Route r = route_of(a, false);
+  if (a->mode != NM_ACT_DYNAMIC || a->w_dtype != NM_W_FP8E4M3 || use_few(a->t, r)) return 0;
   if (a->k % 64 != 0 || a->t < 512) return 0;
-  const char* e = std::getenv("NM_FP8_WIDEN");
-  const bool force = e != nullptr && std::strcmp(e, "1") == 0;
-  if (!force && a->ldw % 16 == 0) return 0;
+  if (!r.has(NM_ROUTE_FP8_WIDEN) && a->ldw % 16 == 0) return 0;
   return a->o * a->k * 2;
 }
 
@@ -304,8 +306,9 @@ inline int64_t hybrid_ldp(int64_t k_s, int64_t k_d) { return hybrid_off1(k_s) + 
 
 nml::FewArgs few_hybrid_args(const uint16_t* x, int64_t ldx, int64_t dbase, int64_t t, int64_t k_s, int64_t k_d,
                              const void* ws_values, const void* ws_meta, const void* wd, int64_t ldwd, int64_t o,
-                             float* y, int64_t ldy, int accumulate) {
+                             float* y, int64_t ldy, int accumulate, const nml::Route& r) {
   nml::FewArgs f{};
+  f.route = r;
   if (k_s > 0) {
     nml::FewSeg& sg = f.seg[f.nseg++];
     sg.w = ws_values; sg.w_meta = (const uint8_t*)ws_meta; sg.w_kind = nml::WK_SP24;
@@ -322,8 +325,10 @@ nml::FewArgs few_hybrid_args(const uint16_t* x, int64_t ldx, int64_t dbase, int6
 
 nml::SparseArgs hybrid_sparse_args(const uint16_t* x, int64_t ldx, int64_t dbase, int64_t t, int64_t k_s,
                                    int64_t k_d, const void* ws_values, const void* ws_meta, const void* wd,
-                                   int64_t ldwd, int64_t o, float* y, int64_t ldy, int accumulate) {
+                                   int64_t ldwd, int64_t o, float* y, int64_t ldy, int accumulate,
+                                   const nml::Route& r) {
   nml::SparseArgs sa{};
+  sa.route = r;
   sa.w_vals = (const uint16_t*)ws_values; sa.w_meta = (const uint8_t*)ws_meta; sa.kc = k_s;
   sa.x = x; sa.ldx = ldx; sa.loader = nml::XL_PLAIN;
   sa.t = t; sa.o = o;
@@ -477,32 +482,35 @@ int64_t nm_spmm_workspace_size(const nm_spmm_args* a) {
     return (a->t > 0 && a->o > 0 && kc > 0 && kc % 128 == 0) ? w8a8_ws_bytes(a, kc) : 0;
   }
   if (gather1_route(a)) return nml::gather1_part_bytes(a->k, a->o, a->m);
+  const nml::Route r = route_of(a, false);
   const int64_t stage = spmm_stage_bytes(a);
   int64_t part = 0;
-  if (use_few(a->t) && a->t > 0 && a->o > 0 && a->k > 0) {
+  if (use_few(a->t, r) && a->t > 0 && a->o > 0 && a->k > 0) {
     if (a->mode == NM_W_COMPRESSED || a->mode == NM_W_SLIDE) {
       if (a->mode == NM_W_SLIDE && (a->ns < 2 || a->ns > 8 || a->k % (2 * a->ns))) return 0;
       const int ns = a->mode == NM_W_SLIDE ? a->ns : 2;
       const int64_t tile = w_mode_tile_bytes(a, w_mode_kc(a), ns);
       if (tile > 0) return tile;
-      part = nml::few_partial_bytes(few_sparse_args(a, w_mode_kc(a), ns));
+      nml::FewArgs f = few_sparse_args(a, w_mode_kc(a), ns);
+      f.route = r;
+      part = nml::few_partial_bytes(f);
     } else if (a->mode == NM_ACT_DYNAMIC || a->mode == NM_ACT_COMPRESSED ||
                (a->mode == NM_ACT_MASKED && a->x_meta == nullptr)) {
       nml::GemmArgs g{};
       g.w = a->w; g.ldw = a->ldw; g.w_fp8 = a->w_dtype == NM_W_FP8E4M3 ? 1 : 0; g.w_scale = a->w_scale;
-      g.t = a->t; g.o = a->o; g.k = a->k; g.prologue = nml::PRO_NONE;
+      g.t = a->t; g.o = a->o; g.k = a->k; g.prologue = nml::PRO_NONE; g.route = r;
       g.ldx = a->mode == NM_ACT_MASKED ? a->ldx : a->k;
       part = dense_few_part_bytes(g);
     }
   }
   if (part > 0) return align256(stage) + part;
-  if ((a->mode == NM_W_SLIDE || a->mode == NM_W_COMPRESSED) && !use_few(a->t) && a->t > 0 && a->o > 0) {
+  if ((a->mode == NM_W_SLIDE || a->mode == NM_W_COMPRESSED) && !use_few(a->t, r) && a->t > 0 && a->o > 0) {
     // large-token product: [lifted X (lowered weights)][K-blocked positions]
     if (a->mode == NM_W_SLIDE && (a->ns < 2 || a->ns > 8 || a->k % (2 * a->ns))) return 0;
     if (a->mode == NM_W_COMPRESSED && a->k % 4) return 0;
     const int64_t kc = w_mode_kc(a);
     const int64_t lift = a->mode == NM_W_SLIDE ? align256(a->t * lift_ld(kc) * 2) : 0;
-    nml::SparseArgs sa = w_mode_sparse_args(a, kc, a->mode == NM_W_SLIDE ? a->ns : 2);
+    nml::SparseArgs sa = w_mode_sparse_args(a, kc, a->mode == NM_W_SLIDE ? a->ns : 2, false);
     const int64_t mb = meta_block_ws(sa);
     return mb > 0 ? lift + mb : lift;
   }
@@ -553,10 +561,11 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
       if (T == 0 || O == 0) return NM_OK;
       if (K == 0) return a->accumulate ? NM_OK : zero_output(a->y, T, O, a->ldy, s);
 
+      const nml::Route R = route_of(a, true);
       nml::GemmArgs g{};
       g.w = a->w; g.ldw = a->ldw; g.w_fp8 = fp8 ? 1 : 0; g.w_scale = a->w_scale;
       g.n = a->n; g.m = a->m; g.t = T; g.o = O; g.k = K;
-      g.y = a->y; g.ldy = a->ldy; g.accumulate = a->accumulate;
+      g.y = a->y; g.ldy = a->ldy; g.accumulate = a->accumulate; g.route = R;
       // workspace: [S(X) or decompressed X staging][few-token partial sums]
       const int64_t stage = spmm_stage_bytes(a);
       const bool have_ws = a->workspace != nullptr && a->workspace_bytes >= stage;
@@ -570,6 +579,7 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
           sa.w_vals = (const uint16_t*)a->x; sa.w_meta = (const uint8_t*)a->x_meta; sa.kc = K;
           sa.x = (const uint16_t*)a->w; sa.ldx = a->ldw; sa.loader = nml::XL_PLAIN;
           sa.t = O; sa.o = T; sa.y = a->y; sa.ldy = a->ldy; sa.accumulate = a->accumulate; sa.trans_out = 1;
+          sa.route = R;
           return hip_status(nml::launch_gemm_sparse(sa, s));
         }
         if (!have_ws) return NM_EINVAL;   // decompressed X needs the workspace
@@ -577,8 +587,9 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
         hipError_t e = nml::launch_decompress(a->m, (const uint16_t*)a->x, (const uint8_t*)a->x_meta,
                                               a->x_meta_fmt == NM_META_2BIT, T, K, a->n, xd, K, s);
         if (e != hipSuccess) return NM_EHIP;
+        R.note(NM_TAKEN_DECOMPRESS);
         g.x = xd; g.ldx = K; g.prologue = nml::PRO_NONE;
-        if (use_few(T)) return run_dense_few(g, part, part_avail, s);
+        if (use_few(T, R)) return run_dense_few(g, part, part_avail, s);
         return hip_status(nml::launch_gemm_dense(g, s));
       }
 
@@ -586,7 +597,7 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
       if (a->mode == NM_ACT_MASKED) {
         g.prologue = a->x_meta != nullptr ? nml::PRO_MASK : nml::PRO_NONE;
         g.x_mask = (const uint32_t*)a->x_meta;
-        if (a->x_meta == nullptr && use_few(T)) return run_dense_few(g, part, part_avail, s);
+        if (a->x_meta == nullptr && use_few(T, R)) return run_dense_few(g, part, part_avail, s);
         return hip_status(nml::launch_gemm_dense(g, s));
       }
 
@@ -596,7 +607,7 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
         if (a->workspace != nullptr && a->workspace_bytes >= need)
           return hip_status(nml::launch_gather1(a->m, (const uint16_t*)a->x, K, a->n, (const uint16_t*)a->w_kmajor, O,
                                                 a->y, a->accumulate, a->x_mask_out, (float*)a->workspace,
-                                                a->workspace_bytes, s));
+                                                a->workspace_bytes, R, s));
       }
       // ACT_DYNAMIC, one token, no mask asked for, n = m/2: the weight-streaming kernel
       // selects inside the X row it stages, with no separate select pass
@@ -610,11 +621,12 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
         }
       }
       // ACT_DYNAMIC, few tokens: select into S(X), then stream the weights
-      if (use_few(T) && have_ws) {
+      if (use_few(T, R) && have_ws) {
         uint16_t* sx = (uint16_t*)a->workspace;
         hipError_t e = nml::launch_select(a->m, (const uint16_t*)a->x, T, K, a->ldx, a->n, sx, K, a->x_mask_out,
                                           nullptr, nullptr, 0, s);
         if (e != hipSuccess) return NM_EHIP;
+        R.note(NM_TAKEN_SELECT);
         g.x = sx; g.ldx = K; g.prologue = nml::PRO_NONE;
         return run_dense_few(g, part, part_avail, s);
       }
@@ -627,25 +639,29 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
         hipError_t e = nml::launch_select(4, (const uint16_t*)a->x, T, K, a->ldx, 2, nullptr, 0, a->x_mask_out,
                                           xv, xm, 1, s);
         if (e != hipSuccess) return NM_EHIP;
+        R.note(NM_TAKEN_SELECT);
         nml::SparseArgs sa{};
+        sa.route = R;
         sa.w_vals = xv; sa.w_meta = xm; sa.kc = K;
         sa.x = (const uint16_t*)a->w; sa.ldx = a->ldw; sa.loader = nml::XL_PLAIN;
         sa.t = O; sa.o = T; sa.y = a->y; sa.ldy = a->ldy; sa.accumulate = a->accumulate; sa.trans_out = 1;
         return hip_status(nml::launch_gemm_sparse(sa, s));
       }
-      const ActRoute route = act_route(T);
+      const ActRoute route = act_route(T, R);
       uint32_t* mask = a->x_mask_out;
       if (route == ROUTE_SX && have_ws) {
         uint16_t* sx = (uint16_t*)a->workspace;
         hipError_t e = nml::launch_select(a->m, (const uint16_t*)a->x, T, K, a->ldx, a->n, sx, K, mask,
                                           nullptr, nullptr, 0, s);
         if (e != hipSuccess) return NM_EHIP;
+        R.note(NM_TAKEN_SELECT);
         g.prologue = nml::PRO_NONE; g.x = sx; g.ldx = K;
         const int64_t widen = fp8_widen_bytes(a), woff = align256(stage);
         if (widen > 0 && a->workspace_bytes >= woff + widen) {
           uint16_t* wb = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(a->workspace) + woff);
           e = nml::launch_widen_fp8((const uint8_t*)a->w, a->ldw, O, K, wb, s);
           if (e != hipSuccess) return NM_EHIP;
+          R.note(NM_TAKEN_WIDEN);
           g.w = wb; g.ldw = K; g.w_fp8 = 0;   // w_scale stays: applied in the epilogue
         }
         return hip_status(nml::launch_gemm_dense(g, s));
@@ -655,6 +671,7 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
         hipError_t e = nml::launch_select(a->m, (const uint16_t*)a->x, T, K, a->ldx, a->n, nullptr, 0, mask,
                                           nullptr, nullptr, 0, s);
         if (e != hipSuccess) return NM_EHIP;
+        R.note(NM_TAKEN_SELECT);
         g.prologue = nml::PRO_MASK; g.x_mask = mask;
         return hip_status(nml::launch_gemm_dense(g, s));
       }
@@ -692,15 +709,17 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
       }
       if (T == 0 || O == 0) return NM_OK;
       if (K == 0) return a->accumulate ? NM_OK : zero_output(a->y, T, O, a->ldy, s);
-      if (use_few(T)) {
+      const nml::Route R = route_of(a, true);
+      if (use_few(T, R)) {
         const int64_t tile = w_mode_tile_bytes(a, kc, ns);
         if (tile > 0 && a->workspace != nullptr && a->workspace_bytes >= tile) {
-          nml::SparseArgs sa = w_mode_sparse_args(a, kc, ns);
+          nml::SparseArgs sa = w_mode_sparse_args(a, kc, ns, true);
           int64_t off = 0;
           if (a->mode == NM_W_SLIDE) {
             uint16_t* xl = (uint16_t*)a->workspace;
             hipError_t e = nml::launch_lift(ns, (const uint16_t*)a->x, T, K, a->ldx, xl, lift_ld(kc), s);
             if (e != hipSuccess) return NM_EHIP;
+            R.note(NM_TAKEN_LIFT);
             sa.x = xl;
             off = align256(T * lift_ld(kc) * 2);
           }
@@ -711,6 +730,7 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
                                           a->workspace ? a->workspace_bytes : 0, s));
       }
       nml::SparseArgs sa{};
+      sa.route = R;
       sa.w_vals = (const uint16_t*)a->w; sa.w_meta = (const uint8_t*)a->w_meta; sa.kc = kc;
       sa.x = (const uint16_t*)a->x; sa.ldx = a->ldx; sa.ns = ns;
       sa.loader = a->mode == NM_W_SLIDE ? nml::XL_LIFT : nml::XL_PLAIN;
@@ -721,6 +741,7 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
         uint16_t* xl = (uint16_t*)a->workspace;
         hipError_t e = nml::launch_lift(ns, (const uint16_t*)a->x, T, K, a->ldx, xl, lift_ld(kc), s);
         if (e != hipSuccess) return NM_EHIP;
+        R.note(NM_TAKEN_LIFT);
         sa.x = xl; sa.ldx = lift_ld(kc); sa.loader = nml::XL_PLAIN;
         off = align256(T * lift_ld(kc) * 2);
       }
@@ -904,24 +925,26 @@ nm_status nm_hybrid_pack(const void* w, int64_t o, int64_t k, int64_t ldw, int64
                                             (uint16_t*)wd, ldwd, workspace, as_stream(stream)));
 }
 
-int64_t nm_hybrid_gemm_workspace_size(int64_t t, int64_t k_s, int64_t k_d, int64_t o, int gathered) {
+int64_t nm_hybrid_gemm_workspace_size(int64_t t, int64_t k_s, int64_t k_d, int64_t o, int gathered, uint32_t route) {
   if (t <= 0 || o <= 0 || k_s < 0 || k_d < 0 || (k_s == 0 && k_d == 0)) return 0;
+  nml::Route r{};
+  r.flags = route;
   const int64_t stage = gathered ? t * hybrid_ldp(k_s, k_d) * 2 : 0;
   int64_t part = 0;
-  if (use_few(t)) {
+  if (use_few(t, r)) {
     const int64_t ldp = gathered ? hybrid_ldp(k_s, k_d) : k_s + k_d;
     const nml::SparseArgs sa = hybrid_sparse_args(nullptr, ldp, gathered ? hybrid_off1(k_s) : k_s, t, k_s, k_d,
-                                                  nullptr, nullptr, nullptr, k_d, o, nullptr, o, 0);
+                                                  nullptr, nullptr, nullptr, k_d, o, nullptr, o, 0, r);
     part = sp_few_tile(sa) ? nml::gemm_lds_sp_small_part_bytes(sa)
                            : nml::few_partial_bytes(few_hybrid_args(nullptr, ldp, 0, t, k_s, k_d, nullptr, nullptr,
-                                                                    nullptr, k_d, o, nullptr, o, 0));
+                                                                    nullptr, k_d, o, nullptr, o, 0, r));
   }
   if (part > 0) return align256(stage) + part;
-  if (!use_few(t) && k_s > 0) {
+  if (!use_few(t, r) && k_s > 0) {
     // large-token product: [permuted X][K-blocked positions]
     const int64_t ldp = gathered ? hybrid_ldp(k_s, k_d) : k_s + k_d;
     const nml::SparseArgs sa = hybrid_sparse_args(nullptr, ldp, gathered ? hybrid_off1(k_s) : k_s, t, k_s, k_d,
-                                                  nullptr, nullptr, nullptr, k_d, o, nullptr, o, 0);
+                                                  nullptr, nullptr, nullptr, k_d, o, nullptr, o, 0, r);
     const int64_t mb = meta_block_ws(sa);
     if (mb > 0) return align256(stage) + mb;
   }
@@ -931,7 +954,8 @@ int64_t nm_hybrid_gemm_workspace_size(int64_t t, int64_t k_s, int64_t k_d, int64
 nm_status nm_hybrid_gemm(const void* x, int64_t t, int64_t ldx, const int32_t* sparse_cols, int64_t k_s,
                          const int32_t* dense_cols, int64_t k_d, const void* ws_values, const void* ws_meta,
                          nm_meta fmt, const void* wd, int64_t ldwd, int64_t o, float* y, int64_t ldy,
-                         int accumulate, void* workspace, int64_t workspace_bytes, void* stream) {
+                         int accumulate, void* workspace, int64_t workspace_bytes, uint32_t route,
+                         uint32_t* route_taken, void* stream) {
   if (t < 0 || o < 0 || k_s < 0 || k_d < 0) return NM_ESHAPE;
   if ((k_s % 4) != 0) return NM_ESHAPE;
   if (accumulate != 0 && accumulate != 1) return NM_EINVAL;
@@ -964,6 +988,9 @@ nm_status nm_hybrid_gemm(const void* x, int64_t t, int64_t ldx, const int32_t* s
   const hipStream_t s = as_stream(stream);
   if (k_s == 0 && k_d == 0) return accumulate ? NM_OK : zero_output(y, t, o, ldy, s);
 
+  nml::Route R{};
+  R.flags = route;
+  R.taken = route_taken;
   const uint16_t* xa = (const uint16_t*)x;
   int64_t lda = ldx, dbase = k_s;
   if (gathered) {
@@ -972,17 +999,18 @@ nm_status nm_hybrid_gemm(const void* x, int64_t t, int64_t ldx, const int32_t* s
     hipError_t e = nml::launch_permute_cols((const uint16_t*)x, t, ldx, kx, sparse_cols, k_s, dense_cols, k_d,
                                             hybrid_off1(k_s), xp, ldp, s);
     if (e != hipSuccess) return NM_EHIP;
+    R.note(NM_TAKEN_PERMUTE);
     xa = xp; lda = ldp; dbase = hybrid_off1(k_s);
   }
   nml::SparseArgs sa = hybrid_sparse_args(xa, lda, dbase, t, k_s, k_d, ws_values, ws_meta, wd, ldwd, o, y, ldy,
-                                          accumulate);
-  if (use_few(t)) {
+                                          accumulate, R);
+  if (use_few(t, R)) {
     int64_t avail = 0;
     float* part = ws_slice(workspace, workspace_bytes, stage > 0 ? align256(stage) : 0, &avail);
     if (sp_few_tile(sa) && avail >= nml::gemm_lds_sp_small_part_bytes(sa))
       return hip_status(nml::launch_gemm_lds_sp_small(sa, part, avail, s));
     return hip_status(nml::launch_few(few_hybrid_args(xa, lda, dbase, t, k_s, k_d, ws_values, ws_meta, wd, ldwd, o,
-                                                      y, ldy, accumulate),
+                                                      y, ldy, accumulate, R),
                                       part, avail, s));
   }
   if ((st = use_meta_block(sa, workspace, workspace_bytes, stage > 0 ? align256(stage) : 0, s))) return st;

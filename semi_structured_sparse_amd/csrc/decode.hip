@@ -973,11 +973,6 @@ struct Plan {
   int64_t splits;
 };
 
-int env_int(const char* name) {   // A/B measurement overrides
-  const char* e = std::getenv(name);
-  return e ? std::atoi(e) : 0;
-}
-
 Plan make_plan(const FewArgs& a, bool allow_split) {
   Plan p;
   p.tb = a.t <= 16 ? 1 : a.t <= 32 ? 2 : a.t <= 64 ? 4 : 8;
@@ -991,7 +986,7 @@ Plan make_plan(const FewArgs& a, bool allow_split) {
     const int64_t c = (a.seg[i].k + ck - 1) / ck;
     chunks = c > chunks ? c : chunks;
   }
-  const int ew = env_int("NM_FEW_WPB"), es = env_int("NM_FEW_SPLITS");
+  const int ew = a.route.few_wpb, es = a.route.few_splits;   // caller's partition (0: chosen here)
   const int64_t nob = (a.o + 16 * p.rw - 1) / (16 * p.rw);
   // about one workgroup of max_wpb waves per CU (256 CUs); many row blocks -> fewer waves
   // per block, few row blocks -> the reduction is also split across workgroups
@@ -1028,7 +1023,7 @@ hipError_t launch_k(const FewArgs& a, const Plan& p, float* part, hipStream_t s)
     if (p.wpb > Dma<TB>::WPB) return hipErrorInvalidConfiguration;
     if constexpr (TB == 1) {
       // one token: stage the X rows in LDS next to the weight rings when they fit
-      // (NM_FEWD_XLDS=0 keeps the register loads, for A/B measurement)
+      // (the NM_ROUTE_NO_XLDS hint keeps the register loads)
       // rows of whole 16-byte pieces from 16-byte aligned starts, staged in whole KiB
       const int64_t xn0 = XL0 == XL_LIFT ? a.seg[0].k / (4 * (NS - 1)) * (2 * NS) : a.seg[0].k;
       const int64_t xn1 = a.nseg > 1 ? a.seg[1].k : 0;
@@ -1038,8 +1033,7 @@ hipError_t launch_k(const FewArgs& a, const Plan& p, float* part, hipStream_t s)
         return n == 0 || (n >= 8 && (n % 8) == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0);
       };
       const bool rows_ok = piece_ok(a.seg[0].x, xn0) && (a.nseg < 2 || piece_ok(a.seg[1].x, xn1)) && xn0 > 0;
-      const char* e = std::getenv("NM_FEWD_XLDS");
-      if (a.t == 1 && rows_ok && ring + xbytes <= 163840 && !(e != nullptr && std::strcmp(e, "0") == 0)) {
+      if (a.t == 1 && rows_ok && ring + xbytes <= 163840 && !a.route.has(NM_ROUTE_NO_XLDS)) {
         auto kern = k_fewd<TB, WK0, XL0, NS, WK1, true>;
         if constexpr (XL0 == XL_PLAIN && WK1 == WK_NONE && (WK0 == WK_BF16 || WK0 == WK_FP8)) {
           switch (a.sel_m) {
@@ -1055,12 +1049,15 @@ hipError_t launch_k(const FewArgs& a, const Plan& p, float* part, hipStream_t s)
         }
         hipError_t ae = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)xbytes);
         if (ae != hipSuccess) return ae;
+        a.route.note(NM_TAKEN_FEW_STREAM | NM_TAKEN_FEW_XLDS | (a.sel_m != 0 ? NM_TAKEN_FEW_SELECT : 0u) |
+                     (WK0 == WK_SP24 ? NM_TAKEN_SPARSE_MMA : 0u));
         kern<<<dim3((unsigned)blocks), dim3(64 * p.wpb), (size_t)xbytes, s>>>(
             a.seg[0], s1, a.w_scale, a.t, a.o, a.y, a.ldy, a.accumulate, pp, (int)p.splits, (int)xn0, (int)xn1);
         return hipGetLastError();
       }
     }
     if (a.sel_m != 0) return hipErrorInvalidValue;   // selection needs the staged row
+    a.route.note(NM_TAKEN_FEW_STREAM | (WK0 == WK_SP24 ? NM_TAKEN_SPARSE_MMA : 0u));
     k_fewd<TB, WK0, XL0, NS, WK1, false><<<dim3((unsigned)blocks), dim3(64 * p.wpb), 0, s>>>(
         a.seg[0], s1, a.w_scale, a.t, a.o, a.y, a.ldy, a.accumulate, pp, (int)p.splits, 0, 0);
   } else {
@@ -1071,6 +1068,7 @@ hipError_t launch_k(const FewArgs& a, const Plan& p, float* part, hipStream_t s)
       if (e != hipSuccess) return e;
     }
     if (a.sel_m != 0) return hipErrorInvalidValue;
+    a.route.note(NM_TAKEN_FEW_STREAM | (WK0 == WK_SP24 ? NM_TAKEN_SPARSE_MMA : 0u));
     kern<<<dim3((unsigned)blocks), dim3(64 * p.wpb), lds, s>>>(a.seg[0], s1, a.w_scale, a.t, a.o, a.y, a.ldy,
                                                                a.accumulate, pp, (int)p.splits);
   }
@@ -1111,10 +1109,7 @@ int64_t few_partial_bytes(const FewArgs& a) {
 }
 
 bool few_select_in_kernel(const FewArgs& a) {
-  const char* e = std::getenv("NM_FEW_SELECT");
-  if (e != nullptr && std::strcmp(e, "0") == 0) return false;
-  const char* ex = std::getenv("NM_FEWD_XLDS");
-  if (ex != nullptr && std::strcmp(ex, "0") == 0) return false;
+  if (a.route.has(NM_ROUTE_NO_FEW_SELECT) || a.route.has(NM_ROUTE_NO_XLDS)) return false;
   if (a.t != 1 || a.nseg != 1 || a.o <= 0) return false;
   const int m = a.sel_m;
   if (m != 4 && m != 8 && m != 16 && m != 32) return false;
@@ -1151,7 +1146,7 @@ hipError_t launch_few(const FewArgs& a, float* part, int64_t part_bytes, hipStre
     e = launch_lift(a, p, part, s);
   }
   if (e != hipSuccess || p.splits == 1) return e;
-  return launch_reduce_parts(part, p.splits, a.w_scale, a.t, a.o, a.y, a.ldy, a.accumulate, s);
+  return launch_reduce_parts(part, p.splits, a.w_scale, a.t, a.o, a.y, a.ldy, a.accumulate, a.route, s);
 }
 
 int64_t gather1_part_bytes(int64_t k, int64_t o, int m) {
@@ -1160,7 +1155,8 @@ int64_t gather1_part_bytes(int64_t k, int64_t o, int m) {
 }
 
 hipError_t launch_gather1(int m, const uint16_t* x, int64_t k, int n, const uint16_t* wk, int64_t o, float* y,
-                          int accumulate, uint32_t* mask_out, float* part, int64_t part_bytes, hipStream_t s) {
+                          int accumulate, uint32_t* mask_out, float* part, int64_t part_bytes, const Route& r,
+                          hipStream_t s) {
   const G1Plan p = g1_plan(k, o, m);
   if (part == nullptr || part_bytes < p.nks * o * 4 || (o % 8) != 0) return hipErrorInvalidValue;
   const int64_t blocks = p.nks * p.nochunk;
@@ -1175,13 +1171,15 @@ hipError_t launch_gather1(int m, const uint16_t* x, int64_t k, int n, const uint
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_reduce_parts(part, p.nks, nullptr, 1, o, y, o, accumulate, s);   // one row: ldy unused
+  r.note(NM_TAKEN_GATHER1);
+  return launch_reduce_parts(part, p.nks, nullptr, 1, o, y, o, accumulate, r, s);   // one row: ldy unused
 }
 
 hipError_t launch_reduce_parts(const float* part, int64_t splits, const float* w_scale, int64_t t, int64_t o,
-                               float* y, int64_t ldy, int accumulate, hipStream_t s) {
+                               float* y, int64_t ldy, int accumulate, const Route& r, hipStream_t s) {
   const int64_t n = t * o;
   if (n == 0) return hipSuccess;
+  r.note(NM_TAKEN_REDUCE);
   // y is 16-byte aligned (checked at the boundary); float4 rows need o and ldy % 4 == 0
   if (splits >= 1 && splits <= 16 && o % 4 == 0 && ldy % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0 &&
       (reinterpret_cast<uintptr_t>(part) & 15) == 0) {

@@ -317,11 +317,12 @@ hipError_t launch_m(const nml::GemmArgs& a, hipStream_t s) {
 namespace nml {
 
 hipError_t launch_gemm_dense(const GemmArgs& a, hipStream_t s) {
-  // NM_GEMM=regs / lds overrides the kernel choice (A/B measurement and tests)
-  const char* force = std::getenv("NM_GEMM");
-  const bool regs_only = force != nullptr && std::strcmp(force, "regs") == 0;
-  const bool lds_any = force != nullptr && std::strcmp(force, "lds") == 0;
+  // the NM_ROUTE_TILE_REGS / NM_ROUTE_TILE_LDS hints override the kernel choice
+  const bool regs_only = a.route.has(NM_ROUTE_TILE_REGS);
+  const bool lds_any = a.route.has(NM_ROUTE_TILE_LDS);
   if (!regs_only && gemm_lds_eligible(a, lds_any)) return launch_gemm_lds(a, s);
+  a.route.note(NM_TAKEN_TILE_REGS | (a.prologue == PRO_SELECT ? NM_TAKEN_FUSED_SELECT : 0u) |
+               (a.prologue == PRO_MASK ? NM_TAKEN_MASK : 0u));
   if (a.w_fp8) {
     switch (a.prologue) {
       case PRO_NONE: return launch_m<PRO_NONE, true>(a, s);

@@ -395,20 +395,13 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
   }
 }
 
-static int env_int(const char* name, int dflt) {
-  const char* e = std::getenv(name);
-  return e != nullptr ? std::atoi(e) : dflt;
-}
-
 // o-tiles per band of the XCD-aware tile order.  An XCD runs 32 tiles at a time (one per
 // CU); a band g o-tiles wide makes that set g o-tiles x 32/g t-tiles, whose K-step
 // footprint g*BM + (32/g)*BN rows is smallest near g = sqrt(32 BN / BM).  Measured on
 // gfx950 at 8192 x 14336 x 4096: bands of 8 (or 4) o-tiles 711 us, of 16 736-820 us
 // (every XCD then streamed all of W twice: 2.1 GB of L2 fills per launch).
-// NM_GEMM_GROUP=<g> overrides for A/B measurement.
 static int group_for(int tiles_m, int bm, int bn) {
-  int g = env_int("NM_GEMM_GROUP", bn >= bm ? 8 : 4);
-  if (g < 1) g = 1;
+  const int g = bn >= bm ? 8 : 4;
   return g < tiles_m ? g : tiles_m;
 }
 
@@ -425,8 +418,9 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s, int64_t splits, float* p
       (const unsigned char*)a.w, a.ldw, a.x, a.ldx, a.x_mask, a.t, a.o, a.k, a.y, a.ldy, a.accumulate, tiles_m, tiles_n,
       kslice, splits > 1 ? part : nullptr, a.w_scale, group_for(tiles_m, BM, BN));
   hipError_t e = hipGetLastError();
+  a.route.note(NM_TAKEN_TILE_LDS | (PRO == PRO_MASK ? NM_TAKEN_MASK : 0u) | (splits > 1 ? NM_TAKEN_TILE_SPLIT : 0u));
   if (e != hipSuccess || splits == 1) return e;
-  return launch_reduce_parts(part, splits, a.w_scale, a.t, a.o, a.y, a.ldy, a.accumulate, s);
+  return launch_reduce_parts(part, splits, a.w_scale, a.t, a.o, a.y, a.ldy, a.accumulate, a.route, s);
 }
 
 }  // namespace
@@ -491,28 +485,14 @@ hipError_t launch_widen_fp8(const uint8_t* w8, int64_t ldw, int64_t o, int64_t k
 // grid has as many workgroups as fit one per CU (the splits' fp32 partial tiles are
 // summed in slice order by a second kernel).  Measured on gfx950 for 33-128 tokens: one
 // workgroup per CU beats two (twice the partial-sum traffic) and beats 256-row tiles
-// (fewer tiles, so more splits); four LDS stages (three K-steps in flight) measured level
-// with two.  NM_TILE_BM=256, NM_TILE_WAVES=4, NM_TILE_STAGES=4 and NM_TILE_WG=<n> (target
-// workgroups) select the other shapes for A/B measurement.
-struct SmallCfg {
-  int bm, bn, waves;
-  int64_t target;
-};
-
-static SmallCfg small_cfg(const GemmArgs& a) {
-  SmallCfg c;
-  c.bn = a.t <= 64 ? 64 : 128;
-  c.bm = (env_int("NM_TILE_BM", 128) == 256 && !a.w_fp8) ? 256 : 128;
-  c.waves = env_int("NM_TILE_WAVES", 8) == 4 ? 4 : 8;
-  c.target = env_int("NM_TILE_WG", 256);
-  if (c.target < 1) c.target = 1;
-  return c;
-}
-
+// (fewer tiles, so more splits); four LDS stages (three K-steps in flight) and four waves
+// of 64 x 32 measured level with two stages and eight waves.  The route's tile_wg sets
+// another target workgroup count.
 static int64_t small_splits(const GemmArgs& a) {
-  const SmallCfg c = small_cfg(a);
-  const int64_t tiles = ((a.o + c.bm - 1) / c.bm) * ((a.t + c.bn - 1) / c.bn);
-  int64_t splits = c.target / tiles;
+  const int64_t bn = a.t <= 64 ? 64 : 128;
+  const int64_t target = a.route.tile_wg > 0 ? a.route.tile_wg : 256;
+  const int64_t tiles = ((a.o + 127) / 128) * ((a.t + bn - 1) / bn);
+  int64_t splits = target / tiles;
   const int64_t ksteps = a.k / BK;
   if (splits > ksteps / 2) splits = ksteps / 2;
   return splits < 1 ? 1 : splits;
@@ -530,27 +510,11 @@ int64_t gemm_lds_small_part_bytes(const GemmArgs& a) {
 hipError_t launch_gemm_lds_small(const GemmArgs& a, float* part, int64_t part_bytes, hipStream_t s) {
   int64_t splits = small_splits(a);
   if (part == nullptr || part_bytes < splits * a.t * a.o * 4) splits = 1;
-  const SmallCfg c = small_cfg(a);
-  const bool st4 = env_int("NM_TILE_STAGES", 2) == 4;
   if (a.w_fp8) {
-    if (a.t <= 64) {
-      if (st4) return launch_cfg<128, 64, 4, 2, PRO_NONE, true, 4>(a, s, splits, part);
-      return launch_cfg<128, 64, 4, 2, PRO_NONE, true>(a, s, splits, part);
-    }
-    if (st4) return launch_cfg<128, 128, 4, 2, PRO_NONE, true, 4>(a, s, splits, part);
+    if (a.t <= 64) return launch_cfg<128, 64, 4, 2, PRO_NONE, true>(a, s, splits, part);
     return launch_cfg<128, 128, 4, 2, PRO_NONE, true>(a, s, splits, part);
   }
-  if (c.bm == 256) {
-    if (a.t <= 64) return launch_cfg<256, 64, 8, 1, PRO_NONE>(a, s, splits, part);
-    return launch_cfg<256, 128, 4, 2, PRO_NONE>(a, s, splits, part);
-  }
-  if (a.t <= 64) {
-    if (c.waves == 4) return launch_cfg<128, 64, 2, 2, PRO_NONE>(a, s, splits, part);
-    if (st4) return launch_cfg<128, 64, 4, 2, PRO_NONE, false, 4>(a, s, splits, part);
-    return launch_cfg<128, 64, 4, 2, PRO_NONE>(a, s, splits, part);
-  }
-  if (c.waves == 4) return launch_cfg<128, 128, 2, 2, PRO_NONE>(a, s, splits, part);
-  if (st4) return launch_cfg<128, 128, 4, 2, PRO_NONE, false, 4>(a, s, splits, part);
+  if (a.t <= 64) return launch_cfg<128, 64, 4, 2, PRO_NONE>(a, s, splits, part);
   return launch_cfg<128, 128, 4, 2, PRO_NONE>(a, s, splits, part);
 }
 

@@ -329,11 +329,9 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
 
 // o-tiles per band of the XCD-aware tile order: an XCD runs 32 tiles at a time, and a
 // band g o-tiles wide keeps their K-step footprint g*BM + (32/g)*BN rows near its minimum
-// (as for the dense direct-to-LDS kernel).  NM_GEMM_GROUP=<g> overrides for A/B.
+// (as for the dense direct-to-LDS kernel).
 static int group_for(int tiles_m, int bm, int bn) {
-  const char* e = std::getenv("NM_GEMM_GROUP");
-  int g = e != nullptr ? std::atoi(e) : (bn >= bm ? 8 : 4);
-  if (g < 1) g = 1;
+  const int g = bn >= bm ? 8 : 4;
   return g < tiles_m ? g : tiles_m;
 }
 
@@ -390,8 +388,9 @@ hipError_t launch_sp_cfg(const SparseArgs& a, hipStream_t s, int64_t splits, flo
   }
 #undef NM_SP_LAUNCH
   hipError_t e = hipGetLastError();
+  a.route.note(NM_TAKEN_TILE_LDS | NM_TAKEN_SPARSE_MMA | (splits > 1 ? NM_TAKEN_TILE_SPLIT : 0u));
   if (e != hipSuccess || splits == 1) return e;
-  return launch_reduce_parts(part, splits, nullptr, a.t, a.o, a.y, a.ldy, a.accumulate, s);
+  return launch_reduce_parts(part, splits, nullptr, a.t, a.o, a.y, a.ldy, a.accumulate, a.route, s);
 }
 
 // Few-token split: 128-row tiles, as many workgroups as fit one per CU.
@@ -399,7 +398,7 @@ int64_t sp_small_splits(const SparseArgs& a) {
   const int bn = a.t <= 64 ? 64 : 128;
   const int64_t tiles = ((a.o + 127) / 128) * ((a.t + bn - 1) / bn);
   const int64_t nk = a.kc / (a.f8 ? 128 : 64) + a.kd / 64;
-  int64_t splits = 256 / tiles;
+  int64_t splits = (a.route.tile_wg > 0 ? a.route.tile_wg : 256) / tiles;
   if (splits > nk / 2) splits = nk / 2;
   return splits < 1 ? 1 : splits;
 }
@@ -433,9 +432,7 @@ hipError_t launch_meta_block(const uint8_t* meta, int64_t o, int64_t kc, int uni
 
 hipError_t launch_gemm_lds_sp(const SparseArgs& a, hipStream_t s) {
   // waves of 128 (o) x 64 (t): the dense X operand, read by WM waves, is the larger LDS
-  // read stream, so WM = 2 beats 4 (measured 1-4% on gfx950); NM_SP_WAVES=4x2 for A/B
-  const char* e = std::getenv("NM_SP_WAVES");
-  if (e != nullptr && std::strcmp(e, "4x2") == 0) return launch_sp_cfg<256, 256, 4, 2>(a, s, 1, nullptr);
+  // read stream, so WM = 2 beats 4 (measured 1-4% on gfx950)
   return launch_sp_cfg<256, 256, 2, 4>(a, s, 1, nullptr);
 }
 

@@ -383,15 +383,13 @@ hipError_t launch_pick(const nml::SparseArgs& a, hipStream_t s) {
 namespace nml {
 
 bool gemm_sparse_uses_lds(const SparseArgs& a) {
-  // NM_GEMM=regs / lds overrides the kernel choice (A/B measurement and tests)
-  const char* force = std::getenv("NM_GEMM");
-  const bool regs_only = force != nullptr && std::strcmp(force, "regs") == 0;
-  const bool lds_any = force != nullptr && std::strcmp(force, "lds") == 0;
-  return !regs_only && gemm_lds_sp_eligible(a, lds_any);
+  // the NM_ROUTE_TILE_REGS / NM_ROUTE_TILE_LDS hints override the kernel choice
+  return !a.route.has(NM_ROUTE_TILE_REGS) && gemm_lds_sp_eligible(a, a.route.has(NM_ROUTE_TILE_LDS));
 }
 
 hipError_t launch_gemm_sparse(const SparseArgs& a, hipStream_t s) {
   if (gemm_sparse_uses_lds(a)) return launch_gemm_lds_sp(a, s);
+  a.route.note(NM_TAKEN_TILE_REGS | NM_TAKEN_SPARSE_MMA);
   switch (a.loader) {
     case XL_PLAIN: return launch_pick<XL_PLAIN>(a, s);
     case XL_LIFT: return launch_pick<XL_LIFT>(a, s);

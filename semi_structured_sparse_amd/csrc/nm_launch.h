@@ -3,7 +3,22 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "nm.h"
+
 namespace nml {
+
+// The caller's route hints (NM_ROUTE_* bits and tuning values, nm.h) travel with every
+// call's arguments; `taken` (a host pointer or null) collects NM_TAKEN_* bits of the
+// kernels the call enqueues.  Nothing is read from the process environment.
+struct Route {
+  uint32_t flags;
+  int few_wpb, few_splits, tile_wg;
+  uint32_t* taken;
+  bool has(uint32_t bit) const { return (flags & bit) != 0; }
+  void note(uint32_t bits) const {
+    if (taken != nullptr) *taken |= bits;
+  }
+};
 
 // scored top-n (m in {4, 8, 16, 32}): score = fp32(|x|) * col_score[k] (use_x) or
 // col_score[k] alone; outputs S(X) and/or the bitmask
@@ -41,6 +56,7 @@ struct GemmArgs {
   int64_t ldy;
   int accumulate;
   uint32_t* mask_out;     // PRO_SELECT: optional mask export
+  Route route;
 };
 hipError_t launch_gemm_dense(const GemmArgs& a, hipStream_t s);
 // direct-to-LDS variant for large PRO_NONE / PRO_MASK problems with K % 64 == 0
@@ -84,6 +100,7 @@ struct SparseArgs {
   int f8;
   const float* x_scale;
   const float* w_scale;
+  Route route;
 };
 hipError_t launch_gemm_sparse(const SparseArgs& a, hipStream_t s);
 // whether launch_gemm_sparse hands this call to the direct-to-LDS kernel
@@ -145,10 +162,12 @@ struct FewArgs {
   int64_t ldy;
   int accumulate;
   int sel_m;              // > 0: seg[0].x is X itself; keep the m/2 largest of every m (see below)
+  Route route;
 };
 // One token, one plain dense segment (bf16 or fp8 W), m in {4, 8, 16, 32}: whether
 // launch_few applies the n = m/2 selection to the X row inside the product (the row
-// staged in LDS), so that no separate select pass is needed.  NM_FEW_SELECT=0: never.
+// staged in LDS), so that no separate select pass is needed (never under the
+// NM_ROUTE_NO_FEW_SELECT or NM_ROUTE_NO_XLDS hints).
 bool few_select_in_kernel(const FewArgs& a);
 // Scratch bytes of fp32 partial sums the preferred launch uses (0: single pass).
 int64_t few_partial_bytes(const FewArgs& a);
@@ -159,10 +178,11 @@ hipError_t launch_few(const FewArgs& a, float* part, int64_t part_bytes, hipStre
 // sum over the n:m-selected k of x[k] * wk[k][o]; part: scratch of gather1_part_bytes.
 int64_t gather1_part_bytes(int64_t k, int64_t o, int m);
 hipError_t launch_gather1(int m, const uint16_t* x, int64_t k, int n, const uint16_t* wk, int64_t o, float* y,
-                          int accumulate, uint32_t* mask_out, float* part, int64_t part_bytes, hipStream_t s);
+                          int accumulate, uint32_t* mask_out, float* part, int64_t part_bytes, const Route& r,
+                          hipStream_t s);
 // y[t][o] (=|+=) w_scale[o] * sum_{s < splits} part[s][t][o]   (part rows have stride o)
 hipError_t launch_reduce_parts(const float* part, int64_t splits, const float* w_scale, int64_t t, int64_t o,
-                               float* y, int64_t ldy, int accumulate, hipStream_t s);
+                               float* y, int64_t ldy, int accumulate, const Route& r, hipStream_t s);
 // xo[t][j] = x[t][c0[j]] (j < k0), xo[t][off1 + j] = x[t][c1[j]] (j < k1); indices
 // clamped to [0, kx)
 hipError_t launch_permute_cols(const uint16_t* x, int64_t t, int64_t ldx, int64_t kx, const int32_t* c0, int64_t k0,

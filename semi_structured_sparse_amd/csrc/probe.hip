@@ -8,7 +8,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "nm.h"
+#include "nm_probe.h"
 #include "nm_device.h"
 
 namespace {

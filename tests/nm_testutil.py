@@ -1,5 +1,8 @@
-"""Helpers shared by the GPU tests: host<->device copies of bit arrays and the GEMM
-tolerance check (relative Frobenius <= 1e-3 and |err| <= 1e-2 * (|A|.|B|) + 1e-4)."""
+"""Helpers shared by the GPU tests: host<->device copies of bit arrays, the GEMM tolerance
+check (relative Frobenius <= 1e-3 and |err| <= 1e-2 * (|A|.|B|) + 1e-4 against the oracle's
+fp32-accumulated product), and the whole-output checks of full-size products: one row of
+every band of output rows against the oracle, no unwritten (NaN pre-filled) element
+anywhere, and random projections of the whole output."""
 import numpy as np
 
 import oracle as O
@@ -72,4 +75,38 @@ def check_gemm_vals(y, y_ref, a_vals, b_vals, label=""):
     worst = (err - ELT_REL * bound - ELT_ABS).max() if err.size else -1
     assert rel <= REL_FRO, f"{label} relative Frobenius error {rel:.3e}"
     assert worst <= 0, f"{label} per-element bound exceeded by {worst:.3e}"
+    return rel
+
+
+def band_rows(t, band=128, seed=0):
+    """One random row from every band of `band` consecutive output rows (so every tile of
+    rows of that height has a checked row), plus the first and the last row."""
+    rng = np.random.default_rng(seed)
+    r = {0, t - 1}
+    for b0 in range(0, t, band):
+        r.add(int(rng.integers(b0, min(t, b0 + band))))
+    return np.array(sorted(r))
+
+
+def check_all_written(y_dev, label=""):
+    """The output was pre-filled with NaN: every element must have been written with a
+    finite value (checked on the device, over the whole output)."""
+    import torch
+
+    bad = int((~torch.isfinite(y_dev)).sum().item())
+    assert bad == 0, f"{label}: {bad} output elements unwritten or not finite"
+
+
+def check_projection(y, a_vals, b_vals, label="", nproj=8, seed=0):
+    """Whole-output check through random projections: (A . B^T) . R = A . (B^T . R) for a
+    Gaussian R [O][nproj].  A wrong or misplaced tile anywhere in y changes its projections
+    by about its share of the output's norm, far above the 1e-3 relative bound.
+    a_vals [T][K] and b_vals [O][K] are the operands contracted (fp64 values), y the
+    output [T][O] (host)."""
+    y = np.asarray(y, dtype=np.float64)
+    r = np.random.default_rng(seed).standard_normal((y.shape[1], nproj))
+    got = y @ r
+    ref = np.asarray(a_vals, np.float64) @ (np.asarray(b_vals, np.float64).T @ r)
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
+    assert rel <= REL_FRO, f"{label}: projection relative error {rel:.3e}"
     return rel

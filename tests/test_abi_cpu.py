@@ -2,6 +2,7 @@
 declares, and rejects every malformed call with the documented status before any HIP
 call is made.  Pointers here are fake, aligned or misaligned addresses that are never
 dereferenced (validation fails first, or the call is a documented no-op)."""
+import math
 import os
 import re
 import subprocess
@@ -16,22 +17,62 @@ Q = 8192
 MIS = 4098        # misaligned
 
 
-def declared_functions():
-    src = open(os.path.join(ROOT, "include", "nm.h")).read()
+def declared_functions(header="nm.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(nm_[a-z0-9_]+)\s*\(", src)))
+
+
+def exported_functions(path):
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
+    return set(re.findall(r"\bT (nm_[a-z0-9_]+)", out))
 
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert {"nm_sparsify", "nm_compress", "nm_lower_slide", "nm_spmm", "nm_hybrid_gemm"} <= set(names)
-    out = subprocess.run(["nm", "-D", "--defined-only", S.LIB_PATH], capture_output=True, text=True).stdout
-    exported = set(re.findall(r"\bT (nm_[a-z0-9_]+)", out))
+    exported = exported_functions(S.LIB_PATH)
     missing = [n for n in names if n not in exported]
     assert not missing, missing
     L = S.lib()
     for n in names:
         assert hasattr(L, n)
+    # the measurement helpers are a library of their own, not part of the product's ABI
+    from semi_structured_sparse_amd import probe
+    pnames = declared_functions("nm_probe.h")
+    assert pnames and not (set(pnames) & exported)
+    assert set(pnames) <= exported_functions(probe.PROBE_LIB_PATH)
+
+
+def test_library_reads_no_environment():
+    """The boundary is stateless: routes come from the call's arguments, never from the
+    process environment (the library imports no getenv / secure_getenv)."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", S.LIB_PATH], capture_output=True, text=True).stdout
+    assert not re.search(r"\b(secure_)?getenv\b", out), out
+
+
+def test_route_fields_change_routes_not_results_host_side():
+    """Route hints steer the workspace query (which is host arithmetic); the query never
+    writes the caller's report."""
+    a = spmm_args(t=64, o=4096, k=14336, n=8, m=16, ldx=14336, ldw=14336, ldy=4096)
+    auto = S.nm_spmm_workspace_size(a)
+    a.route = S.route_bits("no_few")
+    no_few = S.nm_spmm_workspace_size(a)
+    a.route = S.route_bits("few_stream")
+    stream = S.nm_spmm_workspace_size(a)
+    assert auto >= 64 * 14336 * 2 and no_few >= 64 * 14336 * 2
+    assert auto != stream            # the split tile route and the streaming route need different scratch
+    assert S.route_taken(a) == 0
+    assert set(S.ROUTE.values()) == {1 << i for i in range(12)}
+    assert set(S.TAKEN.values()) == {1 << i for i in range(18)}
+    # the header's values are the binding's
+    src = open(os.path.join(ROOT, "include", "nm.h")).read()
+    for name, bit in S.ROUTE.items():
+        i = int(math.log2(bit))
+        assert re.search(rf"NM_ROUTE_{name.upper()} = 1u << {i}\b", src), name
+    for name, bit in S.TAKEN.items():
+        i = int(math.log2(bit))
+        assert re.search(rf"NM_TAKEN_{name.upper()} = 1u << {i}\b", src), name
 
 
 def test_status_strings_and_version():
@@ -257,13 +298,14 @@ def test_binding_lowered_k_matches_oracle():
 def test_probe_helpers_host_side():
     """Measurement helpers: sizes are host arithmetic; bad arguments are rejected before
     any GPU call."""
-    assert S.nm_probe_sink_bytes() >= 2048 * 256 * 4
-    assert S.nm_probe_mfma_flops(10) == 1024 * 4 * 16 * 10 * 16 * 16 * 32 * 2
-    assert S.nm_probe_mfma_flops(-1) == 0
-    assert S.nm_probe_read(None, -16, None, check=False, stream=0) == S.NM_ESHAPE
-    assert S.nm_probe_read(None, 24, None, check=False, stream=0) == S.NM_ESHAPE
-    assert S.nm_probe_read(None, 32, None, check=False, stream=0) == S.NM_EINVAL
-    assert S.nm_probe_read(16 * 1024 + 4, 32, 16 * 1024, check=False, stream=0) == S.NM_EALIGN
-    assert S.nm_probe_mfma(-1, 16 * 1024, check=False, stream=0) == S.NM_ESHAPE
-    assert S.nm_probe_mfma(1, None, check=False, stream=0) == S.NM_EINVAL
-    assert S.nm_probe_mfma(1, 16 * 1024 + 8, check=False, stream=0) == S.NM_EALIGN
+    from semi_structured_sparse_amd import probe as P_
+    assert P_.nm_probe_sink_bytes() >= 2048 * 256 * 4
+    assert P_.nm_probe_mfma_flops(10) == 1024 * 4 * 16 * 10 * 16 * 16 * 32 * 2
+    assert P_.nm_probe_mfma_flops(-1) == 0
+    assert P_.nm_probe_read(None, -16, None, check=False, stream=0) == S.NM_ESHAPE
+    assert P_.nm_probe_read(None, 24, None, check=False, stream=0) == S.NM_ESHAPE
+    assert P_.nm_probe_read(None, 32, None, check=False, stream=0) == S.NM_EINVAL
+    assert P_.nm_probe_read(16 * 1024 + 4, 32, 16 * 1024, check=False, stream=0) == S.NM_EALIGN
+    assert P_.nm_probe_mfma(-1, 16 * 1024, check=False, stream=0) == S.NM_ESHAPE
+    assert P_.nm_probe_mfma(1, None, check=False, stream=0) == S.NM_EINVAL
+    assert P_.nm_probe_mfma(1, 16 * 1024 + 8, check=False, stream=0) == S.NM_EALIGN

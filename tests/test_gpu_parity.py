@@ -3,16 +3,21 @@
 Integer / byte work (masks, S(X), compressed values, index bytes, 2-bit metadata,
 lowered windows, hybrid column lists and packed weights) must match the oracle bit for
 bit.  Products must meet: relative Frobenius error <= 1e-3 and per element
-|err| <= 1e-2 * (|A|.|B|) + 1e-4 against the oracle's fp64 result on the same bf16 inputs.
-"""
-import os
+|err| <= 1e-2 * (|A|.|B|) + 1e-4 against the oracle's fp32-accumulated result on the same
+bf16 inputs.  Full-size products are checked on one row of every band of output rows
+against the oracle, for unwritten outputs everywhere, and through random projections of
+the whole output (nm_testutil).
 
+Kernel routes are chosen through the calls' route hints: a `with use_route(...)` block
+sets the hints that the helpers below put into every call they make.
+"""
 import numpy as np
 import pytest
 
 import oracle as O
 import synth
-from nm_testutil import check_gemm, dev, empty, host, sample_rows, check_gemm_vals
+from nm_testutil import (band_rows, check_all_written, check_gemm, check_gemm_vals, check_projection, dev, empty,
+                         host, sample_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -30,6 +35,51 @@ def _gpu():
 
 def sync():
     torch.cuda.synchronize()
+
+
+# Route hints (and tuning values) for the calls made inside a `with use_route(...)` block,
+# and the route report of the last call made by the helpers below.  This is test-side
+# state: the library reads nothing but its arguments.
+_ROUTE = {"route": 0, "few_wpb": 0, "few_splits": 0, "tile_wg": 0}
+LAST_TAKEN = [0]
+
+
+class use_route:
+    """Hints named as in S.ROUTE; blocks nest (bits are OR-ed, tuning values override)."""
+
+    def __init__(self, *names, few_wpb=0, few_splits=0, tile_wg=0):
+        self.bits = S.route_bits(*names)
+        self.tune = {"few_wpb": few_wpb, "few_splits": few_splits, "tile_wg": tile_wg}
+
+    def __enter__(self):
+        self.old = dict(_ROUTE)
+        _ROUTE["route"] |= self.bits
+        for k, v in self.tune.items():
+            if v:
+                _ROUTE[k] = v
+        return self
+
+    def __exit__(self, *exc):
+        _ROUTE.clear()
+        _ROUTE.update(self.old)
+
+
+def mk_args(*a, **kw):
+    """S.make_spmm_args with the current route hints (an explicit route= is OR-ed in)."""
+    kw["route"] = kw.get("route", 0) | _ROUTE["route"]
+    for k in ("few_wpb", "few_splits", "tile_wg"):
+        kw.setdefault(k, _ROUTE[k])
+    return mk_args(*a, **kw)
+
+
+def spmm_call(a):
+    S.nm_spmm(a)
+    LAST_TAKEN[0] = S.route_taken(a)
+
+
+def taken():
+    """NM_TAKEN_* names reported by the last helper call."""
+    return S.taken_names(LAST_TAKEN[0])
 
 
 def special_rows(k, rng):
@@ -124,7 +174,8 @@ def test_select_bitexact_family_widths(n, m, rows, groups, pad):
 
 @pytest.mark.parametrize("n,m", [(8, 16), (16, 32), (2, 4)])
 def test_select_full_size_sampled(n, m):
-    """Down-projection activations at full size (8192 x 14336); oracle on sampled rows."""
+    """Down-projection activations at full size (8192 x 14336); oracle on one row of every
+    128-row band; exactly n kept per group on every row."""
     print(f"select full n={n} m={m}", flush=True)
     d = synth.mlp_down_8of16(t_max=8192)
     x = d["x"]
@@ -136,7 +187,7 @@ def test_select_full_size_sampled(n, m):
     mask = empty((t, (k + 31) // 32), np.uint32)
     S.nm_compress(xd, n, m, vals, idx, S.NM_META_U8, mask)
     sync()
-    rows = sample_rows(t, 40)
+    rows = band_rows(t, 128, seed=n + m)
     v_ref, i_ref = O.compress(x[rows], n, m)
     keep = O.select_keep(x[rows], n, m)
     assert (host(vals, np.uint16)[rows] == v_ref).all()
@@ -200,7 +251,7 @@ def test_select_scored_full_size_sampled():
     mask = empty((t, (k + 31) // 32), np.uint32)
     S.nm_sparsify_scored(dev(x), 8, 16, dev(c), S.NM_SCORE_ACT_WEIGHTED, y, mask)
     sync()
-    rows = sample_rows(t, 40)
+    rows = band_rows(t, 128, seed=7)
     s_ref, keep = O.sparsify_scored(x[rows], c, 8, 16, O.SCORE_ACT_WEIGHTED)
     assert (host(y, np.uint16)[rows] == s_ref).all()
     assert (host(mask, np.uint32)[rows] == O.pack_mask(keep)).all()
@@ -282,24 +333,15 @@ def run_act(x, w, n, m, route=None, w8=None, s8=None, workspace=True, accumulate
         wd_, dtype, sd = dev(w), S.NM_W_BF16, None
     y = dev(y0.astype(np.float32)) if y0 is not None else empty((t, o), np.float32, fill=float("nan"))
     mask = empty((t, (k + 31) // 32), np.uint32, fill=-1) if want_mask else None
-    a = S.make_spmm_args(S.NM_ACT_DYNAMIC, t, o, k, xd, wd_, y, n=n, m=m, w_dtype=dtype, w_scale=sd,
-                         x_mask_out=mask, accumulate=accumulate)
+    a = mk_args(S.NM_ACT_DYNAMIC, t, o, k, xd, wd_, y, n=n, m=m, w_dtype=dtype, w_scale=sd,
+                x_mask_out=mask, accumulate=accumulate, route=S.route_bits("act_" + route) if route else 0)
     ws = None
     if workspace:
         nb = S.nm_spmm_workspace_size(a)
         ws = empty((max(nb, 16),), np.uint8)
         a.workspace, a.workspace_bytes = ws.data_ptr(), nb
-    old = os.environ.get("NM_ACT_ROUTE")
-    try:
-        if route is not None:
-            os.environ["NM_ACT_ROUTE"] = route
-        S.nm_spmm(a)
-        sync()
-    finally:
-        if old is None:
-            os.environ.pop("NM_ACT_ROUTE", None)
-        else:
-            os.environ["NM_ACT_ROUTE"] = old
+    spmm_call(a)
+    sync()
     return host(y, np.float32), (host(mask, np.uint32) if mask is not None else None)
 
 
@@ -332,65 +374,32 @@ def test_spmm_act_masked_kernels(kernel, t, o, k):
     mask = empty((t, k // 32), np.uint32)
     S.nm_sparsify(xd, 8, 16, None, mask)
     y = empty((t, o), np.float32, fill=float("nan"))
-    a = S.make_spmm_args(S.NM_ACT_MASKED, t, o, k, xd, wdv, y, n=8, m=16, x_meta=mask)
-    old = os.environ.get("NM_GEMM")
-    os.environ["NM_GEMM"] = kernel
-    try:
-        S.nm_spmm(a)
-        sync()
-    finally:
-        if old is None:
-            os.environ.pop("NM_GEMM", None)
-        else:
-            os.environ["NM_GEMM"] = old
+    a = mk_args(S.NM_ACT_MASKED, t, o, k, xd, wdv, y, n=8, m=16, x_meta=mask, route=S.route_bits("tile_" + kernel))
+    spmm_call(a)
+    sync()
+    assert f"tile_{kernel}" in taken() and "mask" in taken()
     sx, keep = O.sparsify(x, 8, 16)
     assert (host(mask, np.uint32) == O.pack_mask(keep)).all()
     check_gemm(host(y, np.float32), O.gemm(sx, w), sx, w, label=f"masked {kernel}")
     # the same kernel with X already sparsified (no mask)
     y2 = empty((t, o), np.float32, fill=float("nan"))
     sxd = dev(sx)
-    a2 = S.make_spmm_args(S.NM_ACT_MASKED, t, o, k, sxd, wdv, y2, n=8, m=16, x_meta=mask)
-    os.environ["NM_GEMM"] = kernel
-    try:
-        S.nm_spmm(a2)
-        sync()
-    finally:
-        if old is None:
-            os.environ.pop("NM_GEMM", None)
-        else:
-            os.environ["NM_GEMM"] = old
+    a2 = mk_args(S.NM_ACT_MASKED, t, o, k, sxd, wdv, y2, n=8, m=16, x_meta=mask,
+                 route=S.route_bits("tile_" + kernel))
+    spmm_call(a2)
+    sync()
     check_gemm(host(y2, np.float32), O.gemm(sx, w), sx, w, label=f"masked presparsified {kernel}")
     # x already S(X), no mask: the plain product
     y3 = empty((t, o), np.float32, fill=float("nan"))
-    a3 = S.make_spmm_args(S.NM_ACT_MASKED, t, o, k, sxd, wdv, y3, n=8, m=16)
+    a3 = mk_args(S.NM_ACT_MASKED, t, o, k, sxd, wdv, y3, n=8, m=16)
     nb = S.nm_spmm_workspace_size(a3)
     ws3 = empty((max(nb, 16),), np.uint8)
     a3.workspace, a3.workspace_bytes = ws3.data_ptr(), nb
-    with env_set(NM_GEMM=kernel):
-        S.nm_spmm(a3)
+    with use_route("tile_" + kernel):
+        a3.route = _ROUTE["route"]
+        spmm_call(a3)
         sync()
     check_gemm(host(y3, np.float32), O.gemm(sx, w), sx, w, label=f"S(X) no mask {kernel}")
-
-
-class env_set:
-    """Temporarily set environment variables (the library reads its route overrides
-    per call)."""
-
-    def __init__(self, **kv):
-        self.kv = kv
-        self.old = {}
-
-    def __enter__(self):
-        for k, v in self.kv.items():
-            self.old[k] = os.environ.get(k)
-            os.environ[k] = v
-
-    def __exit__(self, *exc):
-        for k, v in self.old.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
 
 
 def test_spmm_act_2of4_layer():
@@ -401,35 +410,33 @@ def test_spmm_act_2of4_layer():
     x, w = d["x"], d["w"]
     sx, keep = O.sparsify(x, 2, 4)
     ref = O.gemm(sx, w)
-    for few in ("1", "0"):
+    for few in (True, False):
         for ws in (True, False):
-            with env_set(NM_FEW=few):
+            with use_route(*(() if few else ("no_few",))):
                 y, mask = run_act(x, w, 2, 4, workspace=ws)
             assert (mask == O.pack_mask(keep)).all()
             check_gemm(y, ref, sx, w, label=f"2:4 layer ws={ws} few={few}")
 
 
-# route overrides of the few-token dispatch: weight-streaming kernel, split-K tile kernel
-# (K % 64 == 0; others fall back to streaming) in its default 128-row shape, its 256-row,
-# 4-wave and 4-stage shapes and forced workgroup counts, or the large-T tile kernels
-FEW_ROUTES = {"stream": {"NM_FEW_ROUTE": "stream"}, "tile": {"NM_FEW_ROUTE": "tile"},
-              "tile256": {"NM_FEW_ROUTE": "tile", "NM_TILE_BM": "256"},
-              "tile4w": {"NM_FEW_ROUTE": "tile", "NM_TILE_WAVES": "4", "NM_TILE_WG": "37"},
-              "tile4st": {"NM_FEW_ROUTE": "tile", "NM_TILE_STAGES": "4", "NM_TILE_WG": "100"},
-              "off": {"NM_FEW": "0"}}
+# route hints of the few-token dispatch: weight-streaming kernel, split-K tile kernel
+# (K % 64 == 0; others fall back to streaming) with its default and forced workgroup
+# counts, or the large-T tile kernels
+FEW_ROUTES = {"stream": (("few_stream",), {}), "tile": (("few_tile",), {}),
+              "tile_wg37": (("few_tile",), {"tile_wg": 37}), "tile_wg100": (("few_tile",), {"tile_wg": 100}),
+              "off": (("no_few",), {})}
 
 
 def run_w(mode, x, v, mt, o, k, ns=2, workspace=True, accumulate=0, y0=None):
     t = x.shape[0]
     y = dev(y0.astype(np.float32)) if y0 is not None else empty((t, o), np.float32, fill=float("nan"))
-    a = S.make_spmm_args(mode, t, o, k, dev(x), v, y, ns=ns, w_meta=mt, w_meta_fmt=S.NM_META_2BIT,
-                         accumulate=accumulate)
+    a = mk_args(mode, t, o, k, dev(x), v, y, ns=ns, w_meta=mt, w_meta_fmt=S.NM_META_2BIT,
+                accumulate=accumulate)
     ws = None
     if workspace:
         nb = S.nm_spmm_workspace_size(a)
         ws = empty((max(nb, 16),), np.uint8)
         a.workspace, a.workspace_bytes = ws.data_ptr(), nb
-    S.nm_spmm(a)
+    spmm_call(a)
     sync()
     return host(y, np.float32)
 
@@ -446,7 +453,8 @@ def test_few_token_kernels(route, t, k):
     o = 200
     x = synth.student_t_bf16(rng, (t, k), 4.0, 0.5)
     w = synth.normal_bf16(rng, (o, k), 0.02)
-    with env_set(**FEW_ROUTES[route]):
+    names, tune = FEW_ROUTES[route]
+    with use_route(*names, **tune):
         sx, _ = O.sparsify(x, 8, 16)
         for ws in (True, False):
             y, _ = run_act(x, w, 8, 16, workspace=ws)
@@ -468,7 +476,7 @@ def test_few_token_kernels(route, t, k):
         check_gemm(ys, O.gemm(x8, pr), x8, pr, label="slide 6:8")
 
 
-@pytest.mark.parametrize("wpb,splits", [("4", "0"), ("8", "0"), ("16", "0"), ("16", "3"), ("4", "7")])
+@pytest.mark.parametrize("wpb,splits", [(4, 0), (8, 0), (16, 0), (16, 3), (4, 7)])
 @pytest.mark.parametrize("t", [1, 20, 70])
 def test_few_token_partition_overrides(wpb, splits, t):
     """The weight-streaming kernel under forced in-workgroup wave counts and cross-
@@ -476,15 +484,12 @@ def test_few_token_partition_overrides(wpb, splits, t):
     rounding), with accumulation into a nonzero Y; then bitwise determinism of a repeat
     call.  O = 64 (few row blocks), K = 4096."""
     print(f"few-token partition wpb={wpb} splits={splits} t={t}", flush=True)
-    rng = np.random.default_rng(7 * t + int(wpb))
+    rng = np.random.default_rng(7 * t + wpb)
     o, k = 64, 4096
     x = synth.student_t_bf16(rng, (t, k), 4.0, 0.5)
     w = synth.normal_bf16(rng, (o, k), 0.02)
     y0 = rng.standard_normal((t, o)).astype(np.float32)
-    env = {"NM_FEW_ROUTE": "stream", "NM_FEW_WPB": wpb}
-    if splits != "0":
-        env["NM_FEW_SPLITS"] = splits
-    with env_set(**env):
+    with use_route("few_stream", few_wpb=wpb, few_splits=splits):
         sx, _ = O.sparsify(x, 8, 16)
         y, _ = run_act(x, w, 8, 16, accumulate=1, y0=y0)
         check_gemm(y - y0, O.gemm(sx, w), sx, w, label="8:16 accumulate")
@@ -530,7 +535,7 @@ def test_single_token_kmajor_gather(n, m, k, o):
     for acc in (0, 1):
         y = dev(y0) if acc else empty((1, o), np.float32, fill=float("nan"))
         mask = empty((1, (k + 31) // 32), np.uint32, fill=-1)
-        a = S.make_spmm_args(S.NM_ACT_DYNAMIC, 1, o, k, dev(x), dev(w), y, n=n, m=m, w_kmajor=wk,
+        a = mk_args(S.NM_ACT_DYNAMIC, 1, o, k, dev(x), dev(w), y, n=n, m=m, w_kmajor=wk,
                              x_mask_out=mask, accumulate=acc)
         nb = S.nm_spmm_workspace_size(a)
         assert nb > 0 and nb < 1 << 24          # partial sums only
@@ -554,7 +559,7 @@ def test_single_token_kmajor_full_size():
     o, k = w.shape
     wk = dev(np.ascontiguousarray(w.T))
     y = empty((1, o), np.float32, fill=float("nan"))
-    a = S.make_spmm_args(S.NM_ACT_DYNAMIC, 1, o, k, dev(x), dev(w), y, n=8, m=16, w_kmajor=wk)
+    a = mk_args(S.NM_ACT_DYNAMIC, 1, o, k, dev(x), dev(w), y, n=8, m=16, w_kmajor=wk)
     nb = S.nm_spmm_workspace_size(a)
     ws = empty((nb,), np.uint8)
     a.workspace, a.workspace_bytes = ws.data_ptr(), nb
@@ -573,7 +578,7 @@ def test_spmm_act_compressed_2of4_and_8of16():
         v, i = O.compress(x, n, m)
         meta = O.pack_meta_2bit(i) if fmt == 1 else i
         y = empty((t, o), np.float32, fill=float("nan"))
-        a = S.make_spmm_args(S.NM_ACT_COMPRESSED, t, o, k, dev(v), dev(w), y, n=n, m=m, x_meta=dev(meta),
+        a = mk_args(S.NM_ACT_COMPRESSED, t, o, k, dev(v), dev(w), y, n=n, m=m, x_meta=dev(meta),
                              x_meta_fmt=fmt, ldx=0)
         nb = S.nm_spmm_workspace_size(a)
         ws = empty((nb,), np.uint8)
@@ -601,11 +606,11 @@ def test_spmm_act_accumulate_and_fp8():
         check_gemm(y2 - y0, O.gemm(sx, w), sx, w, label=f"accumulate {route}")
 
 
-@pytest.mark.parametrize("widen", ["0", "1"])
+@pytest.mark.parametrize("widen", [False, True])
 @pytest.mark.parametrize("t,o,k", [(600, 300, 1024), (520, 136, 1056), (1030, 520, 2048)])
 def test_spmm_act_fp8_large_tokens(t, o, k, widen):
     """fp8 weights at prefill sizes (K % 64 == 0): codes staged straight into LDS and
-    widened per fragment, or (NM_FP8_WIDEN=1) widened once to bf16 in the workspace;
+    widened per fragment, or (the fp8_widen hint) widened once to bf16 in the workspace;
     otherwise the register-staged fp8 kernel.  Scale, accumulate, ragged tiles."""
     print(f"fp8 large t={t} o={o} k={k} widen={widen}", flush=True)
     rng = np.random.default_rng(t + k)
@@ -614,7 +619,7 @@ def test_spmm_act_fp8_large_tokens(t, o, k, widen):
     q, sc = synth.fp8_e4m3_quantize_rows(w)
     wdeq = O.fp8_e4m3_to_f64(q) * sc[:, None].astype(np.float64)
     y0 = rng.standard_normal((t, o)).astype(np.float32)
-    with env_set(NM_FP8_WIDEN=widen):
+    with use_route(*(("fp8_widen",) if widen else ())):
         for n, m in ((16, 32), (8, 16)):
             sx, keep = O.sparsify(x, n, m)
             ref = O.spmm_act_fp8(x, q, sc, n, m)
@@ -653,7 +658,8 @@ def test_layer_full_size_sampled(layer8b, group, t):
     """The 8B-shaped layer's linears at full size, each alone and with the linears that
     share an input concatenated along the output dimension (q|k|v 6144 x 4096, gate|up
     28672 x 4096), as the layer measurement runs them: 16:32 and 8:16 activations, bf16
-    and fp8 weights, workspace from the size query; oracle on sampled output rows."""
+    and fp8 weights, workspace from the size query.  Every output written; the oracle on
+    one row of every 256-row band (every 8-row band at 64 tokens)."""
     import torch
 
     parts = LAYER_GROUPS[group]
@@ -664,7 +670,7 @@ def test_layer_full_size_sampled(layer8b, group, t):
     w8 = np.concatenate([layer8b["w8"][p] for p in parts], 0)
     s8 = np.concatenate([layer8b["s8"][p] for p in parts], 0)
     o, k = w.shape
-    rows = sample_rows(t, 6, seed=t + o)
+    rows = band_rows(t, 256 if t > 256 else 8, seed=t + o)
     xd = dev(x)
     wdeq = O.fp8_e4m3_to_f64(w8) * s8[:, None].astype(np.float64)
     for (n, m) in ((16, 32), (8, 16)):
@@ -672,15 +678,16 @@ def test_layer_full_size_sampled(layer8b, group, t):
         for kind in ("bf16", "fp8"):
             y = torch.full((t, o), float("nan"), dtype=torch.float32, device="cuda")
             if kind == "bf16":
-                a = S.make_spmm_args(S.NM_ACT_DYNAMIC, t, o, k, xd, dev(w), y, n=n, m=m)
+                a = mk_args(S.NM_ACT_DYNAMIC, t, o, k, xd, dev(w), y, n=n, m=m)
             else:
-                a = S.make_spmm_args(S.NM_ACT_DYNAMIC, t, o, k, xd, dev(w8), y, n=n, m=m,
+                a = mk_args(S.NM_ACT_DYNAMIC, t, o, k, xd, dev(w8), y, n=n, m=m,
                                      w_dtype=S.NM_W_FP8E4M3, w_scale=dev(s8))
             nb = S.nm_spmm_workspace_size(a)
             ws = empty((max(nb, 16),), np.uint8)
             a.workspace, a.workspace_bytes = ws.data_ptr(), nb
             S.nm_spmm(a)
             sync()
+            check_all_written(y, f"layer {group} t={t} {n}:{m} {kind}")
             yr = y[torch.from_numpy(rows).cuda()].cpu().numpy()
             if kind == "bf16":
                 check_gemm(yr, O.gemm(sx, w), sx, w, label=f"layer {group} t={t} {n}:{m} bf16")
@@ -690,18 +697,31 @@ def test_layer_full_size_sampled(layer8b, group, t):
             del y, ws, a
 
 
-@pytest.mark.parametrize("route", ["fused", "mask", "sx"])
-def test_spmm_act_full_size_sampled(route):
-    """8:16 down-projection at 2048 and 8192 tokens; oracle on sampled output rows."""
-    print(f"act full route={route}", flush=True)
+@pytest.fixture(scope="module")
+def down_full():
+    """The 8:16 down-projection workload at full size with the oracle's selection of every
+    row (computed once per module)."""
     d = synth.mlp_down_8of16(t_max=8192)
-    x_all, w = d["x"], d["w"]
+    sx_all, keep_all = O.sparsify(d["x"], 8, 16)
+    return d["x"], d["w"], sx_all, O.pack_mask(keep_all)
+
+
+@pytest.mark.parametrize("route", ["fused", "mask", "sx"])
+def test_spmm_act_full_size_sampled(route, down_full):
+    """8:16 down-projection at 2048 and 8192 tokens: the mask of every row bit-exact, every
+    output written, random projections of the whole output, and the oracle on one row of
+    every 128-row band."""
+    print(f"act full route={route}", flush=True)
+    x_all, w, sx_all, mask_all = down_full
+    wv = O.bf16_to_f64(w)
     for t in (2048, 8192):
         x = x_all[:t]
         y, mask = run_act(x, w, 8, 16, route=route)
-        rows = sample_rows(t, 24, seed=t)
-        sx, keep = O.sparsify(x[rows], 8, 16)
-        assert (mask[rows] == O.pack_mask(keep)).all()
+        assert (mask == mask_all[:t]).all()
+        assert np.isfinite(y).all(), f"full t={t}: unwritten outputs"
+        check_projection(y, O.bf16_to_f64(sx_all[:t]), wv, label=f"full t={t} projection")
+        rows = band_rows(t, 128, seed=t)
+        sx = sx_all[rows]
         check_gemm(y[rows], O.gemm(sx, w), sx, w, label=f"full t={t}")
 
 
@@ -709,31 +729,29 @@ def test_spmm_act_full_size_sampled(route):
 def test_spmm_act_decode_full_size_sampled(t):
     """8:16 down-projection (W 4096 x 14336) at decode token counts on the default routes
     (select + streaming kernel up to 32 tokens, select + split-K tile kernel above);
-    oracle on sampled output rows."""
+    the oracle on every output row."""
     print(f"act decode full t={t}", flush=True)
     d = synth.mlp_down_8of16(t_max=128)
     x, w = d["x"][:t], d["w"]
     y, mask = run_act(x, w, 8, 16)
-    rows = sample_rows(t, 12, seed=t)
-    sx, keep = O.sparsify(x[rows], 8, 16)
-    assert (mask[rows] == O.pack_mask(keep)).all()
-    check_gemm(y[rows], O.gemm(sx, w), sx, w, label=f"decode full t={t}")
+    sx, keep = O.sparsify(x, 8, 16)
+    assert (mask == O.pack_mask(keep)).all()
+    check_gemm(y, O.gemm(sx, w), sx, w, label=f"decode full t={t}")
 
 
 @pytest.mark.parametrize("t", [16, 64, 128])
 def test_spmm_act_fp8_decode_full_size_sampled(t):
     """fp8 weights (per-row scales) on the 8:16 down-projection (W 4096 x 14336) at decode
-    token counts; oracle on sampled output rows."""
+    token counts; the oracle on every output row."""
     print(f"fp8 decode full t={t}", flush=True)
     d = synth.mlp_down_8of16(t_max=128)
     x, w = d["x"][:t], d["w"]
     q, sc = synth.fp8_e4m3_quantize_rows(w)
     y, mask = run_act(x, None, 8, 16, w8=q, s8=sc)
-    rows = sample_rows(t, 8, seed=t)
-    sx, keep = O.sparsify(x[rows], 8, 16)
-    assert (mask[rows] == O.pack_mask(keep)).all()
+    sx, keep = O.sparsify(x, 8, 16)
+    assert (mask == O.pack_mask(keep)).all()
     wdeq = O.fp8_e4m3_to_f64(q) * sc[:, None].astype(np.float64)
-    check_gemm(y[rows], O.spmm_act_fp8(x[rows], q, sc, 8, 16), sx, wdeq, label=f"fp8 decode full t={t}")
+    check_gemm(y, O.spmm_act_fp8(x, q, sc, 8, 16), sx, wdeq, label=f"fp8 decode full t={t}")
 
 
 # ------------------------------------------------------------------- weight 2:4 ---
@@ -753,7 +771,7 @@ def test_spmm_w_compressed(t, o, k):
     w = synth.normal_bf16(rng, (o, k), 0.02)
     v, mt = gpu_compress_2of4(w)
     y = empty((t, o), np.float32, fill=float("nan"))
-    a = S.make_spmm_args(S.NM_W_COMPRESSED, t, o, k, dev(x), v, y, w_meta=mt, w_meta_fmt=S.NM_META_2BIT)
+    a = mk_args(S.NM_W_COMPRESSED, t, o, k, dev(x), v, y, w_meta=mt, w_meta_fmt=S.NM_META_2BIT)
     S.nm_spmm(a)
     sync()
     ws, _ = O.sparsify(w, 2, 4)
@@ -789,7 +807,7 @@ def test_spmm_w_slide(ns, t):
     assert (host(vp, np.uint16) == vp_ref).all()
     assert (host(mp, np.uint8) == O.pack_meta_2bit(ip_ref)).all()
     y = empty((t, o), np.float32, fill=float("nan"))
-    a = S.make_spmm_args(S.NM_W_SLIDE, t, o, k, dev(x), vp, y, ns=ns, w_meta=mp, w_meta_fmt=S.NM_META_2BIT)
+    a = mk_args(S.NM_W_SLIDE, t, o, k, dev(x), vp, y, ns=ns, w_meta=mp, w_meta_fmt=S.NM_META_2BIT)
     S.nm_spmm(a)
     sync()
     # the lowered product must equal the dense product on the same pruned W
@@ -816,7 +834,7 @@ def test_spmm_w_slide_odd_family(ns):
     mp = empty((o, (kp + 7) // 8), np.uint8)
     S.nm_lower_slide(v, i, o, k, ns, vp, mp, S.NM_META_2BIT)
     y = empty((t, o), np.float32, fill=float("nan"))
-    a = S.make_spmm_args(S.NM_W_SLIDE, t, o, k, dev(x), vp, y, ns=ns, w_meta=mp, w_meta_fmt=S.NM_META_2BIT)
+    a = mk_args(S.NM_W_SLIDE, t, o, k, dev(x), vp, y, ns=ns, w_meta=mp, w_meta_fmt=S.NM_META_2BIT)
     S.nm_spmm(a)
     sync()
     pruned, _ = O.sparsify(w, 2 * ns - 2, 2 * ns)
@@ -824,7 +842,8 @@ def test_spmm_w_slide_odd_family(ns):
 
 
 def test_spmm_w_slide_full_size_sampled():
-    """6:8 weights 4096x4096 lowered to 2:4 over K'=6144, T in {1,16,128,4096}."""
+    """6:8 weights 4096x4096 lowered to 2:4 over K'=6144, T in {1,16,128,4096}: every output
+    written, whole-output projections, the oracle on one row of every 128-row band."""
     d = synth.slide_6of8_layer(t_max=4096)
     x_all, w = d["x"], d["w"]
     o, k = w.shape
@@ -841,25 +860,25 @@ def test_spmm_w_slide_full_size_sampled():
     for t, ws in ((1, True), (16, True), (128, True), (4096, True), (4096, False)):
         x = x_all[:t]
         y = empty((t, o), np.float32, fill=float("nan"))
-        a = S.make_spmm_args(S.NM_W_SLIDE, t, o, k, dev(x), vp, y, ns=4, w_meta=mp, w_meta_fmt=S.NM_META_2BIT)
+        a = mk_args(S.NM_W_SLIDE, t, o, k, dev(x), vp, y, ns=4, w_meta=mp, w_meta_fmt=S.NM_META_2BIT)
         if ws:
             nb = S.nm_spmm_workspace_size(a)
             wsb = empty((max(nb, 16),), np.uint8)
             a.workspace, a.workspace_bytes = wsb.data_ptr(), nb
         S.nm_spmm(a)
         sync()
-        rows = sample_rows(t, 16, seed=t)
-        check_gemm(host(y, np.float32)[rows], O.gemm(x[rows], pruned), x[rows], pruned,
-                   label=f"slide full t={t} ws={ws}")
+        yh = host(y, np.float32)
+        assert np.isfinite(yh).all(), f"slide full t={t}: unwritten outputs"
+        check_projection(yh, O.bf16_to_f64(x), O.bf16_to_f64(pruned), label=f"slide full t={t} projection")
+        rows = band_rows(t, 128, seed=t)
+        check_gemm(yh[rows], O.gemm(x[rows], pruned), x[rows], pruned, label=f"slide full t={t} ws={ws}")
 
 
-SPARSE_KERNELS = {"lds": {"NM_GEMM": "lds"}, "lds4x2": {"NM_GEMM": "lds", "NM_SP_WAVES": "4x2"},
-                  "lds_rowmeta": {"NM_GEMM": "lds", "NM_META_BLOCK": "0"},
-                  "regs": {"NM_GEMM": "regs"},
-                  "tile": {"NM_FEW_ROUTE": "tile"}, "stream": {"NM_FEW_ROUTE": "stream"}}
+SPARSE_KERNELS = {"lds": ("tile_lds",), "lds_rowmeta": ("tile_lds", "no_meta_block"), "regs": ("tile_regs",),
+                  "tile": ("few_tile",), "stream": ("few_stream",)}
 
 
-@pytest.mark.parametrize("kernel,t,o", [("lds", 300, 264), ("lds", 130, 520), ("lds4x2", 300, 264),
+@pytest.mark.parametrize("kernel,t,o", [("lds", 300, 264), ("lds", 130, 520),
                                         ("lds_rowmeta", 300, 264), ("regs", 300, 264),
                                         ("regs", 130, 520), ("tile", 33, 264), ("tile", 64, 520),
                                         ("tile", 100, 264), ("tile", 128, 130), ("stream", 100, 264)])
@@ -870,7 +889,7 @@ def test_sparse_weight_product_kernels(kernel, t, o):
     needs it) and the hybrid format with its dense second phase; ragged T and O."""
     print(f"sparse kernels kernel={kernel} t={t} o={o}", flush=True)
     rng = np.random.default_rng(t + o)
-    with env_set(**SPARSE_KERNELS[kernel]):
+    with use_route(*SPARSE_KERNELS[kernel]):
         k = 1024
         x = synth.normal_bf16(rng, (t, k))
         w = synth.normal_bf16(rng, (o, k), 0.02)
@@ -917,12 +936,16 @@ def hybrid_pack_gpu(w, kd, fmt=S.NM_META_2BIT):
 
 
 def run_hybrid(x, sc, ks, dc, kd, wv, wm, wdd, o, ldwd=None, accumulate=0):
+    import ctypes
     t = x.shape[0]
     y = empty((t, o), np.float32, fill=float("nan"))
-    nb = S.nm_hybrid_gemm_workspace_size(t, ks, kd, o, sc is not None or dc is not None)
+    route = _ROUTE["route"]
+    nb = S.nm_hybrid_gemm_workspace_size(t, ks, kd, o, sc is not None or dc is not None, route)
     ws = empty((max(nb, 16),), np.uint8)
+    rep = ctypes.c_uint32(0)
     S.nm_hybrid_gemm(dev(x), sc, ks, dc, kd, wv, wm, S.NM_META_2BIT, wdd, o, y, accumulate, ldwd=ldwd,
-                     workspace=ws, workspace_bytes=nb)
+                     workspace=ws, workspace_bytes=nb, route=route, taken=rep)
+    LAST_TAKEN[0] = rep.value
     sync()
     return host(y, np.float32)
 
@@ -930,7 +953,7 @@ def run_hybrid(x, sc, ks, dc, kd, wv, wm, wdd, o, ldwd=None, accumulate=0):
 @pytest.mark.parametrize("t,o,kc", [(300, 264, 1088), (257, 130, 64), (512, 520, 2112)])
 def test_blocked_positions_match_row_major(t, o, kc):
     """The large-token 2:4 product reads the weight positions from a K-blocked copy in the
-    workspace; with NM_META_BLOCK=0 it reads them row-major.  Only the source of the same
+    workspace; under the no_meta_block hint it reads them row-major.  Only the source of the same
     bytes differs, so the two outputs agree bit for bit; both match the oracle.  Ragged
     step counts (17, 1, 33 K-steps of 64) and row counts; plain 2:4 and the hybrid format."""
     print(f"blocked positions t={t} o={o} kc={kc}", flush=True)
@@ -939,10 +962,12 @@ def test_blocked_positions_match_row_major(t, o, kc):
     w = synth.normal_bf16(rng, (o, kc), 0.02)
     v, mt = gpu_compress_2of4(w)
     ws24, _ = O.sparsify(w, 2, 4)
-    with env_set(NM_GEMM="lds"):
+    with use_route("tile_lds"):
         y_blk = run_w(S.NM_W_COMPRESSED, x, v, mt, o, kc)
-        with env_set(NM_META_BLOCK="0"):
+        assert "meta_block" in taken()
+        with use_route("no_meta_block"):
             y_row = run_w(S.NM_W_COMPRESSED, x, v, mt, o, kc)
+            assert "meta_block" not in taken() and "tile_lds" in taken()
     assert np.array_equal(y_blk.view(np.uint32), y_row.view(np.uint32)), "blocked vs row-major positions"
     check_gemm(y_blk, O.gemm(x, ws24), x, ws24, label="2:4 blocked positions")
     kd = 64
@@ -953,10 +978,12 @@ def test_blocked_positions_match_row_major(t, o, kc):
     sp, de, hv, hi, hwd = O.hybrid_pack(wh0, kd)
     wh = wh0.copy()
     wh[:, sp] = O.decompress(hv, hi, 2, 4, kc)
-    with env_set(NM_GEMM="lds"):
+    with use_route("tile_lds"):
         yh_blk = run_hybrid(xh, sc, kc, dc, kd, wv, wm, wdd, o)
-        with env_set(NM_META_BLOCK="0"):
+        assert "meta_block" in taken()
+        with use_route("no_meta_block"):
             yh_row = run_hybrid(xh, sc, kc, dc, kd, wv, wm, wdd, o)
+            assert "meta_block" not in taken()
     assert np.array_equal(yh_blk.view(np.uint32), yh_row.view(np.uint32)), "hybrid blocked vs row-major"
     check_gemm(yh_blk, O.hybrid_gemm(xh, sp, de, hv, hi, hwd), xh, wh, label="hybrid blocked positions")
 
@@ -1010,7 +1037,8 @@ def test_hybrid_prepermuted_input():
 
 
 def test_hybrid_full_size_sampled():
-    """W 14336x4096, 25% dense columns; T in {1, 8, 32, 64, 2048}."""
+    """W 14336x4096, 25% dense columns; T in {1, 8, 32, 64, 2048}: every output written,
+    whole-output projections, the oracle on one row of every 128-row band."""
     d = synth.hybrid_up_layer(t_max=2048)
     x_all, w, kd = d["x"], d["w"], d["k_dense"]
     o, k = w.shape
@@ -1027,11 +1055,16 @@ def test_hybrid_full_size_sampled():
     wh = w.copy()
     wh[:, sp] = O.sparsify(np.ascontiguousarray(w[:, sp]), 2, 4)[0]
     del ws_ref
+    hv_full, hi_full = O.compress(np.ascontiguousarray(w[:, sp]), 2, 4)
+    hwd_full = np.ascontiguousarray(w[:, de])
     for t in (1, 8, 32, 64, 2048):
         x = x_all[:t]
         y = run_hybrid(x, sc, k - kd, dc, kd, wv, wm, wdd, o)
-        rows = sample_rows(t, 12, seed=t)
-        check_gemm(y[rows], O.gemm(x[rows], wh), x[rows], wh, label=f"hybrid full t={t}")
+        assert np.isfinite(y).all(), f"hybrid full t={t}: unwritten outputs"
+        check_projection(y, O.bf16_to_f64(x), O.bf16_to_f64(wh), label=f"hybrid full t={t} projection")
+        rows = band_rows(t, 128, seed=t)
+        check_gemm(y[rows], O.hybrid_gemm(x[rows], sp, de, hv_full, hi_full, hwd_full), x[rows], wh,
+                   label=f"hybrid full t={t}")
 
 
 # --------------------------------------------------------- fp8 x fp8 (W8A8) ---
@@ -1082,7 +1115,7 @@ def run_w8a8(x, w8, idx, ws, o, k, ns, accumulate=0, y0=None, rows=None):
     t = x.shape[0]
     mode = S.NM_W_SLIDE if ns > 2 else S.NM_W_COMPRESSED
     y = dev(y0.astype(np.float32)) if y0 is not None else empty((t, o), np.float32, fill=float("nan"))
-    a = S.make_spmm_args(mode, t, o, k, dev(x), dev(w8), y, ns=ns, w_dtype=S.NM_W_FP8E4M3, w_scale=dev(ws),
+    a = mk_args(mode, t, o, k, dev(x), dev(w8), y, ns=ns, w_dtype=S.NM_W_FP8E4M3, w_scale=dev(ws),
                          w_meta=dev(O.pack_meta_2bit(idx)), w_meta_fmt=S.NM_META_2BIT, accumulate=accumulate)
     nb = S.nm_spmm_workspace_size(a)
     wsb = empty((max(nb, 16),), np.uint8)
@@ -1125,7 +1158,8 @@ def test_spmm_w8a8(ns, t, o):
 
 def test_spmm_w8a8_full_size_sampled():
     """6:8 weights 4096 x 4096 lowered to 2:4 over K' = 6144, fp8 weights and activations,
-    T in {1, 128, 4096}; oracle on sampled output rows."""
+    T in {1, 128, 4096}: every output written, whole-output projections, the oracle on one
+    row of every 128-row band."""
     print("w8a8 full", flush=True)
     d = synth.slide_6of8_layer(t_max=4096)
     x_all, w = d["x"], d["w"]
@@ -1135,11 +1169,13 @@ def test_spmm_w8a8_full_size_sampled():
     w8, ws = synth.fp8_e4m3_quantize_rows(vals)
     for t in (1, 128, 4096):
         x = x_all[:t]
-        rows = sample_rows(t, 12, seed=t)
-        y = run_w8a8(x, w8, idx, ws, o, k, 4, rows=rows)
+        y = run_w8a8(x, w8, idx, ws, o, k, 4)
+        assert np.isfinite(y).all(), f"w8a8 full t={t}: unwritten outputs"
+        a_all, b_v = w8a8_operands(x, w8, idx, ws, k, 4)
+        check_projection(y, a_all, b_v, label=f"w8a8 full t={t} projection")
+        rows = band_rows(t, 128, seed=t)
         ref = O.spmm_w8a8_slide(x[rows], w8, idx, ws, k, 4)
-        a_v, b_v = w8a8_operands(x[rows], w8, idx, ws, k, 4)
-        check_gemm_vals(y, ref, a_v, b_v, label=f"w8a8 full t={t}")
+        check_gemm_vals(y[rows], ref, a_all[rows], b_v, label=f"w8a8 full t={t}")
 
 
 # ------------------------------------------------------------------ Spense GLU ---
@@ -1294,7 +1330,7 @@ def test_zero_sizes_and_k_zero():
     y = empty((4, 8), np.float32, fill=5.0)
     x = empty((4, 8), np.uint16, fill=0)
     w = empty((8, 8), np.uint16, fill=0)
-    a = S.make_spmm_args(S.NM_ACT_DYNAMIC, 4, 8, 0, x, w, y, n=2, m=4, ldx=8, ldw=8)
+    a = mk_args(S.NM_ACT_DYNAMIC, 4, 8, 0, x, w, y, n=2, m=4, ldx=8, ldw=8)
     S.nm_spmm(a)
     sync()
     assert (host(y, np.float32) == 0).all()
@@ -1319,14 +1355,15 @@ def test_large_offsets_sampled():
     w = synth.normal_bf16(np.random.default_rng(13), (o, k), 0.02)
     y = empty((t, o), np.float32, fill=float("nan"))
     mask = empty((t, k // 32), np.uint32, fill=-1)
-    a = S.make_spmm_args(S.NM_ACT_DYNAMIC, t, o, k, xd, dev(w), y, n=8, m=16, x_mask_out=mask)
+    a = mk_args(S.NM_ACT_DYNAMIC, t, o, k, xd, dev(w), y, n=8, m=16, x_mask_out=mask)
     nb = S.nm_spmm_workspace_size(a)
     assert nb >= t * k * 2
     ws = empty((nb,), np.uint8)
     a.workspace, a.workspace_bytes = ws.data_ptr(), nb
     S.nm_spmm(a)
     sync()
-    rows = np.array(sorted(set(sample_rows(t, 10, seed=3).tolist()) | {65535, 65536, 69999}))
+    check_all_written(y, "large offsets")
+    rows = np.array(sorted(set(band_rows(t, 4096, seed=3).tolist()) | {65535, 65536, 69999}))
     xr = xd[torch.from_numpy(rows).cuda()].cpu().numpy().view(np.uint16)
     sx, keep = O.sparsify(xr, 8, 16)
     assert (host(mask, np.uint32)[rows] == O.pack_mask(keep)).all()
@@ -1366,7 +1403,7 @@ def test_measurement_probes():
 @pytest.mark.parametrize("o", [200, 4096])
 def test_one_token_staged_x_bitexact(o):
     """One token on the weight-streaming kernel: X rows staged in LDS give the same bits as
-    X read from global memory (NM_FEWD_XLDS=0), and match the oracle, for dense bf16 and
+    X read from global memory (the no_xlds hint), and match the oracle, for dense bf16 and
     fp8 weights (8:16 activations, ragged K), plain 2:4, lowered 6:8 and 4:6, and the
     two-segment hybrid; o = 200 also splits the reduction across workgroups."""
     print(f"one-token staged X o={o}", flush=True)
@@ -1374,10 +1411,12 @@ def test_one_token_staged_x_bitexact(o):
     runs = []
 
     def both(label, fn):
-        with env_set(NM_FEW_ROUTE="stream"):
+        with use_route("few_stream"):
             y_lds = fn()
-            with env_set(NM_FEWD_XLDS="0"):
+            assert {"few_stream", "few_xlds"} <= taken(), (label, taken())
+            with use_route("no_xlds"):
                 y_glb = fn()
+                assert "few_stream" in taken() and "few_xlds" not in taken(), (label, taken())
         assert np.array_equal(y_lds.view(np.uint32), y_glb.view(np.uint32)), f"{label}: staged vs global X"
         runs.append(label)
         return y_lds
@@ -1422,7 +1461,7 @@ def test_one_token_staged_x_bitexact(o):
 def test_one_token_select_in_kernel(m, o):
     """One token, n = m/2, no mask asked for: the weight-streaming kernel selects inside
     the X row it stages in LDS.  Same bits as the separate select pass followed by the
-    product (NM_FEW_SELECT=0), and within tolerance of the oracle, for bf16 and fp8
+    product (the no_few_select hint), and within tolerance of the oracle, for bf16 and fp8
     weights; one row is Student-t, the other has many equal magnitudes (ties to the
     lower index)."""
     print(f"one-token select in kernel m={m} o={o}", flush=True)
@@ -1437,22 +1476,27 @@ def test_one_token_select_in_kernel(m, o):
     xtie = vals[rng.integers(0, len(vals), size=(1, k))].astype(np.uint16)
     for label, x in (("student-t", xt), ("ties", xtie)):
         sx, _ = O.sparsify(x, m // 2, m)
-        with env_set(NM_FEW_ROUTE="stream"):
+        with use_route("few_stream"):
             y_in = run_act(x, w, m // 2, m, want_mask=False)[0]
+            assert {"few_select", "few_xlds"} <= taken() and "select" not in taken(), taken()
             y8_in = run_act(x, None, m // 2, m, w8=q, s8=sc, want_mask=False)[0]
-            with env_set(NM_FEW_SELECT="0"):
+            assert {"few_select", "few_xlds"} <= taken() and "select" not in taken(), taken()
+            with use_route("no_few_select"):
                 y_sep = run_act(x, w, m // 2, m, want_mask=False)[0]
+                assert "select" in taken() and "few_select" not in taken(), taken()
                 y8_sep = run_act(x, None, m // 2, m, w8=q, s8=sc, want_mask=False)[0]
+                assert "select" in taken() and "few_select" not in taken(), taken()
         assert np.array_equal(y_in.view(np.uint32), y_sep.view(np.uint32)), f"{label} bf16: in-kernel vs separate"
         assert np.array_equal(y8_in.view(np.uint32), y8_sep.view(np.uint32)), f"{label} fp8: in-kernel vs separate"
         check_gemm(y_in, O.gemm(sx, w), sx, w, label=f"{label} {m // 2}:{m} bf16 in-kernel select")
         check_gemm(y8_in, O.spmm_act_fp8(x, q, sc, m // 2, m), sx, wdeq, label=f"{label} {m // 2}:{m} fp8")
     # accumulate into a nonzero y, both weight types
     y0 = rng.standard_normal((1, o)).astype(np.float32)
-    with env_set(NM_FEW_ROUTE="stream"):
+    with use_route("few_stream"):
         ya = run_act(xt, w, m // 2, m, accumulate=1, y0=y0, want_mask=False)[0]
+        assert "few_select" in taken()
         ya8 = run_act(xt, None, m // 2, m, w8=q, s8=sc, accumulate=1, y0=y0, want_mask=False)[0]
-        with env_set(NM_FEW_SELECT="0"):
+        with use_route("no_few_select"):
             yb = run_act(xt, w, m // 2, m, accumulate=1, y0=y0, want_mask=False)[0]
             yb8 = run_act(xt, None, m // 2, m, w8=q, s8=sc, accumulate=1, y0=y0, want_mask=False)[0]
     assert np.array_equal(ya.view(np.uint32), yb.view(np.uint32)), "accumulate bf16: in-kernel vs separate"
@@ -1474,29 +1518,37 @@ def test_one_token_graph_replays():
     xd, wd_ = dev(x), dev(w)
     calls = []
     ya = empty((1, o), np.float32)
-    a = S.make_spmm_args(S.NM_ACT_DYNAMIC, 1, o, k, xd, wd_, ya, n=8, m=16)
+    stream = S.route_bits("few_stream")
+    a = mk_args(S.NM_ACT_DYNAMIC, 1, o, k, xd, wd_, ya, n=8, m=16, route=stream)
     wsa = empty((max(S.nm_spmm_workspace_size(a), 16),), np.uint8)
     a.workspace, a.workspace_bytes = wsa.data_ptr(), S.nm_spmm_workspace_size(a)
     calls.append(("8:16 act", lambda: S.nm_spmm(a), ya))
     v, mt = gpu_compress_2of4(w)
     yw = empty((1, o), np.float32)
-    b = S.make_spmm_args(S.NM_W_COMPRESSED, 1, o, k, xd, v, yw, w_meta=mt, w_meta_fmt=S.NM_META_2BIT)
+    b = mk_args(S.NM_W_COMPRESSED, 1, o, k, xd, v, yw, w_meta=mt, w_meta_fmt=S.NM_META_2BIT, route=stream)
     wsb = empty((max(S.nm_spmm_workspace_size(b), 16),), np.uint8)
     b.workspace, b.workspace_bytes = wsb.data_ptr(), S.nm_spmm_workspace_size(b)
     calls.append(("w 2:4", lambda: S.nm_spmm(b), yw))
     kd = 256
     sc_, dc_, wv, wm, wdd = hybrid_pack_gpu(w, kd)
     yh = empty((1, o), np.float32)
-    nbh = S.nm_hybrid_gemm_workspace_size(1, k - kd, kd, o, True)
+    nbh = S.nm_hybrid_gemm_workspace_size(1, k - kd, kd, o, True, stream)
     wsh = empty((max(nbh, 16),), np.uint8)
+    import ctypes
+    hrep = ctypes.c_uint32(0)
     calls.append(("hybrid", lambda: S.nm_hybrid_gemm(xd, sc_, k - kd, dc_, kd, wv, wm, S.NM_META_2BIT, wdd, o, yh,
-                                                     ldwd=kd, workspace=wsh, workspace_bytes=nbh), yh))
-    with env_set(NM_FEW_ROUTE="stream"):
+                                                     ldwd=kd, workspace=wsh, workspace_bytes=nbh, route=stream,
+                                                     taken=hrep), yh))
+    if True:
         eager = []
         for _, fn, y in calls:
             fn()
             sync()
             eager.append(host(y, np.float32).copy())
+        # the routes the test is about: selection in the staged row; staged X; the permute
+        assert {"few_select", "few_xlds"} <= S.taken_names(S.route_taken(a)), S.taken_names(S.route_taken(a))
+        assert {"few_xlds", "sparse_mma"} <= S.taken_names(S.route_taken(b))
+        assert {"permute", "few_xlds"} <= S.taken_names(hrep.value)
         st = torch.cuda.Stream()
         st.wait_stream(torch.cuda.current_stream())
         g = torch.cuda.CUDAGraph()
