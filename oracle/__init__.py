@@ -70,6 +70,8 @@ __all__ = [
     "spmm_act_fp8", "lowered_k", "SCORE_ACT_WEIGHTED", "SCORE_WEIGHT", "selection_scores",
     "select_keep_scored", "sparsify_scored", "spense_glu_scores", "spense_order", "spense_order_tail",
     "spense_pack", "outsplit_gemm", "e4m3_encode", "quantize_tokens", "f32_from_bf16", "spmm_w8a8_slide",
+    "bf16_from_f32_rne", "pts_row_mean", "pts_shift", "sparsify_pts", "var_scale", "weight_sums", "spmm_pts",
+    "PTS_DYNAMIC", "PTS_STATIC", "PTS_VAR",
 ]
 
 
@@ -612,3 +614,140 @@ def spmm_act_fp8(x_bits: np.ndarray, w8: np.ndarray, scale: np.ndarray, n: int, 
     # bf16 x e4m3 products are exact in fp32; fp32 accumulation, then one scale multiply
     acc = gemm_f32_values(f32_from_bf16(s), fp8_e4m3_to_f64(w8).astype(np.float32))
     return (acc * np.asarray(scale, dtype=np.float32)[None, :]).astype(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------- error mitigation (PTS, VAR) ---
+# [FLEX] technical summary 2.B lists light-weight corrections of the pruning error that need
+# little or no calibration: a per-token shift that centres the activations around zero
+# before pruning, dynamic (D-PTS: computed from each token) or static (S-PTS: fixed in
+# advance), and VAR, a per-token correction of the variance after pruning; 4.C ranks them
+# among the most effective.  The page gives no formulas.  Readings (the plainest ones):
+#   D-PTS  mu_t = mean_k x_tk (reproducible, see pts_row_mean); prune x - mu_t; the shift is
+#          undone after the product by the rank-one term mu_t * (W . 1)_o
+#   S-PTS  a caller-given static shift c_k per input channel (a scalar shift is c_k = s);
+#          prune x - c; undone by the constant term (W . c)_o
+#   VAR    alpha_t = sqrt(Var(x~_t) / Var(S(x~_t))), Var = mean of squared deviations over
+#          the row's K entries (pruned entries count as zeros); the pruned row is scaled
+#          by alpha_t, so its variance equals the unpruned (shifted) row's
+# With x~ = the shifted row, Y[t][o] = alpha_t * sum_k S(x~)[t][k] W[o][k] + beta_t v_o,
+# beta_t = mu_t (D-PTS) or 1 (S-PTS), v = W . 1 or W . c; without a shift the last term is 0.
+
+PTS_DYNAMIC = 1   # per-token shift by the row mean
+PTS_STATIC = 2    # per-channel shift given by the caller
+PTS_VAR = 4       # variance correction after pruning
+
+
+def bf16_from_f32_rne(v: np.ndarray) -> np.ndarray:
+    """fp32 values -> bf16 bit patterns, round to nearest even (finite and infinite
+    inputs; a value rounding past the largest bf16 becomes infinity)."""
+    u = np.asarray(v, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def pts_row_mean(x_bits: np.ndarray) -> np.ndarray:
+    """D-PTS shift: the mean of each row, computed so that its bits do not depend on the
+    order of summation (the selection that follows compares bits, so every implementation
+    must reach the same mu).  Per row of finite bf16 values:
+        E   = exponent field of M = max_k |x_k| (1 if M is subnormal);  M < 2^(E-126)
+        q   = 2^(E - 162)                  every |x_k| / q < 2^36
+        n_k = round-half-even(x_k / q)     an integer; exact for every x_k >= 2^(E-159)
+        S   = sum_k n_k                    exact (|S| < 2^52 for K <= 2^16)
+        mu  = fp32( fp64(S * q) / K )      one fp64 division, one rounding to fp32
+    i.e. the exact mean of the row after rounding each value to a multiple of q (at most
+    2^-37 M from the exact mean), rounded once.  mu = +0 for an all-zero row.  Returns fp32 [R]."""
+    bits = np.asarray(x_bits, dtype=np.uint16)
+    r, k = bits.shape
+    if k > 65536:
+        raise ValueError("rows longer than 65536")
+    key = (bits & np.uint16(0x7FFF)).astype(np.int64)
+    if np.any(key >= 0x7F80):
+        raise ValueError("the shift needs finite activations")
+    out = np.zeros(r, dtype=np.float32)
+    vals = bf16_to_f64(bits)
+    for row in range(r):
+        m = int(key[row].max()) if k else 0
+        if m == 0:
+            continue
+        e = max(m >> 7, 1)
+        n = np.rint(np.ldexp(vals[row], 162 - e)).astype(np.int64)   # x / q, exact; then RNE
+        total = 0
+        for v in n.tolist():            # plain integer sum, ascending k (any order is exact)
+            total += v
+        mean = np.ldexp(float(total), e - 162) / float(k)
+        out[row] = np.float32(mean)
+    return out
+
+
+def pts_shift(x_bits: np.ndarray, shift_rows=None, shift_cols=None) -> np.ndarray:
+    """x~ = bf16( fp32(x - shift) ), both roundings to nearest even: shift_rows fp32 [R]
+    (D-PTS, one value per token) or shift_cols fp32 [K] (S-PTS, one per channel)."""
+    x = f32_from_bf16(x_bits)
+    if shift_rows is not None:
+        d = (x - np.asarray(shift_rows, np.float32)[:, None]).astype(np.float32)
+    elif shift_cols is not None:
+        d = (x - np.asarray(shift_cols, np.float32)[None, :]).astype(np.float32)
+    else:
+        return np.asarray(x_bits, dtype=np.uint16).copy()
+    return bf16_from_f32_rne(d)
+
+
+def var_scale(xs_bits: np.ndarray, s_bits: np.ndarray) -> np.ndarray:
+    """VAR: alpha_t = sqrt(Var(x~_t) / Var(S(x~_t))) over the K entries of each row (mean of
+    squared deviations from the row mean, fp64, two passes), alpha = 1 when the pruned row
+    has no variance.  Returns fp32 [R]."""
+    a = bf16_to_f64(xs_bits)
+    b = bf16_to_f64(s_bits)
+    va = ((a - a.mean(axis=1, keepdims=True)) ** 2).mean(axis=1) if a.shape[1] else np.zeros(a.shape[0])
+    vb = ((b - b.mean(axis=1, keepdims=True)) ** 2).mean(axis=1) if b.shape[1] else np.zeros(b.shape[0])
+    alpha = np.ones(a.shape[0])
+    ok = vb > 0
+    alpha[ok] = np.sqrt(va[ok] / vb[ok])
+    return alpha.astype(np.float32)
+
+
+def sparsify_pts(x_bits: np.ndarray, n: int, m: int, mode: int, static_shift=None):
+    """Shift (D-PTS or S-PTS, or none), select (the ACT rule on the shifted bf16 values) and
+    optionally the VAR scale.  Returns (S(x~) bits, keep, mu fp32 [R] or None, alpha fp32 [R]
+    or None).  mode: PTS_DYNAMIC or PTS_STATIC (not both), optionally | PTS_VAR."""
+    if (mode & PTS_DYNAMIC) and (mode & PTS_STATIC):
+        raise ValueError("one shift at a time")
+    mu = None
+    if mode & PTS_DYNAMIC:
+        mu = pts_row_mean(x_bits)
+        xs = pts_shift(x_bits, shift_rows=mu)
+    elif mode & PTS_STATIC:
+        xs = pts_shift(x_bits, shift_cols=np.asarray(static_shift, np.float32))
+    else:
+        xs = np.asarray(x_bits, dtype=np.uint16)
+    s, keep = sparsify(xs, n, m)
+    alpha = var_scale(xs, s) if mode & PTS_VAR else None
+    return s, keep, mu, alpha
+
+
+def weight_sums(w_vals: np.ndarray, shift=None) -> np.ndarray:
+    """The term that undoes a shift after the product: v_o = sum_k W[o][k] * c_k (c = 1 for
+    D-PTS, the static shift for S-PTS), summed in fp64 over ascending k and rounded once to
+    fp32.  w_vals: fp64 weight values [O][K] (bf16, or fp8 codes times their row scale)."""
+    w = np.asarray(w_vals, dtype=np.float64)
+    c = np.ones(w.shape[1]) if shift is None else np.asarray(shift, np.float32).astype(np.float64)
+    out = np.zeros(w.shape[0])
+    for kk in range(w.shape[1]):
+        out = out + w[:, kk] * c[kk]
+    return out.astype(np.float32)
+
+
+def spmm_pts(x_bits, w_bits, n: int, m: int, mode: int, static_shift=None, col_shift=None):
+    """The mitigated layer: Y = alpha_t * (S(x~) . W^T) + beta_t * v_o with the product
+    accumulated in fp32 (gemm) and the two terms added in fp64.  col_shift: v (fp32 [O]) as
+    the caller supplies it (weight_sums of W, with the static shift for S-PTS).
+    Returns (Y fp64, S(x~) bits, keep, mu, alpha)."""
+    s, keep, mu, alpha = sparsify_pts(x_bits, n, m, mode, static_shift)
+    y = gemm(s, w_bits)
+    if alpha is not None:
+        y = y * alpha.astype(np.float64)[:, None]
+    if mode & (PTS_DYNAMIC | PTS_STATIC):
+        v = np.asarray(col_shift, np.float32).astype(np.float64)[None, :]
+        beta = mu.astype(np.float64)[:, None] if mode & PTS_DYNAMIC else 1.0
+        y = y + beta * v
+    return y, s, keep, mu, alpha

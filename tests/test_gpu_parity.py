@@ -69,7 +69,7 @@ def mk_args(*a, **kw):
     kw["route"] = kw.get("route", 0) | _ROUTE["route"]
     for k in ("few_wpb", "few_splits", "tile_wg"):
         kw.setdefault(k, _ROUTE[k])
-    return mk_args(*a, **kw)
+    return S.make_spmm_args(*a, **kw)
 
 
 def spmm_call(a):

@@ -714,3 +714,140 @@ def test_w8a8_slide_is_the_dequantized_dense_product(ns):
     kp = O.lowered_k(k, ns) if ns > 2 else k
     bound = float(gamma_f32(kp)) * (np.abs(xa) @ np.abs(wa).T) + 2 * 2.0 ** -24 * np.abs(ref) * 1.0001
     assert (np.abs(got - ref) <= bound + 1e-30).all()
+
+
+# ------------------------------------------------- error mitigation: PTS and VAR ---
+
+def bf16_round_py(v):
+    """Pure-Python bf16 rounding of a Python float: to fp32 through the C conversion, then
+    round-to-nearest-even on the bit pattern (independent of the oracle's helpers)."""
+    u = struct.unpack("<I", struct.pack("<f", v))[0]
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u & 0xFFFF
+
+
+def test_pts_mean_exact_rows_and_order_free():
+    """mu is the row mean: exactly, where the mean is an fp32 value; within one fp32
+    rounding plus 2^-37 max|x| of the exact rational mean otherwise -- also across a 2^200
+    dynamic range; and bit-identical under any permutation of the row."""
+    x = arr([[1, 2, 3, 4, 5, 6, 7, 8], [-3, -1, 0.5, 0.5, 2, 0, 0, 1], [0, 0, 0, 0, 0, 0, 0, 0],
+             ["-0", 0, "-0", 0, 0, 0, 0, 0]])
+    mu = O.pts_row_mean(x)
+    assert mu.tolist() == [4.5, 0.0, 0.0, 0.0] and not np.signbit(mu[2:]).any()
+    rng = np.random.default_rng(31)
+    xs = synth.student_t_bf16(rng, (6, 160), 4.0, 0.5)
+    xs[5, 3] = bits_of(2.0 ** 100)
+    xs[5, 7] = bits_of(-(2.0 ** -100))
+    xs[5, 9] = 0x0001                                     # a subnormal
+    mu = O.pts_row_mean(xs)
+    for r in range(6):
+        vals = [Fraction(value_of(b)) for b in xs[r]]
+        exact = sum(vals) / len(vals)
+        big = max(abs(v) for v in vals)
+        assert abs(Fraction(float(mu[r])) - exact) <= abs(exact) * Fraction(1, 2 ** 24) + big / 2 ** 37
+        for _ in range(3):
+            perm = rng.permutation(160)
+            assert O.pts_row_mean(xs[r:r + 1, perm])[0].view(np.uint32) == mu[r].view(np.uint32)
+    with pytest.raises(ValueError):
+        O.pts_row_mean(arr([[1, 2, 3, float("inf")]]))
+
+
+def test_pts_zero_static_shift_is_act():
+    """A static shift of zero leaves every value (and -0) unchanged: S-PTS reduces to ACT."""
+    rng = np.random.default_rng(32)
+    x = synth.student_t_bf16(rng, (5, 64), 4.0, 0.5)
+    x[0, :4] = 0x8000
+    for n, m in ((2, 4), (8, 16), (16, 32)):
+        s, keep, mu, alpha = O.sparsify_pts(x, n, m, O.PTS_STATIC, np.zeros(64, np.float32))
+        s_act, keep_act = O.sparsify(x, n, m)
+        assert mu is None and alpha is None
+        assert (keep == keep_act).all()
+        # x - 0 rounds -0 to +0 in fp32 (RNE); kept values are otherwise identical
+        assert (s[s_act != 0x8000] == s_act[s_act != 0x8000]).all()
+
+
+@pytest.mark.parametrize("n,m", [(2, 4), (4, 8)])
+def test_pts_shift_then_select_bruteforce(n, m):
+    """Tiny rows: the shift computed from the exact rational mean, rounded to fp32 and then
+    bf16 in pure Python, and the kept set chosen by brute force over all n-subsets."""
+    rng = np.random.default_rng(33 + m)
+    for trial in range(40):
+        k = m * int(rng.integers(1, 4))
+        x = synth.student_t_bf16(rng, (1, k), 4.0, 0.5)
+        if trial % 4 == 0:                                 # many ties after the shift
+            x[0] = np.array([bits_of(v) for v in rng.choice([0.5, 1.0, 1.5, 2.0, -1.0], size=k)], np.uint16)
+        vals = [Fraction(value_of(b)) for b in x[0]]
+        mean = sum(vals) / k
+        mu = struct.unpack("<f", struct.pack("<f", float(mean)))[0]     # exact mean, one rounding
+        s, keep, mu_o, _ = O.sparsify_pts(x, n, m, O.PTS_DYNAMIC)
+        assert mu_o[0] == mu
+        shifted = [bf16_round_py(float(Fraction(value_of(b)) - Fraction(mu))) for b in x[0]]
+        # fp32(x - mu) is one rounding of the exact difference; bf16 rounds that result
+        sh32 = [f32_round(value_of(b) - mu) for b in x[0]]
+        assert shifted == [bf16_round_py(v) for v in sh32]
+        for g in range(k // m):
+            grp = [value_of(b) for b in shifted[g * m:(g + 1) * m]]
+            bk = brute_keep(grp, n)
+            assert list(keep[0, g * m:(g + 1) * m]) == bk
+            for j in range(m):
+                want = shifted[g * m + j] if bk[j] else 0
+                assert int(s[0, g * m + j]) == want
+
+
+def test_pts_rank_one_term_undoes_the_shift():
+    """Without pruning (n = m) the shift must cancel exactly: on rows whose shifted values
+    are exact in bf16, Y = (x - mu) W^T + mu (W 1) equals x W^T up to the fp32 rounding of
+    the product (exact rational check).  With pruning, Y equals S(x~) W^T + mu (W 1)."""
+    rng = np.random.default_rng(34)
+    x = arr([[1, 2, 3, 4, 5, 6, 7, 8] * 2, [-3, 5, 1, 1, 2, 0, 4, 6] * 2])     # means 4.5, 2
+    w = synth.normal_bf16(rng, (3, 16), 0.02)
+    wv = O.bf16_to_f64(w)
+    v = O.weight_sums(wv)
+    for n in (8, 4):
+        y, s, keep, mu, _ = O.spmm_pts(x, w, n, 8, O.PTS_DYNAMIC, col_shift=v)
+        assert mu.tolist() == [4.5, 2.0]
+        for t in range(2):
+            for o in range(3):
+                a = [Fraction(value_of(b)) for b in (x[t] if n == 8 else s[t])]
+                if n == 8:
+                    exact = sum(a[k] * Fraction(value_of(w[o, k])) for k in range(16))
+                else:
+                    exact = sum(a[k] * Fraction(value_of(w[o, k])) for k in range(16)) + \
+                        Fraction(float(mu[t])) * Fraction(float(v[o]))
+                absum = sum(abs(Fraction(value_of(b)) * Fraction(value_of(w[o, k])))
+                            for k, b in enumerate(s[t])) + abs(Fraction(float(mu[t])) * Fraction(float(v[o])))
+                # fp32 product, fp32 rounding of v, fp64 epilogue
+                tol = gamma_f32(16) * absum + abs(Fraction(float(mu[t]))) * Fraction(1, 2 ** 24) * \
+                    sum(abs(Fraction(value_of(w[o, k]))) for k in range(16)) + Fraction(1, 2 ** 40)
+                assert abs(Fraction(y[t, o]) - exact) <= tol, (n, t, o)
+
+
+def test_var_restores_the_row_variance():
+    """alpha_t S(x~_t) has the variance of x~_t (up to alpha's fp32 rounding); a row whose
+    pruned form has no variance gets alpha = 1."""
+    rng = np.random.default_rng(35)
+    x = synth.student_t_bf16(rng, (6, 256), 4.0, 0.5)
+    x[5] = 0
+    for mode in (O.PTS_VAR, O.PTS_VAR | O.PTS_DYNAMIC):
+        s, keep, mu, alpha = O.sparsify_pts(x, 8, 16, mode)
+        xs = O.pts_shift(x, shift_rows=mu) if mode & O.PTS_DYNAMIC else x
+        for r in range(5):
+            before = np.var(O.bf16_to_f64(xs[r]))
+            after = np.var(float(alpha[r]) * O.bf16_to_f64(s[r]))
+            assert abs(after - before) <= 3e-7 * before
+            assert alpha[r] > 1.0                       # pruning half the entries shrinks the variance
+        assert alpha[5] == 1.0
+
+
+def test_weight_sums_against_exact_sums():
+    rng = np.random.default_rng(36)
+    w = synth.normal_bf16(rng, (5, 96), 0.02)
+    c = rng.standard_normal(96).astype(np.float32)
+    for shift in (None, c):
+        v = O.weight_sums(O.bf16_to_f64(w), shift)
+        for o in range(5):
+            exact = sum(Fraction(value_of(w[o, k])) * (1 if shift is None else Fraction(float(c[k])))
+                        for k in range(96))
+            absum = sum(abs(Fraction(value_of(w[o, k])) * (1 if shift is None else Fraction(float(c[k]))))
+                        for k in range(96))
+            assert abs(Fraction(float(v[o])) - exact) <= abs(exact) / 2 ** 24 + absum * 96 / 2 ** 52
