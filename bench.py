@@ -86,8 +86,7 @@ def cpu_baseline(x_bits, w_bits, n, m, budget_s=15.0):
     total_t = run(rows)
     flops = 2.0 * rows * o * k
     return {"value": round(flops / total_t / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": f"{rows} of {x_bits.shape[0]} token rows, 8:16 select + fp32 C product, 1 thread, "
-                      f"{total_t:.1f} s"}
+            "sample": f"{rows}/{x_bits.shape[0]} rows: 8:16 select + fp32 C product, {total_t:.1f} s"}
 
 
 def gpu_time_us(torch, fn, graph, iters=10, warm=3, settle_ms=30.0):
@@ -175,30 +174,42 @@ def n_copies(wbytes):
 
 
 def measure_ceilings(torch, S):
-    """Achievable ceilings on this machine: a plain streaming read over distinct buffers
-    (cold in the 256 MB Infinity Cache) and over one buffer read again, and the bf16
+    """Achievable ceilings on this machine: streaming reads cycling over 1 GiB of distinct
+    buffers (cold in the 256 MB Infinity Cache), in each of the probe's load forms (16-byte
+    loads at a grid stride; contiguous blocks with 16 loads in flight per lane; direct-to-LDS
+    loads like the weight streams) and over one buffer read again, and the bf16
     matrix-instruction rate on register operands, each after the clock has settled."""
-    from semi_structured_sparse_amd import probe as S  # noqa: N811  (measurement helpers)
-    nb = 117440512
-    bufs = [torch.empty((nb // 4,), dtype=torch.int32, device="cuda").fill_(b) for b in range(6)]
-    sink = torch.empty((S.nm_probe_sink_bytes() // 4,), dtype=torch.int32, device="cuda")
-    cold = gpu_time_rot_us(torch, [(lambda b=b: S.nm_probe_read(b, nb, sink, check=False)) for b in bufs])
-    warm = gpu_time_us(torch, lambda: S.nm_probe_read(bufs[0], nb, sink, check=False), False)
+    from semi_structured_sparse_amd import probe as P
+    nb = 128 << 20
+    bufs = [torch.empty((nb // 4,), dtype=torch.int32, device="cuda").fill_(b) for b in range(8)]
+    sink = torch.empty((P.nm_probe_sink_bytes() // 4,), dtype=torch.int32, device="cuda")
+    # GB/s of the three cold read forms (r0 grid stride, r1 blocks, r2 direct-to-LDS), of
+    # one buffer read again (rw), and TFLOP/s of the matrix probe (mf)
+    res = {}
+    for mode in (0, 1, 2):
+        cold = gpu_time_rot_us(torch, [(lambda b=b: P.nm_probe_read(b, nb, sink, mode=mode, check=False))
+                                       for b in bufs])
+        res[f"r{mode}"] = round(nb / cold / 1e3)
+    warm = gpu_time_us(torch, lambda: P.nm_probe_read(bufs[0], nb, sink, mode=1, check=False), False)
     del bufs
     iters = 2000
-    mf = gpu_time_us(torch, lambda: S.nm_probe_mfma(iters, sink, check=False), False)
-    res = {"hbm_read_cold_GBps": round(nb / cold / 1e3, 1), "hbm_read_warm_GBps": round(nb / warm / 1e3, 1),
-           "mfma_bf16_TFLOPs": round(S.nm_probe_mfma_flops(iters) / mf / 1e6, 1)}
-    log(f"ceilings: streaming read {res['hbm_read_cold_GBps']:.0f} GB/s cold, {res['hbm_read_warm_GBps']:.0f} GB/s "
-        f"re-read; bf16 matrix instructions {res['mfma_bf16_TFLOPs']:.0f} TFLOP/s")
+    mf = gpu_time_us(torch, lambda: P.nm_probe_mfma(iters, sink, check=False), False)
+    res.update({"rw": round(nb / warm / 1e3), "mf": round(P.nm_probe_mfma_flops(iters) / mf / 1e6)})
+    log(f"ceilings: streaming read (cold, 1 GiB distinct) {res['r0']} / {res['r1']} / {res['r2']} GB/s "
+        f"(grid stride / blocks / direct-to-LDS), {res['rw']} GB/s re-read; bf16 matrix instructions "
+        f"{res['mf']} TFLOP/s")
     return res
 
 
-def measure_rows(torch, S, synth, np):
+def measure_rows(torch, S, synth, np, only=None):
     """Every workload row of the method's measurement table: time, dense-equivalent and
     executed TFLOP/s, algorithmic bytes and GB/s, and the fraction of the roofline that
     bounds the row (HBM for few tokens, bf16 matrix peak for many).  Few-token rows cycle
-    through enough copies of their weights that each call reads its weights from HBM."""
+    through enough copies of their weights that each call reads its weights from HBM.
+    only: row-key prefixes to measure (None: all), e.g. ["c3.", "c4.32"] for a profiler run."""
+
+    def want(key):
+        return only is None or any(key.startswith(p) for p in only)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(
         np.int16 if a.dtype == np.uint16 else (np.int32 if a.dtype == np.int32 else np.uint8))).cuda()
     f32 = lambda *sh: torch.empty(sh, dtype=torch.float32, device="cuda")
@@ -206,14 +217,16 @@ def measure_rows(torch, S, synth, np):
     rows = {}
 
     def add(cfg, t, path, us, f_dense, f_exec, nbytes, bound=None, peak=PEAK_BF16_TFLOPS, key=None):
-        """Log the row in full (stderr); keep [us, % of the bounding roof, roof] under a short
-        key for the JSON line: roof "h" = 8 TB/s HBM, "m" = bf16 matrix peak, "m8" = fp8."""
+        """Log the row in full (stderr); keep [us, % of the bounding roof] under a short key
+        for the JSON line.  The roof: 8 TB/s HBM for 128 tokens or fewer and the select rows,
+        otherwise the bf16 matrix peak on executed FLOPs (the fp8 peak for keys ending f8
+        of the lowered fp8 x fp8 rows, c3.*f8)."""
         gbps = nbytes / us / 1e3
         if bound == "hbm" or (bound is None and t <= 128):
             roof, frac = "h", gbps / PEAK_HBM_GBS
         else:
             roof, frac = ("m8" if peak == PEAK_FP8_TFLOPS else "m"), f_exec / us / 1e6 / peak
-        rows[key or f"{cfg}.{t}"] = [round(us, 1), round(100 * frac, 1), roof]
+        rows[key or f"{cfg}.{t}"] = [round(us, 1) if us < 1000 else round(us), round(100 * frac, 1)]
         log(f"  {cfg:5s} T={t:5d} {path:34s} {us:9.1f} us  {f_dense / us / 1e6:8.1f} TF/s dense-eq  "
             f"{f_exec / us / 1e6:8.1f} TF/s exec  {gbps:7.0f} GB/s  {roof} {100 * frac:.1f}%  [{key or cfg}]")
 
@@ -237,44 +250,58 @@ def measure_rows(torch, S, synth, np):
 
     keep = []
     # cfg1: 2:4 activations, 64 x 512 x 512
-    d = synth.layer_2of4_small()
-    x1, w1 = dev(d["x"]), dev(d["w"])
-    y = f32(64, 512)
-    fn = spmm(S.make_spmm_args(S.NM_ACT_DYNAMIC, 64, 512, 512, x1, w1, y, n=2, m=4), keep)
-    add("cfg1", 64, "2:4 act (select + product)", gpu_time_us(torch, fn, True), 2.0 * 64 * 512 * 512,
-        2.0 * 64 * 512 * 512, 64 * 512 * 2 + 512 * 512 * 2 + 64 * 512 * 4, key="c1.64")
+    if want("c1.64"):
+        d = synth.layer_2of4_small()
+        x1, w1 = dev(d["x"]), dev(d["w"])
+        y = f32(64, 512)
+        fn = spmm(S.make_spmm_args(S.NM_ACT_DYNAMIC, 64, 512, 512, x1, w1, y, n=2, m=4), keep)
+        add("cfg1", 64, "2:4 act (select + product)", gpu_time_us(torch, fn, True), 2.0 * 64 * 512 * 512,
+            2.0 * 64 * 512 * 512, 64 * 512 * 2 + 512 * 512 * 2 + 64 * 512 * 4, key="c1.64")
     # cfg2: 8:16 activations, down-projection 4096 x 14336
     d = synth.mlp_down_8of16(t_max=8192)
     x2, w2 = dev(d["x"]), dev(d["w"])
     O2, K2 = 4096, 14336
-    wk2 = dev(np.ascontiguousarray(d["w"].T))
-    y = f32(1, O2)
-    fns = rot_spmm(lambda wk: S.make_spmm_args(S.NM_ACT_DYNAMIC, 1, O2, K2, x2[:1], w2, y, n=8, m=16, w_kmajor=wk),
-                   (wk2,), O2 * K2 * 2, keep)
-    add("cfg2", 1, "8:16 act, K-major gather", gpu_time_rot_us(torch, fns), 2.0 * O2 * K2, 2.0 * O2 * K2 / 2,
-        K2 // 2 * O2 * 2 + K2 * 2 + O2 * 4, key="c2.1g")
-    keep.clear()
-    del wk2
+    if want("c2.1g"):
+        wk2 = dev(np.ascontiguousarray(d["w"].T))
+        y = f32(1, O2)
+        fns = rot_spmm(lambda wk: S.make_spmm_args(S.NM_ACT_DYNAMIC, 1, O2, K2, x2[:1], w2, y, n=8, m=16,
+                                                   w_kmajor=wk), (wk2,), O2 * K2 * 2, keep)
+        add("cfg2", 1, "8:16 act, K-major gather", gpu_time_rot_us(torch, fns), 2.0 * O2 * K2, 2.0 * O2 * K2 / 2,
+            K2 // 2 * O2 * 2 + K2 * 2 + O2 * 4, key="c2.1g")
+        keep.clear()
+        del wk2
     # the select kernel alone at 8192 tokens: S(X) + mask, and values + u8 index + mask
     t = 8192
     sxb = torch.empty((t, K2), dtype=torch.int16, device="cuda")
     mk = torch.empty((t, K2 // 32), dtype=torch.int32, device="cuda")
     vv = torch.empty((t, K2 // 2), dtype=torch.int16, device="cuda")
     ix = torch.empty((t, K2 // 2), dtype=torch.uint8, device="cuda")
-    fn = lambda: S.nm_sparsify(x2, 8, 16, sxb, mk, check=False)
-    add("cfg2", t, "select alone: S(X) + mask", gpu_time_us(torch, fn, False), 0.0, 0.0,
-        t * K2 * 2 + t * K2 * 2 + t * K2 // 8, bound="hbm", key="c2.sel")
-    fn = lambda: S.nm_compress(x2, 8, 16, vv, ix, S.NM_META_U8, mask=mk, check=False)
-    add("cfg2", t, "select alone: values + u8 idx + mask", gpu_time_us(torch, fn, False), 0.0, 0.0,
-        t * K2 * 2 + t * K2 // 2 * 3 + t * K2 // 8, bound="hbm", key="c2.cmp")
-    # scored selection: activations weighted by the fp32 L2 norm of each weight column
-    cs = w2.view(torch.bfloat16).float().pow(2).sum(0).sqrt().contiguous()
-    fn = lambda: S.nm_sparsify_scored(x2, 8, 16, cs, S.NM_SCORE_ACT_WEIGHTED, sxb, mk, check=False)
-    add("cfg2", t, "select alone, |x| * weight-column norm: S(X) + mask", gpu_time_us(torch, fn, False), 0.0, 0.0,
-        t * K2 * 2 + t * K2 * 2 + t * K2 // 8 + K2 * 4, bound="hbm", key="c2.selsc")
-    del cs
+    if want("c2.sel"):
+        fn = lambda: S.nm_sparsify(x2, 8, 16, sxb, mk, check=False)
+        add("cfg2", t, "select alone: S(X) + mask", gpu_time_us(torch, fn, False), 0.0, 0.0,
+            t * K2 * 2 + t * K2 * 2 + t * K2 // 8, bound="hbm", key="c2.sel")
+    if want("c2.cmp"):
+        fn = lambda: S.nm_compress(x2, 8, 16, vv, ix, S.NM_META_U8, mask=mk, check=False)
+        add("cfg2", t, "select alone: values + u8 idx + mask", gpu_time_us(torch, fn, False), 0.0, 0.0,
+            t * K2 * 2 + t * K2 // 2 * 3 + t * K2 // 8, bound="hbm", key="c2.cmp")
+    if want("c2.selsc"):
+        # scored selection: activations weighted by the fp32 L2 norm of each weight column
+        cs = w2.view(torch.bfloat16).float().pow(2).sum(0).sqrt().contiguous()
+        fn = lambda: S.nm_sparsify_scored(x2, 8, 16, cs, S.NM_SCORE_ACT_WEIGHTED, sxb, mk, check=False)
+        add("cfg2", t, "select alone, |x| * weight-column norm: S(X) + mask", gpu_time_us(torch, fn, False), 0.0,
+            0.0, t * K2 * 2 + t * K2 * 2 + t * K2 // 8 + K2 * 4, bound="hbm", key="c2.selsc")
+        del cs
+    if want("c2.selpts"):
+        # the mitigated selection (D-PTS + VAR): row mean, shift, select, variance factor
+        mu_, al_ = f32(t), f32(t)
+        fn = lambda: S.nm_sparsify_pts(x2, 8, 16, S.NM_PTS_DYNAMIC | S.NM_PTS_VAR, sxb, mk, None, mu_, al_,
+                                       check=False)
+        add("cfg2", t, "select alone, D-PTS + VAR: S(x~) + mask", gpu_time_us(torch, fn, False), 0.0, 0.0,
+            t * K2 * 2 + t * K2 * 2 + t * K2 // 8 + 2 * t * 4, bound="hbm", key="c2.selpts")
     del sxb, mk, vv, ix
     for t in (1, 16, 128, 2048, 8192):
+        if not want(f"c2.{t}"):
+            continue
         y = f32(t, O2)
         f = 2.0 * t * O2 * K2
         if t <= 128:
@@ -285,6 +312,23 @@ def measure_rows(torch, S, synth, np):
             us = gpu_time_us(torch, spmm(S.make_spmm_args(S.NM_ACT_DYNAMIC, t, O2, K2, x2[:t], w2, y, n=8, m=16),
                                          keep), False)
         add("cfg2", t, "8:16 act (select + product)", us, f, f, t * K2 * 2 + O2 * K2 * 2 + t * O2 * 4, key=f"c2.{t}")
+        keep.clear()
+    # the same layer with the mitigations (D-PTS + VAR) inside the call
+    v2 = f32(O2)
+    S.nm_weight_sums(w2, v2)
+    for t in (1, 128, 8192):
+        if not want(f"c2.{t}pts"):
+            continue
+        y = f32(t, O2)
+        f = 2.0 * t * O2 * K2
+        mkp = lambda w: S.make_spmm_args(S.NM_ACT_DYNAMIC, t, O2, K2, x2[:t], w, y, n=8, m=16,
+                                         pts=S.NM_PTS_DYNAMIC | S.NM_PTS_VAR, col_shift=v2)
+        if t <= 128:
+            us = gpu_time_rot_us(torch, rot_spmm(mkp, (w2,), O2 * K2 * 2, keep))
+        else:
+            us = gpu_time_us(torch, spmm(mkp(w2), keep), False)
+        add("cfg2", t, "8:16 act, D-PTS + VAR (select + product)", us, f, f,
+            t * K2 * 2 + O2 * K2 * 2 + t * O2 * 4 + O2 * 4, key=f"c2.{t}pts")
         keep.clear()
     del x2, w2
     # cfg3: 6:8 weights lowered to 2:4, 4096 x 4096, lifted activations
@@ -297,6 +341,8 @@ def measure_rows(torch, S, synth, np):
     mp = torch.empty((4096, 768), dtype=torch.uint8, device="cuda")
     S.nm_lower_slide(v, i8, 4096, 4096, 4, vp, mp, S.NM_META_2BIT)
     for t in (1, 16, 128, 4096):
+        if not want(f"c3.{t}"):
+            continue
         y = f32(t, 4096)
         mk3 = lambda v_, m_: S.make_spmm_args(S.NM_W_SLIDE, t, 4096, 4096, x3[:t], v_, y, ns=4, w_meta=m_,
                                               w_meta_fmt=S.NM_META_2BIT)
@@ -314,6 +360,8 @@ def measure_rows(torch, S, synth, np):
     q8d, s8d = dev(q8), torch.from_numpy(s8).cuda()
     wb8 = 4096 * 3072 + 4096 * 768 + 4096 * 4
     for t in (1, 16, 128, 4096):
+        if not want(f"c3.{t}f8"):
+            continue
         y = f32(t, 4096)
         mk8 = lambda q_, s_, m_: S.make_spmm_args(S.NM_W_SLIDE, t, 4096, 4096, x3[:t], q_, y, ns=4,
                                                   w_dtype=S.NM_W_FP8E4M3, w_scale=s_, w_meta=m_,
@@ -341,6 +389,8 @@ def measure_rows(torch, S, synth, np):
     S.nm_hybrid_pack(w4, kd, sc, dc, wv, wm, S.NM_META_2BIT, wd, buf(S.nm_hybrid_pack_workspace_size(k4)))
     wb4 = o4 * ks + o4 * ks // 8 + o4 * kd * 2
     for t in (1, 8, 32, 64, 2048):
+        if not want(f"c4.{t}"):
+            continue
         y = f32(t, o4)
         nb = S.nm_hybrid_gemm_workspace_size(t, ks, kd, o4, True)
         wsb = buf(nb)
@@ -356,6 +406,8 @@ def measure_rows(torch, S, synth, np):
         add("cfg4", t, "hybrid 2:4 + 25% dense columns", us, 2.0 * t * o4 * k4,
             2.0 * t * o4 * (kd + ks / 2), wb4 + t * k4 * 2 + t * o4 * 4, key=f"c4.{t}")
     del w4, x4, sc, dc, wv, wm, wd
+    if not (want("c5.") or want("sp.")):
+        return rows
     # cfg5: one 8B-shaped layer, 16:32 and 8:16, bf16 and fp8 weights, T = 64 and 8192
     lay = synth.transformer_layer(t_max=8192, with_fp8=True)
     names = list(synth.TRANSFORMER_SHAPES)
@@ -366,6 +418,8 @@ def measure_rows(torch, S, synth, np):
     for t in (64, 8192):
         for n, m in ((16, 32), (8, 16)):
             for kind in ("bf16", "fp8"):
+                if not want(f"c5.{t}.{m}{'f8' if kind == 'fp8' else ''}s"):
+                    continue
                 tot_us = tot_f = tot_b = 0.0
                 for nm in names:
                     o_, k_, st = synth.TRANSFORMER_SHAPES[nm]
@@ -388,7 +442,7 @@ def measure_rows(torch, S, synth, np):
                     tot_b += wb + t * k_ * 2 + t * o_ * 4
                     keep.clear()
                 add("cfg5", t, f"layer {n}:{m} act, {kind} W", tot_us, tot_f, tot_f, tot_b,
-                    key=f"c5.{t}.{n}of{m}{'f8' if kind == 'fp8' else ''}")
+                    key=f"c5.{t}.{m}{'f8' if kind == 'fp8' else ''}s")
     # the same layer with the linears that share an input concatenated along the output
     # dimension (q|k|v: 6144 x 4096, gate|up: 28672 x 4096): four calls instead of seven,
     # one selection per input stream, identical outputs
@@ -400,6 +454,8 @@ def measure_rows(torch, S, synth, np):
     for t in (64, 8192):
         for n, m in ((16, 32), (8, 16)):
             for kind in ("bf16", "fp8"):
+                if not want(f"c5.{t}.{m}{'f8' if kind == 'fp8' else ''}c"):
+                    continue
                 tot_us = tot_f = tot_b = 0.0
                 for g, parts in groups:
                     o_ = sum(synth.TRANSFORMER_SHAPES[nm][0] for nm in parts)
@@ -423,7 +479,7 @@ def measure_rows(torch, S, synth, np):
                     tot_b += wb + t * k_ * 2 + t * o_ * 4
                     keep.clear()
                 add("cfg5", t, f"layer {n}:{m} act, {kind} W, fused qkv + gate|up", tot_us, tot_f, tot_f, tot_b,
-                    key=f"c5.{t}.{n}of{m}{'f8' if kind == 'fp8' else ''}.cat")
+                    key=f"c5.{t}.{m}{'f8' if kind == 'fp8' else ''}c")
     # Spense MLP of the same layer: 25% of the intermediate indices dense, chosen by the
     # loss-aware score (Hessian roots from the layer's input streams) and moved to the end;
     # gate|up as one output-split call (rows [gate_s, up_s, gate_d, up_d]), down as an
@@ -454,6 +510,8 @@ def measure_rows(torch, S, synth, np):
     wbytes = o_s * hd + o_s * hd // 8 + o_d * hd * 2 + hd * ns + hd * ns // 8 + hd * n_dense * 2
     packed = (gv, gm, gd, dv, dm, dd)
     for t in (1, 64, 2048):
+        if not want(f"sp.{t}"):
+            continue
         xg, a_in = xdev["mlp_in"][:t], xdev["down_in"][:t]   # down's input: the permuted GLU output's shape
         ygu, yd = f32(t, 2 * i_n), f32(t, hd)
         cps = [packed] + ([tuple(z.clone() for z in packed) for _ in range(n_copies(wbytes) - 1)] if t <= 128 else [])
@@ -489,6 +547,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip the per-workload rows (all five workloads at their token counts)")
+    ap.add_argument("--rows-only", default=None,
+                    help="comma-separated row-key prefixes: measure only those rows and print them (no headline)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB five times (counter calibration)")
     args = ap.parse_args()
@@ -513,11 +573,15 @@ def main():
         print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "launches": 5}))
         return
     S.lib()
+    if args.rows_only is not None:
+        rows = measure_rows(torch, S, synth, np, only=[p for p in args.rows_only.split(",") if p])
+        print(json.dumps({"rows": rows}, separators=(",", ":")), flush=True)
+        return
     extra = {}
     if not args.no_rows:
         # the per-workload rows and the machine ceilings run first: the headline steps are
         # then timed on a GPU whose clock has settled under sustained work
-        extra["ceilings"] = measure_ceilings(torch, S)
+        extra["ceil"] = measure_ceilings(torch, S)
         log("per-workload rows:")
         extra["rows"] = measure_rows(torch, S, synth, np)
         torch.cuda.synchronize()
@@ -568,11 +632,9 @@ def main():
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"8:16 act-sparse down-proj X {T}x{K} t(4)*0.5, W {O_}x{K} N(0,.02), fp32 out",
-                   "tokens": T, "in_features": K, "out_features": O_, "pattern": "8:16"},
-        "executed_tflops": round(value, 2),
-        "kernels": {"select_us": round(sel_ms * 1e3, 1), "select_frac_hbm": round(sel_bytes / sel_ms / 1e6 / PEAK_HBM_GBS, 3),
-                    "product_us": round(gemm_ms * 1e3, 1)},
+        "config": {"workload": f"8:16 act-sparse down-proj X {T}x{K} t(4)*.5, W {O_}x{K} N(0,.02)", "tokens": T,
+                   "pattern": "8:16"},
+        "kernels": {"select_us": round(sel_ms * 1e3, 1), "product_us": round(gemm_ms * 1e3, 1)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
     }

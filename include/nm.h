@@ -108,6 +108,55 @@ nm_status nm_sparsify_scored(const void* x, int64_t rows, int64_t k, int64_t ldx
                              uint32_t* mask, void* stream);
 
 /*
+ * Error mitigation of activation sparsity.  [FLEX] 2.B names light-weight corrections that
+ * need little or no calibration data: a per-token shift centring the activations before
+ * pruning, dynamic (D-PTS) or static (S-PTS), and a per-token variance correction after it
+ * (VAR); [FLEX] 4.C ranks them among the most effective.  The page gives no formulas; this
+ * library's readings:
+ *   NM_PTS_DYNAMIC  x~ = bf16(fp32(x - mu_t)), mu_t = the mean of token row t.  mu_t is
+ *                   computed reproducibly: every value is rounded to a multiple of
+ *                   q = 2^(E-162) (E = exponent field of the row's largest magnitude), the
+ *                   integers are summed exactly and mu = fp32(fp64(sum * q) / k) -- the
+ *                   row mean to within 2^-37 max|x|, the same bits in any summation order.
+ *                   The product adds back mu_t * (W . 1)_o.
+ *   NM_PTS_STATIC   x~ = bf16(fp32(x - c_k)) with the caller's per-channel shift c (a
+ *                   scalar shift is c_k = s); the product adds back (W . c)_o.
+ *   NM_PTS_VAR      alpha_t = sqrt(Var(x~_t) / Var(S(x~_t))) (population variances over the
+ *                   k entries, pruned entries as zeros; 1 when the pruned row has no
+ *                   variance); the product scales token t by alpha_t.
+ * The selection is the ACT rule on x~ (bit-exact); with the mitigation the layer is
+ *   Y[t][o] = alpha_t * sum_k S(x~)[t][k] W[o][k] + beta_t * v_o,
+ * beta_t = mu_t (dynamic) or 1 (static), v = nm_weight_sums(W, shift) (W . 1 or W . c).
+ */
+enum { NM_PTS_DYNAMIC = 1, NM_PTS_STATIC = 2, NM_PTS_VAR = 4 };
+
+/*
+ * nm_sparsify_pts -- shift (pts & (NM_PTS_DYNAMIC | NM_PTS_STATIC), at most one), select
+ * and, with NM_PTS_VAR, the variance correction factor.  [FLEX] 2.A, 2.B, 2.C.
+ *   x          bf16 [rows][ldx], every value finite; k % 8 == 0, k <= 65536
+ *   shift      fp32 [k] (NM_PTS_STATIC; NULL otherwise), finite
+ *   y          bf16 [rows][ldy]: S(x~), required
+ *   mask       uint32 [rows][ceil(k/32)] or NULL
+ *   row_shift  fp32 [rows] or NULL: receives mu_t (NM_PTS_DYNAMIC)
+ *   row_scale  fp32 [rows]: receives alpha_t (required with NM_PTS_VAR)
+ * m in {4, 8, 16, 32}.  y, mask and row_shift are bit-exact; row_scale is the fp64 ratio
+ * rounded to fp32 (summation order free, so equal to the definition within a few ulp).
+ */
+nm_status nm_sparsify_pts(const void* x, int64_t rows, int64_t k, int64_t ldx, int n, int m, int pts,
+                          const float* shift, void* y, int64_t ldy, uint32_t* mask, float* row_shift,
+                          float* row_scale, void* stream);
+
+/*
+ * nm_weight_sums -- the per-output term that undoes a shift of the activations:
+ *   out[o] = fp32( s_o * sum_k dec(W[o][k]) * c_k )
+ * c = shift (fp32 [k], the static shift) or 1 when NULL (the dynamic shift's W . 1),
+ * s = w_scale[o] for fp8 weights, 1 for bf16; summed in fp64.  w bf16 [o][ldw] or e4m3 codes
+ * [o][ldw] bytes (w_dtype); out fp32 [o].  An offline step, once per weight (and shift).
+ */
+nm_status nm_weight_sums(const void* w, int64_t o, int64_t k, int64_t ldw, int w_dtype, const float* w_scale,
+                         const float* shift, float* out, void* stream);
+
+/*
  * nm_compress -- select and compact in one pass, straight from the dense input.
  * [FLEX] 1 (values plus index metadata), [SLIDE] 2.C (load-time compression).
  *   x       bf16 [rows][ldx]
@@ -270,6 +319,16 @@ typedef enum {
  *               split-K tile route for 33-128 tokens needs this).  With less, the call
  *               takes a route that needs none (slower).  Contents after the call are
  *               unspecified.  Calls sharing a workspace must be ordered (same stream).
+ *   pts, pts_shift, col_shift, row_scale, row_shift   the activation-sparsity
+ *               mitigations ([FLEX] 2.B): ACT_DYNAMIC with pts != 0 shifts, selects and
+ *               (NM_PTS_VAR) computes alpha inside the call (x finite, k % 8 == 0,
+ *               k <= 65536, m in {4, 8, 16, 32}, a workspace of nm_spmm_workspace_size
+ *               bytes required), then Y = alpha_t * (S(x~) W^T) + beta_t * col_shift[o].
+ *               In ACT_MASKED / ACT_COMPRESSED the terms come from the caller (the two-pass
+ *               form with nm_sparsify_pts): Y = row_scale[t] * (...) + beta_t * col_shift[o],
+ *               beta_t = row_shift[t] (1 when row_shift is NULL); NULL drops a factor or
+ *               term.  row_shift needs col_shift; all need 16-byte alignment.  W_* modes
+ *               take none of them (NM_EUNSUPPORTED).
  *   route       NM_ROUTE_* hint bits (0: the library chooses by shape)
  *   few_wpb     few-token streaming kernels: waves per workgroup (4, 8 or 16; 0 = chosen)
  *   few_splits  few-token streaming kernels: reduction splits across workgroups (0 = chosen)
@@ -307,6 +366,12 @@ typedef struct {
   int32_t few_splits;
   int32_t tile_wg;
   uint32_t* route_taken;  /* optional host pointer: NM_TAKEN_* bits of what ran    */
+  /* error mitigation and output terms (ACT_* modes), see NM_PTS_*:                */
+  int pts;                /* ACT_DYNAMIC: NM_PTS_* applied inside the call          */
+  const float* pts_shift; /* NM_PTS_STATIC: fp32 [k]                                */
+  const float* col_shift; /* fp32 [o]: v (nm_weight_sums); required with a shift    */
+  const float* row_scale; /* ACT_MASKED / ACT_COMPRESSED: fp32 [t] alpha_t, or NULL */
+  const float* row_shift; /* ACT_MASKED / ACT_COMPRESSED: fp32 [t] beta_t, or NULL  */
 } nm_spmm_args;
 
 /*

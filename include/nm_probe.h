@@ -3,8 +3,11 @@
  * exported by libnmsparse): the achievable ceilings of the machine at hand, reported
  * beside the nominal peaks.  Same conventions as nm.h (device pointers, enqueue-only).
  *   nm_probe_sink_bytes   bytes of the device sink both probes write.
- *   nm_probe_read         one streaming read of `bytes` (a multiple of 16) at buf; buf and
- *                         sink 16-byte aligned.
+ *   nm_probe_read         one streaming read of `bytes` (a multiple of 16; of 16384 for
+ *                         mode 2) at buf; buf and sink 16-byte aligned.  mode 0: 16-byte
+ *                         loads at a grid stride, 4 in flight per lane; 1: one contiguous
+ *                         block per workgroup, 16 loads in flight per lane; 2: direct-to-LDS
+ *                         16-byte loads, contiguous 16 KiB chunks per wave.
  *   nm_probe_mfma         `iters` rounds of 16 independent bf16 16x16x32 matrix instructions
  *                         per wave on register operands; nm_probe_mfma_flops(iters) gives the
  *                         FLOPs one launch performs.
@@ -20,7 +23,7 @@ extern "C" {
 #endif
 
 int64_t nm_probe_sink_bytes(void);
-nm_status nm_probe_read(const void* buf, int64_t bytes, void* sink, void* stream);
+nm_status nm_probe_read(const void* buf, int64_t bytes, void* sink, int mode, void* stream);
 int64_t nm_probe_mfma_flops(int64_t iters);
 nm_status nm_probe_mfma(int64_t iters, void* sink, void* stream);
 

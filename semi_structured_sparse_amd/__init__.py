@@ -23,7 +23,8 @@ __all__ = [
     "nm_spmm_workspace_size", "nm_hybrid_pack", "nm_hybrid_pack_workspace_size", "nm_hybrid_gemm",
     "nm_hybrid_gemm_workspace_size", "lowered_k", "NM_SPENSE_LOSS", "NM_SPENSE_TAIL", "nm_spense_glu_order",
     "nm_spense_glu_order_workspace_size", "nm_spense_pack", "nm_spense_pack_workspace_size",
-    "nm_spense_outsplit_gemm", "nm_spense_outsplit_workspace_size", "nm_quant_lift",
+    "nm_spense_outsplit_gemm", "nm_spense_outsplit_workspace_size", "nm_quant_lift", "NM_PTS_DYNAMIC",
+    "NM_PTS_STATIC", "NM_PTS_VAR", "nm_sparsify_pts", "nm_weight_sums",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnmsparse.so")
@@ -34,6 +35,7 @@ NM_W_BF16, NM_W_FP8E4M3 = 0, 1
 NM_SCORE_ACT_WEIGHTED, NM_SCORE_WEIGHT = 0, 1
 NM_SPENSE_LOSS, NM_SPENSE_TAIL = 0, 1
 NM_ACT_DYNAMIC, NM_ACT_COMPRESSED, NM_W_COMPRESSED, NM_W_SLIDE, NM_ACT_MASKED = range(5)
+NM_PTS_DYNAMIC, NM_PTS_STATIC, NM_PTS_VAR = 1, 2, 4
 
 # route hints (NM_ROUTE_*) and the report of what ran (NM_TAKEN_*), by lower-case name
 ROUTE = {name: 1 << i for i, name in enumerate(
@@ -74,6 +76,7 @@ class nm_spmm_args(ctypes.Structure):
         ("x_mask_out", _vp), ("workspace", _vp), ("workspace_bytes", _i64),
         ("route", ctypes.c_uint32), ("few_wpb", ctypes.c_int32), ("few_splits", ctypes.c_int32),
         ("tile_wg", ctypes.c_int32), ("route_taken", _vp),
+        ("pts", _int), ("pts_shift", _vp), ("col_shift", _vp), ("row_scale", _vp), ("row_shift", _vp),
     ]
 
 
@@ -102,6 +105,10 @@ def lib() -> ctypes.CDLL:
     L.nm_sparsify.argtypes = [_vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _vp]
     L.nm_sparsify_scored.restype = _int
     L.nm_sparsify_scored.argtypes = [_vp, _i64, _i64, _i64, _int, _int, _vp, _int, _vp, _i64, _vp, _vp]
+    L.nm_sparsify_pts.restype = _int
+    L.nm_sparsify_pts.argtypes = [_vp, _i64, _i64, _i64, _int, _int, _int, _vp, _vp, _i64, _vp, _vp, _vp, _vp]
+    L.nm_weight_sums.restype = _int
+    L.nm_weight_sums.argtypes = [_vp, _i64, _i64, _i64, _int, _vp, _vp, _vp, _vp]
     L.nm_compress.restype = _int
     L.nm_compress.argtypes = [_vp, _i64, _i64, _i64, _int, _int, _vp, _vp, _int, _vp, _vp]
     L.nm_decompress.restype = _int
@@ -212,6 +219,29 @@ def nm_sparsify_scored(x, n, m, col_score, mode=NM_SCORE_ACT_WEIGHTED, y=None, m
     return st
 
 
+def nm_sparsify_pts(x, n, m, pts, y, mask=None, shift=None, row_shift=None, row_scale=None, stream=None, *,
+                    rows=None, k=None, ldx=None, ldy=None, check=True):
+    rows = x.shape[0] if rows is None else rows
+    k = x.shape[1] if k is None else k
+    st = lib().nm_sparsify_pts(_ptr(x), rows, k, _ld(x) if ldx is None else ldx, n, m, pts, _ptr(shift), _ptr(y),
+                               _ld(y) if ldy is None else ldy, _ptr(mask), _ptr(row_shift), _ptr(row_scale),
+                               _stream(stream))
+    if check:
+        _check(st, "nm_sparsify_pts")
+    return st
+
+
+def nm_weight_sums(w, out, w_dtype=NM_W_BF16, w_scale=None, shift=None, stream=None, *, o=None, k=None, ldw=None,
+                   check=True):
+    o = w.shape[0] if o is None else o
+    k = w.shape[1] if k is None else k
+    st = lib().nm_weight_sums(_ptr(w), o, k, _ld(w) if ldw is None else ldw, w_dtype, _ptr(w_scale), _ptr(shift),
+                              _ptr(out), _stream(stream))
+    if check:
+        _check(st, "nm_weight_sums")
+    return st
+
+
 def nm_compress(x, n, m, values, meta, fmt=NM_META_U8, mask=None, stream=None, *, rows=None, k=None, ldx=None,
                 check=True):
     rows = x.shape[0] if rows is None else rows
@@ -263,7 +293,8 @@ def nm_spmm_workspace_size(args: nm_spmm_args) -> int:
 def make_spmm_args(mode, t, o, k, x, w, y, *, n=2, m=4, ns=2, ldx=None, x_meta=None, x_meta_fmt=NM_META_U8,
                    ldw=None, w_dtype=NM_W_BF16, w_meta=None, w_meta_fmt=NM_META_2BIT, w_scale=None,
                    w_kmajor=None, ldy=None, accumulate=0, x_mask_out=None, workspace=None, workspace_bytes=0,
-                   route=0, few_wpb=0, few_splits=0, tile_wg=0):
+                   route=0, few_wpb=0, few_splits=0, tile_wg=0, pts=0, pts_shift=None, col_shift=None,
+                   row_scale=None, row_shift=None):
     """Fill an nm_spmm_args from tensors (pointers and leading dimensions only).  The
     returned struct keeps references to the tensors so that their memory stays allocated
     while the struct is alive (it holds raw device pointers), and carries a report cell
@@ -272,8 +303,11 @@ def make_spmm_args(mode, t, o, k, x, w, y, *, n=2, m=4, ns=2, ldx=None, x_meta=N
     a._taken = ctypes.c_uint32(0)
     a.route, a.few_wpb, a.few_splits, a.tile_wg = route, few_wpb, few_splits, tile_wg
     a.route_taken = ctypes.addressof(a._taken)
-    a._tensors = [v for v in (x, w, y, x_meta, w_meta, w_scale, w_kmajor, x_mask_out, workspace)
+    a._tensors = [v for v in (x, w, y, x_meta, w_meta, w_scale, w_kmajor, x_mask_out, workspace, pts_shift,
+                              col_shift, row_scale, row_shift)
                   if v is not None and not isinstance(v, int)]
+    a.pts, a.pts_shift, a.col_shift = pts, _ptr(pts_shift), _ptr(col_shift)
+    a.row_scale, a.row_shift = _ptr(row_scale), _ptr(row_shift)
     a.mode, a.n, a.m, a.ns = mode, n, m, ns
     a.t, a.o, a.k = t, o, k
     a.x, a.ldx = _ptr(x), (_ld(x) if ldx is None else ldx)

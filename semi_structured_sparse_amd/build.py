@@ -12,7 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libnmsparse.so")
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["api.hip", "select.hip", "slide.hip", "gemm_dense.hip", "gemm_lds.hip", "gemm_sparse.hip",
-           "gemm_lds_sp.hip", "hybrid_pack.hip", "spense.hip", "decode.hip"]
+           "gemm_lds_sp.hip", "hybrid_pack.hip", "spense.hip", "decode.hip", "pts.hip"]
 # measurement helpers live in a library of their own (not exported by libnmsparse)
 PROBE_SOURCES = ["probe.hip"]
 PROBE_OUT = os.path.join(PKG, "libnmprobe.so")

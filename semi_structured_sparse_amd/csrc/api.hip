@@ -141,6 +141,7 @@ nml::FewArgs few_dense_args(const nml::GemmArgs& g) {
   sg.x = g.x; sg.ldx = g.ldx; sg.loader = nml::XL_PLAIN; sg.ns = 2; sg.k = g.k;
   f.w_scale = g.w_scale; f.t = g.t; f.o = g.o; f.y = g.y; f.ldy = g.ldy; f.accumulate = g.accumulate;
   f.route = g.route;
+  f.row_scale = g.row_scale; f.row_shift = g.row_shift; f.col_shift = g.col_shift;
   return f;
 }
 
@@ -287,14 +288,16 @@ nm_status w8a8_product(const nm_spmm_args* a, int64_t kc, int ns, hipStream_t s)
 // the NM_ROUTE_FP8_WIDEN hint.
 int64_t fp8_widen_bytes(const nm_spmm_args* a) {
   const nml::Route r = route_of(a, false);
-  if (a->mode != NM_ACT_DYNAMIC || a->w_dtype != NM_W_FP8E4M3 || use_few(a->t, r)) return 0;
+  if (a->mode != NM_ACT_DYNAMIC || a->pts != 0 || a->w_dtype != NM_W_FP8E4M3 || use_few(a->t, r)) return 0;
   if (a->k % 64 != 0 || a->t < 512) return 0;
   if (!r.has(NM_ROUTE_FP8_WIDEN) && a->ldw % 16 == 0) return 0;
   return a->o * a->k * 2;
 }
 
-// Bytes of S(X) / decompressed-X staging at the start of nm_spmm's workspace.
+// Bytes of S(X) / decompressed-X staging at the start of nm_spmm's workspace.  With the
+// activation mitigations: [S(x~)][mu [t]][alpha [t]].
 int64_t spmm_stage_bytes(const nm_spmm_args* a) {
+  if (a->mode == NM_ACT_DYNAMIC && a->pts != 0) return align256(a->t * a->k * 2) + 2 * align256(a->t * 4);
   if (a->mode == NM_ACT_DYNAMIC) return a->t * a->k * 2 + 64;   // also holds the 2:4 compressed X
   if (a->mode == NM_ACT_COMPRESSED) return a->t * a->k * 2;
   return 0;
@@ -389,6 +392,50 @@ nm_status nm_sparsify_scored(const void* x, int64_t rows, int64_t k, int64_t ldx
                                               as_stream(stream)));
 }
 
+nm_status nm_sparsify_pts(const void* x, int64_t rows, int64_t k, int64_t ldx, int n, int m, int pts,
+                          const float* shift, void* y, int64_t ldy, uint32_t* mask, float* row_shift,
+                          float* row_scale, void* stream) {
+  nm_status st = check_pattern(k, n, m);
+  if (st) return st;
+  if (rows < 0) return NM_ESHAPE;
+  if ((pts & ~(NM_PTS_DYNAMIC | NM_PTS_STATIC | NM_PTS_VAR)) != 0) return NM_EINVAL;
+  if ((pts & NM_PTS_DYNAMIC) && (pts & NM_PTS_STATIC)) return NM_EINVAL;
+  if ((pts & NM_PTS_STATIC) && shift == nullptr && k > 0) return NM_EINVAL;
+  if ((pts & NM_PTS_VAR) && row_scale == nullptr && rows > 0) return NM_EINVAL;
+  if (y == nullptr && rows > 0 && k > 0) return NM_EINVAL;
+  if (k % 8 != 0 || k > 65536) return NM_ESHAPE;
+  if ((st = check_bf16(x, rows, k, ldx, true))) return st;
+  if ((st = check_bf16(y, rows, k, ldy, true))) return st;
+  if (!aligned16(mask) || !aligned16(shift) || !aligned16(row_shift) || !aligned16(row_scale)) return NM_EALIGN;
+  if (rows == 0 || k == 0) return NM_OK;
+  if (rows > 0x7FFFFFFF) return NM_ESHAPE;
+  const bool dyn = (pts & NM_PTS_DYNAMIC) != 0;
+  return hip_status(nml::launch_select_pts(m, (const uint16_t*)x, rows, k, ldx, n, dyn ? 1 : 0,
+                                           (pts & NM_PTS_STATIC) ? shift : nullptr, (pts & NM_PTS_VAR) ? 1 : 0,
+                                           (uint16_t*)y, ldy, mask, dyn ? row_shift : nullptr,
+                                           (pts & NM_PTS_VAR) ? row_scale : nullptr, as_stream(stream)));
+}
+
+nm_status nm_weight_sums(const void* w, int64_t o, int64_t k, int64_t ldw, int w_dtype, const float* w_scale,
+                         const float* shift, float* out, void* stream) {
+  if (o < 0 || k < 0) return NM_ESHAPE;
+  if (w_dtype != NM_W_BF16 && w_dtype != NM_W_FP8E4M3) return NM_EINVAL;
+  nm_status st;
+  if (w_dtype == NM_W_BF16) {
+    if ((st = check_bf16(w, o, k, ldw, true, 1))) return st;
+  } else {
+    if (w == nullptr && o > 0 && k > 0) return NM_EINVAL;
+    if (ldw < k || !span_ok(o, ldw)) return NM_ESHAPE;
+    if (w_scale == nullptr && o > 0) return NM_EINVAL;
+  }
+  if (out == nullptr && o > 0) return NM_EINVAL;
+  if (!aligned16(w) || !aligned16(w_scale) || !aligned16(shift) || !aligned16(out)) return NM_EALIGN;
+  if (o == 0) return NM_OK;
+  return hip_status(nml::launch_weight_sums(w, o, k, ldw, w_dtype == NM_W_FP8E4M3 ? 1 : 0,
+                                            w_dtype == NM_W_FP8E4M3 ? w_scale : nullptr, shift, out,
+                                            as_stream(stream)));
+}
+
 nm_status nm_compress(const void* x, int64_t rows, int64_t k, int64_t ldx, int n, int m, void* values,
                       void* meta, nm_meta fmt, uint32_t* mask, void* stream) {
   nm_status st = check_select_pattern(k, n, m, mask != nullptr);
@@ -470,7 +517,7 @@ nm_status nm_quant_lift(const void* x, int64_t t, int64_t k, int64_t ldx, int ns
 
 // Single-token route over K-major weights (reads only the selected K-rows).
 bool gather1_route(const nm_spmm_args* a) {
-  return a->mode == NM_ACT_DYNAMIC && a->t == 1 && a->w_kmajor != nullptr && a->w_dtype == NM_W_BF16 &&
+  return a->mode == NM_ACT_DYNAMIC && a->pts == 0 && a->t == 1 && a->w_kmajor != nullptr && a->w_dtype == NM_W_BF16 &&
          a->w_scale == nullptr && a->o > 0 && a->k > 0 && (a->o % 8) == 0 && supported_m(a->m);
 }
 
@@ -529,6 +576,23 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
     if (a->ldy < O || !span_ok(T, a->ldy)) return NM_ESHAPE;
     if (!aligned16(a->y)) return NM_EALIGN;
   }
+  // activation mitigations and output terms (ACT_* modes only)
+  const bool epi_in = a->row_scale != nullptr || a->row_shift != nullptr || a->col_shift != nullptr;
+  if (a->pts != 0 || epi_in) {
+    if (a->mode == NM_W_COMPRESSED || a->mode == NM_W_SLIDE) return NM_EUNSUPPORTED;
+    if ((a->pts & ~(NM_PTS_DYNAMIC | NM_PTS_STATIC | NM_PTS_VAR)) != 0) return NM_EINVAL;
+    if ((a->pts & NM_PTS_DYNAMIC) && (a->pts & NM_PTS_STATIC)) return NM_EINVAL;
+    if (a->pts != 0 && a->mode != NM_ACT_DYNAMIC) return NM_EINVAL;
+    if (a->mode == NM_ACT_DYNAMIC && (a->row_scale != nullptr || a->row_shift != nullptr)) return NM_EINVAL;
+    const bool shifted = (a->pts & (NM_PTS_DYNAMIC | NM_PTS_STATIC)) != 0;
+    if (a->mode == NM_ACT_DYNAMIC && shifted != (a->col_shift != nullptr)) return NM_EINVAL;
+    if ((a->pts & NM_PTS_STATIC) && a->pts_shift == nullptr && K > 0) return NM_EINVAL;
+    if (a->row_shift != nullptr && a->col_shift == nullptr) return NM_EINVAL;
+    if (!aligned16(a->pts_shift) || !aligned16(a->col_shift) || !aligned16(a->row_scale) ||
+        !aligned16(a->row_shift))
+      return NM_EALIGN;
+    if (a->pts != 0 && (K % 8 != 0 || K > 65536)) return NM_ESHAPE;
+  }
   nm_status st;
   switch (a->mode) {
     case NM_ACT_DYNAMIC:
@@ -566,6 +630,7 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
       g.w = a->w; g.ldw = a->ldw; g.w_fp8 = fp8 ? 1 : 0; g.w_scale = a->w_scale;
       g.n = a->n; g.m = a->m; g.t = T; g.o = O; g.k = K;
       g.y = a->y; g.ldy = a->ldy; g.accumulate = a->accumulate; g.route = R;
+      g.row_scale = a->row_scale; g.row_shift = a->row_shift; g.col_shift = a->col_shift;
       // workspace: [S(X) or decompressed X staging][few-token partial sums]
       const int64_t stage = spmm_stage_bytes(a);
       const bool have_ws = a->workspace != nullptr && a->workspace_bytes >= stage;
@@ -573,7 +638,7 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
       float* part = ws_slice(a->workspace, a->workspace_bytes, stage > 0 ? align256(stage) : 0, &part_avail);
 
       if (a->mode == NM_ACT_COMPRESSED) {
-        if (a->n == 2 && a->m == 4 && a->x_meta_fmt == NM_META_2BIT && !fp8 && a->w_scale == nullptr) {
+        if (a->n == 2 && a->m == 4 && a->x_meta_fmt == NM_META_2BIT && !fp8 && a->w_scale == nullptr && !epi_in) {
           // 2:4 activations: X is the sparse operand of the sparse matrix instruction
           nml::SparseArgs sa{};
           sa.w_vals = (const uint16_t*)a->x; sa.w_meta = (const uint8_t*)a->x_meta; sa.kc = K;
@@ -601,6 +666,26 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
         return hip_status(nml::launch_gemm_dense(g, s));
       }
 
+      // ACT_DYNAMIC with the activation mitigations: the shifted selection (and the VAR
+      // factor) into the workspace, then the product with the epilogue terms
+      if (a->pts != 0) {
+        if (!have_ws) return NM_EINVAL;
+        const bool dyn = (a->pts & NM_PTS_DYNAMIC) != 0, var = (a->pts & NM_PTS_VAR) != 0;
+        uint16_t* sx = (uint16_t*)a->workspace;
+        float* mu = reinterpret_cast<float*>(reinterpret_cast<char*>(a->workspace) + align256(T * K * 2));
+        float* alpha = mu + align256(T * 4) / 4;
+        hipError_t e = nml::launch_select_pts(a->m, (const uint16_t*)a->x, T, K, a->ldx, a->n, dyn ? 1 : 0,
+                                              (a->pts & NM_PTS_STATIC) ? a->pts_shift : nullptr, var ? 1 : 0, sx, K,
+                                              a->x_mask_out, dyn ? mu : nullptr, var ? alpha : nullptr, s);
+        if (e != hipSuccess) return NM_EHIP;
+        R.note(NM_TAKEN_SELECT);
+        g.x = sx; g.ldx = K; g.prologue = nml::PRO_NONE;
+        g.row_scale = var ? alpha : nullptr;
+        g.row_shift = dyn ? mu : nullptr;
+        g.col_shift = a->col_shift;
+        if (use_few(T, R)) return run_dense_few(g, part, part_avail, s);
+        return hip_status(nml::launch_gemm_dense(g, s));
+      }
       // ACT_DYNAMIC, one token with K-major weights: select and gather the kept K-rows
       if (gather1_route(a)) {
         const int64_t need = nml::gather1_part_bytes(K, O, a->m);
@@ -703,7 +788,7 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
         if (a->w_scale == nullptr && O > 0) return NM_EINVAL;
         if (a->w_scale != nullptr && !aligned16(a->w_scale)) return NM_EALIGN;
         if (kc % 128 != 0) return NM_EUNSUPPORTED;
-        if (T == 0 || O == 0) return NM_OK;
+          if (T == 0 || O == 0) return NM_OK;
         if (K == 0) return a->accumulate ? NM_OK : zero_output(a->y, T, O, a->ldy, s);
         return w8a8_product(a, kc, ns, s);
       }
@@ -752,6 +837,7 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
       return NM_EINVAL;
   }
 }
+
 
 // ------------------------------------------------------------- Spense GLU layout ---
 

@@ -276,7 +276,7 @@ __device__ __forceinline__ void part_range(int64_t k, int64_t p, int64_t P, int&
 template <int TB> struct MaxThreads { static constexpr int V = TB >= 4 ? 512 : 1024; };
 
 template <int TB, int RW, int WK0, int XL0, int NS, int WK1>
-__global__ __launch_bounds__(MaxThreads<TB>::V) void k_few(FewSeg s0, FewSeg s1, const float* __restrict__ wscale,
+__global__ __launch_bounds__(MaxThreads<TB>::V) void k_few(FewSeg s0, FewSeg s1, Epi epi,
                                                           int64_t T, int64_t O, float* __restrict__ y, int64_t ldy,
                                                           int accumulate, float* __restrict__ part, int splits) {
   extern __shared__ __align__(16) float red[];   // [waves][16 * TB * 16]
@@ -329,7 +329,7 @@ __global__ __launch_bounds__(MaxThreads<TB>::V) void k_few(FewSeg s0, FewSeg s1,
       if (part != nullptr) {
         part[((int64_t)split * T + t) * O + o] = sum;
       } else {
-        float v = wscale != nullptr ? sum * wscale[o] : sum;
+        float v = epi_apply(epi, sum, t, o);
         if (accumulate) v += y[t * ldy + o];
         y[t * ldy + o] = v;
       }
@@ -595,7 +595,7 @@ __device__ __forceinline__ void stage_row_dma(const uint16_t* __restrict__ src, 
 // workgroup keeps the SELM/2 largest magnitudes of each SELM-group in place (the select
 // pass's ranking, ties to the lower index) before the first multiply.
 template <int TB, int WK0, int XL0, int NS, int WK1, bool XS, int SELM = 0>
-__global__ __launch_bounds__(64 * Dma<TB>::WPB) void k_fewd(FewSeg s0, FewSeg s1, const float* __restrict__ wscale,
+__global__ __launch_bounds__(64 * Dma<TB>::WPB) void k_fewd(FewSeg s0, FewSeg s1, Epi epi,
                                                            int64_t T, int64_t O, float* __restrict__ y, int64_t ldy,
                                                            int accumulate, float* __restrict__ part, int splits,
                                                            int xn0, int xn1) {
@@ -695,7 +695,7 @@ __global__ __launch_bounds__(64 * Dma<TB>::WPB) void k_fewd(FewSeg s0, FewSeg s1
         if (part != nullptr) {
           part[((int64_t)split * T + t) * O + o] = sum;
         } else {
-          float v = wscale != nullptr ? sum * wscale[o] : sum;
+          float v = epi_apply(epi, sum, t, o);
           if (accumulate) v += y[t * ldy + o];
           y[t * ldy + o] = v;
         }
@@ -864,7 +864,7 @@ G1Plan g1_plan(int64_t k, int64_t o, int m) {
 constexpr int RP_OUT = 64, RP_LANES = 4;
 
 __global__ __launch_bounds__(RP_OUT * RP_LANES) void k_reduce_parts(const float* __restrict__ part, int64_t splits,
-                                                                   const float* __restrict__ wscale, int64_t T,
+                                                                   Epi epi, int64_t T,
                                                                    int64_t O, float* __restrict__ y, int64_t ldy,
                                                                    int accumulate) {
   __shared__ float sums[RP_LANES][RP_OUT];
@@ -891,7 +891,7 @@ __global__ __launch_bounds__(RP_OUT * RP_LANES) void k_reduce_parts(const float*
 #pragma unroll
   for (int l = 1; l < RP_LANES; ++l) sum += sums[l][lo];
   const int64_t t = i / O, o = i - t * O;
-  float v = wscale != nullptr ? sum * wscale[o] : sum;
+  float v = epi_apply(epi, sum, t, o);
   if (accumulate) v += y[t * ldy + o];
   y[t * ldy + o] = v;
 }
@@ -901,7 +901,7 @@ __global__ __launch_bounds__(RP_OUT * RP_LANES) void k_reduce_parts(const float*
 constexpr int RP4_THREADS = 256;
 
 __global__ __launch_bounds__(RP4_THREADS) void k_reduce_parts4(const float* __restrict__ part, int64_t splits,
-                                                               const float* __restrict__ wscale, int64_t T,
+                                                               Epi epi, int64_t T,
                                                                int64_t O, float* __restrict__ y, int64_t ldy,
                                                                int accumulate) {
   const int64_t n = T * O;
@@ -930,11 +930,21 @@ __global__ __launch_bounds__(RP4_THREADS) void k_reduce_parts4(const float* __re
     acc.w += v.w;
   }
   const int64_t t = i / O, o = i - t * O;   // O % 4 == 0: the 4 outputs share a row
-  if (wscale != nullptr) {
-    acc.x *= wscale[o];
-    acc.y *= wscale[o + 1];
-    acc.z *= wscale[o + 2];
-    acc.w *= wscale[o + 3];
+  if (epi.w_scale != nullptr) {
+    acc.x *= epi.w_scale[o];
+    acc.y *= epi.w_scale[o + 1];
+    acc.z *= epi.w_scale[o + 2];
+    acc.w *= epi.w_scale[o + 3];
+  }
+  if (epi.extra()) {
+    const float rs = epi.row_scale != nullptr ? epi.row_scale[t] : 1.f;
+    const float rb = epi.col_shift != nullptr ? (epi.row_shift != nullptr ? epi.row_shift[t] : 1.f) : 0.f;
+    const float4 cs = epi.col_shift != nullptr ? *reinterpret_cast<const float4*>(epi.col_shift + o)
+                                              : make_float4(0.f, 0.f, 0.f, 0.f);
+    acc.x = acc.x * rs + rb * cs.x;
+    acc.y = acc.y * rs + rb * cs.y;
+    acc.z = acc.z * rs + rb * cs.z;
+    acc.w = acc.w * rs + rb * cs.w;
   }
   float4* yp = reinterpret_cast<float4*>(y + t * ldy + o);
   if (accumulate) {
@@ -1052,14 +1062,14 @@ hipError_t launch_k(const FewArgs& a, const Plan& p, float* part, hipStream_t s)
         a.route.note(NM_TAKEN_FEW_STREAM | NM_TAKEN_FEW_XLDS | (a.sel_m != 0 ? NM_TAKEN_FEW_SELECT : 0u) |
                      (WK0 == WK_SP24 ? NM_TAKEN_SPARSE_MMA : 0u));
         kern<<<dim3((unsigned)blocks), dim3(64 * p.wpb), (size_t)xbytes, s>>>(
-            a.seg[0], s1, a.w_scale, a.t, a.o, a.y, a.ldy, a.accumulate, pp, (int)p.splits, (int)xn0, (int)xn1);
+            a.seg[0], s1, a.epi(), a.t, a.o, a.y, a.ldy, a.accumulate, pp, (int)p.splits, (int)xn0, (int)xn1);
         return hipGetLastError();
       }
     }
     if (a.sel_m != 0) return hipErrorInvalidValue;   // selection needs the staged row
     a.route.note(NM_TAKEN_FEW_STREAM | (WK0 == WK_SP24 ? NM_TAKEN_SPARSE_MMA : 0u));
     k_fewd<TB, WK0, XL0, NS, WK1, false><<<dim3((unsigned)blocks), dim3(64 * p.wpb), 0, s>>>(
-        a.seg[0], s1, a.w_scale, a.t, a.o, a.y, a.ldy, a.accumulate, pp, (int)p.splits, 0, 0);
+        a.seg[0], s1, a.epi(), a.t, a.o, a.y, a.ldy, a.accumulate, pp, (int)p.splits, 0, 0);
   } else {
     auto kern = k_few<TB, RW, WK0, XL0, NS, WK1>;
     const size_t lds = (size_t)p.wpb * TB * 1024;
@@ -1069,7 +1079,7 @@ hipError_t launch_k(const FewArgs& a, const Plan& p, float* part, hipStream_t s)
     }
     if (a.sel_m != 0) return hipErrorInvalidValue;
     a.route.note(NM_TAKEN_FEW_STREAM | (WK0 == WK_SP24 ? NM_TAKEN_SPARSE_MMA : 0u));
-    kern<<<dim3((unsigned)blocks), dim3(64 * p.wpb), lds, s>>>(a.seg[0], s1, a.w_scale, a.t, a.o, a.y, a.ldy,
+    kern<<<dim3((unsigned)blocks), dim3(64 * p.wpb), lds, s>>>(a.seg[0], s1, a.epi(), a.t, a.o, a.y, a.ldy,
                                                                a.accumulate, pp, (int)p.splits);
   }
   return hipGetLastError();
@@ -1146,7 +1156,7 @@ hipError_t launch_few(const FewArgs& a, float* part, int64_t part_bytes, hipStre
     e = launch_lift(a, p, part, s);
   }
   if (e != hipSuccess || p.splits == 1) return e;
-  return launch_reduce_parts(part, p.splits, a.w_scale, a.t, a.o, a.y, a.ldy, a.accumulate, a.route, s);
+  return launch_reduce_parts(part, p.splits, a.epi(), a.t, a.o, a.y, a.ldy, a.accumulate, a.route, s);
 }
 
 int64_t gather1_part_bytes(int64_t k, int64_t o, int m) {
@@ -1172,23 +1182,23 @@ hipError_t launch_gather1(int m, const uint16_t* x, int64_t k, int n, const uint
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   r.note(NM_TAKEN_GATHER1);
-  return launch_reduce_parts(part, p.nks, nullptr, 1, o, y, o, accumulate, r, s);   // one row: ldy unused
+  return launch_reduce_parts(part, p.nks, Epi{}, 1, o, y, o, accumulate, r, s);   // one row: ldy unused
 }
 
-hipError_t launch_reduce_parts(const float* part, int64_t splits, const float* w_scale, int64_t t, int64_t o,
+hipError_t launch_reduce_parts(const float* part, int64_t splits, const Epi& epi, int64_t t, int64_t o,
                                float* y, int64_t ldy, int accumulate, const Route& r, hipStream_t s) {
   const int64_t n = t * o;
   if (n == 0) return hipSuccess;
   r.note(NM_TAKEN_REDUCE);
   // y is 16-byte aligned (checked at the boundary); float4 rows need o and ldy % 4 == 0
   if (splits >= 1 && splits <= 16 && o % 4 == 0 && ldy % 4 == 0 && (reinterpret_cast<uintptr_t>(y) & 15) == 0 &&
-      (reinterpret_cast<uintptr_t>(part) & 15) == 0) {
+      (reinterpret_cast<uintptr_t>(part) & 15) == 0 && (reinterpret_cast<uintptr_t>(epi.col_shift) & 15) == 0) {
     k_reduce_parts4<<<dim3((unsigned)((n / 4 + RP4_THREADS - 1) / RP4_THREADS)), dim3(RP4_THREADS), 0, s>>>(
-        part, splits, w_scale, t, o, y, ldy, accumulate);
+        part, splits, epi, t, o, y, ldy, accumulate);
     return hipGetLastError();
   }
   k_reduce_parts<<<dim3((unsigned)((n + RP_OUT - 1) / RP_OUT)), dim3(RP_OUT * RP_LANES), 0, s>>>(
-      part, splits, w_scale, t, o, y, ldy, accumulate);
+      part, splits, epi, t, o, y, ldy, accumulate);
   return hipGetLastError();
 }
 

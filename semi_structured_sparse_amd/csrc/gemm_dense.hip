@@ -65,7 +65,7 @@ __device__ __forceinline__ uint32_t select32(const uint32_t (&d)[16], int n) {
 
 template <int BO, int BT, int WO, int WT, int PRO, int M, bool FP8>
 __global__ __launch_bounds__(64 * WO * WT) void k_gemm_dense(
-    const void* __restrict__ wptr, int64_t ldw, const float* __restrict__ wscale,
+    const void* __restrict__ wptr, int64_t ldw, Epi epi,
     const uint16_t* __restrict__ x, int64_t ldx, const uint32_t* __restrict__ xmask, int n,
     int64_t T, int64_t O, int64_t K, float* __restrict__ y, int64_t ldy, int accumulate,
     uint32_t* __restrict__ mask_out, int tiles_o, int tiles_t) {
@@ -244,10 +244,14 @@ __global__ __launch_bounds__(64 * WO * WT) void k_gemm_dense(
 #pragma unroll
   for (int i = 0; i < FI; ++i) {
     const int64_t ob = o0 + wo * SO + i * 16 + 4 * (lane >> 4);
-    float sc[4] = {1.f, 1.f, 1.f, 1.f};
-    if (wscale != nullptr) {
+    float sc[4] = {1.f, 1.f, 1.f, 1.f}, cs[4] = {0.f, 0.f, 0.f, 0.f};
+    if (epi.w_scale != nullptr) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sc[r] = (ob + r < O) ? wscale[ob + r] : 0.f;
+      for (int r = 0; r < 4; ++r) sc[r] = (ob + r < O) ? epi.w_scale[ob + r] : 0.f;
+    }
+    if (epi.col_shift != nullptr) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) cs[r] = (ob + r < O) ? epi.col_shift[ob + r] : 0.f;
     }
 #pragma unroll
     for (int j = 0; j < FJ; ++j) {
@@ -256,6 +260,12 @@ __global__ __launch_bounds__(64 * WO * WT) void k_gemm_dense(
       float v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) v[r] = acc[i][j][r] * sc[r];
+      if (epi.extra()) {
+        const float rs = epi.row_scale != nullptr ? epi.row_scale[t] : 1.f;
+        const float rb = epi.row_shift != nullptr ? epi.row_shift[t] : 1.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = v[r] * rs + rb * cs[r];
+      }
       float* yp = y + t * ldy + ob;
       if (vec_ok && ob + 4 <= O) {
         float4 cur = accumulate ? *reinterpret_cast<float4*>(yp) : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -284,7 +294,7 @@ hipError_t launch_cfg(const nml::GemmArgs& a, hipStream_t s) {
     attr_set = true;
   }
   kern<<<dim3((unsigned)ntiles), dim3(64 * WO * WT), lds, s>>>(
-      a.w, a.ldw, a.w_scale, a.x, a.ldx, a.x_mask, a.n, a.t, a.o, a.k, a.y, a.ldy, a.accumulate,
+      a.w, a.ldw, a.epi(), a.x, a.ldx, a.x_mask, a.n, a.t, a.o, a.k, a.y, a.ldy, a.accumulate,
       a.mask_out, tiles_o, tiles_t);
   return hipGetLastError();
 }

@@ -24,8 +24,7 @@
 //  * 8 waves (2 per SIMD), each owning a 64 (o) x 128 (t) block of 16x16 accumulators
 //    (v_mfma_f32_16x16x32_bf16); 4 waves of 128 x 128 (one per SIMD) were 15% slower.
 //    Workgroups are remapped so each XCD (own L2) runs a near-square block of tiles.
-//  * The few-token shapes (128-row tiles, split K) reuse the kernel with four stages as
-//    an option (three K-steps in flight, per-wave counted waits and a bare barrier).
+//  * The few-token shapes (128-row tiles, split K) reuse the kernel.
 // Requirements (checked by the dispatcher): K % 64 == 0, 16-byte aligned rows.  Rows
 // beyond T or O are read from the last valid row and their outputs are not stored.
 #include "nm_device.h"
@@ -37,10 +36,8 @@ using namespace nmk;
 using namespace nml;
 
 constexpr int BK = 64;                 // bf16 per K-step
-// s_waitcnt immediates: lgkmcnt(0) alone (vmcnt and expcnt at their maxima), and
-// vmcnt(n) alone (vmcnt split over bits 3:0 and 15:14)
+// s_waitcnt immediate: lgkmcnt(0) alone (vmcnt and expcnt at their maxima)
 constexpr int kWaitLgkm0 = 0xC07F;
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -65,12 +62,12 @@ __device__ __forceinline__ uint32_t keep_pair(uint32_t d, uint32_t bits, int q) 
   return d & ((hi & 0xFFFF0000u) | (lo & 0x0000FFFFu));
 }
 
-template <int BM, int BN, int WM, int WN, int PRO, bool W8, int NST, int KH>
+template <int BM, int BN, int WM, int WN, int PRO, bool W8, int KH>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
     const unsigned char* __restrict__ w, int64_t ldw, const uint16_t* __restrict__ x, int64_t ldx,
     const uint32_t* __restrict__ xmask, int64_t T, int64_t O, int64_t K, float* __restrict__ y,
     int64_t ldy, int accumulate, int tiles_m, int tiles_n, int64_t kslice, float* __restrict__ part,
-    const float* __restrict__ wscale, int group) {
+    Epi epi, int group) {
   constexpr int NW = WM * WN;
   constexpr int SM = BM / WM, SN = BN / WN;       // wave sub-tile (o x t)
   constexpr int FI = SM / 16, FJ = SN / 16;
@@ -87,13 +84,10 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
   static_assert(A_GROUPS % NW == 0 && B_GROUPS % NW == 0, "load groups per wave");
   constexpr int MASK_GROUPS = (PRO == PRO_MASK) ? BN / 32 : 0;   // 32 rows x 2 words per inst
 
-  // NST (2 or 4) stages as distinct arrays: every LDS access names its stage statically,
-  // so the compiler tracks the loads into each stage separately
-  static_assert(NST == 2 || (NST == 4 && PRO == PRO_NONE), "four stages take the plain prologue only");
-  constexpr int A_X = NST == 4 ? A_BYTES : 16, B_X = NST == 4 ? B_BYTES : 16;
+  // two stages as distinct arrays: every LDS access names its stage statically, so the
+  // compiler tracks the loads into each stage separately
   __shared__ __align__(16) unsigned char sA0[A_BYTES], sB0[B_BYTES], sM0[MASK_BYTES];
   __shared__ __align__(16) unsigned char sA1[A_BYTES], sB1[B_BYTES], sM1[MASK_BYTES];
-  __shared__ __align__(16) unsigned char sA2[A_X], sB2[B_X], sA3[A_X], sB3[B_X];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (LDS base goes to M0)
   const int wm = wave % WM, wn = wave / WM;
@@ -256,111 +250,31 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
     }
   };
 
-  if constexpr (NST == 2) {
-    issue_all(sA0, sB0, sM0, 0);
-    __builtin_amdgcn_s_waitcnt(0);   // the staged tiles have landed in LDS
+  issue_all(sA0, sB0, sM0, 0);
+  __builtin_amdgcn_s_waitcnt(0);   // the staged tiles have landed in LDS
+  __syncthreads();
+  // Two K-steps per trip (stage 0, then stage 1).  Each step first issues the loads of the
+  // step after it into the other stage (the first matrix step waits for every LDS read
+  // anyway, so no later LDS read waits behind them); the last step reloads step 0 into
+  // the idle stage instead (never read), so every step runs the same code.
+  for (int kt = 0; kt < nk; kt += 2) {
+    issue_all(sA1, sB1, sM1, kt + 1 < nk ? (int64_t)(kt + 1) * SBK : 0);
+    compute(sA0, sB0, sM0);
+    __builtin_amdgcn_s_waitcnt(0);   // next stage landed in LDS
     __syncthreads();
-    // Two K-steps per trip (stage 0, then stage 1).  Each step first issues the loads of
-    // the step after it into the other stage (the first matrix step waits for every LDS
-    // read anyway, so no later LDS read waits behind them); the last step reloads step 0
-    // into the idle stage instead (never read), so every step runs the same code.
-    for (int kt = 0; kt < nk; kt += 2) {
-      issue_all(sA1, sB1, sM1, kt + 1 < nk ? (int64_t)(kt + 1) * SBK : 0);
-      compute(sA0, sB0, sM0);
-      __builtin_amdgcn_s_waitcnt(0);   // next stage landed in LDS
+    if (kt + 1 < nk) {
+      issue_all(sA0, sB0, sM0, kt + 2 < nk ? (int64_t)(kt + 2) * SBK : 0);
+      compute(sA1, sB1, sM1);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (kt + 1 < nk) {
-        issue_all(sA0, sB0, sM0, kt + 2 < nk ? (int64_t)(kt + 2) * SBK : 0);
-        compute(sA1, sB1, sM1);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-      }
-    }
-  } else {
-    // Four stages, three K-steps in flight (few-token shapes are bound by how many bytes
-    // each CU keeps in flight).  Before step k each wave waits until its loads of step k
-    // have landed (the loads of the up to two later steps may still be in flight), then
-    // the barrier makes every wave's loads visible and retires the reads of step k - 1,
-    // whose stage then takes the loads of step k + 3.
-    constexpr int L = NGA + NGB;   // load instructions per wave per step
-    // The barrier is the bare instruction: __syncthreads() would also wait for every load
-    // still in flight.  LDS is coherent within the workgroup, so the per-wave wait before
-    // it is all the loads need; the empty asm statements keep the compiler from moving
-    // memory accesses across it.
-    auto wait_step = [&](int k) {
-      if (k + 2 < nk) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * L));
-      else if (k + 1 < nk) __builtin_amdgcn_s_waitcnt(vmcnt_imm(L));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-    };
-    auto wait_n = [&](int pending) {   // pending: load instructions allowed in flight
-      if (pending == 2 * L) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * L));
-      else if (pending == L) __builtin_amdgcn_s_waitcnt(vmcnt_imm(L));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-    };
-    if (nk % 4 == 0 && nk >= 8) {
-      // Steady trips issue unconditionally, so the compiler's count of loads in flight
-      // into each stage stays exact and it adds no waits of its own; the last trip
-      // (which issues only step nk - 1) is written out after the loop.
-      issue_all(sA0, sB0, sM0, 0);
-      issue_all(sA1, sB1, sM0, SBK);
-      issue_all(sA2, sB2, sM0, 2 * SBK);
-      int kt = 0;
-      for (; kt + 8 <= nk; kt += 4) {
-        wait_n(2 * L);
-        issue_all(sA3, sB3, sM0, (int64_t)(kt + 3) * SBK);
-        compute(sA0, sB0, sM0);
-        wait_n(2 * L);
-        issue_all(sA0, sB0, sM0, (int64_t)(kt + 4) * SBK);
-        compute(sA1, sB1, sM0);
-        wait_n(2 * L);
-        issue_all(sA1, sB1, sM0, (int64_t)(kt + 5) * SBK);
-        compute(sA2, sB2, sM0);
-        wait_n(2 * L);
-        issue_all(sA2, sB2, sM0, (int64_t)(kt + 6) * SBK);
-        compute(sA3, sB3, sM0);
-      }
-      wait_n(2 * L);
-      issue_all(sA3, sB3, sM0, (int64_t)(kt + 3) * SBK);
-      compute(sA0, sB0, sM0);
-      wait_n(2 * L);
-      compute(sA1, sB1, sM0);
-      wait_n(L);
-      compute(sA2, sB2, sM0);
-      wait_n(0);
-      compute(sA3, sB3, sM0);
-    } else {
-    // The first trip (kt = -4) only issues steps 0-2, through the same instructions as
-    // every later trip, so the compiler's tracking of which stage each load writes stays
-    // exact around the loop (a separate prologue makes it wait for all loads).
-    for (int kt = -4; kt < nk; kt += 4) {
-      if (kt >= 0) wait_step(kt);
-      if (kt + 3 >= 0 && kt + 3 < nk) issue_all(sA3, sB3, sM0, (int64_t)(kt + 3) * SBK);
-      if (kt >= 0) compute(sA0, sB0, sM0);
-      if (kt + 1 >= nk) break;
-      if (kt + 1 >= 0) wait_step(kt + 1);
-      if (kt + 4 < nk) issue_all(sA0, sB0, sM0, (int64_t)(kt + 4) * SBK);
-      if (kt + 1 >= 0) compute(sA1, sB1, sM0);
-      if (kt + 2 >= nk) break;
-      if (kt + 2 >= 0) wait_step(kt + 2);
-      if (kt + 5 < nk) issue_all(sA1, sB1, sM0, (int64_t)(kt + 5) * SBK);
-      if (kt + 2 >= 0) compute(sA2, sB2, sM0);
-      if (kt + 3 >= nk) break;
-      if (kt + 3 >= 0) wait_step(kt + 3);
-      if (kt + 6 < nk) issue_all(sA2, sB2, sM0, (int64_t)(kt + 6) * SBK);
-      if (kt + 3 >= 0) compute(sA3, sB3, sM0);
-    }
     }
   }
 
-  // epilogue: lane holds 4 consecutive o for one t in each 16x16 block (per-row weight
-  // scale applied to the finished sums; split-K partials are scaled by the reduction)
+  // epilogue: lane holds 4 consecutive o for one t in each 16x16 block (the Epi terms --
+  // per-row weight scale, per-token scale and shift term -- applied to the finished sums;
+  // split-K partials get them in the reduction)
   const bool vec_ok = ((ldy & 3) == 0);
+  const float* wscale = epi.w_scale;
 #pragma unroll
   for (int i = 0; i < FI; ++i) {
     const int64_t ob = o0 + wm * SM + i * 16 + 4 * fq;
@@ -370,6 +284,20 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
         const float sc = (ob + r < O) ? wscale[ob + r] : 0.f;
 #pragma unroll
         for (int j = 0; j < FJ; ++j) acc[i][j][r] *= sc;
+      }
+    }
+    if (epi.extra() && part == nullptr) {
+      float cs[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) cs[r] = (epi.col_shift != nullptr && ob + r < O) ? epi.col_shift[ob + r] : 0.f;
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) {
+        const int64_t t = t0 + wn * SN + j * 16 + fr;
+        const bool tin = t < T;
+        const float rs = (epi.row_scale != nullptr && tin) ? epi.row_scale[t] : 1.f;
+        const float rb = epi.row_shift != nullptr ? (tin ? epi.row_shift[t] : 0.f) : 1.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = acc[i][j][r] * rs + rb * cs[r];
       }
     }
 #pragma unroll
@@ -405,7 +333,7 @@ static int group_for(int tiles_m, int bm, int bn) {
   return g < tiles_m ? g : tiles_m;
 }
 
-template <int BM, int BN, int WM, int WN, int PRO, bool W8 = false, int NST = 2, int KH = 2>
+template <int BM, int BN, int WM, int WN, int PRO, bool W8 = false, int KH = 2>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s, int64_t splits, float* part) {
   const int tiles_m = (int)((a.o + BM - 1) / BM), tiles_n = (int)((a.t + BN - 1) / BN);
   const int64_t ntiles = (int64_t)tiles_m * tiles_n;
@@ -413,14 +341,14 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s, int64_t splits, float* p
   int64_t kslice = ((a.k / BK + splits - 1) / splits) * BK;
   splits = (a.k + kslice - 1) / kslice;
   if (ntiles * splits > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  auto kern = k_gemm_lds<BM, BN, WM, WN, PRO, W8, NST, KH>;
+  auto kern = k_gemm_lds<BM, BN, WM, WN, PRO, W8, KH>;
   kern<<<dim3((unsigned)(ntiles * splits)), dim3(64 * WM * WN), 0, s>>>(
       (const unsigned char*)a.w, a.ldw, a.x, a.ldx, a.x_mask, a.t, a.o, a.k, a.y, a.ldy, a.accumulate, tiles_m, tiles_n,
-      kslice, splits > 1 ? part : nullptr, a.w_scale, group_for(tiles_m, BM, BN));
+      kslice, splits > 1 ? part : nullptr, a.epi(), group_for(tiles_m, BM, BN));
   hipError_t e = hipGetLastError();
   a.route.note(NM_TAKEN_TILE_LDS | (PRO == PRO_MASK ? NM_TAKEN_MASK : 0u) | (splits > 1 ? NM_TAKEN_TILE_SPLIT : 0u));
   if (e != hipSuccess || splits == 1) return e;
-  return launch_reduce_parts(part, splits, a.w_scale, a.t, a.o, a.y, a.ldy, a.accumulate, a.route, s);
+  return launch_reduce_parts(part, splits, a.epi(), a.t, a.o, a.y, a.ldy, a.accumulate, a.route, s);
 }
 
 }  // namespace

@@ -390,7 +390,7 @@ hipError_t launch_sp_cfg(const SparseArgs& a, hipStream_t s, int64_t splits, flo
   hipError_t e = hipGetLastError();
   a.route.note(NM_TAKEN_TILE_LDS | NM_TAKEN_SPARSE_MMA | (splits > 1 ? NM_TAKEN_TILE_SPLIT : 0u));
   if (e != hipSuccess || splits == 1) return e;
-  return launch_reduce_parts(part, splits, nullptr, a.t, a.o, a.y, a.ldy, a.accumulate, a.route, s);
+  return launch_reduce_parts(part, splits, Epi{}, a.t, a.o, a.y, a.ldy, a.accumulate, a.route, s);
 }
 
 // Few-token split: 128-row tiles, as many workgroups as fit one per CU.

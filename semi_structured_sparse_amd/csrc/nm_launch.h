@@ -20,6 +20,27 @@ struct Route {
   }
 };
 
+// Output epilogue of the dense-operand products, applied to each finished sum:
+//   y[t][o] (=|+=) row_scale[t] * (w_scale[o] * acc) + beta_t * col_shift[o]
+// with beta_t = row_shift[t], or 1 when row_shift is null.  Null pointers drop their
+// factor or term.  Besides the fp8 weights' per-row scale it carries the activation
+// mitigations: the variance correction's per-token scale and the term that undoes a shift
+// of the activations (mu_t * (W . 1)_o, or (W . c)_o for a static shift).
+struct Epi {
+  const float* w_scale;
+  const float* row_scale;
+  const float* row_shift;
+  const float* col_shift;
+  __host__ __device__ bool extra() const { return row_scale != nullptr || col_shift != nullptr; }
+};
+
+__host__ __device__ inline float epi_apply(const Epi& e, float acc, int64_t t, int64_t o) {
+  float v = e.w_scale != nullptr ? acc * e.w_scale[o] : acc;
+  if (e.row_scale != nullptr) v *= e.row_scale[t];
+  if (e.col_shift != nullptr) v += (e.row_shift != nullptr ? e.row_shift[t] : 1.f) * e.col_shift[o];
+  return v;
+}
+
 // scored top-n (m in {4, 8, 16, 32}): score = fp32(|x|) * col_score[k] (use_x) or
 // col_score[k] alone; outputs S(X) and/or the bitmask
 hipError_t launch_select_scored(int m, const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, int n,
@@ -38,6 +59,14 @@ hipError_t launch_quant_lift(int ns, const uint16_t* x, int64_t t, int64_t k, in
                              int64_t ldq, float* xs, hipStream_t s);
 hipError_t launch_lift(int ns, const uint16_t* x, int64_t t, int64_t k, int64_t ldx, uint16_t* xo,
                        int64_t ldo, hipStream_t s);
+// shifted selection (dynamic: row mean; cshift: static per-channel shift; neither: none),
+// S(x~) into y, optional mask, mu_out [rows] (dynamic), alpha_out [rows] (var)
+hipError_t launch_select_pts(int m, const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, int n, int dynamic,
+                             const float* cshift, int var, uint16_t* y, int64_t ldy, uint32_t* mask, float* mu_out,
+                             float* alpha_out, hipStream_t s);
+// out[o] = fp32(s_o * sum_k dec(W[o][k]) * (shift ? shift[k] : 1)), fp64 sum
+hipError_t launch_weight_sums(const void* w, int64_t o, int64_t k, int64_t ldw, int fp8, const float* w_scale,
+                              const float* shift, float* out, hipStream_t s);
 
 // Activation-side prologue applied to X tiles inside the dense-MFMA GEMM.
 enum Prologue { PRO_NONE = 0, PRO_SELECT = 1, PRO_MASK = 2 };
@@ -57,6 +86,11 @@ struct GemmArgs {
   int accumulate;
   uint32_t* mask_out;     // PRO_SELECT: optional mask export
   Route route;
+  // optional epilogue terms (Epi): per-token scale, per-token shift coefficient, per-row term
+  const float* row_scale;
+  const float* row_shift;
+  const float* col_shift;
+  Epi epi() const { return Epi{w_scale, row_scale, row_shift, col_shift}; }
 };
 hipError_t launch_gemm_dense(const GemmArgs& a, hipStream_t s);
 // direct-to-LDS variant for large PRO_NONE / PRO_MASK problems with K % 64 == 0
@@ -163,6 +197,10 @@ struct FewArgs {
   int accumulate;
   int sel_m;              // > 0: seg[0].x is X itself; keep the m/2 largest of every m (see below)
   Route route;
+  const float* row_scale; // optional epilogue terms (Epi)
+  const float* row_shift;
+  const float* col_shift;
+  Epi epi() const { return Epi{w_scale, row_scale, row_shift, col_shift}; }
 };
 // One token, one plain dense segment (bf16 or fp8 W), m in {4, 8, 16, 32}: whether
 // launch_few applies the n = m/2 selection to the X row inside the product (the row
@@ -180,8 +218,8 @@ int64_t gather1_part_bytes(int64_t k, int64_t o, int m);
 hipError_t launch_gather1(int m, const uint16_t* x, int64_t k, int n, const uint16_t* wk, int64_t o, float* y,
                           int accumulate, uint32_t* mask_out, float* part, int64_t part_bytes, const Route& r,
                           hipStream_t s);
-// y[t][o] (=|+=) w_scale[o] * sum_{s < splits} part[s][t][o]   (part rows have stride o)
-hipError_t launch_reduce_parts(const float* part, int64_t splits, const float* w_scale, int64_t t, int64_t o,
+// y[t][o] (=|+=) epi(sum_{s < splits} part[s][t][o])   (part rows have stride o)
+hipError_t launch_reduce_parts(const float* part, int64_t splits, const Epi& epi, int64_t t, int64_t o,
                                float* y, int64_t ldy, int accumulate, const Route& r, hipStream_t s);
 // xo[t][j] = x[t][c0[j]] (j < k0), xo[t][off1 + j] = x[t][c1[j]] (j < k1); indices
 // clamped to [0, kx)

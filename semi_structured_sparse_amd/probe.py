@@ -22,7 +22,7 @@ def plib() -> ctypes.CDLL:
         L.nm_probe_sink_bytes.restype = _i64
         L.nm_probe_sink_bytes.argtypes = []
         L.nm_probe_read.restype = _int
-        L.nm_probe_read.argtypes = [_vp, _i64, _vp, _vp]
+        L.nm_probe_read.argtypes = [_vp, _i64, _vp, _int, _vp]
         L.nm_probe_mfma_flops.restype = _i64
         L.nm_probe_mfma_flops.argtypes = [_i64]
         L.nm_probe_mfma.restype = _int
@@ -40,8 +40,8 @@ def nm_probe_sink_bytes() -> int:
     return int(plib().nm_probe_sink_bytes())
 
 
-def nm_probe_read(buf, nbytes, sink, stream=None, *, check=True):
-    st = plib().nm_probe_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream))
+def nm_probe_read(buf, nbytes, sink, stream=None, *, mode=0, check=True):
+    st = plib().nm_probe_read(_ptr(buf), nbytes, _ptr(sink), mode, _stream(stream))
     if check:
         _check(st, "nm_probe_read")
     return st

@@ -306,6 +306,44 @@ def test_probe_helpers_host_side():
     assert P_.nm_probe_read(None, 24, None, check=False, stream=0) == S.NM_ESHAPE
     assert P_.nm_probe_read(None, 32, None, check=False, stream=0) == S.NM_EINVAL
     assert P_.nm_probe_read(16 * 1024 + 4, 32, 16 * 1024, check=False, stream=0) == S.NM_EALIGN
+    assert P_.nm_probe_read(16 * 1024, 32, 16 * 1024, mode=3, check=False, stream=0) == S.NM_EINVAL
+    assert P_.nm_probe_read(16 * 1024, 32, 16 * 1024, mode=2, check=False, stream=0) == S.NM_ESHAPE
     assert P_.nm_probe_mfma(-1, 16 * 1024, check=False, stream=0) == S.NM_ESHAPE
     assert P_.nm_probe_mfma(1, None, check=False, stream=0) == S.NM_EINVAL
     assert P_.nm_probe_mfma(1, 16 * 1024 + 8, check=False, stream=0) == S.NM_EALIGN
+
+
+def test_pts_validation():
+    f = lambda *a, **kw: S.nm_sparsify_pts(*a, check=False, stream=0, **kw)  # noqa: E731
+    d = dict(rows=4, k=16, ldx=16, ldy=16)
+    assert f(P, 8, 16, 8, Q, **d) == S.NM_EINVAL                                  # unknown mode bit
+    assert f(P, 8, 16, 3, Q, shift=Q, **d) == S.NM_EINVAL                         # two shifts
+    assert f(P, 8, 16, S.NM_PTS_STATIC, Q, **d) == S.NM_EINVAL                    # static needs the shift
+    assert f(P, 8, 16, S.NM_PTS_VAR, Q, **d) == S.NM_EINVAL                       # VAR needs row_scale
+    assert f(P, 8, 16, 0, None, **d) == S.NM_EINVAL                               # S(x~) required
+    assert f(P, 2, 4, 1, Q, rows=4, k=12, ldx=16, ldy=16) == S.NM_ESHAPE          # k % 8
+    assert f(P, 3, 6, 1, Q, rows=4, k=12, ldx=16, ldy=16) == S.NM_EUNSUPPORTED    # width 6
+    assert f(P, 8, 16, 1, Q, mask=MIS, **d) == S.NM_EALIGN
+    assert f(P, 8, 16, 1, Q, row_shift=MIS, **d) == S.NM_EALIGN
+    assert f(P, 8, 16, 1, Q, rows=0, k=16, ldx=16, ldy=16) == S.NM_OK             # empty
+    g = lambda *a, **kw: S.nm_weight_sums(*a, check=False, stream=0, **kw)  # noqa: E731
+    assert g(P, Q, 7, o=4, k=16, ldw=16) == S.NM_EINVAL                            # dtype
+    assert g(P, Q, S.NM_W_FP8E4M3, None, o=4, k=16, ldw=16) == S.NM_EINVAL         # fp8 needs scales
+    assert g(P, None, o=4, k=16, ldw=16) == S.NM_EINVAL                            # output
+    assert g(P, Q, o=4, k=16, ldw=8) == S.NM_ESHAPE
+    assert g(P, Q + 4, o=4, k=16, ldw=16) == S.NM_EALIGN
+    f2 = lambda a: S.nm_spmm(a, check=False, stream=0)  # noqa: E731
+    base = dict(t=4, o=8, k=16, n=8, m=16)
+    assert f2(spmm_args(pts=S.NM_PTS_DYNAMIC, **base)) == S.NM_EINVAL             # shift needs col_shift
+    assert f2(spmm_args(pts=S.NM_PTS_DYNAMIC, col_shift=Q, **base)) == S.NM_EINVAL  # needs the workspace
+    assert f2(spmm_args(pts=S.NM_PTS_VAR, col_shift=Q, **base)) == S.NM_EINVAL      # no shift, no col_shift
+    assert f2(spmm_args(pts=S.NM_PTS_VAR, row_scale=Q, **base)) == S.NM_EINVAL      # rows terms: masked only
+    assert f2(spmm_args(mode=S.NM_ACT_MASKED, pts=S.NM_PTS_VAR, **base)) == S.NM_EINVAL
+    assert f2(spmm_args(mode=S.NM_ACT_MASKED, row_shift=Q, **base)) == S.NM_EINVAL  # row_shift needs col_shift
+    assert f2(spmm_args(mode=S.NM_ACT_MASKED, row_scale=MIS, **base)) == S.NM_EALIGN
+    assert f2(spmm_args(mode=S.NM_W_COMPRESSED, w_meta=P, w_meta_fmt=S.NM_META_2BIT, row_scale=Q)) == \
+        S.NM_EUNSUPPORTED
+    assert f2(spmm_args(pts=S.NM_PTS_VAR, t=4, o=8, k=20, n=2, m=4, ldx=24, ldw=24)) == S.NM_ESHAPE  # k % 8
+    a = spmm_args(pts=S.NM_PTS_DYNAMIC | S.NM_PTS_VAR, col_shift=Q, t=64, o=4096, k=14336, ldx=14336,
+                  ldw=14336, ldy=4096, n=8, m=16)
+    assert S.nm_spmm_workspace_size(a) >= 64 * 14336 * 2 + 2 * 64 * 4

@@ -1380,24 +1380,44 @@ def test_measurement_probes():
     count (small integers, exact in fp32)."""
     print("probes", flush=True)
     import torch
+    from semi_structured_sparse_amd import probe as P_
     nth = 2048 * 256
     rng = np.random.default_rng(11)
     words = rng.integers(0, 2**32, size=(nth, 4), dtype=np.uint64).astype(np.uint32)
     buf = torch.from_numpy(words.view(np.int32)).cuda()
-    sink = torch.zeros((S.nm_probe_sink_bytes() // 4,), dtype=torch.int32, device="cuda")
-    S.nm_probe_read(buf, nth * 16, sink)
+    sink = torch.zeros((P_.nm_probe_sink_bytes() // 4,), dtype=torch.int32, device="cuda")
+    P_.nm_probe_read(buf, nth * 16, sink)
     sync()
     got = sink[:nth].cpu().numpy().view(np.uint32)
     assert (got == (words[:, 0] ^ words[:, 1] ^ words[:, 2] ^ words[:, 3])).all()
     outs = []
     for iters in (0, 3, 6):
-        fs = torch.full((S.nm_probe_sink_bytes() // 4,), float("nan"), dtype=torch.float32, device="cuda")
-        S.nm_probe_mfma(iters, fs)
+        fs = torch.full((P_.nm_probe_sink_bytes() // 4,), float("nan"), dtype=torch.float32, device="cuda")
+        P_.nm_probe_mfma(iters, fs)
         sync()
         outs.append(fs[:1024 * 256].cpu().numpy())
     assert (outs[0] == 0).all()
     assert np.isfinite(outs[1]).all() and (outs[1] > 0).all()
     assert (outs[2] == 2 * outs[1]).all()
+    # contiguous blocks: block b XORs its run; with 4096 elements per block of 256 threads,
+    # thread j of block b XORs elements b*4096 + j + 256*u, u < 16
+    nel = 2048 * 4096
+    w2 = rng.integers(0, 2**32, size=(nel, 4), dtype=np.uint64).astype(np.uint32)
+    buf2 = torch.from_numpy(w2.view(np.int32)).cuda()
+    sink2 = torch.zeros_like(sink)
+    P_.nm_probe_read(buf2, nel * 16, sink2, mode=1)
+    sync()
+    x = np.bitwise_xor.reduce(w2.reshape(2048, 16, 256, 4), axis=1)          # [block][thread][4]
+    ref = (x[..., 0] ^ x[..., 1] ^ x[..., 2] ^ x[..., 3]).reshape(-1)
+    assert (sink2[:2048 * 256].cpu().numpy().view(np.uint32) == ref).all()
+    # direct-to-LDS: 100 chunks of 16 KiB, one per wave; each lane reports the first dword
+    # of its 16 bytes of the chunk's first KiB
+    nch = 100
+    P_.nm_probe_read(buf2, nch * 16384, sink2, mode=2)
+    sync()
+    got = sink2[:nch * 64].cpu().numpy().view(np.uint32).reshape(nch, 64)
+    words = w2.reshape(-1)[:nch * 4096].reshape(nch, 16, 64, 4)                # chunk, KiB, lane, dword
+    assert (got == words[:, 0, :, 0]).all()
 
 
 @pytest.mark.parametrize("o", [200, 4096])
@@ -1571,3 +1591,240 @@ def test_one_token_graph_replays():
                 fn()
             sync()
         del g
+
+
+# ---------------------------------------------- activation mitigations (PTS, VAR) ---
+
+PTS_MODES = {"none": 0, "dyn": S.NM_PTS_DYNAMIC, "static": S.NM_PTS_STATIC, "var": S.NM_PTS_VAR,
+             "dyn+var": S.NM_PTS_DYNAMIC | S.NM_PTS_VAR, "static+var": S.NM_PTS_STATIC | S.NM_PTS_VAR}
+
+
+def pts_rows(rng, t, k):
+    """Student-t rows shifted off zero, with an all-zero row, a row of few distinct values
+    (ties after the shift) and a row spanning a wide dynamic range."""
+    x = synth.student_t_bf16(rng, (t, k), 4.0, 0.5)
+    xf = O.f32_from_bf16(x) + np.float32(0.3)
+    x = synth.bf16_bits_from_f32(xf.astype(np.float32))
+    if t >= 4:
+        x[1] = 0
+        x[2] = np.array([0x3F80, 0x4000, 0x3FC0, 0xBF80], np.uint16)[rng.integers(0, 4, size=k)]
+        x[3, ::7] = 0x6000          # 2^65 (with fp8 weights the raw codes, up to 448, are summed
+                                    # before the row scale: far larger values overflow fp32 there)
+        x[3, 3::11] = 0x0005        # subnormal
+    return x
+
+
+def run_select_pts(x, n, m, mode, c=None, ld=None):
+    t, k = x.shape
+    y = empty((t, k), np.uint16, fill=-1)
+    mask = empty((t, (k + 31) // 32), np.uint32, fill=-1)
+    mu = empty((t,), np.float32, fill=float("nan"))
+    al = empty((t,), np.float32, fill=float("nan"))
+    S.nm_sparsify_pts(dev(x, ld), n, m, mode, y, mask, dev(c) if c is not None else None, mu, al, k=k, ldx=ld or k)
+    sync()
+    return host(y, np.uint16), host(mask, np.uint32), host(mu, np.float32), host(al, np.float32)
+
+
+@pytest.mark.parametrize("mode", list(PTS_MODES))
+@pytest.mark.parametrize("n,m", [(2, 4), (1, 4), (4, 8), (8, 16), (5, 16), (16, 32), (31, 32)])
+@pytest.mark.parametrize("t,k,pad", [(37, 1056, 0), (5, 8, 8), (300, 4096, 24)])
+def test_select_pts_bitexact(mode, n, m, t, k, pad):
+    """Shifted selection: S(x~), mask and the row means bit for bit; the variance factor
+    within one fp32 rounding of the oracle's."""
+    if k % m:
+        pytest.skip("k not a multiple of m")
+    print(f"select pts {mode} {n}:{m} t={t} k={k}", flush=True)
+    rng = np.random.default_rng(t + k + m + n)
+    x = pts_rows(rng, t, k)
+    pts = PTS_MODES[mode]
+    c = (rng.standard_normal(k) * 0.1).astype(np.float32) if pts & S.NM_PTS_STATIC else None
+    y, mask, mu, al = run_select_pts(x, n, m, pts, c, ld=(k + pad) if pad else None)
+    s_ref, keep, mu_ref, al_ref = O.sparsify_pts(x, n, m, pts, c)
+    assert (y == s_ref).all(), "S(x~)"
+    assert (mask == O.pack_mask(keep)).all(), "mask"
+    if pts & S.NM_PTS_DYNAMIC:
+        assert (mu.view(np.uint32) == mu_ref.view(np.uint32)).all(), "row means"
+    if pts & S.NM_PTS_VAR:
+        assert np.all(np.abs(al - al_ref) <= 2.0 ** -23 * np.abs(al_ref)), "variance factors"
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+@pytest.mark.parametrize("shifted", [False, True])
+def test_weight_sums(kind, shifted):
+    rng = np.random.default_rng(41)
+    o, k = 300, 1056
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    c = (rng.standard_normal(k) * 0.1).astype(np.float32) if shifted else None
+    out = empty((o,), np.float32, fill=float("nan"))
+    if kind == "bf16":
+        S.nm_weight_sums(dev(w), out, shift=dev(c) if c is not None else None)
+        wv = O.bf16_to_f64(w)
+    else:
+        q, sc = synth.fp8_e4m3_quantize_rows(w)
+        S.nm_weight_sums(dev(q), out, S.NM_W_FP8E4M3, dev(sc), shift=dev(c) if c is not None else None)
+        wv = O.fp8_e4m3_to_f64(q) * sc[:, None].astype(np.float64)
+    sync()
+    got = host(out, np.float32).astype(np.float64)
+    ref = O.weight_sums(wv, c).astype(np.float64)
+    absum = np.abs(wv) @ (np.abs(c.astype(np.float64)) if c is not None else np.ones(k))
+    assert np.all(np.abs(got - ref) <= 2.0 ** -23 * np.abs(ref) + k * 2.0 ** -50 * absum)
+
+
+def check_pts(y, ref, s_bits, w_vals, alpha, beta, v, label=""):
+    """Tolerance of a mitigated product: relative Frobenius <= 1e-3 and
+    |err| <= 1e-2 * (alpha_t |S(x~)| |W|^T + |beta_t v_o|) + 1e-4."""
+    y = np.asarray(y, np.float64)
+    a = np.abs(O.bf16_to_f64(s_bits)) * (np.asarray(alpha, np.float64)[:, None] if alpha is not None else 1.0)
+    bound = a @ np.abs(np.asarray(w_vals, np.float64)).T
+    if v is not None:
+        bb = np.abs(np.asarray(beta, np.float64))[:, None] if beta is not None else 1.0
+        bound = bound + bb * np.abs(np.asarray(v, np.float64))[None, :]
+    err = np.abs(y - ref)
+    rel = np.linalg.norm(y - ref) / max(np.linalg.norm(ref), 1e-300)
+    assert rel <= 1e-3, f"{label}: relative Frobenius {rel:.3e}"
+    worst = (err - 1e-2 * bound - 1e-4).max() if err.size else -1
+    assert worst <= 0, f"{label}: per-element bound exceeded by {worst:.3e}"
+
+
+def run_spmm_pts(x, w, n, m, pts, c=None, w8=None, s8=None, route=0):
+    """One call: ACT_DYNAMIC with the mitigation; v from nm_weight_sums on the GPU."""
+    t, k = x.shape
+    o = (w if w is not None else w8).shape[0]
+    wt, dt, sd = (dev(w), S.NM_W_BF16, None) if w8 is None else (dev(w8), S.NM_W_FP8E4M3, dev(s8))
+    cd = dev(c) if c is not None else None
+    v = None
+    if pts & (S.NM_PTS_DYNAMIC | S.NM_PTS_STATIC):
+        v = empty((o,), np.float32)
+        S.nm_weight_sums(wt, v, dt, sd, shift=cd)
+    y = empty((t, o), np.float32, fill=float("nan"))
+    mask = empty((t, (k + 31) // 32), np.uint32, fill=-1)
+    a = mk_args(S.NM_ACT_DYNAMIC, t, o, k, dev(x), wt, y, n=n, m=m, w_dtype=dt, w_scale=sd, x_mask_out=mask,
+                pts=pts, pts_shift=cd, col_shift=v, route=route)
+    nb = S.nm_spmm_workspace_size(a)
+    ws = empty((max(nb, 16),), np.uint8)
+    a.workspace, a.workspace_bytes = ws.data_ptr(), nb
+    spmm_call(a)
+    sync()
+    return host(y, np.float32), host(mask, np.uint32)
+
+
+def pts_reference(x, w_bits, w_vals, n, m, pts, c, w8=None, s8=None):
+    """The oracle's mitigated layer (v from the oracle's weight sums)."""
+    v = O.weight_sums(w_vals, c) if pts & (S.NM_PTS_DYNAMIC | S.NM_PTS_STATIC) else None
+    s, keep, mu, alpha = O.sparsify_pts(x, n, m, pts, c)
+    if w8 is None:
+        acc = O.gemm(s, w_bits)
+    else:
+        acc = O.spmm_act_fp8(s, w8, s8, m, m)          # n = m: S(x~) is already selected
+    y = acc * (alpha.astype(np.float64)[:, None] if alpha is not None else 1.0)
+    beta = None
+    if v is not None:
+        beta = mu if pts & S.NM_PTS_DYNAMIC else np.ones(x.shape[0], np.float32)
+        y = y + beta.astype(np.float64)[:, None] * v.astype(np.float64)[None, :]
+    return y, s, keep, alpha, beta, v
+
+
+@pytest.mark.parametrize("mode", ["dyn", "static", "var", "dyn+var", "static+var"])
+@pytest.mark.parametrize("t,route", [(1, ()), (1, ("few_stream",)), (16, ()), (64, ("few_tile",)),
+                                     (64, ("few_stream",)), (128, ()), (300, ()), (600, ("tile_regs",)),
+                                     (600, ())])
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_spmm_pts_routes(mode, t, route, kind):
+    """The mitigated layer in one call on every route that can take it (few-token streaming
+    and split tile kernels with the reduction's epilogue, register and direct-to-LDS tile
+    kernels): mask bit for bit, product within tolerance of the oracle."""
+    print(f"spmm pts {mode} t={t} route={route} {kind}", flush=True)
+    rng = np.random.default_rng(t + len(mode))
+    o, k = 520, 2048
+    x = pts_rows(rng, t, k)
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    pts = PTS_MODES[mode]
+    c = (rng.standard_normal(k) * 0.1).astype(np.float32) if pts & S.NM_PTS_STATIC else None
+    if kind == "bf16":
+        q = sc = None
+        wv = O.bf16_to_f64(w)
+    else:
+        q, sc = synth.fp8_e4m3_quantize_rows(w)
+        wv = O.fp8_e4m3_to_f64(q) * sc[:, None].astype(np.float64)
+    for n, m in ((8, 16), (16, 32)):
+        y, mask = run_spmm_pts(x, w if q is None else None, n, m, pts, c, q, sc, route=S.route_bits(*route))
+        ref, s, keep, alpha, beta, v = pts_reference(x, w, wv, n, m, pts, c, q, sc)
+        assert (mask == O.pack_mask(keep)).all()
+        check_pts(y, ref, s, wv, alpha, beta, v, label=f"pts {mode} {n}:{m} t={t} {kind}")
+
+
+def test_spmm_pts_two_pass_equals_one_call():
+    """nm_sparsify_pts + ACT_MASKED with the caller's row terms gives the same bits as the
+    one-call form (same kernels, same order)."""
+    rng = np.random.default_rng(43)
+    for t in (16, 128, 700):
+        o, k = 264, 1024
+        x = pts_rows(rng, t, k)
+        w = synth.normal_bf16(rng, (o, k), 0.02)
+        pts = S.NM_PTS_DYNAMIC | S.NM_PTS_VAR
+        y1, _ = run_spmm_pts(x, w, 8, 16, pts)
+        wd_ = dev(w)
+        v = empty((o,), np.float32)
+        S.nm_weight_sums(wd_, v)
+        sx = empty((t, k), np.uint16)
+        mu = empty((t,), np.float32)
+        al = empty((t,), np.float32)
+        S.nm_sparsify_pts(dev(x), 8, 16, pts, sx, None, None, mu, al)
+        y2 = empty((t, o), np.float32, fill=float("nan"))
+        a = mk_args(S.NM_ACT_MASKED, t, o, k, sx, wd_, y2, n=8, m=16, col_shift=v, row_shift=mu, row_scale=al)
+        nb = S.nm_spmm_workspace_size(a)
+        ws = empty((max(nb, 16),), np.uint8)
+        a.workspace, a.workspace_bytes = ws.data_ptr(), nb
+        spmm_call(a)
+        sync()
+        assert np.array_equal(y1.view(np.uint32), host(y2, np.float32).view(np.uint32)), f"t={t}"
+
+
+@pytest.mark.parametrize("t", [128, 8192])
+def test_spmm_pts_full_size(t, down_full):
+    """The 8:16 down-projection (4096 x 14336) with D-PTS + VAR at 128 and 8192 tokens: the
+    mask of every row bit for bit, every output written, the oracle on one row of every
+    128-row band."""
+    print(f"pts full t={t}", flush=True)
+    x_all, w = down_full[0], down_full[1]
+    x = x_all[:t]
+    pts = S.NM_PTS_DYNAMIC | S.NM_PTS_VAR
+    y, mask = run_spmm_pts(x, w, 8, 16, pts)
+    assert np.isfinite(y).all(), "unwritten outputs"
+    s_all, keep_all, mu_all, al_all = O.sparsify_pts(x, 8, 16, pts)
+    assert (mask == O.pack_mask(keep_all)).all()
+    rows = band_rows(t, 128, seed=t)
+    wv = O.bf16_to_f64(w)
+    ref, s, keep, alpha, beta, v = pts_reference(x[rows], w, wv, 8, 16, pts, None)
+    check_pts(y[rows], ref, s, wv, alpha, beta, v, label=f"pts full t={t}")
+
+
+@pytest.mark.parametrize("t", [64, 8192])
+@pytest.mark.parametrize("name", ["qkv", "down"])
+def test_spmm_pts_layer_full_size(layer8b, name, t):
+    """Linears of the 8B-shaped layer (q|k|v 6144 x 4096, down 4096 x 14336) with D-PTS +
+    VAR, 16:32 and 8:16, bf16 and fp8 weights: masks bit for bit on every row, every output
+    written, the oracle on one row of every 256-row band (every 8 rows at 64 tokens)."""
+    print(f"pts layer {name} t={t}", flush=True)
+    parts = LAYER_GROUPS[name]
+    st = synth.TRANSFORMER_SHAPES[parts[0]][2]
+    x = layer8b["x"][st][:t]
+    w = np.concatenate([layer8b["w"][p] for p in parts], 0)
+    w8 = np.concatenate([layer8b["w8"][p] for p in parts], 0)
+    s8 = np.concatenate([layer8b["s8"][p] for p in parts], 0)
+    pts = S.NM_PTS_DYNAMIC | S.NM_PTS_VAR
+    rows = band_rows(t, 256 if t > 256 else 8, seed=t)
+    for n, m in ((16, 32), (8, 16)):
+        s_all, keep_all, _, _ = O.sparsify_pts(x, n, m, pts)
+        for kind in ("bf16", "fp8"):
+            if kind == "bf16":
+                y, mask = run_spmm_pts(x, w, n, m, pts)
+                wv = O.bf16_to_f64(w)
+                ref, s, keep, alpha, beta, v = pts_reference(x[rows], w, wv, n, m, pts, None)
+            else:
+                y, mask = run_spmm_pts(x, None, n, m, pts, None, w8, s8)
+                wv = O.fp8_e4m3_to_f64(w8) * s8[:, None].astype(np.float64)
+                ref, s, keep, alpha, beta, v = pts_reference(x[rows], w, wv, n, m, pts, None, w8, s8)
+            assert (mask == O.pack_mask(keep_all)).all()
+            assert np.isfinite(y).all(), "unwritten outputs"
+            check_pts(y[rows], ref, s, wv, alpha, beta, v, label=f"pts layer {name} t={t} {n}:{m} {kind}")
