@@ -61,7 +61,8 @@ typedef enum {
   NM_ESHAPE = 2,        /* inconsistent sizes: K % m, ld < K, negative or overflowing  */
   NM_EALIGN = 3,        /* pointer not 16-byte aligned or leading dimension % 8 != 0    */
   NM_EUNSUPPORTED = 4,  /* well-formed request outside what the kernels implement       */
-  NM_EHIP = 5           /* the HIP runtime reported an error when launching            */
+  NM_EHIP = 5,          /* the HIP runtime reported an error when launching            */
+  NM_ESCRATCH = 6       /* nm_spmm_noalloc: the call needs more scratch than it holds  */
 } nm_status;
 
 typedef enum { NM_META_U8 = 0, NM_META_2BIT = 1 } nm_meta;
@@ -382,6 +383,25 @@ typedef struct {
  * instructions over the selected (zero-filled) operand.
  */
 nm_status nm_spmm(const nm_spmm_args* args, void* stream);
+
+/*
+ * nm_spmm_noalloc -- nm_spmm for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation).  It computes
+ * exactly what nm_spmm computes (the same kernels and routes, bit-identical results) but
+ * takes its scratch from a buffer inside the library instead of args->workspace, which
+ * must be NULL with workspace_bytes 0 (NM_EINVAL otherwise):
+ *   - the buffer is NM_NOALLOC_SCRATCH_BYTES (64 MiB) of device memory per GPU, part of the
+ *     library's code object, held until the process ends; a call whose
+ *     nm_spmm_workspace_size exceeds it returns NM_ESCRATCH and enqueues nothing;
+ *   - the first call on a GPU looks up that GPU's copy of the buffer (no allocation);
+ *   - every call on a GPU shares that GPU's buffer: calls that may overlap in time on one
+ *     GPU (different streams, or different threads without ordering) race on it and must
+ *     be serialised by the caller; calls on one stream are ordered and safe;
+ *   - no route needs the buffer zeroed; it keeps whatever the last call left in it.
+ * Allocates nothing: no hipMalloc, hipFree or allocating library routine.
+ */
+#define NM_NOALLOC_SCRATCH_BYTES (64ll << 20)
+nm_status nm_spmm_noalloc(const nm_spmm_args* args, void* stream);
 
 /* Bytes of workspace for nm_spmm's preferred route with these arguments (0 if it uses
  * none).  Depends on mode, n, m, ns, t, o, k, w_dtype, w_scale, ldx, x_meta and the route

@@ -24,12 +24,14 @@ __all__ = [
     "nm_hybrid_gemm_workspace_size", "lowered_k", "NM_SPENSE_LOSS", "NM_SPENSE_TAIL", "nm_spense_glu_order",
     "nm_spense_glu_order_workspace_size", "nm_spense_pack", "nm_spense_pack_workspace_size",
     "nm_spense_outsplit_gemm", "nm_spense_outsplit_workspace_size", "nm_quant_lift", "NM_PTS_DYNAMIC",
-    "NM_PTS_STATIC", "NM_PTS_VAR", "nm_sparsify_pts", "nm_weight_sums",
+    "NM_PTS_STATIC", "NM_PTS_VAR", "nm_sparsify_pts", "nm_weight_sums", "NM_ESCRATCH", "nm_spmm_noalloc",
+    "NM_NOALLOC_SCRATCH_BYTES",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnmsparse.so")
 
-NM_OK, NM_EINVAL, NM_ESHAPE, NM_EALIGN, NM_EUNSUPPORTED, NM_EHIP = range(6)
+NM_OK, NM_EINVAL, NM_ESHAPE, NM_EALIGN, NM_EUNSUPPORTED, NM_EHIP, NM_ESCRATCH = range(7)
+NM_NOALLOC_SCRATCH_BYTES = 64 << 20
 NM_META_U8, NM_META_2BIT = 0, 1
 NM_W_BF16, NM_W_FP8E4M3 = 0, 1
 NM_SCORE_ACT_WEIGHTED, NM_SCORE_WEIGHT = 0, 1
@@ -119,6 +121,8 @@ def lib() -> ctypes.CDLL:
     L.nm_slide_lift.argtypes = [_vp, _i64, _i64, _i64, _int, _vp, _i64, _vp]
     L.nm_spmm.restype = _int
     L.nm_spmm.argtypes = [ctypes.POINTER(nm_spmm_args), _vp]
+    L.nm_spmm_noalloc.restype = _int
+    L.nm_spmm_noalloc.argtypes = [ctypes.POINTER(nm_spmm_args), _vp]
     L.nm_spmm_workspace_size.restype = _i64
     L.nm_spmm_workspace_size.argtypes = [ctypes.POINTER(nm_spmm_args)]
     L.nm_hybrid_pack.restype = _int
@@ -283,6 +287,14 @@ def nm_spmm(args: nm_spmm_args, stream=None, *, check=True):
     st = lib().nm_spmm(ctypes.byref(args), _stream(stream))
     if check:
         _check(st, "nm_spmm")
+    return st
+
+
+def nm_spmm_noalloc(args: nm_spmm_args, stream=None, *, check=True):
+    """nm_spmm with the library's own scratch (args.workspace must be NULL, bytes 0)."""
+    st = lib().nm_spmm_noalloc(ctypes.byref(args), _stream(stream))
+    if check:
+        _check(st, "nm_spmm_noalloc")
     return st
 
 

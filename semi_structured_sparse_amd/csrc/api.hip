@@ -3,6 +3,8 @@
 // caller's stream.  See include/nm.h for the contract of each call.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "nm.h"
 #include "nm_launch.h"
 
@@ -99,6 +101,37 @@ ActRoute act_route(int64_t t, const nml::Route& r) {
   if (r.has(NM_ROUTE_ACT_MASK)) return ROUTE_MASK;
   if (r.has(NM_ROUTE_ACT_SX)) return ROUTE_SX;
   return t >= 512 ? ROUTE_SX : ROUTE_FUSED;
+}
+
+// ----------------------------------------------------- no-allocation entry point ---
+// The scratch of nm_spmm_noalloc: a file-scope device array, one copy per GPU, held by the
+// library's code object until the process ends.  Host code never uses the array's name
+// as an address (on the host it is only a stand-in for the symbol): each GPU's address is
+// looked up once, with that GPU current, and kept below.
+
+
+__device__ __align__(256) unsigned char scratch[NM_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// This GPU's copy of the scratch array (null on failure, with the HIP error in *err).
+void* scratch_for_current_device(hipError_t* err) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *err = e != hipSuccess ? e : hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  *err = g_scratch_err[dev];
+  return g_scratch_ptr[dev];
 }
 
 int64_t mask_words(int64_t t, int64_t k) { return t * ((k + 31) / 32); }
@@ -352,6 +385,7 @@ const char* nm_status_str(nm_status s) {
     case NM_EALIGN: return "NM_EALIGN: misaligned pointer or leading dimension";
     case NM_EUNSUPPORTED: return "NM_EUNSUPPORTED: valid but not implemented";
     case NM_EHIP: return "NM_EHIP: HIP runtime error";
+    case NM_ESCRATCH: return "NM_ESCRATCH: needs more scratch than nm_spmm_noalloc holds";
   }
   return "NM_?: unknown status";
 }
@@ -565,8 +599,32 @@ int64_t nm_spmm_workspace_size(const nm_spmm_args* a) {
   return widen > 0 ? align256(stage) + widen : stage;
 }
 
-nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// nm_spmm's body.  noalloc: the call brings no workspace (NM_EINVAL if it does); after the
+// arguments are validated, the library's scratch buffer on the current GPU becomes the
+// workspace (NM_ESCRATCH if the preferred route needs more).
+nm_status spmm_impl(const nm_spmm_args* a, void* stream, bool noalloc) {
   if (a == nullptr) return NM_EINVAL;
+  if (noalloc && (a->workspace != nullptr || a->workspace_bytes != 0)) return NM_EINVAL;
+  nm_spmm_args local;
+  // called where validation is complete, before the first HIP call
+  auto bind_scratch = [&]() -> nm_status {
+    if (!noalloc) return NM_OK;
+    const int64_t need = nm_spmm_workspace_size(a);
+    if (need > NM_NOALLOC_SCRATCH_BYTES) return NM_ESCRATCH;
+    if (need <= 0) return NM_OK;
+    hipError_t e = hipSuccess;
+    void* p = scratch_for_current_device(&e);
+    if (p == nullptr) return NM_EHIP;
+    local = *a;
+    local.workspace = p;
+    local.workspace_bytes = need;
+    a = &local;
+    return NM_OK;
+  };
   const hipStream_t s = as_stream(stream);
   const int64_t T = a->t, O = a->o, K = a->k;
   if (T < 0 || O < 0 || K < 0) return NM_ESHAPE;
@@ -622,6 +680,7 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
       if (a->x_mask_out != nullptr && !aligned16(a->x_mask_out)) return NM_EALIGN;
       if (a->workspace != nullptr && !aligned16(a->workspace)) return NM_EALIGN;
       if (a->w_kmajor != nullptr && !aligned16(a->w_kmajor)) return NM_EALIGN;
+      if ((st = bind_scratch())) return st;
       if (T == 0 || O == 0) return NM_OK;
       if (K == 0) return a->accumulate ? NM_OK : zero_output(a->y, T, O, a->ldy, s);
 
@@ -788,10 +847,12 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
         if (a->w_scale == nullptr && O > 0) return NM_EINVAL;
         if (a->w_scale != nullptr && !aligned16(a->w_scale)) return NM_EALIGN;
         if (kc % 128 != 0) return NM_EUNSUPPORTED;
-          if (T == 0 || O == 0) return NM_OK;
+        if ((st = bind_scratch())) return st;
+        if (T == 0 || O == 0) return NM_OK;
         if (K == 0) return a->accumulate ? NM_OK : zero_output(a->y, T, O, a->ldy, s);
         return w8a8_product(a, kc, ns, s);
       }
+      if ((st = bind_scratch())) return st;
       if (T == 0 || O == 0) return NM_OK;
       if (K == 0) return a->accumulate ? NM_OK : zero_output(a->y, T, O, a->ldy, s);
       const nml::Route R = route_of(a, true);
@@ -837,6 +898,14 @@ nm_status nm_spmm(const nm_spmm_args* a, void* stream) {
       return NM_EINVAL;
   }
 }
+
+}  // namespace
+
+extern "C" {
+
+nm_status nm_spmm(const nm_spmm_args* a, void* stream) { return spmm_impl(a, stream, false); }
+
+nm_status nm_spmm_noalloc(const nm_spmm_args* a, void* stream) { return spmm_impl(a, stream, true); }
 
 
 // ------------------------------------------------------------- Spense GLU layout ---

@@ -76,8 +76,9 @@ def test_route_fields_change_routes_not_results_host_side():
 
 
 def test_status_strings_and_version():
-    for code in range(6):
+    for code in range(7):
         assert S.nm_status_str(code).startswith("NM_")
+    assert S.nm_status_str(S.NM_ESCRATCH).startswith("NM_ESCRATCH")
     assert S.nm_version() >= 100
 
 
@@ -347,3 +348,15 @@ def test_pts_validation():
     a = spmm_args(pts=S.NM_PTS_DYNAMIC | S.NM_PTS_VAR, col_shift=Q, t=64, o=4096, k=14336, ldx=14336,
                   ldw=14336, ldy=4096, n=8, m=16)
     assert S.nm_spmm_workspace_size(a) >= 64 * 14336 * 2 + 2 * 64 * 4
+
+
+def test_noalloc_validation():
+    """The no-allocation entry point rejects a caller workspace and, before any HIP call, a
+    call whose scratch need exceeds its buffer."""
+    f = lambda a: S.nm_spmm_noalloc(a, check=False, stream=0)  # noqa: E731
+    assert S.lib().nm_spmm_noalloc(None, None) == S.NM_EINVAL
+    assert f(spmm_args(workspace=Q, workspace_bytes=1024)) == S.NM_EINVAL
+    big = spmm_args(t=8192, o=4096, k=14336, ldx=14336, ldw=14336, ldy=4096, n=8, m=16)
+    assert S.nm_spmm_workspace_size(big) > S.NM_NOALLOC_SCRATCH_BYTES
+    assert f(big) == S.NM_ESCRATCH
+    assert f(spmm_args(accumulate=2)) == S.NM_EINVAL          # the usual validation still applies
