@@ -209,7 +209,8 @@ def measure_rows(torch, S, synth, np, only=None):
     only: row-key prefixes to measure (None: all), e.g. ["c3.", "c4.32"] for a profiler run."""
 
     def want(key):
-        return only is None or any(key.startswith(p) for p in only)
+        """A row key (or the prefix of a section of rows) that the selection asks for."""
+        return only is None or any(key.startswith(p) or p.startswith(key) for p in only)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(
         np.int16 if a.dtype == np.uint16 else (np.int32 if a.dtype == np.int32 else np.uint8))).cuda()
     f32 = lambda *sh: torch.empty(sh, dtype=torch.float32, device="cuda")
