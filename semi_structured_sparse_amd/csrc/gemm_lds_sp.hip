@@ -51,13 +51,99 @@ __device__ __forceinline__ void g2lds4(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
 }
 
-// s_waitcnt immediate for lgkmcnt(0) alone (vmcnt and expcnt at their maxima)
+// s_waitcnt immediates: lgkmcnt(0) alone (vmcnt and expcnt at their maxima), and vmcnt(n)
+// alone (vmcnt split over bits 3:0 and 15:14; expcnt and lgkmcnt at their maxima)
 constexpr int kWaitLgkm0 = 0xC07F;
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// The K-loop over n steps through NST LDS stages (distinct static arrays, named statically
+// at every access so the compiler tracks the direct-to-LDS loads into each one).
+//   NST = 2: each step issues the next step's loads, multiplies, then waits for all loads
+//            and synchronises (one step in flight).
+//   NST = 3: two steps in flight.  Before step s a wave waits until its own loads of step s
+//            have landed -- at most L requests (the loads of step s + 1, issued after them)
+//            may remain, L being the fewest direct-to-LDS requests any wave issues per step,
+//            so the wait is never short -- then the bare barrier makes every wave's loads of
+//            step s visible and retires every read of step s - 1, whose stage then takes the
+//            loads of step s + 2.  The wait is written at the end of step s - 1.  (__syncthreads() would also wait for the loads in flight;
+//            the empty asm statements keep the compiler from moving memory accesses across
+//            the barrier.)
+template <int NST, int L, typename Issue, typename Compute>
+__device__ __forceinline__ void k_loop(int n, unsigned char* a0, unsigned char* b0, unsigned char* a1,
+                                       unsigned char* b1, unsigned char* a2, unsigned char* b2, Issue&& issue,
+                                       Compute&& compute) {
+  if constexpr (NST == 2) {
+    issue(a0, b0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // two steps per trip (stage 0, then stage 1); the next step's loads go out first
+    for (int s = 0; s < n; s += 2) {
+      if (s + 1 < n) issue(a1, b1, s + 1);
+      compute(a0, b0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (s + 1 < n) {
+        if (s + 2 < n) issue(a0, b0, s + 2);
+        compute(a1, b1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+    }
+  } else {
+    static_assert(NST == 3 && L >= 1, "three stages");
+    // Step s: [issue step s + 2 into the stage step s - 1 used], multiply step s, wait for
+    // this wave's loads of step s + 1, barrier.  The issue and the wait are taken on the
+    // same branch (the multiply is written out on both), so on every path the compiler
+    // sees the wait that covers the stage read next and adds none of its own.
+    auto bar = [] {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    auto step = [&](bool more, unsigned char* na, unsigned char* nb, int ns, const unsigned char* a,
+                    const unsigned char* b) {
+      if (more) {
+        issue(na, nb, ns);
+        compute(a, b);
+        __builtin_amdgcn_s_waitcnt(vm_wait(L));
+      } else {
+        compute(a, b);
+        __builtin_amdgcn_s_waitcnt(vm_wait(0));
+      }
+      bar();
+    };
+    issue(a0, b0, 0);
+    if (n == 1) {   // a single step, kept off the loop's path
+      __builtin_amdgcn_s_waitcnt(vm_wait(0));
+      bar();
+      compute(a0, b0);
+      bar();
+      return;
+    }
+    issue(a1, b1, 1);
+    __builtin_amdgcn_s_waitcnt(vm_wait(L));
+    bar();
+    // Steady state: three steps per trip (stages 0, 1, 2), each issuing two steps ahead,
+    // with no branch inside the trip.  The barrier ending a step also retires every read of
+    // it, so the last one leaves the stages free for the next phase.
+    int s = 0;
+    for (; s + 4 < n; s += 3) {
+      step(true, a2, b2, s + 2, a0, b0);
+      step(true, a0, b0, s + 3, a1, b1);
+      step(true, a1, b1, s + 4, a2, b2);
+    }
+    // the last two to four steps (steps s and s + 1 are in flight in stages 0 and 1)
+    step(s + 2 < n, a2, b2, s + 2, a0, b0);
+    step(s + 3 < n, a0, b0, s + 3, a1, b1);
+    if (s + 2 < n) step(false, a0, b0, 0, a2, b2);
+    if (s + 3 < n) step(false, a0, b0, 0, a0, b0);
+  }
+}
 
 __device__ __forceinline__ int swz8(int r, int c) { return c ^ ((r >> 1) & 7); }   // 8 pieces per row
 __device__ __forceinline__ int swz4(int r, int c) { return c ^ ((r >> 2) & 3); }   // 4 pieces per row
 
-template <int BM, int BN, int WM, int WN, bool MB, bool F8>
+template <int BM, int BN, int WM, int WN, bool MB, bool F8, int NST = 2>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
     const uint16_t* __restrict__ wv, const uint8_t* __restrict__ wm, int64_t kc, const uint16_t* __restrict__ x,
     int64_t ldx, const uint16_t* __restrict__ wd, int64_t ldwd, int64_t kd, int64_t dbase, int64_t T, int64_t O,
@@ -78,8 +164,11 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
   constexpr int ND = BM / 8 / NW;            // dense weight load groups (8 rows) per wave
   static_assert(NV >= 1 && NX >= 1 && ND >= 1 && BM % (16 * NW) == 0 && BN % (8 * NW) == 0,
                 "load groups per wave");
+  static_assert(NST == 2 || NST == 3, "two or three stages");
+  constexpr int A3 = NST == 3 ? A_BYTES : 16, B3 = NST == 3 ? B_BYTES : 16;
   __shared__ __align__(16) unsigned char sA0[A_BYTES], sB0[B_BYTES];
   __shared__ __align__(16) unsigned char sA1[A_BYTES], sB1[B_BYTES];
+  __shared__ __align__(16) unsigned char sA2[A3], sB2[B3];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wmi = wave % WM, wni = wave / WM;
@@ -204,22 +293,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
         bcur = bnxt;
       }
     };
-    issue(sA0, sB0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    // two steps per trip (stage 0, then stage 1); the next step's loads go out first
-    for (int s = 0; s < nks; s += 2) {
-      if (s + 1 < nks) issue(sA1, sB1, s + 1);
-      compute(sA0, sB0);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (s + 1 < nks) {
-        if (s + 2 < nks) issue(sA0, sB0, s + 2);
-        compute(sA1, sB1);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-      }
-    }
+    // direct-to-LDS requests per wave per sparse step: values and X (positions: some waves)
+    k_loop<NST, NV + NX>(nks, sA0, sB0, sA1, sB1, sA2, sB2, issue, compute);
   }
 
   // ------------------------------------------------------------ dense phase ---
@@ -271,21 +346,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
         }
       }
     };
-    issue(sA0, sB0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int s = 0; s < nkd; s += 2) {
-      if (s + 1 < nkd) issue(sA1, sB1, s + 1);
-      compute(sA0, sB0);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (s + 1 < nkd) {
-        if (s + 2 < nkd) issue(sA0, sB0, s + 2);
-        compute(sA1, sB1);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-      }
-    }
+    k_loop<NST, ND + NX>(nkd, sA0, sB0, sA1, sB1, sA2, sB2, issue, compute);
   }
 
   // epilogue: lane holds 4 consecutive o for one t in each 16x16 block; fp8 sums take
@@ -362,7 +423,7 @@ __global__ __launch_bounds__(256) void k_meta_block(const uint8_t* __restrict__ 
   }
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int NST = 2>
 hipError_t launch_sp_cfg(const SparseArgs& a, hipStream_t s, int64_t splits, float* part) {
   const int tiles_m = (int)((a.o + BM - 1) / BM), tiles_n = (int)((a.t + BN - 1) / BN);
   const int64_t ntiles = (int64_t)tiles_m * tiles_n;
@@ -376,7 +437,7 @@ hipError_t launch_sp_cfg(const SparseArgs& a, hipStream_t s, int64_t splits, flo
   const int steps = (int)(per > 0 ? per : 1), group = group_for(tiles_m, BM, BN);
   float* pp = splits > 1 ? part : nullptr;
 #define NM_SP_LAUNCH(MBV, F8V, META)                                                                    \
-  k_gemm_lds_sp<BM, BN, WM, WN, MBV, F8V><<<grid, block, 0, s>>>(                                       \
+  k_gemm_lds_sp<BM, BN, WM, WN, MBV, F8V, NST><<<grid, block, 0, s>>>(                                  \
       a.w_vals, META, a.kc, a.x, a.ldx, a.wd, a.ldwd, a.kd, a.dbase, a.t, a.o, a.y, a.ldy, a.accumulate, \
       tiles_m, tiles_n, steps, pp, group, a.x_scale, a.w_scale)
   if (a.f8) {
@@ -444,8 +505,9 @@ int64_t gemm_lds_sp_small_part_bytes(const SparseArgs& a) {
 hipError_t launch_gemm_lds_sp_small(const SparseArgs& a, float* part, int64_t part_bytes, hipStream_t s) {
   int64_t splits = sp_small_splits(a);
   if (part == nullptr || part_bytes < splits * a.t * a.o * 4) splits = 1;
-  if (a.t <= 64) return launch_sp_cfg<128, 64, 4, 2>(a, s, splits, part);
-  return launch_sp_cfg<128, 128, 4, 2>(a, s, splits, part);
+  // three LDS stages (72 / 96 KiB): two K-steps in flight
+  if (a.t <= 64) return launch_sp_cfg<128, 64, 4, 2, 3>(a, s, splits, part);
+  return launch_sp_cfg<128, 128, 4, 2, 3>(a, s, splits, part);
 }
 
 }  // namespace nml
