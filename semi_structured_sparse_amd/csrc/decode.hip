@@ -355,8 +355,6 @@ __device__ __forceinline__ void g2lds4(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
 }
 __device__ __forceinline__ int dswz(int r) { return (r >> 1) & 7; }
-// s_waitcnt immediate: vmcnt(n) alone (bits 3:0 and 15:14; expcnt and lgkmcnt at their maxima)
-constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <int TB> struct Dma {
   static constexpr int WPB = TB == 1 ? 16 : 8;   // waves per workgroup (LDS budget)

@@ -51,10 +51,6 @@ __device__ __forceinline__ void g2lds4(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 4, 0, 0);
 }
 
-// s_waitcnt immediates: lgkmcnt(0) alone (vmcnt and expcnt at their maxima), and vmcnt(n)
-// alone (vmcnt split over bits 3:0 and 15:14; expcnt and lgkmcnt at their maxima)
-constexpr int kWaitLgkm0 = 0xC07F;
-constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // The K-loop over n steps through NST LDS stages (distinct static arrays, named statically
 // at every access so the compiler tracks the direct-to-LDS loads into each one).

@@ -14,6 +14,11 @@ typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+// 11:8): lgkmcnt(0) alone, and vmcnt(n) alone, the other counters at their maxima
+constexpr int kWaitLgkm0 = 0xC07F;
+constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 // ---------------------------------------------------------------------------------
 // Magnitude top-n of one group of M bf16 values.
 //

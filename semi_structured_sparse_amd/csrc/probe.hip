@@ -60,9 +60,6 @@ __global__ __launch_bounds__(kReadThreads) void k_probe_read_block(const u32x4* 
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// s_waitcnt immediate for vmcnt(n) alone (bits 3:0 and 15:14; expcnt, lgkmcnt at their maxima)
-constexpr int vm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
 // mode 2: wave w of block b streams its contiguous run of 16 KiB chunks into a 16 KiB LDS
 // slot with direct-to-LDS loads (16 instructions of 1 KiB per chunk); a wave waits only
 // when 32 of its loads are in flight, and for all of them at the end.
