@@ -18,7 +18,8 @@
 //    of the next step into the other stage, then multiplies; one barrier per K-step.
 //    Fragments are read one matrix step ahead.  Measured on gfx950 (8192 x 14336 x 4096):
 //    without the per-step loads the same loop runs at 2.1 PFLOP/s; 32-wide K-steps with
-//    four stages (three steps in flight) were 13% slower than this (twice the barriers).
+//    four stages (three steps in flight, branch-free steady state, no compiler-added
+//    drains) were 13% slower than this (twice the barriers): 890 against 789 us.
 //  * The keep mask travels with the X tile (two 32-bit words per row per K-step) and is
 //    applied to each 8-element X fragment right after its LDS read.
 //  * 8 waves (2 per SIMD), each owning a 64 (o) x 128 (t) block of 16x16 accumulators
