@@ -552,6 +552,8 @@ def main():
                     help="comma-separated row-key prefixes: measure only those rows and print them (no headline)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of 1 GiB five times (counter calibration)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="only time the vendor bf16 GEMM (torch.mm) on the headline shape, fp32 and bf16 output")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on exactly one GPU; --gpus N > 1 is not supported", file=sys.stderr)
@@ -572,6 +574,21 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "launches": 5}))
+        return
+    if args.vendor_gemm:
+        # context for the product kernel: the library GEMM on the same operands (dense bf16,
+        # no selection), timed like the headline product after the clock has settled
+        d = synth.mlp_down_8of16(t_max=args.tokens)
+        xb = torch.from_numpy(d["x"].view(np.int16)).cuda().view(torch.bfloat16)
+        wt = torch.from_numpy(d["w"].view(np.int16)).cuda().view(torch.bfloat16).t()
+        f = 2.0 * xb.shape[0] * wt.shape[1] * xb.shape[1]
+        res = {}
+        for name, fn in (("fp32_out", lambda: torch.mm(xb, wt, out_dtype=torch.float32)),
+                         ("bf16_out", lambda: torch.mm(xb, wt))):
+            us = gpu_time_us(torch, fn, False, settle_ms=60.0)
+            res[name] = {"us": round(us, 1), "TFLOP/s": round(f / us / 1e6, 1)}
+            log(f"vendor GEMM {name}: {us:.1f} us, {f / us / 1e6:.1f} TFLOP/s")
+        print(json.dumps({"vendor_gemm": res, "tokens": int(xb.shape[0])}), flush=True)
         return
     S.lib()
     if args.rows_only is not None:
