@@ -351,27 +351,20 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
         for (int r = 0; r < 4; ++r) acc[i][j][r] = acc[i][j][r] * rs + rb * cs[r];
       }
     }
+    if (part != nullptr) {
 #pragma unroll
-    for (int j = 0; j < FJ; ++j) {
-      const int64_t t = t0 + wn * SN + j * 16 + fr;
-      if (t >= T) continue;
-      float* yp = y + t * ldy + ob;
-      if (part != nullptr) {
+      for (int j = 0; j < FJ; ++j) {
+        const int64_t t = t0 + wn * SN + j * 16 + fr;
+        if (t >= T) continue;
         float* pp = part + ((int64_t)kpart * T + t) * O + ob;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (ob + r < O) pp[r] = acc[i][j][r];
-      } else if (vec_ok && ob + 4 <= O) {
-        float4 cur = accumulate ? *reinterpret_cast<float4*>(yp) : make_float4(0.f, 0.f, 0.f, 0.f);
-        *reinterpret_cast<float4*>(yp) =
-            make_float4(cur.x + acc[i][j][0], cur.y + acc[i][j][1], cur.z + acc[i][j][2], cur.w + acc[i][j][3]);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (ob + r < O) yp[r] = accumulate ? yp[r] + acc[i][j][r] : acc[i][j][r];
       }
     }
   }
+  if (part != nullptr) return;
+  store_blocks<FI, FJ>(acc, y, ldy, T, O, o0 + wm * SM, t0 + wn * SN, fr, fq, vec_ok && o0 + BM <= O, accumulate);
 }
 
 // o-tiles per band of the XCD-aware tile order.  An XCD runs 32 tiles at a time (one per

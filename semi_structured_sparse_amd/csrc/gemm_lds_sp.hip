@@ -348,40 +348,39 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
   // epilogue: lane holds 4 consecutive o for one t in each 16x16 block; fp8 sums take
   // the token scale, then the row scale: y = (sum * s_t) * s_o
   const bool vec_ok = ((ldy & 3) == 0);
+  if constexpr (F8) {
 #pragma unroll
-  for (int i = 0; i < FI; ++i) {
-    const int64_t ob = o0 + wmi * SM + i * 16 + 4 * fg;
-    float wsr[4] = {1.f, 1.f, 1.f, 1.f};
-    if constexpr (F8) {
+    for (int i = 0; i < FI; ++i) {
+      const int64_t ob = o0 + wmi * SM + i * 16 + 4 * fg;
+      float wsr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) wsr[r] = wscale[ob + r < O ? ob + r : O - 1];
-    }
 #pragma unroll
-    for (int j = 0; j < FJ; ++j) {
-      const int64_t t = t0 + wni * SN + j * 16 + fr;
-      if (t >= T) continue;
-      if constexpr (F8) {
-        const float st = xscale[t];
+      for (int j = 0; j < FJ; ++j) {
+        const int64_t t = t0 + wni * SN + j * 16 + fr;
+        const float st = xscale[t < T ? t : T - 1];
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[i][j][r] = (acc[i][j][r] * st) * wsr[r];
       }
-      float* yp = y + t * ldy + ob;
-      if (part != nullptr) {
+    }
+  }
+  if (part != nullptr) {
+#pragma unroll
+    for (int i = 0; i < FI; ++i) {
+      const int64_t ob = o0 + wmi * SM + i * 16 + 4 * fg;
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) {
+        const int64_t t = t0 + wni * SN + j * 16 + fr;
+        if (t >= T) continue;
         float* pp = part + ((int64_t)kpart * T + t) * O + ob;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (ob + r < O) pp[r] = acc[i][j][r];
-      } else if (vec_ok && ob + 4 <= O) {
-        float4 cur = accumulate ? *reinterpret_cast<float4*>(yp) : make_float4(0.f, 0.f, 0.f, 0.f);
-        *reinterpret_cast<float4*>(yp) =
-            make_float4(cur.x + acc[i][j][0], cur.y + acc[i][j][1], cur.z + acc[i][j][2], cur.w + acc[i][j][3]);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (ob + r < O) yp[r] = accumulate ? yp[r] + acc[i][j][r] : acc[i][j][r];
       }
     }
+    return;
   }
+  store_blocks<FI, FJ>(acc, y, ldy, T, O, o0 + wmi * SM, t0 + wni * SN, fr, fg, vec_ok && o0 + BM <= O, accumulate);
 }
 
 // o-tiles per band of the XCD-aware tile order: an XCD runs 32 tiles at a time, and a

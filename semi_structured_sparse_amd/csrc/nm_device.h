@@ -201,4 +201,62 @@ __device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t q, uint32_t& lo, uint32
   hi = __builtin_amdgcn_perm(__float_as_uint(b.y), __float_as_uint(b.x), 0x07060302u);
 }
 
+// Final fp32 stores of a wave's FI x FJ blocks of 16 x 16 results, v_mfma_f32_16x16 layout:
+// block (i, j) holds, in lane (fr, fq) = (lane & 15, lane >> 4), outputs o = ob0 + 16 i + 4 fq
+// + [0, 4) of token row t = tb0 + 16 j + fr.  y[t][o] (=|+=) the block values; rows t >= T
+// are skipped.  With `whole` (every o of the wave inside O, ldy % 4 == 0, 16-byte aligned y)
+// and FI even, a block pair (i, i + 1) goes out as two stores of whole 128-byte row pieces:
+// lanes fr and fr ^ 8 swap one block, so the first store writes rows 0-7 (lanes fr < 8 block
+// i, lanes fr >= 8 block i + 1 of row fr - 8) and the second rows 8-15.  A store per block
+// would write 64-byte halves of 16 rows, which the memory system wrote back as separate
+// pieces (1.46x the output bytes, measured).  Otherwise element by element, bounds-checked.
+template <int FI, int FJ>
+__device__ __forceinline__ void store_blocks(const f32x4 (&acc)[FI][FJ], float* __restrict__ y, int64_t ldy,
+                                             int64_t T, int64_t O, int64_t ob0, int64_t tb0, int fr, int fq,
+                                             bool whole, int accumulate) {
+  if (FI % 2 == 0 && whole) {
+    const bool up = fr < 8;
+#pragma unroll
+    for (int i = 0; i + 1 < FI; i += 2) {
+      const int64_t ob = ob0 + i * 16 + 4 * fq + (up ? 0 : 16);
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) {
+        const int64_t tb = tb0 + j * 16 + (fr & 7);
+        const f32x4 lo = acc[i][j], hi = acc[i + 1][j];
+        const f32x4 send = up ? hi : lo;
+        f32x4 got;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) got[r] = __shfl_xor(send[r], 8);
+        const f32x4 v0 = up ? lo : got, v1 = up ? got : hi;
+        if (tb < T) {
+          float4* yp = reinterpret_cast<float4*>(y + tb * ldy + ob);
+          const float4 cur = accumulate ? *yp : make_float4(0.f, 0.f, 0.f, 0.f);
+          *yp = make_float4(cur.x + v0[0], cur.y + v0[1], cur.z + v0[2], cur.w + v0[3]);
+        }
+        if (tb + 8 < T) {
+          float4* yp = reinterpret_cast<float4*>(y + (tb + 8) * ldy + ob);
+          const float4 cur = accumulate ? *yp : make_float4(0.f, 0.f, 0.f, 0.f);
+          *yp = make_float4(cur.x + v1[0], cur.y + v1[1], cur.z + v1[2], cur.w + v1[3]);
+        }
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < FI; ++i) {
+    const int64_t ob = ob0 + i * 16 + 4 * fq;
+#pragma unroll
+    for (int j = 0; j < FJ; ++j) {
+      const int64_t t = tb0 + j * 16 + fr;
+      if (t >= T) continue;
+      float* yp = y + t * ldy + ob;
+      // highest o first: a store sequence the compiler does not merge with the whole-line
+      // path's last float4 store
+#pragma unroll
+      for (int r = 3; r >= 0; --r)
+        if (ob + r < O) yp[r] = accumulate ? yp[r] + acc[i][j][r] : acc[i][j][r];
+    }
+  }
+}
+
 }  // namespace nmk
