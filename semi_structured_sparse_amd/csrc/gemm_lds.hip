@@ -83,13 +83,15 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
   static_assert(A_GROUPS % NW == 0 && B_GROUPS % NW == 0, "load groups per wave");
   constexpr int MASK_GROUPS = (PRO == PRO_MASK) ? BN / 32 : 0;   // 32 rows x 2 words per inst
 
-  // two (or three) stages as distinct arrays: every LDS access names its stage statically,
-  // so the compiler tracks the loads into each stage separately
-  static_assert(NST == 2 || (NST == 3 && PRO == PRO_NONE), "three stages: plain prologue");
-  constexpr int A3 = NST == 3 ? A_BYTES : 16, B3 = NST == 3 ? B_BYTES : 16;
+  // two to four stages as distinct arrays: every LDS access names its stage statically, so
+  // the compiler tracks the loads into each stage separately
+  static_assert(NST == 2 || (NST >= 3 && NST <= 4 && PRO == PRO_NONE), "deeper pipelines: plain prologue");
+  constexpr int A2B = NST >= 3 ? A_BYTES : 16, B2B = NST >= 3 ? B_BYTES : 16;
+  constexpr int A3B = NST >= 4 ? A_BYTES : 16, B3B = NST >= 4 ? B_BYTES : 16;
   __shared__ __align__(16) unsigned char sA0[A_BYTES], sB0[B_BYTES], sM0[MASK_BYTES];
   __shared__ __align__(16) unsigned char sA1[A_BYTES], sB1[B_BYTES], sM1[MASK_BYTES];
-  __shared__ __align__(16) unsigned char sA2[A3], sB2[B3];
+  __shared__ __align__(16) unsigned char sA2[A2B], sB2[B2B];
+  __shared__ __align__(16) unsigned char sA3[A3B], sB3[B3B];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (LDS base goes to M0)
   const int wm = wave % WM, wn = wave / WM;
@@ -273,52 +275,12 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds(
       }
     }
   } else {
-    // Three stages, two K-steps in flight.  Step s issues step s + 2 into the stage step
-    // s - 1 used, multiplies, waits until this wave's loads of step s + 1 have landed (at
-    // most L requests, those of step s + 2, may remain) and ends on a bare barrier, which
-    // makes every wave's loads of step s + 1 visible and retires every read of step s.
-    // The issue and its wait sit on one branch (the multiply is written out on both), and
-    // the steady-state trip has no branch at all, so the compiler's own LDS-load tracking
-    // adds no drain inside it.
-    constexpr int L = NGA + NGB;
-    auto bar = [] {
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-    };
-    auto step = [&](bool more, unsigned char* na, unsigned char* nb, int ns, const unsigned char* a,
-                    const unsigned char* b) {
-      if (more) {
-        issue_all(na, nb, sM0, (int64_t)ns * SBK);
-        compute(a, b, sM0);
-        __builtin_amdgcn_s_waitcnt(vm_wait(L));
-      } else {
-        compute(a, b, sM0);
-        __builtin_amdgcn_s_waitcnt(vm_wait(0));
-      }
-      bar();
-    };
-    issue_all(sA0, sB0, sM0, 0);
-    if (nk == 1) {
-      __builtin_amdgcn_s_waitcnt(vm_wait(0));
-      bar();
-      compute(sA0, sB0, sM0);
-    } else if (nk > 1) {
-      issue_all(sA1, sB1, sM0, SBK);
-      __builtin_amdgcn_s_waitcnt(vm_wait(L));
-      bar();
-      int kt = 0;
-      for (; kt + 4 < nk; kt += 3) {
-        step(true, sA2, sB2, kt + 2, sA0, sB0);
-        step(true, sA0, sB0, kt + 3, sA1, sB1);
-        step(true, sA1, sB1, kt + 4, sA2, sB2);
-      }
-      // the last two to four steps (steps kt and kt + 1 in flight in stages 0 and 1)
-      step(kt + 2 < nk, sA2, sB2, kt + 2, sA0, sB0);
-      step(kt + 3 < nk, sA0, sB0, kt + 3, sA1, sB1);
-      if (kt + 2 < nk) step(false, sA0, sB0, 0, sA2, sB2);
-      if (kt + 3 < nk) step(false, sA0, sB0, 0, sA0, sB0);
-    }
+    // NST stages, NST - 1 K-steps in flight (lds_ring)
+    unsigned char* const SA[4] = {sA0, sA1, sA2, sA3};
+    unsigned char* const SB[4] = {sB0, sB1, sB2, sB3};
+    lds_ring<NST, NGA + NGB>(
+        nk, SA, SB, [&](unsigned char* a, unsigned char* b, int ks) { issue_all(a, b, sM0, (int64_t)ks * SBK); },
+        [&](const unsigned char* a, const unsigned char* b) { compute(a, b, sM0); });
   }
 
   // epilogue: lane holds 4 consecutive o for one t in each 16x16 block (the Epi terms --
@@ -458,9 +420,10 @@ hipError_t launch_widen_fp8(const uint8_t* w8, int64_t ldw, int64_t o, int64_t k
 // summed in slice order by a second kernel).  Measured on gfx950 for 33-128 tokens: one
 // workgroup per CU beats two (twice the partial-sum traffic) and beats 256-row tiles
 // (fewer tiles, so more splits); four waves of 64 x 32 measured level with eight waves.
-// Three LDS stages (two K-steps in flight, branch-free steady state) against two, on
-// gfx950: 4096 x 14336 at 128 tokens 53.8 -> 47.9 us, the 64-token MoE expert rows
-// 10-14% faster.  The route's tile_wg sets another target workgroup count.
+// Three LDS stages (two K-steps in flight, lds_ring) against two, on gfx950: 4096 x 14336
+// at 128 tokens 53.8 -> 47.9 us, the 64-token layer rows 10-14% faster; four stages
+// measured level with three (within 3% either way).  The route's tile_wg sets another
+// target workgroup count.
 static int64_t small_splits(const GemmArgs& a) {
   const int64_t bn = a.t <= 64 ? 64 : 128;
   const int64_t target = a.route.tile_wg > 0 ? a.route.tile_wg : 256;

@@ -9,7 +9,8 @@
 //
 // gfx950 design, after the dense direct-to-LDS kernel:
 //  * 256 x 256 output tile, 8 waves of 64 (o) x 128 (t); two LDS stages, each a distinct
-//    static array (so the compiler tracks the DMA into each one separately).
+//    static array (so the compiler tracks the DMA into each one separately); the
+//    few-token tiles use three (lds_ring, two K-steps in flight).
 //  * Few tokens (33-128): 128 x 64 or 128 x 128 tiles and a reduction split across
 //    workgroups (one per CU); each split writes its fp32 partial tile, and a second
 //    kernel sums the splits in a fixed order.  The sparse and dense steps form one
@@ -52,87 +53,26 @@ __device__ __forceinline__ void g2lds4(const void* g, void* lds) {
 }
 
 
-// The K-loop over n steps through NST LDS stages (distinct static arrays, named statically
-// at every access so the compiler tracks the direct-to-LDS loads into each one).
-//   NST = 2: each step issues the next step's loads, multiplies, then waits for all loads
-//            and synchronises (one step in flight).
-//   NST = 3: two steps in flight.  Before step s a wave waits until its own loads of step s
-//            have landed -- at most L requests (the loads of step s + 1, issued after them)
-//            may remain, L being the fewest direct-to-LDS requests any wave issues per step,
-//            so the wait is never short -- then the bare barrier makes every wave's loads of
-//            step s visible and retires every read of step s - 1, whose stage then takes the
-//            loads of step s + 2.  The wait is written at the end of step s - 1.  (__syncthreads() would also wait for the loads in flight;
-//            the empty asm statements keep the compiler from moving memory accesses across
-//            the barrier.)
-template <int NST, int L, typename Issue, typename Compute>
-__device__ __forceinline__ void k_loop(int n, unsigned char* a0, unsigned char* b0, unsigned char* a1,
-                                       unsigned char* b1, unsigned char* a2, unsigned char* b2, Issue&& issue,
-                                       Compute&& compute) {
-  if constexpr (NST == 2) {
-    issue(a0, b0, 0);
+// The two-stage K-loop (one step in flight): each step issues the next step's loads,
+// multiplies, then waits for all loads and synchronises.  Deeper pipelines use lds_ring.
+template <typename Issue, typename Compute>
+__device__ __forceinline__ void k_loop2(int n, unsigned char* a0, unsigned char* b0, unsigned char* a1,
+                                        unsigned char* b1, Issue&& issue, Compute&& compute) {
+  issue(a0, b0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // two steps per trip (stage 0, then stage 1); the next step's loads go out first
+  for (int s = 0; s < n; s += 2) {
+    if (s + 1 < n) issue(a1, b1, s + 1);
+    compute(a0, b0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // two steps per trip (stage 0, then stage 1); the next step's loads go out first
-    for (int s = 0; s < n; s += 2) {
-      if (s + 1 < n) issue(a1, b1, s + 1);
-      compute(a0, b0);
+    if (s + 1 < n) {
+      if (s + 2 < n) issue(a0, b0, s + 2);
+      compute(a1, b1);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (s + 1 < n) {
-        if (s + 2 < n) issue(a0, b0, s + 2);
-        compute(a1, b1);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-      }
     }
-  } else {
-    static_assert(NST == 3 && L >= 1, "three stages");
-    // Step s: [issue step s + 2 into the stage step s - 1 used], multiply step s, wait for
-    // this wave's loads of step s + 1, barrier.  The issue and the wait are taken on the
-    // same branch (the multiply is written out on both), so on every path the compiler
-    // sees the wait that covers the stage read next and adds none of its own.
-    auto bar = [] {
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-    };
-    auto step = [&](bool more, unsigned char* na, unsigned char* nb, int ns, const unsigned char* a,
-                    const unsigned char* b) {
-      if (more) {
-        issue(na, nb, ns);
-        compute(a, b);
-        __builtin_amdgcn_s_waitcnt(vm_wait(L));
-      } else {
-        compute(a, b);
-        __builtin_amdgcn_s_waitcnt(vm_wait(0));
-      }
-      bar();
-    };
-    issue(a0, b0, 0);
-    if (n == 1) {   // a single step, kept off the loop's path
-      __builtin_amdgcn_s_waitcnt(vm_wait(0));
-      bar();
-      compute(a0, b0);
-      bar();
-      return;
-    }
-    issue(a1, b1, 1);
-    __builtin_amdgcn_s_waitcnt(vm_wait(L));
-    bar();
-    // Steady state: three steps per trip (stages 0, 1, 2), each issuing two steps ahead,
-    // with no branch inside the trip.  The barrier ending a step also retires every read of
-    // it, so the last one leaves the stages free for the next phase.
-    int s = 0;
-    for (; s + 4 < n; s += 3) {
-      step(true, a2, b2, s + 2, a0, b0);
-      step(true, a0, b0, s + 3, a1, b1);
-      step(true, a1, b1, s + 4, a2, b2);
-    }
-    // the last two to four steps (steps s and s + 1 are in flight in stages 0 and 1)
-    step(s + 2 < n, a2, b2, s + 2, a0, b0);
-    step(s + 3 < n, a0, b0, s + 3, a1, b1);
-    if (s + 2 < n) step(false, a0, b0, 0, a2, b2);
-    if (s + 3 < n) step(false, a0, b0, 0, a0, b0);
   }
 }
 
@@ -160,11 +100,15 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
   constexpr int ND = BM / 8 / NW;            // dense weight load groups (8 rows) per wave
   static_assert(NV >= 1 && NX >= 1 && ND >= 1 && BM % (16 * NW) == 0 && BN % (8 * NW) == 0,
                 "load groups per wave");
-  static_assert(NST == 2 || NST == 3, "two or three stages");
-  constexpr int A3 = NST == 3 ? A_BYTES : 16, B3 = NST == 3 ? B_BYTES : 16;
+  static_assert(NST >= 2 && NST <= 4, "two to four stages");
+  constexpr int A2B = NST >= 3 ? A_BYTES : 16, B2B = NST >= 3 ? B_BYTES : 16;
+  constexpr int A3B = NST >= 4 ? A_BYTES : 16, B3B = NST >= 4 ? B_BYTES : 16;
   __shared__ __align__(16) unsigned char sA0[A_BYTES], sB0[B_BYTES];
   __shared__ __align__(16) unsigned char sA1[A_BYTES], sB1[B_BYTES];
-  __shared__ __align__(16) unsigned char sA2[A3], sB2[B3];
+  __shared__ __align__(16) unsigned char sA2[A2B], sB2[B2B];
+  __shared__ __align__(16) unsigned char sA3[A3B], sB3[B3B];
+  unsigned char* const SA[4] = {sA0, sA1, sA2, sA3};
+  unsigned char* const SB[4] = {sB0, sB1, sB2, sB3};
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wmi = wave % WM, wni = wave / WM;
@@ -290,7 +234,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
       }
     };
     // direct-to-LDS requests per wave per sparse step: values and X (positions: some waves)
-    k_loop<NST, NV + NX>(nks, sA0, sB0, sA1, sB1, sA2, sB2, issue, compute);
+    if constexpr (NST == 2) k_loop2(nks, sA0, sB0, sA1, sB1, issue, compute);
+    else lds_ring<NST, NV + NX>(nks, SA, SB, issue, compute);
   }
 
   // ------------------------------------------------------------ dense phase ---
@@ -342,7 +287,8 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
         }
       }
     };
-    k_loop<NST, ND + NX>(nkd, sA0, sB0, sA1, sB1, sA2, sB2, issue, compute);
+    if constexpr (NST == 2) k_loop2(nkd, sA0, sB0, sA1, sB1, issue, compute);
+    else lds_ring<NST, ND + NX>(nkd, SA, SB, issue, compute);
   }
 
   // epilogue: lane holds 4 consecutive o for one t in each 16x16 block; fp8 sums take
@@ -500,7 +446,7 @@ int64_t gemm_lds_sp_small_part_bytes(const SparseArgs& a) {
 hipError_t launch_gemm_lds_sp_small(const SparseArgs& a, float* part, int64_t part_bytes, hipStream_t s) {
   int64_t splits = sp_small_splits(a);
   if (part == nullptr || part_bytes < splits * a.t * a.o * 4) splits = 1;
-  // three LDS stages (72 / 96 KiB): two K-steps in flight
+  // three LDS stages (72 / 96 KiB): two K-steps in flight (four measured level)
   if (a.t <= 64) return launch_sp_cfg<128, 64, 4, 2, 3>(a, s, splits, part);
   return launch_sp_cfg<128, 128, 4, 2, 3>(a, s, splits, part);
 }

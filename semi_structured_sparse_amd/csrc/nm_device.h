@@ -201,6 +201,54 @@ __device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t q, uint32_t& lo, uint32
   hi = __builtin_amdgcn_perm(__float_as_uint(b.y), __float_as_uint(b.x), 0x07060302u);
 }
 
+// K-loop over n >= 1 steps through NST >= 3 LDS stages (distinct static arrays A[j], B[j],
+// j < NST, named by constant indices so the compiler tracks the direct-to-LDS loads into
+// each one).  issue(a, b, s) enqueues at least L direct-to-LDS requests per wave for step s
+// into stage (a, b), the same number for every s; compute(a, b) multiplies a staged step.  Step q issues step q + NST - 1 into the
+// stage step q - 1 used, multiplies step q, waits until this wave's requests of step q + 1
+// have landed (the (NST - 2) L requests of the later steps may remain) and ends on a bare
+// barrier, which makes every wave's step q + 1 visible and retires every read of step q.
+// Past the last step the issue re-requests step n - 1 (into a stage no step reads again),
+// so every step runs the same request-and-wait sequence: the compiler's wait analysis,
+// which does not follow which branch issued what, then adds no drain of its own.  The
+// loop ends with every request landed, so the stages are free for the caller.
+template <int NST, int L, typename Issue, typename Compute>
+__device__ __forceinline__ void lds_ring(int n, unsigned char* const* A, unsigned char* const* B, Issue&& issue,
+                                         Compute&& compute) {
+  static_assert(NST >= 3 && L >= 1 && L * (NST - 2) <= 63, "stages and requests per step");
+  auto bar = [] {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+#pragma unroll
+  for (int j = 0; j + 1 < NST; ++j) issue(A[j], B[j], j < n ? j : n - 1);
+  __builtin_amdgcn_s_waitcnt(vm_wait(L * (NST - 2)));
+  bar();
+  auto step = [&](int j, int q) {   // j = q % NST, a constant after unrolling
+    const int ahead = q + NST - 1;
+    issue(A[(j + NST - 1) % NST], B[(j + NST - 1) % NST], ahead < n ? ahead : n - 1);
+    compute(A[j], B[j]);
+    __builtin_amdgcn_s_waitcnt(vm_wait(L * (NST - 2)));
+    bar();
+  };
+  // whole trips of NST steps: one block with no branch (the compiler's analysis added a
+  // drain to loops whose trip had exits)
+  int s = 0;
+  for (; s + NST <= n; s += NST) {
+#pragma unroll
+    for (int j = 0; j < NST; ++j) step(j, s + j);
+  }
+  // the last n % NST steps
+#pragma unroll
+  for (int j = 0; j + 1 < NST; ++j) {
+    if (s + j >= n) break;
+    step(j, s + j);
+  }
+  __builtin_amdgcn_s_waitcnt(vm_wait(0));
+  bar();
+}
+
 // Final fp32 stores of a wave's FI x FJ blocks of 16 x 16 results, v_mfma_f32_16x16 layout:
 // block (i, j) holds, in lane (fr, fq) = (lane & 15, lane >> 4), outputs o = ob0 + 16 i + 4 fq
 // + [0, 4) of token row t = tb0 + 16 j + fr.  y[t][o] (=|+=) the block values; rows t >= T
