@@ -12,7 +12,8 @@
 // largest magnitude found, and -- for the dynamic shift -- its mean computed so that every
 // implementation reaches the same bits whatever its summation order: each value is rounded
 // to a multiple of q = 2^(E - 162) (E = exponent field of the largest magnitude, so every
-// |x|/q < 2^36), the integers are summed exactly in int64, and mu = fp32(fp64(S q) / K).
+// |x|/q < 2^36), the integers are summed exactly (in fp64: every partial sum is an integer
+// below 2^52), and mu = fp32(fp64(S q) / K).
 // Then each thread shifts, ranks and writes whole groups (the select kernel's ranking), the
 // keep bits go into mask words by lane shuffles, and the VAR sums are accumulated in fp64.
 #include <hip/hip_runtime.h>
@@ -25,18 +26,10 @@ namespace {
 
 using namespace nmk;
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 constexpr int PTS_THREADS = 256;
 constexpr int PTS_WAVES = PTS_THREADS / 64;
-
-__device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const int lo = __shfl_xor((int)(uint32_t)v, off);
-    const int hi = __shfl_xor((int)(uint32_t)((uint64_t)v >> 32), off);
-    v += (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
-  }
-  return v;
-}
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
@@ -65,26 +58,36 @@ __device__ __forceinline__ uint32_t shift_bf16(uint32_t h, float shift) {
   return bf16_rne(__fsub_rn(f, shift));
 }
 
-template <int M>
+// SH: 0 no shift, 1 the row mean (dynamic), 2 the caller's per-channel shift (static);
+// VAR: accumulate the variance sums.  Both are template parameters so the per-element
+// work has no branch.
+template <int M, int SH, bool VAR>
 __global__ __launch_bounds__(PTS_THREADS) void k_select_pts(const uint16_t* __restrict__ x, int64_t K, int64_t ldx,
-                                                            int n, int dynamic, const float* __restrict__ cshift,
-                                                            int var, uint16_t* __restrict__ y, int64_t ldy,
+                                                            int n, const float* __restrict__ cshift,
+                                                            uint16_t* __restrict__ y, int64_t ldy,
                                                             uint32_t* __restrict__ mask, float* __restrict__ mu_out,
                                                             float* __restrict__ alpha_out) {
+  constexpr bool dynamic = SH == 1;
   extern __shared__ __align__(16) uint16_t row[];     // the token row, K bf16
   __shared__ int red_i[PTS_WAVES];
-  __shared__ int64_t red_l[PTS_WAVES];
   __shared__ double red_d[4][PTS_WAVES];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t r = blockIdx.x;
   const uint16_t* xr = x + r * ldx;
   const int64_t nch = K / 8;                         // 16-byte pieces (K % 8 == 0)
 
-  // 1. stage the row, largest magnitude key
+  // 1. stage the row: whole KiB with direct-to-LDS loads (every request of the row in
+  // flight at once), the ragged tail through registers; then the largest magnitude key
+  const int64_t nkb = nch / 64;
+  for (int64_t kb = wave; kb < nkb; kb += PTS_WAVES)
+    __builtin_amdgcn_global_load_lds(xr + 8 * (kb * 64 + lane), (lds_void*)(row + 8 * kb * 64), 16, 0, 0);
+  for (int64_t c = nkb * 64 + tid; c < nch; c += PTS_THREADS)
+    *reinterpret_cast<u32x4*>(row + 8 * c) = *reinterpret_cast<const u32x4*>(xr + 8 * c);
+  __builtin_amdgcn_s_waitcnt(vm_wait(0));
+  __syncthreads();
   int mx = 0;
   for (int64_t c = tid; c < nch; c += PTS_THREADS) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(xr + 8 * c);
-    *reinterpret_cast<u32x4*>(row + 8 * c) = v;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(row + 8 * c);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int a = (int)(v[q] & 0x7FFFu), b = (int)((v[q] >> 16) & 0x7FFFu);
@@ -99,29 +102,31 @@ __global__ __launch_bounds__(PTS_THREADS) void k_select_pts(const uint16_t* __re
 #pragma unroll
   for (int w = 1; w < PTS_WAVES; ++w) mx = red_i[w] > mx ? red_i[w] : mx;
 
-  // 2. the dynamic shift: exact integer sum of the values rounded to multiples of q
+  // 2. the dynamic shift: exact sum of the values rounded to multiples of q.  Every
+  // rounded term x / q is an integer below 2^36 in magnitude and every partial sum one
+  // below 2^52, so fp64 adds them exactly (the same integer in any order).
   float shift = 0.f;
-  if (dynamic) {
+  if constexpr (dynamic) {
     const int e = (mx >> 7) > 1 ? (mx >> 7) : 1;
-    int64_t acc = 0;
+    const double scale = __builtin_ldexp(1.0, 162 - e);   // 1 / q, a power of two
+    double acc = 0.0, acc1 = 0.0;   // two chains of dependent adds
     if (mx != 0) {
       for (int64_t c = tid; c < nch; c += PTS_THREADS) {
         const u32x4 v = *reinterpret_cast<const u32x4*>(row + 8 * c);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const uint32_t h = (q & 1) ? (v[q >> 1] >> 16) : (v[q >> 1] & 0xFFFFu);
-          const double d = (double)__uint_as_float(h << 16);
-          acc += (int64_t)__builtin_rint(__builtin_ldexp(d, 162 - e));   // exact: |x| / q < 2^36
+        for (int q = 0; q < 4; ++q) {
+          acc += __builtin_rint((double)__uint_as_float(v[q] << 16) * scale);
+          acc1 += __builtin_rint((double)__uint_as_float(v[q] & 0xFFFF0000u) * scale);
         }
       }
     }
-    acc = wave_sum_i64(acc);
-    if (lane == 0) red_l[wave] = acc;
+    acc = wave_sum_f64(acc + acc1);
+    if (lane == 0) red_d[0][wave] = acc;
     __syncthreads();
-    int64_t tot = 0;
+    double tot = 0.0;
 #pragma unroll
-    for (int w = 0; w < PTS_WAVES; ++w) tot += red_l[w];
-    shift = mx == 0 ? 0.f : (float)(__builtin_ldexp((double)tot, e - 162) / (double)K);
+    for (int w = 0; w < PTS_WAVES; ++w) tot += red_d[0][w];
+    shift = mx == 0 ? 0.f : (float)(__builtin_ldexp(tot, e - 162) / (double)K);
     if (tid == 0 && mu_out != nullptr) mu_out[r] = shift;
   }
 
@@ -134,32 +139,55 @@ __global__ __launch_bounds__(PTS_THREADS) void k_select_pts(const uint16_t* __re
     const int64_t g = g0 + tid;
     uint32_t bits = 0;
     if (g < G) {
+      // the group in whole pieces (8 bytes for m = 4, else 16-byte pieces)
       uint32_t d[M / 2];
+      if constexpr (M == 4) {
+        const uint2 v = *reinterpret_cast<const uint2*>(row + g * M);
+        d[0] = v.x;
+        d[1] = v.y;
+      } else {
 #pragma unroll
-      for (int q = 0; q < M / 2; ++q) {
-        const uint32_t pr = *reinterpret_cast<const uint32_t*>(row + g * M + 2 * q);
-        uint32_t lo = pr & 0xFFFFu, hi = pr >> 16;
-        if (dynamic) {
-          lo = shift_bf16(lo, shift);
-          hi = shift_bf16(hi, shift);
-        } else if (cshift != nullptr) {
-          lo = shift_bf16(lo, cshift[g * M + 2 * q]);
-          hi = shift_bf16(hi, cshift[g * M + 2 * q + 1]);
+        for (int p = 0; p < M / 8; ++p) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(row + g * M + 8 * p);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) d[4 * p + q] = v[q];
         }
-        d[q] = lo | (hi << 16);
+      }
+      if constexpr (SH != 0) {
+        float c[M];
+        if constexpr (SH == 1) {
+#pragma unroll
+          for (int i = 0; i < M; ++i) c[i] = shift;
+        } else {
+#pragma unroll
+          for (int p = 0; p < M / 4; ++p) {
+            const float4 v = *reinterpret_cast<const float4*>(cshift + g * M + 4 * p);
+            c[4 * p] = v.x;
+            c[4 * p + 1] = v.y;
+            c[4 * p + 2] = v.z;
+            c[4 * p + 3] = v.w;
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < M / 2; ++q)
+          d[q] = shift_bf16(d[q] & 0xFFFFu, c[2 * q]) | (shift_bf16(d[q] >> 16, c[2 * q + 1]) << 16);
       }
       bits = (2 * n == M) ? topn_bits_n<M, M / 2>(d) : topn_bits<M>(d, n);
       uint32_t o[M / 2];
 #pragma unroll
       for (int q = 0; q < M / 2; ++q) {
         o[q] = mask_pair(d[q], (bits >> (2 * q)) & 3u);
-        if (var) {
+        if constexpr (VAR) {
           const double a0 = (double)__uint_as_float(d[q] << 16), a1 = (double)__uint_as_float(d[q] & 0xFFFF0000u);
-          const double b0 = (double)__uint_as_float(o[q] << 16), b1 = (double)__uint_as_float(o[q] & 0xFFFF0000u);
-          sa += a0 + a1;
-          sa2 += a0 * a0 + a1 * a1;
-          sb += b0 + b1;
-          sb2 += b0 * b0 + b1 * b1;
+          const double b0 = (bits >> (2 * q)) & 1u ? a0 : 0.0, b1 = (bits >> (2 * q + 1)) & 1u ? a1 : 0.0;
+          sa += a0;
+          sa += a1;
+          sa2 = __builtin_fma(a0, a0, sa2);
+          sa2 = __builtin_fma(a1, a1, sa2);
+          sb += b0;
+          sb += b1;
+          sb2 = __builtin_fma(b0, b0, sb2);
+          sb2 = __builtin_fma(b1, b1, sb2);
         }
       }
       if constexpr (M == 4) {
@@ -180,7 +208,7 @@ __global__ __launch_bounds__(PTS_THREADS) void k_select_pts(const uint16_t* __re
   }
 
   // 4. VAR: alpha = sqrt(Var(x~) / Var(S(x~))), population variances over the K entries
-  if (var) {
+  if constexpr (VAR) {
     sa = wave_sum_f64(sa);
     sa2 = wave_sum_f64(sa2);
     sb = wave_sum_f64(sb);
@@ -255,16 +283,24 @@ hipError_t launch_select_pts(int m, const uint16_t* x, int64_t rows, int64_t k, 
   if (rows > 0x7FFFFFFF || k % 8 != 0 || k > 65536) return hipErrorInvalidValue;
   const size_t lds = (size_t)k * 2;
   const dim3 g((unsigned)rows), b(PTS_THREADS);
-#define NM_PTS(MV)                                                                                          \
+#define NM_PTS_K(MV, SHV, VARV)                                                                             \
   {                                                                                                         \
-    auto kern = k_select_pts<MV>;                                                                          \
+    auto kern = k_select_pts<MV, SHV, VARV>;                                                               \
     if (lds > 65536) {                                                                                      \
       hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,     \
                                          (int)lds);                                                        \
       if (e != hipSuccess) return e;                                                                        \
     }                                                                                                       \
-    kern<<<g, b, lds, s>>>(x, k, ldx, n, dynamic, cshift, var, y, ldy, mask, mu_out, alpha_out);            \
-    break;                                                                                                  \
+    kern<<<g, b, lds, s>>>(x, k, ldx, n, cshift, y, ldy, mask, mu_out, alpha_out);                          \
+    return hipGetLastError();                                                                               \
+  }
+#define NM_PTS_V(MV, SHV) \
+  if (var) NM_PTS_K(MV, SHV, true) else NM_PTS_K(MV, SHV, false)
+#define NM_PTS(MV)                                  \
+  {                                                 \
+    if (dynamic) NM_PTS_V(MV, 1)                    \
+    else if (cshift != nullptr) NM_PTS_V(MV, 2)     \
+    else NM_PTS_V(MV, 0)                            \
   }
   switch (m) {
     case 4: NM_PTS(4)
@@ -274,7 +310,9 @@ hipError_t launch_select_pts(int m, const uint16_t* x, int64_t rows, int64_t k, 
     default: return hipErrorInvalidValue;
   }
 #undef NM_PTS
-  return hipGetLastError();
+#undef NM_PTS_V
+#undef NM_PTS_K
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_weight_sums(const void* w, int64_t o, int64_t k, int64_t ldw, int fp8, const float* w_scale,
