@@ -236,10 +236,11 @@ nml::SparseArgs w_mode_sparse_args(const nm_spmm_args* a, int64_t kc, int ns, bo
   return sa;
 }
 
-// Workspace bytes of the few-token tile route of the W_* modes: [lifted X][partials].
+// Workspace bytes of the few-token tile route of the W_* modes ([lifted X][partials]; 0
+// when it needs none), or -1 when that route does not apply.
 int64_t w_mode_tile_bytes(const nm_spmm_args* a, int64_t kc, int ns) {
   const nml::SparseArgs sa = w_mode_sparse_args(a, kc, ns, false);
-  if (!sp_few_tile(sa)) return 0;
+  if (!sp_few_tile(sa)) return -1;
   const int64_t lift = a->mode == NM_W_SLIDE ? align256(a->t * lift_ld(kc) * 2) : 0;
   return lift + nml::gemm_lds_sp_small_part_bytes(sa);
 }
@@ -571,7 +572,7 @@ int64_t nm_spmm_workspace_size(const nm_spmm_args* a) {
       if (a->mode == NM_W_SLIDE && (a->ns < 2 || a->ns > 8 || a->k % (2 * a->ns))) return 0;
       const int ns = a->mode == NM_W_SLIDE ? a->ns : 2;
       const int64_t tile = w_mode_tile_bytes(a, w_mode_kc(a), ns);
-      if (tile > 0) return tile;
+      if (tile >= 0) return tile;
       nml::FewArgs f = few_sparse_args(a, w_mode_kc(a), ns);
       f.route = r;
       part = nml::few_partial_bytes(f);
@@ -858,7 +859,7 @@ nm_status spmm_impl(const nm_spmm_args* a, void* stream, bool noalloc) {
       const nml::Route R = route_of(a, true);
       if (use_few(T, R)) {
         const int64_t tile = w_mode_tile_bytes(a, kc, ns);
-        if (tile > 0 && a->workspace != nullptr && a->workspace_bytes >= tile) {
+        if (tile == 0 || (tile > 0 && a->workspace != nullptr && a->workspace_bytes >= tile)) {
           nml::SparseArgs sa = w_mode_sparse_args(a, kc, ns, true);
           int64_t off = 0;
           if (a->mode == NM_W_SLIDE) {

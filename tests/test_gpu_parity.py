@@ -476,6 +476,42 @@ def test_few_token_kernels(route, t, k):
         check_gemm(ys, O.gemm(x8, pr), x8, pr, label="slide 6:8")
 
 
+@pytest.mark.parametrize("wg", [1, 6])
+@pytest.mark.parametrize("t", [40, 100])
+@pytest.mark.parametrize("nsteps", [1, 2, 3, 4, 5, 6, 7, 9])
+def test_few_token_tile_step_counts(nsteps, t, wg):
+    """The split-K tile kernels' multi-stage K-loop at every short step count: K = 64
+    nsteps, with tile_wg = 1 (no split: each workgroup runs all nsteps K-steps) and 6
+    (three splits of the two o-tiles), covering every remainder of the steps modulo the
+    stage count, the re-requested last step, and the one-step case.  Dense weights with
+    8:16 activations, 2:4 weights, and the hybrid (sparse then dense K-steps)."""
+    print(f"tile steps={nsteps} t={t} wg={wg}", flush=True)
+    rng = np.random.default_rng(100 * nsteps + t + wg)
+    o, k = 200, 64 * nsteps
+    x = synth.student_t_bf16(rng, (t, k), 4.0, 0.5)
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    with use_route("few_tile", tile_wg=wg):
+        sx, _ = O.sparsify(x, 8, 16)
+        y, _ = run_act(x, w, 8, 16)
+        assert "tile_lds" in taken(), taken()
+        check_gemm(y, O.gemm(sx, w), sx, w, label=f"8:16 steps={nsteps}")
+        v, mt = gpu_compress_2of4(w)
+        ws24, _ = O.sparsify(w, 2, 4)
+        yw = run_w(S.NM_W_COMPRESSED, x, v, mt, o, k)
+        assert "tile_lds" in taken() and "sparse_mma" in taken(), taken()
+        check_gemm(yw, O.gemm(x, ws24), x, ws24, label=f"w 2:4 steps={nsteps}")
+        if nsteps >= 2:
+            # hybrid: the first 64 (nsteps - 1) columns sparse, the last 64 dense
+            ks, kd = 64 * (nsteps - 1), 64
+            wsp, _ = O.sparsify(np.ascontiguousarray(w[:, :ks]), 2, 4)
+            vs, ms = gpu_compress_2of4(np.ascontiguousarray(w[:, :ks]))
+            wd = np.ascontiguousarray(w[:, ks:])
+            yh = run_hybrid(x, None, ks, None, kd, vs, ms, dev(wd), o)
+            ref = O.gemm(np.ascontiguousarray(x[:, :ks]), wsp) + O.gemm(np.ascontiguousarray(x[:, ks:]), wd)
+            wcat = np.concatenate([wsp, wd], axis=1)
+            check_gemm(yh, ref, x, wcat, label=f"hybrid steps={nsteps}")
+
+
 @pytest.mark.parametrize("wpb,splits", [(4, 0), (8, 0), (16, 0), (16, 3), (4, 7)])
 @pytest.mark.parametrize("t", [1, 20, 70])
 def test_few_token_partition_overrides(wpb, splits, t):
