@@ -957,6 +957,7 @@ __global__ __launch_bounds__(RP4_THREADS) void k_reduce_parts4(const float* __re
 
 // X[:, c0] then X[:, c1] side by side: xo[t][j] = x[t][c0[j]] (j < k0),
 // xo[t][off1 + j] = x[t][c1[j]] (j < k1).  Column indices are clamped to [0, kx).
+// Element by element: the form for layouts the row kernel below does not take.
 __global__ void k_permute_cols(const uint16_t* __restrict__ x, int64_t T, int64_t ldx, int64_t kx,
                                const int32_t* __restrict__ c0, int64_t k0, const int32_t* __restrict__ c1,
                                int64_t k1, int64_t off1, uint16_t* __restrict__ xo, int64_t ldo) {
@@ -974,6 +975,42 @@ __global__ void k_permute_cols(const uint16_t* __restrict__ x, int64_t T, int64_
   }
   c = c < 0 ? 0 : (c >= kx ? kx - 1 : c);
   xo[t * ldo + dst] = x[t * ldx + c];
+}
+
+// The same gather a token row per workgroup: the row is read into LDS with 16-byte loads,
+// then each thread gathers 8 consecutive outputs from LDS (column indices read as two
+// 16-byte pieces) and writes them as one 16-byte piece.  Needs kx, ldx, k0, k1, off1 and
+// ldo multiples of 8 and 16-byte aligned x and xo; the row takes kx * 2 bytes of LDS.
+constexpr int PERM_THREADS = 256;
+__global__ __launch_bounds__(PERM_THREADS) void k_permute_rows(const uint16_t* __restrict__ x, int64_t ldx, int kx,
+                                                               const int32_t* __restrict__ c0, int k0,
+                                                               const int32_t* __restrict__ c1, int k1, int64_t off1,
+                                                               uint16_t* __restrict__ xo, int64_t ldo) {
+  extern __shared__ __align__(16) uint16_t xrow[];
+  const int tid = threadIdx.x;
+  const int64_t t = blockIdx.x;
+  const uint16_t* src = x + t * ldx;
+  for (int c = tid; c < kx / 8; c += PERM_THREADS)
+    *reinterpret_cast<uint4*>(xrow + 8 * c) = *reinterpret_cast<const uint4*>(src + 8 * c);
+  __syncthreads();
+  uint16_t* dst = xo + t * ldo;
+  const int n8 = (k0 + k1) / 8;
+  for (int p = tid; p < n8; p += PERM_THREADS) {
+    const int j = 8 * p;
+    const bool first = j < k0;
+    const int32_t* cl = first ? c0 + j : c1 + (j - k0);
+    const int4 ia = *reinterpret_cast<const int4*>(cl), ib = *reinterpret_cast<const int4*>(cl + 4);
+    const int idx[8] = {ia.x, ia.y, ia.z, ia.w, ib.x, ib.y, ib.z, ib.w};
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int a = idx[2 * q], b = idx[2 * q + 1];
+      a = a < 0 ? 0 : (a >= kx ? kx - 1 : a);
+      b = b < 0 ? 0 : (b >= kx ? kx - 1 : b);
+      w[q] = (uint32_t)xrow[a] | ((uint32_t)xrow[b] << 16);
+    }
+    *reinterpret_cast<uint4*>(dst + (first ? j : off1 + (j - k0))) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
 }
 
 struct Plan {
@@ -1205,6 +1242,20 @@ hipError_t launch_permute_cols(const uint16_t* x, int64_t t, int64_t ldx, int64_
                                hipStream_t s) {
   const int64_t n = t * (k0 + k1);
   if (n == 0) return hipSuccess;
+  const bool rows = kx % 8 == 0 && ldx % 8 == 0 && k0 % 8 == 0 && k1 % 8 == 0 && off1 % 8 == 0 && ldo % 8 == 0 &&
+                    ((uintptr_t)x & 15) == 0 && ((uintptr_t)xo & 15) == 0 && ((uintptr_t)c0 & 15) == 0 &&
+                    ((uintptr_t)c1 & 15) == 0 && kx <= 65536 && k0 + k1 <= 0x7FFFFFFF && t <= 0x7FFFFFFF;
+  if (rows) {
+    const size_t lds = (size_t)kx * 2;
+    if (lds > 65536) {
+      hipError_t e = hipFuncSetAttribute((const void*)k_permute_rows, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         (int)lds);
+      if (e != hipSuccess) return e;
+    }
+    k_permute_rows<<<dim3((unsigned)t), dim3(PERM_THREADS), lds, s>>>(x, ldx, (int)kx, c0, (int)k0, c1, (int)k1,
+                                                                       off1, xo, ldo);
+    return hipGetLastError();
+  }
   k_permute_cols<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(x, t, ldx, kx, c0, k0, c1, k1, off1, xo,
                                                                          ldo);
   return hipGetLastError();
