@@ -378,8 +378,12 @@ bool gemm_lds_eligible(const GemmArgs& a, bool any_size) {
 }
 
 hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t s) {
-  // fewer 256 x 256 tiles than CUs: 256 x 128 tiles (twice as many workgroups)
-  const bool half = ((a.o + 255) / 256) * ((a.t + 255) / 256) < 256;
+  // 256 x 128 tiles (twice as many workgroups) when they finish in fewer rounds of one
+  // workgroup per CU: a half tile stages 3/4 of a whole tile's bytes per K-step, and the
+  // loads bound the kernel, so it takes about 3/4 of the time.  (128 whole tiles: one round
+  // of 256 half tiles; 224 whole tiles: one round, against two rounds of half tiles.)
+  const int64_t whole = ((a.o + 255) / 256) * ((a.t + 255) / 256), halves = ((a.o + 255) / 256) * ((a.t + 127) / 128);
+  const bool half = ((halves + 255) / 256) * 3 < ((whole + 255) / 256) * 4;
   if (a.prologue == PRO_MASK) {
     if (half) return launch_cfg<256, 128, 4, 2, PRO_MASK>(a, s, 1, nullptr);
     return launch_cfg<256, 256, 4, 2, PRO_MASK>(a, s, 1, nullptr);
