@@ -270,14 +270,13 @@ nm_status use_meta_block(nml::SparseArgs& sa, void* ws, int64_t ws_bytes, int64_
 struct W8A8Layout {
   int64_t xq, xs, meta, part, total;
 };
-W8A8Layout w8a8_layout(int64_t t, int64_t o, int64_t kc, const nml::SparseArgs* sa_small, const nml::Route& r) {
+W8A8Layout w8a8_layout(int64_t t, int64_t o, int64_t kc, int64_t part_bytes) {
   W8A8Layout L{};
   L.xq = 0;
   L.xs = align256(t * kc);
   L.meta = L.xs + align256(t * 4);
   L.part = L.meta + align256(nml::meta_block_bytes(o, kc));
-  const int64_t pb = (sa_small != nullptr && use_few(t, r)) ? nml::gemm_lds_sp_small_part_bytes(*sa_small) : 0;
-  L.total = L.part + pb;
+  L.total = L.part + part_bytes;
   return L;
 }
 nml::SparseArgs w8a8_args(const nm_spmm_args* a, int64_t kc, const uint8_t* xq, const float* xs, bool report) {
@@ -289,13 +288,35 @@ nml::SparseArgs w8a8_args(const nm_spmm_args* a, int64_t kc, const uint8_t* xq, 
   sa.f8 = 1; sa.x_scale = xs; sa.w_scale = a->w_scale;
   return sa;
 }
-int64_t w8a8_ws_bytes(const nm_spmm_args* a, int64_t kc) {
+// Up to 16 tokens (one token block) the product streams the e4m3 2:4 codes through the
+// weight-streaming kernel (widened to bf16 after their LDS read, exactly, and multiplied
+// on the bf16 sparse instruction with the lifted e4m3 X widened alike: the same products,
+// summed in fp32 in another order), unless the NM_ROUTE_FEW_TILE hint asks for the split
+// tile kernel on the fp8 instruction.
+bool w8a8_stream(const nm_spmm_args* a, const nml::Route& r) {
+  return use_few(a->t, r) && a->t <= 16 && !r.has(NM_ROUTE_FEW_TILE);
+}
+nml::FewArgs w8a8_few_args(const nm_spmm_args* a, int64_t kc, const uint8_t* xq, const float* xs,
+                           const nml::Route& r) {
+  nml::FewArgs f{};
+  f.route = r;
+  nml::FewSeg& sg = f.seg[f.nseg++];
+  sg.w = a->w; sg.ldw = kc / 2; sg.w_meta = (const uint8_t*)a->w_meta; sg.w_kind = nml::WK_SP24F8;
+  sg.x = (const uint16_t*)xq; sg.ldx = kc; sg.loader = nml::XL_F8; sg.ns = 2; sg.k = kc;
+  f.w_scale = a->w_scale; f.row_scale = xs;
+  f.t = a->t; f.o = a->o; f.y = a->y; f.ldy = a->ldy; f.accumulate = a->accumulate;
+  return f;
+}
+int64_t w8a8_part_bytes(const nm_spmm_args* a, int64_t kc) {
   const nml::SparseArgs sa = w8a8_args(a, kc, nullptr, nullptr, false);
-  return w8a8_layout(a->t, a->o, kc, &sa, sa.route).total;
+  if (w8a8_stream(a, sa.route)) return nml::few_partial_bytes(w8a8_few_args(a, kc, nullptr, nullptr, sa.route));
+  return use_few(a->t, sa.route) ? nml::gemm_lds_sp_small_part_bytes(sa) : 0;
+}
+int64_t w8a8_ws_bytes(const nm_spmm_args* a, int64_t kc) {
+  return w8a8_layout(a->t, a->o, kc, w8a8_part_bytes(a, kc)).total;
 }
 nm_status w8a8_product(const nm_spmm_args* a, int64_t kc, int ns, hipStream_t s) {
-  const nml::SparseArgs probe = w8a8_args(a, kc, nullptr, nullptr, false);
-  const W8A8Layout L = w8a8_layout(a->t, a->o, kc, &probe, probe.route);
+  const W8A8Layout L = w8a8_layout(a->t, a->o, kc, w8a8_part_bytes(a, kc));
   if (a->workspace == nullptr || a->workspace_bytes < L.total) return NM_EINVAL;
   char* ws = reinterpret_cast<char*>(a->workspace);
   uint8_t* xq = reinterpret_cast<uint8_t*>(ws + L.xq);
@@ -305,6 +326,9 @@ nm_status w8a8_product(const nm_spmm_args* a, int64_t kc, int ns, hipStream_t s)
   if (e != hipSuccess) return NM_EHIP;
   nml::SparseArgs sa = w8a8_args(a, kc, xq, xs, true);
   sa.route.note(NM_TAKEN_QUANT | (a->mode == NM_W_SLIDE && ns > 2 ? NM_TAKEN_LIFT : 0u));
+  if (w8a8_stream(a, sa.route))
+    return hip_status(nml::launch_few(w8a8_few_args(a, kc, xq, xs, sa.route),
+                                      reinterpret_cast<float*>(ws + L.part), L.total - L.part, s));
   // few tokens: the split tile kernel reads the row-major positions (a blocked copy would
   // cost a launch of about the product's own length); above that the blocked copy pays
   if (use_few(a->t, sa.route))

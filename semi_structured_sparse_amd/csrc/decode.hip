@@ -43,7 +43,24 @@ constexpr int WK_NONE = -1;
 template <int XL, int NS, bool CHECKED>
 __device__ __forceinline__ u32x4 load_x8(const uint16_t* __restrict__ rp, int k, int kend) {
   u32x4 r = {0u, 0u, 0u, 0u};
-  if constexpr (XL == XL_PLAIN) {
+  if constexpr (XL == XL_F8) {
+    // e4m3 codes, one byte per position (rp addresses bytes), widened to bf16
+    const uint8_t* bp = reinterpret_cast<const uint8_t*>(rp);
+    uint32_t q[2] = {0u, 0u};
+    if (!CHECKED || k + 8 <= kend) {
+      const uint2 v = *reinterpret_cast<const uint2*>(bp + k);
+      q[0] = v.x;
+      q[1] = v.y;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (k + e < kend) q[e >> 2] |= (uint32_t)bp[k + e] << (8 * (e & 3));
+    }
+    uint32_t c0, c1, c2, c3;
+    fp8x4_to_bf16x4(q[0], c0, c1);
+    fp8x4_to_bf16x4(q[1], c2, c3);
+    return u32x4{c0, c1, c2, c3};
+  } else if constexpr (XL == XL_PLAIN) {
     if (!CHECKED || k + 8 <= kend) return *reinterpret_cast<const u32x4*>(rp + k);
 #pragma unroll
     for (int e = 0; e < 8; ++e)
@@ -68,9 +85,19 @@ __device__ __forceinline__ u32x4 load_x8(const uint16_t* __restrict__ rp, int k,
   }
 }
 
+// 2:4 weights on the sparse matrix instruction: bf16 values, or e4m3 codes of them
+constexpr bool sp_kind(int wk) { return wk == WK_SP24 || wk == WK_SP24F8; }
+
+// the row of token t of an X segment (XL_F8 rows are bytes, ldx in bytes)
+template <int XL>
+__device__ __forceinline__ const uint16_t* x_row(const FewSeg& sg, int64_t t) {
+  if constexpr (XL == XL_F8) return reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(sg.x) + t * sg.ldx);
+  else return sg.x + t * sg.ldx;
+}
+
 // reduction positions covered by one matrix instruction: 32 (dense) or 64 (2:4 sparse,
 // dense-equivalent)
-template <int WK> struct Chunk { static constexpr int K = (WK == WK_SP24) ? 64 : 32; };
+template <int WK> struct Chunk { static constexpr int K = sp_kind(WK) ? 64 : 32; };
 
 // 16-row weight tiles per wave: each X fragment feeds RW matrix instructions, so the X
 // bytes a wave pulls through L1 per weight byte drop from TB to TB/RW (2 TB/RW for 2:4).
@@ -80,7 +107,7 @@ constexpr int rw_for(int tb, int wk) { return tb == 1 ? 1 : tb == 2 ? 2 : tb == 
 // next to the accumulators, within 128 VGPRs for 1-2 token blocks (up to 16 waves per
 // workgroup) and 256 above
 constexpr int unroll_for(int tb, int rw, int wk) {
-  const int per_chunk = rw * (wk == WK_SP24 ? 5 : 4) + tb * (wk == WK_SP24 ? 8 : 4);
+  const int per_chunk = rw * (sp_kind(wk) ? 5 : 4) + tb * (sp_kind(wk) ? 8 : 4);
   const int budget = (tb <= 2 ? 128 : 256) - 48 - 4 * rw * tb - 2 * tb;
   const int u = budget / (2 * per_chunk);
   return u < 1 ? 1 : (u > 4 ? 4 : u);
@@ -105,7 +132,7 @@ __device__ __forceinline__ void stream_seg(f32x4 (&acc)[RW][TB], const FewSeg& s
 #pragma unroll
   for (int j = 0; j < TB; ++j) {
     const int64_t t = 16 * j + fr;
-    xrow[j] = sg.x + (t < T ? t : T - 1) * sg.ldx;
+    xrow[j] = x_row<XL>(sg, t < T ? t : T - 1);
   }
   const int kcv = (int)(sg.k / 2);            // compressed row length (2:4)
   const int mstride = (int)((sg.k + 7) >> 3); // 2-bit metadata bytes per row
@@ -115,8 +142,9 @@ __device__ __forceinline__ void stream_seg(f32x4 (&acc)[RW][TB], const FewSeg& s
   for (int i = 0; i < RW; ++i) {
     if constexpr (WK == WK_BF16) wrow[i] = reinterpret_cast<const uint8_t*>(sg.w) + orow[i] * sg.ldw * 2;
     else if constexpr (WK == WK_FP8) wrow[i] = reinterpret_cast<const uint8_t*>(sg.w) + orow[i] * sg.ldw;
+    else if constexpr (WK == WK_SP24F8) wrow[i] = reinterpret_cast<const uint8_t*>(sg.w) + orow[i] * (int64_t)kcv;
     else wrow[i] = reinterpret_cast<const uint8_t*>(sg.w) + orow[i] * (int64_t)kcv * 2;
-    mrow[i] = (WK == WK_SP24) ? sg.w_meta + orow[i] * (int64_t)mstride : nullptr;
+    mrow[i] = sp_kind(WK) ? sg.w_meta + orow[i] * (int64_t)mstride : nullptr;
   }
 
   struct Batch {
@@ -134,6 +162,11 @@ __device__ __forceinline__ void stream_seg(f32x4 (&acc)[RW][TB], const FewSeg& s
       } else if constexpr (WK == WK_FP8) {
         const uint2 q = *reinterpret_cast<const uint2*>(wrow[i] + k + 8 * fq);
         bt.w[u][i] = u32x4{q.x, q.y, 0u, 0u};   // widened to bf16 at use
+      } else if constexpr (WK == WK_SP24F8) {
+        const int v0 = k / 2 + 8 * fq;
+        const uint2 q = *reinterpret_cast<const uint2*>(wrow[i] + v0);
+        bt.w[u][i] = u32x4{q.x, q.y, 0u, 0u};   // widened to bf16 at use
+        bt.m[u][i] = *reinterpret_cast<const uint16_t*>(mrow[i] + (v0 >> 2));   // v0 % 8 == 0
       } else {
         const int v0 = k / 2 + 8 * fq;
         bt.w[u][i] = *reinterpret_cast<const u32x4*>(wrow[i] + 2 * v0);
@@ -143,7 +176,7 @@ __device__ __forceinline__ void stream_seg(f32x4 (&acc)[RW][TB], const FewSeg& s
 #pragma unroll
     for (int j = 0; j < TB; ++j) {
       bt.xl[u][j] = load_x8<XL, NS, false>(xrow[j], k + 8 * fq, k + CK);
-      if constexpr (WK == WK_SP24) bt.xh[u][j] = load_x8<XL, NS, false>(xrow[j], k + 32 + 8 * fq, k + CK);
+      if constexpr (sp_kind(WK)) bt.xh[u][j] = load_x8<XL, NS, false>(xrow[j], k + 32 + 8 * fq, k + CK);
     }
   };
   // checked loads of chunk k (any part of it may lie beyond k1)
@@ -167,6 +200,19 @@ __device__ __forceinline__ void stream_seg(f32x4 (&acc)[RW][TB], const FewSeg& s
         for (int e = 0; e < 8; ++e)
           if (kk + e < k1) qq[e >> 2] |= (uint32_t)rp[kk + e] << (8 * (e & 3));
         bt.w[u][i] = u32x4{qq[0], qq[1], 0u, 0u};
+      } else if constexpr (WK == WK_SP24F8) {
+        const int v0 = k / 2 + 8 * fq;
+        const uint8_t* vp = wrow[i] + v0;
+        const uint8_t* mp = mrow[i] + (v0 >> 2);
+        uint32_t qq[2] = {0u, 0u}, m = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (k + 16 * fq + 2 * e < k1 && v0 + e < kcv) qq[e >> 2] |= (uint32_t)vp[e] << (8 * (e & 3));
+#pragma unroll
+        for (int bq = 0; bq < 2; ++bq)
+          if ((v0 >> 2) + bq < mstride) m |= (uint32_t)mp[bq] << (8 * bq);
+        bt.w[u][i] = u32x4{qq[0], qq[1], 0u, 0u};
+        bt.m[u][i] = m;
       } else {
         const int v0 = k / 2 + 8 * fq;
         const uint16_t* vp = reinterpret_cast<const uint16_t*>(wrow[i]) + v0;
@@ -186,7 +232,7 @@ __device__ __forceinline__ void stream_seg(f32x4 (&acc)[RW][TB], const FewSeg& s
 #pragma unroll
     for (int j = 0; j < TB; ++j) {
       bt.xl[u][j] = load_x8<XL, NS, true>(xrow[j], k + 8 * fq, k1);
-      if constexpr (WK == WK_SP24) bt.xh[u][j] = load_x8<XL, NS, true>(xrow[j], k + 32 + 8 * fq, k1);
+      if constexpr (sp_kind(WK)) bt.xh[u][j] = load_x8<XL, NS, true>(xrow[j], k + 32 + 8 * fq, k1);
     }
   };
   auto mma = [&](const Batch& bt, int u) {
@@ -194,7 +240,7 @@ __device__ __forceinline__ void stream_seg(f32x4 (&acc)[RW][TB], const FewSeg& s
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
       u32x4 wv = bt.w[u][i];
-      if constexpr (WK == WK_FP8) {
+      if constexpr (WK == WK_FP8 || WK == WK_SP24F8) {
         uint32_t c0, c1, c2, c3;
         fp8x4_to_bf16x4(wv[0], c0, c1);
         fp8x4_to_bf16x4(wv[1], c2, c3);
@@ -204,7 +250,7 @@ __device__ __forceinline__ void stream_seg(f32x4 (&acc)[RW][TB], const FewSeg& s
     }
 #pragma unroll
     for (int j = 0; j < TB; ++j) {
-      if constexpr (WK == WK_SP24) {
+      if constexpr (sp_kind(WK)) {
         const u32x4 lo = bt.xl[u][j], hi = bt.xh[u][j];
         const u32x8 bb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         const bf16x16 bv = __builtin_bit_cast(bf16x16, bb);
@@ -231,8 +277,9 @@ __device__ __forceinline__ void stream_seg(f32x4 (&acc)[RW][TB], const FewSeg& s
     for (int u = 0; u < UNROLL; ++u) mma(bt, u);
   };
 
-  // whole-chunk loads need 16-byte aligned compressed rows for 2:4 weights
-  const bool aligned = WK != WK_SP24 || (kcv & 7) == 0;
+  // whole-chunk loads need 16-byte aligned compressed rows for 2:4 weights (8-byte for
+  // their e4m3 codes)
+  const bool aligned = !sp_kind(WK) || (kcv & 7) == 0;
   constexpr int STEP = CK * UNROLL;
   const int nb = aligned ? (k1 - k0) / STEP : 0;   // batches of whole chunks
   if (nb > 0) {
@@ -356,15 +403,24 @@ __device__ __forceinline__ void g2lds4(const void* g, void* lds) {
 }
 __device__ __forceinline__ int dswz(int r) { return (r >> 1) & 7; }
 
-template <int TB> struct Dma {
-  static constexpr int WPB = TB == 1 ? 16 : 8;   // waves per workgroup (LDS budget)
+template <int TB, int WK = WK_BF16> struct Dma {
+  // waves per workgroup (LDS budget: four ring stages per wave; e4m3 2:4 stages are larger)
+  static constexpr int WPB = TB == 1 ? (WK == WK_SP24F8 ? 12 : 16) : 8;
   static constexpr int RW = TB == 1 ? 1 : 2;     // 16-row tiles per wave (= rw_for)
 };
 template <int WK> struct DmaFmt {
-  static constexpr int U = WK == WK_FP8 ? 4 : 2;    // chunks per stage: one 128-byte row segment
-  static constexpr int BPE = WK == WK_BF16 ? 2 : 1; // weight bytes per reduction position
+  // chunks per stage: one 128-byte segment of every weight row
+  static constexpr int U = (WK == WK_FP8 || WK == WK_SP24F8) ? 4 : 2;
+  // weight bytes of reduction positions [0, kpos) of a row
+  static __device__ __forceinline__ int64_t off(int kpos) {
+    return WK == WK_BF16 ? 2 * (int64_t)kpos : WK == WK_SP24F8 ? (int64_t)kpos / 2 : (int64_t)kpos;
+  }
 };
-constexpr int dma_stage_bytes(int rw, int wk) { return rw * (2048 + (wk == WK_SP24 ? 256 : 0)); }
+// a wave's ring stage: RW tiles of 16 rows x 128 bytes, then the 2-bit positions of the
+// stage (16 bytes per row for bf16 2:4 values, 32 for their e4m3 codes)
+constexpr int dma_stage_bytes(int rw, int wk) {
+  return rw * (2048 + (wk == WK_SP24 ? 256 : wk == WK_SP24F8 ? 512 : 0));
+}
 
 // XS: the segment's X row (T == 1) is staged in LDS at xs.  `pre` runs before the first
 // weight stages are requested and `mid(n)` after them, n = the requests this wave issued
@@ -377,8 +433,8 @@ __device__ __forceinline__ void stream_dma(f32x4 (&acc)[RW][TB], const FewSeg& s
                                            const uint16_t* xs, Pre&& pre, Mid&& mid) {
   constexpr int CK = Chunk<WK>::K;
   constexpr int U = DmaFmt<WK>::U;
-  constexpr int BPE = DmaFmt<WK>::BPE;
   constexpr int SK = U * CK;   // reduction positions per stage (128 bytes of every weight row)
+  constexpr int MB = WK == WK_SP24F8 ? 512 : 256;   // position bytes per tile per stage
   const int fr = lane & 15, fq = lane >> 4;
   const int kcv = (int)(sg.k / 2);
   const int mstride = (int)((sg.k + 7) >> 3);
@@ -386,6 +442,7 @@ __device__ __forceinline__ void stream_dma(f32x4 (&acc)[RW][TB], const FewSeg& s
     o = o < O ? o : O - 1;
     if constexpr (WK == WK_BF16) return reinterpret_cast<const uint8_t*>(sg.w) + o * sg.ldw * 2;
     else if constexpr (WK == WK_FP8) return reinterpret_cast<const uint8_t*>(sg.w) + o * sg.ldw;
+    else if constexpr (WK == WK_SP24F8) return reinterpret_cast<const uint8_t*>(sg.w) + o * (int64_t)kcv;
     else return reinterpret_cast<const uint8_t*>(sg.w) + o * (int64_t)kcv * 2;
   };
   // DMA sources: tile i, half h -> row 8h + lane/8, logical piece (lane&7) ^ swizzle
@@ -398,7 +455,7 @@ __device__ __forceinline__ void stream_dma(f32x4 (&acc)[RW][TB], const FewSeg& s
       const int r = 8 * h + (lane >> 3);
       dsrc[i][h] = row_ptr(rbase + 16 * i + r) + 16 * ((lane & 7) ^ dswz(r));
     }
-    if constexpr (WK == WK_SP24) {
+    if constexpr (sp_kind(WK)) {
       int64_t o = rbase + 16 * i + (lane >> 2);
       o = o < O ? o : O - 1;
       msrc[i] = sg.w_meta + o * (int64_t)mstride + 4 * (lane & 3);
@@ -408,16 +465,18 @@ __device__ __forceinline__ void stream_dma(f32x4 (&acc)[RW][TB], const FewSeg& s
 #pragma unroll
   for (int j = 0; j < TB; ++j) {
     const int64_t t = 16 * j + fr;
-    xrow[j] = XS ? xs : sg.x + (t < T ? t : T - 1) * sg.ldx;
+    xrow[j] = XS ? xs : x_row<XL>(sg, t < T ? t : T - 1);
   }
 
   auto issue_w = [&](unsigned char* R, int st) {
     const int kpos = k0 + st * SK;
 #pragma unroll
     for (int i = 0; i < RW; ++i) {
-      g2lds16(dsrc[i][0] + (int64_t)kpos * BPE, R + i * 2048);
-      g2lds16(dsrc[i][1] + (int64_t)kpos * BPE, R + i * 2048 + 1024);
-      if constexpr (WK == WK_SP24) g2lds4(msrc[i] + (kpos >> 3), R + RW * 2048 + i * 256);
+      g2lds16(dsrc[i][0] + DmaFmt<WK>::off(kpos), R + i * 2048);
+      g2lds16(dsrc[i][1] + DmaFmt<WK>::off(kpos), R + i * 2048 + 1024);
+      // positions: 16 rows x 16 bytes per request (lane -> row lane / 4, bytes 4 (lane % 4))
+      if constexpr (sp_kind(WK)) g2lds4(msrc[i] + (kpos >> 3), R + RW * 2048 + i * MB);
+      if constexpr (WK == WK_SP24F8) g2lds4(msrc[i] + (kpos >> 3) + 16, R + RW * 2048 + i * MB + 256);
     }
   };
   struct XB {
@@ -431,7 +490,7 @@ __device__ __forceinline__ void stream_dma(f32x4 (&acc)[RW][TB], const FewSeg& s
 #pragma unroll
       for (int j = 0; j < TB; ++j) {
         xb.xl[u][j] = load_x8<XL, NS, false>(xrow[j], kpos + u * CK + 8 * fq, 0);
-        if constexpr (WK == WK_SP24) xb.xh[u][j] = load_x8<XL, NS, false>(xrow[j], kpos + u * CK + 32 + 8 * fq, 0);
+        if constexpr (sp_kind(WK)) xb.xh[u][j] = load_x8<XL, NS, false>(xrow[j], kpos + u * CK + 32 + 8 * fq, 0);
       }
   };
   // XS: the stage about to be read has landed once at most `later` stages' requests
@@ -439,7 +498,7 @@ __device__ __forceinline__ void stream_dma(f32x4 (&acc)[RW][TB], const FewSeg& s
   // which are requested after their stage's weights, order the LDS reads; with X in LDS
   // nothing would, and the compiler does not order LDS reads after direct-to-LDS loads
   // on every path, so the waits are explicit.
-  constexpr int OPS = 2 * RW + (WK == WK_SP24 ? RW : 0);   // requests per stage
+  constexpr int OPS = 2 * RW + (WK == WK_SP24 ? RW : WK == WK_SP24F8 ? 2 * RW : 0);   // requests per stage
   auto stage_ready = [&](auto later) {
     if constexpr (XS) {
       constexpr int n = decltype(later)::value * OPS;
@@ -459,7 +518,8 @@ __device__ __forceinline__ void stream_dma(f32x4 (&acc)[RW][TB], const FewSeg& s
 #pragma unroll
       for (int i = 0; i < RW; ++i) {
         const unsigned char* tile = R + i * 2048 + (fr >> 3) * 1024 + (fr & 7) * 128;
-        if constexpr (WK == WK_FP8) {
+        if constexpr (WK == WK_FP8 || WK == WK_SP24F8) {
+          // 8 codes (fp8 dense: positions 8 fq of chunk u; e4m3 2:4: values 8 fq of chunk u)
           const int pc = 2 * u + (fq >> 1);
           const uint2 q = *reinterpret_cast<const uint2*>(tile + 16 * (pc ^ dswz(fr)) + 8 * (fq & 1));
           uint32_t c0, c1, c2, c3;
@@ -472,10 +532,13 @@ __device__ __forceinline__ void stream_dma(f32x4 (&acc)[RW][TB], const FewSeg& s
         }
         if constexpr (WK == WK_SP24)
           meta[i] = *reinterpret_cast<const uint16_t*>(R + RW * 2048 + i * 256 + fr * 16 + 8 * u + 2 * fq);
+        if constexpr (WK == WK_SP24F8)   // chunks 0-1 in the first 256 bytes, 2-3 in the second
+          meta[i] = *reinterpret_cast<const uint16_t*>(R + RW * 2048 + i * MB + (u >> 1) * 256 + fr * 16 +
+                                                       8 * (u & 1) + 2 * fq);
       }
 #pragma unroll
       for (int j = 0; j < TB; ++j) {
-        if constexpr (WK == WK_SP24) {
+        if constexpr (sp_kind(WK)) {
           const u32x4 lo = xb.xl[u][j], hi = xb.xh[u][j];
           const u32x8 bb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           const bf16x16 bv = __builtin_bit_cast(bf16x16, bb);
@@ -494,7 +557,7 @@ __device__ __forceinline__ void stream_dma(f32x4 (&acc)[RW][TB], const FewSeg& s
   };
 
   // whole stages need 16-byte aligned compressed rows and 4-byte aligned metadata rows
-  const bool aligned = WK != WK_SP24 || ((kcv & 7) == 0 && (mstride & 3) == 0);
+  const bool aligned = !sp_kind(WK) || (((WK == WK_SP24F8 ? kcv : 2 * kcv) & 15) == 0 && (mstride & 3) == 0);
   const int ns = (aligned && k0 < k1) ? (k1 - k0) / SK : 0;
   pre();
   if (ns > 0) {
@@ -593,11 +656,11 @@ __device__ __forceinline__ void stage_row_dma(const uint16_t* __restrict__ src, 
 // workgroup keeps the SELM/2 largest magnitudes of each SELM-group in place (the select
 // pass's ranking, ties to the lower index) before the first multiply.
 template <int TB, int WK0, int XL0, int NS, int WK1, bool XS, int SELM = 0>
-__global__ __launch_bounds__(64 * Dma<TB>::WPB) void k_fewd(FewSeg s0, FewSeg s1, Epi epi,
+__global__ __launch_bounds__((64 * Dma<TB, WK0>::WPB)) void k_fewd(FewSeg s0, FewSeg s1, Epi epi,
                                                            int64_t T, int64_t O, float* __restrict__ y, int64_t ldy,
                                                            int accumulate, float* __restrict__ part, int splits,
                                                            int xn0, int xn1) {
-  constexpr int RW = Dma<TB>::RW, WPB = Dma<TB>::WPB;
+  constexpr int RW = Dma<TB, WK0>::RW, WPB = Dma<TB, WK0>::WPB;
   constexpr int STAGE = dma_stage_bytes(RW, WK0);   // the first segment's kind is the larger one
   static_assert(WK1 == WK_NONE || dma_stage_bytes(RW, WK1) <= STAGE, "stage size");
   static_assert(STAGE >= TB * 1024, "reduction buffer reuses stage 0");
@@ -635,8 +698,10 @@ __global__ __launch_bounds__(64 * Dma<TB>::WPB) void k_fewd(FewSeg s0, FewSeg s1
     // them are in flight; then the barrier makes every wave's X visible
     auto mid = [&](int n) {
       if constexpr (XS) {
-        switch (n) {   // 0 to 3 stages of 2 or 3 requests
+        switch (n) {   // 0 to 3 stages of 2, 3 or 4 requests
+          case 12: __builtin_amdgcn_s_waitcnt(vm_wait(12)); break;
           case 9: __builtin_amdgcn_s_waitcnt(vm_wait(9)); break;
+          case 8: __builtin_amdgcn_s_waitcnt(vm_wait(8)); break;
           case 6: __builtin_amdgcn_s_waitcnt(vm_wait(6)); break;
           case 4: __builtin_amdgcn_s_waitcnt(vm_wait(4)); break;
           case 3: __builtin_amdgcn_s_waitcnt(vm_wait(3)); break;
@@ -1024,10 +1089,10 @@ Plan make_plan(const FewArgs& a, bool allow_split) {
   p.rw = rw_for(p.tb, a.seg[0].w_kind);
   // waves per workgroup: LDS rings bound the direct-to-LDS kernels (16 waves for one token
   // block, 8 for two); 4 measured best for the register kernel at four token blocks
-  const int max_wpb = p.tb == 1 ? 16 : p.tb == 4 ? 4 : 8;
+  const int max_wpb = p.tb == 1 ? (a.seg[0].w_kind == WK_SP24F8 ? Dma<1, WK_SP24F8>::WPB : 16) : p.tb == 4 ? 4 : 8;
   int64_t chunks = 0;   // chunks of the longest segment
   for (int i = 0; i < a.nseg; ++i) {
-    const int ck = a.seg[i].w_kind == WK_SP24 ? 64 : 32;
+    const int ck = sp_kind(a.seg[i].w_kind) ? 64 : 32;
     const int64_t c = (a.seg[i].k + ck - 1) / ck;
     chunks = c > chunks ? c : chunks;
   }
@@ -1064,16 +1129,18 @@ hipError_t launch_k(const FewArgs& a, const Plan& p, float* part, hipStream_t s)
   const FewSeg s1 = a.nseg > 1 ? a.seg[1] : FewSeg{};
   float* pp = p.splits > 1 ? part : nullptr;
   if constexpr (TB <= 2) {
-    static_assert(RW == Dma<TB>::RW, "row tiles");
-    if (p.wpb > Dma<TB>::WPB) return hipErrorInvalidConfiguration;
+    static_assert(RW == Dma<TB, WK0>::RW, "row tiles");
+    if (p.wpb > Dma<TB, WK0>::WPB) return hipErrorInvalidConfiguration;
     if constexpr (TB == 1) {
       // one token: stage the X rows in LDS next to the weight rings when they fit
       // (the NM_ROUTE_NO_XLDS hint keeps the register loads)
       // rows of whole 16-byte pieces from 16-byte aligned starts, staged in whole KiB
-      const int64_t xn0 = XL0 == XL_LIFT ? a.seg[0].k / (4 * (NS - 1)) * (2 * NS) : a.seg[0].k;
+      // (in 2-byte units: an e4m3 row of k codes is k / 2 of them)
+      const int64_t xn0 = XL0 == XL_LIFT ? a.seg[0].k / (4 * (NS - 1)) * (2 * NS)
+                                         : XL0 == XL_F8 ? a.seg[0].k / 2 : a.seg[0].k;
       const int64_t xn1 = a.nseg > 1 ? a.seg[1].k : 0;
       const int64_t xbytes = (((xn0 + 511) >> 9) + ((xn1 + 511) >> 9)) * 1024;
-      const int64_t ring = 4LL * Dma<TB>::WPB * dma_stage_bytes(RW, WK0);
+      const int64_t ring = 4LL * Dma<TB, WK0>::WPB * dma_stage_bytes(RW, WK0);
       auto piece_ok = [](const uint16_t* x, int64_t n) {
         return n == 0 || (n >= 8 && (n % 8) == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0);
       };
@@ -1095,14 +1162,14 @@ hipError_t launch_k(const FewArgs& a, const Plan& p, float* part, hipStream_t s)
         hipError_t ae = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)xbytes);
         if (ae != hipSuccess) return ae;
         a.route.note(NM_TAKEN_FEW_STREAM | NM_TAKEN_FEW_XLDS | (a.sel_m != 0 ? NM_TAKEN_FEW_SELECT : 0u) |
-                     (WK0 == WK_SP24 ? NM_TAKEN_SPARSE_MMA : 0u));
+                     (sp_kind(WK0) ? NM_TAKEN_SPARSE_MMA : 0u));
         kern<<<dim3((unsigned)blocks), dim3(64 * p.wpb), (size_t)xbytes, s>>>(
             a.seg[0], s1, a.epi(), a.t, a.o, a.y, a.ldy, a.accumulate, pp, (int)p.splits, (int)xn0, (int)xn1);
         return hipGetLastError();
       }
     }
     if (a.sel_m != 0) return hipErrorInvalidValue;   // selection needs the staged row
-    a.route.note(NM_TAKEN_FEW_STREAM | (WK0 == WK_SP24 ? NM_TAKEN_SPARSE_MMA : 0u));
+    a.route.note(NM_TAKEN_FEW_STREAM | (sp_kind(WK0) ? NM_TAKEN_SPARSE_MMA : 0u));
     k_fewd<TB, WK0, XL0, NS, WK1, false><<<dim3((unsigned)blocks), dim3(64 * p.wpb), 0, s>>>(
         a.seg[0], s1, a.epi(), a.t, a.o, a.y, a.ldy, a.accumulate, pp, (int)p.splits, 0, 0);
   } else {
@@ -1113,7 +1180,7 @@ hipError_t launch_k(const FewArgs& a, const Plan& p, float* part, hipStream_t s)
       if (e != hipSuccess) return e;
     }
     if (a.sel_m != 0) return hipErrorInvalidValue;
-    a.route.note(NM_TAKEN_FEW_STREAM | (WK0 == WK_SP24 ? NM_TAKEN_SPARSE_MMA : 0u));
+    a.route.note(NM_TAKEN_FEW_STREAM | (sp_kind(WK0) ? NM_TAKEN_SPARSE_MMA : 0u));
     kern<<<dim3((unsigned)blocks), dim3(64 * p.wpb), lds, s>>>(a.seg[0], s1, a.epi(), a.t, a.o, a.y, a.ldy,
                                                                a.accumulate, pp, (int)p.splits);
   }
@@ -1189,6 +1256,8 @@ hipError_t launch_few(const FewArgs& a, float* part, int64_t part_bytes, hipStre
     e = launch_tb<WK_SP24, XL_PLAIN, 0, WK_NONE>(a, p, part, s);
   } else if (s0.w_kind == WK_SP24 && s0.loader == XL_LIFT) {
     e = launch_lift(a, p, part, s);
+  } else if (s0.w_kind == WK_SP24F8 && s0.loader == XL_F8 && p.tb == 1) {
+    e = launch_k<1, WK_SP24F8, XL_F8, 0, WK_NONE>(a, p, part, s);
   }
   if (e != hipSuccess || p.splits == 1) return e;
   return launch_reduce_parts(part, p.splits, a.epi(), a.t, a.o, a.y, a.ldy, a.accumulate, a.route, s);

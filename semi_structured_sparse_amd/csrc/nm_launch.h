@@ -108,7 +108,9 @@ hipError_t launch_gemm_lds_small(const GemmArgs& a, float* part, int64_t part_by
 // 2:4 sparse-operand GEMM on the gfx950 sparse matrix instructions.  The sparse
 // operand is W (values [O][kc/2], 2-bit meta [O][ceil(kc/8)]) over a (possibly lowered)
 // reduction length kc; the dense operand is X, read plainly or lifted.
-enum XLoader { XL_PLAIN = 0, XL_LIFT = 1 };
+// XL_F8: the X rows are e4m3 codes, one byte per position (x as bytes, ldx in bytes),
+// widened to bf16 (exactly) as they are loaded.
+enum XLoader { XL_PLAIN = 0, XL_LIFT = 1, XL_F8 = 2 };
 struct SparseArgs {
   const uint16_t* w_vals;
   const uint8_t* w_meta;  // 2-bit
@@ -176,11 +178,12 @@ hipError_t launch_gemm_lds_sp_small(const SparseArgs& a, float* part, int64_t pa
 
 // Few-token streaming product (T <= 128): one or two weight segments summed into one
 // accumulator, then scaled (w_scale, per output row) and written or added to y.
-enum WKind { WK_BF16 = 0, WK_FP8 = 1, WK_SP24 = 2 };
+enum WKind { WK_BF16 = 0, WK_FP8 = 1, WK_SP24 = 2, WK_SP24F8 = 3 };
 struct FewSeg {
-  const void* w;          // WK_BF16 [o][ldw] bf16, WK_FP8 [o][ldw] bytes, WK_SP24 values [o][k/2]
+  const void* w;          // WK_BF16 [o][ldw] bf16, WK_FP8 [o][ldw] bytes, WK_SP24 values [o][k/2],
+                          // WK_SP24F8 e4m3 codes of the values [o][k/2] bytes
   int64_t ldw;
-  const uint8_t* w_meta;  // WK_SP24: 2-bit metadata [o][ceil(k/8)]
+  const uint8_t* w_meta;  // WK_SP24, WK_SP24F8: 2-bit metadata [o][ceil(k/8)]
   int w_kind;
   const uint16_t* x;      // X rows of this segment (first column of the segment)
   int64_t ldx;

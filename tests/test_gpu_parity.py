@@ -1156,7 +1156,7 @@ def run_w8a8(x, w8, idx, ws, o, k, ns, accumulate=0, y0=None, rows=None):
     nb = S.nm_spmm_workspace_size(a)
     wsb = empty((max(nb, 16),), np.uint8)
     a.workspace, a.workspace_bytes = wsb.data_ptr(), nb
-    S.nm_spmm(a)
+    spmm_call(a)
     sync()
     if rows is None:
         return host(y, np.float32)
@@ -1190,6 +1190,36 @@ def test_spmm_w8a8(ns, t, o):
     y0 = rng.standard_normal((t, o)).astype(np.float32)
     y2 = run_w8a8(x, w8, idx, ws, o, k, ns, accumulate=1, y0=y0)
     check_gemm_vals(y2.astype(np.float64) - y0, ref, a_v, b_v, label=f"w8a8 ns={ns} accumulate")
+
+
+@pytest.mark.parametrize("ns", [2, 4])
+@pytest.mark.parametrize("t,o", [(1, 264), (1, 100), (3, 264), (16, 520)])
+def test_spmm_w8a8_stream(ns, t, o):
+    """fp8 weights and per-token fp8 activations at up to 16 tokens: the quantizing pass,
+    then the weight-streaming kernel on the e4m3 2:4 codes (widened to bf16 after their
+    LDS read, the one-token X row staged in LDS), against the oracle and against the
+    split tile kernel on the fp8 instruction (the NM_ROUTE_FEW_TILE hint).  The reduction
+    (K' = 1152 or 1920) leaves half a stage for the register path."""
+    print(f"w8a8 stream ns={ns} t={t} o={o}", flush=True)
+    rng = np.random.default_rng(ns * 100 + t + o)
+    k = 1152 if ns == 2 else 1280
+    x = synth.student_t_bf16(rng, (t, k), 4.0, 0.5)
+    w8, idx, ws = w8a8_weights(rng, o, k, ns)
+    ref = O.spmm_w8a8_slide(x, w8, idx, ws, k, ns)
+    a_v, b_v = w8a8_operands(x, w8, idx, ws, k, ns)
+    y = run_w8a8(x, w8, idx, ws, o, k, ns)
+    tk = taken()
+    assert {"quant", "few_stream", "sparse_mma"} <= tk and "tile_split" not in tk, tk
+    if t == 1:
+        assert "few_xlds" in tk, tk
+    check_gemm_vals(y, ref, a_v, b_v, label=f"w8a8 stream ns={ns} t={t}")
+    y0 = rng.standard_normal((t, o)).astype(np.float32)
+    y2 = run_w8a8(x, w8, idx, ws, o, k, ns, accumulate=1, y0=y0)
+    check_gemm_vals(y2.astype(np.float64) - y0, ref, a_v, b_v, label=f"w8a8 stream ns={ns} t={t} accumulate")
+    with use_route("few_tile"):
+        yt = run_w8a8(x, w8, idx, ws, o, k, ns)
+        assert "few_stream" not in taken(), taken()
+    check_gemm_vals(yt, ref, a_v, b_v, label=f"w8a8 tile ns={ns} t={t}")
 
 
 def test_spmm_w8a8_full_size_sampled():
