@@ -321,8 +321,19 @@ nm_status w8a8_product(const nm_spmm_args* a, int64_t kc, int ns, hipStream_t s)
   char* ws = reinterpret_cast<char*>(a->workspace);
   uint8_t* xq = reinterpret_cast<uint8_t*>(ws + L.xq);
   float* xs = reinterpret_cast<float*>(ws + L.xs);
-  hipError_t e = nml::launch_quant_lift(a->mode == NM_W_SLIDE ? ns : 2, (const uint16_t*)a->x, a->t, a->k,
-                                        a->ldx, xq, kc, xs, s);
+  const int qns = a->mode == NM_W_SLIDE ? ns : 2;
+  {
+    // one token: the streaming kernel quantizes and lifts the row itself (no separate pass)
+    const nml::Route r = route_of(a, true);
+    if (w8a8_stream(a, r)) {
+      nml::FewArgs f = w8a8_few_args(a, kc, nullptr, xs, r);
+      f.seg[0].x = (const uint16_t*)a->x;
+      f.q_ns = qns;
+      if (nml::few_quant_in_kernel(f))
+        return hip_status(nml::launch_few(f, reinterpret_cast<float*>(ws + L.part), L.total - L.part, s));
+    }
+  }
+  hipError_t e = nml::launch_quant_lift(qns, (const uint16_t*)a->x, a->t, a->k, a->ldx, xq, kc, xs, s);
   if (e != hipSuccess) return NM_EHIP;
   nml::SparseArgs sa = w8a8_args(a, kc, xq, xs, true);
   sa.route.note(NM_TAKEN_QUANT | (a->mode == NM_W_SLIDE && ns > 2 ? NM_TAKEN_LIFT : 0u));

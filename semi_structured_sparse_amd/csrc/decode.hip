@@ -655,11 +655,11 @@ __device__ __forceinline__ void stage_row_dma(const uint16_t* __restrict__ src, 
 // SELM > 0 (with XS, one plain segment): the staged row is X itself; after it lands every
 // workgroup keeps the SELM/2 largest magnitudes of each SELM-group in place (the select
 // pass's ranking, ties to the lower index) before the first multiply.
-template <int TB, int WK0, int XL0, int NS, int WK1, bool XS, int SELM = 0>
+template <int TB, int WK0, int XL0, int NS, int WK1, bool XS, int SELM = 0, int QNS = 0>
 __global__ __launch_bounds__((64 * Dma<TB, WK0>::WPB)) void k_fewd(FewSeg s0, FewSeg s1, Epi epi,
                                                            int64_t T, int64_t O, float* __restrict__ y, int64_t ldy,
                                                            int accumulate, float* __restrict__ part, int splits,
-                                                           int xn0, int xn1) {
+                                                           int xn0, int xn1, float* __restrict__ q_out) {
   constexpr int RW = Dma<TB, WK0>::RW, WPB = Dma<TB, WK0>::WPB;
   constexpr int STAGE = dma_stage_bytes(RW, WK0);   // the first segment's kind is the larger one
   static_assert(WK1 == WK_NONE || dma_stage_bytes(RW, WK1) <= STAGE, "stage size");
@@ -685,6 +685,11 @@ __global__ __launch_bounds__((64 * Dma<TB, WK0>::WPB)) void k_fewd(FewSeg s0, Fe
   unsigned char* w3 = r3 + wave * STAGE;
   extern __shared__ __align__(16) uint16_t xs_lds[];
   const int off1 = ((xn0 + 511) >> 9) << 9;   // whole KiB per staged row
+  // QNS: the staged bf16 row (xn0 elements), then its lifted e4m3 codes (s0.k bytes, read
+  // by the stream), then 1 KiB for the maximum's reduction
+  static_assert(QNS == 0 || (XS && TB == 1 && WK0 == WK_SP24F8 && XL0 == XL_F8 && WK1 == WK_NONE), "quantize in LDS");
+  uint16_t* const xs_read = QNS > 0 ? xs_lds + off1 : xs_lds;
+  float qs = 1.f;   // QNS: the token scale
   {
     int k0, k1;
     part_range<WK0>(s0.k, p, P, k0, k1);
@@ -728,9 +733,51 @@ __global__ __launch_bounds__((64 * Dma<TB, WK0>::WPB)) void k_fewd(FewSeg s0, Fe
           __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS writes done
           __builtin_amdgcn_s_barrier();
         }
+        if constexpr (QNS > 0) {
+          // the row's largest magnitude pattern, the token's scales, then the codes (the
+          // quantizing pass's arithmetic), with the weight requests still in flight
+          uint32_t* red = reinterpret_cast<uint32_t*>(xs_lds + off1 + (((s0.k >> 1) + 511) >> 9 << 9));
+          uint32_t mk = 0;
+          for (int c = threadIdx.x; c < xn0 / 8; c += blockDim.x) {
+            const uint4 v = *reinterpret_cast<const uint4*>(xs_lds + 8 * c);
+            const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t lo = d[q] & 0x7FFFu, hi = (d[q] >> 16) & 0x7FFFu;
+              mk = lo > mk ? lo : mk;
+              mk = hi > mk ? hi : mk;
+            }
+          }
+#pragma unroll
+          for (int off = 32; off > 0; off >>= 1) {
+            const uint32_t o = (uint32_t)__shfl_xor((int)mk, off, 64);
+            mk = o > mk ? o : mk;
+          }
+          if (lane == 0) red[wave] = mk;
+          __builtin_amdgcn_s_waitcnt(0xC07F);
+          __builtin_amdgcn_s_barrier();
+          mk = red[0];
+          for (int w = 1; w < wpb; ++w) mk = red[w] > mk ? red[w] : mk;
+          float r;
+          token_scales(mk, r, qs);
+          if (blockIdx.x == 0 && threadIdx.x == 0 && q_out != nullptr) q_out[0] = qs;
+          constexpr int W = QNS - 1;
+          uint32_t* codes = reinterpret_cast<uint32_t*>(xs_read);
+          for (int g = threadIdx.x; g < xn0 / (2 * QNS); g += blockDim.x) {
+            uint32_t v16[2 * QNS];
+#pragma unroll
+            for (int i = 0; i < 2 * QNS; ++i) v16[i] = xs_lds[g * 2 * QNS + i];
+            uint32_t win[W];
+            quant_lift_group<QNS>(v16, r, win);
+#pragma unroll
+            for (int w = 0; w < W; ++w) codes[g * W + w] = win[w];
+          }
+          __builtin_amdgcn_s_waitcnt(0xC07F);
+          __builtin_amdgcn_s_barrier();
+        }
       }
     };
-    stream_dma<TB, RW, WK0, XL0, NS, XS>(acc, s0, ob * RB, O, T, k0, k1, lane, w0, w1, w2, w3, xs_lds, pre, mid);
+    stream_dma<TB, RW, WK0, XL0, NS, XS>(acc, s0, ob * RB, O, T, k0, k1, lane, w0, w1, w2, w3, xs_read, pre, mid);
   }
   if constexpr (WK1 != WK_NONE) {
     int k0, k1;
@@ -757,6 +804,13 @@ __global__ __launch_bounds__((64 * Dma<TB, WK0>::WPB)) void k_fewd(FewSeg s0, Fe
         if (t >= T || o >= O) continue;
         if (part != nullptr) {
           part[((int64_t)split * T + t) * O + o] = sum;
+        } else if constexpr (QNS > 0) {
+          // the token scale from LDS (row_scale[0] is written by workgroup 0 for the reduction)
+          Epi e = epi;
+          e.row_scale = nullptr;
+          float v = qs * epi_apply(e, sum, t, o);
+          if (accumulate) v += y[t * ldy + o];
+          y[t * ldy + o] = v;
         } else {
           float v = epi_apply(epi, sum, t, o);
           if (accumulate) v += y[t * ldy + o];
@@ -1135,11 +1189,15 @@ hipError_t launch_k(const FewArgs& a, const Plan& p, float* part, hipStream_t s)
       // one token: stage the X rows in LDS next to the weight rings when they fit
       // (the NM_ROUTE_NO_XLDS hint keeps the register loads)
       // rows of whole 16-byte pieces from 16-byte aligned starts, staged in whole KiB
-      // (in 2-byte units: an e4m3 row of k codes is k / 2 of them)
+      // (in 2-byte units: an e4m3 row of k codes is k / 2 of them; quantized in the kernel:
+      // the bf16 row, then its codes and 1 KiB for the maximum)
+      const int qn = XL0 == XL_F8 ? a.q_ns : 0;
       const int64_t xn0 = XL0 == XL_LIFT ? a.seg[0].k / (4 * (NS - 1)) * (2 * NS)
-                                         : XL0 == XL_F8 ? a.seg[0].k / 2 : a.seg[0].k;
+                          : qn > 0       ? a.seg[0].k / (4 * (qn - 1)) * (2 * qn)
+                          : XL0 == XL_F8 ? a.seg[0].k / 2
+                                         : a.seg[0].k;
       const int64_t xn1 = a.nseg > 1 ? a.seg[1].k : 0;
-      const int64_t xbytes = (((xn0 + 511) >> 9) + ((xn1 + 511) >> 9)) * 1024;
+      const int64_t xbytes = (((xn0 + 511) >> 9) + ((xn1 + 511) >> 9) + (qn > 0 ? ((a.seg[0].k / 2 + 511) >> 9) + 1 : 0)) * 1024;
       const int64_t ring = 4LL * Dma<TB, WK0>::WPB * dma_stage_bytes(RW, WK0);
       auto piece_ok = [](const uint16_t* x, int64_t n) {
         return n == 0 || (n >= 8 && (n % 8) == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0);
@@ -1147,6 +1205,19 @@ hipError_t launch_k(const FewArgs& a, const Plan& p, float* part, hipStream_t s)
       const bool rows_ok = piece_ok(a.seg[0].x, xn0) && (a.nseg < 2 || piece_ok(a.seg[1].x, xn1)) && xn0 > 0;
       if (a.t == 1 && rows_ok && ring + xbytes <= 163840 && !a.route.has(NM_ROUTE_NO_XLDS)) {
         auto kern = k_fewd<TB, WK0, XL0, NS, WK1, true>;
+        if constexpr (WK0 == WK_SP24F8 && XL0 == XL_F8 && WK1 == WK_NONE) {
+          switch (qn) {
+            case 0: break;
+            case 2: kern = k_fewd<TB, WK0, XL0, NS, WK1, true, 0, 2>; break;
+            case 3: kern = k_fewd<TB, WK0, XL0, NS, WK1, true, 0, 3>; break;
+            case 4: kern = k_fewd<TB, WK0, XL0, NS, WK1, true, 0, 4>; break;
+            case 5: kern = k_fewd<TB, WK0, XL0, NS, WK1, true, 0, 5>; break;
+            case 6: kern = k_fewd<TB, WK0, XL0, NS, WK1, true, 0, 6>; break;
+            case 7: kern = k_fewd<TB, WK0, XL0, NS, WK1, true, 0, 7>; break;
+            case 8: kern = k_fewd<TB, WK0, XL0, NS, WK1, true, 0, 8>; break;
+            default: return hipErrorInvalidValue;
+          }
+        }
         if constexpr (XL0 == XL_PLAIN && WK1 == WK_NONE && (WK0 == WK_BF16 || WK0 == WK_FP8)) {
           switch (a.sel_m) {
             case 0: break;
@@ -1162,16 +1233,17 @@ hipError_t launch_k(const FewArgs& a, const Plan& p, float* part, hipStream_t s)
         hipError_t ae = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)xbytes);
         if (ae != hipSuccess) return ae;
         a.route.note(NM_TAKEN_FEW_STREAM | NM_TAKEN_FEW_XLDS | (a.sel_m != 0 ? NM_TAKEN_FEW_SELECT : 0u) |
-                     (sp_kind(WK0) ? NM_TAKEN_SPARSE_MMA : 0u));
+                     (sp_kind(WK0) ? NM_TAKEN_SPARSE_MMA : 0u) | (qn > 0 ? NM_TAKEN_QUANT : 0u));
         kern<<<dim3((unsigned)blocks), dim3(64 * p.wpb), (size_t)xbytes, s>>>(
-            a.seg[0], s1, a.epi(), a.t, a.o, a.y, a.ldy, a.accumulate, pp, (int)p.splits, (int)xn0, (int)xn1);
+            a.seg[0], s1, a.epi(), a.t, a.o, a.y, a.ldy, a.accumulate, pp, (int)p.splits, (int)xn0, (int)xn1,
+            qn > 0 ? const_cast<float*>(a.row_scale) : nullptr);
         return hipGetLastError();
       }
     }
-    if (a.sel_m != 0) return hipErrorInvalidValue;   // selection needs the staged row
+    if (a.sel_m != 0 || a.q_ns != 0) return hipErrorInvalidValue;   // these need the staged row
     a.route.note(NM_TAKEN_FEW_STREAM | (sp_kind(WK0) ? NM_TAKEN_SPARSE_MMA : 0u));
     k_fewd<TB, WK0, XL0, NS, WK1, false><<<dim3((unsigned)blocks), dim3(64 * p.wpb), 0, s>>>(
-        a.seg[0], s1, a.epi(), a.t, a.o, a.y, a.ldy, a.accumulate, pp, (int)p.splits, 0, 0);
+        a.seg[0], s1, a.epi(), a.t, a.o, a.y, a.ldy, a.accumulate, pp, (int)p.splits, 0, 0, nullptr);
   } else {
     auto kern = k_few<TB, RW, WK0, XL0, NS, WK1>;
     const size_t lds = (size_t)p.wpb * TB * 1024;
@@ -1179,7 +1251,7 @@ hipError_t launch_k(const FewArgs& a, const Plan& p, float* part, hipStream_t s)
       hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
     }
-    if (a.sel_m != 0) return hipErrorInvalidValue;
+    if (a.sel_m != 0 || a.q_ns != 0) return hipErrorInvalidValue;
     a.route.note(NM_TAKEN_FEW_STREAM | (sp_kind(WK0) ? NM_TAKEN_SPARSE_MMA : 0u));
     kern<<<dim3((unsigned)blocks), dim3(64 * p.wpb), lds, s>>>(a.seg[0], s1, a.epi(), a.t, a.o, a.y, a.ldy,
                                                                a.accumulate, pp, (int)p.splits);
@@ -1235,12 +1307,28 @@ bool few_select_in_kernel(const FewArgs& a) {
   return make_plan(a, true).tb == 1;
 }
 
+bool few_quant_in_kernel(const FewArgs& a) {
+  if (a.route.has(NM_ROUTE_NO_XLDS)) return false;
+  if (a.t != 1 || a.nseg != 1 || a.o <= 0 || a.sel_m != 0) return false;
+  const FewSeg& sg = a.seg[0];
+  const int q = a.q_ns;
+  if (sg.w_kind != WK_SP24F8 || sg.loader != XL_F8 || q < 2 || q > 8 || a.row_scale == nullptr) return false;
+  if (sg.k <= 0 || sg.k % (4 * (q - 1)) != 0) return false;
+  const int64_t kx = sg.k / (4 * (q - 1)) * (2 * q);   // the bf16 row's length
+  if (kx < 8 || kx % 8 != 0 || (reinterpret_cast<uintptr_t>(sg.x) & 15) != 0) return false;
+  const int64_t xbytes = (((kx + 511) >> 9) + ((sg.k / 2 + 511) >> 9) + 1) * 1024;
+  const int64_t ring = 4LL * Dma<1, WK_SP24F8>::WPB * dma_stage_bytes(1, WK_SP24F8);
+  if (ring + xbytes > 163840) return false;
+  return make_plan(a, true).tb == 1;
+}
+
 hipError_t launch_few(const FewArgs& a, float* part, int64_t part_bytes, hipStream_t s) {
   if (a.t > 128 || a.nseg < 1 || a.nseg > 2) return hipErrorInvalidValue;
   for (int i = 0; i < a.nseg; ++i)   // reduction indices are 32-bit inside the kernel
     if (a.seg[i].k > 0x3FFFFFFF) return hipErrorInvalidValue;
   if (a.t == 0 || a.o == 0) return hipSuccess;
   if (a.sel_m != 0 && !few_select_in_kernel(a)) return hipErrorInvalidValue;
+  if (a.q_ns != 0 && !few_quant_in_kernel(a)) return hipErrorInvalidValue;
   Plan p = make_plan(a, part != nullptr);
   if (p.splits > 1 && part_bytes < p.splits * a.t * a.o * 4) p = make_plan(a, false);
   const FewSeg& s0 = a.seg[0];

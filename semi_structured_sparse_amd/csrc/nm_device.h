@@ -201,6 +201,52 @@ __device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t q, uint32_t& lo, uint32
   hi = __builtin_amdgcn_perm(__float_as_uint(b.y), __float_as_uint(b.x), 0x07060302u);
 }
 
+// ---------------------------------------------------------------------------------
+// Per-token e4m3 quantization (the fp8 x fp8 lowered product; shared by the quantizing
+// pass and the one-token weight-streaming kernel, so both produce the same codes).
+// ---------------------------------------------------------------------------------
+
+// e4m3fn code of v (|v| <= 448, finite), round to nearest, ties to even: in the normal
+// range the 23 fraction bits are rounded to 3 (a carry moves to the next exponent), below
+// 2^-6 the value is rounded to a multiple of the subnormal step 2^-9 (q = 8 is code 0x08,
+// the smallest normal).
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const uint32_t a = b & 0x7FFFFFFFu;
+  if (__uint_as_float(a) >= 0x1p-6f) {
+    int e = (int)(a >> 23) - 127;
+    uint32_t m3 = (a >> 20) & 7u;
+    const uint32_t rem = a & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) ++m3;
+    if (m3 == 8u) { m3 = 0u; ++e; }
+    return sign | ((uint32_t)(e + 7) << 3) | m3;
+  }
+  return sign | (uint32_t)rintf(__uint_as_float(a) * 512.0f);
+}
+
+// From the row's largest 15-bit magnitude pattern mk: r = fp32(448 / amax) scales the
+// values to codes, s = fp32(amax / 448) is the token scale (both 1 for an all-zero row).
+__device__ __forceinline__ void token_scales(uint32_t mk, float& r, float& s) {
+  const float amax = __uint_as_float(mk << 16);
+  r = mk == 0 ? 1.0f : 448.0f / amax;
+  s = mk == 0 ? 1.0f : amax / 448.0f;
+}
+
+// One group of 2 NS bf16 values (low 16 bits of v16) -> e4m3(clamp(x r, +-448)), lifted:
+// window w (one dword) holds the codes of values 2w .. 2w + 3 (NS = 2: the group itself).
+template <int NS>
+__device__ __forceinline__ void quant_lift_group(const uint32_t (&v16)[2 * NS], float r, uint32_t (&win)[NS - 1]) {
+  uint32_t q[2 * NS];
+#pragma unroll
+  for (int i = 0; i < 2 * NS; ++i) {
+    const float v = __uint_as_float(v16[i] << 16) * r;
+    q[i] = e4m3_rne(fminf(fmaxf(v, -448.0f), 448.0f));
+  }
+#pragma unroll
+  for (int w = 0; w < NS - 1; ++w) win[w] = q[2 * w] | (q[2 * w + 1] << 8) | (q[2 * w + 2] << 16) | (q[2 * w + 3] << 24);
+}
+
 // K-loop over n >= 1 steps through NST >= 3 LDS stages (distinct static arrays A[j], B[j],
 // j < NST, named by constant indices so the compiler tracks the direct-to-LDS loads into
 // each one).  issue(a, b, s) enqueues at least L direct-to-LDS requests per wave for step s

@@ -199,6 +199,9 @@ struct FewArgs {
   int64_t ldy;
   int accumulate;
   int sel_m;              // > 0: seg[0].x is X itself; keep the m/2 largest of every m (see below)
+  int q_ns;               // > 0 (one token, seg[0] e4m3 2:4 with the XL_F8 loader): seg[0].x is the
+                          // bf16 X row itself; the kernel quantizes it to e4m3 per token and lifts it
+                          // (NS = q_ns) in LDS, applies the token scale, and writes it to row_scale[0]
   Route route;
   const float* row_scale; // optional epilogue terms (Epi)
   const float* row_shift;
@@ -210,6 +213,9 @@ struct FewArgs {
 // staged in LDS), so that no separate select pass is needed (never under the
 // NM_ROUTE_NO_FEW_SELECT or NM_ROUTE_NO_XLDS hints).
 bool few_select_in_kernel(const FewArgs& a);
+// One token, one e4m3 2:4 segment (XL_F8): whether launch_few can quantize and lift the
+// bf16 X row inside the product (q_ns > 0; the raw row and its codes staged in LDS).
+bool few_quant_in_kernel(const FewArgs& a);
 // Scratch bytes of fp32 partial sums the preferred launch uses (0: single pass).
 int64_t few_partial_bytes(const FewArgs& a);
 // part: scratch of part_bytes bytes or null; with less than few_partial_bytes(a) the

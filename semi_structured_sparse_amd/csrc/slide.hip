@@ -12,6 +12,8 @@
 
 namespace {
 
+using namespace nmk;
+
 // One thread lowers two consecutive groups of one row, so that its 2-bit metadata
 // output (4(N-1) slots = N-1 bytes) never shares a byte with another thread.
 template <int NS>
@@ -96,25 +98,6 @@ __global__ __launch_bounds__(256) void k_lift(const uint16_t* __restrict__ x, in
     for (int s = 0; s < 4; ++s) dst[4 * w + s] = src[2 * w + s];
 }
 
-// e4m3fn code of v (|v| <= 448, finite), round to nearest, ties to even: in the normal
-// range the 23 fraction bits are rounded to 3 (a carry moves to the next exponent), below
-// 2^-6 the value is rounded to a multiple of the subnormal step 2^-9 (q = 8 is code 0x08,
-// the smallest normal).
-__device__ __forceinline__ uint32_t e4m3_rne(float v) {
-  const uint32_t b = __float_as_uint(v);
-  const uint32_t sign = (b >> 24) & 0x80u;
-  const uint32_t a = b & 0x7FFFFFFFu;
-  if (__uint_as_float(a) >= 0x1p-6f) {
-    int e = (int)(a >> 23) - 127;
-    uint32_t m3 = (a >> 20) & 7u;
-    const uint32_t rem = a & 0xFFFFFu;
-    if (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) ++m3;
-    if (m3 == 8u) { m3 = 0u; ++e; }
-    return sign | ((uint32_t)(e + 7) << 3) | m3;
-  }
-  return sign | (uint32_t)rintf(__uint_as_float(a) * 512.0f);
-}
-
 // Per-token fp8 quantization fused with the lift (SlideSparse page, technical summary
 // 2.B: the online step quantizes the activations and expands them for the lowered
 // weights in one pass).  One workgroup per token row: the row's magnitude maximum (on
@@ -161,9 +144,9 @@ __global__ __launch_bounds__(256) void k_quant_lift(const uint16_t* __restrict__
   mk = red[0];
 #pragma unroll
   for (int w = 1; w < 4; ++w) mk = red[w] > mk ? red[w] : mk;
-  const float amax = __uint_as_float(mk << 16);
-  const float r = mk == 0 ? 1.0f : 448.0f / amax;
-  if (tid == 0) xs[row] = mk == 0 ? 1.0f : amax / 448.0f;
+  float r, st;
+  token_scales(mk, r, st);
+  if (tid == 0) xs[row] = st;
   const int64_t G = k / (2 * NS);
   for (int64_t g = tid; g < G; g += 256) {
     uint32_t v16[2 * NS];
@@ -176,17 +159,11 @@ __global__ __launch_bounds__(256) void k_quant_lift(const uint16_t* __restrict__
 #pragma unroll
       for (int i = 0; i < 2 * NS; ++i) v16[i] = xr[g * 2 * NS + i];
     }
-    uint32_t q[2 * NS];
-#pragma unroll
-    for (int i = 0; i < 2 * NS; ++i) {
-      const float v = __uint_as_float(v16[i] << 16) * r;
-      q[i] = e4m3_rne(fminf(fmaxf(v, -448.0f), 448.0f));
-    }
-    // 4 (NS - 1) lifted codes = NS - 1 dwords, one per window
+    uint32_t win[W];
+    quant_lift_group<NS>(v16, r, win);
     uint32_t* dst = reinterpret_cast<uint32_t*>(qr + g * 4 * W);
 #pragma unroll
-    for (int w = 0; w < W; ++w)
-      dst[w] = q[2 * w] | (q[2 * w + 1] << 8) | (q[2 * w + 2] << 16) | (q[2 * w + 3] << 24);
+    for (int w = 0; w < W; ++w) dst[w] = win[w];
   }
   for (int64_t i = G * 4 * W + tid; i < ldq; i += 256) qr[i] = 0;
 }

@@ -1220,6 +1220,14 @@ def test_spmm_w8a8_stream(ns, t, o):
         yt = run_w8a8(x, w8, idx, ws, o, k, ns)
         assert "few_stream" not in taken(), taken()
     check_gemm_vals(yt, ref, a_v, b_v, label=f"w8a8 tile ns={ns} t={t}")
+    if t == 1:
+        # the separate quantizing pass with X fragments in registers (the one-token kernel
+        # otherwise quantizes the row in LDS itself): the same codes and scale, so the same
+        # products, summed in the same order
+        with use_route("no_xlds"):
+            yr = run_w8a8(x, w8, idx, ws, o, k, ns)
+            assert "few_xlds" not in taken() and "quant" in taken(), taken()
+        check_gemm_vals(yr, ref, a_v, b_v, label=f"w8a8 stream registers ns={ns}")
 
 
 def test_spmm_w8a8_full_size_sampled():
