@@ -655,12 +655,15 @@ __device__ __forceinline__ void stage_row_dma(const uint16_t* __restrict__ src, 
 // SELM > 0 (with XS, one plain segment): the staged row is X itself; after it lands every
 // workgroup keeps the SELM/2 largest magnitudes of each SELM-group in place (the select
 // pass's ranking, ties to the lower index) before the first multiply.
-template <int TB, int WK0, int XL0, int NS, int WK1, bool XS, int SELM = 0, int QNS = 0>
+// RWV: the waves the LDS rings are sized for (the launch may not exceed it).  Rings for
+// half the waves let two workgroups share a CU's LDS.
+template <int TB, int WK0, int XL0, int NS, int WK1, bool XS, int SELM = 0, int QNS = 0, int RWV = Dma<TB, WK0>::WPB>
 __global__ __launch_bounds__((64 * Dma<TB, WK0>::WPB)) void k_fewd(FewSeg s0, FewSeg s1, Epi epi,
                                                            int64_t T, int64_t O, float* __restrict__ y, int64_t ldy,
                                                            int accumulate, float* __restrict__ part, int splits,
                                                            int xn0, int xn1, float* __restrict__ q_out) {
-  constexpr int RW = Dma<TB, WK0>::RW, WPB = Dma<TB, WK0>::WPB;
+  constexpr int RW = Dma<TB, WK0>::RW, WPB = RWV;
+  static_assert(RWV >= 1 && RWV <= Dma<TB, WK0>::WPB, "ring waves");
   constexpr int STAGE = dma_stage_bytes(RW, WK0);   // the first segment's kind is the larger one
   static_assert(WK1 == WK_NONE || dma_stage_bytes(RW, WK1) <= STAGE, "stage size");
   static_assert(STAGE >= TB * 1024, "reduction buffer reuses stage 0");
@@ -1157,9 +1160,12 @@ Plan make_plan(const FewArgs& a, bool allow_split) {
   int wpb = max_wpb;
   int64_t splits = 1;
   if (nob >= 256) {
-    // two segments (hybrid) keep 8 waves: each wave's parts are short, and more waves per
-    // block keep more of them in flight (measured 14336 x 4096 hybrid, 1 token: 27 vs 31 us)
-    const int floor_wpb = (a.nseg == 2 && max_wpb >= 8) ? 8 : 4;
+    // past one workgroup per CU: the direct-to-LDS kernels take half the waves on rings
+    // sized for them, two workgroups per CU (measured at 14336 and 21504 rows, 1 and 8
+    // tokens: 16-27% faster than whole rings with 16 waves, 5-11% faster than with 4 waves
+    // on half rings); the register kernel keeps 4 (two segments: 8, since each wave's parts
+    // are short and more waves keep more of them in flight)
+    const int floor_wpb = p.tb <= 2 ? max_wpb / 2 : (a.nseg == 2 && max_wpb >= 8) ? 8 : 4;
     while (wpb > floor_wpb && nob * wpb > 256 * max_wpb) wpb /= 2;
   } else if (allow_split) {
     splits = (256 + nob - 1) / nob;
@@ -1185,6 +1191,11 @@ hipError_t launch_k(const FewArgs& a, const Plan& p, float* part, hipStream_t s)
   if constexpr (TB <= 2) {
     static_assert(RW == Dma<TB, WK0>::RW, "row tiles");
     if (p.wpb > Dma<TB, WK0>::WPB) return hipErrorInvalidConfiguration;
+    // at most half the waves the rings are sized for: rings for half of them, so that two
+    // workgroups share a CU's LDS (the plain kernels; selection and quantization keep
+    // whole rings)
+    constexpr int HALFW = Dma<TB, WK0>::WPB / 2;
+    const bool half = p.wpb <= HALFW && a.sel_m == 0 && a.q_ns == 0;
     if constexpr (TB == 1) {
       // one token: stage the X rows in LDS next to the weight rings when they fit
       // (the NM_ROUTE_NO_XLDS hint keeps the register loads)
@@ -1198,13 +1209,20 @@ hipError_t launch_k(const FewArgs& a, const Plan& p, float* part, hipStream_t s)
                                          : a.seg[0].k;
       const int64_t xn1 = a.nseg > 1 ? a.seg[1].k : 0;
       const int64_t xbytes = (((xn0 + 511) >> 9) + ((xn1 + 511) >> 9) + (qn > 0 ? ((a.seg[0].k / 2 + 511) >> 9) + 1 : 0)) * 1024;
-      const int64_t ring = 4LL * Dma<TB, WK0>::WPB * dma_stage_bytes(RW, WK0);
+      const int64_t full_ring = 4LL * Dma<TB, WK0>::WPB * dma_stage_bytes(RW, WK0);
+      const int64_t half_ring = 4LL * HALFW * dma_stage_bytes(RW, WK0);
       auto piece_ok = [](const uint16_t* x, int64_t n) {
         return n == 0 || (n >= 8 && (n % 8) == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0);
       };
       const bool rows_ok = piece_ok(a.seg[0].x, xn0) && (a.nseg < 2 || piece_ok(a.seg[1].x, xn1)) && xn0 > 0;
-      if (a.t == 1 && rows_ok && ring + xbytes <= 163840 && !a.route.has(NM_ROUTE_NO_XLDS)) {
+      // half rings only while two workgroups with their staged rows still share a CU;
+      // otherwise one workgroup per CU, with every wave the whole rings serve
+      const bool half_x = half && 2 * (half_ring + xbytes) <= 163840;
+      const int wpb_x = half && !half_x ? Dma<TB, WK0>::WPB : p.wpb;
+      if (a.t == 1 && rows_ok && (half_x ? half_ring : full_ring) + xbytes <= 163840 &&
+          !a.route.has(NM_ROUTE_NO_XLDS)) {
         auto kern = k_fewd<TB, WK0, XL0, NS, WK1, true>;
+        if (half_x) kern = k_fewd<TB, WK0, XL0, NS, WK1, true, 0, 0, HALFW>;
         if constexpr (WK0 == WK_SP24F8 && XL0 == XL_F8 && WK1 == WK_NONE) {
           switch (qn) {
             case 0: break;
@@ -1234,7 +1252,7 @@ hipError_t launch_k(const FewArgs& a, const Plan& p, float* part, hipStream_t s)
         if (ae != hipSuccess) return ae;
         a.route.note(NM_TAKEN_FEW_STREAM | NM_TAKEN_FEW_XLDS | (a.sel_m != 0 ? NM_TAKEN_FEW_SELECT : 0u) |
                      (sp_kind(WK0) ? NM_TAKEN_SPARSE_MMA : 0u) | (qn > 0 ? NM_TAKEN_QUANT : 0u));
-        kern<<<dim3((unsigned)blocks), dim3(64 * p.wpb), (size_t)xbytes, s>>>(
+        kern<<<dim3((unsigned)blocks), dim3(64 * wpb_x), (size_t)xbytes, s>>>(
             a.seg[0], s1, a.epi(), a.t, a.o, a.y, a.ldy, a.accumulate, pp, (int)p.splits, (int)xn0, (int)xn1,
             qn > 0 ? const_cast<float*>(a.row_scale) : nullptr);
         return hipGetLastError();
@@ -1242,8 +1260,10 @@ hipError_t launch_k(const FewArgs& a, const Plan& p, float* part, hipStream_t s)
     }
     if (a.sel_m != 0 || a.q_ns != 0) return hipErrorInvalidValue;   // these need the staged row
     a.route.note(NM_TAKEN_FEW_STREAM | (sp_kind(WK0) ? NM_TAKEN_SPARSE_MMA : 0u));
-    k_fewd<TB, WK0, XL0, NS, WK1, false><<<dim3((unsigned)blocks), dim3(64 * p.wpb), 0, s>>>(
-        a.seg[0], s1, a.epi(), a.t, a.o, a.y, a.ldy, a.accumulate, pp, (int)p.splits, 0, 0, nullptr);
+    auto kern = k_fewd<TB, WK0, XL0, NS, WK1, false>;
+    if (half) kern = k_fewd<TB, WK0, XL0, NS, WK1, false, 0, 0, HALFW>;
+    kern<<<dim3((unsigned)blocks), dim3(64 * p.wpb), 0, s>>>(a.seg[0], s1, a.epi(), a.t, a.o, a.y, a.ldy,
+                                                            a.accumulate, pp, (int)p.splits, 0, 0, nullptr);
   } else {
     auto kern = k_few<TB, RW, WK0, XL0, NS, WK1>;
     const size_t lds = (size_t)p.wpb * TB * 1024;
