@@ -932,13 +932,26 @@ __global__ __launch_bounds__(G1_THREADS) void k_gather1(const uint16_t* __restri
         e += stride;
       }
     }
-    for (; e < nsel; e += nkl) {
-      const u32x4 wv = *reinterpret_cast<const u32x4*>(wcol + (int64_t)sk[e] * O);
-      const float v = sv[e];
+    // the ragged end (fewer than 8 rows per thread: nsel - e < stride): requested together,
+    // rows past the list re-read the first one and are not added; same order as a batch
+    if (e < nsel) {
+      B8 bt;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        acc[2 * c] += v * __uint_as_float(wv[c] << 16);
-        acc[2 * c + 1] += v * __uint_as_float(wv[c] & 0xFFFF0000u);
+      for (int q = 0; q < 8; ++q) {
+        const int ee = e + q * nkl;
+        const int es = ee < nsel ? ee : e;
+        bt.w[q] = *reinterpret_cast<const u32x4*>(wcol + (int64_t)sk[es] * O);
+        bt.v[q] = sv[es];
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (e + q * nkl < nsel) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            acc[2 * c] += bt.v[q] * __uint_as_float(bt.w[q][c] << 16);
+            acc[2 * c + 1] += bt.v[q] * __uint_as_float(bt.w[q][c] & 0xFFFF0000u);
+          }
+        }
       }
     }
   }
