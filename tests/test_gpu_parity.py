@@ -1494,6 +1494,44 @@ def test_measurement_probes():
     assert (got == words[:, 0, :, 0]).all()
 
 
+@pytest.mark.parametrize("kind", ["act", "w24"])
+@pytest.mark.parametrize("t,k", [(1, 14336), (1, 4096), (8, 4096)])
+def test_few_token_half_rings(kind, t, k):
+    """Past 256 row blocks (o = 8208: 513 blocks of 16 rows, the last ragged) the weight-
+    streaming kernel runs 8 waves per workgroup on rings sized for 8, two workgroups per
+    CU.  One token stages its X row beside the rings; a 14336-wide bf16 row does not fit
+    twice per CU, so that call keeps whole rings and 16 waves (and the 2:4 one, whose whole
+    rings leave no room for the row, reads X from global memory).  Forced 16 waves on whole
+    rings partition the reduction differently: both against the oracle (8:16 activations
+    with the mask, so the select pass runs apart; and 2:4 weights)."""
+    print(f"few-token half rings kind={kind} t={t} k={k}", flush=True)
+    o = 8208
+    rng = np.random.default_rng(t * 31 + k)
+    x = synth.student_t_bf16(rng, (t, k), 4.0, 0.5)
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    if kind == "act":
+        sx, keep = O.sparsify(x, 8, 16)
+        ref, a_op, b_op = O.gemm(sx, w), sx, w
+        run = lambda: run_act(x, w, 8, 16)
+    else:
+        ws24, _ = O.sparsify(w, 2, 4)
+        v, mt = gpu_compress_2of4(w)
+        ref, a_op, b_op = O.gemm(x, ws24), x, ws24
+        run = lambda: (run_w(S.NM_W_COMPRESSED, x, v, mt, o, k), None)
+    outs = {}
+    for wpb in (0, 16):
+        with use_route("few_stream", few_wpb=wpb):
+            y, mask = run()
+            assert "few_stream" in taken(), taken()
+            if t == 1 and (kind == "act" or k == 4096):
+                assert "few_xlds" in taken(), taken()
+        if mask is not None:
+            assert (mask == O.pack_mask(keep)).all()
+        check_gemm(y, ref, a_op, b_op, label=f"{kind} t={t} k={k} wpb={wpb}")
+        outs[wpb] = y
+    assert not np.isnan(outs[0]).any()
+
+
 @pytest.mark.parametrize("o", [200, 4096])
 def test_one_token_staged_x_bitexact(o):
     """One token on the weight-streaming kernel: X rows staged in LDS give the same bits as
