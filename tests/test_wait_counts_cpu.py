@@ -9,10 +9,15 @@ current step plus those of the NST - 3 steps before it.  If the compiler moved a
 across a wait or a barrier, or a loader issued a different number of loads than the wait
 assumes, the next step could read a stage that has not landed.
 
+The one-token weight-streaming kernel (X row staged in LDS) has the same hazard: each
+wave owns a four-stage ring with three stages in flight and waits explicitly for the
+stage it reads (no barriers there; its waves never synchronise inside the loop).
+
 This test compiles the kernels to gfx950 assembly (hipcc, no GPU needed), finds each
 ring kernel's steady-state loop, and replays its body (three trips, so that the groups
 before the first waits come from the previous trips) with a count of loads per step
-(steps are delimited by the barriers), checking every vmcnt wait against that bound.
+(steps are delimited by the barriers, or for the per-wave rings by the waits),
+checking every vmcnt wait against that bound.
 """
 import os
 import re
@@ -55,8 +60,8 @@ def _functions(asm, name):
 
 def _template_ints(mangled):
     """Integer and bool template arguments of a mangled kernel name, in order."""
-    args = re.search(r"I((?:L[ib]\d+E)+)E", mangled).group(1)
-    return [int(v) for v in re.findall(r"L[ib](\d+)E", args)]
+    args = re.search(r"I((?:L[ib]n?\d+E)+)E", mangled).group(1)
+    return [int(v.replace("n", "-")) for v in re.findall(r"L[ib](n?\d+)E", args)]
 
 
 def _loops(lines):
@@ -110,6 +115,45 @@ def _check_ring_loop(ev, nst, label):
                                    f"({later} loads issued after it)")
             checked += 1
     return checked
+
+
+def _check_stream_loop(ev, depth, label):
+    """Per-wave rings with no barriers (the one-token weight-streaming kernels): each stage
+    issues its loads, then waits for the stage it reads, issued `depth` stages earlier.
+    Intervals between waits hold one stage's loads, so at each wait N must not exceed the
+    loads of the last `depth` intervals (this one included)."""
+    intervals, cur, trip_len, checked = [], 0, len(ev), 0
+    for idx, e in enumerate(ev * 3):
+        if e[0] in ("load", "vload"):
+            cur += 1
+        elif e[0] == "wait":
+            intervals.append(cur)
+            cur = 0
+            if idx >= trip_len:
+                later = sum(intervals[-depth:])
+                assert e[1] <= later, (f"{label}: s_waitcnt vmcnt({e[1]}) lets the loads of a stage still in flight "
+                                       f"({later} loads issued after it)")
+                checked += 1
+    return checked
+
+
+def test_stream_waits_cover_their_stage(tmp_path):
+    """The weight-streaming kernel with its X row staged in LDS (one token): the four-
+    stage per-wave ring's explicit waits (three stages in flight), on its steady-state loop."""
+    asm = _assembly("decode.hip", tmp_path)
+    # k_fewd<TB, WK0, XL0, NS, WK1, XS, SELM, QNS, RWV>: XS is the sixth argument
+    kernels = [(n, b) for n, b in _functions(asm, "k_fewdI") if _template_ints(n)[5] == 1]
+    assert kernels, "no k_fewd instantiation with the staged X row"
+    n_loops = 0
+    for name, body in kernels:
+        for lp in _loops(body):
+            ev = _events(lp)
+            n_load = sum(1 for e in ev if e[0] == "load")
+            n_wait = sum(1 for e in ev if e[0] == "wait")
+            if n_load >= 8 and n_wait >= 4:   # the steady state: four stages per trip
+                assert _check_stream_loop(ev, 3, name) >= 4
+                n_loops += 1
+    assert n_loops > 0, "no steady-state ring loop found"
 
 
 @pytest.mark.parametrize("src,kernel,nst_index", [
