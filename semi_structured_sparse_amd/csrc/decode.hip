@@ -1229,13 +1229,23 @@ hipError_t launch_k(const FewArgs& a, const Plan& p, float* part, hipStream_t s)
       };
       const bool rows_ok = piece_ok(a.seg[0].x, xn0) && (a.nseg < 2 || piece_ok(a.seg[1].x, xn1)) && xn0 > 0;
       // half rings only while two workgroups with their staged rows still share a CU;
-      // otherwise one workgroup per CU, with every wave the whole rings serve
+      // otherwise one workgroup per CU, with every wave the whole rings serve.  Two-segment
+      // (hybrid) rows too long to fit beside whole rings get rings for three quarters of
+      // the waves (measured, 4096 x 14336 hybrid at one token: 19.2 us against 25.0 us
+      // with X read from global memory; one-segment 2:4 weights were faster with X from
+      // global memory and all 16 waves, 16.6 against 18.5 us, so they keep that)
       const bool half_x = half && 2 * (half_ring + xbytes) <= 163840;
-      const int wpb_x = half && !half_x ? Dma<TB, WK0>::WPB : p.wpb;
-      if (a.t == 1 && rows_ok && (half_x ? half_ring : full_ring) + xbytes <= 163840 &&
-          !a.route.has(NM_ROUTE_NO_XLDS)) {
+      constexpr int TQW = 3 * Dma<TB, WK0>::WPB / 4;
+      const bool tq_x = !half && WK1 != WK_NONE && a.nseg == 2 && a.sel_m == 0 && a.q_ns == 0 &&
+                        full_ring + xbytes > 163840 && 4LL * TQW * dma_stage_bytes(RW, WK0) + xbytes <= 163840;
+      const int wpb_x = tq_x ? TQW : half && !half_x ? Dma<TB, WK0>::WPB : p.wpb;
+      const int64_t ring_x = half_x ? half_ring : tq_x ? 4LL * TQW * dma_stage_bytes(RW, WK0) : full_ring;
+      if (a.t == 1 && rows_ok && ring_x + xbytes <= 163840 && !a.route.has(NM_ROUTE_NO_XLDS)) {
         auto kern = k_fewd<TB, WK0, XL0, NS, WK1, true>;
         if (half_x) kern = k_fewd<TB, WK0, XL0, NS, WK1, true, 0, 0, HALFW>;
+        if constexpr (WK1 != WK_NONE) {
+          if (tq_x) kern = k_fewd<TB, WK0, XL0, NS, WK1, true, 0, 0, TQW>;
+        }
         if constexpr (WK0 == WK_SP24F8 && XL0 == XL_F8 && WK1 == WK_NONE) {
           switch (qn) {
             case 0: break;

@@ -1532,6 +1532,32 @@ def test_few_token_half_rings(kind, t, k):
     assert not np.isnan(outs[0]).any()
 
 
+def test_one_token_long_hybrid_row():
+    """One token, hybrid input split over a 14336-wide row (10752 2:4 columns, then 3584
+    dense, no column lists: the Spense down-projection form), 4096 outputs.  The staged
+    row does not fit beside whole rings, so the call takes rings for 12 waves with the row
+    in LDS; X read from global memory with 16 waves (no_xlds) partitions the reduction
+    differently.  Both against the oracle."""
+    print("one-token long hybrid row", flush=True)
+    rng = np.random.default_rng(14336)
+    o, ks, kd = 4096, 10752, 3584
+    x = synth.normal_bf16(rng, (1, ks + kd))
+    w = synth.normal_bf16(rng, (o, ks + kd), 0.02)
+    wsp, _ = O.sparsify(np.ascontiguousarray(w[:, :ks]), 2, 4)
+    vs, ms = gpu_compress_2of4(np.ascontiguousarray(w[:, :ks]))
+    wd = np.ascontiguousarray(w[:, ks:])
+    ref = O.gemm(np.ascontiguousarray(x[:, :ks]), wsp) + O.gemm(np.ascontiguousarray(x[:, ks:]), wd)
+    wcat = np.concatenate([wsp, wd], axis=1)
+    with use_route("few_stream"):
+        y = run_hybrid(x, None, ks, None, kd, vs, ms, dev(wd), o)
+        assert {"few_stream", "few_xlds"} <= taken(), taken()
+        with use_route("no_xlds"):
+            y_glb = run_hybrid(x, None, ks, None, kd, vs, ms, dev(wd), o)
+            assert "few_xlds" not in taken(), taken()
+    check_gemm(y, ref, x, wcat, label="hybrid row staged (12 waves)")
+    check_gemm(y_glb, ref, x, wcat, label="hybrid row from global memory")
+
+
 @pytest.mark.parametrize("o", [200, 4096])
 def test_one_token_staged_x_bitexact(o):
     """One token on the weight-streaming kernel: X rows staged in LDS give the same bits as
