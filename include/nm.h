@@ -244,7 +244,10 @@ enum {
   NM_ROUTE_NO_FEW_SELECT = 1u << 9, /* one token: a separate select pass rather than the
                                        selection inside the product's staged X row          */
   NM_ROUTE_TILE_LDS = 1u << 10,     /* tile products: the direct-to-LDS kernels at any size */
-  NM_ROUTE_TILE_REGS = 1u << 11     /* tile products: the register-staged kernels           */
+  NM_ROUTE_TILE_REGS = 1u << 11,    /* tile products: the register-staged kernels           */
+  NM_ROUTE_LIFT_COPY = 1u << 12     /* W_SLIDE tile products: lift X into the workspace
+                                       first (otherwise the tile loads build the lifted
+                                       rows from the raw X)                                 */
 };
 
 /*
@@ -312,7 +315,9 @@ typedef enum {
  *               nm_spmm_workspace_size(args): ACT_DYNAMIC may run select and product as
  *               two passes (S(x) staged in the workspace), ACT_COMPRESSED stages the
  *               decompressed x there (required unless n:m = 2:4 with 2BIT metadata),
- *               W_SLIDE calls above 16-32 tokens stage the lifted x there, W_* calls
+ *               W_SLIDE calls that run the register-staged tile kernel (or carry the
+ *               NM_ROUTE_LIFT_COPY hint) stage the lifted x there (the direct-to-LDS tile
+ *               kernels build the lifted rows from x in their own loads), W_* calls
  *               above 128 tokens also place a K-blocked copy of the 2-bit positions
  *               there (o * kc / 8 bytes: fewer, larger loads per tile), and few-token
  *               calls (t <= 128) may split the reduction across workgroups, writing fp32

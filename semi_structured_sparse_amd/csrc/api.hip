@@ -223,15 +223,28 @@ bool sp_few_tile(const nml::SparseArgs& sa) {
   return (sa.t > 32 && sa.o >= 2048) || (sa.t > 16 && sa.o >= 8192);
 }
 
-// The W_* modes as a tile-kernel call; lowered weights read X lifted into a buffer of
-// row stride lift_ld(kc) (pointer filled in by the caller).
+// Lowered weights on the direct-to-LDS tile kernels: the loads build the lifted X rows
+// from the raw X (bf16 weights; the NM_ROUTE_LIFT_COPY hint lifts X into the workspace
+// first instead).
+bool w_lift_dma(const nm_spmm_args* a) {
+  return a->mode == NM_W_SLIDE && a->w_dtype == NM_W_BF16 && !(a->route & NM_ROUTE_LIFT_COPY);
+}
+
+// The W_* modes as a tile-kernel call.  Lowered weights: the raw X, lifted by the tile
+// loads, or (NM_ROUTE_LIFT_COPY) X lifted into a buffer of row stride lift_ld(kc)
+// (pointer filled in by the caller).
 nml::SparseArgs w_mode_sparse_args(const nm_spmm_args* a, int64_t kc, int ns, bool report) {
   nml::SparseArgs sa{};
   sa.route = route_of(a, report);
   sa.w_vals = (const uint16_t*)a->w; sa.w_meta = (const uint8_t*)a->w_meta; sa.kc = kc;
   sa.x = (const uint16_t*)a->x; sa.ldx = a->ldx; sa.ns = ns;
   sa.loader = nml::XL_PLAIN;
-  if (a->mode == NM_W_SLIDE) sa.ldx = lift_ld(kc);
+  if (w_lift_dma(a)) {
+    sa.loader = nml::XL_LIFT;
+    sa.lift_dma = 1;
+  } else if (a->mode == NM_W_SLIDE) {
+    sa.ldx = lift_ld(kc);
+  }
   sa.t = a->t; sa.o = a->o; sa.y = a->y; sa.ldy = a->ldy; sa.accumulate = a->accumulate; sa.trans_out = 0;
   return sa;
 }
@@ -241,7 +254,7 @@ nml::SparseArgs w_mode_sparse_args(const nm_spmm_args* a, int64_t kc, int ns, bo
 int64_t w_mode_tile_bytes(const nm_spmm_args* a, int64_t kc, int ns) {
   const nml::SparseArgs sa = w_mode_sparse_args(a, kc, ns, false);
   if (!sp_few_tile(sa)) return -1;
-  const int64_t lift = a->mode == NM_W_SLIDE ? align256(a->t * lift_ld(kc) * 2) : 0;
+  const int64_t lift = (a->mode == NM_W_SLIDE && !sa.lift_dma) ? align256(a->t * lift_ld(kc) * 2) : 0;
   return lift + nml::gemm_lds_sp_small_part_bytes(sa);
 }
 
@@ -626,8 +639,10 @@ int64_t nm_spmm_workspace_size(const nm_spmm_args* a) {
     if (a->mode == NM_W_SLIDE && (a->ns < 2 || a->ns > 8 || a->k % (2 * a->ns))) return 0;
     if (a->mode == NM_W_COMPRESSED && a->k % 4) return 0;
     const int64_t kc = w_mode_kc(a);
-    const int64_t lift = a->mode == NM_W_SLIDE ? align256(a->t * lift_ld(kc) * 2) : 0;
     nml::SparseArgs sa = w_mode_sparse_args(a, kc, a->mode == NM_W_SLIDE ? a->ns : 2, false);
+    // a lifted copy of X only where the tile loads do not lift it themselves
+    const bool lifted_loads = sa.lift_dma && nml::gemm_sparse_uses_lds(sa);
+    const int64_t lift = (a->mode == NM_W_SLIDE && !lifted_loads) ? align256(a->t * lift_ld(kc) * 2) : 0;
     const int64_t mb = meta_block_ws(sa);
     return mb > 0 ? lift + mb : lift;
   }
@@ -897,7 +912,7 @@ nm_status spmm_impl(const nm_spmm_args* a, void* stream, bool noalloc) {
         if (tile == 0 || (tile > 0 && a->workspace != nullptr && a->workspace_bytes >= tile)) {
           nml::SparseArgs sa = w_mode_sparse_args(a, kc, ns, true);
           int64_t off = 0;
-          if (a->mode == NM_W_SLIDE) {
+          if (a->mode == NM_W_SLIDE && !sa.lift_dma) {
             uint16_t* xl = (uint16_t*)a->workspace;
             hipError_t e = nml::launch_lift(ns, (const uint16_t*)a->x, T, K, a->ldx, xl, lift_ld(kc), s);
             if (e != hipSuccess) return NM_EHIP;
@@ -917,8 +932,10 @@ nm_status spmm_impl(const nm_spmm_args* a, void* stream, bool noalloc) {
       sa.x = (const uint16_t*)a->x; sa.ldx = a->ldx; sa.ns = ns;
       sa.loader = a->mode == NM_W_SLIDE ? nml::XL_LIFT : nml::XL_PLAIN;
       sa.t = T; sa.o = O; sa.y = a->y; sa.ldy = a->ldy; sa.accumulate = a->accumulate; sa.trans_out = 0;
+      sa.lift_dma = w_lift_dma(a) ? 1 : 0;
+      if (sa.lift_dma && !nml::gemm_sparse_uses_lds(sa)) sa.lift_dma = 0;   // register kernel: lift in its loader
       int64_t off = 0;
-      if (a->mode == NM_W_SLIDE && a->workspace != nullptr && a->workspace_bytes >= T * lift_ld(kc) * 2) {
+      if (a->mode == NM_W_SLIDE && !sa.lift_dma && a->workspace != nullptr && a->workspace_bytes >= T * lift_ld(kc) * 2) {
         // materialise lift(X) once so the product kernel reads X with 16-byte loads
         uint16_t* xl = (uint16_t*)a->workspace;
         hipError_t e = nml::launch_lift(ns, (const uint16_t*)a->x, T, K, a->ldx, xl, lift_ld(kc), s);

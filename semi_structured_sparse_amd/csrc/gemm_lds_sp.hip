@@ -2,8 +2,10 @@
 //   Y[t][o] (=|+=) sum_k X[t][k] * W24[o][k]  (+ sum_j X[t][dbase + j] * Wd[o][j])
 //
 // W24 is 2:4 along the reduction (values [O][kc/2], 2-bit positions [O][kc/8]) -- plain
-// 2:4 weights, or (2N-2):2N weights lowered to overlapping 2:4 windows whose activations
-// were lifted beforehand (SlideSparse page, technical summary 2.A/2.B).  The optional
+// 2:4 weights, or (2N-2):2N weights lowered to overlapping 2:4 windows with lifted
+// activations (SlideSparse page, technical summary 2.A/2.B): X lifted beforehand, or (LX)
+// the raw X, whose lifted rows the stage loads build with one dword per lane (every lifted
+// dword is one raw dword: a window is 4 bf16 starting at an even raw position).  The optional
 // dense second phase is the hybrid format's dense region, accumulated into the same
 // accumulators (SpenseGPT page, technical summary 2.A).
 //
@@ -79,7 +81,10 @@ __device__ __forceinline__ void k_loop2(int n, unsigned char* a0, unsigned char*
 __device__ __forceinline__ int swz8(int r, int c) { return c ^ ((r >> 1) & 7); }   // 8 pieces per row
 __device__ __forceinline__ int swz4(int r, int c) { return c ^ ((r >> 2) & 3); }   // 4 pieces per row
 
-template <int BM, int BN, int WM, int WN, bool MB, bool F8, int NST = 2>
+// LX > 0: the weights are (2 LX - 2):2 LX rows lowered to 2:4 windows and x is the raw
+// activation: the loads of each step build the lifted X rows in LDS themselves (no
+// lifted copy of X; the sparse phase only).
+template <int BM, int BN, int WM, int WN, bool MB, bool F8, int NST = 2, int LX = 0>
 __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
     const uint16_t* __restrict__ wv, const uint8_t* __restrict__ wm, int64_t kc, const uint16_t* __restrict__ x,
     int64_t ldx, const uint16_t* __restrict__ wd, int64_t ldwd, int64_t kd, int64_t dbase, int64_t T, int64_t O,
@@ -98,6 +103,10 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
   constexpr int NV = BM / 16 / NW;           // value load groups (16 rows) per wave
   constexpr int NX = BN / 8 / NW;            // X load groups (8 rows) per wave
   constexpr int ND = BM / 8 / NW;            // dense weight load groups (8 rows) per wave
+  // lifted X: each request fills 256 bytes of the stage (two token rows' 128-byte step
+  // pieces) with one dword per lane, gathered from the raw row
+  static_assert(LX == 0 || (!F8 && LX >= 2 && LX <= 8 && BN % (2 * NW) == 0), "lifted X: bf16, 2 <= N <= 8");
+  constexpr int NXL = LX > 0 ? BN / 2 / NW : NX;   // X requests per wave per sparse step
   static_assert(NV >= 1 && NX >= 1 && ND >= 1 && BM % (16 * NW) == 0 && BN % (8 * NW) == 0,
                 "load groups per wave");
   static_assert(NST >= 2 && NST <= 4, "two to four stages");
@@ -178,6 +187,23 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
       o = o < O ? o : O - 1;
       msrc = wm + o * (MB ? MU : mstride) + (F8 ? 0 : 4 * (lane & 1));
     }
+    // LX: request q of a wave fills rows 2 (wave + q NW) + {0, 1}; lane -> row + lane / 32,
+    // physical 16-byte slot (lane / 4) % 8 (holding logical piece swz8(row, slot)), dword
+    // lane % 4.  Its lifted dword of step s is D = 32 s + xd[q] of the row: lifted group
+    // g = D / (2 (LX - 1)) (4 (LX - 1) positions, 2 LX raw positions), window w and dword
+    // e within it, raw dword LX g + w + e.
+    const unsigned char* xraw[LX > 0 ? NXL : 1];
+    int xd[LX > 0 ? NXL : 1];
+    if constexpr (LX > 0) {
+#pragma unroll
+      for (int q = 0; q < NXL; ++q) {
+        const int r = (wave + q * NW) * 2 + (lane >> 5);
+        int64_t t = t0 + r;
+        t = t < T ? t : T - 1;
+        xraw[q] = reinterpret_cast<const unsigned char*>(x) + t * ldxb;
+        xd[q] = 4 * swz8(r, (lane >> 2) & 7) + (lane & 3);
+      }
+    }
     auto issue = [&](unsigned char* a, unsigned char* b, int s) {
       const int64_t v0 = (int64_t)(ks0 + s) * 64;   // value bytes per row per step: 64
 #pragma unroll
@@ -186,8 +212,19 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
         if constexpr (F8) g2lds16(msrc + (ks0 + s) * mstep, a + SV_BYTES + wave * 1024);
         else g2lds4(msrc + (ks0 + s) * mstep, a + SV_BYTES + wave * 256);
       }
+      if constexpr (LX > 0) {
+        constexpr uint32_t P = 2 * (LX - 1);   // lifted dwords per group
 #pragma unroll
-      for (int q = 0; q < NX; ++q) g2lds16(xsrc[q] + (int64_t)(ks0 + s) * 128, b + (wave + q * NW) * 1024);
+        for (int q = 0; q < NXL; ++q) {
+          const uint32_t D = (uint32_t)(ks0 + s) * 32u + (uint32_t)xd[q];
+          const uint32_t g = D / P, rr = D - g * P;
+          const int64_t raw = (int64_t)g * LX + (rr >> 1) + (rr & 1);
+          g2lds4(xraw[q] + 4 * raw, b + (wave + q * NW) * 256);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < NX; ++q) g2lds16(xsrc[q] + (int64_t)(ks0 + s) * 128, b + (wave + q * NW) * 1024);
+      }
     };
     // The B fragment of column block j + 1 is read while block j is multiplied; the wait
     // for it sits before the next reads (while a direct-to-LDS load is in flight the
@@ -235,7 +272,7 @@ __global__ __launch_bounds__(64 * WM * WN) void k_gemm_lds_sp(
     };
     // direct-to-LDS requests per wave per sparse step: values and X (positions: some waves)
     if constexpr (NST == 2) k_loop2(nks, sA0, sB0, sA1, sB1, issue, compute);
-    else lds_ring<NST, NV + NX>(nks, SA, SB, issue, compute);
+    else lds_ring<NST, NV + NXL>(nks, SA, SB, issue, compute);
   }
 
   // ------------------------------------------------------------ dense phase ---
@@ -364,7 +401,7 @@ __global__ __launch_bounds__(256) void k_meta_block(const uint8_t* __restrict__ 
   }
 }
 
-template <int BM, int BN, int WM, int WN, int NST = 2>
+template <int BM, int BN, int WM, int WN, int NST = 2, int LX = 0>
 hipError_t launch_sp_cfg(const SparseArgs& a, hipStream_t s, int64_t splits, float* part) {
   const int tiles_m = (int)((a.o + BM - 1) / BM), tiles_n = (int)((a.t + BN - 1) / BN);
   const int64_t ntiles = (int64_t)tiles_m * tiles_n;
@@ -378,10 +415,14 @@ hipError_t launch_sp_cfg(const SparseArgs& a, hipStream_t s, int64_t splits, flo
   const int steps = (int)(per > 0 ? per : 1), group = group_for(tiles_m, BM, BN);
   float* pp = splits > 1 ? part : nullptr;
 #define NM_SP_LAUNCH(MBV, F8V, META)                                                                    \
-  k_gemm_lds_sp<BM, BN, WM, WN, MBV, F8V, NST><<<grid, block, 0, s>>>(                                  \
+  k_gemm_lds_sp<BM, BN, WM, WN, MBV, F8V, NST, LX><<<grid, block, 0, s>>>(                              \
       a.w_vals, META, a.kc, a.x, a.ldx, a.wd, a.ldwd, a.kd, a.dbase, a.t, a.o, a.y, a.ldy, a.accumulate, \
       tiles_m, tiles_n, steps, pp, group, a.x_scale, a.w_scale)
-  if (a.f8) {
+  if constexpr (LX > 0) {
+    if (a.f8 || a.kd != 0) return hipErrorInvalidValue;
+    if (a.w_meta_blk != nullptr) NM_SP_LAUNCH(true, false, a.w_meta_blk);
+    else NM_SP_LAUNCH(false, false, a.w_meta);
+  } else if (a.f8) {
     if (a.w_meta_blk != nullptr) NM_SP_LAUNCH(true, true, a.w_meta_blk);
     else NM_SP_LAUNCH(false, true, a.w_meta);
   } else {
@@ -393,6 +434,21 @@ hipError_t launch_sp_cfg(const SparseArgs& a, hipStream_t s, int64_t splits, flo
   a.route.note(NM_TAKEN_TILE_LDS | NM_TAKEN_SPARSE_MMA | (splits > 1 ? NM_TAKEN_TILE_SPLIT : 0u));
   if (e != hipSuccess || splits == 1) return e;
   return launch_reduce_parts(part, splits, Epi{}, a.t, a.o, a.y, a.ldy, a.accumulate, a.route, s);
+}
+
+// the configuration for lowered weights whose lifted X rows the loads build (N = a.ns)
+template <int BM, int BN, int WM, int WN, int NST>
+hipError_t launch_sp_lx(const SparseArgs& a, hipStream_t s, int64_t splits, float* part) {
+  switch (a.ns) {
+    case 2: return launch_sp_cfg<BM, BN, WM, WN, NST, 2>(a, s, splits, part);
+    case 3: return launch_sp_cfg<BM, BN, WM, WN, NST, 3>(a, s, splits, part);
+    case 4: return launch_sp_cfg<BM, BN, WM, WN, NST, 4>(a, s, splits, part);
+    case 5: return launch_sp_cfg<BM, BN, WM, WN, NST, 5>(a, s, splits, part);
+    case 6: return launch_sp_cfg<BM, BN, WM, WN, NST, 6>(a, s, splits, part);
+    case 7: return launch_sp_cfg<BM, BN, WM, WN, NST, 7>(a, s, splits, part);
+    case 8: return launch_sp_cfg<BM, BN, WM, WN, NST, 8>(a, s, splits, part);
+  }
+  return hipErrorInvalidValue;
 }
 
 // Few-token split: 128-row tiles, as many workgroups as fit one per CU.
@@ -410,7 +466,8 @@ int64_t sp_small_splits(const SparseArgs& a) {
 namespace nml {
 
 bool gemm_lds_sp_eligible(const SparseArgs& a, bool any_size) {
-  if (a.loader != XL_PLAIN || a.trans_out) return false;
+  const bool lifted = a.loader == XL_LIFT && a.lift_dma && a.kd == 0 && !a.f8 && a.ns >= 2 && a.ns <= 8;
+  if ((a.loader != XL_PLAIN && !lifted) || a.trans_out) return false;
   if (a.kc % 64 != 0 || a.kd % 64 != 0 || (a.kc == 0 && a.kd == 0)) return false;
   if (a.f8 && (a.kc % 128 != 0 || a.kd != 0 || (a.ldx % 16) != 0 || a.x_scale == nullptr || a.w_scale == nullptr))
     return false;
@@ -435,6 +492,7 @@ hipError_t launch_meta_block(const uint8_t* meta, int64_t o, int64_t kc, int uni
 hipError_t launch_gemm_lds_sp(const SparseArgs& a, hipStream_t s) {
   // waves of 128 (o) x 64 (t): the dense X operand, read by WM waves, is the larger LDS
   // read stream, so WM = 2 beats 4 (measured 1-4% on gfx950)
+  if (a.lift_dma && a.loader == XL_LIFT) return launch_sp_lx<256, 256, 2, 4, 2>(a, s, 1, nullptr);
   return launch_sp_cfg<256, 256, 2, 4>(a, s, 1, nullptr);
 }
 
@@ -447,6 +505,10 @@ hipError_t launch_gemm_lds_sp_small(const SparseArgs& a, float* part, int64_t pa
   int64_t splits = sp_small_splits(a);
   if (part == nullptr || part_bytes < splits * a.t * a.o * 4) splits = 1;
   // three LDS stages (72 / 96 KiB): two K-steps in flight (four measured level)
+  if (a.lift_dma && a.loader == XL_LIFT) {
+    if (a.t <= 64) return launch_sp_lx<128, 64, 4, 2, 3>(a, s, splits, part);
+    return launch_sp_lx<128, 128, 4, 2, 3>(a, s, splits, part);
+  }
   if (a.t <= 64) return launch_sp_cfg<128, 64, 4, 2, 3>(a, s, splits, part);
   return launch_sp_cfg<128, 128, 4, 2, 3>(a, s, splits, part);
 }

@@ -136,6 +136,9 @@ struct SparseArgs {
   int f8;
   const float* x_scale;
   const float* w_scale;
+  // lowered weights (loader XL_LIFT, no dense phase, bf16): the direct-to-LDS kernels build
+  // the lifted X rows from the raw x in their loads (no lifted copy)
+  int lift_dma;
   Route route;
 };
 hipError_t launch_gemm_sparse(const SparseArgs& a, hipStream_t s);

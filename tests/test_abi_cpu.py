@@ -63,7 +63,7 @@ def test_route_fields_change_routes_not_results_host_side():
     assert auto >= 64 * 14336 * 2 and no_few >= 64 * 14336 * 2
     assert auto != stream            # the split tile route and the streaming route need different scratch
     assert S.route_taken(a) == 0
-    assert set(S.ROUTE.values()) == {1 << i for i in range(12)}
+    assert set(S.ROUTE.values()) == {1 << i for i in range(13)}
     assert set(S.TAKEN.values()) == {1 << i for i in range(18)}
     # the header's values are the binding's
     src = open(os.path.join(ROOT, "include", "nm.h")).read()
@@ -172,13 +172,16 @@ def test_spmm_validation():
     assert S.nm_spmm_workspace_size(a) >= 2 * 4 * 64 * 4
     a = spmm_args(mode=S.NM_W_COMPRESSED, t=4, o=8192, k=4096, w_meta=P, w_meta_fmt=S.NM_META_2BIT, ldy=8192)
     assert S.nm_spmm_workspace_size(a) == 0
-    # large tokens: the K-blocked copy of the weight positions (2:4), after the lifted X
-    # (6:8 lowered to 2:4 over K' = 1.5 K)
+    # large tokens: the K-blocked copy of the weight positions (2:4); 6:8 lowered to 2:4
+    # over K' = 1.5 K: the direct-to-LDS kernel lifts X in its loads, so the positions
+    # alone, and with the lift_copy hint the lifted X before them
     a = spmm_args(mode=S.NM_W_COMPRESSED, t=4096, o=4096, k=6144, w_meta=P, w_meta_fmt=S.NM_META_2BIT, ldx=6144,
                   ldy=4096)
     assert S.nm_spmm_workspace_size(a) >= 4096 * 6144 // 8
     a = spmm_args(mode=S.NM_W_SLIDE, ns=4, t=4096, o=4096, k=4096, w_meta=P, w_meta_fmt=S.NM_META_2BIT, ldx=4096,
                   ldy=4096)
+    assert S.nm_spmm_workspace_size(a) == 4096 * 6144 // 8
+    a.route = S.route_bits("lift_copy")
     assert S.nm_spmm_workspace_size(a) >= 4096 * 6144 * 2 + 4096 * 6144 // 8
     a = spmm_args(mode=S.NM_W_COMPRESSED, t=4, o=8, k=16, w_meta=P, w_meta_fmt=S.NM_META_2BIT,
                   workspace=MIS, workspace_bytes=1 << 20)

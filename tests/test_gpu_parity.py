@@ -850,6 +850,33 @@ def test_spmm_w_slide(ns, t):
     check_gemm(host(y, np.float32), O.gemm(x, pruned), x, pruned, label=f"slide ns={ns}")
 
 
+@pytest.mark.parametrize("ns", [2, 3, 4, 5, 8])
+@pytest.mark.parametrize("t,o,hint", [(40, 2056, "few_tile"), (100, 2056, "few_tile"), (300, 264, "tile_lds"),
+                                      (1030, 1040, "tile_lds")])
+def test_slide_lift_in_loads_bitexact(ns, t, o, hint):
+    """Lowered (2N-2):2N weights on the direct-to-LDS tile kernels: the loads build the
+    lifted X rows from the raw X (no lifted copy), so the stages hold the same bytes as
+    when X is lifted into the workspace first (the lift_copy hint): the same bits, and
+    the dense product on the pruned W within tolerance.  Few-token split tiles (40 and 100
+    tokens, 2056 rows) and the large-token kernel (ragged tiles in both dimensions)."""
+    print(f"slide lift in loads ns={ns} t={t} o={o}", flush=True)
+    rng = np.random.default_rng(ns * 7 + t)
+    k = 2 * ns * 64 * (3 if ns != 8 else 1)
+    x = synth.normal_bf16(rng, (t, k))
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    vp, mp = slide_pack_gpu(w, ns)
+    pruned, _ = O.sparsify(w, 2 * ns - 2, 2 * ns)
+    hints = (hint,) if hint else ()
+    with use_route(*hints):
+        y = run_w(S.NM_W_SLIDE, x, vp, mp, o, k, ns=ns)
+        assert "tile_lds" in taken() and "lift" not in taken(), taken()
+        with use_route("lift_copy"):
+            y_copy = run_w(S.NM_W_SLIDE, x, vp, mp, o, k, ns=ns)
+            assert "tile_lds" in taken() and "lift" in taken(), taken()
+    assert np.array_equal(y.view(np.uint32), y_copy.view(np.uint32)), "lift in loads vs lifted copy"
+    check_gemm(y, O.gemm(x, pruned), x, pruned, label=f"slide ns={ns} t={t} lift in loads")
+
+
 @pytest.mark.parametrize("ns", [3, 5, 6, 7])
 def test_spmm_w_slide_odd_family(ns):
     """4:6, 8:10, 10:12 and 12:14 weights end to end on the GPU: compressed by the
