@@ -211,16 +211,17 @@ inline int64_t lift_ld(int64_t kp) { return (kp + 7) / 8 * 8; }
 
 // Few-token products with a 2:4 weight operand (plain, lowered or hybrid): the split-K
 // tile kernel, whose workgroups share each X slice through LDS across 128 weight rows,
-// when its shape rules hold (plain loader: lowered weights read a lifted copy of X), above
-// 32 tokens for weights of at least 2048 rows and above 16 tokens from 8192 rows; the
-// streaming kernel otherwise.  Measured on gfx950: 6:8 lowered 4096 x 4096 at 128 tokens
-// 30 vs 58 us, 14336 x 4096 at 16 tokens 40 vs 56 us; 2:4 14336 x 4096 at 33 tokens 31 vs
-// 38 us.  The NM_ROUTE_FEW_STREAM / NM_ROUTE_FEW_TILE hints force either.
+// when its shape rules hold, above 32 tokens for weights of at least 2048 rows and above
+// 16 tokens from 8192 rows (or from 2048 rows for lowered weights, whose lift the tile
+// loads do); the streaming kernel otherwise.  Measured on gfx950: 6:8 lowered 4096 x
+// 4096 at 128 tokens 30 vs 58 us, at 24 / 32 tokens 16.9 / 18.0 vs 20.0 / 22.3 us (tile
+// against stream), 14336 x 4096 at 16 tokens 40 vs 56 us; 2:4 14336 x 4096 at 33 tokens
+// 31 vs 38 us.  The NM_ROUTE_FEW_STREAM / NM_ROUTE_FEW_TILE hints force either.
 bool sp_few_tile(const nml::SparseArgs& sa) {
   if (!nml::gemm_lds_sp_eligible(sa, true)) return false;
   if (sa.route.has(NM_ROUTE_FEW_TILE)) return true;
   if (sa.route.has(NM_ROUTE_FEW_STREAM)) return false;
-  return (sa.t > 32 && sa.o >= 2048) || (sa.t > 16 && sa.o >= 8192);
+  return (sa.t > 32 && sa.o >= 2048) || (sa.t > 16 && (sa.o >= 8192 || (sa.lift_dma && sa.o >= 2048)));
 }
 
 // Lowered weights on the direct-to-LDS tile kernels: the loads build the lifted X rows
