@@ -233,7 +233,8 @@ enum {
                                        workspace, the product applies it to X fragments     */
   NM_ROUTE_ACT_SX = 1u << 2,        /* ... a select pass writes S(X) to the workspace, the
                                        product streams it                                   */
-  NM_ROUTE_NO_FEW = 1u << 3,        /* never the few-token (t <= 128) kernels               */
+  NM_ROUTE_NO_FEW = 1u << 3,        /* never the few-token (t <= 128) kernels, nor the split
+                                       tile kernel above 128 tokens                         */
   NM_ROUTE_FEW_STREAM = 1u << 4,    /* few tokens: the weight-streaming kernels             */
   NM_ROUTE_FEW_TILE = 1u << 5,      /* few tokens: the split-K tile kernels where they apply*/
   NM_ROUTE_NO_META_BLOCK = 1u << 6, /* large-token 2:4 products read the row-major 2-bit
@@ -243,7 +244,8 @@ enum {
   NM_ROUTE_NO_XLDS = 1u << 8,       /* one token: X fragments in registers, not staged in LDS*/
   NM_ROUTE_NO_FEW_SELECT = 1u << 9, /* one token: a separate select pass rather than the
                                        selection inside the product's staged X row          */
-  NM_ROUTE_TILE_LDS = 1u << 10,     /* tile products: the direct-to-LDS kernels at any size */
+  NM_ROUTE_TILE_LDS = 1u << 10,     /* tile products: the direct-to-LDS large-tile kernels
+                                       at any size                                          */
   NM_ROUTE_TILE_REGS = 1u << 11,    /* tile products: the register-staged kernels           */
   NM_ROUTE_LIFT_COPY = 1u << 12     /* W_SLIDE tile products: lift X into the workspace
                                        first (otherwise the tile loads build the lifted
@@ -259,7 +261,7 @@ enum {
   NM_TAKEN_FEW_STREAM = 1u << 1,    /* a few-token weight-streaming kernel                  */
   NM_TAKEN_FEW_XLDS = 1u << 2,      /* ... with the X row staged in LDS                     */
   NM_TAKEN_FEW_SELECT = 1u << 3,    /* ... selecting inside the staged X row                */
-  NM_TAKEN_TILE_SPLIT = 1u << 4,    /* a split-K tile kernel for few tokens                 */
+  NM_TAKEN_TILE_SPLIT = 1u << 4,    /* a split-K tile kernel (partial tiles in workspace)   */
   NM_TAKEN_REDUCE = 1u << 5,        /* a pass adding partial sums in a fixed order          */
   NM_TAKEN_TILE_LDS = 1u << 6,      /* a direct-to-LDS tile kernel                          */
   NM_TAKEN_TILE_REGS = 1u << 7,     /* a register-staged tile kernel                        */
@@ -320,10 +322,11 @@ typedef enum {
  *               kernels build the lifted rows from x in their own loads), W_* calls
  *               above 128 tokens also place a K-blocked copy of the 2-bit positions
  *               there (o * kc / 8 bytes: fewer, larger loads per tile), and few-token
- *               calls (t <= 128) may split the reduction across workgroups, writing fp32
- *               partial sums there that a second kernel adds in a fixed order (the
- *               split-K tile route for 33-128 tokens needs this).  With less, the call
- *               takes a route that needs none (slower).  Contents after the call are
+ *               calls (t <= 128), and larger calls whose 256 x 256 output tiles number
+ *               under 128, may split the reduction across workgroups, writing fp32
+ *               partial sums there that a second kernel adds in a fixed order (at most
+ *               256 partial tiles of 128 x 128; the split-K tile route needs this).  With
+ *               less, the call takes a route that needs none (slower).  Contents after the call are
  *               unspecified.  Calls sharing a workspace must be ordered (same stream).
  *   pts, pts_shift, col_shift, row_scale, row_shift   the activation-sparsity
  *               mitigations ([FLEX] 2.B): ACT_DYNAMIC with pts != 0 shifts, selects and

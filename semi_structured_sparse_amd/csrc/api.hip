@@ -88,19 +88,20 @@ nml::Route route_of(const nm_spmm_args* a, bool report) {
   return r;
 }
 
-// Which activation route nm_spmm takes (the NM_ROUTE_ACT_* hints choose one):
+// Which activation route nm_spmm takes above the few-token range (the NM_ROUTE_ACT_*
+// hints choose one; sx by default, fused when there is no workspace for S(X)):
 //   fused: top-n selected inside the product kernel's X-tile loader;
 //   mask:  a select pass writes the keep bitmask, the product applies it to X fragments;
 //   sx:    a select pass writes S(X) to the workspace, the product streams it unchanged.
-// Measured on gfx950 at 8192 x 14336 x 4096 (8:16): sx 90 + 767 us, mask 67 + 1091 us;
-// the fused loader re-selects X once per output tile and is slowest at large T.
+// Measured on gfx950, 8:16: at 8192 x 14336 x 4096 sx 90 + 767 us, mask 67 + 1091 us; the
+// fused loader re-selects X once per output tile and is slower at every size (192 tokens
+// on 4096 x 14336: 509 us, against 263 us for sx on the same register-staged kernel).
 enum ActRoute { ROUTE_FUSED = 0, ROUTE_MASK = 1, ROUTE_SX = 2 };
 
-ActRoute act_route(int64_t t, const nml::Route& r) {
+ActRoute act_route(const nml::Route& r) {
   if (r.has(NM_ROUTE_ACT_FUSED)) return ROUTE_FUSED;
   if (r.has(NM_ROUTE_ACT_MASK)) return ROUTE_MASK;
-  if (r.has(NM_ROUTE_ACT_SX)) return ROUTE_SX;
-  return t >= 512 ? ROUTE_SX : ROUTE_FUSED;
+  return ROUTE_SX;
 }
 
 // ----------------------------------------------------- no-allocation entry point ---
@@ -140,6 +141,44 @@ int64_t mask_words(int64_t t, int64_t k) { return t * ((k + 31) / 32); }
 constexpr int64_t kFewMaxT = 128;
 
 bool use_few(int64_t t, const nml::Route& r) { return t <= kFewMaxT && !r.has(NM_ROUTE_NO_FEW); }
+
+// Above the few-token range, a shape with fewer than 128 tiles of 256 x 256 leaves most
+// of the 256 CUs idle on the large-tile kernels (one workgroup per tile, each running the
+// whole reduction).  There the split-K 128-row tile kernel of the few-token products
+// takes the call: its reduction splits fill the chip, and a second kernel sums the
+// partial tiles (workspace) in split order.  Measured on gfx950 (graph replays, cold
+// weights, us, large-tile route -> split):
+//   8:16 S(X) x bf16 4096 x 14336: 192 tokens 263 -> 58, 512: 304 -> 96, 1536: 321 -> 243;
+//   8:16 S(X) x bf16 14336 x 4096: 192: 87 -> 49, 384: 107 -> 81, 512: 108 -> 88;
+//   lowered 6:8 4096 x 4096: 256: 161 -> 36, 1024: 166 -> 72, 1536: 200 -> 122;
+//   2:4 4096 x 4096: 256: 107 -> 28, 1024: 109 -> 44, 1536: 129 -> 73.
+// From 128 large tiles on, the large-tile kernels are as fast or faster (4096 x 4096 2:4
+// at 3072 tokens: 81 against 110 us).  The NM_ROUTE_NO_FEW, NM_ROUTE_TILE_REGS and
+// NM_ROUTE_TILE_LDS hints keep the large-tile kernels.
+bool mid_split_ok(int64_t t, int64_t o, const nml::Route& r) {
+  return t > kFewMaxT && !r.has(NM_ROUTE_NO_FEW) && !r.has(NM_ROUTE_TILE_REGS) && !r.has(NM_ROUTE_TILE_LDS) &&
+         ((o + 255) / 256) * ((t + 255) / 256) < 128;
+}
+
+// Dense weights on an activation operand that is already S(X) (PRO_NONE), above the
+// few-token range: the split tile kernel by the rule above, else the large-tile kernels.
+bool mid_split_dense(const nml::GemmArgs& g) {
+  return mid_split_ok(g.t, g.o, g.route) && g.prologue == nml::PRO_NONE && nml::gemm_lds_small_eligible(g);
+}
+
+// Partial-sum bytes the split reserves in a large-token dense call's workspace (0 when
+// the rule does not split; its eligibility is checked at the call, so this may over-reserve).
+int64_t mid_split_dense_bytes(int64_t t, int64_t o, int64_t k, const nml::Route& r) {
+  if (!mid_split_ok(t, o, r)) return 0;
+  nml::GemmArgs g{};
+  g.t = t; g.o = o; g.k = k; g.route = r;
+  return nml::gemm_lds_small_part_bytes(g);
+}
+
+nm_status run_dense_large(const nml::GemmArgs& g, float* part, int64_t part_bytes, hipStream_t s) {
+  if (mid_split_dense(g)) return hip_status(nml::launch_gemm_lds_small(g, part, part_bytes, s));
+  return hip_status(nml::launch_gemm_dense(g, s));
+}
 
 inline int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
 
@@ -216,9 +255,11 @@ inline int64_t lift_ld(int64_t kp) { return (kp + 7) / 8 * 8; }
 // loads do); the streaming kernel otherwise.  Measured on gfx950: 6:8 lowered 4096 x
 // 4096 at 128 tokens 30 vs 58 us, at 24 / 32 tokens 16.9 / 18.0 vs 20.0 / 22.3 us (tile
 // against stream), 14336 x 4096 at 16 tokens 40 vs 56 us; 2:4 14336 x 4096 at 33 tokens
-// 31 vs 38 us.  The NM_ROUTE_FEW_STREAM / NM_ROUTE_FEW_TILE hints force either.
+// 31 vs 38 us.  The NM_ROUTE_FEW_STREAM / NM_ROUTE_FEW_TILE hints force either.  Above
+// the few-token range the same kernel takes shapes with too few large tiles (mid_split_ok).
 bool sp_few_tile(const nml::SparseArgs& sa) {
   if (!nml::gemm_lds_sp_eligible(sa, true)) return false;
+  if (sa.t > kFewMaxT) return mid_split_ok(sa.t, sa.o, sa.route);   // above the few-token range
   if (sa.route.has(NM_ROUTE_FEW_TILE)) return true;
   if (sa.route.has(NM_ROUTE_FEW_STREAM)) return false;
   return (sa.t > 32 && sa.o >= 2048) || (sa.t > 16 && (sa.o >= 8192 || (sa.lift_dma && sa.o >= 2048)));
@@ -324,7 +365,7 @@ nml::FewArgs w8a8_few_args(const nm_spmm_args* a, int64_t kc, const uint8_t* xq,
 int64_t w8a8_part_bytes(const nm_spmm_args* a, int64_t kc) {
   const nml::SparseArgs sa = w8a8_args(a, kc, nullptr, nullptr, false);
   if (w8a8_stream(a, sa.route)) return nml::few_partial_bytes(w8a8_few_args(a, kc, nullptr, nullptr, sa.route));
-  return use_few(a->t, sa.route) ? nml::gemm_lds_sp_small_part_bytes(sa) : 0;
+  return use_few(a->t, sa.route) || mid_split_ok(a->t, a->o, sa.route) ? nml::gemm_lds_sp_small_part_bytes(sa) : 0;
 }
 int64_t w8a8_ws_bytes(const nm_spmm_args* a, int64_t kc) {
   return w8a8_layout(a->t, a->o, kc, w8a8_part_bytes(a, kc)).total;
@@ -354,9 +395,10 @@ nm_status w8a8_product(const nm_spmm_args* a, int64_t kc, int ns, hipStream_t s)
   if (w8a8_stream(a, sa.route))
     return hip_status(nml::launch_few(w8a8_few_args(a, kc, xq, xs, sa.route),
                                       reinterpret_cast<float*>(ws + L.part), L.total - L.part, s));
-  // few tokens: the split tile kernel reads the row-major positions (a blocked copy would
-  // cost a launch of about the product's own length); above that the blocked copy pays
-  if (use_few(a->t, sa.route))
+  // few tokens, or too few large tiles to fill the chip: the split tile kernel reads the
+  // row-major positions (a blocked copy would cost a launch of about the product's own
+  // length); above that the blocked copy pays
+  if (use_few(a->t, sa.route) || mid_split_ok(a->t, a->o, sa.route))
     return hip_status(nml::launch_gemm_lds_sp_small(sa, reinterpret_cast<float*>(ws + L.part), L.total - L.part, s));
   uint8_t* blk = reinterpret_cast<uint8_t*>(ws + L.meta);
   if (nml::launch_meta_block(sa.w_meta, sa.o, kc, 16, blk, s) != hipSuccess) return NM_EHIP;
@@ -640,6 +682,11 @@ int64_t nm_spmm_workspace_size(const nm_spmm_args* a) {
     if (a->mode == NM_W_SLIDE && (a->ns < 2 || a->ns > 8 || a->k % (2 * a->ns))) return 0;
     if (a->mode == NM_W_COMPRESSED && a->k % 4) return 0;
     const int64_t kc = w_mode_kc(a);
+    if (a->t > kFewMaxT) {
+      // the split tile kernel when the large tiles would not fill the chip
+      const int64_t tile = w_mode_tile_bytes(a, kc, a->mode == NM_W_SLIDE ? a->ns : 2);
+      if (tile >= 0) return tile;
+    }
     nml::SparseArgs sa = w_mode_sparse_args(a, kc, a->mode == NM_W_SLIDE ? a->ns : 2, false);
     // a lifted copy of X only where the tile loads do not lift it themselves
     const bool lifted_loads = sa.lift_dma && nml::gemm_sparse_uses_lds(sa);
@@ -648,6 +695,11 @@ int64_t nm_spmm_workspace_size(const nm_spmm_args* a) {
     return mb > 0 ? lift + mb : lift;
   }
   const int64_t widen = fp8_widen_bytes(a);
+  if (a->mode == NM_ACT_DYNAMIC || a->mode == NM_ACT_COMPRESSED || (a->mode == NM_ACT_MASKED && a->x_meta == nullptr)) {
+    // [staging][widened W][partial sums of the split tile kernel]
+    const int64_t mid = mid_split_dense_bytes(a->t, a->o, a->k, r);
+    if (mid > 0) return align256(stage) + (widen > 0 ? align256(widen) : 0) + mid;
+  }
   return widen > 0 ? align256(stage) + widen : stage;
 }
 
@@ -766,7 +818,7 @@ nm_status spmm_impl(const nm_spmm_args* a, void* stream, bool noalloc) {
         R.note(NM_TAKEN_DECOMPRESS);
         g.x = xd; g.ldx = K; g.prologue = nml::PRO_NONE;
         if (use_few(T, R)) return run_dense_few(g, part, part_avail, s);
-        return hip_status(nml::launch_gemm_dense(g, s));
+        return run_dense_large(g, part, part_avail, s);
       }
 
       g.x = (const uint16_t*)a->x; g.ldx = a->ldx;
@@ -774,7 +826,7 @@ nm_status spmm_impl(const nm_spmm_args* a, void* stream, bool noalloc) {
         g.prologue = a->x_meta != nullptr ? nml::PRO_MASK : nml::PRO_NONE;
         g.x_mask = (const uint32_t*)a->x_meta;
         if (a->x_meta == nullptr && use_few(T, R)) return run_dense_few(g, part, part_avail, s);
-        return hip_status(nml::launch_gemm_dense(g, s));
+        return run_dense_large(g, part, part_avail, s);
       }
 
       // ACT_DYNAMIC with the activation mitigations: the shifted selection (and the VAR
@@ -795,7 +847,7 @@ nm_status spmm_impl(const nm_spmm_args* a, void* stream, bool noalloc) {
         g.row_shift = dyn ? mu : nullptr;
         g.col_shift = a->col_shift;
         if (use_few(T, R)) return run_dense_few(g, part, part_avail, s);
-        return hip_status(nml::launch_gemm_dense(g, s));
+        return run_dense_large(g, part, part_avail, s);
       }
       // ACT_DYNAMIC, one token with K-major weights: select and gather the kept K-rows
       if (gather1_route(a)) {
@@ -843,7 +895,7 @@ nm_status spmm_impl(const nm_spmm_args* a, void* stream, bool noalloc) {
         sa.t = O; sa.o = T; sa.y = a->y; sa.ldy = a->ldy; sa.accumulate = a->accumulate; sa.trans_out = 1;
         return hip_status(nml::launch_gemm_sparse(sa, s));
       }
-      const ActRoute route = act_route(T, R);
+      const ActRoute route = act_route(R);
       uint32_t* mask = a->x_mask_out;
       if (route == ROUTE_SX && have_ws) {
         uint16_t* sx = (uint16_t*)a->workspace;
@@ -853,14 +905,18 @@ nm_status spmm_impl(const nm_spmm_args* a, void* stream, bool noalloc) {
         R.note(NM_TAKEN_SELECT);
         g.prologue = nml::PRO_NONE; g.x = sx; g.ldx = K;
         const int64_t widen = fp8_widen_bytes(a), woff = align256(stage);
+        int64_t poff = woff;   // [S(X)][widened W][partial sums]
         if (widen > 0 && a->workspace_bytes >= woff + widen) {
           uint16_t* wb = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(a->workspace) + woff);
           e = nml::launch_widen_fp8((const uint8_t*)a->w, a->ldw, O, K, wb, s);
           if (e != hipSuccess) return NM_EHIP;
           R.note(NM_TAKEN_WIDEN);
           g.w = wb; g.ldw = K; g.w_fp8 = 0;   // w_scale stays: applied in the epilogue
+          poff = woff + align256(widen);
         }
-        return hip_status(nml::launch_gemm_dense(g, s));
+        int64_t pavail = 0;
+        float* pp = ws_slice(a->workspace, a->workspace_bytes, poff, &pavail);
+        return run_dense_large(g, pp, pavail, s);
       }
       if (route == ROUTE_MASK && (mask != nullptr || have_ws)) {
         if (mask == nullptr) mask = (uint32_t*)a->workspace;
@@ -908,7 +964,8 @@ nm_status spmm_impl(const nm_spmm_args* a, void* stream, bool noalloc) {
       if (T == 0 || O == 0) return NM_OK;
       if (K == 0) return a->accumulate ? NM_OK : zero_output(a->y, T, O, a->ldy, s);
       const nml::Route R = route_of(a, true);
-      if (use_few(T, R)) {
+      if (use_few(T, R) || T > kFewMaxT) {
+        // the split tile kernel (few tokens, or too few large tiles to fill the chip)
         const int64_t tile = w_mode_tile_bytes(a, kc, ns);
         if (tile == 0 || (tile > 0 && a->workspace != nullptr && a->workspace_bytes >= tile)) {
           nml::SparseArgs sa = w_mode_sparse_args(a, kc, ns, true);
@@ -924,8 +981,9 @@ nm_status spmm_impl(const nm_spmm_args* a, void* stream, bool noalloc) {
           return hip_status(nml::launch_gemm_lds_sp_small(
               sa, reinterpret_cast<float*>(reinterpret_cast<char*>(a->workspace) + off), a->workspace_bytes - off, s));
         }
-        return hip_status(nml::launch_few(few_sparse_args(a, kc, ns), (float*)a->workspace,
-                                          a->workspace ? a->workspace_bytes : 0, s));
+        if (use_few(T, R))
+          return hip_status(nml::launch_few(few_sparse_args(a, kc, ns), (float*)a->workspace,
+                                            a->workspace ? a->workspace_bytes : 0, s));
       }
       nml::SparseArgs sa{};
       sa.route = R;
@@ -1140,13 +1198,14 @@ int64_t nm_hybrid_gemm_workspace_size(int64_t t, int64_t k_s, int64_t k_d, int64
   r.flags = route;
   const int64_t stage = gathered ? t * hybrid_ldp(k_s, k_d) * 2 : 0;
   int64_t part = 0;
-  if (use_few(t, r)) {
+  if (use_few(t, r) || t > kFewMaxT) {
     const int64_t ldp = gathered ? hybrid_ldp(k_s, k_d) : k_s + k_d;
     const nml::SparseArgs sa = hybrid_sparse_args(nullptr, ldp, gathered ? hybrid_off1(k_s) : k_s, t, k_s, k_d,
                                                   nullptr, nullptr, nullptr, k_d, o, nullptr, o, 0, r);
-    part = sp_few_tile(sa) ? nml::gemm_lds_sp_small_part_bytes(sa)
-                           : nml::few_partial_bytes(few_hybrid_args(nullptr, ldp, 0, t, k_s, k_d, nullptr, nullptr,
-                                                                    nullptr, k_d, o, nullptr, o, 0, r));
+    if (sp_few_tile(sa)) part = nml::gemm_lds_sp_small_part_bytes(sa);
+    else if (use_few(t, r))
+      part = nml::few_partial_bytes(few_hybrid_args(nullptr, ldp, 0, t, k_s, k_d, nullptr, nullptr, nullptr, k_d, o,
+                                                    nullptr, o, 0, r));
   }
   if (part > 0) return align256(stage) + part;
   if (!use_few(t, r) && k_s > 0) {
@@ -1213,14 +1272,16 @@ nm_status nm_hybrid_gemm(const void* x, int64_t t, int64_t ldx, const int32_t* s
   }
   nml::SparseArgs sa = hybrid_sparse_args(xa, lda, dbase, t, k_s, k_d, ws_values, ws_meta, wd, ldwd, o, y, ldy,
                                           accumulate, R);
-  if (use_few(t, R)) {
+  if (use_few(t, R) || t > kFewMaxT) {
+    // the split tile kernel (few tokens, or too few large tiles to fill the chip)
     int64_t avail = 0;
     float* part = ws_slice(workspace, workspace_bytes, stage > 0 ? align256(stage) : 0, &avail);
     if (sp_few_tile(sa) && avail >= nml::gemm_lds_sp_small_part_bytes(sa))
       return hip_status(nml::launch_gemm_lds_sp_small(sa, part, avail, s));
-    return hip_status(nml::launch_few(few_hybrid_args(xa, lda, dbase, t, k_s, k_d, ws_values, ws_meta, wd, ldwd, o,
-                                                      y, ldy, accumulate, R),
-                                      part, avail, s));
+    if (use_few(t, R))
+      return hip_status(nml::launch_few(few_hybrid_args(xa, lda, dbase, t, k_s, k_d, ws_values, ws_meta, wd, ldwd, o,
+                                                        y, ldy, accumulate, R),
+                                        part, avail, s));
   }
   if ((st = use_meta_block(sa, workspace, workspace_bytes, stage > 0 ? align256(stage) : 0, s))) return st;
   return hip_status(nml::launch_gemm_sparse(sa, s));

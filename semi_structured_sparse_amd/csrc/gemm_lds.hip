@@ -439,7 +439,7 @@ static int64_t small_splits(const GemmArgs& a) {
 }
 
 bool gemm_lds_small_eligible(const GemmArgs& a) {
-  return a.prologue == PRO_NONE && a.k % BK == 0 && a.k > 0 && w_rows_ok(a) && (a.ldx % 8) == 0 && a.t <= 128;
+  return a.prologue == PRO_NONE && a.k % BK == 0 && a.k > 0 && w_rows_ok(a) && (a.ldx % 8) == 0;
 }
 
 int64_t gemm_lds_small_part_bytes(const GemmArgs& a) {

@@ -98,7 +98,8 @@ bool gemm_lds_eligible(const GemmArgs& a, bool any_size);
 hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t s);
 // fp8 e4m3fn weights [o][ldw] bytes -> bf16 [o][k] (exact), k % 8 == 0
 hipError_t launch_widen_fp8(const uint8_t* w8, int64_t ldw, int64_t o, int64_t k, uint16_t* wb, hipStream_t s);
-// few-token split-K variant (T <= 128, PRO_NONE, bf16): with part (scratch of at least
+// split-K variant with 128-row tiles (PRO_NONE; few tokens, and token counts whose
+// 256 x 256 tiles would not fill the chip): with part (scratch of at least
 // gemm_lds_small_part_bytes(a) bytes) the K slices write fp32 partial tiles that a second
 // kernel sums in slice order; without it, one slice.
 bool gemm_lds_small_eligible(const GemmArgs& a);
@@ -173,7 +174,8 @@ hipError_t launch_gather_rows(const uint16_t* w, int64_t ldw, int64_t o, int64_t
 // direct-to-LDS variant for large problems (plain loader, kc % 64 == 0, kd % 64 == 0)
 bool gemm_lds_sp_eligible(const SparseArgs& a, bool any_size);
 hipError_t launch_gemm_lds_sp(const SparseArgs& a, hipStream_t s);
-// few-token split variant (same eligibility with any_size): with part (scratch of at least
+// split variant with 128-row tiles (same eligibility with any_size; few tokens, and
+// token counts whose 256 x 256 tiles would not fill the chip): with part (scratch of at least
 // gemm_lds_sp_small_part_bytes(a) bytes) the splits write fp32 partial tiles that a second
 // kernel sums in split order; without it, one split.
 int64_t gemm_lds_sp_small_part_bytes(const SparseArgs& a);

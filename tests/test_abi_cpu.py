@@ -75,6 +75,24 @@ def test_route_fields_change_routes_not_results_host_side():
         assert re.search(rf"NM_TAKEN_{name.upper()} = 1u << {i}\b", src), name
 
 
+def test_mid_range_workspace_holds_the_split_partials():
+    """Above 128 tokens, a product whose 256 x 256 output tiles number under 128 takes the
+    split tile kernel: the workspace query adds its partial tiles (splits x t x o fp32,
+    splits = 256 // 128-row tiles, at most half the K-steps) after the staging; the
+    no_few and tile hints keep the large-tile kernels and ask for no partials."""
+    t, o, k = 300, 4096, 14336
+    a = spmm_args(t=t, o=o, k=k, n=8, m=16, ldx=k, ldw=k, ldy=o)
+    stage = -(-(t * k * 2 + 64) // 256) * 256
+    splits = 256 // (32 * 3)
+    assert S.nm_spmm_workspace_size(a) == stage + splits * t * o * 4
+    for hint in ("no_few", "tile_lds", "tile_regs"):
+        a.route = S.route_bits(hint)
+        assert S.nm_spmm_workspace_size(a) == t * k * 2 + 64, hint
+    # enough large tiles: no partials
+    a = spmm_args(t=4096, o=o, k=k, n=8, m=16, ldx=k, ldw=k, ldy=o)
+    assert S.nm_spmm_workspace_size(a) == 4096 * k * 2 + 64
+
+
 def test_status_strings_and_version():
     for code in range(7):
         assert S.nm_status_str(code).startswith("NM_")

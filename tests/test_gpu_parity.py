@@ -744,13 +744,13 @@ def down_full():
 
 @pytest.mark.parametrize("route", ["fused", "mask", "sx"])
 def test_spmm_act_full_size_sampled(route, down_full):
-    """8:16 down-projection at 2048 and 8192 tokens: the mask of every row bit-exact, every
-    output written, random projections of the whole output, and the oracle on one row of
-    every 128-row band."""
+    """8:16 down-projection at 300 (the split tile kernel on the default route), 2048 and
+    8192 tokens: the mask of every row bit-exact, every output written, random projections
+    of the whole output, and the oracle on one row of every 128-row band."""
     print(f"act full route={route}", flush=True)
     x_all, w, sx_all, mask_all = down_full
     wv = O.bf16_to_f64(w)
-    for t in (2048, 8192):
+    for t in (300, 2048, 8192):
         x = x_all[:t]
         y, mask = run_act(x, w, 8, 16, route=route)
         assert (mask == mask_all[:t]).all()
@@ -1011,6 +1011,81 @@ def run_hybrid(x, sc, ks, dc, kd, wv, wm, wdd, o, ldwd=None, accumulate=0):
     LAST_TAKEN[0] = rep.value
     sync()
     return host(y, np.float32)
+
+
+@pytest.mark.parametrize("kind", ["act", "act_fp8", "w24", "slide", "slide_copy", "hybrid", "w8a8"])
+@pytest.mark.parametrize("t", [200, 700])
+def test_mid_range_split_tile(kind, t):
+    """Above 128 tokens, shapes whose 256 x 256 output tiles would not fill the chip run on
+    the split-K 128-row tile kernel with partial tiles in the workspace, for every weight
+    kind on its default route: 8:16 activations (select, then the product) on bf16 and fp8
+    weights, 2:4, lowered 6:8 with the lift in the tile loads or (lift_copy hint) staged,
+    the hybrid format, fp8 weights with fp8 activations.  Ragged T and O (9 row tiles, 2 or
+    6 token tiles), the oracle on every row; the no_few hint keeps the large-tile kernels."""
+    print(f"mid-range split kind={kind} t={t}", flush=True)
+    rng = np.random.default_rng(t + len(kind))
+    o, k = 1040, 2048
+    x = synth.student_t_bf16(rng, (t, k), 4.0, 0.5)
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+
+    def routes(fn, extra=()):
+        with use_route(*extra):
+            y = fn()
+            tk = taken()
+            assert {"tile_split", "tile_lds"} <= tk, (kind, tk)
+            with use_route("no_few"):
+                y_large = fn()
+                assert "tile_split" not in taken(), (kind, taken())
+        return y, y_large, tk
+
+    if kind in ("act", "act_fp8"):
+        sx, keep = O.sparsify(x, 8, 16)
+        if kind == "act":
+            ref, wv = O.gemm(sx, w), w
+            fn = lambda: run_act(x, w, 8, 16)
+        else:
+            q, sc = synth.fp8_e4m3_quantize_rows(w)
+            ref, wv = O.spmm_act_fp8(x, q, sc, 8, 16), O.fp8_e4m3_to_f64(q) * sc[:, None].astype(np.float64)
+            fn = lambda: run_act(x, None, 8, 16, w8=q, s8=sc)
+        (y, mask), (y_large, mask_large), tk = routes(fn)
+        assert "select" in tk, tk
+        assert (mask == O.pack_mask(keep)).all() and (mask_large == mask).all()
+        for yy, lab in ((y, "split"), (y_large, "large")):
+            check_gemm(yy, ref, sx, wv, label=f"mid {kind} t={t} {lab}")
+    elif kind == "w24":
+        v, mt = gpu_compress_2of4(w)
+        pr, _ = O.sparsify(w, 2, 4)
+        y, y_large, tk = routes(lambda: run_w(S.NM_W_COMPRESSED, x, v, mt, o, k))
+        assert "sparse_mma" in tk, tk
+        for yy, lab in ((y, "split"), (y_large, "large")):
+            check_gemm(yy, O.gemm(x, pr), x, pr, label=f"mid 2:4 t={t} {lab}")
+    elif kind in ("slide", "slide_copy"):
+        vp, mp = slide_pack_gpu(w, 4)
+        pr, _ = O.sparsify(w, 6, 8)
+        extra = ("lift_copy",) if kind == "slide_copy" else ()
+        y, y_large, tk = routes(lambda: run_w(S.NM_W_SLIDE, x, vp, mp, o, k, ns=4), extra)
+        assert ("lift" in tk) == (kind == "slide_copy"), tk
+        for yy, lab in ((y, "split"), (y_large, "large")):
+            check_gemm(yy, O.gemm(x, pr), x, pr, label=f"mid {kind} t={t} {lab}")
+    elif kind == "hybrid":
+        kd = 256
+        sc, dc, wv, wm, wdd = hybrid_pack_gpu(w, kd)
+        sync()
+        sp, de, hv, hi, hwd = O.hybrid_pack(w, kd)
+        wh = w.copy()
+        wh[:, sp] = O.decompress(hv, hi, 2, 4, k - kd)
+        y, y_large, tk = routes(lambda: run_hybrid(x, sc, k - kd, dc, kd, wv, wm, wdd, o))
+        ref = O.hybrid_gemm(x, sp, de, hv, hi, hwd)
+        for yy, lab in ((y, "split"), (y_large, "large")):
+            check_gemm(yy, ref, x, wh, label=f"mid hybrid t={t} {lab}")
+    else:
+        w8, idx, wsc = w8a8_weights(rng, o, k, 4)
+        ref = O.spmm_w8a8_slide(x, w8, idx, wsc, k, 4)
+        a_v, b_v = w8a8_operands(x, w8, idx, wsc, k, 4)
+        y, y_large, tk = routes(lambda: run_w8a8(x, w8, idx, wsc, o, k, 4))
+        assert "quant" in tk, tk
+        for yy, lab in ((y, "split"), (y_large, "large")):
+            check_gemm_vals(yy, ref, a_v, b_v, label=f"mid w8a8 t={t} {lab}")
 
 
 @pytest.mark.parametrize("t,o,kc", [(300, 264, 1088), (257, 130, 64), (512, 520, 2112)])
