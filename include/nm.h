@@ -395,12 +395,15 @@ nm_status nm_spmm(const nm_spmm_args* args, void* stream);
 /*
  * nm_spmm_noalloc -- nm_spmm for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid allocation).  It computes
- * exactly what nm_spmm computes (the same kernels and routes, bit-identical results) but
- * takes its scratch from a buffer inside the library instead of args->workspace, which
- * must be NULL with workspace_bytes 0 (NM_EINVAL otherwise):
+ * what nm_spmm computes (the same kernels and routes, bit-identical results, except as
+ * below) but takes its scratch from a buffer inside the library instead of
+ * args->workspace, which must be NULL with workspace_bytes 0 (NM_EINVAL otherwise):
  *   - the buffer is NM_NOALLOC_SCRATCH_BYTES (64 MiB) of device memory per GPU, part of the
- *     library's code object, held until the process ends; a call whose
- *     nm_spmm_workspace_size exceeds it returns NM_ESCRATCH and enqueues nothing;
+ *     library's code object, held until the process ends;
+ *   - when nm_spmm_workspace_size exceeds it because the preferred route splits the
+ *     reduction of its 256 x 256 tiles, the call runs those tiles unsplit (another
+ *     summation order, the same tolerance); a call that still needs more returns
+ *     NM_ESCRATCH and enqueues nothing;
  *   - the first call on a GPU looks up that GPU's copy of the buffer (no allocation);
  *   - every call on a GPU shares that GPU's buffer: calls that may overlap in time on one
  *     GPU (different streams, or different threads without ordering) race on it and must

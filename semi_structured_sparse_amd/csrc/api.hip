@@ -142,43 +142,90 @@ constexpr int64_t kFewMaxT = 128;
 
 bool use_few(int64_t t, const nml::Route& r) { return t <= kFewMaxT && !r.has(NM_ROUTE_NO_FEW); }
 
-// Above the few-token range, a shape with fewer than 128 tiles of 256 x 256 leaves most
-// of the 256 CUs idle on the large-tile kernels (one workgroup per tile, each running the
-// whole reduction).  There the split-K 128-row tile kernel of the few-token products
-// takes the call: its reduction splits fill the chip, and a second kernel sums the
-// partial tiles (workspace) in split order.  Measured on gfx950 (graph replays, cold
-// weights, us, large-tile route -> split):
-//   8:16 S(X) x bf16 4096 x 14336: 192 tokens 263 -> 58, 512: 304 -> 96, 1536: 321 -> 243;
-//   8:16 S(X) x bf16 14336 x 4096: 192: 87 -> 49, 384: 107 -> 81, 512: 108 -> 88;
-//   lowered 6:8 4096 x 4096: 256: 161 -> 36, 1024: 166 -> 72, 1536: 200 -> 122;
-//   2:4 4096 x 4096: 256: 107 -> 28, 1024: 109 -> 44, 1536: 129 -> 73.
-// From 128 large tiles on, the large-tile kernels are as fast or faster (4096 x 4096 2:4
-// at 3072 tokens: 81 against 110 us).  The NM_ROUTE_NO_FEW, NM_ROUTE_TILE_REGS and
-// NM_ROUTE_TILE_LDS hints keep the large-tile kernels.
-bool mid_split_ok(int64_t t, int64_t o, const nml::Route& r) {
-  return t > kFewMaxT && !r.has(NM_ROUTE_NO_FEW) && !r.has(NM_ROUTE_TILE_REGS) && !r.has(NM_ROUTE_TILE_LDS) &&
-         ((o + 255) / 256) * ((t + 255) / 256) < 128;
+// Above the few-token range, 256 x 256 output tiles that number under 256 leave CUs idle on
+// the large-tile kernels (one workgroup per tile, each running the whole reduction).  Two
+// remedies, chosen per call by large_plan:
+//   split: the large-tile kernel with its reduction split in 2-4 K ranges (at most one
+//     round of workgroups), when each range keeps enough K-steps to outweigh writing and
+//     re-reading the partial tiles: 100 steps of 64 for the dense kernel, 24 for the
+//     sparse kernel (whose steps take about twice as long);
+//   mid: otherwise, under 128 tiles, the split-K 128-row tile kernel of the few-token
+//     products, whose splits fill the chip.
+// A second kernel sums the partial tiles (workspace) in split order.  Measured on gfx950
+// (graph replays, cold weights, us, unsplit large-tile route -> plan):
+//   8:16 S(X) x bf16 4096 x 14336: 192 tokens 263 -> 58 (mid), 512: 304 -> 96 (mid),
+//     1024: 310 -> 144 (mid), 1536: 321 -> 200 (split), 2048: 261 -> 242 (split);
+//   8:16 S(X) x bf16 14336 x 4096: 192: 87 -> 49 (mid), 512: 108 -> 88 (mid);
+//   lowered 6:8 4096 x 4096: 256: 161 -> 36 (mid), 1024: 166 -> 71 (mid), 1536: 200 -> 105
+//     (split), 2048: 126 -> 114 (split);
+//   2:4 4096 x 14336: 1024 / 1536 / 2048 tokens split 119 / 165 / 187 (mid 133 / 233 / 245).
+// The other choice, where measured, was slower: the dense 4096 x 14336 product at 1024
+// tokens split in four 157 us, 4096 x 4096 at 2048 tokens split in two 100 us against 77.
+// The NM_ROUTE_NO_FEW, NM_ROUTE_TILE_REGS and NM_ROUTE_TILE_LDS hints keep the unsplit
+// large-tile kernels.
+constexpr int64_t kMinSplitStepsDense = 100, kMinSplitStepsSparse = 24;
+
+// Internal route bit (not in nm.h): no split of the large tiles.  The no-allocation entry
+// point sets it when the split's partial tiles would not fit its buffer.
+constexpr uint32_t kRouteNoLargeSplit = 1u << 31;
+
+enum class Large { kTiles, kMid, kSplit };
+struct LargePlan {
+  Large kind;
+  int64_t splits;
+};
+
+// steps: the product's K-steps (64 positions; 128 for the fp8 sparse kernel)
+LargePlan large_plan(int64_t t, int64_t o, int64_t steps, int64_t min_steps, const nml::Route& r) {
+  if (t <= kFewMaxT || r.has(NM_ROUTE_NO_FEW) || r.has(NM_ROUTE_TILE_REGS) || r.has(NM_ROUTE_TILE_LDS))
+    return {Large::kTiles, 1};
+  const int64_t tiles = ((o + 255) / 256) * ((t + 255) / 256);
+  const int64_t sp = tiles > 0 ? 256 / tiles : 1;
+  if (sp >= 2 && sp <= 4 && steps / sp >= min_steps && !r.has(kRouteNoLargeSplit)) return {Large::kSplit, sp};
+  return {tiles < 128 ? Large::kMid : Large::kTiles, 1};
 }
+
+LargePlan dense_plan(const nml::GemmArgs& g) { return large_plan(g.t, g.o, g.k / 64, kMinSplitStepsDense, g.route); }
 
 // Dense weights on an activation operand that is already S(X) (PRO_NONE), above the
-// few-token range: the split tile kernel by the rule above, else the large-tile kernels.
-bool mid_split_dense(const nml::GemmArgs& g) {
-  return mid_split_ok(g.t, g.o, g.route) && g.prologue == nml::PRO_NONE && nml::gemm_lds_small_eligible(g);
-}
-
-// Partial-sum bytes the split reserves in a large-token dense call's workspace (0 when
-// the rule does not split; its eligibility is checked at the call, so this may over-reserve).
-int64_t mid_split_dense_bytes(int64_t t, int64_t o, int64_t k, const nml::Route& r) {
-  if (!mid_split_ok(t, o, r)) return 0;
-  nml::GemmArgs g{};
-  g.t = t; g.o = o; g.k = k; g.route = r;
-  return nml::gemm_lds_small_part_bytes(g);
-}
-
+// few-token range, by the plan: the split large tiles, the split 128-row tiles, or the
+// large-tile kernels (which also take every other prologue).
 nm_status run_dense_large(const nml::GemmArgs& g, float* part, int64_t part_bytes, hipStream_t s) {
-  if (mid_split_dense(g)) return hip_status(nml::launch_gemm_lds_small(g, part, part_bytes, s));
+  if (g.prologue == nml::PRO_NONE) {
+    const LargePlan p = dense_plan(g);
+    if (p.kind == Large::kSplit && nml::gemm_lds_eligible(g, true))
+      return hip_status(nml::launch_gemm_lds_split(g, p.splits, part, part_bytes, s));
+    if (p.kind == Large::kMid && nml::gemm_lds_small_eligible(g))
+      return hip_status(nml::launch_gemm_lds_small(g, part, part_bytes, s));
+  }
   return hip_status(nml::launch_gemm_dense(g, s));
 }
+
+// Partial-sum bytes a large-token dense call reserves in its workspace for the plan (the
+// kernels' eligibility is checked at the call, so this may over-reserve).
+int64_t dense_large_part_bytes(int64_t t, int64_t o, int64_t k, const nml::Route& r) {
+  nml::GemmArgs g{};
+  g.t = t; g.o = o; g.k = k; g.route = r;
+  const LargePlan p = dense_plan(g);
+  if (p.kind == Large::kSplit) return p.splits * t * o * 4;
+  if (p.kind == Large::kMid) return nml::gemm_lds_small_part_bytes(g);
+  return 0;
+}
+
+LargePlan sparse_plan(const nml::SparseArgs& sa) {
+  return large_plan(sa.t, sa.o, sa.f8 ? sa.kc / 128 : (sa.kc + sa.kd) / 64, kMinSplitStepsSparse, sa.route);
+}
+
+// Splits of the plan for a large-token 2:4-family product on the direct-to-LDS kernel (1
+// when the plan does not split or the kernel does not take the shape).
+int64_t sparse_splits(const nml::SparseArgs& sa) {
+  const LargePlan p = sparse_plan(sa);
+  return p.kind == Large::kSplit && nml::gemm_lds_sp_eligible(sa, true) ? p.splits : 1;
+}
+
+// Large-token 2:4-family products on the direct-to-LDS kernel: by its size rule or a
+// hint, or split by the plan.
+bool sparse_lds_large(const nml::SparseArgs& sa) { return nml::gemm_sparse_uses_lds(sa) || sparse_splits(sa) > 1; }
 
 inline int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
 
@@ -256,10 +303,10 @@ inline int64_t lift_ld(int64_t kp) { return (kp + 7) / 8 * 8; }
 // 4096 at 128 tokens 30 vs 58 us, at 24 / 32 tokens 16.9 / 18.0 vs 20.0 / 22.3 us (tile
 // against stream), 14336 x 4096 at 16 tokens 40 vs 56 us; 2:4 14336 x 4096 at 33 tokens
 // 31 vs 38 us.  The NM_ROUTE_FEW_STREAM / NM_ROUTE_FEW_TILE hints force either.  Above
-// the few-token range the same kernel takes shapes with too few large tiles (mid_split_ok).
+// the few-token range the same kernel takes the mid plan of large_plan.
 bool sp_few_tile(const nml::SparseArgs& sa) {
   if (!nml::gemm_lds_sp_eligible(sa, true)) return false;
-  if (sa.t > kFewMaxT) return mid_split_ok(sa.t, sa.o, sa.route);   // above the few-token range
+  if (sa.t > kFewMaxT) return sparse_plan(sa).kind == Large::kMid;   // above the few-token range
   if (sa.route.has(NM_ROUTE_FEW_TILE)) return true;
   if (sa.route.has(NM_ROUTE_FEW_STREAM)) return false;
   return (sa.t > 32 && sa.o >= 2048) || (sa.t > 16 && (sa.o >= 8192 || (sa.lift_dma && sa.o >= 2048)));
@@ -305,10 +352,10 @@ int64_t w_mode_tile_bytes(const nm_spmm_args* a, int64_t kc, int ns) {
 // workspace holds it (the NM_ROUTE_NO_META_BLOCK hint keeps the row-major positions).
 bool meta_block_wanted(const nml::SparseArgs& sa) {
   if (sa.route.has(NM_ROUTE_NO_META_BLOCK)) return false;
-  return sa.kc > 0 && sa.w_meta != nullptr && nml::gemm_sparse_uses_lds(sa);
+  return sa.kc > 0 && sa.w_meta != nullptr && sparse_lds_large(sa);
 }
 int64_t meta_block_ws(const nml::SparseArgs& sa) {
-  if (sa.route.has(NM_ROUTE_NO_META_BLOCK) || sa.kc <= 0 || !nml::gemm_sparse_uses_lds(sa)) return 0;
+  if (sa.route.has(NM_ROUTE_NO_META_BLOCK) || sa.kc <= 0 || !sparse_lds_large(sa)) return 0;
   return nml::meta_block_bytes(sa.o, sa.kc);
 }
 nm_status use_meta_block(nml::SparseArgs& sa, void* ws, int64_t ws_bytes, int64_t off, hipStream_t s) {
@@ -365,7 +412,10 @@ nml::FewArgs w8a8_few_args(const nm_spmm_args* a, int64_t kc, const uint8_t* xq,
 int64_t w8a8_part_bytes(const nm_spmm_args* a, int64_t kc) {
   const nml::SparseArgs sa = w8a8_args(a, kc, nullptr, nullptr, false);
   if (w8a8_stream(a, sa.route)) return nml::few_partial_bytes(w8a8_few_args(a, kc, nullptr, nullptr, sa.route));
-  return use_few(a->t, sa.route) || mid_split_ok(a->t, a->o, sa.route) ? nml::gemm_lds_sp_small_part_bytes(sa) : 0;
+  if (use_few(a->t, sa.route)) return nml::gemm_lds_sp_small_part_bytes(sa);
+  const LargePlan p = sparse_plan(sa);
+  if (p.kind == Large::kMid) return nml::gemm_lds_sp_small_part_bytes(sa);
+  return p.kind == Large::kSplit ? p.splits * a->t * a->o * 4 : 0;
 }
 int64_t w8a8_ws_bytes(const nm_spmm_args* a, int64_t kc) {
   return w8a8_layout(a->t, a->o, kc, w8a8_part_bytes(a, kc)).total;
@@ -395,15 +445,19 @@ nm_status w8a8_product(const nm_spmm_args* a, int64_t kc, int ns, hipStream_t s)
   if (w8a8_stream(a, sa.route))
     return hip_status(nml::launch_few(w8a8_few_args(a, kc, xq, xs, sa.route),
                                       reinterpret_cast<float*>(ws + L.part), L.total - L.part, s));
-  // few tokens, or too few large tiles to fill the chip: the split tile kernel reads the
-  // row-major positions (a blocked copy would cost a launch of about the product's own
-  // length); above that the blocked copy pays
-  if (use_few(a->t, sa.route) || mid_split_ok(a->t, a->o, sa.route))
+  // few tokens, or the mid plan: the split tile kernel reads the row-major positions (a
+  // blocked copy would cost a launch of about the product's own length); above that the
+  // blocked copy pays
+  const LargePlan p = sparse_plan(sa);
+  if (use_few(a->t, sa.route) || p.kind == Large::kMid)
     return hip_status(nml::launch_gemm_lds_sp_small(sa, reinterpret_cast<float*>(ws + L.part), L.total - L.part, s));
   uint8_t* blk = reinterpret_cast<uint8_t*>(ws + L.meta);
   if (nml::launch_meta_block(sa.w_meta, sa.o, kc, 16, blk, s) != hipSuccess) return NM_EHIP;
   sa.w_meta_blk = blk;
   sa.route.note(NM_TAKEN_META_BLOCK);
+  if (p.kind == Large::kSplit)
+    return hip_status(nml::launch_gemm_lds_sp_split(sa, p.splits, reinterpret_cast<float*>(ws + L.part),
+                                                    L.total - L.part, s));
   return hip_status(nml::launch_gemm_lds_sp(sa, s));
 }
 
@@ -688,17 +742,22 @@ int64_t nm_spmm_workspace_size(const nm_spmm_args* a) {
       if (tile >= 0) return tile;
     }
     nml::SparseArgs sa = w_mode_sparse_args(a, kc, a->mode == NM_W_SLIDE ? a->ns : 2, false);
-    // a lifted copy of X only where the tile loads do not lift it themselves
-    const bool lifted_loads = sa.lift_dma && nml::gemm_sparse_uses_lds(sa);
-    const int64_t lift = (a->mode == NM_W_SLIDE && !lifted_loads) ? align256(a->t * lift_ld(kc) * 2) : 0;
-    const int64_t mb = meta_block_ws(sa);
-    return mb > 0 ? lift + mb : lift;
+    // [lifted X][K-blocked positions][partial sums of the split large tiles]; a lifted copy
+    // of X only where the tile loads do not lift it themselves
+    const bool lifted_loads = sa.lift_dma && sparse_lds_large(sa);
+    int64_t lift = 0;
+    if (a->mode == NM_W_SLIDE && !lifted_loads) {
+      lift = align256(a->t * lift_ld(kc) * 2);
+      sa.loader = nml::XL_PLAIN; sa.lift_dma = 0; sa.ldx = lift_ld(kc);   // the kernel then reads the copy
+    }
+    const int64_t mb = meta_block_ws(sa), sp = sparse_splits(sa);
+    return lift + align256(mb) + (sp > 1 ? sp * a->t * a->o * 4 : 0);
   }
   const int64_t widen = fp8_widen_bytes(a);
   if (a->mode == NM_ACT_DYNAMIC || a->mode == NM_ACT_COMPRESSED || (a->mode == NM_ACT_MASKED && a->x_meta == nullptr)) {
-    // [staging][widened W][partial sums of the split tile kernel]
-    const int64_t mid = mid_split_dense_bytes(a->t, a->o, a->k, r);
-    if (mid > 0) return align256(stage) + (widen > 0 ? align256(widen) : 0) + mid;
+    // [staging][widened W][partial sums of the split tiles]
+    const int64_t part_l = dense_large_part_bytes(a->t, a->o, a->k, r);
+    if (part_l > 0) return align256(stage) + (widen > 0 ? align256(widen) : 0) + part_l;
   }
   return widen > 0 ? align256(stage) + widen : stage;
 }
@@ -717,15 +776,21 @@ nm_status spmm_impl(const nm_spmm_args* a, void* stream, bool noalloc) {
   // called where validation is complete, before the first HIP call
   auto bind_scratch = [&]() -> nm_status {
     if (!noalloc) return NM_OK;
-    const int64_t need = nm_spmm_workspace_size(a);
-    if (need > NM_NOALLOC_SCRATCH_BYTES) return NM_ESCRATCH;
-    if (need <= 0) return NM_OK;
-    hipError_t e = hipSuccess;
-    void* p = scratch_for_current_device(&e);
-    if (p == nullptr) return NM_EHIP;
     local = *a;
-    local.workspace = p;
-    local.workspace_bytes = need;
+    int64_t need = nm_spmm_workspace_size(&local);
+    if (need > NM_NOALLOC_SCRATCH_BYTES) {
+      // without the split of the large tiles (whose partial tiles may not fit the buffer)
+      local.route |= kRouteNoLargeSplit;
+      need = nm_spmm_workspace_size(&local);
+      if (need > NM_NOALLOC_SCRATCH_BYTES) return NM_ESCRATCH;
+    }
+    if (need > 0) {
+      hipError_t e = hipSuccess;
+      void* p = scratch_for_current_device(&e);
+      if (p == nullptr) return NM_EHIP;
+      local.workspace = p;
+      local.workspace_bytes = need;
+    }
     a = &local;
     return NM_OK;
   };
@@ -992,7 +1057,7 @@ nm_status spmm_impl(const nm_spmm_args* a, void* stream, bool noalloc) {
       sa.loader = a->mode == NM_W_SLIDE ? nml::XL_LIFT : nml::XL_PLAIN;
       sa.t = T; sa.o = O; sa.y = a->y; sa.ldy = a->ldy; sa.accumulate = a->accumulate; sa.trans_out = 0;
       sa.lift_dma = w_lift_dma(a) ? 1 : 0;
-      if (sa.lift_dma && !nml::gemm_sparse_uses_lds(sa)) sa.lift_dma = 0;   // register kernel: lift in its loader
+      if (sa.lift_dma && !sparse_lds_large(sa)) sa.lift_dma = 0;   // register kernel: lift in its loader
       int64_t off = 0;
       if (a->mode == NM_W_SLIDE && !sa.lift_dma && a->workspace != nullptr && a->workspace_bytes >= T * lift_ld(kc) * 2) {
         // materialise lift(X) once so the product kernel reads X with 16-byte loads
@@ -1004,6 +1069,13 @@ nm_status spmm_impl(const nm_spmm_args* a, void* stream, bool noalloc) {
         off = align256(T * lift_ld(kc) * 2);
       }
       if ((st = use_meta_block(sa, a->workspace, a->workspace_bytes, off, s))) return st;
+      if (const int64_t sp = sparse_splits(sa); sp > 1) {
+        // [lifted X][K-blocked positions][partial sums]
+        const int64_t poff = off + (sa.w_meta_blk != nullptr ? align256(nml::meta_block_bytes(sa.o, sa.kc)) : 0);
+        int64_t avail = 0;
+        float* part = ws_slice(a->workspace, a->workspace_bytes, poff, &avail);
+        return hip_status(nml::launch_gemm_lds_sp_split(sa, sp, part, avail, s));
+      }
       return hip_status(nml::launch_gemm_sparse(sa, s));
     }
     default:
@@ -1208,13 +1280,13 @@ int64_t nm_hybrid_gemm_workspace_size(int64_t t, int64_t k_s, int64_t k_d, int64
                                                     nullptr, o, 0, r));
   }
   if (part > 0) return align256(stage) + part;
-  if (!use_few(t, r) && k_s > 0) {
-    // large-token product: [permuted X][K-blocked positions]
+  if (!use_few(t, r)) {
+    // large-token product: [permuted X][K-blocked positions][partial sums of split tiles]
     const int64_t ldp = gathered ? hybrid_ldp(k_s, k_d) : k_s + k_d;
     const nml::SparseArgs sa = hybrid_sparse_args(nullptr, ldp, gathered ? hybrid_off1(k_s) : k_s, t, k_s, k_d,
                                                   nullptr, nullptr, nullptr, k_d, o, nullptr, o, 0, r);
-    const int64_t mb = meta_block_ws(sa);
-    if (mb > 0) return align256(stage) + mb;
+    const int64_t mb = k_s > 0 ? meta_block_ws(sa) : 0, sp = sparse_splits(sa);
+    if (mb > 0 || sp > 1) return align256(stage) + align256(mb) + (sp > 1 ? sp * t * o * 4 : 0);
   }
   return stage;
 }
@@ -1283,7 +1355,15 @@ nm_status nm_hybrid_gemm(const void* x, int64_t t, int64_t ldx, const int32_t* s
                                                         y, ldy, accumulate, R),
                                         part, avail, s));
   }
-  if ((st = use_meta_block(sa, workspace, workspace_bytes, stage > 0 ? align256(stage) : 0, s))) return st;
+  const int64_t soff = stage > 0 ? align256(stage) : 0;
+  if ((st = use_meta_block(sa, workspace, workspace_bytes, soff, s))) return st;
+  if (const int64_t sp = sparse_splits(sa); sp > 1) {
+    // [permuted X][K-blocked positions][partial sums]
+    const int64_t poff = soff + (sa.w_meta_blk != nullptr ? align256(nml::meta_block_bytes(sa.o, sa.kc)) : 0);
+    int64_t avail = 0;
+    float* part = ws_slice(workspace, workspace_bytes, poff, &avail);
+    return hip_status(nml::launch_gemm_lds_sp_split(sa, sp, part, avail, s));
+  }
   return hip_status(nml::launch_gemm_sparse(sa, s));
 }
 

@@ -396,6 +396,16 @@ hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t s) {
   return launch_cfg<256, 256, 4, 2, PRO_NONE>(a, s, 1, nullptr);
 }
 
+// 256 x 256 tiles with the reduction split in `splits` K ranges, for token counts whose
+// tiles fill under one round of workgroups (PRO_NONE, bf16 or fp8 weights); one range when
+// `part` holds fewer than splits * t * o floats.
+hipError_t launch_gemm_lds_split(const GemmArgs& a, int64_t splits, float* part, int64_t part_bytes, hipStream_t s) {
+  if (a.prologue != PRO_NONE) return hipErrorInvalidValue;
+  if (splits < 1 || part == nullptr || part_bytes < splits * a.t * a.o * 4) splits = 1;
+  if (a.w_fp8) return launch_cfg<256, 256, 4, 2, PRO_NONE, true>(a, s, splits, part);
+  return launch_cfg<256, 256, 4, 2, PRO_NONE>(a, s, splits, part);
+}
+
 // fp8 weights widened once to bf16 (exact), for the kernels that read bf16 weights only
 // (kept as an A/B alternative to the fp8 direct-to-LDS variant).
 __global__ void k_widen_fp8(const uint8_t* __restrict__ w8, int64_t ldw, int64_t O, int64_t K,

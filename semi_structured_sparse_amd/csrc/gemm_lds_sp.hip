@@ -496,6 +496,13 @@ hipError_t launch_gemm_lds_sp(const SparseArgs& a, hipStream_t s) {
   return launch_sp_cfg<256, 256, 2, 4>(a, s, 1, nullptr);
 }
 
+hipError_t launch_gemm_lds_sp_split(const SparseArgs& a, int64_t splits, float* part, int64_t part_bytes,
+                                    hipStream_t s) {
+  if (splits < 1 || part == nullptr || part_bytes < splits * a.t * a.o * 4) splits = 1;
+  if (a.lift_dma && a.loader == XL_LIFT) return launch_sp_lx<256, 256, 2, 4, 2>(a, s, splits, part);
+  return launch_sp_cfg<256, 256, 2, 4>(a, s, splits, part);
+}
+
 int64_t gemm_lds_sp_small_part_bytes(const SparseArgs& a) {
   const int64_t splits = sp_small_splits(a);
   return splits > 1 ? splits * a.t * a.o * 4 : 0;

@@ -96,6 +96,10 @@ hipError_t launch_gemm_dense(const GemmArgs& a, hipStream_t s);
 // direct-to-LDS variant for large PRO_NONE / PRO_MASK problems with K % 64 == 0
 bool gemm_lds_eligible(const GemmArgs& a, bool any_size);
 hipError_t launch_gemm_lds(const GemmArgs& a, hipStream_t s);
+// 256 x 256 tiles with the reduction split in `splits` K ranges (PRO_NONE): with part
+// (scratch of at least splits * t * o floats) the ranges write fp32 partial tiles that a
+// second kernel sums in range order; without it, one range.
+hipError_t launch_gemm_lds_split(const GemmArgs& a, int64_t splits, float* part, int64_t part_bytes, hipStream_t s);
 // fp8 e4m3fn weights [o][ldw] bytes -> bf16 [o][k] (exact), k % 8 == 0
 hipError_t launch_widen_fp8(const uint8_t* w8, int64_t ldw, int64_t o, int64_t k, uint16_t* wb, hipStream_t s);
 // split-K variant with 128-row tiles (PRO_NONE; few tokens, and token counts whose
@@ -174,6 +178,11 @@ hipError_t launch_gather_rows(const uint16_t* w, int64_t ldw, int64_t o, int64_t
 // direct-to-LDS variant for large problems (plain loader, kc % 64 == 0, kd % 64 == 0)
 bool gemm_lds_sp_eligible(const SparseArgs& a, bool any_size);
 hipError_t launch_gemm_lds_sp(const SparseArgs& a, hipStream_t s);
+// its 256 x 256 tiles with the reduction split in `splits` step ranges (gemm_lds_sp_eligible
+// with any_size): with part (scratch of at least splits * t * o floats) the ranges write
+// fp32 partial tiles that a second kernel sums in range order; without it, one range.
+hipError_t launch_gemm_lds_sp_split(const SparseArgs& a, int64_t splits, float* part, int64_t part_bytes,
+                                    hipStream_t s);
 // split variant with 128-row tiles (same eligibility with any_size; few tokens, and
 // token counts whose 256 x 256 tiles would not fill the chip): with part (scratch of at least
 // gemm_lds_sp_small_part_bytes(a) bytes) the splits write fp32 partial tiles that a second

@@ -1088,6 +1088,87 @@ def test_mid_range_split_tile(kind, t):
             check_gemm_vals(yy, ref, a_v, b_v, label=f"mid w8a8 t={t} {lab}")
 
 
+# shapes whose 256 x 256 tiles fill under one round with long reductions: (t, o, k) with
+# ragged T and O; 90 tiles split in two, 72 tiles split in three
+LARGE_SPLIT = {"act": (2500, 2056, 12800), "act_fp8": (2500, 2056, 12800), "act_pts": (2500, 2056, 12800),
+               "w24": (1800, 2056, 6144), "slide": (1800, 2056, 8192), "hybrid": (1800, 2056, 6144),
+               "w8a8": (2500, 2056, 8192)}
+
+
+@pytest.mark.parametrize("kind", list(LARGE_SPLIT))
+def test_large_tile_split(kind):
+    """Above 128 tokens, 256 x 256 tiles that fill under one round of workgroups, with
+    enough K-steps per range, have their reduction split in two to four ranges (partial
+    tiles in the workspace, summed in range order): 8:16 activations on bf16 and fp8
+    weights and with the mitigations' epilogue (D-PTS + VAR), 2:4, lowered 6:8 with the
+    lift in the loads, the hybrid format and fp8 x fp8, the sparse ones on K-blocked
+    positions.  Every output written; the oracle on one row of every 256-row band and the
+    last row."""
+    t, o, k = LARGE_SPLIT[kind]
+    print(f"large tile split kind={kind} t={t} o={o} k={k}", flush=True)
+    rng = np.random.default_rng(t + o + len(kind))
+    rows = np.unique(np.r_[np.minimum(np.arange(0, t, 256) + rng.integers(0, 256, (t + 255) // 256), t - 1), t - 1])
+    x = (pts_rows(rng, t, k) if kind == "act_pts" else synth.student_t_bf16(rng, (t, k), 4.0, 0.5))
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    if kind in ("act", "act_fp8"):
+        sx, keep = O.sparsify(x[rows], 8, 16)
+        if kind == "act":
+            y, _ = run_act(x, w, 8, 16, want_mask=False)
+            ref, wv = O.gemm(sx, w), w
+        else:
+            q, sc = synth.fp8_e4m3_quantize_rows(w)
+            y, _ = run_act(x, None, 8, 16, w8=q, s8=sc, want_mask=False)
+            ref, wv = O.spmm_act_fp8(x[rows], q, sc, 8, 16), O.fp8_e4m3_to_f64(q) * sc[:, None].astype(np.float64)
+        tk = taken()
+        assert np.isfinite(y).all(), kind
+        check_gemm(y[rows], ref, sx, wv, label=f"large split {kind}")
+    elif kind == "act_pts":
+        pts = S.NM_PTS_DYNAMIC | S.NM_PTS_VAR
+        y, mask = run_spmm_pts(x, w, 8, 16, pts)
+        tk = taken()
+        ref, sp_, keep, alpha, beta, v = pts_reference(x[rows], w, O.bf16_to_f64(w), 8, 16, pts, None)
+        assert (mask[rows] == O.pack_mask(keep)).all()
+        assert np.isfinite(y).all(), kind
+        check_pts(y[rows], ref, sp_, O.bf16_to_f64(w), alpha, beta, v, label="large split pts")
+    elif kind == "w24":
+        v, mt = gpu_compress_2of4(w)
+        pr, _ = O.sparsify(w, 2, 4)
+        y = run_w(S.NM_W_COMPRESSED, x, v, mt, o, k)
+        tk = taken()
+        assert np.isfinite(y).all(), kind
+        check_gemm(y[rows], O.gemm(x[rows], pr), x[rows], pr, label="large split 2:4")
+    elif kind == "slide":
+        vp, mp = slide_pack_gpu(w, 4)
+        pr, _ = O.sparsify(w, 6, 8)
+        y = run_w(S.NM_W_SLIDE, x, vp, mp, o, k, ns=4)
+        tk = taken()
+        assert "lift" not in tk, tk
+        assert np.isfinite(y).all(), kind
+        check_gemm(y[rows], O.gemm(x[rows], pr), x[rows], pr, label="large split 6:8")
+    elif kind == "hybrid":
+        kd = 1024
+        sc, dc, wv, wm, wdd = hybrid_pack_gpu(w, kd)
+        sync()
+        sp, de, hv, hi, hwd = O.hybrid_pack(w, kd)
+        wh = w.copy()
+        wh[:, sp] = O.decompress(hv, hi, 2, 4, k - kd)
+        y = run_hybrid(x, sc, k - kd, dc, kd, wv, wm, wdd, o)
+        tk = taken()
+        assert np.isfinite(y).all(), kind
+        check_gemm(y[rows], O.hybrid_gemm(x[rows], sp, de, hv, hi, hwd), x[rows], wh, label="large split hybrid")
+    else:
+        w8, idx, wsc = w8a8_weights(rng, o, k, 4)
+        y = run_w8a8(x, w8, idx, wsc, o, k, 4)
+        tk = taken()
+        assert "quant" in tk, tk
+        assert np.isfinite(y).all(), kind
+        a_v, b_v = w8a8_operands(x[rows], w8, idx, wsc, k, 4)
+        check_gemm_vals(y[rows], O.spmm_w8a8_slide(x[rows], w8, idx, wsc, k, 4), a_v, b_v, label="large split w8a8")
+    assert {"tile_split", "tile_lds", "reduce"} <= tk, (kind, tk)
+    if kind in ("w24", "slide", "hybrid", "w8a8"):
+        assert {"meta_block", "sparse_mma"} <= tk, (kind, tk)
+
+
 @pytest.mark.parametrize("t,o,kc", [(300, 264, 1088), (257, 130, 64), (512, 520, 2112)])
 def test_blocked_positions_match_row_major(t, o, kc):
     """The large-token 2:4 product reads the weight positions from a K-blocked copy in the
