@@ -147,7 +147,7 @@ bool use_few(int64_t t, const nml::Route& r) { return t <= kFewMaxT && !r.has(NM
 // remedies, chosen per call by large_plan:
 //   split: the large-tile kernel with its reduction split in 2-4 K ranges (at most one
 //     round of workgroups), when each range keeps enough K-steps to outweigh writing and
-//     re-reading the partial tiles: 100 steps of 64 for the dense kernel, 24 for the
+//     re-reading the partial tiles: 100 steps of 64 for the dense kernel, 32 for the
 //     sparse kernel (whose steps take about twice as long);
 //   mid: otherwise, under 128 tiles, the split-K 128-row tile kernel of the few-token
 //     products, whose splits fill the chip.
@@ -160,10 +160,11 @@ bool use_few(int64_t t, const nml::Route& r) { return t <= kFewMaxT && !r.has(NM
 //     (split), 2048: 126 -> 114 (split);
 //   2:4 4096 x 14336: 1024 / 1536 / 2048 tokens split 119 / 165 / 187 (mid 133 / 233 / 245).
 // The other choice, where measured, was slower: the dense 4096 x 14336 product at 1024
-// tokens split in four 157 us, 4096 x 4096 at 2048 tokens split in two 100 us against 77.
+// tokens split in four 157 us, 4096 x 4096 at 2048 tokens split in two 100 us against 77,
+// lowered 6:8 4096 x 4096 at 1024 tokens split in four (24 steps each) 83-85 us against 71.
 // The NM_ROUTE_NO_FEW, NM_ROUTE_TILE_REGS and NM_ROUTE_TILE_LDS hints keep the unsplit
 // large-tile kernels.
-constexpr int64_t kMinSplitStepsDense = 100, kMinSplitStepsSparse = 24;
+constexpr int64_t kMinSplitStepsDense = 100, kMinSplitStepsSparse = 32;
 
 // Internal route bit (not in nm.h): no split of the large tiles.  The no-allocation entry
 // point sets it when the split's partial tiles would not fit its buffer.
