@@ -247,9 +247,12 @@ enum {
   NM_ROUTE_TILE_LDS = 1u << 10,     /* tile products: the direct-to-LDS large-tile kernels
                                        at any size                                          */
   NM_ROUTE_TILE_REGS = 1u << 11,    /* tile products: the register-staged kernels           */
-  NM_ROUTE_LIFT_COPY = 1u << 12     /* W_SLIDE tile products: lift X into the workspace
+  NM_ROUTE_LIFT_COPY = 1u << 12,    /* W_SLIDE tile products: lift X into the workspace
                                        first (otherwise the tile loads build the lifted
                                        rows from the raw X)                                 */
+  NM_ROUTE_ACT_SPARSE_X = 1u << 13  /* ACT_DYNAMIC 2:4 above the few-token sizes: compress
+                                       X, then the sparse matrix instruction with X as the
+                                       sparse operand (otherwise S(X) on dense tiles)       */
 };
 
 /*

@@ -945,9 +945,12 @@ nm_status spmm_impl(const nm_spmm_args* a, void* stream, bool noalloc) {
         return run_dense_few(g, part, part_avail, s);
       }
 
-      // ACT_DYNAMIC
-      if (a->n == 2 && a->m == 4 && !fp8 && a->w_scale == nullptr && have_ws) {
-        // 2:4: compress X once, then the sparse matrix instruction with X as sparse operand
+      // ACT_DYNAMIC 2:4 under the NM_ROUTE_ACT_SPARSE_X hint: compress X once, then the
+      // sparse matrix instruction with X as the sparse operand (register-staged tiles,
+      // transposed output).  Measured on gfx950 slower than S(X) on the direct-to-LDS
+      // dense tiles at every size: 4096 x 14336 at 256 / 8192 tokens 392 / 1315 us against
+      // 62 / 805 us, 14336 x 4096 at 1024 tokens 302 against 124 us.
+      if (R.has(NM_ROUTE_ACT_SPARSE_X) && a->n == 2 && a->m == 4 && !fp8 && a->w_scale == nullptr && have_ws) {
         uint16_t* xv = (uint16_t*)a->workspace;
         uint8_t* xm = (uint8_t*)a->workspace + ((T * (K / 2) * 2 + 15) / 16) * 16;
         hipError_t e = nml::launch_select(4, (const uint16_t*)a->x, T, K, a->ldx, 2, nullptr, 0, a->x_mask_out,

@@ -346,7 +346,7 @@ def run_act(x, w, n, m, route=None, w8=None, s8=None, workspace=True, accumulate
 
 
 @pytest.mark.parametrize("n,m", [(8, 16), (16, 32), (4, 8), (2, 4), (1, 4), (6, 8)])
-@pytest.mark.parametrize("route", ["fused", "mask", "sx"])
+@pytest.mark.parametrize("route", ["fused", "mask", "sx", "sparse_x"])
 @pytest.mark.parametrize("t,o,k", [(300, 200, 1024), (17, 520, 1056), (513, 264, 2048)])
 def test_spmm_act_dynamic(n, m, route, t, o, k):
     print(f"spmm act n={n} m={m} route={route} t={t} o={o} k={k}", flush=True)
@@ -404,18 +404,21 @@ def test_spmm_act_masked_kernels(kernel, t, o, k):
 
 def test_spmm_act_2of4_layer():
     """Single 2:4 activation-sparse layer (X 64x512, W 512x512): the weight-streaming
-    few-token kernel, the sparse matrix path (compress + SMFMAC with X as the sparse
-    operand) and the fused dense path."""
+    few-token kernel, and with the no_few hint the S(X) product (workspace), the fused
+    dense path (none) and, under the act_sparse_x hint, the sparse matrix path (compress +
+    SMFMAC with X as the sparse operand)."""
     d = synth.layer_2of4_small()
     x, w = d["x"], d["w"]
     sx, keep = O.sparsify(x, 2, 4)
     ref = O.gemm(sx, w)
-    for few in (True, False):
+    for hints in ((), ("no_few",), ("no_few", "act_sparse_x")):
         for ws in (True, False):
-            with use_route(*(() if few else ("no_few",))):
+            with use_route(*hints):
                 y, mask = run_act(x, w, 2, 4, workspace=ws)
+                if "act_sparse_x" in hints and ws:
+                    assert "sparse_mma" in taken(), taken()
             assert (mask == O.pack_mask(keep)).all()
-            check_gemm(y, ref, sx, w, label=f"2:4 layer ws={ws} few={few}")
+            check_gemm(y, ref, sx, w, label=f"2:4 layer ws={ws} hints={hints}")
 
 
 # route hints of the few-token dispatch: weight-streaming kernel, split-K tile kernel
