@@ -85,6 +85,28 @@ __device__ __forceinline__ u32x4 load_x8(const uint16_t* __restrict__ rp, int k,
   }
 }
 
+// The window pair (k/4, k/4 + 1) of a lifted X row in global memory (k % 8 == 0, both
+// windows inside the row, raw row length kraw >= 64) with one 16-byte load instead of two
+// 8-byte ones.  The first window starts at raw position a (dword aligned; global memory
+// takes dword-aligned multi-dword accesses).  The second starts one dword later when both
+// lie in one group, two dwords later when the first closes its group; in the first case
+// the load starts a dword early where a + 8 would pass the row end, so it never reads
+// outside [a, end of the second window] except inside the row.  Same values as load_x8.
+template <int NS>
+__device__ __forceinline__ u32x4 load_x8_lift_pair(const uint16_t* __restrict__ rp, int k, int kraw) {
+  constexpr uint32_t WPG = NS - 1;   // windows per group (compile-time divisor)
+  const uint32_t win = (uint32_t)k >> 2;
+  const uint32_t g = win / WPG;
+  const uint32_t w = win - g * WPG;
+  const int a = (int)(g * (2 * NS) + 2 * w);
+  const bool same = w + 1 < WPG;
+  const bool back = same && a + 8 > kraw;   // only with both windows in one group
+  u32x4 v;
+  __builtin_memcpy(&v, rp + (back ? a - 2 : a), 16);
+  if (back) return u32x4{v[1], v[2], v[2], v[3]};
+  return same ? u32x4{v[0], v[1], v[1], v[2]} : u32x4{v[0], v[1], v[2], v[3]};
+}
+
 // 2:4 weights on the sparse matrix instruction: bf16 values, or e4m3 codes of them
 constexpr bool sp_kind(int wk) { return wk == WK_SP24 || wk == WK_SP24F8; }
 
@@ -483,14 +505,22 @@ __device__ __forceinline__ void stream_dma(f32x4 (&acc)[RW][TB], const FewSeg& s
     u32x4 xl[U][TB];
     u32x4 xh[U][TB];
   };
+  // lifted rows in global memory: a window pair per 16-byte load (raw row length kraw)
+  constexpr bool PAIR = XL == XL_LIFT && !XS;
+  const int kraw = PAIR ? (int)(sg.k / (4 * (NS - 1)) * (2 * NS)) : 0;
   auto load_x = [&](XB& xb, int st) {
     const int kpos = k0 + st * SK;
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int j = 0; j < TB; ++j) {
-        xb.xl[u][j] = load_x8<XL, NS, false>(xrow[j], kpos + u * CK + 8 * fq, 0);
-        if constexpr (sp_kind(WK)) xb.xh[u][j] = load_x8<XL, NS, false>(xrow[j], kpos + u * CK + 32 + 8 * fq, 0);
+        if constexpr (PAIR) {
+          xb.xl[u][j] = load_x8_lift_pair<NS>(xrow[j], kpos + u * CK + 8 * fq, kraw);
+          if constexpr (sp_kind(WK)) xb.xh[u][j] = load_x8_lift_pair<NS>(xrow[j], kpos + u * CK + 32 + 8 * fq, kraw);
+        } else {
+          xb.xl[u][j] = load_x8<XL, NS, false>(xrow[j], kpos + u * CK + 8 * fq, 0);
+          if constexpr (sp_kind(WK)) xb.xh[u][j] = load_x8<XL, NS, false>(xrow[j], kpos + u * CK + 32 + 8 * fq, 0);
+        }
       }
   };
   // XS: the stage about to be read has landed once at most `later` stages' requests

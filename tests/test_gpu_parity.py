@@ -880,6 +880,32 @@ def test_slide_lift_in_loads_bitexact(ns, t, o, hint):
     check_gemm(y, O.gemm(x, pruned), x, pruned, label=f"slide ns={ns} t={t} lift in loads")
 
 
+@pytest.mark.parametrize("ns", [2, 3, 4, 5, 8])
+@pytest.mark.parametrize("t,o,groups", [(2, 264, 48), (7, 520, 200), (16, 4096, 512), (29, 264, 72)])
+def test_stream_lift_pairs_bitexact(ns, t, o, groups):
+    """Lowered (2N-2):2N weights on the few-token weight-streaming kernel with X in global
+    memory: its whole-stage loads take each pair of lifted windows with one 16-byte load
+    of the raw row (starting a dword early where the load would pass the row end), the
+    ragged end window by window.  The same bits as the same kernel on X lifted beforehand
+    (plain loads of the lifted row, W_COMPRESSED over K'), and the dense product on the
+    pruned W within tolerance.  Row lengths with whole stages only and with ragged ends."""
+    print(f"stream lift pairs ns={ns} t={t} o={o} groups={groups}", flush=True)
+    rng = np.random.default_rng(ns * 31 + t)
+    k = 2 * ns * groups
+    x = synth.normal_bf16(rng, (t, k))
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    vp, mp = slide_pack_gpu(w, ns)
+    kp = O.lowered_k(k, ns)
+    with use_route("few_stream"):
+        y = run_w(S.NM_W_SLIDE, x, vp, mp, o, k, ns=ns)
+        assert "few_stream" in taken() and "tile_lds" not in taken(), taken()
+        y_pre = run_w(S.NM_W_COMPRESSED, O.lift(x, ns), vp, mp, o, kp)
+        assert "few_stream" in taken(), taken()
+    assert np.array_equal(y.view(np.uint32), y_pre.view(np.uint32)), "lifted loads vs pre-lifted X"
+    pruned, _ = O.sparsify(w, 2 * ns - 2, 2 * ns)
+    check_gemm(y, O.gemm(x, pruned), x, pruned, label=f"stream lift pairs ns={ns} t={t}")
+
+
 @pytest.mark.parametrize("ns", [3, 5, 6, 7])
 def test_spmm_w_slide_odd_family(ns):
     """4:6, 8:10, 10:12 and 12:14 weights end to end on the GPU: compressed by the
