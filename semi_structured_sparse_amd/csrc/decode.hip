@@ -1144,9 +1144,12 @@ __global__ void k_permute_cols(const uint16_t* __restrict__ x, int64_t T, int64_
 
 // The same gather a token row per workgroup: the row is read into LDS with 16-byte loads,
 // then each thread gathers 8 consecutive outputs from LDS (column indices read as two
-// 16-byte pieces) and writes them as one 16-byte piece.  Needs kx, ldx, k0, k1, off1 and
-// ldo multiples of 8 and 16-byte aligned x and xo; the row takes kx * 2 bytes of LDS.
+// 16-byte pieces) and writes them as one 16-byte piece.  The first pieces' indices are
+// requested before the row, so the two reads overlap instead of following each other.
+// Needs kx, ldx, k0, k1, off1 and ldo multiples of 8 and 16-byte aligned x and xo; the row
+// takes kx * 2 bytes of LDS.
 constexpr int PERM_THREADS = 256;
+constexpr int PERM_BATCH = 4;   // 8-output pieces per thread whose indices are in flight together
 __global__ __launch_bounds__(PERM_THREADS) void k_permute_rows(const uint16_t* __restrict__ x, int64_t ldx, int kx,
                                                                const int32_t* __restrict__ c0, int k0,
                                                                const int32_t* __restrict__ c1, int k1, int64_t off1,
@@ -1155,26 +1158,43 @@ __global__ __launch_bounds__(PERM_THREADS) void k_permute_rows(const uint16_t* _
   const int tid = threadIdx.x;
   const int64_t t = blockIdx.x;
   const uint16_t* src = x + t * ldx;
+  uint16_t* dst = xo + t * ldo;
+  const int n8 = (k0 + k1) / 8;
+  int4 ia[PERM_BATCH], ib[PERM_BATCH];
+  auto load_idx = [&](int p0) {
+#pragma unroll
+    for (int q = 0; q < PERM_BATCH; ++q) {
+      const int p = p0 + q * PERM_THREADS + tid;
+      if (p < n8) {
+        const int j = 8 * p;
+        const int32_t* cl = j < k0 ? c0 + j : c1 + (j - k0);
+        ia[q] = *reinterpret_cast<const int4*>(cl);
+        ib[q] = *reinterpret_cast<const int4*>(cl + 4);
+      }
+    }
+  };
+  load_idx(0);
   for (int c = tid; c < kx / 8; c += PERM_THREADS)
     *reinterpret_cast<uint4*>(xrow + 8 * c) = *reinterpret_cast<const uint4*>(src + 8 * c);
   __syncthreads();
-  uint16_t* dst = xo + t * ldo;
-  const int n8 = (k0 + k1) / 8;
-  for (int p = tid; p < n8; p += PERM_THREADS) {
-    const int j = 8 * p;
-    const bool first = j < k0;
-    const int32_t* cl = first ? c0 + j : c1 + (j - k0);
-    const int4 ia = *reinterpret_cast<const int4*>(cl), ib = *reinterpret_cast<const int4*>(cl + 4);
-    const int idx[8] = {ia.x, ia.y, ia.z, ia.w, ib.x, ib.y, ib.z, ib.w};
-    uint32_t w[4];
+  for (int p0 = 0; p0 < n8; p0 += PERM_BATCH * PERM_THREADS) {
+    if (p0 > 0) load_idx(p0);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      int a = idx[2 * q], b = idx[2 * q + 1];
-      a = a < 0 ? 0 : (a >= kx ? kx - 1 : a);
-      b = b < 0 ? 0 : (b >= kx ? kx - 1 : b);
-      w[q] = (uint32_t)xrow[a] | ((uint32_t)xrow[b] << 16);
+    for (int q = 0; q < PERM_BATCH; ++q) {
+      const int p = p0 + q * PERM_THREADS + tid;
+      if (p >= n8) continue;
+      const int j = 8 * p;
+      const int idx[8] = {ia[q].x, ia[q].y, ia[q].z, ia[q].w, ib[q].x, ib[q].y, ib[q].z, ib[q].w};
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        int a = idx[2 * e], b = idx[2 * e + 1];
+        a = a < 0 ? 0 : (a >= kx ? kx - 1 : a);
+        b = b < 0 ? 0 : (b >= kx ? kx - 1 : b);
+        w[e] = (uint32_t)xrow[a] | ((uint32_t)xrow[b] << 16);
+      }
+      *reinterpret_cast<uint4*>(dst + (j < k0 ? j : off1 + (j - k0))) = make_uint4(w[0], w[1], w[2], w[3]);
     }
-    *reinterpret_cast<uint4*>(dst + (first ? j : off1 + (j - k0))) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
