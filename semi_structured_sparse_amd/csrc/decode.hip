@@ -1060,8 +1060,11 @@ __global__ __launch_bounds__(RP_OUT * RP_LANES) void k_reduce_parts(const float*
 }
 
 // Few splits over many outputs (the split-K tile kernels): each thread owns 4 consecutive
-// outputs and adds the splits' float4 partials in split order, four loads in flight.
+// outputs and adds the splits' float4 partials in split order.  The partials of up to
+// RP4_BATCH splits are requested together before the first add (one memory round trip
+// per batch, not one per split past the first four).
 constexpr int RP4_THREADS = 256;
+constexpr int RP4_BATCH = 16;
 
 __global__ __launch_bounds__(RP4_THREADS) void k_reduce_parts4(const float* __restrict__ part, int64_t splits,
                                                                Epi epi, int64_t T,
@@ -1071,26 +1074,21 @@ __global__ __launch_bounds__(RP4_THREADS) void k_reduce_parts4(const float* __re
   const int64_t i = ((int64_t)blockIdx.x * RP4_THREADS + threadIdx.x) * 4;
   if (i >= n) return;
   const float* p = part + i;
-  float4 acc = *reinterpret_cast<const float4*>(p);
-  int64_t sp = 1;
-  for (; sp + 3 < splits; sp += 4) {
-    float4 v[4];
+  float4 acc = *reinterpret_cast<const float4*>(p);   // split 0 (its bits kept, -0 included)
+  for (int64_t s0 = 1; s0 < splits; s0 += RP4_BATCH) {
+    float4 v[RP4_BATCH];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const float4*>(p + (sp + q) * n);
+    for (int q = 0; q < RP4_BATCH; ++q)
+      if (s0 + q < splits) v[q] = *reinterpret_cast<const float4*>(p + (s0 + q) * n);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      acc.x += v[q].x;
-      acc.y += v[q].y;
-      acc.z += v[q].z;
-      acc.w += v[q].w;
+    for (int q = 0; q < RP4_BATCH; ++q) {
+      if (s0 + q < splits) {
+        acc.x += v[q].x;
+        acc.y += v[q].y;
+        acc.z += v[q].z;
+        acc.w += v[q].w;
+      }
     }
-  }
-  for (; sp < splits; ++sp) {
-    const float4 v = *reinterpret_cast<const float4*>(p + sp * n);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
   }
   const int64_t t = i / O, o = i - t * O;   // O % 4 == 0: the 4 outputs share a row
   if (epi.w_scale != nullptr) {
