@@ -1317,7 +1317,8 @@ def test_hybrid_full_size_sampled():
 
 # --------------------------------------------------------- fp8 x fp8 (W8A8) ---
 
-@pytest.mark.parametrize("ns,t,k,pad", [(4, 37, 1024, 0), (2, 5, 256, 16), (3, 64, 96, 32), (4, 1, 64, 48)])
+@pytest.mark.parametrize("ns,t,k,pad", [(4, 37, 1024, 0), (2, 5, 256, 16), (3, 64, 96, 32), (4, 1, 64, 48),
+                                      (4, 3, 2056, 0), (4, 2, 8192, 16), (4, 2, 8200, 0)])
 def test_quant_lift_bitexact(ns, t, k, pad):
     """Per-token e4m3 codes (lifted) and scales bit for bit against the oracle: Student-t
     rows, an all-zero row, tiny values (subnormal codes), ties of the largest magnitude."""
