@@ -53,6 +53,18 @@ Readings where the pages are silent (each is listed in the design notes):
   region is pruned 2:4 by magnitude over consecutive permuted columns.
 * fp8 weights: OCP E4M3FN codes with one fp32 scale per output row, applied after the
   K reduction.
+* Per-token fp8 activations (quantize_tokens): symmetric absmax scaling, codes of
+  x * fp32(448 / amax).  PARITY UNPINNED in that one choice: dividing by
+  fp32(amax / 448) is an equally plain reading that differs by one code at rounding
+  boundaries, and the pages give no scheme.  Its properties (every code within half an
+  e4m3 step of x/s, the row maximum at +-448, zero rows, the encoder against an
+  independent library) are pinned.
+* Activation mitigations ([FLEX] 2.B): D-PTS shifts each token row by its mean before
+  the selection, S-PTS by a given per-channel vector, and the shift is undone by the
+  rank-one term mu_t * (W . 1)_o (or (W . c)_o); VAR scales each pruned row to its
+  unpruned variance.  The page names these steps without formulas: these are the
+  plainest readings, pinned by their reductions and identities (zero shift = ACT, the
+  rank-one identity, the restored variance), not by printed values.
 """
 from __future__ import annotations
 
@@ -572,6 +584,7 @@ def quantize_tokens(x_bits: np.ndarray):
         amax_t = max_k |x_tk|;  r_t = fp32(448 / amax_t);  s_t = fp32(amax_t / 448)
         q_tk  = e4m3_encode(clamp(fp32(x_tk * r_t), -448, 448))
     with r_t = s_t = 1 for an all-zero row; every fp32 operation rounds to nearest even.
+    Parity unpinned in the multiply-by-r reading (x / s is as plain; see the header).
     Returns (codes uint8 [T][K], scales fp32 [T]); x ~= dec(q) * s."""
     x = f32_from_bf16(x_bits)
     amax = np.abs(x).max(axis=1) if x.shape[1] else np.zeros(x.shape[0], np.float32)
