@@ -1198,6 +1198,33 @@ def test_large_tile_split(kind):
         assert {"meta_block", "sparse_mma"} <= tk, (kind, tk)
 
 
+@pytest.mark.parametrize("kind", ["act", "act_fp8"])
+def test_large_half_tiles(kind):
+    """Dense-weight products whose 256 x 256 tiles would have their reduction split (99
+    tiles, 200 K-steps) while 256 x 128 tiles fill three quarters to one round (198) take
+    the unsplit half tiles: no partial tiles, no second pass.  8:16 activations on bf16
+    and fp8 weights; every output written, the oracle on one row of every 256-row band and
+    the last row."""
+    t, o, k = 2800, 2056, 12800
+    print(f"large half tiles kind={kind} t={t} o={o} k={k}", flush=True)
+    rng = np.random.default_rng(t + o + len(kind))
+    rows = np.unique(np.r_[np.minimum(np.arange(0, t, 256) + rng.integers(0, 256, (t + 255) // 256), t - 1), t - 1])
+    x = synth.student_t_bf16(rng, (t, k), 4.0, 0.5)
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    sx, keep = O.sparsify(x[rows], 8, 16)
+    if kind == "act":
+        y, _ = run_act(x, w, 8, 16, want_mask=False)
+        ref, wv = O.gemm(sx, w), w
+    else:
+        q, sc = synth.fp8_e4m3_quantize_rows(w)
+        y, _ = run_act(x, None, 8, 16, w8=q, s8=sc, want_mask=False)
+        ref, wv = O.spmm_act_fp8(x[rows], q, sc, 8, 16), O.fp8_e4m3_to_f64(q) * sc[:, None].astype(np.float64)
+    tk = taken()
+    assert "tile_lds" in tk and "tile_split" not in tk and "reduce" not in tk, (kind, tk)
+    assert np.isfinite(y).all(), kind
+    check_gemm(y[rows], ref, sx, wv, label=f"large half tiles {kind}")
+
+
 @pytest.mark.parametrize("t,o,kc", [(300, 264, 1088), (257, 130, 64), (512, 520, 2112)])
 def test_blocked_positions_match_row_major(t, o, kc):
     """The large-token 2:4 product reads the weight positions from a K-blocked copy in the
