@@ -107,28 +107,33 @@ def test_noalloc_mitigated_selection():
 
 def test_noalloc_without_the_large_split():
     """A call whose preferred route splits the reduction of its 256 x 256 tiles with more
-    scratch than the buffer holds (8:16 S(X) staged, then partial tiles: 2048 tokens of the
-    14336 -> 4096 down projection) runs those tiles unsplit: every output written, one row
+    scratch than the buffer holds (2:4 weights, 4096 x 14336, 2048 tokens: K-blocked
+    positions, then partial tiles) runs those tiles unsplit: every output written, one row
     of every 256-row band and the last within tolerance of the oracle, as nm_spmm's split
     route is."""
     t, o, k = 2048, 4096, 14336
-    d = synth.mlp_down_8of16(t_max=t)
-    x, w = d["x"], d["w"]
+    rng = np.random.default_rng(93)
+    x = synth.normal_bf16(rng, (t, k))
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    v = torch.empty((o, k // 2), dtype=torch.int16, device="cuda")
+    mt = torch.empty((o, k // 8), dtype=torch.uint8, device="cuda")
+    S.nm_compress(dev(w), 2, 4, v, mt, S.NM_META_2BIT)
+    sync()
+    xd = dev(x)
 
     def make(_):
         y = empty((t, o), np.float32, fill=float("nan"))
-        return y, S.make_spmm_args(S.NM_ACT_DYNAMIC, t, o, k, dev(x), dev(w), y, n=8, m=16)
+        return y, S.make_spmm_args(S.NM_W_COMPRESSED, t, o, k, xd, v, y, w_meta=mt, w_meta_fmt=S.NM_META_2BIT)
 
     assert S.nm_spmm_workspace_size(make(None)[1]) > S.NM_NOALLOC_SCRATCH_BYTES
     y1, y2, tk1, tk2 = both(make)
     assert "tile_split" in tk2 and "tile_split" not in tk1, (tk1, tk2)
-    rng = np.random.default_rng(5)
     rows = np.unique(np.r_[np.arange(0, t, 256) + rng.integers(0, 256, t // 256), t - 1])
-    sx, _ = O.sparsify(x[rows], 8, 16)
-    ref = O.gemm(sx, w)
+    pr, _ = O.sparsify(w, 2, 4)
+    ref = O.gemm(x[rows], pr)
     for yy, lab in ((y1, "noalloc unsplit"), (y2, "workspace split")):
         assert np.isfinite(yy).all(), lab
-        check_gemm(yy[rows], ref, sx, w, label=lab)
+        check_gemm(yy[rows], ref, x[rows], pr, label=lab)
 
 
 def test_noalloc_refuses_oversized_calls():
