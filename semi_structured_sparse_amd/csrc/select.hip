@@ -56,9 +56,13 @@ __device__ __forceinline__ void store_group(uint16_t* p, const uint32_t (&d)[M /
   }
 }
 
-// Copy `count` u16 from an LDS strip to global memory, lanes striding by 64.
+// Copy `count` u16 from an LDS strip (16-byte aligned) to global memory, lanes striding by
+// 64: 16-byte pieces where the destination and count allow, else dwords or single values.
 __device__ __forceinline__ void copy_u16(uint16_t* dst, const uint16_t* lds, int count, int lane) {
-  if ((reinterpret_cast<uintptr_t>(dst) & 3) == 0) {
+  if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0 && (count & 7) == 0) {
+    for (int e = lane; e < count / 8; e += 64)
+      reinterpret_cast<uint4*>(dst)[e] = reinterpret_cast<const uint4*>(lds)[e];
+  } else if ((reinterpret_cast<uintptr_t>(dst) & 3) == 0) {
     const int pairs = count >> 1;
     for (int e = lane; e < pairs; e += 64)
       reinterpret_cast<uint32_t*>(dst)[e] = reinterpret_cast<const uint32_t*>(lds)[e];
@@ -69,7 +73,10 @@ __device__ __forceinline__ void copy_u16(uint16_t* dst, const uint16_t* lds, int
 }
 
 __device__ __forceinline__ void copy_u8(uint8_t* dst, const uint8_t* lds, int count, int lane) {
-  if ((reinterpret_cast<uintptr_t>(dst) & 3) == 0) {
+  if ((reinterpret_cast<uintptr_t>(dst) & 15) == 0 && (count & 15) == 0) {
+    for (int e = lane; e < count / 16; e += 64)
+      reinterpret_cast<uint4*>(dst)[e] = reinterpret_cast<const uint4*>(lds)[e];
+  } else if ((reinterpret_cast<uintptr_t>(dst) & 3) == 0) {
     const int quads = count >> 2;
     for (int e = lane; e < quads; e += 64)
       reinterpret_cast<uint32_t*>(dst)[e] = reinterpret_cast<const uint32_t*>(lds)[e];
