@@ -96,16 +96,18 @@ def test_mid_range_workspace_holds_the_split_partials():
 def test_large_tile_split_workspace():
     """256 x 256 tiles that fill under one round, with at least 100 K-steps of 64 per range
     (dense): the reduction splits in 256 // tiles ranges, whose partial tiles the workspace
-    query adds; fewer steps per range take the 128-row split kernel instead."""
-    o, k = 4096, 14336
-    def size(t, **kw):
+    query adds, unless 256 x 128 tiles fill three quarters to one round (then those,
+    unsplit); fewer steps per range take the 128-row split kernel instead."""
+    k = 14336
+    def size(t, o=4096, **kw):
         return S.nm_spmm_workspace_size(spmm_args(mode=S.NM_ACT_MASKED, t=t, o=o, k=k, ldx=k, ldw=k, ldy=o, **kw))
-    assert size(2048) == 2 * 2048 * o * 4          # 128 tiles, two ranges of 112 steps
-    assert size(1536) == 2 * 1536 * o * 4          # 96 tiles
+    assert size(2500, o=2056) == 2 * 2500 * 2056 * 4   # 90 tiles, two ranges of 112 steps (180 half tiles)
+    assert size(2048) == 0                         # 128 tiles, but 256 half tiles fill one round
+    assert size(1536) == 0                         # 96 tiles, 192 half tiles
     assert size(1024) == 0                         # 64 tiles: four ranges of 56 steps are too short;
                                                    # 256 tiles of 128 rows, unsplit
     assert size(3072) == 0                         # 192 tiles: one round already
-    assert size(2048, route=S.route_bits("tile_lds")) == 0
+    assert size(2500, o=2056, route=S.route_bits("tile_lds")) == 0
 
 
 def test_status_strings_and_version():
