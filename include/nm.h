@@ -250,9 +250,12 @@ enum {
   NM_ROUTE_LIFT_COPY = 1u << 12,    /* W_SLIDE tile products: lift X into the workspace
                                        first (otherwise the tile loads build the lifted
                                        rows from the raw X)                                 */
-  NM_ROUTE_ACT_SPARSE_X = 1u << 13  /* ACT_DYNAMIC 2:4 above the few-token sizes: compress
+  NM_ROUTE_ACT_SPARSE_X = 1u << 13, /* ACT_DYNAMIC 2:4 above the few-token sizes: compress
                                        X, then the sparse matrix instruction with X as the
                                        sparse operand (otherwise S(X) on dense tiles)       */
+  NM_ROUTE_ROW_SX = 1u << 14        /* ACT_DYNAMIC, 2-32 tokens on the streaming kernel:
+                                       S(X) staged row-major (otherwise in blocks of 16
+                                       token rows, each 32-position piece contiguous)       */
 };
 
 /*

@@ -42,7 +42,7 @@ NM_PTS_DYNAMIC, NM_PTS_STATIC, NM_PTS_VAR = 1, 2, 4
 # route hints (NM_ROUTE_*) and the report of what ran (NM_TAKEN_*), by lower-case name
 ROUTE = {name: 1 << i for i, name in enumerate(
     ["act_fused", "act_mask", "act_sx", "no_few", "few_stream", "few_tile", "no_meta_block", "fp8_widen",
-     "no_xlds", "no_few_select", "tile_lds", "tile_regs", "lift_copy", "act_sparse_x"])}
+     "no_xlds", "no_few_select", "tile_lds", "tile_regs", "lift_copy", "act_sparse_x", "row_sx"])}
 TAKEN = {name: 1 << i for i, name in enumerate(
     ["select", "few_stream", "few_xlds", "few_select", "tile_split", "reduce", "tile_lds", "tile_regs",
      "fused_select", "mask", "gather1", "lift", "meta_block", "permute", "quant", "widen", "decompress",

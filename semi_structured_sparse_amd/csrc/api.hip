@@ -492,7 +492,8 @@ int64_t fp8_widen_bytes(const nm_spmm_args* a) {
 // activation mitigations: [S(x~)][mu [t]][alpha [t]].
 int64_t spmm_stage_bytes(const nm_spmm_args* a) {
   if (a->mode == NM_ACT_DYNAMIC && a->pts != 0) return align256(a->t * a->k * 2) + 2 * align256(a->t * 4);
-  if (a->mode == NM_ACT_DYNAMIC) return a->t * a->k * 2 + 64;   // also holds the 2:4 compressed X
+  // also holds the 2:4 compressed X; 2-32 tokens may stage S(X) in whole 16-token blocks
+  if (a->mode == NM_ACT_DYNAMIC) return (a->t >= 2 && a->t <= 32 ? (a->t + 15) / 16 * 16 : a->t) * a->k * 2 + 64;
   if (a->mode == NM_ACT_COMPRESSED) return a->t * a->k * 2;
   return 0;
 }
@@ -948,14 +949,24 @@ nm_status spmm_impl(const nm_spmm_args* a, void* stream, bool noalloc) {
           if (nml::few_select_in_kernel(f)) return hip_status(nml::launch_few(f, part, part_avail, s));
         }
       }
-      // ACT_DYNAMIC, few tokens: select into S(X), then stream the weights
+      // ACT_DYNAMIC, few tokens: select into S(X), then stream the weights.  For 2-32
+      // tokens on the streaming kernel S(X) is staged in 16-token blocks, so that each X
+      // fragment load of the kernel reads 8 whole cache lines instead of 16 half lines.
       if (use_few(T, R) && have_ws) {
         uint16_t* sx = (uint16_t*)a->workspace;
+        g.x = sx; g.ldx = K; g.prologue = nml::PRO_NONE;
+        const bool blk = T >= 2 && T <= 32 && K % 32 == 0 && (a->m == 4 || a->m == 8 || a->m == 16 || a->m == 32) &&
+                         !R.has(NM_ROUTE_ROW_SX) && !few_use_tile(g);
         hipError_t e = nml::launch_select(a->m, (const uint16_t*)a->x, T, K, a->ldx, a->n, sx, K, a->x_mask_out,
-                                          nullptr, nullptr, 0, s);
+                                          nullptr, nullptr, 0, s, blk ? 1 : 0);
         if (e != hipSuccess) return NM_EHIP;
         R.note(NM_TAKEN_SELECT);
-        g.x = sx; g.ldx = K; g.prologue = nml::PRO_NONE;
+        if (blk) {
+          nml::FewArgs f = few_dense_args(g);
+          f.seg[0].loader = nml::XL_BLK;
+          f.seg[0].ldx = K * 16;
+          return hip_status(nml::launch_few(f, part, part_avail, s));
+        }
         return run_dense_few(g, part, part_avail, s);
       }
 

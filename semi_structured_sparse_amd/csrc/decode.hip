@@ -60,6 +60,15 @@ __device__ __forceinline__ u32x4 load_x8(const uint16_t* __restrict__ rp, int k,
     fp8x4_to_bf16x4(q[0], c0, c1);
     fp8x4_to_bf16x4(q[1], c2, c3);
     return u32x4{c0, c1, c2, c3};
+  } else if constexpr (XL == XL_BLK) {
+    // rp: the token's row inside its 16-token block; positions [k, k + 8) lie in one
+    // 32-position piece (k % 8 == 0)
+    const uint16_t* pp = rp + ((k >> 5) << 9) + (k & 31);
+    if (!CHECKED || k + 8 <= kend) return *reinterpret_cast<const u32x4*>(pp);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (k + e < kend) r[e >> 1] |= (uint32_t)pp[e] << (16 * (e & 1));
+    return r;
   } else if constexpr (XL == XL_PLAIN) {
     if (!CHECKED || k + 8 <= kend) return *reinterpret_cast<const u32x4*>(rp + k);
 #pragma unroll
@@ -114,6 +123,7 @@ constexpr bool sp_kind(int wk) { return wk == WK_SP24 || wk == WK_SP24F8; }
 template <int XL>
 __device__ __forceinline__ const uint16_t* x_row(const FewSeg& sg, int64_t t) {
   if constexpr (XL == XL_F8) return reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(sg.x) + t * sg.ldx);
+  else if constexpr (XL == XL_BLK) return sg.x + (t >> 4) * sg.ldx + (t & 15) * 32;   // ldx: block stride
   else return sg.x + t * sg.ldx;
 }
 
@@ -1257,7 +1267,7 @@ hipError_t launch_k(const FewArgs& a, const Plan& p, float* part, hipStream_t s)
     // whole rings)
     constexpr int HALFW = Dma<TB, WK0>::WPB / 2;
     const bool half = p.wpb <= HALFW && a.sel_m == 0 && a.q_ns == 0;
-    if constexpr (TB == 1) {
+    if constexpr (TB == 1 && XL0 != XL_BLK) {
       // one token: stage the X rows in LDS next to the weight rings when they fit
       // (the NM_ROUTE_NO_XLDS hint keeps the register loads)
       // rows of whole 16-byte pieces from 16-byte aligned starts, staged in whole KiB
@@ -1437,6 +1447,14 @@ hipError_t launch_few(const FewArgs& a, float* part, int64_t part_bytes, hipStre
     e = launch_lift(a, p, part, s);
   } else if (s0.w_kind == WK_SP24F8 && s0.loader == XL_F8 && p.tb == 1) {
     e = launch_k<1, WK_SP24F8, XL_F8, 0, WK_NONE>(a, p, part, s);
+  } else if (s0.loader == XL_BLK && a.t >= 2 && (s0.w_kind == WK_BF16 || s0.w_kind == WK_FP8) && p.tb <= 2) {
+    // token-blocked S(X) (2-32 tokens, weight-streaming kernel only)
+    if (s0.w_kind == WK_BF16)
+      e = p.tb == 1 ? launch_k<1, WK_BF16, XL_BLK, 0, WK_NONE>(a, p, part, s)
+                    : launch_k<2, WK_BF16, XL_BLK, 0, WK_NONE>(a, p, part, s);
+    else
+      e = p.tb == 1 ? launch_k<1, WK_FP8, XL_BLK, 0, WK_NONE>(a, p, part, s)
+                    : launch_k<2, WK_FP8, XL_BLK, 0, WK_NONE>(a, p, part, s);
   }
   if (e != hipSuccess || p.splits == 1) return e;
   return launch_reduce_parts(part, p.splits, a.epi(), a.t, a.o, a.y, a.ldy, a.accumulate, a.route, s);

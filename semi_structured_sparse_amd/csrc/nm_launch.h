@@ -46,9 +46,11 @@ __host__ __device__ inline float epi_apply(const Epi& e, float acc, int64_t t, i
 hipError_t launch_select_scored(int m, const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, int n,
                                 const float* col_score, int use_x, uint16_t* y, int64_t ldy, uint32_t* mask,
                                 hipStream_t s);
+// yblk: S(X) written in blocks of 16 token rows, [rows / 16][k / 32][16][32] (ldy unused;
+// m in {4, 8, 16, 32}, k % 32 == 0) for the few-token streaming kernel's XL_BLK loader
 hipError_t launch_select(int m, const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, int n,
                          uint16_t* y, int64_t ldy, uint32_t* mask, uint16_t* values,
-                         uint8_t* meta, int meta_2bit, hipStream_t s);
+                         uint8_t* meta, int meta_2bit, hipStream_t s, int yblk = 0);
 hipError_t launch_decompress(int m, const uint16_t* values, const uint8_t* meta, int meta_2bit,
                              int64_t rows, int64_t k, int n, uint16_t* y, int64_t ldy, hipStream_t s);
 hipError_t launch_lower_slide(int ns, const uint16_t* values, const uint8_t* idx, int64_t rows,
@@ -115,7 +117,9 @@ hipError_t launch_gemm_lds_small(const GemmArgs& a, float* part, int64_t part_by
 // reduction length kc; the dense operand is X, read plainly or lifted.
 // XL_F8: the X rows are e4m3 codes, one byte per position (x as bytes, ldx in bytes),
 // widened to bf16 (exactly) as they are loaded.
-enum XLoader { XL_PLAIN = 0, XL_LIFT = 1, XL_F8 = 2 };
+// XL_BLK (few-token streaming kernel only): X rows in blocks of 16 tokens,
+// [t / 16][k / 32][t % 16][32], block stride ldx elements (16 k).
+enum XLoader { XL_PLAIN = 0, XL_LIFT = 1, XL_F8 = 2, XL_BLK = 3 };
 struct SparseArgs {
   const uint16_t* w_vals;
   const uint8_t* w_meta;  // 2-bit

@@ -92,7 +92,7 @@ template <int M, int NT>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void k_select(
     const uint16_t* __restrict__ x, int64_t rows, int64_t k, int64_t ldx, int n,
     uint16_t* __restrict__ y, int64_t ldy, uint32_t* __restrict__ mask,
-    uint16_t* __restrict__ values, uint8_t* __restrict__ meta, int meta_2bit) {
+    uint16_t* __restrict__ values, uint8_t* __restrict__ meta, int meta_2bit, int yblk) {
   // per-wave compaction strips (+64 dump slots for pruned elements)
   __shared__ __align__(16) uint16_t s_val[kWavesPerBlock][64 * (kMaxN + 1)];
   __shared__ __align__(16) uint8_t s_idx[kWavesPerBlock][64 * (kMaxN + 1)];
@@ -127,7 +127,12 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void k_select(
     uint32_t o[M / 2];
 #pragma unroll
     for (int q = 0; q < M / 2; ++q) o[q] = mask_pair(d[q], keep >> (2 * q));
-    store_group<M>(y + row * ldy + g * M, o);
+    // yblk (M divides 32, k % 32 == 0): S(X) in blocks of 16 token rows, each 32-position
+    // piece of the block's rows contiguous: [row / 16][k / 32][row % 16][32]
+    uint16_t* yp = y + row * ldy + g * M;
+    if constexpr (32 % M == 0)
+      if (yblk) yp = y + (row >> 4) * (k * 16) + (((g * M) >> 5) << 9) + (row & 15) * 32 + ((g * M) & 31);
+    store_group<M>(yp, o);
   }
 
   if constexpr (32 % M == 0) if (mask != nullptr) {
@@ -291,7 +296,8 @@ hipError_t launch_select_scored(int m, const uint16_t* x, int64_t rows, int64_t 
 
 hipError_t launch_select(int m, const uint16_t* x, int64_t rows, int64_t k, int64_t ldx, int n,
                          uint16_t* y, int64_t ldy, uint32_t* mask, uint16_t* values,
-                         uint8_t* meta, int meta_2bit, hipStream_t s) {
+                         uint8_t* meta, int meta_2bit, hipStream_t s, int yblk) {
+  if (yblk && (32 % m != 0 || k % 32 != 0)) return hipErrorInvalidValue;
   const int64_t G = k / m;
   const int64_t strips = rows * ((G + 63) / 64);
   const int64_t blocks = (strips + kWavesPerBlock - 1) / kWavesPerBlock;
@@ -300,18 +306,18 @@ hipError_t launch_select(int m, const uint16_t* x, int64_t rows, int64_t k, int6
   dim3 grid((unsigned)blocks), block(64 * kWavesPerBlock);
 #define NM_SELECT(MM)                                                                              \
   if (n == (MM) / 2)                                                                               \
-    k_select<MM, (MM) / 2><<<grid, block, 0, s>>>(x, rows, k, ldx, n, y, ldy, mask, values, meta, meta_2bit); \
+    k_select<MM, (MM) / 2><<<grid, block, 0, s>>>(x, rows, k, ldx, n, y, ldy, mask, values, meta, meta_2bit, yblk); \
   else                                                                                             \
-    k_select<MM, 0><<<grid, block, 0, s>>>(x, rows, k, ldx, n, y, ldy, mask, values, meta, meta_2bit);
+    k_select<MM, 0><<<grid, block, 0, s>>>(x, rows, k, ldx, n, y, ldy, mask, values, meta, meta_2bit, yblk);
   switch (m) {
     case 4: NM_SELECT(4) break;
     case 8: NM_SELECT(8) break;
     case 16: NM_SELECT(16) break;
     case 32: NM_SELECT(32) break;
-    case 6: k_select<6, 0><<<grid, block, 0, s>>>(x, rows, k, ldx, n, y, ldy, nullptr, values, meta, meta_2bit); break;
-    case 10: k_select<10, 0><<<grid, block, 0, s>>>(x, rows, k, ldx, n, y, ldy, nullptr, values, meta, meta_2bit); break;
-    case 12: k_select<12, 0><<<grid, block, 0, s>>>(x, rows, k, ldx, n, y, ldy, nullptr, values, meta, meta_2bit); break;
-    case 14: k_select<14, 0><<<grid, block, 0, s>>>(x, rows, k, ldx, n, y, ldy, nullptr, values, meta, meta_2bit); break;
+    case 6: k_select<6, 0><<<grid, block, 0, s>>>(x, rows, k, ldx, n, y, ldy, nullptr, values, meta, meta_2bit, 0); break;
+    case 10: k_select<10, 0><<<grid, block, 0, s>>>(x, rows, k, ldx, n, y, ldy, nullptr, values, meta, meta_2bit, 0); break;
+    case 12: k_select<12, 0><<<grid, block, 0, s>>>(x, rows, k, ldx, n, y, ldy, nullptr, values, meta, meta_2bit, 0); break;
+    case 14: k_select<14, 0><<<grid, block, 0, s>>>(x, rows, k, ldx, n, y, ldy, nullptr, values, meta, meta_2bit, 0); break;
     default: return hipErrorInvalidValue;
   }
 #undef NM_SELECT

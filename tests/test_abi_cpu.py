@@ -63,7 +63,7 @@ def test_route_fields_change_routes_not_results_host_side():
     assert auto >= 64 * 14336 * 2 and no_few >= 64 * 14336 * 2
     assert auto != stream            # the split tile route and the streaming route need different scratch
     assert S.route_taken(a) == 0
-    assert set(S.ROUTE.values()) == {1 << i for i in range(14)}
+    assert set(S.ROUTE.values()) == {1 << i for i in range(15)}
     assert set(S.TAKEN.values()) == {1 << i for i in range(18)}
     # the header's values are the binding's
     src = open(os.path.join(ROOT, "include", "nm.h")).read()

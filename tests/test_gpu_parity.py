@@ -778,6 +778,40 @@ def test_spmm_act_decode_full_size_sampled(t):
     check_gemm(y, O.gemm(sx, w), sx, w, label=f"decode full t={t}")
 
 
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+@pytest.mark.parametrize("t", [2, 7, 16, 17, 32])
+def test_few_token_blocked_sx(t, kind):
+    """2-32 tokens on the weight-streaming kernel: S(X) staged in 16-token blocks (each
+    32-position piece of a block's rows contiguous) against the row-major staging (the
+    row_sx hint): the same bits and the same selection mask, and the oracle on every row.
+    Ragged token blocks (7, 17 tokens), ragged 16-row weight blocks, and a reduction length
+    whose parts end unevenly (the checked tail loads)."""
+    print(f"blocked S(X) t={t} {kind}", flush=True)
+    rng = np.random.default_rng(t * 3 + len(kind))
+    o, k = 520, 4064
+    x = synth.student_t_bf16(rng, (t, k), 4.0, 0.5)
+    w = synth.normal_bf16(rng, (o, k), 0.02)
+    kw = {}
+    if kind == "fp8":
+        q, sc = synth.fp8_e4m3_quantize_rows(w)
+        kw = dict(w8=q, s8=sc)
+    wa = None if kind == "fp8" else w
+    y, mask = run_act(x, wa, 8, 16, **kw)
+    tk = taken()
+    assert {"select", "few_stream"} <= tk, tk
+    with use_route("row_sx"):
+        y_row, mask_row = run_act(x, wa, 8, 16, **kw)
+    assert np.array_equal(y.view(np.uint32), y_row.view(np.uint32)), "blocked vs row-major S(X)"
+    assert (mask == mask_row).all()
+    sx, keep = O.sparsify(x, 8, 16)
+    assert (mask == O.pack_mask(keep)).all()
+    if kind == "bf16":
+        check_gemm(y, O.gemm(sx, w), sx, w, label=f"blocked S(X) t={t}")
+    else:
+        wdeq = O.fp8_e4m3_to_f64(q) * sc[:, None].astype(np.float64)
+        check_gemm(y, O.spmm_act_fp8(x, q, sc, 8, 16), sx, wdeq, label=f"blocked S(X) fp8 t={t}")
+
+
 @pytest.mark.parametrize("t", [16, 64, 128])
 def test_spmm_act_fp8_decode_full_size_sampled(t):
     """fp8 weights (per-row scales) on the 8:16 down-projection (W 4096 x 14336) at decode
